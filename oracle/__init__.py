@@ -1,0 +1,222 @@
+"""Plain CPU oracle of the SplitZip BF16 exponent-split codec (ctypes binding).
+
+TEST INFRASTRUCTURE ONLY.  The oracle defines the exact compressed byte format
+that the GPU library must reproduce.  Only the test suite, the smoke check and
+the CPU-baseline leg of the benchmark may import this package; the GPU library
+never does, and this package imports nothing from it.
+
+The arithmetic lives in ``splitzip_oracle.c`` (plain single-threaded C); this
+module only builds it with gcc, marshals numpy arrays, and reports errors.
+Sources: "SplitZip: Ultra-Fast Lossless KV Compression for Disaggregated LLM
+Serving" (GitHub README: Abstract, Highlights, Codec API) and its arXiv
+abstract.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "splitzip_oracle.c")
+LIB_PATH = os.path.join(_HERE, "libsplitzip_oracle.so")
+
+OK, BAD_ARGUMENT, BAD_STREAM, NO_ROOM, WRONG_CODEBOOK = 0, 1, 2, 3, 4
+_NAMES = {1: "bad argument", 2: "bad stream", 3: "no room for escapes", 4: "wrong codebook"}
+
+
+class OracleError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"oracle {what}: {_NAMES.get(code, code)}")
+        self.code = code
+
+
+def build(out: str = LIB_PATH, src: str = _SRC, extra_flags: tuple = ()) -> str:
+    """Compile the oracle with the host C compiler (no HIP involved)."""
+    cmd = ["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-shared", "-fPIC",
+           *extra_flags, "-o", out, src]
+    subprocess.run(cmd, check=True, cwd=os.path.dirname(src))
+    return out
+
+
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_u64p = ctypes.POINTER(ctypes.c_uint64)
+
+
+def _ptr(a: np.ndarray, t):
+    return a.ctypes.data_as(t)
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+        if path == LIB_PATH:
+            build()
+    lib = ctypes.CDLL(path)
+    lib.szo_histogram.argtypes = [_u16p, ctypes.c_uint64, _u64p]
+    lib.szo_histogram.restype = None
+    lib.szo_codebook.argtypes = [_u64p, _u8p]
+    lib.szo_codebook.restype = None
+    lib.szo_coverage.argtypes = [_u64p, _u8p, ctypes.c_uint64]
+    lib.szo_coverage.restype = ctypes.c_double
+    lib.szo_compressed_bytes.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint64]
+    lib.szo_compressed_bytes.restype = ctypes.c_uint64
+    lib.szo_encode.argtypes = [_u16p, ctypes.c_uint64, _u8p, ctypes.c_uint32, _u8p, _u8p, _u64p,
+                               _u16p, _u8p, ctypes.c_uint64, _u64p]
+    lib.szo_encode.restype = ctypes.c_int
+    lib.szo_decode.argtypes = [_u8p, _u8p, _u64p, _u16p, _u8p, ctypes.c_uint64, ctypes.c_uint64,
+                               _u8p, ctypes.c_uint32, _u16p]
+    lib.szo_decode.restype = ctypes.c_int
+    lib.szo_serialize.argtypes = [_u8p, _u8p, _u64p, _u16p, _u8p, ctypes.c_uint64,
+                                  ctypes.c_uint64, _u8p, ctypes.c_uint32, _u8p, ctypes.c_uint64]
+    lib.szo_serialize.restype = ctypes.c_int
+    lib.szo_stream_info.argtypes = [_u8p, ctypes.c_uint64, _u64p, ctypes.POINTER(ctypes.c_uint32),
+                                    _u64p, _u8p]
+    lib.szo_stream_info.restype = ctypes.c_int
+    lib.szo_decode_stream.argtypes = [_u8p, ctypes.c_uint64, _u8p, _u16p, ctypes.c_uint64]
+    lib.szo_decode_stream.restype = ctypes.c_int
+    return lib
+
+
+class Oracle:
+    """numpy-level wrapper around one loaded copy of the oracle library."""
+
+    def __init__(self, path: str = LIB_PATH):
+        self.lib = load(path)
+
+    # -- calibration ---------------------------------------------------------------
+    def histogram(self, x: np.ndarray) -> np.ndarray:
+        x = _u16(x)
+        h = np.zeros(256, np.uint64)
+        self.lib.szo_histogram(_ptr(x, _u16p), x.size, _ptr(h, _u64p))
+        return h
+
+    def codebook(self, hist: np.ndarray) -> np.ndarray:
+        hist = np.ascontiguousarray(hist, np.uint64)
+        cb = np.zeros(16, np.uint8)
+        self.lib.szo_codebook(_ptr(hist, _u64p), _ptr(cb, _u8p))
+        return cb
+
+    def coverage(self, hist: np.ndarray, cb: np.ndarray, m: int) -> float:
+        hist = np.ascontiguousarray(hist, np.uint64)
+        cb = np.ascontiguousarray(cb, np.uint8)
+        return float(self.lib.szo_coverage(_ptr(hist, _u64p), _ptr(cb, _u8p), m))
+
+    def calibrate(self, cal: np.ndarray):
+        """(codebook, coverage, histogram) of a calibration tensor."""
+        h = self.histogram(cal)
+        cb = self.codebook(h)
+        return cb, self.coverage(h, cb, _u16(cal).size), h
+
+    # -- sizes ---------------------------------------------------------------------
+    def compressed_bytes(self, n: int, chunk_size: int, n_escapes: int) -> int:
+        return int(self.lib.szo_compressed_bytes(n, chunk_size, n_escapes))
+
+    # -- encode / decode -----------------------------------------------------------
+    def encode(self, x: np.ndarray, cb: np.ndarray, chunk_size: int) -> dict:
+        """Sections of the compressed stream as numpy arrays (plus E and total bytes)."""
+        x = _u16(x)
+        cb = np.ascontiguousarray(cb, np.uint8)
+        n = x.size
+        n_chunks = -(-n // chunk_size) if chunk_size > 0 else 0
+        sm = np.zeros(n, np.uint8)
+        codes = np.zeros((n + 1) // 2, np.uint8)
+        chunk_off = np.zeros(n_chunks + 1, np.uint64)
+        cap = n
+        esc_pos = np.zeros(max(cap, 1), np.uint16)
+        esc_exp = np.zeros(max(cap, 1), np.uint8)
+        E = ctypes.c_uint64(0)
+        rc = self.lib.szo_encode(_ptr(x, _u16p), n, _ptr(cb, _u8p), chunk_size, _ptr(sm, _u8p),
+                                 _ptr(codes, _u8p), _ptr(chunk_off, _u64p), _ptr(esc_pos, _u16p),
+                                 _ptr(esc_exp, _u8p), cap, ctypes.byref(E))
+        if rc != OK:
+            raise OracleError(rc, "encode")
+        E = E.value
+        return {
+            "n": n, "chunk_size": chunk_size, "codebook": cb.copy(), "n_escapes": E,
+            "sm": sm, "codes": codes, "chunk_off": chunk_off,
+            "esc_pos": esc_pos[:E].copy(), "esc_exp": esc_exp[:E].copy(),
+            "compressed_bytes": self.compressed_bytes(n, chunk_size, E),
+        }
+
+    def decode(self, enc: dict, cb: np.ndarray | None = None) -> np.ndarray:
+        cb = np.ascontiguousarray(enc["codebook"] if cb is None else cb, np.uint8)
+        n, E = int(enc["n"]), int(enc["n_escapes"])
+        sm = np.ascontiguousarray(enc["sm"], np.uint8)
+        codes = np.ascontiguousarray(enc["codes"], np.uint8)
+        chunk_off = np.ascontiguousarray(enc["chunk_off"], np.uint64)
+        esc_pos = np.ascontiguousarray(enc["esc_pos"], np.uint16)
+        esc_exp = np.ascontiguousarray(enc["esc_exp"], np.uint8)
+        if esc_pos.size == 0:
+            esc_pos = np.zeros(1, np.uint16)
+            esc_exp = np.zeros(1, np.uint8)
+        y = np.zeros(max(n, 1), np.uint16)
+        rc = self.lib.szo_decode(_ptr(sm, _u8p), _ptr(codes, _u8p), _ptr(chunk_off, _u64p),
+                                 _ptr(esc_pos, _u16p), _ptr(esc_exp, _u8p), n, E,
+                                 _ptr(cb, _u8p), int(enc["chunk_size"]), _ptr(y, _u16p))
+        if rc != OK:
+            raise OracleError(rc, "decode")
+        return y[:n]
+
+    def serialize(self, enc: dict) -> bytes:
+        n, E, C = int(enc["n"]), int(enc["n_escapes"]), int(enc["chunk_size"])
+        total = self.compressed_bytes(n, C, E)
+        out = np.zeros(total, np.uint8)
+        sm = np.ascontiguousarray(enc["sm"], np.uint8)
+        codes = np.ascontiguousarray(enc["codes"], np.uint8)
+        chunk_off = np.ascontiguousarray(enc["chunk_off"], np.uint64)
+        esc_pos = np.ascontiguousarray(enc["esc_pos"], np.uint16)
+        esc_exp = np.ascontiguousarray(enc["esc_exp"], np.uint8)
+        cb = np.ascontiguousarray(enc["codebook"], np.uint8)
+        rc = self.lib.szo_serialize(_ptr(sm, _u8p), _ptr(codes, _u8p), _ptr(chunk_off, _u64p),
+                                    _ptr(esc_pos, _u16p), _ptr(esc_exp, _u8p), n, E,
+                                    _ptr(cb, _u8p), C, _ptr(out, _u8p), total)
+        if rc != OK:
+            raise OracleError(rc, "serialize")
+        return out.tobytes()
+
+    def stream_info(self, buf: bytes) -> dict:
+        b = np.frombuffer(buf, np.uint8).copy()
+        n, E = ctypes.c_uint64(0), ctypes.c_uint64(0)
+        C = ctypes.c_uint32(0)
+        cb = np.zeros(16, np.uint8)
+        rc = self.lib.szo_stream_info(_ptr(b, _u8p), b.size, ctypes.byref(n), ctypes.byref(C),
+                                      ctypes.byref(E), _ptr(cb, _u8p))
+        if rc != OK:
+            raise OracleError(rc, "stream header")
+        return {"n": n.value, "chunk_size": C.value, "n_escapes": E.value, "codebook": cb}
+
+    def decode_stream(self, buf: bytes, cb: np.ndarray) -> np.ndarray:
+        b = np.frombuffer(buf, np.uint8).copy()
+        if b.size == 0:
+            b = np.zeros(1, np.uint8)[:0]
+        info_n = int.from_bytes(bytes(b[16:24]), "little") if b.size >= 24 else 0
+        y = np.zeros(max(info_n, 1), np.uint16)
+        cb = np.ascontiguousarray(cb, np.uint8)
+        rc = self.lib.szo_decode_stream(_ptr(b, _u8p), b.size, _ptr(cb, _u8p), _ptr(y, _u16p),
+                                        info_n)
+        if rc != OK:
+            raise OracleError(rc, "decode stream")
+        return y[:info_n]
+
+
+def _u16(x) -> np.ndarray:
+    a = np.asarray(x)
+    if a.dtype != np.uint16:
+        if a.dtype.itemsize != 2:
+            raise TypeError(f"expected 16-bit words, got {a.dtype}")
+        a = a.view(np.uint16)
+    return np.ascontiguousarray(a).reshape(-1)
+
+
+_default: Oracle | None = None
+
+
+def get() -> Oracle:
+    """The process-wide oracle instance (built on first use if missing)."""
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default

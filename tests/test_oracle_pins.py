@@ -1,0 +1,151 @@
+"""CPU tests: the oracle against its pins (worked example, closed forms, brute force,
+statistics of the normal distribution), its error handling, and a mutation check
+that planted mistakes in the oracle are caught by the pins."""
+from __future__ import annotations
+
+import math
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins as pins
+import workloads
+
+O = oracle.get()
+
+
+def test_worked_example_bytes():
+    pins.check_worked_example(O)
+
+
+@pytest.mark.parametrize("C", [16, 1024, 4096, 65536])
+def test_exhaustive_words_closed_form(C):
+    pins.check_exhaustive(O, C)
+
+
+def test_brute_force_float_semantics():
+    pins.check_brute_force(O, seeds=range(40))
+
+
+def test_round_trips():
+    pins.check_round_trips(O)
+
+
+def test_codebook_rules():
+    pins.check_codebook_rules(O)
+
+
+def test_no_escape_and_all_escape():
+    cb = np.arange(100, 116, dtype=np.uint8)
+    # every exponent in the codebook: no escapes, chunk_off all zero
+    x = np.array([(e << 7) | (e % 128) for e in range(100, 116)] * 7, np.uint16)
+    enc = O.encode(x, cb, 16)
+    assert enc["n_escapes"] == 0 and not enc["chunk_off"].any()
+    # no exponent in the codebook: every element escapes, positions 0..len-1 per chunk
+    y = np.array([((e % 90) << 7) | 0x8000 for e in range(50)], np.uint16)
+    enc = O.encode(y, cb, 16)
+    assert enc["n_escapes"] == 50
+    assert enc["esc_pos"].tolist() == list(range(16)) * 3 + [0, 1]
+    assert enc["chunk_off"].tolist() == [0, 16, 32, 48, 50]
+    assert not enc["codes"].any()
+    assert np.array_equal(O.decode(enc), y)
+
+
+def test_normal_calibration_statistics():
+    """N(0,1) rounded to BF16: exponent field e holds |x| in [2^(e-127), 2^(e-126)) up to
+    rounding.  The 16 most likely fields are 114..129 and the mass outside them is
+    P(|x| < 2^-13) + P(|x| >= 8); the observed coverage must sit within 5 binomial sigma."""
+    wl = workloads.config1()
+    cb, cov, _ = O.calibrate(wl.calibration)
+    assert sorted(cb.tolist()) == list(range(114, 130))
+    p_out = math.erf(2.0 ** -13 / math.sqrt(2)) + math.erfc(8 / math.sqrt(2))
+    m = wl.calibration.size
+    assert abs((1 - cov) - p_out) < 5 * math.sqrt(p_out / m)
+    enc = O.encode(wl.segments[0], cb, 1024)
+    assert abs(enc["n_escapes"] / m - p_out) < 5 * math.sqrt(p_out / m)
+    assert np.array_equal(O.decode(enc), wl.segments[0])
+
+
+def test_rejects_bad_arguments_and_streams():
+    _, cal, x = pins.worked_example()
+    cb, _, _ = O.calibrate(cal)
+    for C in (0, 8, 15, 24, 1000, 131072):
+        with pytest.raises(oracle.OracleError):
+            O.encode(x, cb, C)
+    with pytest.raises(oracle.OracleError):
+        O.encode(x, np.zeros(16, np.uint8), 16)          # codebook entries must differ
+    enc = O.encode(x, cb, 16)
+    s = O.serialize(enc)
+    bad = []
+    b = bytearray(s); b[0] ^= 1; bad.append(bytes(b))             # magic
+    b = bytearray(s); b[4] = 2; bad.append(bytes(b))              # version
+    b = bytearray(s); b[8] = 24; bad.append(bytes(b))             # chunk size not 2^k
+    b = bytearray(s); b[24] = 3; bad.append(bytes(b))             # n_chunks
+    b = bytearray(s); b[60] = 1; bad.append(bytes(b))             # reserved
+    bad.append(s[:-1])                                            # truncated
+    for t in bad:
+        with pytest.raises(oracle.OracleError) as ei:
+            O.decode_stream(t, cb)
+        assert ei.value.code == oracle.BAD_STREAM
+    with pytest.raises(oracle.OracleError) as ei:
+        O.decode_stream(s, cb[::-1].copy())
+    assert ei.value.code == oracle.WRONG_CODEBOOK
+    # escape metadata: unsorted positions, position past the chunk, broken offsets
+    for mutate in (lambda e: e["esc_pos"].__setitem__(1, 4),
+                   lambda e: e["esc_pos"].__setitem__(10, 4),
+                   lambda e: e["chunk_off"].__setitem__(1, 12),
+                   lambda e: e["chunk_off"].__setitem__(2, 10)):
+        e = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in enc.items()}
+        mutate(e)
+        with pytest.raises(oracle.OracleError):
+            O.decode(e)
+
+
+# ---- mutation check: planted mistakes must fail a pin --------------------------------------
+
+MUTANTS = [
+    ("sign bit read from bit 14", "(u >> 15) & 0x1u", "(u >> 14) & 0x1u"),
+    ("exponent shifted by 8", "(u >> 7) & 0xFFu", "(u >> 8) & 0xFFu"),
+    ("exponent mask 7 bits", "(u >> 7) & 0xFFu", "(u >> 7) & 0x7Fu"),
+    ("mantissa mask 6 bits", "return u & 0x7Fu;", "return u & 0x3Fu;"),
+    ("ties ranked toward the larger exponent", "hist[e] > hist[best]", "hist[e] >= hist[best]"),
+    ("least frequent first", "hist[e] > hist[best]", "hist[e] < hist[best]"),
+    ("nibbles swapped in encode", "(code << (4 * (i % 2)))", "(code << (4 * (1 - i % 2)))"),
+    ("escape position not chunk-local", "esc_pos[E] = (uint16_t)(i - start);",
+     "esc_pos[E] = (uint16_t)(i);"),
+    ("escape keeps the exponent's low 7 bits", "esc_exp[E] = (uint8_t)e;",
+     "esc_exp[E] = (uint8_t)(e & 0x7Fu);"),
+    ("escape nibble set to 15", "code = 0;\n                if", "code = 15;\n                if"),
+    ("inclusive chunk offsets", "chunk_off[c] = E;\n        for", "for"),
+    ("total missing", "chunk_off[n_chunks] = E;\n    *n_escapes", "chunk_off[n_chunks] = 0;\n    *n_escapes"),
+    ("size without the final offset", "8u * (n_chunks + 1u)", "8u * n_chunks"),
+    ("big-endian fields", "p[b] = (uint8_t)(v >> (8 * b));", "p[b] = (uint8_t)(v >> (8 * (bytes - 1 - b)));"),
+    ("header version 2", "put_le(out + 4, 1, 2);", "put_le(out + 4, 2, 2);"),
+    ("sign dropped in sm", "sm[i] = (uint8_t)((bf16_sign(u) << 7) | bf16_mantissa(u));",
+     "sm[i] = (uint8_t)(bf16_mantissa(u));"),
+    ("decode patch ignores the stored exponent", "bf16_join(bf16_sign(y[i]), esc_exp[j], bf16_mantissa(y[i]))",
+     "bf16_join(bf16_sign(y[i]), cb[0], bf16_mantissa(y[i]))"),
+    ("decode reads the wrong nibble", "unsigned code = (codes[i / 2] >> (4 * (i % 2))) & 0xFu;",
+     "unsigned code = (codes[i / 2] >> (4 * (1 - i % 2))) & 0xFu;"),
+    ("codebook of 15", "for (k = 0; k < 16; ++k)\n        if (cb[k] == e)",
+     "for (k = 0; k < 15; ++k)\n        if (cb[k] == e)"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, name, old, new):
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "splitzip_oracle.c")).read()
+    assert src.count(old) == 1, f"mutation site for '{name}' not unique"
+    d = tmp_path / "mutant"
+    d.mkdir()
+    shutil.copy(os.path.join(os.path.dirname(oracle.__file__), "splitzip_oracle.h"), d)
+    (d / "splitzip_oracle.c").write_text(src.replace(old, new))
+    lib = str(d / "libmutant.so")
+    oracle.build(out=lib, src=str(d / "splitzip_oracle.c"))
+    mutant = oracle.Oracle(lib)
+    with pytest.raises((AssertionError, oracle.OracleError)):
+        pins.run_all(mutant)
