@@ -1,0 +1,249 @@
+"""Benchmark of the SplitZip BF16 codec on one MI355X.
+
+A step is one pass of the hot path over one batch: encode the whole input (split,
+pack, escape compaction, chunk offsets) and decode it back.  The codebook is
+calibrated once on the workload's separate calibration draw before timing, as the
+pages prescribe (offline calibration).  Inputs are resident in HBM before timing.
+
+Prints one JSON line.  Throughput is GB/s of BF16 input (2 bytes per word, 10^9).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("splitzip_kernels.hip", "splitzip_internal.h"):
+        with open(os.path.join(ROOT, "lossless_bf16_kv_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None when they
+    were taken on another kernel source or workload."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    src = kernel_source_hash()
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            p = line.split()
+            if len(p) == 5 and not line.startswith("#") and p[0] == kernel and p[1] == workload \
+                    and p[2] == src:
+                return {"fetch_bytes": int(p[3]), "write_bytes": int(p[4]),
+                        "total_bytes": int(p[3]) + int(p[4])}
+    return None
+
+
+def load_workload(args):
+    import workloads
+    if args.config == 3:
+        return workloads.config3(layers=args.layers, chunk_size=args.chunk_size)
+    if args.config == 4:
+        return workloads.config4(chunk_size=args.chunk_size)
+    wl = workloads.CONFIGS[args.config]()
+    wl.chunk_size = args.chunk_size
+    return wl
+
+
+def algorithmic_bytes(ns, Es, C):
+    """(read, write) bytes of one encode launch; decode is the reverse."""
+    r = w = 0
+    for n, E in zip(ns, Es):
+        n_ch = -(-n // C)
+        r += 2 * n
+        w += n + (n + 1) // 2 + 8 * (n_ch + 1) + 3 * E
+    return r, w
+
+
+def cpu_baseline(wl, codebook: bytes, sample_words: int):
+    """The plain single-threaded oracle timed on a bounded prefix of the same workload."""
+    import numpy as np
+    import oracle
+    o = oracle.get()
+    cb = np.frombuffer(codebook, np.uint8)
+    x = wl.segments[0][:sample_words]
+    t0 = time.perf_counter()
+    enc = o.encode(x, cb, wl.chunk_size)
+    t1 = time.perf_counter()
+    y = o.decode(enc)
+    t2 = time.perf_counter()
+    assert np.array_equal(y, x)
+    gb = 2 * x.size / 1e9
+    return {"value": round(gb / (t2 - t0), 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {x.size} BF16 words of the timed workload, encode + decode, "
+                      f"single-threaded plain C",
+            "encode_GBps": round(gb / (t1 - t0), 4), "decode_GBps": round(gb / (t2 - t1), 4)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--chunk-size", type=int, default=1024)
+    ap.add_argument("--layers", type=int, default=64, help="long-prefill KV layers (64 = 8.6 GB)")
+    ap.add_argument("--cpu-sample-words", type=int, default=1 << 30)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy-ceiling", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+                                   "(segments shard across GPUs with no exchange, see DESIGN.md)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import lossless_bf16_kv_amd as sz
+
+    t_gen = time.perf_counter()
+    wl = load_workload(args)
+    t_gen = time.perf_counter() - t_gen
+    dev = torch.device("cuda:0")
+    C = wl.chunk_size
+
+    xs = [torch.from_numpy(s.view(np.int16)).to(dev) for s in wl.segments]
+    cal = torch.from_numpy(wl.calibration.view(np.int16)).to(dev)
+    codec = sz.Codec(dev, C)
+    coverage = codec.calibrate(cal)
+    del cal
+
+    encs = codec.encode_batch(xs)              # sizes the escape arrays (retry if needed)
+    ys = [torch.empty_like(x) for x in xs]
+    result = torch.zeros(1 + len(xs), dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # One step = encode (non-blocking: escape counts stay in device memory, as a transfer
+    # engine would consume them) + decode, both enqueued on the same stream.
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        codec.encode_into_async(xs, encs, result)
+        if ev is not None:
+            ev[1].record(stream)
+        codec.decode_into(encs, ys)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert codec.finish_async(encs, result) == sz.OK
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    # verify the escape counts and the bitwise round trip before reporting
+    assert codec.finish_async(encs, result) == sz.OK
+    for x, y in zip(xs, ys):
+        assert torch.equal(x, y), "round trip is not bitwise"
+
+    enc_ms = sorted(e[0].elapsed_time(e[1]) for e in events)
+    dec_ms = sorted(e[1].elapsed_time(e[2]) for e in events)
+    enc_avg = sum(enc_ms) / len(enc_ms)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+    ns = [e.n for e in encs]
+    Es = [e.n_escapes for e in encs]
+    n = sum(ns)
+    E = sum(Es)
+    comp = sum(e.compressed_bytes for e in encs)
+    rd, wr = algorithmic_bytes(ns, Es, C)
+    enc_gbps_alg = (rd + wr) / (enc_avg * 1e-3) / 1e9
+    dec_gbps_alg = (rd + wr) / (dec_avg * 1e-3) / 1e9
+    wall_s = t1 - t0
+    value = 2 * n * args.steps / wall_s / 1e9
+
+    dominant = "encode_kernel" if enc_avg >= dec_avg else "decode_kernel"
+    dom_avg = max(enc_avg, dec_avg)
+    achieved = (rd + wr) / (dom_avg * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": measured_traffic(dominant, wl.name + f"_c{C}"),
+                "algorithmic_bytes": rd + wr, "avg_launch_ms": round(dom_avg, 4)}
+    other = "decode_kernel" if dominant == "encode_kernel" else "encode_kernel"
+    oth_avg = min(enc_avg, dec_avg)
+    roofline_other = {"bound": "hbm", "kernel": other,
+                      "achieved": round((rd + wr) / (oth_avg * 1e-3) / 1e9, 1),
+                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                      "frac": round((rd + wr) / (oth_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                      "traffic": measured_traffic(other, wl.name + f"_c{C}"),
+                      "avg_launch_ms": round(oth_avg, 4)}
+
+    copy_gbps = None
+    if not args.no_copy_ceiling:
+        a = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ce[0].record(stream)
+        for _ in range(5):
+            b.copy_(a)
+        ce[1].record(stream)
+        torch.cuda.synchronize()
+        copy_gbps = round(2 * a.numel() * 5 / (ce[0].elapsed_time(ce[1]) * 1e-3) / 1e9, 1)
+        del a, b
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, codec.codebook, args.cpu_sample_words)
+
+    out = {
+        "metric": "encode & decode GB/s (BF16 in) + % HBM roofline + compression ratio, 8.6 GB KV",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_s / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "n_words": n, "segments": len(ns), "chunk_size": C,
+                   "bytes_bf16": 2 * n, "description": wl.description},
+        "encode_GBps": round(2 * n / (enc_avg * 1e-3) / 1e9, 2),
+        "decode_GBps": round(2 * n / (dec_avg * 1e-3) / 1e9, 2),
+        "encode_hbm_frac": round(enc_gbps_alg / HBM_PEAK_GBPS, 4),
+        "decode_hbm_frac": round(dec_gbps_alg / HBM_PEAK_GBPS, 4),
+        "encode_ms": {"avg": round(enc_avg, 4), "min": round(enc_ms[0], 4),
+                      "median": round(enc_ms[len(enc_ms) // 2], 4)},
+        "decode_ms": {"avg": round(dec_avg, 4), "min": round(dec_ms[0], 4),
+                      "median": round(dec_ms[len(dec_ms) // 2], 4)},
+        "compression_ratio": round(2 * n / comp, 5),
+        "compressed_bytes": comp,
+        "n_escapes": E,
+        "coverage_calibration": coverage,
+        "coverage_input": 1 - E / n if n else None,
+        "roofline": roofline,
+        "roofline_other": roofline_other,
+        "copy_ceiling_GBps": copy_gbps,
+        "cpu_baseline": cpu,
+        "generate_s": round(t_gen, 1),
+        "kernel_source": kernel_source_hash(),
+        "round_trip_bitwise": True,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

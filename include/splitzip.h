@@ -1,0 +1,191 @@
+/*
+ * splitzip.h -- C ABI of the SplitZip BF16 exponent-split codec for AMD MI355X (gfx950).
+ *
+ * The calls follow the stateful codec the SplitZip README describes ("SplitZip:
+ * Ultra-Fast Lossless KV Compression for Disaggregated LLM Serving", sections
+ * "Codec API" and "Highlights"): a codec is built for one chunk size, calibrated once
+ * on a separate calibration tensor (which fixes its top-16 exponent codebook and
+ * returns the coverage), then encodes BF16 tensors into a compressed form whose size
+ * is reported, and decodes them back bit for bit.  Per the README "Abstract" and the
+ * arXiv abstract, the compressed form of n BF16 words is
+ *
+ *   sm[n]         one byte per word: (sign << 7) | 7-bit mantissa, kept exactly
+ *   codes[n/2]    one 4-bit code per word (word 2j in the low nibble of byte j) that
+ *                 indexes the 16-entry exponent codebook; 0 for escaped words
+ *   chunk_off[]   u64, n_chunks + 1 entries: escapes before each chunk start, then E
+ *   esc_pos[E]    u16 position of each escaped word inside its chunk
+ *   esc_exp[E]    u8 exponent of each escaped word (any exponent outside the codebook)
+ *
+ * with chunks of chunk_size words and escapes listed in ascending word order.  Its
+ * canonical serialization is a 64-byte header followed by the five sections;
+ * compressed_bytes = 64 + n + ceil(n/2) + 8 (n_chunks + 1) + 3 E.
+ *
+ * Conventions for every call
+ *   - Pointers named d_* and every pointer inside splitzip_segment are DEVICE
+ *     pointers on the codec's GPU; everything else is host memory.
+ *   - Device buffers are owned by the caller (they may be PyTorch tensors); the
+ *     library never frees them.  The codec owns only its small tables and a
+ *     per-stream workspace, released by splitzip_free.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream) of the device
+ *     that was current when the codec was created; work is enqueued on it.
+ *   - Every call returns a splitzip_status and never throws.  On error, a message
+ *     is available from splitzip_last_error() (per host thread).
+ *   - Alignment: BF16 data, sm and codes 16-byte aligned; chunk_off 8-byte;
+ *     esc_pos 2-byte.  n per segment < 2^38.
+ *   - A codec may be used from several host threads and streams; calls on one
+ *     stream are ordered, calls on different streams use different workspaces.
+ */
+#ifndef SPLITZIP_H
+#define SPLITZIP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPLITZIP_ABI_VERSION 1
+#define SPLITZIP_HEADER_BYTES 64
+#define SPLITZIP_MIN_CHUNK 16
+#define SPLITZIP_MAX_CHUNK 65536
+
+typedef enum splitzip_status {
+    SPLITZIP_OK = 0,
+    SPLITZIP_E_INVALID = 1,  /* null or misaligned pointer, bad chunk size, bad size   */
+    SPLITZIP_E_NOMEM = 2,    /* device or pinned host allocation failed                */
+    SPLITZIP_E_DEVICE = 3,   /* HIP runtime or kernel error                            */
+    SPLITZIP_E_CODEBOOK = 4, /* stream codebook differs from the codec's               */
+    SPLITZIP_E_FORMAT = 5,   /* bad magic, version, sizes or escape metadata           */
+    SPLITZIP_E_CAPACITY = 6  /* encode: more escapes than esc_capacity (see below)     */
+} splitzip_status;
+
+typedef struct splitzip_codec splitzip_codec;
+
+/*
+ * One tensor ("segment") of an encode or decode call.  A call may carry many
+ * segments (a ragged batch, one kernel launch); each has its own chunking, which
+ * restarts at the segment's first word, and its own output sections.
+ *
+ *   data             BF16 words, n of them.  encode reads, decode writes.
+ *   sm, codes,       compressed sections (sizes above).  encode writes, decode reads.
+ *   chunk_off
+ *   esc_pos, esc_exp escape arrays with esc_capacity slots.
+ *   esc_capacity     encode: slots available.  decode: ignored.
+ *   n_escapes        encode: OUT, the segment's E (also when E > esc_capacity).
+ *                    decode: IN, the E the sections were written with.
+ *   compressed_bytes encode: OUT, canonical stream size.  decode: ignored.
+ */
+typedef struct splitzip_segment {
+    uint16_t *data;
+    uint64_t n;
+    uint8_t *sm;
+    uint8_t *codes;
+    uint64_t *chunk_off;
+    uint16_t *esc_pos;
+    uint8_t *esc_exp;
+    uint64_t esc_capacity;
+    uint64_t n_escapes;
+    uint64_t compressed_bytes;
+} splitzip_segment;
+
+/*
+ * Calibrate a new codec on d_cal[0..n_cal) (README "Codec API": calibrate on a
+ * separate calibration set; README "Highlights" and arXiv abstract: top-16 exponent
+ * codebook fixed offline).  The codebook is the 16 exponents ranked first by
+ * (count descending, exponent ascending); *out_coverage = fraction of the n_cal
+ * exponents it holds (0 when n_cal = 0).  out_hist (optional, host uint64[256])
+ * receives the exponent histogram.  Blocks until the histogram is on the host.
+ * chunk_size: power of two in [16, 65536].  *out_codec is released by splitzip_free.
+ */
+int splitzip_calibrate(const uint16_t *d_cal, uint64_t n_cal, uint32_t chunk_size, void *stream,
+                       splitzip_codec **out_codec, double *out_coverage, uint64_t *out_hist);
+
+/*
+ * Build a codec from a known codebook (16 distinct exponents), e.g. the one carried by
+ * a received stream header (README "Roadmap": codebook metadata that travels with the
+ * payload).  The codec is bound to the current HIP device.
+ */
+int splitzip_codec_from_codebook(const uint8_t codebook[16], uint32_t chunk_size,
+                                 splitzip_codec **out_codec);
+
+/* Read back a codec's codebook, chunk size and device (any output may be NULL). */
+int splitzip_codec_info(const splitzip_codec *codec, uint8_t codebook[16], uint32_t *chunk_size,
+                        int *device);
+
+/*
+ * Encode n_seg segments (host array `segs`) in one launch.  Blocks until each
+ * segment's escape count is known, then fills n_escapes and compressed_bytes.
+ * Returns SPLITZIP_E_CAPACITY if some segment has more escapes than esc_capacity:
+ * its n_escapes then holds the count needed, its escape arrays hold only the first
+ * esc_capacity escapes, and the caller re-encodes with larger escape arrays.
+ * Segments with n = 0 are allowed (chunk_off[0] = 0 is written).
+ */
+int splitzip_encode(splitzip_codec *codec, uint32_t n_seg, splitzip_segment *segs, void *stream);
+
+/*
+ * Non-blocking encode: the same launch as splitzip_encode without the wait.  The
+ * kernel writes into d_result (device, caller-owned, 1 + n_seg uint64 words):
+ * d_result[0] = error bits (0 = success), d_result[1 + s] = E of segment s.
+ * segs[].n_escapes / compressed_bytes are not filled.  Once the stream has passed
+ * this work, a segment with E > esc_capacity holds only its first esc_capacity escapes
+ * and must be re-encoded with larger escape arrays.  The input and output buffers must
+ * stay valid until then.
+ */
+int splitzip_encode_async(splitzip_codec *codec, uint32_t n_seg, const splitzip_segment *segs,
+                          void *stream, uint64_t *d_result);
+
+/*
+ * Decode n_seg segments (host array `segs`, n_escapes as written by encode) into
+ * their `data` buffers, in one launch.  Asynchronous: only enqueues work on `stream`.
+ * The kernel never reads or writes outside the given sections even when the escape
+ * metadata is corrupt; it then ORs a nonzero flag into *d_error (optional device
+ * uint32, caller-owned, caller zeroes it) and leaves the affected words unpatched.
+ */
+int splitzip_decode(splitzip_codec *codec, uint32_t n_seg, const splitzip_segment *segs,
+                    void *stream, uint32_t *d_error);
+
+/* Release a codec, its tables and workspaces (NULL is a no-op).  Work that uses the
+ * codec must have completed; freeing its device memory synchronizes the device. */
+void splitzip_free(splitzip_codec *codec);
+
+/* ---- host helpers (no device work) ---- */
+
+/* ceil(n / chunk_size); 0 for an invalid chunk size. */
+uint64_t splitzip_chunk_count(uint64_t n, uint32_t chunk_size);
+
+/* 64 + n + ceil(n/2) + 8 (n_chunks + 1) + 3 n_escapes; 0 for an invalid chunk size. */
+uint64_t splitzip_compressed_bytes(uint64_t n, uint32_t chunk_size, uint64_t n_escapes);
+
+/*
+ * The canonical 64-byte stream header (little-endian): "SZB1", version u16 = 1,
+ * header bytes u16 = 64, chunk_size u32, flags u32 = 0, n u64, n_chunks u64,
+ * n_escapes u64, codebook[16], 8 zero bytes.
+ */
+int splitzip_write_header(const splitzip_codec *codec, uint64_t n, uint64_t n_escapes,
+                          uint8_t out[SPLITZIP_HEADER_BYTES]);
+
+/*
+ * Parse a header; total_len is the full stream length (checked against the sizes).
+ * Returns SPLITZIP_E_FORMAT for a malformed header.
+ */
+int splitzip_read_header(const uint8_t *buf, uint64_t total_len, uint64_t *n,
+                         uint32_t *chunk_size, uint64_t *n_escapes, uint8_t codebook[16]);
+
+/*
+ * Check that a received stream (header + total length) can be decoded by this codec:
+ * SPLITZIP_E_FORMAT if the header is malformed, SPLITZIP_E_CODEBOOK if its codebook or
+ * chunk size differs from the codec's (README "Codec API": encoded objects are decoded
+ * with the same calibrated state).
+ */
+int splitzip_check_header(const splitzip_codec *codec, const uint8_t *buf, uint64_t total_len);
+
+const char *splitzip_status_string(int status);
+
+/* Message describing the last failing call on this host thread ("" if none). */
+const char *splitzip_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPLITZIP_H */

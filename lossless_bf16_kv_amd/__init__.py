@@ -1,0 +1,437 @@
+"""SplitZip BF16 exponent-split codec on AMD MI355X (gfx950): Python binding.
+
+Every step of calibrate / encode / decode runs in the HIP kernels of
+``libsplitzip.so`` (sources in ``csrc/``); this module only marshals arguments
+through ctypes.  PyTorch provides device memory and streams.  There is no CPU
+fallback: if the library is missing or no GPU is present the calls raise.
+
+Two layers, mirroring the codec API of "SplitZip: Ultra-Fast Lossless KV
+Compression for Disaggregated LLM Serving" (README, "Codec API"):
+
+* the C ABI under the same names (``splitzip_calibrate``, ``splitzip_encode``,
+  ``splitzip_decode``, ``splitzip_free`` and host helpers), taking raw device
+  pointers as Python ints;
+* ``Codec(device, chunk_size)`` with ``calibrate(x) -> coverage``,
+  ``encode(x) -> Encoded`` (``.compressed_bytes``) and ``decode(encoded)``,
+  plus ``encode_batch`` / ``decode_batch`` for ragged batches in one launch.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsplitzip.so")
+
+OK, E_INVALID, E_NOMEM, E_DEVICE, E_CODEBOOK, E_FORMAT, E_CAPACITY = range(7)
+HEADER_BYTES = 64
+MIN_CHUNK, MAX_CHUNK = 16, 65536
+
+
+class SplitZipError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"splitzip status {status}: {message}")
+        self.status = status
+
+
+class splitzip_segment(ctypes.Structure):
+    """Mirror of ``splitzip_segment`` in include/splitzip.h."""
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("n", ctypes.c_uint64),
+        ("sm", ctypes.c_void_p),
+        ("codes", ctypes.c_void_p),
+        ("chunk_off", ctypes.c_void_p),
+        ("esc_pos", ctypes.c_void_p),
+        ("esc_exp", ctypes.c_void_p),
+        ("esc_capacity", ctypes.c_uint64),
+        ("n_escapes", ctypes.c_uint64),
+        ("compressed_bytes", ctypes.c_uint64),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsplitzip.so (built by ``__graft_entry__.build()``); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise SplitZipError(E_DEVICE, f"{LIB_PATH} is not built; run __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, u64, u32, i32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int
+    P = ctypes.POINTER
+    L.splitzip_calibrate.argtypes = [vp, u64, u32, vp, P(vp), P(ctypes.c_double), P(u64)]
+    L.splitzip_codec_from_codebook.argtypes = [P(ctypes.c_uint8), u32, P(vp)]
+    L.splitzip_codec_info.argtypes = [vp, P(ctypes.c_uint8), P(u32), P(i32)]
+    L.splitzip_encode.argtypes = [vp, u32, P(splitzip_segment), vp]
+    L.splitzip_encode_async.argtypes = [vp, u32, P(splitzip_segment), vp, vp]
+    L.splitzip_decode.argtypes = [vp, u32, P(splitzip_segment), vp, vp]
+    L.splitzip_free.argtypes = [vp]
+    L.splitzip_free.restype = None
+    L.splitzip_chunk_count.argtypes = [u64, u32]
+    L.splitzip_chunk_count.restype = u64
+    L.splitzip_compressed_bytes.argtypes = [u64, u32, u64]
+    L.splitzip_compressed_bytes.restype = u64
+    L.splitzip_write_header.argtypes = [vp, u64, u64, P(ctypes.c_uint8)]
+    L.splitzip_read_header.argtypes = [P(ctypes.c_uint8), u64, P(u64), P(u32), P(u64),
+                                       P(ctypes.c_uint8)]
+    L.splitzip_check_header.argtypes = [vp, P(ctypes.c_uint8), u64]
+    L.splitzip_status_string.argtypes = [i32]
+    L.splitzip_status_string.restype = ctypes.c_char_p
+    L.splitzip_last_error.argtypes = []
+    L.splitzip_last_error.restype = ctypes.c_char_p
+    for f in ("splitzip_calibrate", "splitzip_codec_from_codebook", "splitzip_codec_info",
+              "splitzip_encode", "splitzip_encode_async", "splitzip_decode",
+              "splitzip_write_header",
+              "splitzip_read_header", "splitzip_check_header"):
+        getattr(L, f).restype = i32
+    _lib = L
+    return L
+
+
+def _check(status: int, allow=()) -> int:
+    if status != OK and status not in allow:
+        msg = lib().splitzip_last_error().decode() or lib().splitzip_status_string(status).decode()
+        raise SplitZipError(status, msg)
+    return status
+
+
+def _u8buf(b: bytes):
+    return (ctypes.c_uint8 * len(b)).from_buffer_copy(b) if b else (ctypes.c_uint8 * 1)()
+
+
+# ---- C ABI, same names (pointers are Python ints) -------------------------------------
+
+def splitzip_calibrate(d_cal: int, n_cal: int, chunk_size: int, stream: int = 0):
+    """-> (codec handle, coverage, histogram list[256])."""
+    h = ctypes.c_void_p()
+    cov = ctypes.c_double()
+    hist = (ctypes.c_uint64 * 256)()
+    _check(lib().splitzip_calibrate(d_cal or None, n_cal, chunk_size, stream or None,
+                                    ctypes.byref(h), ctypes.byref(cov), hist))
+    return h.value, cov.value, list(hist)
+
+
+def splitzip_codec_from_codebook(codebook: bytes, chunk_size: int) -> int:
+    if len(codebook) != 16:
+        raise ValueError("codebook must be 16 bytes")
+    h = ctypes.c_void_p()
+    _check(lib().splitzip_codec_from_codebook(_u8buf(bytes(codebook)), chunk_size, ctypes.byref(h)))
+    return h.value
+
+
+def splitzip_codec_info(codec: int):
+    cb = (ctypes.c_uint8 * 16)()
+    c, d = ctypes.c_uint32(), ctypes.c_int()
+    _check(lib().splitzip_codec_info(codec, cb, ctypes.byref(c), ctypes.byref(d)))
+    return bytes(cb), c.value, d.value
+
+
+def splitzip_encode(codec: int, segs, stream: int = 0) -> int:
+    """Encode a ctypes array of splitzip_segment in place; returns OK or E_CAPACITY."""
+    return _check(lib().splitzip_encode(codec, len(segs), segs, stream or None), allow=(E_CAPACITY,))
+
+
+def splitzip_encode_async(codec: int, segs, stream: int, d_result: int) -> None:
+    """Enqueue an encode; error bits and per-segment E land in d_result (device u64[1+n])."""
+    _check(lib().splitzip_encode_async(codec, len(segs), segs, stream or None, d_result))
+
+
+def splitzip_decode(codec: int, segs, stream: int = 0, d_error: int = 0) -> None:
+    _check(lib().splitzip_decode(codec, len(segs), segs, stream or None, d_error or None))
+
+
+def splitzip_free(codec: int) -> None:
+    if codec:
+        lib().splitzip_free(codec)
+
+
+def splitzip_chunk_count(n: int, chunk_size: int) -> int:
+    return int(lib().splitzip_chunk_count(n, chunk_size))
+
+
+def splitzip_compressed_bytes(n: int, chunk_size: int, n_escapes: int) -> int:
+    return int(lib().splitzip_compressed_bytes(n, chunk_size, n_escapes))
+
+
+def splitzip_write_header(codec: int, n: int, n_escapes: int) -> bytes:
+    out = (ctypes.c_uint8 * HEADER_BYTES)()
+    _check(lib().splitzip_write_header(codec, n, n_escapes, out))
+    return bytes(out)
+
+
+def splitzip_read_header(buf: bytes) -> dict:
+    n, e = ctypes.c_uint64(), ctypes.c_uint64()
+    c = ctypes.c_uint32()
+    cb = (ctypes.c_uint8 * 16)()
+    _check(lib().splitzip_read_header(_u8buf(buf[:HEADER_BYTES]), len(buf), ctypes.byref(n),
+                                      ctypes.byref(c), ctypes.byref(e), cb))
+    return {"n": n.value, "chunk_size": c.value, "n_escapes": e.value, "codebook": bytes(cb)}
+
+
+def splitzip_check_header(codec: int, buf: bytes) -> None:
+    _check(lib().splitzip_check_header(codec, _u8buf(buf[:HEADER_BYTES]), len(buf)))
+
+
+# ---- README-style stateful codec --------------------------------------------------------
+
+@dataclasses.dataclass
+class Encoded:
+    """Compressed form of one tensor: device sections plus the sizes the codec reported."""
+    n: int
+    shape: tuple
+    dtype: object
+    chunk_size: int
+    codebook: bytes
+    sm: object            # torch.uint8 [n]
+    codes: object         # torch.uint8 [ceil(n/2)]
+    chunk_off: object     # torch.int64 [n_chunks + 1] (u64 values)
+    esc_pos_buf: object   # torch.int16 [capacity] (u16 values)
+    esc_exp_buf: object   # torch.uint8 [capacity]
+    n_escapes: int = 0
+    compressed_bytes: int = 0
+
+    @property
+    def esc_pos(self):
+        return self.esc_pos_buf[:self.n_escapes]
+
+    @property
+    def esc_exp(self):
+        return self.esc_exp_buf[:self.n_escapes]
+
+    @property
+    def ratio(self) -> float:
+        return 2 * self.n / self.compressed_bytes
+
+    def segment(self, data_ptr: int = 0) -> splitzip_segment:
+        return splitzip_segment(data_ptr or None, self.n, _ptr(self.sm), _ptr(self.codes),
+                                _ptr(self.chunk_off), _ptr(self.esc_pos_buf),
+                                _ptr(self.esc_exp_buf), self.esc_pos_buf.numel(),
+                                self.n_escapes, self.compressed_bytes)
+
+    def to_bytes(self, codec: "Codec") -> bytes:
+        """Canonical serialized stream: 64-byte header, then the five sections."""
+        import torch
+        head = splitzip_write_header(codec.handle, self.n, self.n_escapes)
+        parts = [self.sm, self.codes, self.chunk_off.view(torch.uint8),
+                 self.esc_pos.contiguous().view(torch.uint8), self.esc_exp]
+        body = b"".join(p.cpu().numpy().tobytes() for p in parts)
+        return head + body
+
+
+def _ptr(t) -> int | None:
+    return t.data_ptr() if t is not None and t.numel() > 0 else None
+
+
+def _words(x, device):
+    """Flat contiguous 16-bit view of a BF16 (or int16/uint16) device tensor."""
+    import torch
+    if x.element_size() != 2:
+        raise TypeError(f"expected a 16-bit tensor (BF16 words), got {x.dtype}")
+    if x.device != device:
+        raise ValueError(f"tensor is on {x.device}, codec is on {device}")
+    if not x.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return x.reshape(-1).view(torch.int16)
+
+
+class Codec:
+    """Stateful SplitZip codec bound to one GPU and one chunk size."""
+
+    def __init__(self, device="cuda", chunk_size: int = 1024):
+        import torch
+        if not torch.cuda.is_available():
+            raise SplitZipError(E_DEVICE, "no GPU: the SplitZip codec runs only on the GPU")
+        d = torch.device(device)
+        if d.index is None:
+            d = torch.device(d.type, torch.cuda.current_device())
+        if not (MIN_CHUNK <= chunk_size <= MAX_CHUNK and chunk_size & (chunk_size - 1) == 0):
+            raise ValueError("chunk_size must be a power of two in [16, 65536]")
+        lib()
+        self.device = d
+        self.chunk_size = chunk_size
+        self.handle = 0
+        self.coverage = None
+        self.histogram = None
+        self._escape_rate = 0.0
+
+    # -- state -----------------------------------------------------------------------
+    @classmethod
+    def from_codebook(cls, codebook: bytes, chunk_size: int = 1024, device="cuda") -> "Codec":
+        import torch
+        c = cls(device, chunk_size)
+        with torch.cuda.device(c.device):
+            c.handle = splitzip_codec_from_codebook(bytes(codebook), chunk_size)
+        return c
+
+    @property
+    def codebook(self) -> bytes:
+        self._need_handle()
+        return splitzip_codec_info(self.handle)[0]
+
+    def _need_handle(self):
+        if not self.handle:
+            raise SplitZipError(E_INVALID, "codec is not calibrated")
+
+    def _stream(self) -> int:
+        import torch
+        return torch.cuda.current_stream(self.device).cuda_stream
+
+    def __del__(self):
+        try:
+            splitzip_free(self.handle)
+        except Exception:
+            pass
+        self.handle = 0
+
+    # -- a1 -------------------------------------------------------------------------
+    def calibrate(self, x) -> float:
+        """Fix the top-16 exponent codebook from a calibration tensor; returns its coverage."""
+        import torch
+        w = _words(x, self.device)
+        with torch.cuda.device(self.device):
+            h, cov, hist = splitzip_calibrate(w.data_ptr() if w.numel() else 0, w.numel(),
+                                              self.chunk_size, self._stream())
+        splitzip_free(self.handle)
+        self.handle, self.coverage, self.histogram = h, cov, hist
+        self._escape_rate = 1.0 - cov if w.numel() else 0.0
+        return cov
+
+    # -- a2-a4, a7 -----------------------------------------------------------------
+    def empty_encoded(self, n: int, shape=None, dtype=None, escape_capacity: int | None = None):
+        """Allocate the device sections for an n-word tensor."""
+        import torch
+        n_chunks = -(-n // self.chunk_size)
+        if escape_capacity is None:
+            guess = math.ceil(n * max(self._escape_rate, 1e-4) * 1.25) + 64 * (n_chunks + 1)
+            escape_capacity = min(n, max(1024, guess))
+        kw = dict(device=self.device)
+        return Encoded(
+            n=n, shape=tuple(shape) if shape is not None else (n,),
+            dtype=dtype if dtype is not None else torch.bfloat16,
+            chunk_size=self.chunk_size, codebook=self.codebook,
+            sm=torch.empty(n, dtype=torch.uint8, **kw),
+            codes=torch.empty((n + 1) // 2, dtype=torch.uint8, **kw),
+            chunk_off=torch.empty(n_chunks + 1, dtype=torch.int64, **kw),
+            esc_pos_buf=torch.empty(max(escape_capacity, 1), dtype=torch.int16, **kw),
+            esc_exp_buf=torch.empty(max(escape_capacity, 1), dtype=torch.uint8, **kw))
+
+    def encode_into(self, xs, encs) -> int:
+        """One encode launch over tensors xs into preallocated encs; returns OK or E_CAPACITY
+        (then the Encoded whose n_escapes exceeds its capacity must be re-allocated)."""
+        import torch
+        self._need_handle()
+        words = [_words(x, self.device) for x in xs]
+        segs = (splitzip_segment * len(words))()
+        for i, (w, e) in enumerate(zip(words, encs)):
+            if w.numel() != e.n:
+                raise ValueError("tensor size differs from the preallocated sections")
+            segs[i] = e.segment(w.data_ptr() if w.numel() else 0)
+        with torch.cuda.device(self.device):
+            st = splitzip_encode(self.handle, segs, self._stream())
+        for i, e in enumerate(encs):
+            e.n_escapes = int(segs[i].n_escapes)
+            e.compressed_bytes = int(segs[i].compressed_bytes)
+        return st
+
+    def encode_into_async(self, xs, encs, result) -> None:
+        """Enqueue one encode launch without waiting.  `result` is a device int64 tensor
+        of 1 + len(xs) words: [error bits, E per segment].  The Encoded objects' n_escapes
+        / compressed_bytes are left as they are; call `finish_async` after the stream has
+        passed this work to fill them and check capacities."""
+        import torch
+        self._need_handle()
+        if result.dtype != torch.int64 or result.numel() < 1 + len(xs):
+            raise ValueError("result must be an int64 device tensor of 1 + len(xs) words")
+        words = [_words(x, self.device) for x in xs]
+        segs = (splitzip_segment * len(words))()
+        for i, (w, e) in enumerate(zip(words, encs)):
+            if w.numel() != e.n:
+                raise ValueError("tensor size differs from the preallocated sections")
+            segs[i] = e.segment(w.data_ptr() if w.numel() else 0)
+        with torch.cuda.device(self.device):
+            splitzip_encode_async(self.handle, segs, self._stream(), result.data_ptr())
+
+    def finish_async(self, encs, result) -> int:
+        """Read the result words of an encode_into_async (synchronizes with the host)."""
+        r = result.cpu().tolist()
+        if r[0] != 0:
+            raise SplitZipError(E_DEVICE, f"encode kernel reported error bits {r[0]:#x}")
+        st = OK
+        for i, e in enumerate(encs):
+            e.n_escapes = int(r[1 + i])
+            e.compressed_bytes = splitzip_compressed_bytes(e.n, self.chunk_size, e.n_escapes)
+            if e.n_escapes > e.esc_pos_buf.numel():
+                st = E_CAPACITY
+        return st
+
+    def encode(self, x, escape_capacity: int | None = None) -> Encoded:
+        return self.encode_batch([x], escape_capacity)[0]
+
+    def encode_batch(self, xs, escape_capacity: int | None = None) -> list:
+        """Encode several tensors (a ragged batch) in one launch."""
+        self._need_handle()
+        encs = [self.empty_encoded(x.numel(), x.shape, x.dtype, escape_capacity) for x in xs]
+        st = self.encode_into(xs, encs)
+        if st == E_CAPACITY:
+            for i, e in enumerate(encs):
+                if e.n_escapes > e.esc_pos_buf.numel():
+                    encs[i] = self.empty_encoded(e.n, e.shape, e.dtype, e.n_escapes)
+            st = self.encode_into(xs, encs)
+            assert st == OK
+        total = sum(e.n for e in encs)
+        if total:
+            self._escape_rate = max(self._escape_rate, sum(e.n_escapes for e in encs) / total)
+        return encs
+
+    # -- a5-a7 ------------------------------------------------------------------------
+    def decode_into(self, encs, outs, d_error: int = 0) -> None:
+        import torch
+        self._need_handle()
+        segs = (splitzip_segment * len(encs))()
+        for i, (e, y) in enumerate(zip(encs, outs)):
+            w = _words(y, self.device)
+            if w.numel() != e.n:
+                raise ValueError("output size differs from the encoded tensor")
+            if e.chunk_size != self.chunk_size or e.codebook != self.codebook:
+                raise SplitZipError(E_CODEBOOK, "encoded with a different codec state")
+            segs[i] = e.segment(w.data_ptr() if w.numel() else 0)
+        with torch.cuda.device(self.device):
+            splitzip_decode(self.handle, segs, self._stream(), d_error)
+
+    def decode(self, enc: Encoded):
+        return self.decode_batch([enc])[0]
+
+    def decode_batch(self, encs) -> list:
+        import torch
+        outs = [torch.empty(e.shape, dtype=e.dtype, device=self.device) for e in encs]
+        self.decode_into(encs, outs)
+        return outs
+
+    def decode_bytes(self, buf: bytes, shape=None, dtype=None):
+        """Decode a canonical serialized stream written by a codec with the same state."""
+        import numpy as np
+        import torch
+        self._need_handle()
+        splitzip_check_header(self.handle, buf)
+        h = splitzip_read_header(buf)
+        n, E = h["n"], h["n_escapes"]
+        n_chunks = splitzip_chunk_count(n, self.chunk_size)
+        enc = self.empty_encoded(n, shape, dtype, max(E, 1))
+        b = np.frombuffer(buf, np.uint8)
+        p = HEADER_BYTES
+        sizes = [n, (n + 1) // 2, 8 * (n_chunks + 1), 2 * E, E]
+        dests = [enc.sm, enc.codes, enc.chunk_off.view(torch.uint8),
+                 enc.esc_pos_buf[:E].view(torch.uint8), enc.esc_exp_buf[:E]]
+        for size, dst in zip(sizes, dests):
+            if size:
+                dst.copy_(torch.from_numpy(b[p:p + size].copy()))
+            p += size
+        enc.n_escapes = E
+        enc.compressed_bytes = len(buf)
+        return self.decode(enc)

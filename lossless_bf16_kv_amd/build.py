@@ -1,0 +1,47 @@
+"""Build the gfx950 shared library libsplitzip.so in-tree with hipcc."""
+from __future__ import annotations
+
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+SOURCES = [os.path.join(CSRC, "splitzip_kernels.hip"), os.path.join(CSRC, "splitzip_host.hip")]
+HEADERS = [os.path.join(CSRC, "splitzip_internal.h"), os.path.join(ROOT, "include", "splitzip.h")]
+LIB_PATH = os.path.join(HERE, "libsplitzip.so")
+ARCH = "gfx950"
+
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Wall", "-Wextra", "-Wno-unused-parameter",
+    # never let the compiler form packed-FP32 instructions
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return os.path.join(rocm, "bin", "hipcc")
+
+
+def build(out: str = LIB_PATH, extra_flags: tuple = (), verbose: bool = False) -> str:
+    """Compile every HIP source of the codec for gfx950 into one shared library."""
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"),
+           "-I", CSRC, "-o", out + ".tmp", *SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True, cwd=ROOT)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def is_stale(path: str = LIB_PATH) -> bool:
+    if not os.path.exists(path):
+        return True
+    t = os.path.getmtime(path)
+    return any(os.path.getmtime(s) > t for s in SOURCES + HEADERS)
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,729 @@
+// splitzip_host.hip -- host runtime and C ABI of the SplitZip BF16 exponent-split codec.
+//
+// The stateful codec follows "SplitZip: Ultra-Fast Lossless KV Compression for
+// Disaggregated LLM Serving" (README "Codec API"): built once per chunk size,
+// calibrated once (top-16 exponent codebook, coverage), then used for any number of
+// encode/decode calls whose outputs belong to that codec state.  This file owns:
+//   - argument validation and status/error reporting (never throws across the ABI);
+//   - codebook selection from the GPU histogram (count descending, exponent ascending);
+//   - per-stream workspaces: look-back status words, tile ticket counter, per-segment
+//     escape counts, pinned descriptor staging for ragged batches;
+//   - kernel launches and the one small readback that encode needs.
+#include "splitzip_internal.h"
+
+#include <splitzip.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+namespace {
+
+constexpr uint32_t kCodecMagic = 0x53a2c0dcu;
+constexpr int kStagingSlots = 4;
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int fail_hip(hipError_t e, const char *what)
+{
+    return fail(e == hipErrorOutOfMemory ? SPLITZIP_E_NOMEM : SPLITZIP_E_DEVICE, "%s: %s", what,
+                hipGetErrorString(e));
+}
+
+#define SZ_HIP(call, what)                     \
+    do {                                       \
+        hipError_t e_ = (call);                \
+        if (e_ != hipSuccess)                  \
+            return fail_hip(e_, what);         \
+    } while (0)
+
+bool chunk_size_ok(uint32_t c)
+{
+    return c >= SPLITZIP_MIN_CHUNK && c <= SPLITZIP_MAX_CHUNK && (c & (c - 1)) == 0;
+}
+
+uint32_t log2u(uint32_t c)
+{
+    uint32_t l = 0;
+    while ((1u << l) < c)
+        ++l;
+    return l;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+uint64_t ceil_div(uint64_t a, uint64_t b) { return a / b + (a % b != 0); }
+
+// Makes the codec's device current for the duration of a call.
+struct DeviceGuard {
+    int prev = -1;
+    bool switched = false;
+    hipError_t err = hipSuccess;
+    explicit DeviceGuard(int dev)
+    {
+        err = hipGetDevice(&prev);
+        if (err == hipSuccess && prev != dev) {
+            err = hipSetDevice(dev);
+            switched = err == hipSuccess;
+        }
+    }
+    ~DeviceGuard()
+    {
+        if (switched)
+            (void)hipSetDevice(prev);
+    }
+};
+
+// Descriptor tables of one ragged-batch launch, staged through pinned memory.
+struct Staging {
+    sz::SegDesc *h_segs = nullptr;
+    uint32_t *h_tiles = nullptr;
+    sz::SegDesc *d_segs = nullptr;
+    uint32_t *d_tiles = nullptr;
+    uint32_t cap = 0;
+    hipEvent_t done = nullptr;   // recorded after the last copy out of h_*
+    bool used = false;
+};
+
+// Everything a launch on one stream needs besides the caller's buffers.
+struct Workspace {
+    std::mutex mu;
+    hipStream_t stream = nullptr;
+    // device
+    uint64_t *status = nullptr;       // look-back words
+    uint64_t status_cap = 0;
+    unsigned long long *ticket = nullptr;
+    uint8_t *result = nullptr;        // [err u32, pad u32, seg_escapes u64 * result_cap]
+    uint32_t result_cap = 0;
+    // host
+    uint8_t *h_result = nullptr;      // pinned mirror of `result`
+    uint64_t ticket_base = 0;
+    uint32_t epoch = 0;
+    Staging staging[kStagingSlots];
+    int next_slot = 0;
+
+    ~Workspace()
+    {
+        (void)hipFree(status);
+        (void)hipFree(ticket);
+        (void)hipFree(result);
+        (void)hipHostFree(h_result);
+        for (Staging &s : staging) {
+            (void)hipHostFree(s.h_segs);
+            (void)hipHostFree(s.h_tiles);
+            (void)hipFree(s.d_segs);
+            (void)hipFree(s.d_tiles);
+            if (s.done)
+                (void)hipEventDestroy(s.done);
+        }
+    }
+};
+
+}  // namespace
+
+struct splitzip_codec {
+    uint32_t magic = kCodecMagic;
+    int device = 0;
+    uint32_t chunk_size = 0;
+    uint32_t log2_chunk = 0;
+    uint8_t cb[16] = {};
+    uint8_t *d_lut = nullptr;   // device [256] inverse LUT
+    std::mutex mu;
+    std::map<hipStream_t, std::unique_ptr<Workspace>> ws;
+};
+
+namespace {
+
+int codec_check(const splitzip_codec *c)
+{
+    if (!c || c->magic != kCodecMagic)
+        return fail(SPLITZIP_E_INVALID, "codec handle is NULL or not a codec");
+    return SPLITZIP_OK;
+}
+
+bool codebook_distinct(const uint8_t cb[16])
+{
+    bool seen[256] = {};
+    for (int k = 0; k < 16; ++k) {
+        if (seen[cb[k]])
+            return false;
+        seen[cb[k]] = true;
+    }
+    return true;
+}
+
+int make_codec(const uint8_t cb[16], uint32_t chunk_size, int device, hipStream_t stream,
+               splitzip_codec **out)
+{
+    std::unique_ptr<splitzip_codec> c(new (std::nothrow) splitzip_codec);
+    if (!c)
+        return fail(SPLITZIP_E_NOMEM, "host allocation of the codec failed");
+    c->device = device;
+    c->chunk_size = chunk_size;
+    c->log2_chunk = log2u(chunk_size);
+    std::memcpy(c->cb, cb, 16);
+    uint8_t lut[256];
+    std::memset(lut, sz::kEscapeEntry, sizeof lut);
+    for (int k = 0; k < 16; ++k)
+        lut[cb[k]] = (uint8_t)k;
+    SZ_HIP(hipMalloc(&c->d_lut, 256), "hipMalloc(codec tables)");
+    hipError_t e = hipMemcpyAsync(c->d_lut, lut, 256, hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) {
+        (void)hipFree(c->d_lut);
+        return fail_hip(e, "upload of codec tables");
+    }
+    *out = c.release();
+    return SPLITZIP_OK;
+}
+
+// Workspace of (codec, stream), created on first use.
+int get_workspace(splitzip_codec *c, hipStream_t stream, Workspace **out)
+{
+    std::lock_guard<std::mutex> lock(c->mu);
+    auto it = c->ws.find(stream);
+    if (it != c->ws.end()) {
+        *out = it->second.get();
+        return SPLITZIP_OK;
+    }
+    std::unique_ptr<Workspace> w(new (std::nothrow) Workspace);
+    if (!w)
+        return fail(SPLITZIP_E_NOMEM, "host allocation of a workspace failed");
+    w->stream = stream;
+    SZ_HIP(hipMalloc(&w->ticket, sizeof(unsigned long long)), "hipMalloc(ticket)");
+    SZ_HIP(hipMemsetAsync(w->ticket, 0, sizeof(unsigned long long), stream), "hipMemsetAsync(ticket)");
+    *out = w.get();
+    c->ws.emplace(stream, std::move(w));
+    return SPLITZIP_OK;
+}
+
+int ensure_status(Workspace *w, uint64_t n_tiles)
+{
+    if (w->status_cap >= n_tiles)
+        return SPLITZIP_OK;
+    uint64_t cap = std::max<uint64_t>(n_tiles, 2 * w->status_cap);
+    SZ_HIP(hipStreamSynchronize(w->stream), "hipStreamSynchronize");
+    (void)hipFree(w->status);
+    w->status = nullptr;
+    w->status_cap = 0;
+    SZ_HIP(hipMalloc(&w->status, cap * sizeof(uint64_t)), "hipMalloc(look-back status)");
+    SZ_HIP(hipMemsetAsync(w->status, 0, cap * sizeof(uint64_t), w->stream), "hipMemsetAsync(status)");
+    w->status_cap = cap;
+    return SPLITZIP_OK;
+}
+
+int ensure_result(Workspace *w, uint32_t n_seg)
+{
+    if (w->result_cap >= n_seg)
+        return SPLITZIP_OK;
+    uint32_t cap = std::max<uint32_t>(n_seg, std::max<uint32_t>(64, 2 * w->result_cap));
+    SZ_HIP(hipStreamSynchronize(w->stream), "hipStreamSynchronize");
+    (void)hipFree(w->result);
+    (void)hipHostFree(w->h_result);
+    w->result = nullptr;
+    w->h_result = nullptr;
+    w->result_cap = 0;
+    const size_t bytes = 8 + 8 * (size_t)cap;
+    SZ_HIP(hipMalloc(&w->result, bytes), "hipMalloc(results)");
+    SZ_HIP(hipHostMalloc(&w->h_result, bytes, hipHostMallocDefault), "hipHostMalloc(results)");
+    SZ_HIP(hipMemsetAsync(w->result, 0, bytes, w->stream), "hipMemsetAsync(results)");
+    w->result_cap = cap;
+    return SPLITZIP_OK;
+}
+
+// Copy the descriptor tables of a ragged batch to the device through a pinned slot.
+int stage_descriptors(Workspace *w, const std::vector<sz::SegDesc> &segs,
+                      const std::vector<uint32_t> &tiles, const sz::SegDesc **d_segs,
+                      const uint32_t **d_tiles)
+{
+    Staging &s = w->staging[w->next_slot];
+    w->next_slot = (w->next_slot + 1) % kStagingSlots;
+    const uint32_t n = (uint32_t)segs.size();
+    if (s.used)
+        SZ_HIP(hipEventSynchronize(s.done), "hipEventSynchronize(staging)");
+    if (s.cap < n) {
+        (void)hipHostFree(s.h_segs);
+        (void)hipHostFree(s.h_tiles);
+        (void)hipFree(s.d_segs);
+        (void)hipFree(s.d_tiles);
+        s.h_segs = nullptr;
+        s.h_tiles = nullptr;
+        s.d_segs = nullptr;
+        s.d_tiles = nullptr;
+        s.cap = 0;
+        const uint32_t cap = std::max<uint32_t>(n, 64);
+        SZ_HIP(hipHostMalloc(&s.h_segs, cap * sizeof(sz::SegDesc), hipHostMallocDefault), "hipHostMalloc(descriptors)");
+        SZ_HIP(hipHostMalloc(&s.h_tiles, (cap + 1) * sizeof(uint32_t), hipHostMallocDefault), "hipHostMalloc(tiles)");
+        SZ_HIP(hipMalloc(&s.d_segs, cap * sizeof(sz::SegDesc)), "hipMalloc(descriptors)");
+        SZ_HIP(hipMalloc(&s.d_tiles, (cap + 1) * sizeof(uint32_t)), "hipMalloc(tiles)");
+        s.cap = cap;
+    }
+    if (!s.done)
+        SZ_HIP(hipEventCreateWithFlags(&s.done, hipEventDisableTiming), "hipEventCreate");
+    std::memcpy(s.h_segs, segs.data(), n * sizeof(sz::SegDesc));
+    std::memcpy(s.h_tiles, tiles.data(), (n + 1) * sizeof(uint32_t));
+    SZ_HIP(hipMemcpyAsync(s.d_segs, s.h_segs, n * sizeof(sz::SegDesc), hipMemcpyHostToDevice, w->stream),
+           "hipMemcpyAsync(descriptors)");
+    SZ_HIP(hipMemcpyAsync(s.d_tiles, s.h_tiles, (n + 1) * sizeof(uint32_t), hipMemcpyHostToDevice, w->stream),
+           "hipMemcpyAsync(tiles)");
+    SZ_HIP(hipEventRecord(s.done, w->stream), "hipEventRecord(staging)");
+    s.used = true;
+    *d_segs = s.d_segs;
+    *d_tiles = s.d_tiles;
+    return SPLITZIP_OK;
+}
+
+// Shared validation of segment arrays; builds descriptors and tile starts.
+int prepare_segments(const splitzip_codec *c, uint32_t n_seg, const splitzip_segment *segs,
+                     bool encode, std::vector<sz::SegDesc> &desc, std::vector<uint32_t> &tiles)
+{
+    if (n_seg == 0)
+        return fail(SPLITZIP_E_INVALID, "n_seg is 0");
+    if (!segs)
+        return fail(SPLITZIP_E_INVALID, "segs is NULL");
+    desc.resize(n_seg);
+    tiles.resize((size_t)n_seg + 1);
+    uint64_t total = 0;
+    for (uint32_t i = 0; i < n_seg; ++i) {
+        const splitzip_segment &g = segs[i];
+        if (g.n >= sz::kMaxSegmentWords)
+            return fail(SPLITZIP_E_INVALID, "segment %u: n = %llu exceeds 2^38 - 1", i,
+                        (unsigned long long)g.n);
+        if (!g.chunk_off || !aligned(g.chunk_off, 8))
+            return fail(SPLITZIP_E_INVALID, "segment %u: chunk_off NULL or not 8-byte aligned", i);
+        if (g.n > 0) {
+            if (!g.data || !g.sm || !g.codes)
+                return fail(SPLITZIP_E_INVALID, "segment %u: NULL data/sm/codes", i);
+            if (!aligned(g.data, 16) || !aligned(g.sm, 16) || !aligned(g.codes, 16))
+                return fail(SPLITZIP_E_INVALID, "segment %u: data/sm/codes not 16-byte aligned", i);
+        }
+        const uint64_t esc = encode ? g.esc_capacity : g.n_escapes;
+        if (esc > 0 && (!g.esc_pos || !g.esc_exp || !aligned(g.esc_pos, 2)))
+            return fail(SPLITZIP_E_INVALID, "segment %u: escape arrays NULL or misaligned", i);
+        if (!encode && g.n_escapes > g.n)
+            return fail(SPLITZIP_E_FORMAT, "segment %u: %llu escapes for %llu words", i,
+                        (unsigned long long)g.n_escapes, (unsigned long long)g.n);
+        desc[i] = sz::SegDesc{g.data, g.sm, g.codes, g.chunk_off, g.esc_pos, g.esc_exp, g.n, esc};
+        tiles[i] = (uint32_t)total;
+        total += std::max<uint64_t>(1, ceil_div(g.n, sz::kTileWords));
+        if (total > 0xFFFFFFF0ull)
+            return fail(SPLITZIP_E_INVALID, "too many tiles in one call");
+    }
+    tiles[n_seg] = (uint32_t)total;
+    (void)c;
+    return SPLITZIP_OK;
+}
+
+}  // namespace
+
+// ======================================================================================
+// C ABI
+// ======================================================================================
+
+extern "C" {
+
+int splitzip_calibrate(const uint16_t *d_cal, uint64_t n_cal, uint32_t chunk_size, void *stream_,
+                       splitzip_codec **out_codec, double *out_coverage, uint64_t *out_hist)
+{
+    g_last_error.clear();
+    if (!out_codec)
+        return fail(SPLITZIP_E_INVALID, "out_codec is NULL");
+    if (!chunk_size_ok(chunk_size))
+        return fail(SPLITZIP_E_INVALID, "chunk_size %u is not a power of two in [16, 65536]", chunk_size);
+    if (n_cal > 0 && (!d_cal || !aligned(d_cal, 16)))
+        return fail(SPLITZIP_E_INVALID, "calibration pointer NULL or not 16-byte aligned");
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    int device = 0;
+    SZ_HIP(hipGetDevice(&device), "hipGetDevice");
+
+    uint64_t hist[256] = {};
+    if (n_cal > 0) {
+        const uint32_t blocks = sz::calibrate_blocks(n_cal);
+        uint32_t *d_partial = nullptr;
+        uint64_t *d_hist = nullptr;
+        SZ_HIP(hipMalloc(&d_partial, (size_t)blocks * 256 * sizeof(uint32_t)), "hipMalloc(histogram)");
+        hipError_t e = hipMalloc(&d_hist, 256 * sizeof(uint64_t));
+        if (e == hipSuccess)
+            e = sz::launch_calibrate(d_cal, n_cal, d_partial, blocks, d_hist, stream);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(hist, d_hist, sizeof hist, hipMemcpyDeviceToHost, stream);
+        if (e == hipSuccess)
+            e = hipStreamSynchronize(stream);
+        (void)hipFree(d_partial);
+        (void)hipFree(d_hist);
+        if (e != hipSuccess)
+            return fail_hip(e, "calibration histogram");
+    }
+    // Rank all 256 exponents by count (descending), ties by exponent (ascending).
+    int order[256];
+    for (int e = 0; e < 256; ++e)
+        order[e] = e;
+    std::stable_sort(order, order + 256, [&](int a, int b) { return hist[a] > hist[b]; });
+    uint8_t cb[16];
+    uint64_t covered = 0;
+    for (int k = 0; k < 16; ++k) {
+        cb[k] = (uint8_t)order[k];
+        covered += hist[order[k]];
+    }
+    splitzip_codec *c = nullptr;
+    int rc = make_codec(cb, chunk_size, device, stream, &c);
+    if (rc != SPLITZIP_OK)
+        return rc;
+    if (out_coverage)
+        *out_coverage = n_cal ? (double)covered / (double)n_cal : 0.0;
+    if (out_hist)
+        std::memcpy(out_hist, hist, sizeof hist);
+    *out_codec = c;
+    return SPLITZIP_OK;
+}
+
+int splitzip_codec_from_codebook(const uint8_t codebook[16], uint32_t chunk_size,
+                                 splitzip_codec **out_codec)
+{
+    g_last_error.clear();
+    if (!codebook || !out_codec)
+        return fail(SPLITZIP_E_INVALID, "codebook or out_codec is NULL");
+    if (!chunk_size_ok(chunk_size))
+        return fail(SPLITZIP_E_INVALID, "chunk_size %u is not a power of two in [16, 65536]", chunk_size);
+    if (!codebook_distinct(codebook))
+        return fail(SPLITZIP_E_INVALID, "codebook entries are not 16 distinct exponents");
+    int device = 0;
+    SZ_HIP(hipGetDevice(&device), "hipGetDevice");
+    return make_codec(codebook, chunk_size, device, nullptr, out_codec);
+}
+
+int splitzip_codec_info(const splitzip_codec *codec, uint8_t codebook[16], uint32_t *chunk_size,
+                        int *device)
+{
+    int rc = codec_check(codec);
+    if (rc != SPLITZIP_OK)
+        return rc;
+    if (codebook)
+        std::memcpy(codebook, codec->cb, 16);
+    if (chunk_size)
+        *chunk_size = codec->chunk_size;
+    if (device)
+        *device = codec->device;
+    return SPLITZIP_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Validation, workspace and launch shared by the blocking and non-blocking encode; the
+// caller holds the workspace lock.  d_result (optional): where the kernel writes its
+// error bits and per-segment escape counts instead of the workspace's result buffer.
+int encode_launch(splitzip_codec *codec, uint32_t n_seg, const splitzip_segment *segs,
+                  hipStream_t stream, uint64_t *d_result, Workspace **out_ws, uint32_t *out_tiles)
+{
+    int rc = codec_check(codec);
+    if (rc != SPLITZIP_OK)
+        return rc;
+    std::vector<sz::SegDesc> desc;
+    std::vector<uint32_t> tiles;
+    rc = prepare_segments(codec, n_seg, segs, true, desc, tiles);
+    if (rc != SPLITZIP_OK)
+        return rc;
+    Workspace *w = nullptr;
+    rc = get_workspace(codec, stream, &w);
+    if (rc != SPLITZIP_OK)
+        return rc;
+    const uint32_t n_tiles = tiles[n_seg];
+    if ((rc = ensure_status(w, n_tiles)) != SPLITZIP_OK)
+        return rc;
+    if (!d_result && (rc = ensure_result(w, n_seg)) != SPLITZIP_OK)
+        return rc;
+
+    sz::EncodeArgs a{};
+    a.seg0 = desc[0];
+    if (n_seg > 1 && (rc = stage_descriptors(w, desc, tiles, &a.segs, &a.tile_start)) != SPLITZIP_OK)
+        return rc;
+    // a new epoch per launch keeps earlier launches' status words from being read as
+    // current; after 2^24 - 1 launches the words are cleared and the count restarts
+    if (w->epoch >= sz::kEpochMax) {
+        SZ_HIP(hipMemsetAsync(w->status, 0, w->status_cap * sizeof(uint64_t), stream), "hipMemsetAsync(status)");
+        w->epoch = 0;
+    }
+    w->epoch += 1;
+    uint8_t *res = d_result ? reinterpret_cast<uint8_t *>(d_result) : w->result;
+    a.lut = codec->d_lut;
+    a.status = w->status;
+    a.ticket = w->ticket;
+    a.err = reinterpret_cast<uint32_t *>(res);
+    a.seg_escapes = reinterpret_cast<uint64_t *>(res + 8);
+    a.ticket_base = w->ticket_base;
+    a.epoch_tag = (uint64_t)w->epoch << sz::kEpochShift;
+    a.n_seg = n_seg;
+    a.n_tiles = n_tiles;
+    a.log2_chunk = codec->log2_chunk;
+    hipError_t e = sz::launch_encode(a, stream);
+    if (e != hipSuccess) {
+        // the counter state is unknown after a failed launch: start the workspace over
+        (void)hipMemsetAsync(w->ticket, 0, sizeof(unsigned long long), stream);
+        w->ticket_base = 0;
+        w->epoch = sz::kEpochMax;
+        return fail_hip(e, "encode launch");
+    }
+    w->ticket_base += n_tiles;
+    *out_ws = w;
+    *out_tiles = n_tiles;
+    return SPLITZIP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int splitzip_encode_async(splitzip_codec *codec, uint32_t n_seg, const splitzip_segment *segs,
+                          void *stream_, uint64_t *d_result)
+{
+    g_last_error.clear();
+    if (!d_result || !aligned(d_result, 8))
+        return fail(SPLITZIP_E_INVALID, "d_result NULL or not 8-byte aligned");
+    int rc = codec_check(codec);
+    if (rc != SPLITZIP_OK)
+        return rc;
+    DeviceGuard dg(codec->device);
+    if (dg.err != hipSuccess)
+        return fail_hip(dg.err, "hipSetDevice");
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    Workspace *ws = nullptr;
+    rc = get_workspace(codec, stream, &ws);
+    if (rc != SPLITZIP_OK)
+        return rc;
+    // the lock covers only the launch: nothing is read back
+    std::lock_guard<std::mutex> lock(ws->mu);
+    Workspace *w = nullptr;
+    uint32_t n_tiles = 0;
+    return encode_launch(codec, n_seg, segs, stream, d_result, &w, &n_tiles);
+}
+
+int splitzip_encode(splitzip_codec *codec, uint32_t n_seg, splitzip_segment *segs, void *stream_)
+{
+    g_last_error.clear();
+    int rc = codec_check(codec);
+    if (rc != SPLITZIP_OK)
+        return rc;
+    DeviceGuard dg(codec->device);
+    if (dg.err != hipSuccess)
+        return fail_hip(dg.err, "hipSetDevice");
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    Workspace *ws = nullptr;
+    rc = get_workspace(codec, stream, &ws);
+    if (rc != SPLITZIP_OK)
+        return rc;
+    std::lock_guard<std::mutex> lock(ws->mu);
+    Workspace *w = nullptr;
+    uint32_t n_tiles = 0;
+    rc = encode_launch(codec, n_seg, segs, stream, nullptr, &w, &n_tiles);
+    if (rc != SPLITZIP_OK)
+        return rc;
+    hipError_t e = hipMemcpyAsync(w->h_result, w->result, 8 + 8 * (size_t)n_seg, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(stream);
+    if (e != hipSuccess)
+        return fail_hip(e, "encode readback");
+    uint32_t kerr = 0;
+    std::memcpy(&kerr, w->h_result, 4);
+    if (kerr) {
+        SZ_HIP(hipMemsetAsync(w->result, 0, 8, stream), "hipMemsetAsync(err)");
+        return fail(SPLITZIP_E_DEVICE, "encode kernel reported error bits 0x%x", kerr);
+    }
+    const uint64_t *E = reinterpret_cast<const uint64_t *>(w->h_result + 8);
+    rc = SPLITZIP_OK;
+    for (uint32_t i = 0; i < n_seg; ++i) {
+        segs[i].n_escapes = E[i];
+        segs[i].compressed_bytes = splitzip_compressed_bytes(segs[i].n, codec->chunk_size, E[i]);
+        if (E[i] > segs[i].esc_capacity && rc == SPLITZIP_OK)
+            rc = fail(SPLITZIP_E_CAPACITY, "segment %u has %llu escapes, capacity %llu", i,
+                      (unsigned long long)E[i], (unsigned long long)segs[i].esc_capacity);
+    }
+    return rc;
+}
+
+int splitzip_decode(splitzip_codec *codec, uint32_t n_seg, const splitzip_segment *segs,
+                    void *stream_, uint32_t *d_error)
+{
+    g_last_error.clear();
+    int rc = codec_check(codec);
+    if (rc != SPLITZIP_OK)
+        return rc;
+    std::vector<sz::SegDesc> desc;
+    std::vector<uint32_t> tiles;
+    rc = prepare_segments(codec, n_seg, segs, false, desc, tiles);
+    if (rc != SPLITZIP_OK)
+        return rc;
+    if (d_error && !aligned(d_error, 4))
+        return fail(SPLITZIP_E_INVALID, "d_error not 4-byte aligned");
+    DeviceGuard dg(codec->device);
+    if (dg.err != hipSuccess)
+        return fail_hip(dg.err, "hipSetDevice");
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+
+    sz::DecodeArgs a{};
+    a.seg0 = desc[0];
+    if (n_seg > 1) {
+        Workspace *w = nullptr;
+        rc = get_workspace(codec, stream, &w);
+        if (rc != SPLITZIP_OK)
+            return rc;
+        std::lock_guard<std::mutex> lock(w->mu);
+        if ((rc = stage_descriptors(w, desc, tiles, &a.segs, &a.tile_start)) != SPLITZIP_OK)
+            return rc;
+    }
+    std::memcpy(a.cb, codec->cb, 16);
+    a.err = d_error;
+    a.n_seg = n_seg;
+    a.n_tiles = tiles[n_seg];
+    a.log2_chunk = codec->log2_chunk;
+    hipError_t e = sz::launch_decode(a, stream);
+    if (e != hipSuccess)
+        return fail_hip(e, "decode launch");
+    return SPLITZIP_OK;
+}
+
+void splitzip_free(splitzip_codec *codec)
+{
+    if (!codec || codec->magic != kCodecMagic)
+        return;
+    {
+        DeviceGuard dg(codec->device);
+        codec->ws.clear();
+        (void)hipFree(codec->d_lut);
+    }
+    codec->magic = 0;
+    delete codec;
+}
+
+uint64_t splitzip_chunk_count(uint64_t n, uint32_t chunk_size)
+{
+    return chunk_size_ok(chunk_size) ? ceil_div(n, chunk_size) : 0;
+}
+
+uint64_t splitzip_compressed_bytes(uint64_t n, uint32_t chunk_size, uint64_t n_escapes)
+{
+    if (!chunk_size_ok(chunk_size))
+        return 0;
+    return SPLITZIP_HEADER_BYTES + n + ceil_div(n, 2) + 8 * (ceil_div(n, chunk_size) + 1) + 3 * n_escapes;
+}
+
+static void le_put(uint8_t *p, uint64_t v, int bytes)
+{
+    for (int b = 0; b < bytes; ++b)
+        p[b] = (uint8_t)(v >> (8 * b));
+}
+
+static uint64_t le_get(const uint8_t *p, int bytes)
+{
+    uint64_t v = 0;
+    for (int b = 0; b < bytes; ++b)
+        v |= (uint64_t)p[b] << (8 * b);
+    return v;
+}
+
+int splitzip_write_header(const splitzip_codec *codec, uint64_t n, uint64_t n_escapes,
+                          uint8_t out[SPLITZIP_HEADER_BYTES])
+{
+    g_last_error.clear();
+    int rc = codec_check(codec);
+    if (rc != SPLITZIP_OK)
+        return rc;
+    if (!out)
+        return fail(SPLITZIP_E_INVALID, "out is NULL");
+    std::memset(out, 0, SPLITZIP_HEADER_BYTES);
+    std::memcpy(out, "SZB1", 4);
+    le_put(out + 4, 1, 2);
+    le_put(out + 6, SPLITZIP_HEADER_BYTES, 2);
+    le_put(out + 8, codec->chunk_size, 4);
+    le_put(out + 12, 0, 4);
+    le_put(out + 16, n, 8);
+    le_put(out + 24, ceil_div(n, codec->chunk_size), 8);
+    le_put(out + 32, n_escapes, 8);
+    std::memcpy(out + 40, codec->cb, 16);
+    return SPLITZIP_OK;
+}
+
+int splitzip_read_header(const uint8_t *buf, uint64_t total_len, uint64_t *n, uint32_t *chunk_size,
+                         uint64_t *n_escapes, uint8_t codebook[16])
+{
+    g_last_error.clear();
+    if (!buf)
+        return fail(SPLITZIP_E_INVALID, "buf is NULL");
+    if (total_len < SPLITZIP_HEADER_BYTES)
+        return fail(SPLITZIP_E_FORMAT, "stream shorter than its header");
+    if (std::memcmp(buf, "SZB1", 4) != 0)
+        return fail(SPLITZIP_E_FORMAT, "bad magic");
+    if (le_get(buf + 4, 2) != 1 || le_get(buf + 6, 2) != SPLITZIP_HEADER_BYTES || le_get(buf + 12, 4) != 0)
+        return fail(SPLITZIP_E_FORMAT, "unsupported version, header size or flags");
+    for (int i = 56; i < 64; ++i)
+        if (buf[i])
+            return fail(SPLITZIP_E_FORMAT, "reserved header bytes are not zero");
+    const uint32_t c = (uint32_t)le_get(buf + 8, 4);
+    const uint64_t nn = le_get(buf + 16, 8), nch = le_get(buf + 24, 8), e = le_get(buf + 32, 8);
+    if (!chunk_size_ok(c) || nch != ceil_div(nn, c))
+        return fail(SPLITZIP_E_FORMAT, "bad chunk size or chunk count");
+    if (e > nn || total_len != splitzip_compressed_bytes(nn, c, e))
+        return fail(SPLITZIP_E_FORMAT, "sizes do not match the stream length");
+    if (n)
+        *n = nn;
+    if (chunk_size)
+        *chunk_size = c;
+    if (n_escapes)
+        *n_escapes = e;
+    if (codebook)
+        std::memcpy(codebook, buf + 40, 16);
+    return SPLITZIP_OK;
+}
+
+int splitzip_check_header(const splitzip_codec *codec, const uint8_t *buf, uint64_t total_len)
+{
+    int rc = codec_check(codec);
+    if (rc != SPLITZIP_OK)
+        return rc;
+    uint32_t c = 0;
+    uint8_t cb[16];
+    rc = splitzip_read_header(buf, total_len, nullptr, &c, nullptr, cb);
+    if (rc != SPLITZIP_OK)
+        return rc;
+    if (c != codec->chunk_size || std::memcmp(cb, codec->cb, 16) != 0)
+        return fail(SPLITZIP_E_CODEBOOK, "stream codebook or chunk size differs from the codec's");
+    return SPLITZIP_OK;
+}
+
+const char *splitzip_status_string(int status)
+{
+    switch (status) {
+    case SPLITZIP_OK: return "ok";
+    case SPLITZIP_E_INVALID: return "invalid argument";
+    case SPLITZIP_E_NOMEM: return "out of memory";
+    case SPLITZIP_E_DEVICE: return "device error";
+    case SPLITZIP_E_CODEBOOK: return "codebook mismatch";
+    case SPLITZIP_E_FORMAT: return "malformed stream";
+    case SPLITZIP_E_CAPACITY: return "escape capacity exceeded";
+    default: return "unknown status";
+    }
+}
+
+const char *splitzip_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,599 @@
+// splitzip_kernels.hip -- gfx950 (CDNA4) kernels of the SplitZip BF16 exponent-split codec.
+//
+// Method ("SplitZip: Ultra-Fast Lossless KV Compression for Disaggregated LLM Serving",
+// README "Abstract" and "Highlights"; arXiv abstract): each BF16 word keeps its sign and
+// 7 mantissa bits exactly in one byte; its 8-bit exponent becomes a 4-bit code into a
+// top-16 exponent codebook calibrated offline; exponents outside the codebook go to a
+// chunk-local sparse escape stream of (position, exponent).  Decoding is the dense path
+// (code -> codebook exponent) plus a sparse correction at the escape positions.
+//
+// The work is pure integer/byte manipulation and bound by HBM bandwidth: no floating
+// point touches a value and no MFMA is used.  Design points:
+//   - 16-byte, lane-contiguous loads and stores (a wave touches 1 KiB per instruction);
+//   - encode: 256-byte inverse LUT in LDS (exponent -> code or escape bit), sign+mantissa
+//     bytes gathered with v_perm_b32, codes packed two per byte;
+//   - encode: escape ranks inside a tile by a wave prefix of packed per-group counts plus
+//     an LDS prefix over the 4 waves; across tiles by a single-pass decoupled look-back
+//     (dynamic tile tickets, one packed 64-bit status word per tile, agent-scope atomics
+//     so that the 8 XCDs, whose L2s are not coherent with each other, see one another);
+//   - decode: codebook lookup with two v_perm_b32 byte selects per 4 codes (codebook in
+//     SGPRs), exponent bytes staged in LDS only for tiles that hold escapes, where the
+//     escapes overwrite them before the words are assembled.
+#include "splitzip_internal.h"
+
+namespace sz {
+
+// ---- small wave64 helpers -------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t lane_id()
+{
+    return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+__device__ __forceinline__ uint32_t shfl_u32(uint32_t v, uint32_t src_lane)
+{
+    return (uint32_t)__builtin_amdgcn_ds_bpermute((int)(src_lane << 2), (int)v);
+}
+
+// Inclusive prefix sum over the 64 lanes (all lanes must be active).  Used on words that
+// pack two 16-bit counters whose sums stay below 65536.
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v, uint32_t lane)
+{
+#pragma unroll
+    for (uint32_t d = 1; d < 64; d <<= 1) {
+        uint32_t t = shfl_u32(v, lane >= d ? lane - d : lane);
+        if (lane >= d)
+            v += t;
+    }
+    return v;
+}
+
+__device__ __forceinline__ uint64_t wave_total_u64(uint64_t v, uint32_t lane)
+{
+#pragma unroll
+    for (uint32_t d = 1; d < 64; d <<= 1) {
+        uint32_t lo = shfl_u32((uint32_t)v, lane ^ d);
+        uint32_t hi = shfl_u32((uint32_t)(v >> 32), lane ^ d);
+        v += ((uint64_t)hi << 32) | lo;
+    }
+    return v;
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
+{
+    // v_perm_b32: selector byte s picks byte s of the 8-byte value {hi, lo} (s < 8).
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// Segment that owns global tile t: largest s with tile_start[s] <= t.
+__device__ __forceinline__ uint32_t find_segment(const uint32_t *tile_start, uint32_t n_seg,
+                                                 uint32_t t)
+{
+    uint32_t lo = 0, hi = n_seg;
+    while (hi - lo > 1) {
+        uint32_t mid = (lo + hi) >> 1;
+        if (tile_start[mid] <= t)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    return lo;
+}
+
+// ======================================================================================
+// a1  calibration histogram
+// ======================================================================================
+
+__global__ __launch_bounds__(kThreads) void calib_hist_kernel(const uint16_t *__restrict__ x,
+                                                              uint64_t n,
+                                                              uint32_t *__restrict__ partial)
+{
+    // one sub-histogram per wave keeps LDS atomic contention on the few hot exponents down
+    __shared__ uint32_t h[kWaves][256];
+    const uint32_t tid = threadIdx.x;
+    for (uint32_t i = tid; i < kWaves * 256; i += kThreads)
+        (&h[0][0])[i] = 0;
+    __syncthreads();
+    uint32_t *mine = h[tid >> 6];
+
+    const uint64_t groups = n / kGroupWords;
+    const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+    for (uint64_t g = (uint64_t)blockIdx.x * kThreads + tid; g < groups; g += stride) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(x + g * kGroupWords);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            atomicAdd(&mine[(w[k] >> 7) & 0xFFu], 1u);
+            atomicAdd(&mine[(w[k] >> 23) & 0xFFu], 1u);
+        }
+    }
+    // ragged tail (fewer than 8 words), handled by the first workgroup
+    if (blockIdx.x == 0 && tid < n - groups * kGroupWords)
+        atomicAdd(&mine[(x[groups * kGroupWords + tid] >> 7) & 0xFFu], 1u);
+    __syncthreads();
+    for (uint32_t e = tid; e < 256; e += kThreads) {
+        uint32_t s = 0;
+        for (int w = 0; w < kWaves; ++w)
+            s += h[w][e];
+        partial[(uint64_t)blockIdx.x * 256 + e] = s;
+    }
+}
+
+__global__ __launch_bounds__(256) void calib_reduce_kernel(const uint32_t *__restrict__ partial,
+                                                           uint32_t blocks,
+                                                           uint64_t *__restrict__ hist)
+{
+    const uint32_t e = threadIdx.x;
+    uint64_t s = 0;
+    for (uint32_t b = 0; b < blocks; ++b)
+        s += partial[(uint64_t)b * 256 + e];
+    hist[e] = s;
+}
+
+uint32_t calibrate_blocks(uint64_t n)
+{
+    const uint64_t per_block = (uint64_t)kThreads * kGroupWords * 8;
+    uint64_t b = (n + per_block - 1) / per_block;
+    if (b < 1)
+        b = 1;
+    if (b > kCalibBlocksMax)
+        b = kCalibBlocksMax;
+    return (uint32_t)b;
+}
+
+hipError_t launch_calibrate(const uint16_t *d_x, uint64_t n, uint32_t *d_partial,
+                            uint32_t n_blocks, uint64_t *d_hist, hipStream_t stream)
+{
+    calib_hist_kernel<<<n_blocks, kThreads, 0, stream>>>(d_x, n, d_partial);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    calib_reduce_kernel<<<1, 256, 0, stream>>>(d_partial, n_blocks, d_hist);
+    return hipGetLastError();
+}
+
+// ======================================================================================
+// a2-a4, a7  encode
+// ======================================================================================
+
+// Split one group of 8 words (4 dwords, word 2m in the low half of dword m).
+//   sm_lo/sm_hi: sign+mantissa bytes of words 0..3 / 4..7
+//   codes:       nibble k = code of word k (0 for escapes)
+//   flags:       escape bit of word k at bit 8*(k>>1) + 4 + (k&1)
+__device__ __forceinline__ void split_group(const uint4 v, const uint8_t *lut, uint32_t &sm_lo,
+                                            uint32_t &sm_hi, uint32_t &codes, uint32_t &flags)
+{
+    // sign+mantissa: low byte of each word gives mantissa (bits 0..6), high byte gives the
+    // sign (bit 7); gather the 4 low and the 4 high bytes, then merge with one bit-select.
+    sm_lo = (perm(v.y, v.x, 0x07050301u) & 0x80808080u) | (perm(v.y, v.x, 0x06040200u) & 0x7F7F7F7Fu);
+    sm_hi = (perm(v.w, v.z, 0x07050301u) & 0x80808080u) | (perm(v.w, v.z, 0x06040200u) & 0x7F7F7F7Fu);
+
+    const uint32_t c0 = lut[(v.x >> 7) & 0xFFu], c1 = lut[(v.x >> 23) & 0xFFu];
+    const uint32_t c2 = lut[(v.y >> 7) & 0xFFu], c3 = lut[(v.y >> 23) & 0xFFu];
+    const uint32_t c4 = lut[(v.z >> 7) & 0xFFu], c5 = lut[(v.z >> 23) & 0xFFu];
+    const uint32_t c6 = lut[(v.w >> 7) & 0xFFu], c7 = lut[(v.w >> 23) & 0xFFu];
+    const uint32_t even = c0 | (c2 << 8) | (c4 << 16) | (c6 << 24);
+    const uint32_t odd = c1 | (c3 << 8) | (c5 << 16) | (c7 << 24);
+    codes = (even & 0x0F0F0F0Fu) | ((odd & 0x0F0F0F0Fu) << 4);
+    flags = (even & 0x10101010u) | ((odd & 0x10101010u) << 1);
+}
+
+__device__ __forceinline__ uint32_t flag_bit_to_word(uint32_t b) { return ((b >> 3) << 1) | (b & 1u); }
+
+// Mask keeping the codes / escape flags of the first nv (< 8) words of a group.
+__device__ __forceinline__ uint32_t codes_keep(uint32_t nv) { return nv >= 8 ? ~0u : (1u << (4 * nv)) - 1u; }
+__device__ __forceinline__ uint32_t flags_keep(uint32_t nv)
+{
+    return nv >= 8 ? ~0u : (1u << (8 * (nv >> 1) + 4 + (nv & 1))) - 1u;
+}
+
+__device__ __forceinline__ uint64_t status_load(const uint64_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void status_store(uint64_t *p, uint64_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Exclusive escape prefix of global tile t inside its segment, whose first tile is `first`.
+// Run by one full wave.  Each pass reads the status words of the 64 preceding tiles (one
+// per lane), waits until all of them are published by this launch, and adds the values
+// from the nearest tile back to (and including) the nearest one holding an inclusive
+// prefix.  Status value+flag+epoch sit in one 64-bit word, so relaxed atomics suffice.
+__device__ uint64_t lookback(const uint64_t *status, uint32_t t, uint32_t first, uint64_t tag,
+                             uint32_t lane, uint32_t *err)
+{
+    uint64_t excl = 0;
+    int64_t end = t;
+    uint32_t spins = 0;
+    for (;;) {
+        const int64_t idx = end - 1 - (int64_t)lane;
+        const bool in = idx >= (int64_t)first;
+        uint64_t st = 0, flag = 0;
+        for (;;) {
+            if (in) {
+                st = status_load(status + idx);
+                flag = ((st >> kEpochShift) == (tag >> kEpochShift)) ? (st & kFlagMask) : 0;
+            }
+            if (!ballot(in && flag == 0))
+                break;
+            // give up at the limit, or at once when another tile has already given up
+            const bool abandoned = (spins & 63u) == 63u &&
+                __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+            if (++spins > kSpinLimit || abandoned) {
+                // no progress: give up (the launch is reported as failed), drain the grid
+                if (lane == 0)
+                    atomicOr(err, kErrLookbackTimeout);
+                if (in && flag == 0) {
+                    flag = kFlagPrefix;
+                    st = 0;
+                }
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        const uint64_t pmask = ballot(in && flag == kFlagPrefix);
+        const uint32_t stop = pmask ? (uint32_t)__builtin_ctzll(pmask) : 63u;
+        const uint64_t val = (in && lane <= stop) ? (st & kValueMask) : 0;
+        excl += wave_total_u64(val, lane);
+        if (pmask || end - 64 <= (int64_t)first)
+            break;
+        end -= 64;
+    }
+    return excl;
+}
+
+__global__ __launch_bounds__(kThreads) void encode_kernel(const EncodeArgs a)
+{
+    __shared__ uint8_t s_lut[256];
+    __shared__ uint32_t s_ticket;
+    __shared__ uint32_t s_wave_total[kWaves];
+    __shared__ uint64_t s_excl;
+
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = lane_id();
+    const uint32_t wave = tid >> 6;
+
+    if (tid == 0)
+        s_ticket = (uint32_t)(atomicAdd(a.ticket, 1ull) - a.ticket_base);
+    if (tid < 64)
+        reinterpret_cast<uint32_t *>(s_lut)[tid] = reinterpret_cast<const uint32_t *>(a.lut)[tid];
+    __syncthreads();
+
+    // tile -> segment (wave-uniform values)
+    const uint32_t t = __builtin_amdgcn_readfirstlane(s_ticket);
+    if (t >= a.n_tiles) {
+        // the ticket counter was not where the host expected: touch nothing, report
+        if (tid == 0)
+            atomicOr(a.err, kErrBadTicket);
+        return;
+    }
+    uint32_t s = 0, first = 0, last = a.n_tiles - 1;
+    SegDesc sd = a.seg0;
+    if (a.n_seg > 1) {
+        s = find_segment(a.tile_start, a.n_seg, t);
+        first = a.tile_start[s];
+        last = a.tile_start[s + 1] - 1;
+        sd = a.segs[s];
+    }
+    const uint64_t n = sd.n;
+    const uint64_t base = (uint64_t)(t - first) << kTileShift;
+    const uint64_t cmask = (1ull << a.log2_chunk) - 1;
+
+    // ---- a2: dense split and pack -------------------------------------------------------
+    uint4 v[kGroupsPerLane];
+    uint32_t flags[kGroupsPerLane];
+    uint32_t counts[kGroupsPerLane];
+#pragma unroll
+    for (int j = 0; j < kGroupsPerLane; ++j) {
+        const uint64_t g0 = base + (uint64_t)(((wave * kGroupsPerLane + j) << 6) + lane) * kGroupWords;
+        if (g0 + kGroupWords <= n) {
+            v[j] = *reinterpret_cast<const uint4 *>(sd.data + g0);
+        } else {
+            uint16_t wds[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                wds[k] = (g0 + k < n) ? sd.data[g0 + k] : (uint16_t)0;
+            v[j] = make_uint4(wds[0] | ((uint32_t)wds[1] << 16), wds[2] | ((uint32_t)wds[3] << 16),
+                              wds[4] | ((uint32_t)wds[5] << 16), wds[6] | ((uint32_t)wds[7] << 16));
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kGroupsPerLane; ++j) {
+        const uint64_t g0 = base + (uint64_t)(((wave * kGroupsPerLane + j) << 6) + lane) * kGroupWords;
+        uint32_t sm_lo, sm_hi, codes, fl;
+        split_group(v[j], s_lut, sm_lo, sm_hi, codes, fl);
+        if (g0 + kGroupWords <= n) {
+            *reinterpret_cast<uint2 *>(sd.sm + g0) = make_uint2(sm_lo, sm_hi);
+            *reinterpret_cast<uint32_t *>(sd.codes + (g0 >> 1)) = codes;
+        } else {
+            const uint32_t nv = g0 < n ? (uint32_t)(n - g0) : 0u;
+            codes &= codes_keep(nv);
+            fl &= flags_keep(nv);
+            for (uint32_t k = 0; k < nv; ++k)
+                sd.sm[g0 + k] = (uint8_t)((k < 4 ? sm_lo : sm_hi) >> (8 * (k & 3)));
+            for (uint32_t k = 0; k < (nv + 1) / 2; ++k)
+                sd.codes[(g0 >> 1) + k] = (uint8_t)(codes >> (8 * k));
+        }
+        flags[j] = fl;
+        counts[j] = __popc(fl);
+    }
+
+    // ---- a3: escape ranks inside the tile -------------------------------------------------
+    // Word order inside a wave is (group j, lane, word k).  Pack the per-group counts two per
+    // dword (16-bit fields), prefix-sum them over the lanes, then offset each group by the
+    // wave totals of the groups before it.
+    uint32_t rank_in_wave[kGroupsPerLane];
+    uint32_t wave_sum = 0;
+#pragma unroll
+    for (int j = 0; j < kGroupsPerLane; j += 2) {
+        const uint32_t packed = counts[j] | (counts[j + 1] << 16);
+        const uint32_t incl = wave_inclusive_sum(packed, lane);
+        const uint32_t excl = incl - packed;
+        const uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
+        rank_in_wave[j] = wave_sum + (excl & 0xFFFFu);
+        wave_sum += tot & 0xFFFFu;
+        rank_in_wave[j + 1] = wave_sum + (excl >> 16);
+        wave_sum += tot >> 16;
+    }
+    if (lane == 0)
+        s_wave_total[wave] = wave_sum;
+    __syncthreads();
+    uint32_t wave_base = 0, tile_total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const uint32_t x = s_wave_total[w];
+        wave_base += (w < (int)wave) ? x : 0u;
+        tile_total += x;
+    }
+
+    // ---- a4: cross-tile escape offsets (decoupled look-back) -------------------------------
+    if (wave == 0) {
+        uint64_t excl = 0;
+        if (t == first) {
+            if (lane == 0)
+                status_store(a.status + t, a.epoch_tag | kFlagPrefix | tile_total);
+        } else {
+            if (lane == 0)
+                status_store(a.status + t, a.epoch_tag | kFlagAggregate | tile_total);
+            excl = lookback(a.status, t, first, a.epoch_tag, lane, a.err);
+            if (lane == 0)
+                status_store(a.status + t, a.epoch_tag | kFlagPrefix | ((excl + tile_total) & kValueMask));
+        }
+        if (lane == 0)
+            s_excl = excl;
+    }
+    __syncthreads();
+    const uint64_t tile_excl = s_excl;
+
+    // escape records and chunk offsets
+#pragma unroll
+    for (int j = 0; j < kGroupsPerLane; ++j) {
+        const uint64_t g0 = base + (uint64_t)(((wave * kGroupsPerLane + j) << 6) + lane) * kGroupWords;
+        const uint64_t before = tile_excl + wave_base + rank_in_wave[j];
+        if (g0 < n && (g0 & cmask) == 0)
+            sd.chunk_off[g0 >> a.log2_chunk] = before;
+        uint32_t z = flags[j];
+        if (z) {
+            // the group's 8 exponents, word k in byte k (a dword >> 7 holds the exponent of
+            // its low word in byte 0 and of its high word in byte 2)
+            const uint64_t ex8 = perm(v[j].y >> 7, v[j].x >> 7, 0x06040200u)
+                               | ((uint64_t)perm(v[j].w >> 7, v[j].z >> 7, 0x06040200u) << 32);
+            uint64_t r = before;
+            do {
+                const uint32_t k = flag_bit_to_word((uint32_t)__builtin_ctz(z));
+                if (r < sd.esc) {
+                    sd.esc_pos[r] = (uint16_t)((g0 + k) & cmask);
+                    sd.esc_exp[r] = (uint8_t)(ex8 >> (8 * k));
+                }
+                ++r;
+                z &= z - 1;
+            } while (z);
+        }
+    }
+    if (t == last && tid == 0) {
+        const uint64_t E = tile_excl + tile_total;
+        const uint64_t n_chunks = (n + cmask) >> a.log2_chunk;
+        sd.chunk_off[n_chunks] = E;
+        a.seg_escapes[s] = E;
+    }
+}
+
+hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream)
+{
+    encode_kernel<<<a.n_tiles, kThreads, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+// ======================================================================================
+// a5-a7  decode
+// ======================================================================================
+
+// Codebook lookup of 4 codes (one per byte, each 0..15): two byte-permutes over the
+// low and high halves of the 16-byte codebook, merged on bit 3 of each code.
+__device__ __forceinline__ uint32_t codebook_lookup(uint32_t x, const uint32_t cb[4])
+{
+    const uint32_t sel = x & 0x07070707u;
+    const uint32_t lo = perm(cb[1], cb[0], sel);
+    const uint32_t hi = perm(cb[3], cb[2], sel);
+    const uint32_t b3 = (x >> 3) & 0x01010101u;
+    const uint32_t m = (b3 << 8) - b3;   // 0xFF in every byte whose code has bit 3 set
+    return (hi & m) | (lo & ~m);
+}
+
+// Two BF16 words from sign+mantissa bytes s (words 2m, 2m+1 at bytes 2m', 2m'+1 of s, per
+// selector) and exponent bytes taken from even/odd.
+__device__ __forceinline__ uint32_t assemble(uint32_t s, uint32_t sm_sel, uint32_t even,
+                                             uint32_t odd, uint32_t ex_sel)
+{
+    const uint32_t p = perm(s, s, sm_sel);          // [s1 s1 s0 s0]
+    const uint32_t q = perm(odd, even, ex_sel);     // [0 e1 0 e0]
+    return (p & 0x807F807Fu) | (q << 7);
+}
+
+__global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
+{
+    __shared__ uint32_t s_exp[kTileWords / 4];              // exponent bytes of the tile
+    __shared__ uint64_t s_off[kTileWords / 16 + 1];         // chunk offsets of the tile
+
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = lane_id();
+    const uint32_t wave = tid >> 6;
+    const uint32_t t = blockIdx.x;
+
+    uint32_t first = 0;
+    SegDesc sd = a.seg0;
+    if (a.n_seg > 1) {
+        const uint32_t s = find_segment(a.tile_start, a.n_seg, t);
+        first = a.tile_start[s];
+        sd = a.segs[s];
+    }
+    const uint64_t n = sd.n;
+    const uint64_t base = (uint64_t)(t - first) << kTileShift;
+    if (base >= n)
+        return;                                              // empty segment
+    const uint64_t valid = n - base < (uint64_t)kTileWords ? n - base : (uint64_t)kTileWords;
+    const uint32_t log2c = a.log2_chunk;
+    const uint64_t C = 1ull << log2c;
+    const uint64_t E = sd.esc;
+    const uint32_t cb[4] = {a.cb[0], a.cb[1], a.cb[2], a.cb[3]};
+
+    // ---- loads ---------------------------------------------------------------------------
+    uint2 smv[kGroupsPerLane];
+    uint32_t cw[kGroupsPerLane];
+#pragma unroll
+    for (int j = 0; j < kGroupsPerLane; ++j) {
+        const uint64_t g0 = base + (uint64_t)(((wave * kGroupsPerLane + j) << 6) + lane) * kGroupWords;
+        if (g0 + kGroupWords <= n) {
+            smv[j] = *reinterpret_cast<const uint2 *>(sd.sm + g0);
+            cw[j] = *reinterpret_cast<const uint32_t *>(sd.codes + (g0 >> 1));
+        } else {
+            uint32_t b[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            uint32_t c = 0;
+            for (uint32_t k = 0; k < 8; ++k)
+                if (g0 + k < n)
+                    b[k] = sd.sm[g0 + k];
+            for (uint32_t k = 0; k < 4; ++k)
+                if (g0 + 2 * k < n)
+                    c |= (uint32_t)sd.codes[(g0 >> 1) + k] << (8 * k);
+            smv[j] = make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
+                                b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
+            cw[j] = c;
+        }
+    }
+
+    // ---- escape range of the tile --------------------------------------------------------
+    const bool sub_chunk = log2c > (uint32_t)kTileShift;     // the tile lies inside one chunk
+    uint64_t c0, nc;
+    if (!sub_chunk) {
+        c0 = base >> log2c;
+        nc = (valid + C - 1) >> log2c;                       // chunks of this tile
+    } else {
+        c0 = base >> log2c;
+        nc = 1;
+    }
+    for (uint32_t i = tid; i <= nc; i += kThreads)
+        s_off[i] = sd.chunk_off[c0 + i];
+    __syncthreads();
+    const uint64_t j0 = s_off[0], j1 = s_off[nc];
+    bool patch = j1 > j0;
+    if (j0 > j1 || j1 > E) {
+        patch = false;
+        if (tid == 0 && a.err)
+            atomicOr(a.err, kErrBadOffsets);
+    }
+
+    // ---- a5: dense path ------------------------------------------------------------------
+    uint32_t ex_even[kGroupsPerLane], ex_odd[kGroupsPerLane];
+#pragma unroll
+    for (int j = 0; j < kGroupsPerLane; ++j) {
+        ex_even[j] = codebook_lookup(cw[j] & 0x0F0F0F0Fu, cb);
+        ex_odd[j] = codebook_lookup((cw[j] >> 4) & 0x0F0F0F0Fu, cb);
+    }
+
+    // ---- a6: sparse escape correction (exponent bytes in LDS) ----------------------------
+    if (patch) {
+#pragma unroll
+        for (int j = 0; j < kGroupsPerLane; ++j) {
+            const uint32_t q = ((wave * kGroupsPerLane + j) << 6) + lane;
+            s_exp[2 * q] = ex_even[j];
+            s_exp[2 * q + 1] = ex_odd[j];
+        }
+        __syncthreads();
+        uint8_t *bytes = reinterpret_cast<uint8_t *>(s_exp);
+        if (!sub_chunk) {
+            for (uint64_t ci = wave; ci < nc; ci += kWaves) {
+                const uint64_t ea = s_off[ci], eb = s_off[ci + 1];
+                if (ea > eb || eb > E) {
+                    if (lane == 0 && a.err)
+                        atomicOr(a.err, kErrBadOffsets);
+                    continue;
+                }
+                const uint64_t cstart = (c0 + ci) << log2c;
+                const uint64_t clen = n - cstart < C ? n - cstart : C;
+                for (uint64_t jj = ea + lane; jj < eb; jj += 64) {
+                    const uint32_t pos = sd.esc_pos[jj];
+                    if (pos >= clen) {
+                        if (a.err)
+                            atomicOr(a.err, kErrBadPosition);
+                        continue;
+                    }
+                    const uint32_t p = (uint32_t)(cstart + pos - base);
+                    bytes[(p >> 3) * 8 + (p & 1u) * 4 + ((p >> 1) & 3u)] = sd.esc_exp[jj];
+                }
+            }
+        } else {
+            const uint64_t lo = base - (c0 << log2c);
+            const uint64_t clen = n - (c0 << log2c) < C ? n - (c0 << log2c) : C;
+            for (uint64_t jj = j0 + tid; jj < j1; jj += kThreads) {
+                const uint32_t pos = sd.esc_pos[jj];
+                if (pos >= clen) {
+                    if (a.err)
+                        atomicOr(a.err, kErrBadPosition);
+                    continue;
+                }
+                if (pos >= lo && pos < lo + valid) {
+                    const uint32_t p = (uint32_t)(pos - lo);
+                    bytes[(p >> 3) * 8 + (p & 1u) * 4 + ((p >> 1) & 3u)] = sd.esc_exp[jj];
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kGroupsPerLane; ++j) {
+            const uint32_t q = ((wave * kGroupsPerLane + j) << 6) + lane;
+            ex_even[j] = s_exp[2 * q];
+            ex_odd[j] = s_exp[2 * q + 1];
+        }
+    }
+
+    // ---- assemble and store ------------------------------------------------------------------
+#pragma unroll
+    for (int j = 0; j < kGroupsPerLane; ++j) {
+        const uint64_t g0 = base + (uint64_t)(((wave * kGroupsPerLane + j) << 6) + lane) * kGroupWords;
+        uint4 o;
+        o.x = assemble(smv[j].x, 0x01010000u, ex_even[j], ex_odd[j], 0x0C040C00u);
+        o.y = assemble(smv[j].x, 0x03030202u, ex_even[j], ex_odd[j], 0x0C050C01u);
+        o.z = assemble(smv[j].y, 0x01010000u, ex_even[j], ex_odd[j], 0x0C060C02u);
+        o.w = assemble(smv[j].y, 0x03030202u, ex_even[j], ex_odd[j], 0x0C070C03u);
+        if (g0 + kGroupWords <= n) {
+            *reinterpret_cast<uint4 *>(sd.data + g0) = o;
+        } else {
+            const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+            for (uint32_t k = 0; g0 + k < n; ++k)
+                sd.data[g0 + k] = (uint16_t)(w[k >> 1] >> (16 * (k & 1)));
+        }
+    }
+}
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream)
+{
+    decode_kernel<<<a.n_tiles, kThreads, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace sz

@@ -1,0 +1,108 @@
+"""CPU tests of the C ABI library: it loads, exports every symbol include/splitzip.h
+declares, and its host-side logic (sizes, header parsing, argument validation) agrees
+with the oracle.  No compute call is made (there is no GPU here)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import lossless_bf16_kv_amd as sz
+import oracle
+import oracle_pins as pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions() -> list:
+    text = open(os.path.join(ROOT, "include", "splitzip.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(splitzip_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"splitzip_calibrate", "splitzip_encode", "splitzip_decode", "splitzip_free"} <= set(names)
+    L = sz.lib()
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_segment_struct_matches_header():
+    # ten 8-byte fields, no padding
+    assert ctypes.sizeof(sz.splitzip_segment) == 80
+
+
+@pytest.mark.parametrize("n,C,E", [(0, 16, 0), (7, 16, 3), (20, 16, 11), (1 << 32, 1024, 12345),
+                                   (65536, 1024, 61440), (1000003, 4096, 77)])
+def test_sizes_match_oracle(n, C, E):
+    o = oracle.get()
+    assert sz.splitzip_compressed_bytes(n, C, E) == o.compressed_bytes(n, C, E)
+    assert sz.splitzip_chunk_count(n, C) == -(-n // C)
+
+
+def test_bad_chunk_sizes_have_no_size():
+    for C in (0, 8, 24, 131072):
+        assert sz.splitzip_compressed_bytes(100, C, 0) == 0
+        assert sz.splitzip_chunk_count(100, C) == 0
+
+
+def test_read_header_of_oracle_streams():
+    o = oracle.get()
+    g, cal, x = pins.worked_example()
+    cb, _, _ = o.calibrate(cal)
+    for n in (0, 7, 20):
+        s = o.serialize(o.encode(x[:n], cb, 16))
+        h = sz.splitzip_read_header(s)
+        assert h == {"n": n, "chunk_size": 16, "n_escapes": o.stream_info(s)["n_escapes"],
+                     "codebook": bytes(cb)}
+
+
+def test_read_header_rejects_malformed():
+    o = oracle.get()
+    _, cal, x = pins.worked_example()
+    cb, _, _ = o.calibrate(cal)
+    s = o.serialize(o.encode(x, cb, 16))
+    for i, val in ((0, 0x54), (4, 2), (6, 65), (8, 24), (12, 1), (24, 9), (60, 1)):
+        b = bytearray(s)
+        b[i] = val
+        with pytest.raises(sz.SplitZipError) as ei:
+            sz.splitzip_read_header(bytes(b))
+        assert ei.value.status == sz.E_FORMAT
+    with pytest.raises(sz.SplitZipError):
+        sz.splitzip_read_header(s[:-1])
+    with pytest.raises(sz.SplitZipError):
+        sz.splitzip_read_header(s[:10])
+
+
+def test_argument_validation_before_any_device_call():
+    L = sz.lib()
+    h = ctypes.c_void_p()
+    cov = ctypes.c_double()
+    for C in (0, 8, 1000, 1 << 17):
+        assert L.splitzip_calibrate(None, 0, C, None, ctypes.byref(h), ctypes.byref(cov), None) == sz.E_INVALID
+    # misaligned calibration pointer
+    assert L.splitzip_calibrate(ctypes.c_void_p(0x1002), 8, 1024, None, ctypes.byref(h),
+                                ctypes.byref(cov), None) == sz.E_INVALID
+    assert b"aligned" in L.splitzip_last_error()
+    # no codec
+    segs = (sz.splitzip_segment * 1)()
+    assert L.splitzip_encode(None, 1, segs, None) == sz.E_INVALID
+    assert L.splitzip_decode(None, 1, segs, None, None) == sz.E_INVALID
+    # duplicate codebook entries
+    cb = (ctypes.c_uint8 * 16)(*([5] * 16))
+    assert L.splitzip_codec_from_codebook(cb, 1024, ctypes.byref(h)) == sz.E_INVALID
+    L.splitzip_free(None)   # no-op
+    assert sz.lib().splitzip_status_string(6) == b"escape capacity exceeded"
+
+
+def test_no_cpu_fallback():
+    # the product path refuses to run without a GPU instead of computing on the CPU
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("GPU present")
+    with pytest.raises(sz.SplitZipError):
+        sz.Codec("cuda", 1024)

@@ -1,0 +1,327 @@
+"""GPU parity: the HIP codec (through the C ABI) against the CPU oracle.
+
+Encoded streams must equal the oracle's byte for byte, decode must return the input
+bit for bit, and calibration must give the oracle's histogram, codebook and coverage.
+Small and mid-size inputs are compared element by element; the full-size workloads
+(8.6 GB long-prefill KV, 512-segment ragged batch) are compared on sampled chunks
+plus properties that hold at any size."""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import lossless_bf16_kv_amd as sz
+import oracle
+import oracle_pins as pins
+import workloads
+from conftest import hex_bytes, ints
+
+pytestmark = pytest.mark.gpu
+
+O = oracle.get()
+DEV = torch.device("cuda:0")
+
+
+def dev(words: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(words, np.uint16).view(np.int16)).to(DEV)
+
+
+def host(t: torch.Tensor, dtype) -> np.ndarray:
+    return t.cpu().numpy().view(dtype)
+
+
+def codec_for(cal: np.ndarray, C: int) -> sz.Codec:
+    c = sz.Codec(DEV, C)
+    c.calibrate(dev(cal))
+    return c
+
+
+def assert_same_stream(codec: sz.Codec, enc: sz.Encoded, x: np.ndarray):
+    cb = np.frombuffer(codec.codebook, np.uint8)
+    ref = O.encode(x, cb, codec.chunk_size)
+    assert enc.n_escapes == ref["n_escapes"]
+    assert enc.compressed_bytes == ref["compressed_bytes"]
+    assert np.array_equal(host(enc.sm, np.uint8), ref["sm"])
+    assert np.array_equal(host(enc.codes, np.uint8), ref["codes"])
+    assert np.array_equal(host(enc.chunk_off, np.uint64), ref["chunk_off"])
+    assert np.array_equal(host(enc.esc_pos, np.uint16), ref["esc_pos"])
+    assert np.array_equal(host(enc.esc_exp, np.uint8), ref["esc_exp"])
+    assert enc.to_bytes(codec) == O.serialize(ref)
+    return ref
+
+
+# ---- worked example and exhaustive words ----------------------------------------------
+
+def test_worked_example():
+    g, cal, x = pins.worked_example()
+    codec = sz.Codec(DEV, int(g["chunk_size"]))
+    cov = codec.calibrate(dev(cal))
+    assert codec.codebook == hex_bytes(g["codebook"])
+    assert cov == float(g["calibration_coverage"])
+    enc = codec.encode(dev(x))
+    assert bytes(host(enc.sm, np.uint8)) == hex_bytes(g["sm"])
+    assert bytes(host(enc.codes, np.uint8)) == hex_bytes(g["codes"])
+    assert host(enc.chunk_off, np.uint64).tolist() == ints(g["chunk_off"])
+    assert host(enc.esc_pos, np.uint16).tolist() == ints(g["esc_pos"])
+    assert host(enc.esc_exp, np.uint8).tolist() == ints(g["esc_exp"])
+    assert enc.compressed_bytes == int(g["compressed_bytes"])
+    assert enc.to_bytes(codec)[:64] == hex_bytes(g["header"])
+    assert np.array_equal(host(codec.decode(enc), np.uint16), x)
+    for n in (0, 7):
+        e = codec.encode(dev(x[:n]))
+        assert_same_stream(codec, e, x[:n])
+        assert np.array_equal(host(codec.decode(e), np.uint16), x[:n])
+
+
+@pytest.mark.parametrize("C", [16, 1024, 4096, 65536])
+def test_exhaustive_words(C):
+    x = np.arange(1 << 16, dtype=np.uint16)
+    codec = codec_for(x, C)
+    assert codec.codebook == bytes(range(16))
+    assert codec.coverage == 1 / 16
+    enc = codec.encode(dev(x))
+    assert_same_stream(codec, enc, x)
+    assert np.array_equal(host(codec.decode(enc), np.uint16), x)
+
+
+# ---- calibration --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [1, 5, 8, 17, 4099, 1000003])
+def test_calibration_matches_oracle(n):
+    x = workloads.mixed_words(n, seed=n, wide_fraction=0.2)
+    codec = codec_for(x, 1024)
+    cb, cov, h = O.calibrate(x)
+    assert codec.histogram == h.tolist()
+    assert codec.codebook == bytes(cb)
+    assert codec.coverage == cov
+
+
+def test_calibration_empty_and_few_exponents():
+    codec = sz.Codec(DEV, 64)
+    assert codec.calibrate(torch.empty(0, dtype=torch.int16, device=DEV)) == 0.0
+    assert codec.codebook == bytes(range(16))
+    x = np.full(100, 0x3F80, np.uint16)
+    codec.calibrate(dev(x))
+    assert codec.codebook == bytes(O.calibrate(x)[0])
+
+
+# ---- fuzz: sizes spanning several tiles with ragged tails, every chunk-size regime ---------
+
+FUZZ = [(n, C, gen) for n, C, gen in [
+    (1, 16, "random"), (9, 16, "mixed"), (8191, 1024, "mixed"), (8192, 1024, "normal"),
+    (8193, 16, "random"), (3 * 8192 + 13, 64, "mixed"), (100003, 1024, "random"),
+    (100003, 4096, "mixed"), (65536 * 3 + 5, 16384, "mixed"), (65536 * 3 + 5, 65536, "random"),
+    ((1 << 20) + 77, 1024, "mixed"), ((1 << 20) + 77, 32, "random"),
+]]
+
+
+@pytest.mark.parametrize("n,C,gen", FUZZ)
+def test_fuzz_stream_parity(n, C, gen):
+    make = {"random": workloads.random_words, "mixed": workloads.mixed_words,
+            "normal": workloads.normal_words}[gen]
+    x = make(n, 17 * n + C)
+    codec = codec_for(workloads.normal_words(50000, 3), C)
+    enc = codec.encode(dev(x))
+    ref = assert_same_stream(codec, enc, x)
+    assert np.array_equal(host(codec.decode(enc), np.uint16), x)
+    # the GPU decodes the oracle's serialized stream too
+    y = codec.decode_bytes(O.serialize(ref))
+    assert np.array_equal(host(y, np.uint16), x)
+
+
+def test_batch_with_empty_and_tiny_segments():
+    sizes = [0, 1, 7, 8192, 8193, 0, 100, 3 * 8192 + 5]
+    xs = [workloads.mixed_words(n, 100 + i, wide_fraction=0.3) for i, n in enumerate(sizes)]
+    codec = codec_for(workloads.normal_words(20000, 4), 16)
+    encs = codec.encode_batch([dev(x) for x in xs])
+    for x, e in zip(xs, encs):
+        assert_same_stream(codec, e, x)
+    ys = codec.decode_batch(encs)
+    for x, y in zip(xs, ys):
+        assert np.array_equal(host(y, np.uint16), x)
+
+
+def test_capacity_retry_gives_identical_stream():
+    x = workloads.random_words(50000, 9)           # ~94 % escapes
+    codec = codec_for(workloads.normal_words(20000, 5), 1024)
+    enc = codec.empty_encoded(x.size, escape_capacity=10)
+    st = codec.encode_into([dev(x)], [enc])
+    assert st == sz.E_CAPACITY
+    ref = O.encode(x, np.frombuffer(codec.codebook, np.uint8), 1024)
+    assert enc.n_escapes == ref["n_escapes"]
+    enc2 = codec.encode(dev(x))
+    assert_same_stream(codec, enc2, x)
+
+
+def test_deterministic_and_stream_independent():
+    x = workloads.mixed_words(5 * 8192 + 3, 11, wide_fraction=0.1)
+    codec = codec_for(workloads.normal_words(20000, 6), 1024)
+    xd = dev(x)
+    a = codec.encode(xd).to_bytes(codec)
+    b = codec.encode(xd).to_bytes(codec)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(s1):
+        c = codec.encode(xd)
+    with torch.cuda.stream(s2):
+        d = codec.encode(xd)
+    torch.cuda.synchronize()
+    assert a == b == c.to_bytes(codec) == d.to_bytes(codec)
+
+
+def test_decode_flags_corrupt_metadata_without_faulting():
+    x = workloads.mixed_words(4 * 8192, 12, wide_fraction=0.2)
+    codec = codec_for(workloads.normal_words(20000, 7), 1024)
+    enc = codec.encode(dev(x))
+    assert enc.n_escapes > 100
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    bad = dataclass_copy(enc)
+    bad.chunk_off[3] = enc.n_escapes + 1000            # offset beyond E
+    bad.esc_pos_buf[5] = 4000                          # position beyond its chunk
+    y = torch.empty_like(codec.decode(enc))
+    codec.decode_into([bad], [y], d_error=err.data_ptr())
+    torch.cuda.synchronize()
+    assert int(err.item()) != 0
+    # an intact stream leaves the flag at zero
+    err.zero_()
+    codec.decode_into([enc], [y], d_error=err.data_ptr())
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0 and np.array_equal(host(y, np.uint16), x)
+
+
+def dataclass_copy(e: sz.Encoded) -> sz.Encoded:
+    import dataclasses
+    return dataclasses.replace(e, sm=e.sm.clone(), codes=e.codes.clone(),
+                               chunk_off=e.chunk_off.clone(), esc_pos_buf=e.esc_pos_buf.clone(),
+                               esc_exp_buf=e.esc_exp_buf.clone())
+
+
+def test_codebook_mismatch_rejected():
+    x = workloads.normal_words(1000, 1)
+    a = codec_for(workloads.normal_words(5000, 2), 1024)
+    b = sz.Codec.from_codebook(bytes(range(100, 116)), 1024, DEV)
+    enc = a.encode(dev(x))
+    with pytest.raises(sz.SplitZipError) as ei:
+        b.decode(enc)
+    assert ei.value.status == sz.E_CODEBOOK
+    with pytest.raises(sz.SplitZipError) as ei:
+        b.decode_bytes(enc.to_bytes(a))
+    assert ei.value.status == sz.E_CODEBOOK
+    # a codec rebuilt from the stream header decodes it
+    c = sz.Codec.from_codebook(sz.splitzip_read_header(enc.to_bytes(a))["codebook"], 1024, DEV)
+    assert np.array_equal(host(c.decode_bytes(enc.to_bytes(a)), np.uint16), x)
+
+
+# ---- the five workloads -------------------------------------------------------------------
+
+def test_config1_single_tensor():
+    wl = workloads.config1()
+    codec = codec_for(wl.calibration, wl.chunk_size)
+    cb, cov, _ = O.calibrate(wl.calibration)
+    assert codec.codebook == bytes(cb) and codec.coverage == cov
+    x = wl.segments[0]
+    enc = codec.encode(dev(x).view(1024, 4096))
+    assert_same_stream(codec, enc, x)
+    y = codec.decode(enc)
+    assert y.shape == (1024, 4096)
+    assert np.array_equal(host(y, np.uint16).reshape(-1), x)
+
+
+def test_config2_kv_layer_two_segments():
+    wl = workloads.config2()
+    codec = codec_for(wl.calibration, wl.chunk_size)
+    assert codec.codebook == bytes(O.calibrate(wl.calibration)[0])
+    encs = codec.encode_batch([dev(s) for s in wl.segments])
+    for x, e in zip(wl.segments, encs):
+        assert_same_stream(codec, e, x)
+    for x, y in zip(wl.segments, codec.decode_batch(encs)):
+        assert np.array_equal(host(y, np.uint16), x)
+
+
+@pytest.mark.parametrize("C", [1024, 4096])
+def test_config4_escape_stress(C):
+    wl = workloads.config4(chunk_size=C)
+    codec = codec_for(wl.calibration, C)
+    x = wl.segments[0]
+    enc = codec.encode(dev(x))
+    ref = assert_same_stream(codec, enc, x)
+    assert 0.2 < ref["n_escapes"] / x.size < 0.4
+    assert np.array_equal(host(codec.decode(enc), np.uint16), x)
+
+
+def check_sampled_chunks(codec, enc, x, chunks):
+    """Oracle-encode each sampled chunk on its own and compare with the GPU sections."""
+    C = codec.chunk_size
+    cb = np.frombuffer(codec.codebook, np.uint8)
+    off = host(enc.chunk_off, np.uint64)
+    for c in chunks:
+        lo, hi = c * C, min((c + 1) * C, x.size)
+        ref = O.encode(x[lo:hi], cb, C)
+        a, b = int(off[c]), int(off[c + 1])
+        assert b - a == ref["n_escapes"], f"chunk {c}"
+        assert np.array_equal(host(enc.sm[lo:hi], np.uint8), ref["sm"])
+        assert np.array_equal(host(enc.codes[lo // 2:(hi + 1) // 2], np.uint8), ref["codes"])
+        assert np.array_equal(host(enc.esc_pos_buf[a:b], np.uint16), ref["esc_pos"])
+        assert np.array_equal(host(enc.esc_exp_buf[a:b], np.uint8), ref["esc_exp"])
+
+
+def check_properties(codec, enc, x, hist_x):
+    """Size-independent checks: E from the oracle's exact histogram, offsets, sizes."""
+    C = codec.chunk_size
+    cb = np.frombuffer(codec.codebook, np.uint8)
+    E = int(x.size - sum(int(hist_x[e]) for e in cb))
+    assert enc.n_escapes == E
+    off = enc.chunk_off
+    assert int(off[0]) == 0 and int(off[-1]) == E
+    assert bool((off[1:] >= off[:-1]).all())
+    assert bool((off[1:] - off[:-1] <= C).all())
+    assert enc.compressed_bytes == O.compressed_bytes(x.size, C, E)
+
+
+@pytest.fixture(scope="module")
+def config3_data():
+    wl = workloads.config3()
+    return wl
+
+
+@pytest.mark.parametrize("C", [1024, 4096])
+def test_config3_long_prefill_full_size(config3_data, C):
+    wl = config3_data
+    x = wl.segments[0]
+    assert x.size == 1 << 32
+    xd = dev(x)
+    codec = codec_for(wl.calibration, C)
+    cb, cov, _ = O.calibrate(wl.calibration)
+    assert codec.codebook == bytes(cb) and codec.coverage == cov
+    enc = codec.encode(xd)
+    rng = np.random.default_rng(C)
+    n_chunks = x.size // C
+    sample = sorted(set(rng.integers(0, n_chunks, 48).tolist()) | {0, 1, n_chunks - 1})
+    check_sampled_chunks(codec, enc, x, sample)
+    check_properties(codec, enc, x, O.histogram(x))
+    y = codec.decode(enc)
+    assert torch.equal(y, xd)
+    del y
+
+
+def test_config3_full_size_histogram(config3_data):
+    x = config3_data.segments[0]
+    c = codec_for(x, 1024)             # calibrating on the data itself gives its histogram
+    assert c.histogram == O.histogram(x).tolist()
+
+
+def test_config5_ragged_batch():
+    wl = workloads.config5()
+    codec = codec_for(wl.calibration, wl.chunk_size)
+    assert len(wl.segments) == 512
+    xds = [dev(s) for s in wl.segments]
+    encs = codec.encode_batch(xds)                 # one launch, 512 segments
+    for i in range(0, 512, 37):                    # full streams of a spread of segments
+        assert_same_stream(codec, encs[i], wl.segments[i])
+    for x, e in zip(wl.segments, encs):
+        check_properties(codec, e, x, O.histogram(x))
+    ys = codec.decode_batch(encs)                  # one launch
+    for xd, y in zip(xds, ys):
+        assert torch.equal(y, xd)
