@@ -123,13 +123,14 @@ int splitzip_codec_info(const splitzip_codec *codec, uint8_t codebook[16], uint3
 int splitzip_encode(splitzip_codec *codec, uint32_t n_seg, splitzip_segment *segs, void *stream);
 
 /*
- * Non-blocking encode: the same launch as splitzip_encode without the wait.  The
- * kernel writes into d_result (device, caller-owned, 1 + n_seg uint64 words):
- * d_result[0] = error bits (0 = success), d_result[1 + s] = E of segment s.
+ * Non-blocking encode: the same launches as splitzip_encode without the wait.  The
+ * kernels write into d_result (device, caller-owned, 1 + n_seg uint64 words):
+ * d_result[1 + s] = E of segment s, and error bits are OR-ed into d_result[0] (the
+ * caller zeroes it; bit 3 alone means some segment exceeded its escape capacity).
  * segs[].n_escapes / compressed_bytes are not filled.  Once the stream has passed
- * this work, a segment with E > esc_capacity holds only its first esc_capacity escapes
- * and must be re-encoded with larger escape arrays.  The input and output buffers must
- * stay valid until then.
+ * this work, a segment with E > esc_capacity holds only part of its escapes and must be
+ * re-encoded with larger escape arrays.  The input and output buffers must stay valid
+ * until then.
  */
 int splitzip_encode_async(splitzip_codec *codec, uint32_t n_seg, const splitzip_segment *segs,
                           void *stream, uint64_t *d_result);

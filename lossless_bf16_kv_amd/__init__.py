@@ -360,14 +360,15 @@ class Codec:
     def finish_async(self, encs, result) -> int:
         """Read the result words of an encode_into_async (synchronizes with the host)."""
         r = result.cpu().tolist()
-        if r[0] != 0:
-            raise SplitZipError(E_DEVICE, f"encode kernel reported error bits {r[0]:#x}")
         st = OK
         for i, e in enumerate(encs):
             e.n_escapes = int(r[1 + i])
             e.compressed_bytes = splitzip_compressed_bytes(e.n, self.chunk_size, e.n_escapes)
             if e.n_escapes > e.esc_pos_buf.numel():
                 st = E_CAPACITY
+        overflow_area = 8
+        if r[0] & ~overflow_area or (r[0] and st != E_CAPACITY):
+            raise SplitZipError(E_DEVICE, f"encode kernel reported error bits {r[0]:#x}")
         return st
 
     def encode(self, x, escape_capacity: int | None = None) -> Encoded:

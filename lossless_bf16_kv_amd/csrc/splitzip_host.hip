@@ -6,8 +6,9 @@
 // encode/decode calls whose outputs belong to that codec state.  This file owns:
 //   - argument validation and status/error reporting (never throws across the ABI);
 //   - codebook selection from the GPU histogram (count descending, exponent ascending);
-//   - per-stream workspaces: look-back status words, tile ticket counter, per-segment
-//     escape counts, pinned descriptor staging for ragged batches;
+//   - per-stream workspaces: encode scratch (per-tile escape slots and counts, overflow
+//     area, segmented sums), per-segment escape counts, pinned descriptor staging for
+//     ragged batches;
 //   - kernel launches and the one small readback that encode needs.
 #include "splitzip_internal.h"
 
@@ -108,22 +109,20 @@ struct Workspace {
     std::mutex mu;
     hipStream_t stream = nullptr;
     // device
-    uint64_t *status = nullptr;       // look-back words
-    uint64_t status_cap = 0;
-    unsigned long long *ticket = nullptr;
+    uint8_t *scratch = nullptr;       // encode scratch (see EncodeScratch)
+    uint64_t scratch_cap = 0;         // bytes
+    unsigned long long *ovf_next = nullptr;
     uint8_t *result = nullptr;        // [err u32, pad u32, seg_escapes u64 * result_cap]
     uint32_t result_cap = 0;
     // host
     uint8_t *h_result = nullptr;      // pinned mirror of `result`
-    uint64_t ticket_base = 0;
-    uint32_t epoch = 0;
     Staging staging[kStagingSlots];
     int next_slot = 0;
 
     ~Workspace()
     {
-        (void)hipFree(status);
-        (void)hipFree(ticket);
+        (void)hipFree(scratch);
+        (void)hipFree(ovf_next);
         (void)hipFree(result);
         (void)hipHostFree(h_result);
         for (Staging &s : staging) {
@@ -209,25 +208,41 @@ int get_workspace(splitzip_codec *c, hipStream_t stream, Workspace **out)
     if (!w)
         return fail(SPLITZIP_E_NOMEM, "host allocation of a workspace failed");
     w->stream = stream;
-    SZ_HIP(hipMalloc(&w->ticket, sizeof(unsigned long long)), "hipMalloc(ticket)");
-    SZ_HIP(hipMemsetAsync(w->ticket, 0, sizeof(unsigned long long), stream), "hipMemsetAsync(ticket)");
     *out = w.get();
     c->ws.emplace(stream, std::move(w));
     return SPLITZIP_OK;
 }
 
-int ensure_status(Workspace *w, uint64_t n_tiles)
+// Byte offsets of the encode scratch arrays for one launch.
+struct EncodeScratch {
+    uint64_t tile_count, tile_ovf, slots, block_sum, ovf, total;
+    EncodeScratch(uint64_t n_tiles, uint64_t ovf_cap)
+    {
+        auto up = [](uint64_t x) { return (x + 255) & ~uint64_t(255); };
+        tile_count = 0;
+        tile_ovf = up(tile_count + 4 * n_tiles);
+        slots = up(tile_ovf + 8 * n_tiles);
+        block_sum = up(slots + 4 * (uint64_t)sz::kSlotEscapes * n_tiles);
+        ovf = up(block_sum + 8 * ((n_tiles + sz::kSumTiles - 1) / sz::kSumTiles));
+        total = up(ovf + 4 * ovf_cap);
+    }
+};
+
+int ensure_scratch(Workspace *w, uint64_t bytes)
 {
-    if (w->status_cap >= n_tiles)
+    if (!w->ovf_next) {
+        SZ_HIP(hipMalloc(&w->ovf_next, sizeof(unsigned long long)), "hipMalloc(overflow counter)");
+        SZ_HIP(hipMemsetAsync(w->ovf_next, 0, sizeof(unsigned long long), w->stream), "hipMemsetAsync(counter)");
+    }
+    if (w->scratch_cap >= bytes)
         return SPLITZIP_OK;
-    uint64_t cap = std::max<uint64_t>(n_tiles, 2 * w->status_cap);
+    const uint64_t cap = std::max<uint64_t>(bytes, w->scratch_cap + w->scratch_cap / 2);
     SZ_HIP(hipStreamSynchronize(w->stream), "hipStreamSynchronize");
-    (void)hipFree(w->status);
-    w->status = nullptr;
-    w->status_cap = 0;
-    SZ_HIP(hipMalloc(&w->status, cap * sizeof(uint64_t)), "hipMalloc(look-back status)");
-    SZ_HIP(hipMemsetAsync(w->status, 0, cap * sizeof(uint64_t), w->stream), "hipMemsetAsync(status)");
-    w->status_cap = cap;
+    (void)hipFree(w->scratch);
+    w->scratch = nullptr;
+    w->scratch_cap = 0;
+    SZ_HIP(hipMalloc(&w->scratch, cap), "hipMalloc(encode scratch)");
+    w->scratch_cap = cap;
     return SPLITZIP_OK;
 }
 
@@ -293,8 +308,9 @@ int stage_descriptors(Workspace *w, const std::vector<sz::SegDesc> &segs,
 }
 
 // Shared validation of segment arrays; builds descriptors and tile starts.
-int prepare_segments(const splitzip_codec *c, uint32_t n_seg, const splitzip_segment *segs,
-                     bool encode, std::vector<sz::SegDesc> &desc, std::vector<uint32_t> &tiles)
+int prepare_segments_tiled(const splitzip_codec *c, uint32_t n_seg, const splitzip_segment *segs,
+                           bool encode, uint64_t tile_words, std::vector<sz::SegDesc> &desc,
+                           std::vector<uint32_t> &tiles)
 {
     if (n_seg == 0)
         return fail(SPLITZIP_E_INVALID, "n_seg is 0");
@@ -324,13 +340,20 @@ int prepare_segments(const splitzip_codec *c, uint32_t n_seg, const splitzip_seg
                         (unsigned long long)g.n_escapes, (unsigned long long)g.n);
         desc[i] = sz::SegDesc{g.data, g.sm, g.codes, g.chunk_off, g.esc_pos, g.esc_exp, g.n, esc};
         tiles[i] = (uint32_t)total;
-        total += std::max<uint64_t>(1, ceil_div(g.n, sz::kTileWords));
+        total += std::max<uint64_t>(1, ceil_div(g.n, tile_words));
         if (total > 0xFFFFFFF0ull)
             return fail(SPLITZIP_E_INVALID, "too many tiles in one call");
     }
     tiles[n_seg] = (uint32_t)total;
     (void)c;
     return SPLITZIP_OK;
+}
+
+int prepare_segments(const splitzip_codec *c, uint32_t n_seg, const splitzip_segment *segs,
+                     bool encode, std::vector<sz::SegDesc> &desc, std::vector<uint32_t> &tiles)
+{
+    const uint64_t tile_words = encode ? sz::kEncTileWords : sz::kDecTileWords;
+    return prepare_segments_tiled(c, n_seg, segs, encode, tile_words, desc, tiles);
 }
 
 }  // namespace
@@ -449,7 +472,11 @@ int encode_launch(splitzip_codec *codec, uint32_t n_seg, const splitzip_segment 
     if (rc != SPLITZIP_OK)
         return rc;
     const uint32_t n_tiles = tiles[n_seg];
-    if ((rc = ensure_status(w, n_tiles)) != SPLITZIP_OK)
+    uint64_t ovf_cap = 1;
+    for (uint32_t i = 0; i < n_seg; ++i)
+        ovf_cap += segs[i].esc_capacity;
+    const EncodeScratch lay(n_tiles, ovf_cap);
+    if ((rc = ensure_scratch(w, lay.total)) != SPLITZIP_OK)
         return rc;
     if (!d_result && (rc = ensure_result(w, n_seg)) != SPLITZIP_OK)
         return rc;
@@ -458,33 +485,26 @@ int encode_launch(splitzip_codec *codec, uint32_t n_seg, const splitzip_segment 
     a.seg0 = desc[0];
     if (n_seg > 1 && (rc = stage_descriptors(w, desc, tiles, &a.segs, &a.tile_start)) != SPLITZIP_OK)
         return rc;
-    // a new epoch per launch keeps earlier launches' status words from being read as
-    // current; after 2^24 - 1 launches the words are cleared and the count restarts
-    if (w->epoch >= sz::kEpochMax) {
-        SZ_HIP(hipMemsetAsync(w->status, 0, w->status_cap * sizeof(uint64_t), stream), "hipMemsetAsync(status)");
-        w->epoch = 0;
-    }
-    w->epoch += 1;
     uint8_t *res = d_result ? reinterpret_cast<uint8_t *>(d_result) : w->result;
     a.lut = codec->d_lut;
-    a.status = w->status;
-    a.ticket = w->ticket;
+    a.tile_count = reinterpret_cast<uint32_t *>(w->scratch + lay.tile_count);
+    a.tile_ovf = reinterpret_cast<uint64_t *>(w->scratch + lay.tile_ovf);
+    a.slots = reinterpret_cast<uint32_t *>(w->scratch + lay.slots);
+    a.block_sum = reinterpret_cast<uint64_t *>(w->scratch + lay.block_sum);
+    a.ovf = reinterpret_cast<uint32_t *>(w->scratch + lay.ovf);
+    a.ovf_next = w->ovf_next;
+    a.ovf_cap = ovf_cap;
     a.err = reinterpret_cast<uint32_t *>(res);
     a.seg_escapes = reinterpret_cast<uint64_t *>(res + 8);
-    a.ticket_base = w->ticket_base;
-    a.epoch_tag = (uint64_t)w->epoch << sz::kEpochShift;
     a.n_seg = n_seg;
     a.n_tiles = n_tiles;
     a.log2_chunk = codec->log2_chunk;
     hipError_t e = sz::launch_encode(a, stream);
     if (e != hipSuccess) {
-        // the counter state is unknown after a failed launch: start the workspace over
-        (void)hipMemsetAsync(w->ticket, 0, sizeof(unsigned long long), stream);
-        w->ticket_base = 0;
-        w->epoch = sz::kEpochMax;
+        // a launch that did not run to its end may leave the overflow counter set
+        (void)hipMemsetAsync(w->ovf_next, 0, sizeof(unsigned long long), stream);
         return fail_hip(e, "encode launch");
     }
-    w->ticket_base += n_tiles;
     *out_ws = w;
     *out_tiles = n_tiles;
     return SPLITZIP_OK;
@@ -545,11 +565,16 @@ int splitzip_encode(splitzip_codec *codec, uint32_t n_seg, splitzip_segment *seg
         return fail_hip(e, "encode readback");
     uint32_t kerr = 0;
     std::memcpy(&kerr, w->h_result, 4);
+    const uint64_t *E = reinterpret_cast<const uint64_t *>(w->h_result + 8);
+    bool over_capacity = false;
+    for (uint32_t i = 0; i < n_seg; ++i)
+        over_capacity |= E[i] > segs[i].esc_capacity;
     if (kerr) {
         SZ_HIP(hipMemsetAsync(w->result, 0, 8, stream), "hipMemsetAsync(err)");
-        return fail(SPLITZIP_E_DEVICE, "encode kernel reported error bits 0x%x", kerr);
+        // an exhausted overflow area is expected only when some segment is over capacity
+        if ((kerr & ~sz::kErrOverflowArea) || !over_capacity)
+            return fail(SPLITZIP_E_DEVICE, "encode kernel reported error bits 0x%x", kerr);
     }
-    const uint64_t *E = reinterpret_cast<const uint64_t *>(w->h_result + 8);
     rc = SPLITZIP_OK;
     for (uint32_t i = 0; i < n_seg; ++i) {
         segs[i].n_escapes = E[i];

@@ -8,41 +8,39 @@
 namespace sz {
 
 // ---- tiling -------------------------------------------------------------------------
-// A workgroup is 4 wave64s.  Each lane owns kGroupsPerLane groups of 8 consecutive
-// words (one 16-byte load each); wave w's groups cover 64 * 8 * kGroupsPerLane
-// consecutive words, so a tile is 8192 words (16 KiB of BF16) handled by one workgroup.
+// A workgroup is 4 wave64s.  Each lane owns k*Groups groups of 8 consecutive words (one
+// 16-byte load each); wave w's groups cover 64 * 8 * k*Groups consecutive words.  An
+// encode tile is 8192 words (16 KiB of BF16), a decode tile 16384 words.
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kGroupsPerLane = 4;
 constexpr int kGroupWords = 8;
-constexpr int kTileShift = 13;
-constexpr int kTileWords = 1 << kTileShift;
-static_assert(kThreads * kGroupsPerLane * kGroupWords == kTileWords, "tile geometry");
+constexpr int kEncGroups = 4;
+constexpr int kEncTileShift = 13;
+constexpr int kEncTileWords = 1 << kEncTileShift;
+constexpr int kDecGroups = 8;
+constexpr int kDecTileShift = 14;
+constexpr int kDecTileWords = 1 << kDecTileShift;
+static_assert(kThreads * kEncGroups * kGroupWords == kEncTileWords, "encode tile geometry");
+static_assert(kThreads * kDecGroups * kGroupWords == kDecTileWords, "decode tile geometry");
 
 // Inverse-LUT entry of an exponent outside the codebook: nibble 0 plus an escape bit.
 constexpr uint8_t kEscapeEntry = 0x10;
 
-// ---- decoupled look-back tile status (one u64 per tile) ------------------------------
-//   bits 63..40  epoch of the launch that wrote it (never 0)
-//   bits 39..38  1 = tile aggregate only, 2 = inclusive prefix
-//   bits 37..0   escape count
-constexpr int kValueBits = 38;
-constexpr uint64_t kValueMask = (1ull << kValueBits) - 1;
-constexpr uint64_t kFlagAggregate = 1ull << kValueBits;
-constexpr uint64_t kFlagPrefix = 2ull << kValueBits;
-constexpr uint64_t kFlagMask = 3ull << kValueBits;
-constexpr int kEpochShift = 40;
-constexpr uint32_t kEpochMax = (1u << 24) - 1;
-constexpr uint64_t kMaxSegmentWords = 1ull << kValueBits;
-// Bounded waits: a look-back that sees no progress for this many polls gives up, flags
-// an error and lets the grid drain instead of spinning forever.
-constexpr uint32_t kSpinLimit = 1u << 20;
+// ---- encode scratch --------------------------------------------------------------------
+// Each tile's escapes are first written compacted to a slot of kSlotEscapes entries (or, if
+// more, to an overflow area) as (position inside the tile | exponent << 16), then moved to
+// their final place once the tile's escape offset is known.
+constexpr uint32_t kSlotEscapes = 32;
+constexpr uint32_t kSumTiles = 2048;          // tiles per segmented-sum block
+constexpr uint32_t kPlaceTiles = kThreads;    // tiles per placement workgroup (one per thread)
+constexpr uint64_t kMaxSegmentWords = 1ull << 38;
+static_assert(kEncTileWords <= 65536, "in-tile positions must fit 16 bits");
+static_assert(kSumTiles % kThreads == 0 && kSumTiles % kPlaceTiles == 0, "sum blocks");
 
 // error bits written by the kernels
-constexpr uint32_t kErrLookbackTimeout = 1u;
-constexpr uint32_t kErrBadOffsets = 2u;
-constexpr uint32_t kErrBadPosition = 4u;
-constexpr uint32_t kErrBadTicket = 8u;
+constexpr uint32_t kErrBadOffsets = 2u;      // decode: chunk offsets out of range
+constexpr uint32_t kErrBadPosition = 4u;     // decode: escape position outside its chunk
+constexpr uint32_t kErrOverflowArea = 8u;    // encode: overflow area too small
 
 struct SegDesc {
     uint16_t *data;         // encode: input words; decode: output words
@@ -60,12 +58,15 @@ struct EncodeArgs {
     const SegDesc *segs;          // device table when n_seg > 1
     const uint32_t *tile_start;   // device [n_seg + 1] first tile of each segment
     const uint8_t *lut;           // device [256] inverse LUT (code, or kEscapeEntry)
-    uint64_t *status;             // [n_tiles] look-back words
-    unsigned long long *ticket;   // dynamic tile counter (monotone across launches)
+    uint32_t *tile_count;         // [n_tiles] escapes per tile
+    uint64_t *tile_ovf;           // [n_tiles] overflow offset of tiles past kSlotEscapes
+    uint32_t *slots;              // [n_tiles * kSlotEscapes]
+    uint32_t *ovf;                // [ovf_cap]
+    unsigned long long *ovf_next; // overflow bump counter, 0 between encodes
+    uint64_t ovf_cap;
+    uint64_t *block_sum;          // [ceil(n_tiles / kSumTiles)] segmented sums, bit 63 = head
     uint64_t *seg_escapes;        // [n_seg] OUT: E per segment
     uint32_t *err;                // OUT: error bits
-    uint64_t ticket_base;         // counter value when this launch starts
-    uint64_t epoch_tag;           // epoch << kEpochShift
     uint32_t n_seg;
     uint32_t n_tiles;
     uint32_t log2_chunk;

@@ -13,9 +13,9 @@
 //   - encode: 256-byte inverse LUT in LDS (exponent -> code or escape bit), sign+mantissa
 //     bytes gathered with v_perm_b32, codes packed two per byte;
 //   - encode: escape ranks inside a tile by a wave prefix of packed per-group counts plus
-//     an LDS prefix over the 4 waves; across tiles by a single-pass decoupled look-back
-//     (dynamic tile tickets, one packed 64-bit status word per tile, agent-scope atomics
-//     so that the 8 XCDs, whose L2s are not coherent with each other, see one another);
+//     an LDS prefix over the 4 waves; the tile's escapes go compacted to a scratch slot, and
+//     two small launches turn the per-tile counts into global offsets (segmented sums) and
+//     move the escapes into place, so no workgroup ever waits on another;
 //   - decode: codebook lookup with two v_perm_b32 byte selects per 4 codes (codebook in
 //     SGPRs), exponent bytes staged in LDS only for tiles that hold escapes, where the
 //     escapes overwrite them before the words are assembled.
@@ -156,6 +156,16 @@ hipError_t launch_calibrate(const uint16_t *d_x, uint64_t n, uint32_t *d_partial
 
 // ======================================================================================
 // a2-a4, a7  encode
+//
+// Three launches, none of which waits on another workgroup:
+//   pack   (one workgroup per tile of kEncTileWords words): sign+mantissa bytes and codes,
+//          escape ranks inside the tile, escapes written compacted to the tile's scratch slot
+//          (or, past kSlotEscapes, to an overflow area reserved with one atomic), tile-local
+//          chunk offsets into chunk_off, the tile's escape count;
+//   sums   (one workgroup per kSumTiles tiles): segmented sums of the tile counts;
+//   place  (one workgroup per kPlaceTiles tiles): each tile's escape offset from those sums,
+//          escapes moved to their final positions, chunk offsets made global, per-segment
+//          totals.
 // ======================================================================================
 
 // Split one group of 8 words (4 dwords, word 2m in the low half of dword m).
@@ -189,155 +199,107 @@ __device__ __forceinline__ uint32_t flags_keep(uint32_t nv)
     return nv >= 8 ? ~0u : (1u << (8 * (nv >> 1) + 4 + (nv & 1))) - 1u;
 }
 
-__device__ __forceinline__ uint64_t status_load(const uint64_t *p)
+// Segment and first tile of global tile t (uniform when t is).
+__device__ __forceinline__ uint32_t tile_segment(const EncodeArgs &a, uint32_t t)
 {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return a.n_seg > 1 ? find_segment(a.tile_start, a.n_seg, t) : 0u;
 }
 
-__device__ __forceinline__ void status_store(uint64_t *p, uint64_t v)
+__device__ __forceinline__ uint32_t segment_first_tile(const EncodeArgs &a, uint32_t s)
 {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return a.n_seg > 1 ? a.tile_start[s] : 0u;
 }
 
-// Exclusive escape prefix of global tile t inside its segment, whose first tile is `first`.
-// Run by one full wave.  Each pass reads the status words of the 64 preceding tiles (one
-// per lane), waits until all of them are published by this launch, and adds the values
-// from the nearest tile back to (and including) the nearest one holding an inclusive
-// prefix.  Status value+flag+epoch sit in one 64-bit word, so relaxed atomics suffice.
-__device__ uint64_t lookback(const uint64_t *status, uint32_t t, uint32_t first, uint64_t tag,
-                             uint32_t lane, uint32_t *err)
+__device__ __forceinline__ uint32_t segment_end_tile(const EncodeArgs &a, uint32_t s)
 {
-    uint64_t excl = 0;
-    int64_t end = t;
-    uint32_t spins = 0;
-    for (;;) {
-        const int64_t idx = end - 1 - (int64_t)lane;
-        const bool in = idx >= (int64_t)first;
-        uint64_t st = 0, flag = 0;
-        for (;;) {
-            if (in) {
-                st = status_load(status + idx);
-                flag = ((st >> kEpochShift) == (tag >> kEpochShift)) ? (st & kFlagMask) : 0;
-            }
-            if (!ballot(in && flag == 0))
-                break;
-            // give up at the limit, or at once when another tile has already given up
-            const bool abandoned = (spins & 63u) == 63u &&
-                __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
-            if (++spins > kSpinLimit || abandoned) {
-                // no progress: give up (the launch is reported as failed), drain the grid
-                if (lane == 0)
-                    atomicOr(err, kErrLookbackTimeout);
-                if (in && flag == 0) {
-                    flag = kFlagPrefix;
-                    st = 0;
-                }
-                break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-        }
-        const uint64_t pmask = ballot(in && flag == kFlagPrefix);
-        const uint32_t stop = pmask ? (uint32_t)__builtin_ctzll(pmask) : 63u;
-        const uint64_t val = (in && lane <= stop) ? (st & kValueMask) : 0;
-        excl += wave_total_u64(val, lane);
-        if (pmask || end - 64 <= (int64_t)first)
-            break;
-        end -= 64;
-    }
-    return excl;
+    return a.n_seg > 1 ? a.tile_start[s + 1] : a.n_tiles;
 }
 
-__global__ __launch_bounds__(kThreads) void encode_kernel(const EncodeArgs a)
+__device__ __forceinline__ SegDesc segment_desc(const EncodeArgs &a, uint32_t s)
+{
+    return a.n_seg > 1 ? a.segs[s] : a.seg0;
+}
+
+// ---- pack ---------------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs a)
 {
     __shared__ uint8_t s_lut[256];
-    __shared__ uint32_t s_ticket;
     __shared__ uint32_t s_wave_total[kWaves];
-    __shared__ uint64_t s_excl;
+    __shared__ uint64_t s_ovf;
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = lane_id();
     const uint32_t wave = tid >> 6;
+    const uint32_t t = blockIdx.x;
 
-    if (tid == 0)
-        s_ticket = (uint32_t)(atomicAdd(a.ticket, 1ull) - a.ticket_base);
     if (tid < 64)
         reinterpret_cast<uint32_t *>(s_lut)[tid] = reinterpret_cast<const uint32_t *>(a.lut)[tid];
-    __syncthreads();
 
-    // tile -> segment (wave-uniform values)
-    const uint32_t t = __builtin_amdgcn_readfirstlane(s_ticket);
-    if (t >= a.n_tiles) {
-        // the ticket counter was not where the host expected: touch nothing, report
-        if (tid == 0)
-            atomicOr(a.err, kErrBadTicket);
-        return;
-    }
-    uint32_t s = 0, first = 0, last = a.n_tiles - 1;
-    SegDesc sd = a.seg0;
-    if (a.n_seg > 1) {
-        s = find_segment(a.tile_start, a.n_seg, t);
-        first = a.tile_start[s];
-        last = a.tile_start[s + 1] - 1;
-        sd = a.segs[s];
-    }
+    const uint32_t s = tile_segment(a, t);
+    const SegDesc sd = segment_desc(a, s);
     const uint64_t n = sd.n;
-    const uint64_t base = (uint64_t)(t - first) << kTileShift;
+    const uint64_t base = (uint64_t)(t - segment_first_tile(a, s)) << kEncTileShift;
     const uint64_t cmask = (1ull << a.log2_chunk) - 1;
 
-    // ---- a2: dense split and pack -------------------------------------------------------
-    uint4 v[kGroupsPerLane];
-    uint32_t flags[kGroupsPerLane];
-    uint32_t counts[kGroupsPerLane];
+    // word order inside the tile: wave w covers 64 * 8 * kEncGroups consecutive words, its group
+    // j covers 512 of them, lane l the 8 at offset 8 l.
+    uint64_t g0[kEncGroups];
+    uint4 v[kEncGroups];
 #pragma unroll
-    for (int j = 0; j < kGroupsPerLane; ++j) {
-        const uint64_t g0 = base + (uint64_t)(((wave * kGroupsPerLane + j) << 6) + lane) * kGroupWords;
-        if (g0 + kGroupWords <= n) {
-            v[j] = *reinterpret_cast<const uint4 *>(sd.data + g0);
+    for (int j = 0; j < kEncGroups; ++j) {
+        g0[j] = base + (uint64_t)(((wave * kEncGroups + j) << 6) + lane) * kGroupWords;
+        if (g0[j] + kGroupWords <= n) {
+            v[j] = *reinterpret_cast<const uint4 *>(sd.data + g0[j]);
         } else {
             uint16_t wds[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k)
-                wds[k] = (g0 + k < n) ? sd.data[g0 + k] : (uint16_t)0;
+                wds[k] = (g0[j] + k < n) ? sd.data[g0[j] + k] : (uint16_t)0;
             v[j] = make_uint4(wds[0] | ((uint32_t)wds[1] << 16), wds[2] | ((uint32_t)wds[3] << 16),
                               wds[4] | ((uint32_t)wds[5] << 16), wds[6] | ((uint32_t)wds[7] << 16));
         }
     }
+    __syncthreads();   // LUT in LDS
+
+    // ---- a2: dense split and pack ---------------------------------------------------------
+    uint32_t flags[kEncGroups];
+    uint32_t counts[kEncGroups];
 #pragma unroll
-    for (int j = 0; j < kGroupsPerLane; ++j) {
-        const uint64_t g0 = base + (uint64_t)(((wave * kGroupsPerLane + j) << 6) + lane) * kGroupWords;
+    for (int j = 0; j < kEncGroups; ++j) {
         uint32_t sm_lo, sm_hi, codes, fl;
         split_group(v[j], s_lut, sm_lo, sm_hi, codes, fl);
-        if (g0 + kGroupWords <= n) {
-            *reinterpret_cast<uint2 *>(sd.sm + g0) = make_uint2(sm_lo, sm_hi);
-            *reinterpret_cast<uint32_t *>(sd.codes + (g0 >> 1)) = codes;
+        if (g0[j] + kGroupWords <= n) {
+            *reinterpret_cast<uint2 *>(sd.sm + g0[j]) = make_uint2(sm_lo, sm_hi);
+            *reinterpret_cast<uint32_t *>(sd.codes + (g0[j] >> 1)) = codes;
         } else {
-            const uint32_t nv = g0 < n ? (uint32_t)(n - g0) : 0u;
+            const uint32_t nv = g0[j] < n ? (uint32_t)(n - g0[j]) : 0u;
             codes &= codes_keep(nv);
             fl &= flags_keep(nv);
             for (uint32_t k = 0; k < nv; ++k)
-                sd.sm[g0 + k] = (uint8_t)((k < 4 ? sm_lo : sm_hi) >> (8 * (k & 3)));
+                sd.sm[g0[j] + k] = (uint8_t)((k < 4 ? sm_lo : sm_hi) >> (8 * (k & 3)));
             for (uint32_t k = 0; k < (nv + 1) / 2; ++k)
-                sd.codes[(g0 >> 1) + k] = (uint8_t)(codes >> (8 * k));
+                sd.codes[(g0[j] >> 1) + k] = (uint8_t)(codes >> (8 * k));
         }
         flags[j] = fl;
         counts[j] = __popc(fl);
     }
 
-    // ---- a3: escape ranks inside the tile -------------------------------------------------
+    // ---- a3: escape ranks inside the tile ---------------------------------------------------
     // Word order inside a wave is (group j, lane, word k).  Pack the per-group counts two per
-    // dword (16-bit fields), prefix-sum them over the lanes, then offset each group by the
-    // wave totals of the groups before it.
-    uint32_t rank_in_wave[kGroupsPerLane];
+    // dword (16-bit fields), prefix-sum them over the lanes, then offset each group by the wave
+    // totals of the groups before it and by the totals of the earlier waves.
+    uint32_t rank[kEncGroups];
     uint32_t wave_sum = 0;
 #pragma unroll
-    for (int j = 0; j < kGroupsPerLane; j += 2) {
+    for (int j = 0; j < kEncGroups; j += 2) {
         const uint32_t packed = counts[j] | (counts[j + 1] << 16);
         const uint32_t incl = wave_inclusive_sum(packed, lane);
         const uint32_t excl = incl - packed;
         const uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
-        rank_in_wave[j] = wave_sum + (excl & 0xFFFFu);
+        rank[j] = wave_sum + (excl & 0xFFFFu);
         wave_sum += tot & 0xFFFFu;
-        rank_in_wave[j + 1] = wave_sum + (excl >> 16);
+        rank[j + 1] = wave_sum + (excl >> 16);
         wave_sum += tot >> 16;
     }
     if (lane == 0)
@@ -351,61 +313,262 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const EncodeArgs a)
         tile_total += x;
     }
 
-    // ---- a4: cross-tile escape offsets (decoupled look-back) -------------------------------
-    if (wave == 0) {
-        uint64_t excl = 0;
-        if (t == first) {
-            if (lane == 0)
-                status_store(a.status + t, a.epoch_tag | kFlagPrefix | tile_total);
-        } else {
-            if (lane == 0)
-                status_store(a.status + t, a.epoch_tag | kFlagAggregate | tile_total);
-            excl = lookback(a.status, t, first, a.epoch_tag, lane, a.err);
-            if (lane == 0)
-                status_store(a.status + t, a.epoch_tag | kFlagPrefix | ((excl + tile_total) & kValueMask));
+    // where the tile's escapes go: its slot, or a range of the overflow area
+    uint32_t *dst = a.slots + (uint64_t)t * kSlotEscapes;
+    uint64_t room = kSlotEscapes;
+    if (tile_total > kSlotEscapes) {
+        if (tid == 0) {
+            const uint64_t off = atomicAdd(a.ovf_next, (unsigned long long)tile_total);
+            s_ovf = off;
+            a.tile_ovf[t] = off;
+            if (off + tile_total > a.ovf_cap)
+                atomicOr(a.err, kErrOverflowArea);
         }
-        if (lane == 0)
-            s_excl = excl;
+        __syncthreads();
+        const uint64_t off = s_ovf;
+        dst = a.ovf + off;
+        room = off < a.ovf_cap ? a.ovf_cap - off : 0;
     }
-    __syncthreads();
-    const uint64_t tile_excl = s_excl;
+    if (tid == 0)
+        a.tile_count[t] = tile_total;
 
-    // escape records and chunk offsets
+    // escapes: (position inside the tile, exponent); tile-local chunk offsets
 #pragma unroll
-    for (int j = 0; j < kGroupsPerLane; ++j) {
-        const uint64_t g0 = base + (uint64_t)(((wave * kGroupsPerLane + j) << 6) + lane) * kGroupWords;
-        const uint64_t before = tile_excl + wave_base + rank_in_wave[j];
-        if (g0 < n && (g0 & cmask) == 0)
-            sd.chunk_off[g0 >> a.log2_chunk] = before;
+    for (int j = 0; j < kEncGroups; ++j) {
+        const uint32_t r0 = wave_base + rank[j];
+        if (g0[j] < n && (g0[j] & cmask) == 0)
+            sd.chunk_off[g0[j] >> a.log2_chunk] = r0;
         uint32_t z = flags[j];
         if (z) {
-            // the group's 8 exponents, word k in byte k (a dword >> 7 holds the exponent of
-            // its low word in byte 0 and of its high word in byte 2)
+            // the group's 8 exponents, word k in byte k (a dword >> 7 holds the exponent of its
+            // low word in byte 0 and of its high word in byte 2)
             const uint64_t ex8 = perm(v[j].y >> 7, v[j].x >> 7, 0x06040200u)
                                | ((uint64_t)perm(v[j].w >> 7, v[j].z >> 7, 0x06040200u) << 32);
-            uint64_t r = before;
+            const uint32_t p0 = (uint32_t)(g0[j] - base);
+            uint32_t r = r0;
             do {
                 const uint32_t k = flag_bit_to_word((uint32_t)__builtin_ctz(z));
-                if (r < sd.esc) {
-                    sd.esc_pos[r] = (uint16_t)((g0 + k) & cmask);
-                    sd.esc_exp[r] = (uint8_t)(ex8 >> (8 * k));
-                }
+                if (r < room)
+                    dst[r] = (p0 + k) | ((uint32_t)(uint8_t)(ex8 >> (8 * k)) << 16);
                 ++r;
                 z &= z - 1;
             } while (z);
         }
     }
-    if (t == last && tid == 0) {
-        const uint64_t E = tile_excl + tile_total;
-        const uint64_t n_chunks = (n + cmask) >> a.log2_chunk;
+}
+
+// ---- sums ---------------------------------------------------------------------------------
+
+// Segmented sum: (head, value) pairs combined in order; a head (first tile of a segment)
+// discards what came before it.
+struct SegSum {
+    uint32_t head;
+    uint64_t v;
+};
+
+__device__ __forceinline__ SegSum seg_combine(SegSum a, SegSum b)
+{
+    return SegSum{a.head | b.head, b.head ? b.v : a.v + b.v};
+}
+
+__device__ __forceinline__ SegSum seg_shfl_up(SegSum x, uint32_t d, uint32_t lane)
+{
+    const uint32_t src = lane >= d ? lane - d : lane;
+    SegSum y;
+    y.head = shfl_u32(x.head, src);
+    y.v = ((uint64_t)shfl_u32((uint32_t)(x.v >> 32), src) << 32) | shfl_u32((uint32_t)x.v, src);
+    return y;
+}
+
+// Inclusive segmented scan over the 256 threads of the workgroup (thread order).
+__device__ SegSum block_seg_scan(SegSum x, uint32_t tid, uint32_t lane, SegSum *s_wave)
+{
+#pragma unroll
+    for (uint32_t d = 1; d < 64; d <<= 1) {
+        const SegSum y = seg_shfl_up(x, d, lane);
+        if (lane >= d)
+            x = seg_combine(y, x);
+    }
+    if (lane == 63)
+        s_wave[tid >> 6] = x;
+    __syncthreads();
+    SegSum carry{0, 0};
+    for (uint32_t w = 0; w < (tid >> 6); ++w)
+        carry = seg_combine(carry, s_wave[w]);
+    __syncthreads();
+    return seg_combine(carry, x);
+}
+
+__device__ uint32_t block_max_u32(uint32_t x, uint32_t tid, uint32_t lane, uint32_t *s_red)
+{
+#pragma unroll
+    for (uint32_t d = 1; d < 64; d <<= 1)
+        x = max(x, shfl_u32(x, lane ^ d));
+    if (lane == 0)
+        s_red[tid >> 6] = x;
+    __syncthreads();
+    uint32_t m = 0;
+    for (int w = 0; w < kWaves; ++w)
+        m = max(m, s_red[w]);
+    __syncthreads();
+    return m;
+}
+
+__device__ uint64_t block_sum_u64(uint64_t x, uint32_t tid, uint32_t lane, uint64_t *s_red)
+{
+    x = wave_total_u64(x, lane);
+    if (lane == 0)
+        s_red[tid >> 6] = x;
+    __syncthreads();
+    uint64_t m = 0;
+    for (int w = 0; w < kWaves; ++w)
+        m += s_red[w];
+    __syncthreads();
+    return m;
+}
+
+__device__ __forceinline__ bool is_segment_head(const EncodeArgs &a, uint32_t u)
+{
+    return segment_first_tile(a, tile_segment(a, u)) == u;
+}
+
+// Segmented fold of the tile counts [u, u + len) ∩ [0, limit) in order.
+__device__ __forceinline__ SegSum fold_tiles(const EncodeArgs &a, uint32_t u, uint32_t len,
+                                             uint32_t limit)
+{
+    SegSum acc{0, 0};
+    for (uint32_t i = 0; i < len && u + i < limit; ++i)
+        acc = seg_combine(acc, SegSum{is_segment_head(a, u + i) ? 1u : 0u, a.tile_count[u + i]});
+    return acc;
+}
+
+__global__ __launch_bounds__(kThreads) void encode_sums_kernel(const EncodeArgs a)
+{
+    __shared__ SegSum s_wave[kWaves];
+    const uint32_t tid = threadIdx.x;
+    const uint32_t per = kSumTiles / kThreads;
+    const uint32_t u0 = blockIdx.x * kSumTiles + tid * per;
+    const SegSum mine = fold_tiles(a, u0, per, a.n_tiles);
+    const SegSum all = block_seg_scan(mine, tid, lane_id(), s_wave);
+    if (tid == kThreads - 1)
+        a.block_sum[blockIdx.x] = all.v | ((uint64_t)all.head << 63);
+    if (blockIdx.x == 0 && tid == 0)
+        *a.ovf_next = 0;            // the pack launch of this encode has finished with it
+}
+
+// ---- place --------------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs a)
+{
+    __shared__ SegSum s_wave[kWaves + 1];
+    __shared__ uint32_t s_red32[kWaves];
+    __shared__ uint64_t s_red64[kWaves];
+    __shared__ uint64_t s_prefix[kPlaceTiles];
+    __shared__ uint32_t s_count[kPlaceTiles];
+    __shared__ uint32_t s_seg[kPlaceTiles];
+
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = lane_id();
+    const uint32_t wave = tid >> 6;
+    const uint32_t u_first = blockIdx.x * kPlaceTiles;
+    const uint32_t sum_block = u_first / kSumTiles;
+
+    // carry-in: segmented sum of every tile before u_first.  (1) The sum blocks before this
+    // one: from the last one holding a segment head (if any) to the end.  (2) The tiles of this
+    // sum block before u_first, folded in order.
+    uint32_t last_head = 0, any_head = 0;
+    for (uint32_t b = tid; b < sum_block; b += kThreads)
+        if (a.block_sum[b] >> 63) {
+            last_head = b;        // b grows with the loop, so this keeps the largest
+            any_head = 1;
+        }
+    last_head = block_max_u32(any_head ? last_head + 1 : 0u, tid, lane, s_red32);
+    any_head = last_head != 0;
+    const uint32_t from = any_head ? last_head - 1 : 0u;
+    uint64_t part = 0;
+    for (uint32_t b = from + tid; b < sum_block; b += kThreads)
+        part += a.block_sum[b] & ~(1ull << 63);
+    part = block_sum_u64(part, tid, lane, s_red64);
+    SegSum before{any_head, part};
+    {
+        const uint32_t per = kSumTiles / kThreads;
+        const SegSum mine = fold_tiles(a, sum_block * kSumTiles + tid * per, per, u_first);
+        const SegSum all = block_seg_scan(mine, tid, lane, s_wave);
+        if (tid == kThreads - 1)
+            s_wave[kWaves] = all;
+        __syncthreads();
+        before = seg_combine(before, s_wave[kWaves]);
+        __syncthreads();
+    }
+
+    // each thread: one tile; exclusive segmented prefix = carry-in combined with the earlier tiles
+    const uint32_t u = u_first + tid;
+    const bool valid = u < a.n_tiles;
+    const uint32_t seg = valid ? tile_segment(a, u) : 0u;
+    const uint32_t head = valid && segment_first_tile(a, seg) == u ? 1u : 0u;
+    const uint32_t count = valid ? a.tile_count[u] : 0u;
+    const SegSum incl = block_seg_scan(SegSum{head, count}, tid, lane, s_wave);
+    const SegSum with_carry = seg_combine(before, incl);
+    const uint64_t prefix = head ? 0 : with_carry.v - count;
+    s_prefix[tid] = prefix;
+    s_count[tid] = count;
+    s_seg[tid] = seg;
+    if (valid && u + 1 == segment_end_tile(a, seg)) {
+        // the segment's last tile knows the segment's escape count
+        const SegDesc sd = segment_desc(a, seg);
+        const uint64_t E = prefix + count;
+        const uint64_t n_chunks = (sd.n + (1ull << a.log2_chunk) - 1) >> a.log2_chunk;
         sd.chunk_off[n_chunks] = E;
-        a.seg_escapes[s] = E;
+        a.seg_escapes[seg] = E;
+    }
+    __syncthreads();
+
+    // one wave per tile: move the escapes, make the tile's chunk offsets global
+    const uint64_t cmask = (1ull << a.log2_chunk) - 1;
+    const uint32_t n_here = a.n_tiles - u_first < kPlaceTiles ? a.n_tiles - u_first : kPlaceTiles;
+    for (uint32_t i = wave; i < n_here; i += kWaves) {
+        const uint32_t ut = u_first + i;
+        const uint32_t sg = s_seg[i];
+        const SegDesc sd = segment_desc(a, sg);
+        const uint64_t base = (uint64_t)(ut - segment_first_tile(a, sg)) << kEncTileShift;
+        if (base >= sd.n)
+            continue;                                   // empty segment
+        const uint64_t pre = s_prefix[i];
+        const uint32_t cnt = s_count[i];
+        const uint32_t *src = a.slots + (uint64_t)ut * kSlotEscapes;
+        uint64_t room = cnt;
+        if (cnt > kSlotEscapes) {
+            const uint64_t off = a.tile_ovf[ut];
+            src = a.ovf + off;
+            room = off < a.ovf_cap ? a.ovf_cap - off : 0;
+        }
+        for (uint32_t r = lane; r < cnt; r += 64) {
+            const uint64_t d = pre + r;
+            if (r < room && d < sd.esc) {
+                const uint32_t e = src[r];
+                sd.esc_pos[d] = (uint16_t)((base + (e & 0xFFFFu)) & cmask);
+                sd.esc_exp[d] = (uint8_t)(e >> 16);
+            }
+        }
+        // chunks that start inside this tile
+        const uint64_t valid_words = sd.n - base < (uint64_t)kEncTileWords ? sd.n - base : (uint64_t)kEncTileWords;
+        const uint64_t c_first = (base + cmask) >> a.log2_chunk;
+        const uint64_t c_end = (base + valid_words + cmask) >> a.log2_chunk;
+        for (uint64_t c = c_first + lane; c < c_end; c += 64)
+            sd.chunk_off[c] += pre;
     }
 }
 
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream)
 {
-    encode_kernel<<<a.n_tiles, kThreads, 0, stream>>>(a);
+    encode_pack_kernel<<<a.n_tiles, kThreads, 0, stream>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    encode_sums_kernel<<<(a.n_tiles + kSumTiles - 1) / kSumTiles, kThreads, 0, stream>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    encode_place_kernel<<<(a.n_tiles + kPlaceTiles - 1) / kPlaceTiles, kThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 
@@ -437,8 +600,8 @@ __device__ __forceinline__ uint32_t assemble(uint32_t s, uint32_t sm_sel, uint32
 
 __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
 {
-    __shared__ uint32_t s_exp[kTileWords / 4];              // exponent bytes of the tile
-    __shared__ uint64_t s_off[kTileWords / 16 + 1];         // chunk offsets of the tile
+    __shared__ uint32_t s_exp[kDecTileWords / 4];              // exponent bytes of the tile
+    __shared__ uint64_t s_off[kDecTileWords / 16 + 1];         // chunk offsets of the tile
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = lane_id();
@@ -453,21 +616,21 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
         sd = a.segs[s];
     }
     const uint64_t n = sd.n;
-    const uint64_t base = (uint64_t)(t - first) << kTileShift;
+    const uint64_t base = (uint64_t)(t - first) << kDecTileShift;
     if (base >= n)
         return;                                              // empty segment
-    const uint64_t valid = n - base < (uint64_t)kTileWords ? n - base : (uint64_t)kTileWords;
+    const uint64_t valid = n - base < (uint64_t)kDecTileWords ? n - base : (uint64_t)kDecTileWords;
     const uint32_t log2c = a.log2_chunk;
     const uint64_t C = 1ull << log2c;
     const uint64_t E = sd.esc;
     const uint32_t cb[4] = {a.cb[0], a.cb[1], a.cb[2], a.cb[3]};
 
     // ---- loads ---------------------------------------------------------------------------
-    uint2 smv[kGroupsPerLane];
-    uint32_t cw[kGroupsPerLane];
+    uint2 smv[kDecGroups];
+    uint32_t cw[kDecGroups];
 #pragma unroll
-    for (int j = 0; j < kGroupsPerLane; ++j) {
-        const uint64_t g0 = base + (uint64_t)(((wave * kGroupsPerLane + j) << 6) + lane) * kGroupWords;
+    for (int j = 0; j < kDecGroups; ++j) {
+        const uint64_t g0 = base + (uint64_t)(((wave * kDecGroups + j) << 6) + lane) * kGroupWords;
         if (g0 + kGroupWords <= n) {
             smv[j] = *reinterpret_cast<const uint2 *>(sd.sm + g0);
             cw[j] = *reinterpret_cast<const uint32_t *>(sd.codes + (g0 >> 1));
@@ -487,7 +650,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
     }
 
     // ---- escape range of the tile --------------------------------------------------------
-    const bool sub_chunk = log2c > (uint32_t)kTileShift;     // the tile lies inside one chunk
+    const bool sub_chunk = log2c > (uint32_t)kDecTileShift;     // the tile lies inside one chunk
     uint64_t c0, nc;
     if (!sub_chunk) {
         c0 = base >> log2c;
@@ -508,9 +671,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
     }
 
     // ---- a5: dense path ------------------------------------------------------------------
-    uint32_t ex_even[kGroupsPerLane], ex_odd[kGroupsPerLane];
+    uint32_t ex_even[kDecGroups], ex_odd[kDecGroups];
 #pragma unroll
-    for (int j = 0; j < kGroupsPerLane; ++j) {
+    for (int j = 0; j < kDecGroups; ++j) {
         ex_even[j] = codebook_lookup(cw[j] & 0x0F0F0F0Fu, cb);
         ex_odd[j] = codebook_lookup((cw[j] >> 4) & 0x0F0F0F0Fu, cb);
     }
@@ -518,8 +681,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
     // ---- a6: sparse escape correction (exponent bytes in LDS) ----------------------------
     if (patch) {
 #pragma unroll
-        for (int j = 0; j < kGroupsPerLane; ++j) {
-            const uint32_t q = ((wave * kGroupsPerLane + j) << 6) + lane;
+        for (int j = 0; j < kDecGroups; ++j) {
+            const uint32_t q = ((wave * kDecGroups + j) << 6) + lane;
             s_exp[2 * q] = ex_even[j];
             s_exp[2 * q + 1] = ex_odd[j];
         }
@@ -564,8 +727,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
         }
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < kGroupsPerLane; ++j) {
-            const uint32_t q = ((wave * kGroupsPerLane + j) << 6) + lane;
+        for (int j = 0; j < kDecGroups; ++j) {
+            const uint32_t q = ((wave * kDecGroups + j) << 6) + lane;
             ex_even[j] = s_exp[2 * q];
             ex_odd[j] = s_exp[2 * q + 1];
         }
@@ -573,8 +736,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
 
     // ---- assemble and store ------------------------------------------------------------------
 #pragma unroll
-    for (int j = 0; j < kGroupsPerLane; ++j) {
-        const uint64_t g0 = base + (uint64_t)(((wave * kGroupsPerLane + j) << 6) + lane) * kGroupWords;
+    for (int j = 0; j < kDecGroups; ++j) {
+        const uint64_t g0 = base + (uint64_t)(((wave * kDecGroups + j) << 6) + lane) * kGroupWords;
         uint4 o;
         o.x = assemble(smv[j].x, 0x01010000u, ex_even[j], ex_odd[j], 0x0C040C00u);
         o.y = assemble(smv[j].x, 0x03030202u, ex_even[j], ex_odd[j], 0x0C050C01u);

@@ -30,6 +30,8 @@ def dev(words: np.ndarray) -> torch.Tensor:
 
 
 def host(t: torch.Tensor, dtype) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        t = t.view(torch.int16)
     return t.cpu().numpy().view(dtype)
 
 
