@@ -58,14 +58,37 @@ def load_workload(args):
     return wl
 
 
+ENC_TILE_WORDS = 8192      # encode tile (words per workgroup)
+SLOT_ESCAPES = 32          # escapes a tile keeps in its scratch slot
+
+
 def algorithmic_bytes(ns, Es, C):
-    """(read, write) bytes of one encode launch; decode is the reverse."""
-    r = w = 0
+    """Bytes each kernel must move per launch (reads + writes), from the stream format.
+
+    encode (the three launches together) reads 2n and writes the sections
+    n + ceil(n/2) + 8 (n_chunks + 1) + 3E; decode is the reverse.  The pack kernel reads
+    2n and writes sm, codes, tile-local chunk offsets, 4-byte scratch escapes and one
+    count per tile; place reads the scratch escapes, counts and chunk offsets and writes
+    escapes (3E) and chunk offsets; sums reads one count per tile."""
+    out = {"encode": 0, "decode": 0, "encode_pack": 0, "encode_sums": 0, "encode_place": 0}
     for n, E in zip(ns, Es):
         n_ch = -(-n // C)
-        r += 2 * n
-        w += n + (n + 1) // 2 + 8 * (n_ch + 1) + 3 * E
-    return r, w
+        tiles = max(1, -(-n // ENC_TILE_WORDS))
+        sections = n + (n + 1) // 2 + 8 * (n_ch + 1) + 3 * E
+        out["encode"] += 2 * n + sections
+        out["decode"] += sections + 2 * n
+        out["encode_pack"] += 2 * n + n + (n + 1) // 2 + 8 * n_ch + 4 * E + 4 * tiles
+        out["encode_sums"] += 4 * tiles + 8 * (-(-tiles // 2048))
+        out["encode_place"] += 4 * tiles + 4 * E + 3 * E + 16 * n_ch + 8
+    return out
+
+
+def roofline(name, bytes_, ms, workload):
+    achieved = bytes_ / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
+    return {"bound": "hbm", "kernel": name, "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(name, workload), "algorithmic_bytes": bytes_,
+            "avg_launch_ms": round(ms, 4)}
 
 
 def cpu_baseline(wl, codebook: bytes, sample_words: int):
@@ -144,12 +167,15 @@ def main():
     torch.cuda.synchronize()
     assert codec.finish_async(encs, result) == sz.OK
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    codec.profile(True)                        # HIP events around every kernel launch
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         step(events[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    ktimes = codec.kernel_times()
+    codec.profile(False)
 
     # verify the escape counts and the bitwise round trip before reporting
     assert codec.finish_async(encs, result) == sz.OK
@@ -165,27 +191,18 @@ def main():
     n = sum(ns)
     E = sum(Es)
     comp = sum(e.compressed_bytes for e in encs)
-    rd, wr = algorithmic_bytes(ns, Es, C)
-    enc_gbps_alg = (rd + wr) / (enc_avg * 1e-3) / 1e9
-    dec_gbps_alg = (rd + wr) / (dec_avg * 1e-3) / 1e9
+    alg = algorithmic_bytes(ns, Es, C)
     wall_s = t1 - t0
     value = 2 * n * args.steps / wall_s / 1e9
+    wname = wl.name + f"_c{C}"
 
-    dominant = "encode_kernel" if enc_avg >= dec_avg else "decode_kernel"
-    dom_avg = max(enc_avg, dec_avg)
-    achieved = (rd + wr) / (dom_avg * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": measured_traffic(dominant, wl.name + f"_c{C}"),
-                "algorithmic_bytes": rd + wr, "avg_launch_ms": round(dom_avg, 4)}
-    other = "decode_kernel" if dominant == "encode_kernel" else "encode_kernel"
-    oth_avg = min(enc_avg, dec_avg)
-    roofline_other = {"bound": "hbm", "kernel": other,
-                      "achieved": round((rd + wr) / (oth_avg * 1e-3) / 1e9, 1),
-                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                      "frac": round((rd + wr) / (oth_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                      "traffic": measured_traffic(other, wl.name + f"_c{C}"),
-                      "avg_launch_ms": round(oth_avg, 4)}
+    kernels = {k: roofline(k, alg[k], ms, wname) for k, (ms, cnt) in ktimes.items() if cnt}
+    for k, (ms, cnt) in ktimes.items():
+        if k in kernels:
+            kernels[k]["launches_timed"] = cnt
+    dominant = max(kernels, key=lambda k: kernels[k]["avg_launch_ms"])
+    ops = {"encode": roofline("encode (pack+sums+place)", alg["encode"], enc_avg, wname),
+           "decode": roofline("decode", alg["decode"], dec_avg, wname)}
 
     copy_gbps = None
     if not args.no_copy_ceiling:
@@ -223,8 +240,8 @@ def main():
                    "bytes_bf16": 2 * n, "description": wl.description},
         "encode_GBps": round(2 * n / (enc_avg * 1e-3) / 1e9, 2),
         "decode_GBps": round(2 * n / (dec_avg * 1e-3) / 1e9, 2),
-        "encode_hbm_frac": round(enc_gbps_alg / HBM_PEAK_GBPS, 4),
-        "decode_hbm_frac": round(dec_gbps_alg / HBM_PEAK_GBPS, 4),
+        "encode_hbm_frac": ops["encode"]["frac"],
+        "decode_hbm_frac": ops["decode"]["frac"],
         "encode_ms": {"avg": round(enc_avg, 4), "min": round(enc_ms[0], 4),
                       "median": round(enc_ms[len(enc_ms) // 2], 4)},
         "decode_ms": {"avg": round(dec_avg, 4), "min": round(dec_ms[0], 4),
@@ -234,8 +251,9 @@ def main():
         "n_escapes": E,
         "coverage_calibration": coverage,
         "coverage_input": 1 - E / n if n else None,
-        "roofline": roofline,
-        "roofline_other": roofline_other,
+        "roofline": kernels[dominant],
+        "roofline_ops": ops,
+        "roofline_kernels": kernels,
         "copy_ceiling_GBps": copy_gbps,
         "cpu_baseline": cpu,
         "generate_s": round(t_gen, 1),

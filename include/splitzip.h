@@ -149,6 +149,31 @@ int splitzip_decode(splitzip_codec *codec, uint32_t n_seg, const splitzip_segmen
  * codec must have completed; freeing its device memory synchronizes the device. */
 void splitzip_free(splitzip_codec *codec);
 
+/* ---- per-kernel timing (for benchmarks and profilers) ---- */
+
+/* Kernels whose durations splitzip_profile_read reports, in this order. */
+#define SPLITZIP_KERNEL_PACK 0    /* encode: split, pack, in-tile escape compaction   */
+#define SPLITZIP_KERNEL_SUMS 1    /* encode: segmented sums of per-tile escape counts */
+#define SPLITZIP_KERNEL_PLACE 2   /* encode: escape placement, global chunk offsets   */
+#define SPLITZIP_KERNEL_DECODE 3  /* decode                                            */
+#define SPLITZIP_KERNELS 4
+
+/*
+ * enable != 0: every later encode/decode call on this codec records HIP events around
+ * each of its kernel launches, on the call's stream.  enable == 0 stops recording and
+ * discards accumulated timings.
+ */
+int splitzip_profile(splitzip_codec *codec, int enable);
+
+/*
+ * Wait for `stream`, then report for each kernel kind the mean duration in ms and the
+ * number of launches timed on that stream since profiling was enabled or last reset
+ * (reset != 0 clears the totals after reading).  avg_ms and counts: host arrays of
+ * SPLITZIP_KERNELS entries.
+ */
+int splitzip_profile_read(splitzip_codec *codec, void *stream, double *avg_ms, uint64_t *counts,
+                          int reset);
+
 /* ---- host helpers (no device work) ---- */
 
 /* ceil(n / chunk_size); 0 for an invalid chunk size. */

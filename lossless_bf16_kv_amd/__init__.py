@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
     L.splitzip_encode.argtypes = [vp, u32, P(splitzip_segment), vp]
     L.splitzip_encode_async.argtypes = [vp, u32, P(splitzip_segment), vp, vp]
     L.splitzip_decode.argtypes = [vp, u32, P(splitzip_segment), vp, vp]
+    L.splitzip_profile.argtypes = [vp, i32]
+    L.splitzip_profile_read.argtypes = [vp, vp, P(ctypes.c_double), P(u64), i32]
     L.splitzip_free.argtypes = [vp]
     L.splitzip_free.restype = None
     L.splitzip_chunk_count.argtypes = [u64, u32]
@@ -87,7 +89,7 @@ def lib() -> ctypes.CDLL:
     L.splitzip_last_error.restype = ctypes.c_char_p
     for f in ("splitzip_calibrate", "splitzip_codec_from_codebook", "splitzip_codec_info",
               "splitzip_encode", "splitzip_encode_async", "splitzip_decode",
-              "splitzip_write_header",
+              "splitzip_write_header", "splitzip_profile", "splitzip_profile_read",
               "splitzip_read_header", "splitzip_check_header"):
         getattr(L, f).restype = i32
     _lib = L
@@ -144,6 +146,21 @@ def splitzip_encode_async(codec: int, segs, stream: int, d_result: int) -> None:
 
 def splitzip_decode(codec: int, segs, stream: int = 0, d_error: int = 0) -> None:
     _check(lib().splitzip_decode(codec, len(segs), segs, stream or None, d_error or None))
+
+
+KERNELS = ("encode_pack", "encode_sums", "encode_place", "decode")
+
+
+def splitzip_profile(codec: int, enable: bool) -> None:
+    _check(lib().splitzip_profile(codec, 1 if enable else 0))
+
+
+def splitzip_profile_read(codec: int, stream: int = 0, reset: bool = False) -> dict:
+    """{kernel: (mean ms, launches timed)} for the calls made on `stream`."""
+    avg = (ctypes.c_double * len(KERNELS))()
+    cnt = (ctypes.c_uint64 * len(KERNELS))()
+    _check(lib().splitzip_profile_read(codec, stream or None, avg, cnt, 1 if reset else 0))
+    return {k: (avg[i], int(cnt[i])) for i, k in enumerate(KERNELS)}
 
 
 def splitzip_free(codec: int) -> None:
@@ -281,6 +298,18 @@ class Codec:
     def _stream(self) -> int:
         import torch
         return torch.cuda.current_stream(self.device).cuda_stream
+
+    def profile(self, enable: bool = True) -> None:
+        """Time every kernel launch of later calls with HIP events (see kernel_times)."""
+        self._need_handle()
+        splitzip_profile(self.handle, enable)
+
+    def kernel_times(self, reset: bool = False) -> dict:
+        """{kernel: (mean ms, launches)} over the profiled calls on the current stream."""
+        import torch
+        self._need_handle()
+        with torch.cuda.device(self.device):
+            return splitzip_profile_read(self.handle, self._stream(), reset)
 
     def __del__(self):
         try:

@@ -104,6 +104,13 @@ struct Staging {
     bool used = false;
 };
 
+// Events of one profiled call: kind of the first kernel, then n + 1 events around n kernels.
+struct TimedCall {
+    int first_kind = 0;
+    int n = 0;
+    hipEvent_t ev[4] = {};
+};
+
 // Everything a launch on one stream needs besides the caller's buffers.
 struct Workspace {
     std::mutex mu;
@@ -118,9 +125,19 @@ struct Workspace {
     uint8_t *h_result = nullptr;      // pinned mirror of `result`
     Staging staging[kStagingSlots];
     int next_slot = 0;
+    // profiling
+    std::vector<TimedCall> pending;
+    std::vector<hipEvent_t> spare_events;
+    double sum_ms[SPLITZIP_KERNELS] = {};
+    uint64_t timed[SPLITZIP_KERNELS] = {};
 
     ~Workspace()
     {
+        for (TimedCall &c : pending)
+            for (int i = 0; i <= c.n; ++i)
+                (void)hipEventDestroy(c.ev[i]);
+        for (hipEvent_t e : spare_events)
+            (void)hipEventDestroy(e);
         (void)hipFree(scratch);
         (void)hipFree(ovf_next);
         (void)hipFree(result);
@@ -141,6 +158,7 @@ struct Workspace {
 struct splitzip_codec {
     uint32_t magic = kCodecMagic;
     int device = 0;
+    bool profiling = false;
     uint32_t chunk_size = 0;
     uint32_t log2_chunk = 0;
     uint8_t cb[16] = {};
@@ -212,6 +230,84 @@ int get_workspace(splitzip_codec *c, hipStream_t stream, Workspace **out)
     c->ws.emplace(stream, std::move(w));
     return SPLITZIP_OK;
 }
+
+// ---- profiling: events around each launch, resolved into per-kernel totals ----------
+
+hipEvent_t take_event(Workspace *w)
+{
+    if (!w->spare_events.empty()) {
+        hipEvent_t e = w->spare_events.back();
+        w->spare_events.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess)
+        return nullptr;
+    return e;
+}
+
+// Fold finished calls into the totals (all of them when `wait`).
+void resolve_timings(Workspace *w, bool wait)
+{
+    size_t done = 0;
+    for (; done < w->pending.size(); ++done) {
+        TimedCall &c = w->pending[done];
+        if (wait)
+            (void)hipEventSynchronize(c.ev[c.n]);
+        else if (hipEventQuery(c.ev[c.n]) != hipSuccess)
+            break;
+        for (int i = 0; i < c.n; ++i) {
+            float ms = 0.f;
+            if (hipEventElapsedTime(&ms, c.ev[i], c.ev[i + 1]) == hipSuccess) {
+                w->sum_ms[c.first_kind + i] += ms;
+                w->timed[c.first_kind + i] += 1;
+            }
+        }
+        for (int i = 0; i <= c.n; ++i)
+            w->spare_events.push_back(c.ev[i]);
+    }
+    w->pending.erase(w->pending.begin(), w->pending.begin() + done);
+}
+
+// Starts a profiled call of n kernels (no-op when profiling is off or events run out).
+struct CallTimer {
+    Workspace *w = nullptr;
+    TimedCall call;
+    int recorded = 0;
+    hipStream_t stream = nullptr;
+    CallTimer(splitzip_codec *c, Workspace *ws, hipStream_t s, int first_kind, int n)
+    {
+        if (!c->profiling || !ws)
+            return;
+        resolve_timings(ws, false);
+        call.first_kind = first_kind;
+        call.n = n;
+        for (int i = 0; i <= n; ++i)
+            if (!(call.ev[i] = take_event(ws))) {
+                for (int k = 0; k < i; ++k)
+                    ws->spare_events.push_back(call.ev[k]);
+                return;
+            }
+        w = ws;
+        stream = s;
+    }
+    void mark()   // after each launch, and once before the first
+    {
+        if (w && recorded <= call.n)
+            (void)hipEventRecord(call.ev[recorded++], stream);
+    }
+    ~CallTimer()
+    {
+        if (!w)
+            return;
+        if (recorded == call.n + 1) {
+            w->pending.push_back(call);
+        } else {
+            for (int i = 0; i <= call.n; ++i)
+                w->spare_events.push_back(call.ev[i]);
+        }
+    }
+};
 
 // Byte offsets of the encode scratch arrays for one launch.
 struct EncodeScratch {
@@ -499,7 +595,15 @@ int encode_launch(splitzip_codec *codec, uint32_t n_seg, const splitzip_segment 
     a.n_seg = n_seg;
     a.n_tiles = n_tiles;
     a.log2_chunk = codec->log2_chunk;
-    hipError_t e = sz::launch_encode(a, stream);
+    hipError_t e = hipSuccess;
+    {
+        CallTimer timer(codec, w, stream, SPLITZIP_KERNEL_PACK, sz::kEncodeStages);
+        timer.mark();
+        for (int stage = 0; stage < sz::kEncodeStages && e == hipSuccess; ++stage) {
+            e = sz::launch_encode_stage(stage, a, stream);
+            timer.mark();
+        }
+    }
     if (e != hipSuccess) {
         // a launch that did not run to its end may leave the overflow counter set
         (void)hipMemsetAsync(w->ovf_next, 0, sizeof(unsigned long long), stream);
@@ -607,23 +711,88 @@ int splitzip_decode(splitzip_codec *codec, uint32_t n_seg, const splitzip_segmen
 
     sz::DecodeArgs a{};
     a.seg0 = desc[0];
-    if (n_seg > 1) {
-        Workspace *w = nullptr;
+    Workspace *w = nullptr;
+    std::unique_lock<std::mutex> lock;
+    if (n_seg > 1 || codec->profiling) {
         rc = get_workspace(codec, stream, &w);
         if (rc != SPLITZIP_OK)
             return rc;
-        std::lock_guard<std::mutex> lock(w->mu);
-        if ((rc = stage_descriptors(w, desc, tiles, &a.segs, &a.tile_start)) != SPLITZIP_OK)
-            return rc;
+        lock = std::unique_lock<std::mutex>(w->mu);
     }
+    if (n_seg > 1 && (rc = stage_descriptors(w, desc, tiles, &a.segs, &a.tile_start)) != SPLITZIP_OK)
+        return rc;
     std::memcpy(a.cb, codec->cb, 16);
     a.err = d_error;
     a.n_seg = n_seg;
     a.n_tiles = tiles[n_seg];
     a.log2_chunk = codec->log2_chunk;
-    hipError_t e = sz::launch_decode(a, stream);
+    hipError_t e;
+    {
+        CallTimer timer(codec, w, stream, SPLITZIP_KERNEL_DECODE, 1);
+        timer.mark();
+        e = sz::launch_decode(a, stream);
+        timer.mark();
+    }
     if (e != hipSuccess)
         return fail_hip(e, "decode launch");
+    return SPLITZIP_OK;
+}
+
+int splitzip_profile(splitzip_codec *codec, int enable)
+{
+    g_last_error.clear();
+    int rc = codec_check(codec);
+    if (rc != SPLITZIP_OK)
+        return rc;
+    DeviceGuard dg(codec->device);
+    std::vector<Workspace *> all;
+    {
+        // workspace locks are taken without the codec lock held (calls hold them the other
+        // way round)
+        std::lock_guard<std::mutex> lock(codec->mu);
+        codec->profiling = enable != 0;
+        for (auto &kv : codec->ws)
+            all.push_back(kv.second.get());
+    }
+    if (!enable) {
+        for (Workspace *w : all) {
+            std::lock_guard<std::mutex> wl(w->mu);
+            resolve_timings(w, true);
+            std::fill(w->sum_ms, w->sum_ms + SPLITZIP_KERNELS, 0.0);
+            std::fill(w->timed, w->timed + SPLITZIP_KERNELS, 0);
+        }
+    }
+    return SPLITZIP_OK;
+}
+
+int splitzip_profile_read(splitzip_codec *codec, void *stream_, double *avg_ms, uint64_t *counts,
+                          int reset)
+{
+    g_last_error.clear();
+    int rc = codec_check(codec);
+    if (rc != SPLITZIP_OK)
+        return rc;
+    if (!avg_ms || !counts)
+        return fail(SPLITZIP_E_INVALID, "avg_ms or counts is NULL");
+    DeviceGuard dg(codec->device);
+    if (dg.err != hipSuccess)
+        return fail_hip(dg.err, "hipSetDevice");
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    Workspace *w = nullptr;
+    rc = get_workspace(codec, stream, &w);
+    if (rc != SPLITZIP_OK)
+        return rc;
+    std::lock_guard<std::mutex> lock(w->mu);
+    SZ_HIP(hipStreamSynchronize(stream), "hipStreamSynchronize");
+    resolve_timings(w, true);
+    for (int k = 0; k < SPLITZIP_KERNELS; ++k) {
+        counts[k] = w->timed[k];
+        avg_ms[k] = w->timed[k] ? w->sum_ms[k] / (double)w->timed[k] : 0.0;
+        if (reset) {
+            w->sum_ms[k] = 0.0;
+            w->timed[k] = 0;
+        }
+    }
     return SPLITZIP_OK;
 }
 

@@ -9,13 +9,13 @@ namespace sz {
 
 // ---- tiling -------------------------------------------------------------------------
 // A workgroup is 4 wave64s.  Each lane owns k*Groups groups of 8 consecutive words (one
-// 16-byte load each); wave w's groups cover 64 * 8 * k*Groups consecutive words.  An
-// encode tile is 8192 words (16 KiB of BF16), a decode tile 16384 words.
+// 16-byte load each); wave w's groups cover 64 * 8 * k*Groups consecutive words.  Encode
+// and decode tiles are 16384 words (32 KiB of BF16).
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kGroupWords = 8;
-constexpr int kEncGroups = 4;
-constexpr int kEncTileShift = 13;
+constexpr int kEncGroups = 8;
+constexpr int kEncTileShift = 14;
 constexpr int kEncTileWords = 1 << kEncTileShift;
 constexpr int kDecGroups = 8;
 constexpr int kDecTileShift = 14;
@@ -30,7 +30,7 @@ constexpr uint8_t kEscapeEntry = 0x10;
 // Each tile's escapes are first written compacted to a slot of kSlotEscapes entries (or, if
 // more, to an overflow area) as (position inside the tile | exponent << 16), then moved to
 // their final place once the tile's escape offset is known.
-constexpr uint32_t kSlotEscapes = 32;
+constexpr uint32_t kSlotEscapes = 64;
 constexpr uint32_t kSumTiles = 2048;          // tiles per segmented-sum block
 constexpr uint32_t kPlaceTiles = kThreads;    // tiles per placement workgroup (one per thread)
 constexpr uint64_t kMaxSegmentWords = 1ull << 38;
@@ -91,7 +91,9 @@ constexpr int kCalibBlocksMax = 1024;
 hipError_t launch_calibrate(const uint16_t *d_x, uint64_t n, uint32_t *d_partial,
                             uint32_t n_blocks, uint64_t *d_hist, hipStream_t stream);
 uint32_t calibrate_blocks(uint64_t n);
-hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream);
+// Encode stages, launched in order 0 (pack), 1 (sums), 2 (place) on one stream.
+constexpr int kEncodeStages = 3;
+hipError_t launch_encode_stage(int stage, const EncodeArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 
 }  // namespace sz

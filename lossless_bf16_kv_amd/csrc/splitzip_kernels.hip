@@ -23,6 +23,28 @@
 
 namespace sz {
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming accesses of the pack kernel: every byte is touched once, so the loads and stores
+// carry the nontemporal hint and do not displace other data in the caches.
+__device__ __forceinline__ uint4 load_stream16(const uint16_t *p)
+{
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+__device__ __forceinline__ void store_stream8(uint8_t *p, uint32_t lo, uint32_t hi)
+{
+    const u32x2 t = {lo, hi};
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x2 *>(p));
+}
+
+__device__ __forceinline__ void store_stream4(uint8_t *p, uint32_t x)
+{
+    __builtin_nontemporal_store(x, reinterpret_cast<uint32_t *>(p));
+}
+
 // ---- small wave64 helpers -------------------------------------------------------------
 
 __device__ __forceinline__ uint32_t lane_id()
@@ -250,7 +272,7 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
     for (int j = 0; j < kEncGroups; ++j) {
         g0[j] = base + (uint64_t)(((wave * kEncGroups + j) << 6) + lane) * kGroupWords;
         if (g0[j] + kGroupWords <= n) {
-            v[j] = *reinterpret_cast<const uint4 *>(sd.data + g0[j]);
+            v[j] = load_stream16(sd.data + g0[j]);
         } else {
             uint16_t wds[8];
 #pragma unroll
@@ -270,8 +292,8 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
         uint32_t sm_lo, sm_hi, codes, fl;
         split_group(v[j], s_lut, sm_lo, sm_hi, codes, fl);
         if (g0[j] + kGroupWords <= n) {
-            *reinterpret_cast<uint2 *>(sd.sm + g0[j]) = make_uint2(sm_lo, sm_hi);
-            *reinterpret_cast<uint32_t *>(sd.codes + (g0[j] >> 1)) = codes;
+            store_stream8(sd.sm + g0[j], sm_lo, sm_hi);
+            store_stream4(sd.codes + (g0[j] >> 1), codes);
         } else {
             const uint32_t nv = g0[j] < n ? (uint32_t)(n - g0[j]) : 0u;
             codes &= codes_keep(nv);
@@ -414,6 +436,22 @@ __device__ uint32_t block_max_u32(uint32_t x, uint32_t tid, uint32_t lane, uint3
     return m;
 }
 
+constexpr uint64_t kFromOverflow = 1ull << 63;
+
+// Inclusive prefix sum over the 256 threads of the workgroup (thread order).
+__device__ uint32_t block_inclusive_sum_u32(uint32_t x, uint32_t tid, uint32_t lane, uint32_t *s_red)
+{
+    x = wave_inclusive_sum(x, lane);
+    if (lane == 63)
+        s_red[tid >> 6] = x;
+    __syncthreads();
+    uint32_t carry = 0;
+    for (uint32_t w = 0; w < (tid >> 6); ++w)
+        carry += s_red[w];
+    __syncthreads();
+    return carry + x;
+}
+
 __device__ uint64_t block_sum_u64(uint64_t x, uint32_t tid, uint32_t lane, uint64_t *s_red)
 {
     x = wave_total_u64(x, lane);
@@ -463,13 +501,14 @@ __global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs
     __shared__ SegSum s_wave[kWaves + 1];
     __shared__ uint32_t s_red32[kWaves];
     __shared__ uint64_t s_red64[kWaves];
-    __shared__ uint64_t s_prefix[kPlaceTiles];
-    __shared__ uint32_t s_count[kPlaceTiles];
+    __shared__ uint64_t s_prefix[kPlaceTiles];   // escape offset of each tile in its segment
+    __shared__ uint64_t s_base[kPlaceTiles];     // first word of each tile in its segment
+    __shared__ uint64_t s_src[kPlaceTiles];      // slot index, or overflow offset | kFromOverflow
     __shared__ uint32_t s_seg[kPlaceTiles];
+    __shared__ uint32_t s_first[kPlaceTiles + 1];
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = lane_id();
-    const uint32_t wave = tid >> 6;
     const uint32_t u_first = blockIdx.x * kPlaceTiles;
     const uint32_t sum_block = u_first / kSumTiles;
 
@@ -510,65 +549,85 @@ __global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs
     const SegSum incl = block_seg_scan(SegSum{head, count}, tid, lane, s_wave);
     const SegSum with_carry = seg_combine(before, incl);
     const uint64_t prefix = head ? 0 : with_carry.v - count;
-    s_prefix[tid] = prefix;
-    s_count[tid] = count;
-    s_seg[tid] = seg;
-    if (valid && u + 1 == segment_end_tile(a, seg)) {
-        // the segment's last tile knows the segment's escape count
-        const SegDesc sd = segment_desc(a, seg);
-        const uint64_t E = prefix + count;
-        const uint64_t n_chunks = (sd.n + (1ull << a.log2_chunk) - 1) >> a.log2_chunk;
-        sd.chunk_off[n_chunks] = E;
-        a.seg_escapes[seg] = E;
-    }
-    __syncthreads();
-
-    // one wave per tile: move the escapes, make the tile's chunk offsets global
     const uint64_t cmask = (1ull << a.log2_chunk) - 1;
-    const uint32_t n_here = a.n_tiles - u_first < kPlaceTiles ? a.n_tiles - u_first : kPlaceTiles;
-    for (uint32_t i = wave; i < n_here; i += kWaves) {
-        const uint32_t ut = u_first + i;
-        const uint32_t sg = s_seg[i];
-        const SegDesc sd = segment_desc(a, sg);
-        const uint64_t base = (uint64_t)(ut - segment_first_tile(a, sg)) << kEncTileShift;
-        if (base >= sd.n)
-            continue;                                   // empty segment
-        const uint64_t pre = s_prefix[i];
-        const uint32_t cnt = s_count[i];
-        const uint32_t *src = a.slots + (uint64_t)ut * kSlotEscapes;
-        uint64_t room = cnt;
-        if (cnt > kSlotEscapes) {
-            const uint64_t off = a.tile_ovf[ut];
-            src = a.ovf + off;
-            room = off < a.ovf_cap ? a.ovf_cap - off : 0;
+    uint64_t base = 0;
+    if (valid) {
+        const SegDesc sd = segment_desc(a, seg);
+        base = (uint64_t)(u - segment_first_tile(a, seg)) << kEncTileShift;
+        if (u + 1 == segment_end_tile(a, seg)) {
+            // the segment's last tile knows the segment's escape count
+            const uint64_t E = prefix + count;
+            sd.chunk_off[(sd.n + cmask) >> a.log2_chunk] = E;
+            a.seg_escapes[seg] = E;
         }
-        for (uint32_t r = lane; r < cnt; r += 64) {
-            const uint64_t d = pre + r;
-            if (r < room && d < sd.esc) {
-                const uint32_t e = src[r];
-                sd.esc_pos[d] = (uint16_t)((base + (e & 0xFFFFu)) & cmask);
-                sd.esc_exp[d] = (uint8_t)(e >> 16);
-            }
+        // chunks that start inside this tile: tile-local offsets become segment offsets
+        if (base < sd.n) {
+            const uint64_t words = sd.n - base < (uint64_t)kEncTileWords ? sd.n - base : (uint64_t)kEncTileWords;
+            const uint64_t c_end = (base + words + cmask) >> a.log2_chunk;
+            for (uint64_t c = (base + cmask) >> a.log2_chunk; c < c_end; ++c)
+                sd.chunk_off[c] += prefix;
         }
-        // chunks that start inside this tile
-        const uint64_t valid_words = sd.n - base < (uint64_t)kEncTileWords ? sd.n - base : (uint64_t)kEncTileWords;
-        const uint64_t c_first = (base + cmask) >> a.log2_chunk;
-        const uint64_t c_end = (base + valid_words + cmask) >> a.log2_chunk;
-        for (uint64_t c = c_first + lane; c < c_end; c += 64)
-            sd.chunk_off[c] += pre;
+    }
+    s_prefix[tid] = prefix;
+    s_base[tid] = base;
+    s_seg[tid] = seg;
+    s_src[tid] = count > kSlotEscapes ? (a.tile_ovf[u] | kFromOverflow) : (uint64_t)u * kSlotEscapes;
+
+    // exclusive scan of the counts inside the workgroup: escape j of the workgroup belongs to
+    // the tile i with s_first[i] <= j < s_first[i + 1]
+    const uint32_t inc = block_inclusive_sum_u32(count, tid, lane, s_red32);
+    s_first[tid + 1] = inc;
+    if (tid == 0)
+        s_first[0] = 0;
+    __syncthreads();
+    const uint32_t total = s_first[kPlaceTiles];
+
+    // move the escapes: consecutive threads take consecutive escapes (coalesced reads of the
+    // scratch entries, coalesced writes of the final arrays)
+    SegDesc sd = a.seg0;
+    for (uint32_t j = tid; j < total; j += kThreads) {
+        uint32_t lo = 0, hi = kPlaceTiles;          // s_first[lo] <= j < s_first[hi]
+        while (hi - lo > 1) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (s_first[mid] <= j)
+                lo = mid;
+            else
+                hi = mid;
+        }
+        const uint32_t r = j - s_first[lo];
+        const uint64_t src = s_src[lo];
+        uint32_t e;
+        if (src & kFromOverflow) {
+            const uint64_t off = (src & ~kFromOverflow) + r;
+            if (off >= a.ovf_cap)
+                continue;
+            e = a.ovf[off];
+        } else {
+            e = a.slots[src + r];
+        }
+        if (a.n_seg > 1)
+            sd = a.segs[s_seg[lo]];
+        const uint64_t d = s_prefix[lo] + r;
+        if (d < sd.esc) {
+            sd.esc_pos[d] = (uint16_t)((s_base[lo] + (e & 0xFFFFu)) & cmask);
+            sd.esc_exp[d] = (uint8_t)(e >> 16);
+        }
     }
 }
 
-hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream)
+hipError_t launch_encode_stage(int stage, const EncodeArgs &a, hipStream_t stream)
 {
-    encode_pack_kernel<<<a.n_tiles, kThreads, 0, stream>>>(a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    encode_sums_kernel<<<(a.n_tiles + kSumTiles - 1) / kSumTiles, kThreads, 0, stream>>>(a);
-    if ((e = hipGetLastError()) != hipSuccess)
-        return e;
-    encode_place_kernel<<<(a.n_tiles + kPlaceTiles - 1) / kPlaceTiles, kThreads, 0, stream>>>(a);
+    switch (stage) {
+    case 0:
+        encode_pack_kernel<<<a.n_tiles, kThreads, 0, stream>>>(a);
+        break;
+    case 1:
+        encode_sums_kernel<<<(a.n_tiles + kSumTiles - 1) / kSumTiles, kThreads, 0, stream>>>(a);
+        break;
+    default:
+        encode_place_kernel<<<(a.n_tiles + kPlaceTiles - 1) / kPlaceTiles, kThreads, 0, stream>>>(a);
+        break;
+    }
     return hipGetLastError();
 }
 
