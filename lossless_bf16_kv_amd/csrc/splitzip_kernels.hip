@@ -143,15 +143,28 @@ __global__ __launch_bounds__(kThreads) void calib_hist_kernel(const uint16_t *__
     }
 }
 
-__global__ __launch_bounds__(256) void calib_reduce_kernel(const uint32_t *__restrict__ partial,
-                                                           uint32_t blocks,
-                                                           uint64_t *__restrict__ hist)
+// One workgroup per exponent value: its threads add up that bin over the partial histograms.
+__global__ __launch_bounds__(kThreads) void calib_reduce_kernel(const uint32_t *__restrict__ partial,
+                                                                uint32_t blocks,
+                                                                uint64_t *__restrict__ hist)
 {
-    const uint32_t e = threadIdx.x;
+    __shared__ uint64_t s_wave[kWaves];
+    const uint32_t e = blockIdx.x;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = lane_id();
     uint64_t s = 0;
-    for (uint32_t b = 0; b < blocks; ++b)
+    for (uint32_t b = tid; b < blocks; b += kThreads)
         s += partial[(uint64_t)b * 256 + e];
-    hist[e] = s;
+    s = wave_total_u64(s, lane);
+    if (lane == 0)
+        s_wave[tid >> 6] = s;
+    __syncthreads();
+    if (tid == 0) {
+        uint64_t t = 0;
+        for (int w = 0; w < kWaves; ++w)
+            t += s_wave[w];
+        hist[e] = t;
+    }
 }
 
 uint32_t calibrate_blocks(uint64_t n)
@@ -172,7 +185,7 @@ hipError_t launch_calibrate(const uint16_t *d_x, uint64_t n, uint32_t *d_partial
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    calib_reduce_kernel<<<1, 256, 0, stream>>>(d_partial, n_blocks, d_hist);
+    calib_reduce_kernel<<<256, kThreads, 0, stream>>>(d_partial, n_blocks, d_hist);
     return hipGetLastError();
 }
 

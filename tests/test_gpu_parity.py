@@ -327,3 +327,43 @@ def test_config5_ragged_batch():
     ys = codec.decode_batch(encs)                  # one launch
     for xd, y in zip(xds, ys):
         assert torch.equal(y, xd)
+
+
+# ---- non-blocking encode, per-kernel timing ----------------------------------------------------
+
+def test_async_encode_matches_blocking_and_reports_capacity():
+    xs_np = [workloads.mixed_words(n, 200 + n, wide_fraction=0.05) for n in (3 * 16384 + 11, 70000, 0, 5)]
+    codec = codec_for(workloads.normal_words(30000, 8), 1024)
+    xs = [dev(x) for x in xs_np]
+    ref = codec.encode_batch(xs)
+    encs = [codec.empty_encoded(e.n, escape_capacity=max(e.n_escapes, 1)) for e in ref]
+    result = torch.zeros(1 + len(xs), dtype=torch.int64, device=DEV)
+    codec.encode_into_async(xs, encs, result)
+    torch.cuda.synchronize()
+    assert codec.finish_async(encs, result) == sz.OK
+    for x, e, r in zip(xs_np, encs, ref):
+        assert e.n_escapes == r.n_escapes and e.to_bytes(codec) == r.to_bytes(codec)
+        assert_same_stream(codec, e, x)
+    # too little room: reported after the fact, counts still exact
+    small = [codec.empty_encoded(e.n, escape_capacity=1) for e in ref]
+    result.zero_()
+    codec.encode_into_async(xs, small, result)
+    torch.cuda.synchronize()
+    assert codec.finish_async(small, result) == sz.E_CAPACITY
+    assert [e.n_escapes for e in small] == [e.n_escapes for e in ref]
+
+
+def test_kernel_timing():
+    x = dev(workloads.normal_words(5 * 16384, 9))
+    codec = codec_for(workloads.normal_words(30000, 10), 1024)
+    codec.profile(True)
+    for _ in range(3):
+        codec.decode(codec.encode(x))
+    times = codec.kernel_times(reset=True)
+    assert set(times) == {"encode_pack", "encode_sums", "encode_place", "decode"}
+    for k, (ms, count) in times.items():
+        assert count == 3 and ms > 0, k
+    assert all(c == 0 for _, c in codec.kernel_times().values())
+    codec.profile(False)
+    codec.decode(codec.encode(x))
+    assert all(c == 0 for _, c in codec.kernel_times().values())
