@@ -152,11 +152,12 @@ void splitzip_free(splitzip_codec *codec);
 /* ---- per-kernel timing (for benchmarks and profilers) ---- */
 
 /* Kernels whose durations splitzip_profile_read reports, in this order. */
-#define SPLITZIP_KERNEL_PACK 0    /* encode: split, pack, in-tile escape compaction   */
-#define SPLITZIP_KERNEL_SUMS 1    /* encode: segmented sums of per-tile escape counts */
-#define SPLITZIP_KERNEL_PLACE 2   /* encode: escape placement, global chunk offsets   */
-#define SPLITZIP_KERNEL_DECODE 3  /* decode                                            */
-#define SPLITZIP_KERNELS 4
+#define SPLITZIP_KERNEL_PACK 0    /* encode: split, pack, in-tile escape compaction      */
+#define SPLITZIP_KERNEL_SUMS 1    /* encode: segmented sums of per-tile escape counts    */
+#define SPLITZIP_KERNEL_PLACE 2   /* encode: escape placement, global chunk offsets      */
+#define SPLITZIP_KERNEL_SPILL 3   /* encode: placement of escape-heavy tiles' escapes    */
+#define SPLITZIP_KERNEL_DECODE 4  /* decode                                               */
+#define SPLITZIP_KERNELS 5
 
 /*
  * enable != 0: every later encode/decode call on this codec records HIP events around

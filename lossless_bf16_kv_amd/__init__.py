@@ -148,7 +148,7 @@ def splitzip_decode(codec: int, segs, stream: int = 0, d_error: int = 0) -> None
     _check(lib().splitzip_decode(codec, len(segs), segs, stream or None, d_error or None))
 
 
-KERNELS = ("encode_pack", "encode_sums", "encode_place", "decode")
+KERNELS = ("encode_pack", "encode_sums", "encode_place", "encode_spill", "decode")
 
 
 def splitzip_profile(codec: int, enable: bool) -> None:
@@ -400,6 +400,11 @@ class Codec:
             raise SplitZipError(E_DEVICE, f"encode kernel reported error bits {r[0]:#x}")
         return st
 
+    def prepare(self, xs, encs, outs=None) -> "PreparedBatch":
+        """Fix the tensors of a batch once (inputs, their Encoded sections, optional decode
+        outputs) so that repeated encode/decode calls skip the per-call argument marshalling."""
+        return PreparedBatch(self, xs, encs, outs)
+
     def encode(self, x, escape_capacity: int | None = None) -> Encoded:
         return self.encode_batch([x], escape_capacity)[0]
 
@@ -465,3 +470,49 @@ class Codec:
         enc.n_escapes = E
         enc.compressed_bytes = len(buf)
         return self.decode(enc)
+
+
+class PreparedBatch:
+    """A batch whose device buffers stay fixed across calls (e.g. one serving step after
+    another): the segment descriptors are built once."""
+
+    def __init__(self, codec: Codec, xs, encs, outs=None):
+        import torch
+        if len(xs) != len(encs) or (outs is not None and len(outs) != len(xs)):
+            raise ValueError("xs, encs and outs must have the same length")
+        self.codec = codec
+        self.xs, self.encs, self.outs = list(xs), list(encs), (list(outs) if outs is not None else None)
+        self._enc = (splitzip_segment * len(xs))()
+        for i, (x, e) in enumerate(zip(self.xs, self.encs)):
+            w = _words(x, codec.device)
+            if w.numel() != e.n:
+                raise ValueError("tensor size differs from the preallocated sections")
+            self._enc[i] = e.segment(w.data_ptr() if w.numel() else 0)
+        self._dec = None
+        if self.outs is not None:
+            self._dec = (splitzip_segment * len(xs))()
+            for i, (y, e) in enumerate(zip(self.outs, self.encs)):
+                w = _words(y, codec.device)
+                if w.numel() != e.n:
+                    raise ValueError("output size differs from the encoded tensor")
+                self._dec[i] = e.segment(w.data_ptr() if w.numel() else 0)
+        self._torch = torch
+
+    def encode_async(self, result) -> None:
+        """Enqueue the encode; see Codec.encode_into_async and Codec.finish_async."""
+        with self._torch.cuda.device(self.codec.device):
+            splitzip_encode_async(self.codec.handle, self._enc, self.codec._stream(), result.data_ptr())
+
+    def finish(self, result) -> int:
+        st = self.codec.finish_async(self.encs, result)
+        if self._dec is not None:
+            for i, e in enumerate(self.encs):
+                self._dec[i].n_escapes = e.n_escapes
+        return st
+
+    def decode(self, d_error: int = 0) -> None:
+        """Enqueue the decode of the batch into its outputs (n_escapes as of the last finish)."""
+        if self._dec is None:
+            raise ValueError("no decode outputs were given")
+        with self._torch.cuda.device(self.codec.device):
+            splitzip_decode(self.codec.handle, self._dec, self.codec._stream(), d_error)

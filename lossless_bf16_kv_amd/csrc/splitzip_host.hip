@@ -108,7 +108,7 @@ struct Staging {
 struct TimedCall {
     int first_kind = 0;
     int n = 0;
-    hipEvent_t ev[4] = {};
+    hipEvent_t ev[SPLITZIP_KERNELS] = {};
 };
 
 // Everything a launch on one stream needs besides the caller's buffers.
@@ -118,7 +118,7 @@ struct Workspace {
     // device
     uint8_t *scratch = nullptr;       // encode scratch (see EncodeScratch)
     uint64_t scratch_cap = 0;         // bytes
-    unsigned long long *ovf_next = nullptr;
+    unsigned long long *ovf_ctr = nullptr;   // [2], see EncodeArgs
     uint8_t *result = nullptr;        // [err u32, pad u32, seg_escapes u64 * result_cap]
     uint32_t result_cap = 0;
     // host
@@ -139,7 +139,7 @@ struct Workspace {
         for (hipEvent_t e : spare_events)
             (void)hipEventDestroy(e);
         (void)hipFree(scratch);
-        (void)hipFree(ovf_next);
+        (void)hipFree(ovf_ctr);
         (void)hipFree(result);
         (void)hipHostFree(h_result);
         for (Staging &s : staging) {
@@ -311,13 +311,15 @@ struct CallTimer {
 
 // Byte offsets of the encode scratch arrays for one launch.
 struct EncodeScratch {
-    uint64_t tile_count, tile_ovf, slots, block_sum, ovf, total;
+    uint64_t tile_count, tile_ovf, tile_prefix, ovf_tiles, slots, block_sum, ovf, total;
     EncodeScratch(uint64_t n_tiles, uint64_t ovf_cap)
     {
         auto up = [](uint64_t x) { return (x + 255) & ~uint64_t(255); };
         tile_count = 0;
         tile_ovf = up(tile_count + 4 * n_tiles);
-        slots = up(tile_ovf + 8 * n_tiles);
+        tile_prefix = up(tile_ovf + 8 * n_tiles);
+        ovf_tiles = up(tile_prefix + 8 * n_tiles);
+        slots = up(ovf_tiles + 4 * n_tiles);
         block_sum = up(slots + 4 * (uint64_t)sz::kSlotEscapes * n_tiles);
         ovf = up(block_sum + 8 * ((n_tiles + sz::kSumTiles - 1) / sz::kSumTiles));
         total = up(ovf + 4 * ovf_cap);
@@ -326,9 +328,9 @@ struct EncodeScratch {
 
 int ensure_scratch(Workspace *w, uint64_t bytes)
 {
-    if (!w->ovf_next) {
-        SZ_HIP(hipMalloc(&w->ovf_next, sizeof(unsigned long long)), "hipMalloc(overflow counter)");
-        SZ_HIP(hipMemsetAsync(w->ovf_next, 0, sizeof(unsigned long long), w->stream), "hipMemsetAsync(counter)");
+    if (!w->ovf_ctr) {
+        SZ_HIP(hipMalloc(&w->ovf_ctr, 2 * sizeof(unsigned long long)), "hipMalloc(overflow counter)");
+        SZ_HIP(hipMemsetAsync(w->ovf_ctr, 0, 2 * sizeof(unsigned long long), w->stream), "hipMemsetAsync(counter)");
     }
     if (w->scratch_cap >= bytes)
         return SPLITZIP_OK;
@@ -585,10 +587,12 @@ int encode_launch(splitzip_codec *codec, uint32_t n_seg, const splitzip_segment 
     a.lut = codec->d_lut;
     a.tile_count = reinterpret_cast<uint32_t *>(w->scratch + lay.tile_count);
     a.tile_ovf = reinterpret_cast<uint64_t *>(w->scratch + lay.tile_ovf);
+    a.tile_prefix = reinterpret_cast<uint64_t *>(w->scratch + lay.tile_prefix);
+    a.ovf_tiles = reinterpret_cast<uint32_t *>(w->scratch + lay.ovf_tiles);
     a.slots = reinterpret_cast<uint32_t *>(w->scratch + lay.slots);
     a.block_sum = reinterpret_cast<uint64_t *>(w->scratch + lay.block_sum);
     a.ovf = reinterpret_cast<uint32_t *>(w->scratch + lay.ovf);
-    a.ovf_next = w->ovf_next;
+    a.ovf_ctr = w->ovf_ctr;
     a.ovf_cap = ovf_cap;
     a.err = reinterpret_cast<uint32_t *>(res);
     a.seg_escapes = reinterpret_cast<uint64_t *>(res + 8);
@@ -606,7 +610,7 @@ int encode_launch(splitzip_codec *codec, uint32_t n_seg, const splitzip_segment 
     }
     if (e != hipSuccess) {
         // a launch that did not run to its end may leave the overflow counter set
-        (void)hipMemsetAsync(w->ovf_next, 0, sizeof(unsigned long long), stream);
+        (void)hipMemsetAsync(w->ovf_ctr, 0, 2 * sizeof(unsigned long long), stream);
         return fail_hip(e, "encode launch");
     }
     *out_ws = w;

@@ -9,16 +9,16 @@ namespace sz {
 
 // ---- tiling -------------------------------------------------------------------------
 // A workgroup is 4 wave64s.  Each lane owns k*Groups groups of 8 consecutive words (one
-// 16-byte load each); wave w's groups cover 64 * 8 * k*Groups consecutive words.  Encode
-// and decode tiles are 16384 words (32 KiB of BF16).
+// 16-byte load each); wave w's groups cover 64 * 8 * k*Groups consecutive words.  An encode
+// tile is 16384 words (32 KiB of BF16), a decode tile 8192 words.
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kGroupWords = 8;
 constexpr int kEncGroups = 8;
 constexpr int kEncTileShift = 14;
 constexpr int kEncTileWords = 1 << kEncTileShift;
-constexpr int kDecGroups = 8;
-constexpr int kDecTileShift = 14;
+constexpr int kDecGroups = 4;
+constexpr int kDecTileShift = 13;
 constexpr int kDecTileWords = 1 << kDecTileShift;
 static_assert(kThreads * kEncGroups * kGroupWords == kEncTileWords, "encode tile geometry");
 static_assert(kThreads * kDecGroups * kGroupWords == kDecTileWords, "decode tile geometry");
@@ -32,7 +32,11 @@ constexpr uint8_t kEscapeEntry = 0x10;
 // their final place once the tile's escape offset is known.
 constexpr uint32_t kSlotEscapes = 64;
 constexpr uint32_t kSumTiles = 2048;          // tiles per segmented-sum block
-constexpr uint32_t kPlaceTiles = kThreads;    // tiles per placement workgroup (one per thread)
+constexpr uint32_t kPlaceTiles = 64;          // tiles per placement workgroup
+constexpr uint32_t kSpillBlocks = 1024;       // workgroups moving the overflow tiles' escapes
+// overflow counter: escapes reserved so far (low 40 bits) and overflow tiles listed (high 24)
+constexpr int kOvfTileShift = 40;
+constexpr uint64_t kOvfOffsetMask = (1ull << kOvfTileShift) - 1;
 constexpr uint64_t kMaxSegmentWords = 1ull << 38;
 static_assert(kEncTileWords <= 65536, "in-tile positions must fit 16 bits");
 static_assert(kSumTiles % kThreads == 0 && kSumTiles % kPlaceTiles == 0, "sum blocks");
@@ -60,9 +64,12 @@ struct EncodeArgs {
     const uint8_t *lut;           // device [256] inverse LUT (code, or kEscapeEntry)
     uint32_t *tile_count;         // [n_tiles] escapes per tile
     uint64_t *tile_ovf;           // [n_tiles] overflow offset of tiles past kSlotEscapes
+    uint64_t *tile_prefix;        // [n_tiles] escape offset in the segment (overflow tiles)
+    uint32_t *ovf_tiles;          // [n_tiles] list of the overflow tiles
     uint32_t *slots;              // [n_tiles * kSlotEscapes]
     uint32_t *ovf;                // [ovf_cap]
-    unsigned long long *ovf_next; // overflow bump counter, 0 between encodes
+    unsigned long long *ovf_ctr;  // [2]: running overflow counter (0 between encodes), and
+                                  // its final value saved by the sums launch
     uint64_t ovf_cap;
     uint64_t *block_sum;          // [ceil(n_tiles / kSumTiles)] segmented sums, bit 63 = head
     uint64_t *seg_escapes;        // [n_seg] OUT: E per segment
@@ -91,8 +98,8 @@ constexpr int kCalibBlocksMax = 1024;
 hipError_t launch_calibrate(const uint16_t *d_x, uint64_t n, uint32_t *d_partial,
                             uint32_t n_blocks, uint64_t *d_hist, hipStream_t stream);
 uint32_t calibrate_blocks(uint64_t n);
-// Encode stages, launched in order 0 (pack), 1 (sums), 2 (place) on one stream.
-constexpr int kEncodeStages = 3;
+// Encode stages, launched in order 0 (pack), 1 (sums), 2 (place), 3 (spill) on one stream.
+constexpr int kEncodeStages = 4;
 hipError_t launch_encode_stage(int stage, const EncodeArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 

@@ -89,6 +89,20 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
     return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
+// Workgroups are started round robin over the 8 XCDs (workgroup b on XCD b mod 8).  Giving
+// each XCD a contiguous range of tiles instead of every 8th one streams measurably better
+// (about 3 % in a copy probe).  The mapping is a bijection on [0, n_tiles) whatever the
+// hardware does; extra workgroups of the rounded-up grid find t >= n_tiles and exit.
+constexpr uint32_t kXcds = 8;
+
+__device__ __forceinline__ uint32_t xcd_tile(uint32_t b, uint32_t n_tiles)
+{
+    const uint32_t per_xcd = (n_tiles + kXcds - 1) / kXcds;
+    return (b % kXcds) * per_xcd + b / kXcds;
+}
+
+static inline uint32_t xcd_grid(uint32_t n_tiles) { return (n_tiles + kXcds - 1) / kXcds * kXcds; }
+
 // Segment that owns global tile t: largest s with tile_start[s] <= t.
 __device__ __forceinline__ uint32_t find_segment(const uint32_t *tile_start, uint32_t n_seg,
                                                  uint32_t t)
@@ -102,6 +116,28 @@ __device__ __forceinline__ uint32_t find_segment(const uint32_t *tile_start, uin
             hi = mid;
     }
     return lo;
+}
+
+// Segment of tile t, found by the whole workgroup with one round of independent loads (a
+// binary search would chain dependent ones): the number of s >= 1 with tile_start[s] <= t.
+// Call from uniform control flow; contains barriers.
+__device__ uint32_t find_segment_block(const uint32_t *tile_start, uint32_t n_seg, uint32_t t,
+                                       uint32_t tid, uint32_t lane, uint32_t *s_cnt)
+{
+    uint32_t c = 0;
+    for (uint32_t k = 1 + tid; k < n_seg; k += kThreads)
+        c += tile_start[k] <= t ? 1u : 0u;
+#pragma unroll
+    for (uint32_t d = 1; d < 64; d <<= 1)
+        c += shfl_u32(c, lane ^ d);
+    if (lane == 0)
+        s_cnt[tid >> 6] = c;
+    __syncthreads();
+    uint32_t seg = 0;
+    for (int w = 0; w < kWaves; ++w)
+        seg += s_cnt[w];
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(seg);
 }
 
 // ======================================================================================
@@ -199,8 +235,10 @@ hipError_t launch_calibrate(const uint16_t *d_x, uint64_t n, uint32_t *d_partial
 //          chunk offsets into chunk_off, the tile's escape count;
 //   sums   (one workgroup per kSumTiles tiles): segmented sums of the tile counts;
 //   place  (one workgroup per kPlaceTiles tiles): each tile's escape offset from those sums,
-//          escapes moved to their final positions, chunk offsets made global, per-segment
-//          totals.
+//          slot escapes moved to their final positions, chunk offsets made global,
+//          per-segment totals;
+//   spill  (a fixed grid over the list of overflow tiles): their escapes moved into place,
+//          one tile per workgroup at a time, so escape-heavy inputs keep the whole GPU busy.
 // ======================================================================================
 
 // Split one group of 8 words (4 dwords, word 2m in the low half of dword m).
@@ -271,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
     if (tid < 64)
         reinterpret_cast<uint32_t *>(s_lut)[tid] = reinterpret_cast<const uint32_t *>(a.lut)[tid];
 
-    const uint32_t s = tile_segment(a, t);
+    const uint32_t s = a.n_seg > 1 ? find_segment_block(a.tile_start, a.n_seg, t, tid, lane, s_wave_total) : 0u;
     const SegDesc sd = segment_desc(a, s);
     const uint64_t n = sd.n;
     const uint64_t base = (uint64_t)(t - segment_first_tile(a, s)) << kEncTileShift;
@@ -353,9 +391,12 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
     uint64_t room = kSlotEscapes;
     if (tile_total > kSlotEscapes) {
         if (tid == 0) {
-            const uint64_t off = atomicAdd(a.ovf_next, (unsigned long long)tile_total);
+            // one atomic reserves the escapes' room and the tile's place in the overflow list
+            const uint64_t old = atomicAdd(a.ovf_ctr, (unsigned long long)tile_total + (1ull << kOvfTileShift));
+            const uint64_t off = old & kOvfOffsetMask;
             s_ovf = off;
             a.tile_ovf[t] = off;
+            a.ovf_tiles[old >> kOvfTileShift] = t;
             if (off + tile_total > a.ovf_cap)
                 atomicOr(a.err, kErrOverflowArea);
         }
@@ -449,8 +490,6 @@ __device__ uint32_t block_max_u32(uint32_t x, uint32_t tid, uint32_t lane, uint3
     return m;
 }
 
-constexpr uint64_t kFromOverflow = 1ull << 63;
-
 // Inclusive prefix sum over the 256 threads of the workgroup (thread order).
 __device__ uint32_t block_inclusive_sum_u32(uint32_t x, uint32_t tid, uint32_t lane, uint32_t *s_red)
 {
@@ -503,8 +542,12 @@ __global__ __launch_bounds__(kThreads) void encode_sums_kernel(const EncodeArgs 
     const SegSum all = block_seg_scan(mine, tid, lane_id(), s_wave);
     if (tid == kThreads - 1)
         a.block_sum[blockIdx.x] = all.v | ((uint64_t)all.head << 63);
-    if (blockIdx.x == 0 && tid == 0)
-        *a.ovf_next = 0;            // the pack launch of this encode has finished with it
+    if (blockIdx.x == 0 && tid == 0) {
+        // the pack launch of this encode has finished with the counter: keep its final value
+        // for the spill launch and leave it at 0 for the next encode
+        a.ovf_ctr[1] = a.ovf_ctr[0];
+        a.ovf_ctr[0] = 0;
+    }
 }
 
 // ---- place --------------------------------------------------------------------------------
@@ -516,7 +559,6 @@ __global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs
     __shared__ uint64_t s_red64[kWaves];
     __shared__ uint64_t s_prefix[kPlaceTiles];   // escape offset of each tile in its segment
     __shared__ uint64_t s_base[kPlaceTiles];     // first word of each tile in its segment
-    __shared__ uint64_t s_src[kPlaceTiles];      // slot index, or overflow offset | kFromOverflow
     __shared__ uint32_t s_seg[kPlaceTiles];
     __shared__ uint32_t s_first[kPlaceTiles + 1];
 
@@ -555,7 +597,7 @@ __global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs
 
     // each thread: one tile; exclusive segmented prefix = carry-in combined with the earlier tiles
     const uint32_t u = u_first + tid;
-    const bool valid = u < a.n_tiles;
+    const bool valid = tid < kPlaceTiles && u < a.n_tiles;
     const uint32_t seg = valid ? tile_segment(a, u) : 0u;
     const uint32_t head = valid && segment_first_tile(a, seg) == u ? 1u : 0u;
     const uint32_t count = valid ? a.tile_count[u] : 0u;
@@ -581,15 +623,21 @@ __global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs
                 sd.chunk_off[c] += prefix;
         }
     }
-    s_prefix[tid] = prefix;
-    s_base[tid] = base;
-    s_seg[tid] = seg;
-    s_src[tid] = count > kSlotEscapes ? (a.tile_ovf[u] | kFromOverflow) : (uint64_t)u * kSlotEscapes;
+    // overflow tiles are moved by the spill launch; the others here, from their slots
+    const bool spilled = count > kSlotEscapes;
+    if (spilled)
+        a.tile_prefix[u] = prefix;
+    if (tid < kPlaceTiles) {
+        s_prefix[tid] = prefix;
+        s_base[tid] = base;
+        s_seg[tid] = seg;
+    }
 
-    // exclusive scan of the counts inside the workgroup: escape j of the workgroup belongs to
-    // the tile i with s_first[i] <= j < s_first[i + 1]
-    const uint32_t inc = block_inclusive_sum_u32(count, tid, lane, s_red32);
-    s_first[tid + 1] = inc;
+    // exclusive scan of the slot counts inside the workgroup: escape j of the workgroup belongs
+    // to the tile i with s_first[i] <= j < s_first[i + 1]
+    const uint32_t inc = block_inclusive_sum_u32(spilled ? 0u : count, tid, lane, s_red32);
+    if (tid < kPlaceTiles)
+        s_first[tid + 1] = inc;
     if (tid == 0)
         s_first[0] = 0;
     __syncthreads();
@@ -608,22 +656,40 @@ __global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs
                 hi = mid;
         }
         const uint32_t r = j - s_first[lo];
-        const uint64_t src = s_src[lo];
-        uint32_t e;
-        if (src & kFromOverflow) {
-            const uint64_t off = (src & ~kFromOverflow) + r;
-            if (off >= a.ovf_cap)
-                continue;
-            e = a.ovf[off];
-        } else {
-            e = a.slots[src + r];
-        }
+        const uint32_t e = a.slots[(uint64_t)(u_first + lo) * kSlotEscapes + r];
         if (a.n_seg > 1)
             sd = a.segs[s_seg[lo]];
         const uint64_t d = s_prefix[lo] + r;
         if (d < sd.esc) {
             sd.esc_pos[d] = (uint16_t)((s_base[lo] + (e & 0xFFFFu)) & cmask);
             sd.esc_exp[d] = (uint8_t)(e >> 16);
+        }
+    }
+}
+
+// ---- spill --------------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kThreads) void encode_spill_kernel(const EncodeArgs a)
+{
+    const uint32_t tid = threadIdx.x;
+    const uint64_t cmask = (1ull << a.log2_chunk) - 1;
+    const uint32_t n_spilled = (uint32_t)(a.ovf_ctr[1] >> kOvfTileShift);
+    for (uint32_t i = blockIdx.x; i < n_spilled; i += gridDim.x) {
+        const uint32_t t = a.ovf_tiles[i];
+        const uint32_t s = tile_segment(a, t);
+        const SegDesc sd = segment_desc(a, s);
+        const uint64_t base = (uint64_t)(t - segment_first_tile(a, s)) << kEncTileShift;
+        const uint64_t pre = a.tile_prefix[t];
+        const uint32_t cnt = a.tile_count[t];
+        const uint64_t off = a.tile_ovf[t];
+        const uint64_t room = off < a.ovf_cap ? a.ovf_cap - off : 0;
+        for (uint32_t r = tid; r < cnt && r < room; r += kThreads) {
+            const uint64_t d = pre + r;
+            if (d < sd.esc) {
+                const uint32_t e = a.ovf[off + r];
+                sd.esc_pos[d] = (uint16_t)((base + (e & 0xFFFFu)) & cmask);
+                sd.esc_exp[d] = (uint8_t)(e >> 16);
+            }
         }
     }
 }
@@ -637,8 +703,11 @@ hipError_t launch_encode_stage(int stage, const EncodeArgs &a, hipStream_t strea
     case 1:
         encode_sums_kernel<<<(a.n_tiles + kSumTiles - 1) / kSumTiles, kThreads, 0, stream>>>(a);
         break;
-    default:
+    case 2:
         encode_place_kernel<<<(a.n_tiles + kPlaceTiles - 1) / kPlaceTiles, kThreads, 0, stream>>>(a);
+        break;
+    default:
+        encode_spill_kernel<<<a.n_tiles < kSpillBlocks ? a.n_tiles : kSpillBlocks, kThreads, 0, stream>>>(a);
         break;
     }
     return hipGetLastError();
@@ -675,15 +744,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
     __shared__ uint32_t s_exp[kDecTileWords / 4];              // exponent bytes of the tile
     __shared__ uint64_t s_off[kDecTileWords / 16 + 1];         // chunk offsets of the tile
 
+    __shared__ uint32_t s_cnt[kWaves];
+
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = lane_id();
     const uint32_t wave = tid >> 6;
-    const uint32_t t = blockIdx.x;
+    const uint32_t t = xcd_tile(blockIdx.x, a.n_tiles);
+    if (t >= a.n_tiles)
+        return;
 
     uint32_t first = 0;
     SegDesc sd = a.seg0;
     if (a.n_seg > 1) {
-        const uint32_t s = find_segment(a.tile_start, a.n_seg, t);
+        const uint32_t s = find_segment_block(a.tile_start, a.n_seg, t, tid, lane, s_cnt);
         first = a.tile_start[s];
         sd = a.segs[s];
     }
@@ -761,25 +834,30 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
         __syncthreads();
         uint8_t *bytes = reinterpret_cast<uint8_t *>(s_exp);
         if (!sub_chunk) {
-            for (uint64_t ci = wave; ci < nc; ci += kWaves) {
-                const uint64_t ea = s_off[ci], eb = s_off[ci + 1];
-                if (ea > eb || eb > E) {
-                    if (lane == 0 && a.err)
-                        atomicOr(a.err, kErrBadOffsets);
+            // the tile's escapes are the contiguous range [j0, j1): one per thread and round;
+            // escape jj belongs to the last chunk ci whose offset s_off[ci] <= jj
+            for (uint64_t ci = tid; ci < nc; ci += kThreads)
+                if (s_off[ci] > s_off[ci + 1] && a.err)
+                    atomicOr(a.err, kErrBadOffsets);
+            for (uint64_t jj = j0 + tid; jj < j1; jj += kThreads) {
+                uint32_t lo = 0, hi = (uint32_t)nc;          // s_off[lo] <= jj < s_off[hi]
+                while (hi - lo > 1) {
+                    const uint32_t mid = (lo + hi) >> 1;
+                    if (s_off[mid] <= jj)
+                        lo = mid;
+                    else
+                        hi = mid;
+                }
+                const uint64_t cstart = (c0 + lo) << log2c;
+                const uint64_t clen = n - cstart < C ? n - cstart : C;
+                const uint32_t pos = sd.esc_pos[jj];
+                if (pos >= clen) {
+                    if (a.err)
+                        atomicOr(a.err, kErrBadPosition);
                     continue;
                 }
-                const uint64_t cstart = (c0 + ci) << log2c;
-                const uint64_t clen = n - cstart < C ? n - cstart : C;
-                for (uint64_t jj = ea + lane; jj < eb; jj += 64) {
-                    const uint32_t pos = sd.esc_pos[jj];
-                    if (pos >= clen) {
-                        if (a.err)
-                            atomicOr(a.err, kErrBadPosition);
-                        continue;
-                    }
-                    const uint32_t p = (uint32_t)(cstart + pos - base);
-                    bytes[(p >> 3) * 8 + (p & 1u) * 4 + ((p >> 1) & 3u)] = sd.esc_exp[jj];
-                }
+                const uint32_t p = (uint32_t)(cstart + pos - base);
+                bytes[(p >> 3) * 8 + (p & 1u) * 4 + ((p >> 1) & 3u)] = sd.esc_exp[jj];
             }
         } else {
             const uint64_t lo = base - (c0 << log2c);
@@ -827,7 +905,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream)
 {
-    decode_kernel<<<a.n_tiles, kThreads, 0, stream>>>(a);
+    decode_kernel<<<xcd_grid(a.n_tiles), kThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 

@@ -360,10 +360,28 @@ def test_kernel_timing():
     for _ in range(3):
         codec.decode(codec.encode(x))
     times = codec.kernel_times(reset=True)
-    assert set(times) == {"encode_pack", "encode_sums", "encode_place", "decode"}
+    assert set(times) == {"encode_pack", "encode_sums", "encode_place", "encode_spill", "decode"}
     for k, (ms, count) in times.items():
         assert count == 3 and ms > 0, k
     assert all(c == 0 for _, c in codec.kernel_times().values())
     codec.profile(False)
     codec.decode(codec.encode(x))
     assert all(c == 0 for _, c in codec.kernel_times().values())
+
+
+def test_prepared_batch_round_trip():
+    xs_np = [workloads.mixed_words(n, 300 + n, wide_fraction=0.02) for n in (16384 * 2 + 7, 100, 0, 40000)]
+    codec = codec_for(workloads.normal_words(30000, 11), 64)
+    xs = [dev(x) for x in xs_np]
+    encs = codec.encode_batch(xs)
+    ys = [torch.empty_like(x) for x in xs]
+    batch = codec.prepare(xs, encs, ys)
+    result = torch.zeros(1 + len(xs), dtype=torch.int64, device=DEV)
+    for _ in range(3):
+        batch.encode_async(result)
+        batch.decode()
+    torch.cuda.synchronize()
+    assert batch.finish(result) == sz.OK
+    for x, e, y in zip(xs_np, encs, ys):
+        assert_same_stream(codec, e, x)
+        assert np.array_equal(host(y, np.uint16), x)
