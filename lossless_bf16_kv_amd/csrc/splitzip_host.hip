@@ -311,7 +311,7 @@ struct CallTimer {
 
 // Byte offsets of the encode scratch arrays for one launch.
 struct EncodeScratch {
-    uint64_t tile_count, tile_ovf, tile_prefix, ovf_tiles, slots, block_sum, ovf, total;
+    uint64_t tile_count, tile_ovf, tile_prefix, ovf_tiles, slots, block_sum, group_sum, ovf, total;
     EncodeScratch(uint64_t n_tiles, uint64_t ovf_cap)
     {
         auto up = [](uint64_t x) { return (x + 255) & ~uint64_t(255); };
@@ -321,7 +321,8 @@ struct EncodeScratch {
         ovf_tiles = up(tile_prefix + 8 * n_tiles);
         slots = up(ovf_tiles + 4 * n_tiles);
         block_sum = up(slots + 4 * (uint64_t)sz::kSlotEscapes * n_tiles);
-        ovf = up(block_sum + 8 * ((n_tiles + sz::kSumTiles - 1) / sz::kSumTiles));
+        group_sum = up(block_sum + 8 * ((n_tiles + sz::kSumTiles - 1) / sz::kSumTiles));
+        ovf = up(group_sum + 8 * ((n_tiles + sz::kPlaceTiles - 1) / sz::kPlaceTiles));
         total = up(ovf + 4 * ovf_cap);
     }
 };
@@ -591,6 +592,7 @@ int encode_launch(splitzip_codec *codec, uint32_t n_seg, const splitzip_segment 
     a.ovf_tiles = reinterpret_cast<uint32_t *>(w->scratch + lay.ovf_tiles);
     a.slots = reinterpret_cast<uint32_t *>(w->scratch + lay.slots);
     a.block_sum = reinterpret_cast<uint64_t *>(w->scratch + lay.block_sum);
+    a.group_sum = reinterpret_cast<uint64_t *>(w->scratch + lay.group_sum);
     a.ovf = reinterpret_cast<uint32_t *>(w->scratch + lay.ovf);
     a.ovf_ctr = w->ovf_ctr;
     a.ovf_cap = ovf_cap;

@@ -22,6 +22,8 @@ constexpr int kDecTileShift = 13;
 constexpr int kDecTileWords = 1 << kDecTileShift;
 static_assert(kThreads * kEncGroups * kGroupWords == kEncTileWords, "encode tile geometry");
 static_assert(kThreads * kDecGroups * kGroupWords == kDecTileWords, "decode tile geometry");
+// Extra LDS reserved per decode workgroup to hold occupancy at 5 workgroups per CU.
+constexpr unsigned kDecodeLdsReserve = 16384;
 
 // Inverse-LUT entry of an exponent outside the codebook: nibble 0 plus an escape bit.
 constexpr uint8_t kEscapeEntry = 0x10;
@@ -40,6 +42,8 @@ constexpr uint64_t kOvfOffsetMask = (1ull << kOvfTileShift) - 1;
 constexpr uint64_t kMaxSegmentWords = 1ull << 38;
 static_assert(kEncTileWords <= 65536, "in-tile positions must fit 16 bits");
 static_assert(kSumTiles % kThreads == 0 && kSumTiles % kPlaceTiles == 0, "sum blocks");
+static_assert(kSumTiles / kPlaceTiles <= kThreads, "group sums of a block fit one pass");
+static_assert(kPlaceTiles % (kSumTiles / kThreads) == 0 && kPlaceTiles <= kThreads, "groups");
 
 // error bits written by the kernels
 constexpr uint32_t kErrBadOffsets = 2u;      // decode: chunk offsets out of range
@@ -72,6 +76,7 @@ struct EncodeArgs {
                                   // its final value saved by the sums launch
     uint64_t ovf_cap;
     uint64_t *block_sum;          // [ceil(n_tiles / kSumTiles)] segmented sums, bit 63 = head
+    uint64_t *group_sum;          // [ceil(n_tiles / kPlaceTiles)] the same per placement group
     uint64_t *seg_escapes;        // [n_seg] OUT: E per segment
     uint32_t *err;                // OUT: error bits
     uint32_t n_seg;
