@@ -64,11 +64,13 @@ ENC_TILE_WORDS = 16384     # encode tile (words per workgroup)
 def algorithmic_bytes(ns, Es, C):
     """Bytes each kernel must move per launch (reads + writes), from the stream format.
 
-    encode (the three launches together) reads 2n and writes the sections
+    encode (its four launches together) reads 2n and writes the sections
     n + ceil(n/2) + 8 (n_chunks + 1) + 3E; decode is the reverse.  The pack kernel reads
     2n and writes sm, codes, tile-local chunk offsets, 4-byte scratch escapes and one
-    count per tile; place reads the scratch escapes, counts and chunk offsets and writes
-    escapes (3E) and chunk offsets; sums reads one count per tile."""
+    count per tile; sums reads one count per tile; place reads the scratch escapes,
+    counts and chunk offsets and writes escapes (3E) and chunk offsets.  The spill launch
+    moves only the escapes of tiles with more than a slot's worth (a data-dependent
+    amount), so it has no fixed figure."""
     out = {"encode": 0, "decode": 0, "encode_pack": 0, "encode_sums": 0, "encode_place": 0}
     for n, E in zip(ns, Es):
         n_ch = -(-n // C)
@@ -113,7 +115,7 @@ def cpu_baseline(wl, codebook: bytes, sample_words: int):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--chunk-size", type=int, default=1024)
