@@ -757,12 +757,23 @@ __global__ __launch_bounds__(kThreads) void encode_spill_kernel(const EncodeArgs
         const uint32_t cnt = a.tile_count[t];
         const uint64_t off = a.tile_ovf[t];
         const uint64_t room = off < a.ovf_cap ? a.ovf_cap - off : 0;
-        for (uint32_t r = tid; r < cnt && r < room; r += kThreads) {
-            const uint64_t d = pre + r;
-            if (d < sd.esc) {
-                const uint32_t e = a.ovf[off + r];
-                sd.esc_pos[d] = (uint16_t)((base + (e & 0xFFFFu)) & cmask);
-                sd.esc_exp[d] = (uint8_t)(e >> 16);
+        // four loads in flight before the stores
+        constexpr int kBatch = 4;
+        const uint32_t lim = cnt < room ? cnt : (uint32_t)room;
+        for (uint32_t r0 = tid; r0 < lim; r0 += kBatch * kThreads) {
+            uint32_t e[kBatch];
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k)
+                if (r0 + k * kThreads < lim)
+                    e[k] = a.ovf[off + r0 + k * kThreads];
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+                const uint32_t r = r0 + k * kThreads;
+                const uint64_t d = pre + r;
+                if (r < lim && d < sd.esc) {
+                    sd.esc_pos[d] = (uint16_t)((base + (e[k] & 0xFFFFu)) & cmask);
+                    sd.esc_exp[d] = (uint8_t)(e[k] >> 16);
+                }
             }
         }
     }

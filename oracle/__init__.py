@@ -36,7 +36,7 @@ class OracleError(RuntimeError):
 def build(out: str = LIB_PATH, src: str = _SRC, extra_flags: tuple = ()) -> str:
     """Compile the oracle with the host C compiler (no HIP involved)."""
     cmd = ["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-shared", "-fPIC",
-           *extra_flags, "-o", out, src]
+           *extra_flags, "-o", out, src, "-lm"]
     subprocess.run(cmd, check=True, cwd=os.path.dirname(src))
     return out
 
@@ -61,6 +61,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.szo_codebook.restype = None
     lib.szo_coverage.argtypes = [_u64p, _u8p, ctypes.c_uint64]
     lib.szo_coverage.restype = ctypes.c_double
+    lib.szo_entropy.argtypes = [_u64p]
+    lib.szo_entropy.restype = ctypes.c_double
     lib.szo_compressed_bytes.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint64]
     lib.szo_compressed_bytes.restype = ctypes.c_uint64
     lib.szo_encode.argtypes = [_u16p, ctypes.c_uint64, _u8p, ctypes.c_uint32, _u8p, _u8p, _u64p,
@@ -103,6 +105,11 @@ class Oracle:
         hist = np.ascontiguousarray(hist, np.uint64)
         cb = np.ascontiguousarray(cb, np.uint8)
         return float(self.lib.szo_coverage(_ptr(hist, _u64p), _ptr(cb, _u8p), m))
+
+    def entropy(self, hist: np.ndarray) -> float:
+        """Shannon entropy (bits) of the exponent distribution given by a histogram."""
+        hist = np.ascontiguousarray(hist, np.uint64)
+        return float(self.lib.szo_entropy(_ptr(hist, _u64p)))
 
     def calibrate(self, cal: np.ndarray):
         """(codebook, coverage, histogram) of a calibration tensor."""

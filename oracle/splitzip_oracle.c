@@ -18,6 +18,7 @@
  */
 #include "splitzip_oracle.h"
 
+#include <math.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -104,6 +105,31 @@ double szo_coverage(const uint64_t hist[256], const uint8_t cb[16], uint64_t m)
     for (k = 0; k < 16; ++k)
         covered += hist[cb[k]];
     return (double)covered / (double)m;
+}
+
+/* ---- exponent statistics [README, Repository Contents and Reproducing Paper Artifact
+ *      Scripts: exponent entropy and top-16 coverage analysis of KV tensors; ZIPSERV,
+ *      Information-Theoretic Limits and Exponent Entropy Bounds: Shannon entropy of the
+ *      exponent field] ---- */
+
+double szo_entropy(const uint64_t hist[256])
+{
+    /* H = -sum over exponent values of p log2 p, with p = count / total; values that
+     * never occur contribute nothing. */
+    uint64_t m = 0;
+    double h = 0.0;
+    int e;
+    for (e = 0; e < 256; ++e)
+        m += hist[e];
+    if (m == 0)
+        return 0.0;
+    for (e = 0; e < 256; ++e) {
+        if (hist[e] != 0) {
+            const double p = (double)hist[e] / (double)m;
+            h -= p * log2(p);
+        }
+    }
+    return h;
 }
 
 /* ---- sizes: n sign+mantissa bytes + n/2 code bytes + escape bytes + chunk metadata ---- */

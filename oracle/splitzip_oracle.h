@@ -61,6 +61,9 @@ void szo_codebook(const uint64_t hist[256], uint8_t cb[16]);
 /* Fraction of the m counted exponents that the codebook holds (0 if m == 0). */
 double szo_coverage(const uint64_t hist[256], const uint8_t cb[16], uint64_t m);
 
+/* Shannon entropy, in bits, of the exponent distribution hist (0 for an empty one). */
+double szo_entropy(const uint64_t hist[256]);
+
 /* Number of bytes of the canonical stream. */
 uint64_t szo_compressed_bytes(uint64_t n, uint32_t chunk_size, uint64_t n_escapes);
 

@@ -209,6 +209,33 @@ def check_codebook_rules(o) -> None:
     assert o.calibrate(np.zeros(0, np.uint16))[1] == 0.0
 
 
+def check_entropy(o) -> None:
+    """Exponent entropy against values the definition fixes exactly: the exhaustive word
+    set has 256 equally likely exponents (8 bits); a dyadic distribution (1/2, 1/4, 1/8,
+    1/8) has 1.75 bits; one value or none has 0; random histograms agree with scipy's
+    entropy routine in base 2."""
+    from scipy.stats import entropy as scipy_entropy
+    x = np.arange(65536, dtype=np.uint16)
+    assert o.entropy(o.histogram(x)) == 8.0
+    h = np.zeros(256, np.uint64)
+    assert o.entropy(h) == 0.0
+    h[77] = 1000
+    assert o.entropy(h) == 0.0
+    h[:] = 0
+    h[[127, 3, 200, 0]] = [4000, 2000, 1000, 1000]
+    assert o.entropy(h) == 1.75
+    h[:] = 0
+    h[[5, 250]] = [3, 3]
+    assert o.entropy(h) == 1.0
+    rng = np.random.default_rng(123)
+    for k in range(20):
+        h = rng.integers(0, 1000, 256).astype(np.uint64)
+        h[rng.random(256) < 0.7] = 0
+        h[rng.integers(256)] += 1
+        want = float(scipy_entropy(h.astype(np.float64), base=2))
+        assert abs(o.entropy(h) - want) <= 1e-12 * max(1.0, want)
+
+
 def run_all(o) -> None:
     check_worked_example(o)
     check_exhaustive(o, 1024)
@@ -217,3 +244,4 @@ def run_all(o) -> None:
     check_brute_force(o)
     check_round_trips(o)
     check_codebook_rules(o)
+    check_entropy(o)

@@ -70,6 +70,40 @@ def test_normal_calibration_statistics():
     assert np.array_equal(O.decode(enc), wl.segments[0])
 
 
+def test_entropy_closed_forms():
+    pins.check_entropy(O)
+
+
+def test_normal_exponent_entropy():
+    """Exponent entropy of N(0,1) rounded to BF16, from the normal CDF: field e holds
+    |x| in [2^(e-127) (1 - 2^-9), 2^(e-126) (1 - 2^-9)) (round to nearest even of the
+    8-bit significand moves the upper 2^-9 of each binade up).  The entropy of the
+    config-1 calibration draw must sit within 5 sigma of the analytic value, with sigma
+    the standard error of the plug-in estimate, sqrt(Var[log2 p] / m)."""
+    def cdf_abs(t):                       # P(|x| < t)
+        return math.erf(t / math.sqrt(2))
+    lo_edge = 1 - 2.0 ** -9
+    p = {}
+    for e in range(1, 255):
+        a = 2.0 ** (e - 127) * lo_edge
+        b = 2.0 ** (e - 126) * lo_edge
+        if a > 40:
+            break
+        q = cdf_abs(b) - cdf_abs(a)
+        if q > 0:
+            p[e] = q
+    p[0] = cdf_abs(2.0 ** -126 * lo_edge)
+    total = sum(p.values())
+    assert abs(total - 1) < 1e-12
+    h_true = -sum(q * math.log2(q) for q in p.values() if q > 0)
+    second = sum(q * math.log2(q) ** 2 for q in p.values() if q > 0)
+    wl = workloads.config1()
+    m = wl.calibration.size
+    sigma = math.sqrt((second - h_true ** 2) / m)
+    h = O.entropy(O.histogram(wl.calibration))
+    assert abs(h - h_true) < 5 * sigma, (h, h_true, sigma)
+
+
 def test_rejects_bad_arguments_and_streams():
     _, cal, x = pins.worked_example()
     cb, _, _ = O.calibrate(cal)
@@ -131,6 +165,10 @@ MUTANTS = [
      "bf16_join(bf16_sign(y[i]), cb[0], bf16_mantissa(y[i]))"),
     ("decode reads the wrong nibble", "unsigned code = (codes[i / 2] >> (4 * (i % 2))) & 0xFu;",
      "unsigned code = (codes[i / 2] >> (4 * (1 - i % 2))) & 0xFu;"),
+    ("entropy in nats", "h -= p * log2(p);", "h -= p * log(p);"),
+    ("entropy sign", "h -= p * log2(p);", "h += p * log2(p);"),
+    ("entropy of unnormalized counts", "const double p = (double)hist[e] / (double)m;",
+     "const double p = (double)hist[e];"),
     ("codebook of 15", "for (k = 0; k < 16; ++k)\n        if (cb[k] == e)",
      "for (k = 0; k < 15; ++k)\n        if (cb[k] == e)"),
 ]
