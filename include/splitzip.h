@@ -44,10 +44,11 @@
 extern "C" {
 #endif
 
-#define SPLITZIP_ABI_VERSION 1
+#define SPLITZIP_ABI_VERSION 2
 #define SPLITZIP_HEADER_BYTES 64
 #define SPLITZIP_MIN_CHUNK 16
 #define SPLITZIP_MAX_CHUNK 65536
+#define SPLITZIP_MAX_BOOKS 4096   /* codebooks per codec */
 
 typedef enum splitzip_status {
     SPLITZIP_OK = 0,
@@ -74,6 +75,10 @@ typedef struct splitzip_codec splitzip_codec;
  *   n_escapes        encode: OUT, the segment's E (also when E > esc_capacity).
  *                    decode: IN, the E the sections were written with.
  *   compressed_bytes encode: OUT, canonical stream size.  decode: ignored.
+ *   book             which of the codec's codebooks the segment is coded with (0 for a
+ *                    codec with one codebook); decode must use the book it was encoded
+ *                    with, which the stream header identifies by its codebook copy.
+ *   reserved         set to 0.
  */
 typedef struct splitzip_segment {
     uint16_t *data;
@@ -86,6 +91,8 @@ typedef struct splitzip_segment {
     uint64_t esc_capacity;
     uint64_t n_escapes;
     uint64_t compressed_bytes;
+    uint32_t book;
+    uint32_t reserved;
 } splitzip_segment;
 
 /*
@@ -108,7 +115,30 @@ int splitzip_calibrate(const uint16_t *d_cal, uint64_t n_cal, uint32_t chunk_siz
 int splitzip_codec_from_codebook(const uint8_t codebook[16], uint32_t chunk_size,
                                  splitzip_codec **out_codec);
 
-/* Read back a codec's codebook, chunk size and device (any output may be NULL). */
+/*
+ * A codec with several codebooks (README "Highlights": offline-calibrated top-16 exponent
+ * codebooks), for example one per layer, or one for K and one for V: book b is calibrated
+ * on d_cal[b][0..n_cal[b]) exactly as splitzip_calibrate does for one tensor, and every
+ * segment of an encode or decode call names its book.  d_cal and n_cal are host arrays of
+ * n_books (1..SPLITZIP_MAX_BOOKS) device pointers and sizes.  coverage (optional, host
+ * double[n_books]) and hist (optional, host uint64[n_books * 256]) receive each book's
+ * coverage and calibration histogram.  All histograms are taken in one pass (two
+ * launches).  Blocks until they are on the host.
+ */
+int splitzip_calibrate_books(uint32_t n_books, const uint16_t *const *d_cal, const uint64_t *n_cal,
+                             uint32_t chunk_size, void *stream, splitzip_codec **out_codec,
+                             double *coverage, uint64_t *hist);
+
+/* A codec from n_books known codebooks (host uint8[n_books * 16], book b at 16 b), each
+ * 16 distinct exponents, bound to the current HIP device. */
+int splitzip_codec_from_codebooks(uint32_t n_books, const uint8_t *codebooks, uint32_t chunk_size,
+                                  splitzip_codec **out_codec);
+
+/* Number of codebooks of a codec and (if codebooks != NULL) all of them, host
+ * uint8[n_books * 16]. */
+int splitzip_codec_books(const splitzip_codec *codec, uint32_t *n_books, uint8_t *codebooks);
+
+/* Read back a codec's codebook (book 0), chunk size and device (any output may be NULL). */
 int splitzip_codec_info(const splitzip_codec *codec, uint8_t codebook[16], uint32_t *chunk_size,
                         int *device);
 
@@ -175,6 +205,30 @@ int splitzip_profile(splitzip_codec *codec, int enable);
 int splitzip_profile_read(splitzip_codec *codec, void *stream, double *avg_ms, uint64_t *counts,
                           int reset);
 
+/* ---- exponent statistics (README "Repository Contents" and "Reproducing Paper Artifact
+ *      Scripts": BF16 KV exponent entropy and top-16 coverage analysis) ---- */
+
+/*
+ * Exponent histograms of n_seg BF16 tensors in one pass (two launches):
+ * hist[256 s + e] = number of words of tensor s whose exponent field (bits 14..7) is e.
+ * d_x and n are host arrays of n_seg device pointers (16-byte aligned) and word counts
+ * (n[s] = 0 allowed).  hist is host memory; the call blocks until it is filled.  Scratch
+ * device memory is allocated for the call and released before it returns.
+ */
+int splitzip_histogram(uint32_t n_seg, const uint16_t *const *d_x, const uint64_t *n, void *stream,
+                       uint64_t *hist);
+
+/*
+ * Statistics of one exponent histogram (host only, no device work): the Shannon entropy
+ * in bits, -sum p log2 p over the exponent values that occur with p = count / total
+ * (ZipServ guide, "Information-Theoretic Limits and Exponent Entropy Bounds"); the top-16
+ * codebook a calibration on this histogram picks (count descending, exponent ascending);
+ * its coverage; and the number of distinct exponent values.  Any output may be NULL.  An
+ * empty histogram gives entropy 0 and coverage 0.
+ */
+int splitzip_exponent_stats(const uint64_t hist[256], double *entropy_bits, double *coverage,
+                            uint8_t codebook[16], uint32_t *distinct);
+
 /* ---- host helpers (no device work) ---- */
 
 /* ceil(n / chunk_size); 0 for an invalid chunk size. */
@@ -186,10 +240,10 @@ uint64_t splitzip_compressed_bytes(uint64_t n, uint32_t chunk_size, uint64_t n_e
 /*
  * The canonical 64-byte stream header (little-endian): "SZB1", version u16 = 1,
  * header bytes u16 = 64, chunk_size u32, flags u32 = 0, n u64, n_chunks u64,
- * n_escapes u64, codebook[16], 8 zero bytes.
+ * n_escapes u64, codebook[16] (that of `book`), 8 zero bytes.
  */
-int splitzip_write_header(const splitzip_codec *codec, uint64_t n, uint64_t n_escapes,
-                          uint8_t out[SPLITZIP_HEADER_BYTES]);
+int splitzip_write_header(const splitzip_codec *codec, uint32_t book, uint64_t n,
+                          uint64_t n_escapes, uint8_t out[SPLITZIP_HEADER_BYTES]);
 
 /*
  * Parse a header; total_len is the full stream length (checked against the sizes).
@@ -200,11 +254,13 @@ int splitzip_read_header(const uint8_t *buf, uint64_t total_len, uint64_t *n,
 
 /*
  * Check that a received stream (header + total length) can be decoded by this codec:
- * SPLITZIP_E_FORMAT if the header is malformed, SPLITZIP_E_CODEBOOK if its codebook or
- * chunk size differs from the codec's (README "Codec API": encoded objects are decoded
- * with the same calibrated state).
+ * SPLITZIP_E_FORMAT if the header is malformed, SPLITZIP_E_CODEBOOK if its chunk size
+ * differs from the codec's or its codebook is none of the codec's (README "Codec API":
+ * encoded objects are decoded with the same calibrated state).  On success *book
+ * (optional) receives the first book whose codebook the header carries.
  */
-int splitzip_check_header(const splitzip_codec *codec, const uint8_t *buf, uint64_t total_len);
+int splitzip_check_header(const splitzip_codec *codec, const uint8_t *buf, uint64_t total_len,
+                          uint32_t *book);
 
 const char *splitzip_status_string(int status);
 

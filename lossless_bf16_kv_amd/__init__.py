@@ -13,7 +13,10 @@ Compression for Disaggregated LLM Serving" (README, "Codec API"):
   pointers as Python ints;
 * ``Codec(device, chunk_size)`` with ``calibrate(x) -> coverage``,
   ``encode(x) -> Encoded`` (``.compressed_bytes``) and ``decode(encoded)``,
-  plus ``encode_batch`` / ``decode_batch`` for ragged batches in one launch.
+  plus ``encode_batch`` / ``decode_batch`` for ragged batches in one launch,
+  and ``calibrate_books`` for several codebooks (per layer, per K and V);
+* ``histograms`` / ``exponent_stats``: the exponent entropy and top-16 coverage
+  analysis of BF16 tensors.
 """
 from __future__ import annotations
 
@@ -28,6 +31,7 @@ LIB_PATH = os.path.join(_HERE, "libsplitzip.so")
 OK, E_INVALID, E_NOMEM, E_DEVICE, E_CODEBOOK, E_FORMAT, E_CAPACITY = range(7)
 HEADER_BYTES = 64
 MIN_CHUNK, MAX_CHUNK = 16, 65536
+MAX_BOOKS = 4096
 
 
 class SplitZipError(RuntimeError):
@@ -49,6 +53,8 @@ class splitzip_segment(ctypes.Structure):
         ("esc_capacity", ctypes.c_uint64),
         ("n_escapes", ctypes.c_uint64),
         ("compressed_bytes", ctypes.c_uint64),
+        ("book", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
     ]
 
 
@@ -67,6 +73,13 @@ def lib() -> ctypes.CDLL:
     P = ctypes.POINTER
     L.splitzip_calibrate.argtypes = [vp, u64, u32, vp, P(vp), P(ctypes.c_double), P(u64)]
     L.splitzip_codec_from_codebook.argtypes = [P(ctypes.c_uint8), u32, P(vp)]
+    L.splitzip_calibrate_books.argtypes = [u32, P(vp), P(u64), u32, vp, P(vp), P(ctypes.c_double),
+                                           P(u64)]
+    L.splitzip_codec_from_codebooks.argtypes = [u32, P(ctypes.c_uint8), u32, P(vp)]
+    L.splitzip_codec_books.argtypes = [vp, P(u32), P(ctypes.c_uint8)]
+    L.splitzip_histogram.argtypes = [u32, P(vp), P(u64), vp, P(u64)]
+    L.splitzip_exponent_stats.argtypes = [P(u64), P(ctypes.c_double), P(ctypes.c_double),
+                                          P(ctypes.c_uint8), P(u32)]
     L.splitzip_codec_info.argtypes = [vp, P(ctypes.c_uint8), P(u32), P(i32)]
     L.splitzip_encode.argtypes = [vp, u32, P(splitzip_segment), vp]
     L.splitzip_encode_async.argtypes = [vp, u32, P(splitzip_segment), vp, vp]
@@ -79,15 +92,17 @@ def lib() -> ctypes.CDLL:
     L.splitzip_chunk_count.restype = u64
     L.splitzip_compressed_bytes.argtypes = [u64, u32, u64]
     L.splitzip_compressed_bytes.restype = u64
-    L.splitzip_write_header.argtypes = [vp, u64, u64, P(ctypes.c_uint8)]
+    L.splitzip_write_header.argtypes = [vp, u32, u64, u64, P(ctypes.c_uint8)]
     L.splitzip_read_header.argtypes = [P(ctypes.c_uint8), u64, P(u64), P(u32), P(u64),
                                        P(ctypes.c_uint8)]
-    L.splitzip_check_header.argtypes = [vp, P(ctypes.c_uint8), u64]
+    L.splitzip_check_header.argtypes = [vp, P(ctypes.c_uint8), u64, P(u32)]
     L.splitzip_status_string.argtypes = [i32]
     L.splitzip_status_string.restype = ctypes.c_char_p
     L.splitzip_last_error.argtypes = []
     L.splitzip_last_error.restype = ctypes.c_char_p
     for f in ("splitzip_calibrate", "splitzip_codec_from_codebook", "splitzip_codec_info",
+              "splitzip_calibrate_books", "splitzip_codec_from_codebooks", "splitzip_codec_books",
+              "splitzip_histogram", "splitzip_exponent_stats",
               "splitzip_encode", "splitzip_encode_async", "splitzip_decode",
               "splitzip_write_header", "splitzip_profile", "splitzip_profile_read",
               "splitzip_read_header", "splitzip_check_header"):
@@ -125,6 +140,65 @@ def splitzip_codec_from_codebook(codebook: bytes, chunk_size: int) -> int:
     h = ctypes.c_void_p()
     _check(lib().splitzip_codec_from_codebook(_u8buf(bytes(codebook)), chunk_size, ctypes.byref(h)))
     return h.value
+
+
+def _ptr_array(ptrs):
+    return (ctypes.c_void_p * len(ptrs))(*[p or None for p in ptrs])
+
+
+def splitzip_calibrate_books(d_cal, n_cal, chunk_size: int, stream: int = 0):
+    """d_cal, n_cal: one device pointer and size per book.
+    -> (codec handle, coverage list, histogram list of 256-lists)."""
+    k = len(d_cal)
+    h = ctypes.c_void_p()
+    cov = (ctypes.c_double * max(k, 1))()
+    hist = (ctypes.c_uint64 * (256 * max(k, 1)))()
+    _check(lib().splitzip_calibrate_books(k, _ptr_array(d_cal), (ctypes.c_uint64 * max(k, 1))(*n_cal),
+                                          chunk_size, stream or None, ctypes.byref(h), cov, hist))
+    return h.value, list(cov)[:k], [list(hist[256 * b:256 * b + 256]) for b in range(k)]
+
+
+def splitzip_codec_from_codebooks(codebooks: bytes, chunk_size: int) -> int:
+    """codebooks: 16 bytes per book, concatenated."""
+    if not codebooks or len(codebooks) % 16:
+        raise ValueError("codebooks must be a non-empty multiple of 16 bytes")
+    h = ctypes.c_void_p()
+    _check(lib().splitzip_codec_from_codebooks(len(codebooks) // 16, _u8buf(bytes(codebooks)),
+                                               chunk_size, ctypes.byref(h)))
+    return h.value
+
+
+def splitzip_codec_books(codec: int) -> list:
+    """The codec's codebooks, 16 bytes each."""
+    k = ctypes.c_uint32()
+    _check(lib().splitzip_codec_books(codec, ctypes.byref(k), None))
+    buf = (ctypes.c_uint8 * (16 * k.value))()
+    _check(lib().splitzip_codec_books(codec, ctypes.byref(k), buf))
+    raw = bytes(buf)
+    return [raw[16 * b:16 * b + 16] for b in range(k.value)]
+
+
+def splitzip_histogram(d_x, n, stream: int = 0) -> list:
+    """Exponent histograms of several device tensors in one pass -> list of 256-lists."""
+    k = len(d_x)
+    hist = (ctypes.c_uint64 * (256 * max(k, 1)))()
+    _check(lib().splitzip_histogram(k, _ptr_array(d_x), (ctypes.c_uint64 * max(k, 1))(*n),
+                                    stream or None, hist))
+    return [list(hist[256 * b:256 * b + 256]) for b in range(k)]
+
+
+def splitzip_exponent_stats(hist) -> dict:
+    """Entropy (bits), top-16 codebook, its coverage and the distinct exponent count of
+    one 256-bin exponent histogram (host computation)."""
+    if len(hist) != 256:
+        raise ValueError("hist must have 256 bins")
+    h = (ctypes.c_uint64 * 256)(*[int(v) for v in hist])
+    ent, cov = ctypes.c_double(), ctypes.c_double()
+    cb = (ctypes.c_uint8 * 16)()
+    d = ctypes.c_uint32()
+    _check(lib().splitzip_exponent_stats(h, ctypes.byref(ent), ctypes.byref(cov), cb, ctypes.byref(d)))
+    return {"entropy_bits": ent.value, "coverage": cov.value, "codebook": bytes(cb),
+            "distinct": d.value}
 
 
 def splitzip_codec_info(codec: int):
@@ -176,9 +250,9 @@ def splitzip_compressed_bytes(n: int, chunk_size: int, n_escapes: int) -> int:
     return int(lib().splitzip_compressed_bytes(n, chunk_size, n_escapes))
 
 
-def splitzip_write_header(codec: int, n: int, n_escapes: int) -> bytes:
+def splitzip_write_header(codec: int, book: int, n: int, n_escapes: int) -> bytes:
     out = (ctypes.c_uint8 * HEADER_BYTES)()
-    _check(lib().splitzip_write_header(codec, n, n_escapes, out))
+    _check(lib().splitzip_write_header(codec, book, n, n_escapes, out))
     return bytes(out)
 
 
@@ -191,8 +265,11 @@ def splitzip_read_header(buf: bytes) -> dict:
     return {"n": n.value, "chunk_size": c.value, "n_escapes": e.value, "codebook": bytes(cb)}
 
 
-def splitzip_check_header(codec: int, buf: bytes) -> None:
-    _check(lib().splitzip_check_header(codec, _u8buf(buf[:HEADER_BYTES]), len(buf)))
+def splitzip_check_header(codec: int, buf: bytes) -> int:
+    """Raises unless the codec can decode the stream; returns the book it was coded with."""
+    book = ctypes.c_uint32()
+    _check(lib().splitzip_check_header(codec, _u8buf(buf[:HEADER_BYTES]), len(buf), ctypes.byref(book)))
+    return book.value
 
 
 # ---- README-style stateful codec --------------------------------------------------------
@@ -212,6 +289,7 @@ class Encoded:
     esc_exp_buf: object   # torch.uint8 [capacity]
     n_escapes: int = 0
     compressed_bytes: int = 0
+    book: int = 0         # which of the codec's codebooks
 
     @property
     def esc_pos(self):
@@ -229,12 +307,12 @@ class Encoded:
         return splitzip_segment(data_ptr or None, self.n, _ptr(self.sm), _ptr(self.codes),
                                 _ptr(self.chunk_off), _ptr(self.esc_pos_buf),
                                 _ptr(self.esc_exp_buf), self.esc_pos_buf.numel(),
-                                self.n_escapes, self.compressed_bytes)
+                                self.n_escapes, self.compressed_bytes, self.book, 0)
 
     def to_bytes(self, codec: "Codec") -> bytes:
         """Canonical serialized stream: 64-byte header, then the five sections."""
         import torch
-        head = splitzip_write_header(codec.handle, self.n, self.n_escapes)
+        head = splitzip_write_header(codec.handle, self.book, self.n, self.n_escapes)
         parts = [self.sm, self.codes, self.chunk_off.view(torch.uint8),
                  self.esc_pos.contiguous().view(torch.uint8), self.esc_exp]
         body = b"".join(p.cpu().numpy().tobytes() for p in parts)
@@ -288,8 +366,23 @@ class Codec:
 
     @property
     def codebook(self) -> bytes:
+        """Codebook of book 0 (the only one after ``calibrate``)."""
         self._need_handle()
         return splitzip_codec_info(self.handle)[0]
+
+    @property
+    def books(self) -> list:
+        """All codebooks, 16 bytes each."""
+        self._need_handle()
+        return splitzip_codec_books(self.handle)
+
+    @classmethod
+    def from_codebooks(cls, codebooks, chunk_size: int = 1024, device="cuda") -> "Codec":
+        import torch
+        c = cls(device, chunk_size)
+        with torch.cuda.device(c.device):
+            c.handle = splitzip_codec_from_codebooks(b"".join(bytes(b) for b in codebooks), chunk_size)
+        return c
 
     def _need_handle(self):
         if not self.handle:
@@ -331,9 +424,25 @@ class Codec:
         self._escape_rate = 1.0 - cov if w.numel() else 0.0
         return cov
 
+    def calibrate_books(self, cals) -> list:
+        """One codebook per calibration tensor (e.g. per layer, per K and V), all histograms
+        in one pass; returns the coverage of each.  Segments then pick a book on encode."""
+        import torch
+        ws = [_words(x, self.device) for x in cals]
+        with torch.cuda.device(self.device):
+            h, cov, hist = splitzip_calibrate_books([w.data_ptr() if w.numel() else 0 for w in ws],
+                                                    [w.numel() for w in ws], self.chunk_size,
+                                                    self._stream())
+        splitzip_free(self.handle)
+        self.handle, self.coverage, self.histogram = h, cov, hist
+        rates = [1.0 - c for c, w in zip(cov, ws) if w.numel()]
+        self._escape_rate = max(rates) if rates else 0.0
+        return cov
+
     # -- a2-a4, a7 -----------------------------------------------------------------
-    def empty_encoded(self, n: int, shape=None, dtype=None, escape_capacity: int | None = None):
-        """Allocate the device sections for an n-word tensor."""
+    def empty_encoded(self, n: int, shape=None, dtype=None, escape_capacity: int | None = None,
+                      book: int = 0):
+        """Allocate the device sections for an n-word tensor coded with codebook `book`."""
         import torch
         n_chunks = -(-n // self.chunk_size)
         if escape_capacity is None:
@@ -343,7 +452,7 @@ class Codec:
         return Encoded(
             n=n, shape=tuple(shape) if shape is not None else (n,),
             dtype=dtype if dtype is not None else torch.bfloat16,
-            chunk_size=self.chunk_size, codebook=self.codebook,
+            chunk_size=self.chunk_size, codebook=self.books[book], book=book,
             sm=torch.empty(n, dtype=torch.uint8, **kw),
             codes=torch.empty((n + 1) // 2, dtype=torch.uint8, **kw),
             chunk_off=torch.empty(n_chunks + 1, dtype=torch.int64, **kw),
@@ -405,18 +514,23 @@ class Codec:
         outputs) so that repeated encode/decode calls skip the per-call argument marshalling."""
         return PreparedBatch(self, xs, encs, outs)
 
-    def encode(self, x, escape_capacity: int | None = None) -> Encoded:
-        return self.encode_batch([x], escape_capacity)[0]
+    def encode(self, x, escape_capacity: int | None = None, book: int = 0) -> Encoded:
+        return self.encode_batch([x], escape_capacity, [book])[0]
 
-    def encode_batch(self, xs, escape_capacity: int | None = None) -> list:
-        """Encode several tensors (a ragged batch) in one launch."""
+    def encode_batch(self, xs, escape_capacity: int | None = None, books=None) -> list:
+        """Encode several tensors (a ragged batch) in one launch; books[i] (default 0) is
+        the codebook of tensor i."""
         self._need_handle()
-        encs = [self.empty_encoded(x.numel(), x.shape, x.dtype, escape_capacity) for x in xs]
+        books = list(books) if books is not None else [0] * len(xs)
+        if len(books) != len(xs):
+            raise ValueError("one book per tensor")
+        encs = [self.empty_encoded(x.numel(), x.shape, x.dtype, escape_capacity, b)
+                for x, b in zip(xs, books)]
         st = self.encode_into(xs, encs)
         if st == E_CAPACITY:
             for i, e in enumerate(encs):
                 if e.n_escapes > e.esc_pos_buf.numel():
-                    encs[i] = self.empty_encoded(e.n, e.shape, e.dtype, e.n_escapes)
+                    encs[i] = self.empty_encoded(e.n, e.shape, e.dtype, e.n_escapes, e.book)
             st = self.encode_into(xs, encs)
             assert st == OK
         total = sum(e.n for e in encs)
@@ -429,11 +543,12 @@ class Codec:
         import torch
         self._need_handle()
         segs = (splitzip_segment * len(encs))()
+        books = self.books
         for i, (e, y) in enumerate(zip(encs, outs)):
             w = _words(y, self.device)
             if w.numel() != e.n:
                 raise ValueError("output size differs from the encoded tensor")
-            if e.chunk_size != self.chunk_size or e.codebook != self.codebook:
+            if e.chunk_size != self.chunk_size or e.book >= len(books) or e.codebook != books[e.book]:
                 raise SplitZipError(E_CODEBOOK, "encoded with a different codec state")
             segs[i] = e.segment(w.data_ptr() if w.numel() else 0)
         with torch.cuda.device(self.device):
@@ -453,11 +568,11 @@ class Codec:
         import numpy as np
         import torch
         self._need_handle()
-        splitzip_check_header(self.handle, buf)
+        book = splitzip_check_header(self.handle, buf)
         h = splitzip_read_header(buf)
         n, E = h["n"], h["n_escapes"]
         n_chunks = splitzip_chunk_count(n, self.chunk_size)
-        enc = self.empty_encoded(n, shape, dtype, max(E, 1))
+        enc = self.empty_encoded(n, shape, dtype, max(E, 1), book)
         b = np.frombuffer(buf, np.uint8)
         p = HEADER_BYTES
         sizes = [n, (n + 1) // 2, 8 * (n_chunks + 1), 2 * E, E]
@@ -516,3 +631,22 @@ class PreparedBatch:
             raise ValueError("no decode outputs were given")
         with self._torch.cuda.device(self.codec.device):
             splitzip_decode(self.codec.handle, self._dec, self.codec._stream(), d_error)
+
+
+# ---- exponent statistics ----------------------------------------------------------------
+
+def histograms(xs, device=None) -> list:
+    """Exponent histograms (256 bins each) of BF16 device tensors, one pass on the GPU."""
+    import torch
+    if not torch.cuda.is_available():
+        raise SplitZipError(E_DEVICE, "no GPU: histograms run only on the GPU")
+    dev = torch.device(device) if device is not None else xs[0].device
+    ws = [_words(x, dev) for x in xs]
+    with torch.cuda.device(dev):
+        return splitzip_histogram([w.data_ptr() if w.numel() else 0 for w in ws],
+                                  [w.numel() for w in ws], torch.cuda.current_stream(dev).cuda_stream)
+
+
+def exponent_stats(hist) -> dict:
+    """Entropy in bits, top-16 codebook, coverage and distinct exponents of a histogram."""
+    return splitzip_exponent_stats(hist)

@@ -5,7 +5,8 @@
 // calibrated once (top-16 exponent codebook, coverage), then used for any number of
 // encode/decode calls whose outputs belong to that codec state.  This file owns:
 //   - argument validation and status/error reporting (never throws across the ABI);
-//   - codebook selection from the GPU histogram (count descending, exponent ascending);
+//   - codebook selection from the GPU histogram (count descending, exponent ascending),
+//     one codebook or several per codec, and the exponent statistics of a histogram;
 //   - per-stream workspaces: encode scratch (per-tile escape slots and counts, overflow
 //     area, segmented sums), per-segment escape counts, pinned descriptor staging for
 //     ragged batches;
@@ -15,6 +16,7 @@
 #include <splitzip.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -161,8 +163,10 @@ struct splitzip_codec {
     bool profiling = false;
     uint32_t chunk_size = 0;
     uint32_t log2_chunk = 0;
-    uint8_t cb[16] = {};
-    uint8_t *d_lut = nullptr;   // device [256] inverse LUT
+    uint32_t n_books = 0;
+    std::vector<uint8_t> cbs;   // [16 * n_books] codebooks
+    uint8_t *d_lut = nullptr;   // device [256 * n_books] inverse LUTs
+    uint32_t *d_cbs = nullptr;  // device [4 * n_books] codebooks as little-endian dwords
     std::mutex mu;
     std::map<hipStream_t, std::unique_ptr<Workspace>> ws;
 };
@@ -187,8 +191,8 @@ bool codebook_distinct(const uint8_t cb[16])
     return true;
 }
 
-int make_codec(const uint8_t cb[16], uint32_t chunk_size, int device, hipStream_t stream,
-               splitzip_codec **out)
+int make_codec(const uint8_t *cbs, uint32_t n_books, uint32_t chunk_size, int device,
+               hipStream_t stream, splitzip_codec **out)
 {
     std::unique_ptr<splitzip_codec> c(new (std::nothrow) splitzip_codec);
     if (!c)
@@ -196,20 +200,95 @@ int make_codec(const uint8_t cb[16], uint32_t chunk_size, int device, hipStream_
     c->device = device;
     c->chunk_size = chunk_size;
     c->log2_chunk = log2u(chunk_size);
-    std::memcpy(c->cb, cb, 16);
-    uint8_t lut[256];
-    std::memset(lut, sz::kEscapeEntry, sizeof lut);
-    for (int k = 0; k < 16; ++k)
-        lut[cb[k]] = (uint8_t)k;
-    SZ_HIP(hipMalloc(&c->d_lut, 256), "hipMalloc(codec tables)");
-    hipError_t e = hipMemcpyAsync(c->d_lut, lut, 256, hipMemcpyHostToDevice, stream);
+    c->n_books = n_books;
+    c->cbs.assign(cbs, cbs + 16 * (size_t)n_books);
+    // inverse LUT of each book: exponent -> code, or the escape entry
+    std::vector<uint8_t> lut(256 * (size_t)n_books, sz::kEscapeEntry);
+    for (uint32_t b = 0; b < n_books; ++b)
+        for (int k = 0; k < 16; ++k)
+            lut[256 * (size_t)b + cbs[16 * (size_t)b + k]] = (uint8_t)k;
+    SZ_HIP(hipMalloc(&c->d_lut, lut.size()), "hipMalloc(codec tables)");
+    hipError_t e = hipMalloc(&c->d_cbs, c->cbs.size());
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(c->d_lut, lut.data(), lut.size(), hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(c->d_cbs, c->cbs.data(), c->cbs.size(), hipMemcpyHostToDevice, stream);
     if (e == hipSuccess)
         e = hipStreamSynchronize(stream);
     if (e != hipSuccess) {
         (void)hipFree(c->d_lut);
+        (void)hipFree(c->d_cbs);
         return fail_hip(e, "upload of codec tables");
     }
     *out = c.release();
+    return SPLITZIP_OK;
+}
+
+// Rank all 256 exponents by count (descending), ties by exponent (ascending); the first 16
+// are the codebook.  Returns how many of the counted exponents it holds.
+uint64_t pick_codebook(const uint64_t hist[256], uint8_t cb[16])
+{
+    int order[256];
+    for (int e = 0; e < 256; ++e)
+        order[e] = e;
+    std::stable_sort(order, order + 256, [&](int a, int b) { return hist[a] > hist[b]; });
+    uint64_t covered = 0;
+    for (int k = 0; k < 16; ++k) {
+        cb[k] = (uint8_t)order[k];
+        covered += hist[order[k]];
+    }
+    return covered;
+}
+
+// Exponent histograms of n_seg tensors into host hist[256 * n_seg]; blocks.
+int run_histograms(uint32_t n_seg, const uint16_t *const *d_x, const uint64_t *n,
+                   hipStream_t stream, uint64_t *hist)
+{
+    std::vector<sz::HistSeg> segs(n_seg);
+    std::vector<uint32_t> start((size_t)n_seg + 1);
+    uint64_t blocks = 0;
+    for (uint32_t s = 0; s < n_seg; ++s) {
+        if (n[s] > 0 && (!d_x[s] || !aligned(d_x[s], 16)))
+            return fail(SPLITZIP_E_INVALID, "tensor %u: pointer NULL or not 16-byte aligned", s);
+        segs[s] = sz::HistSeg{n[s] ? d_x[s] : nullptr, n[s]};
+        start[s] = (uint32_t)blocks;
+        blocks += sz::hist_blocks(n[s]);
+        if (blocks > 0x7FFFFFFFull)
+            return fail(SPLITZIP_E_INVALID, "too many tensors in one call");
+    }
+    start[n_seg] = (uint32_t)blocks;
+    // one device allocation: partial counts, histograms, then the tables
+    auto up = [](uint64_t x) { return (x + 255) & ~uint64_t(255); };
+    const uint64_t off_hist = up(blocks * 256 * sizeof(uint32_t));
+    const uint64_t off_segs = up(off_hist + (uint64_t)n_seg * 256 * sizeof(uint64_t));
+    const uint64_t off_start = up(off_segs + (uint64_t)n_seg * sizeof(sz::HistSeg));
+    const uint64_t total = off_start + ((uint64_t)n_seg + 1) * sizeof(uint32_t);
+    uint8_t *d = nullptr;
+    SZ_HIP(hipMalloc(&d, total), "hipMalloc(histogram scratch)");
+    sz::HistArgs a{};
+    a.seg0 = segs[0];
+    a.segs = reinterpret_cast<const sz::HistSeg *>(d + off_segs);
+    a.block_start = reinterpret_cast<const uint32_t *>(d + off_start);
+    a.partial = reinterpret_cast<uint32_t *>(d);
+    a.hist = reinterpret_cast<uint64_t *>(d + off_hist);
+    a.n_seg = n_seg;
+    a.n_blocks = (uint32_t)blocks;
+    hipError_t e = hipSuccess;
+    if (n_seg > 1) {
+        e = hipMemcpyAsync(d + off_segs, segs.data(), n_seg * sizeof(sz::HistSeg), hipMemcpyHostToDevice, stream);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(d + off_start, start.data(), start.size() * sizeof(uint32_t),
+                               hipMemcpyHostToDevice, stream);
+    }
+    if (e == hipSuccess)
+        e = sz::launch_histogram(a, stream);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(hist, a.hist, (size_t)n_seg * 256 * sizeof(uint64_t), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(stream);
+    (void)hipFree(d);
+    if (e != hipSuccess)
+        return fail_hip(e, "exponent histogram");
     return SPLITZIP_OK;
 }
 
@@ -437,15 +516,27 @@ int prepare_segments_tiled(const splitzip_codec *c, uint32_t n_seg, const splitz
         if (!encode && g.n_escapes > g.n)
             return fail(SPLITZIP_E_FORMAT, "segment %u: %llu escapes for %llu words", i,
                         (unsigned long long)g.n_escapes, (unsigned long long)g.n);
-        desc[i] = sz::SegDesc{g.data, g.sm, g.codes, g.chunk_off, g.esc_pos, g.esc_exp, g.n, esc};
+        if (g.book >= c->n_books)
+            return fail(SPLITZIP_E_INVALID, "segment %u: book %u, the codec has %u", i, g.book,
+                        c->n_books);
+        desc[i] = sz::SegDesc{g.data, g.sm, g.codes, g.chunk_off, g.esc_pos, g.esc_exp, g.n, esc,
+                              g.book, 0u};
         tiles[i] = (uint32_t)total;
         total += std::max<uint64_t>(1, ceil_div(g.n, tile_words));
         if (total > 0xFFFFFFF0ull)
             return fail(SPLITZIP_E_INVALID, "too many tiles in one call");
     }
     tiles[n_seg] = (uint32_t)total;
-    (void)c;
     return SPLITZIP_OK;
+}
+
+// The one book every segment uses, or -1 when they differ.
+int64_t common_book(uint32_t n_seg, const splitzip_segment *segs)
+{
+    for (uint32_t i = 1; i < n_seg; ++i)
+        if (segs[i].book != segs[0].book)
+            return -1;
+    return segs[0].book;
 }
 
 int prepare_segments(const splitzip_codec *c, uint32_t n_seg, const splitzip_segment *segs,
@@ -463,74 +554,128 @@ int prepare_segments(const splitzip_codec *c, uint32_t n_seg, const splitzip_seg
 
 extern "C" {
 
-int splitzip_calibrate(const uint16_t *d_cal, uint64_t n_cal, uint32_t chunk_size, void *stream_,
-                       splitzip_codec **out_codec, double *out_coverage, uint64_t *out_hist)
+int splitzip_calibrate_books(uint32_t n_books, const uint16_t *const *d_cal, const uint64_t *n_cal,
+                             uint32_t chunk_size, void *stream_, splitzip_codec **out_codec,
+                             double *coverage, uint64_t *hist)
 {
     g_last_error.clear();
     if (!out_codec)
         return fail(SPLITZIP_E_INVALID, "out_codec is NULL");
+    if (n_books == 0 || n_books > SPLITZIP_MAX_BOOKS)
+        return fail(SPLITZIP_E_INVALID, "n_books %u outside 1..%u", n_books, SPLITZIP_MAX_BOOKS);
+    if (!d_cal || !n_cal)
+        return fail(SPLITZIP_E_INVALID, "d_cal or n_cal is NULL");
     if (!chunk_size_ok(chunk_size))
         return fail(SPLITZIP_E_INVALID, "chunk_size %u is not a power of two in [16, 65536]", chunk_size);
-    if (n_cal > 0 && (!d_cal || !aligned(d_cal, 16)))
-        return fail(SPLITZIP_E_INVALID, "calibration pointer NULL or not 16-byte aligned");
+    for (uint32_t b = 0; b < n_books; ++b)
+        if (n_cal[b] > 0 && (!d_cal[b] || !aligned(d_cal[b], 16)))
+            return fail(SPLITZIP_E_INVALID, "calibration tensor %u: pointer NULL or not 16-byte aligned", b);
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     int device = 0;
     SZ_HIP(hipGetDevice(&device), "hipGetDevice");
-
-    uint64_t hist[256] = {};
-    if (n_cal > 0) {
-        const uint32_t blocks = sz::calibrate_blocks(n_cal);
-        uint32_t *d_partial = nullptr;
-        uint64_t *d_hist = nullptr;
-        SZ_HIP(hipMalloc(&d_partial, (size_t)blocks * 256 * sizeof(uint32_t)), "hipMalloc(histogram)");
-        hipError_t e = hipMalloc(&d_hist, 256 * sizeof(uint64_t));
-        if (e == hipSuccess)
-            e = sz::launch_calibrate(d_cal, n_cal, d_partial, blocks, d_hist, stream);
-        if (e == hipSuccess)
-            e = hipMemcpyAsync(hist, d_hist, sizeof hist, hipMemcpyDeviceToHost, stream);
-        if (e == hipSuccess)
-            e = hipStreamSynchronize(stream);
-        (void)hipFree(d_partial);
-        (void)hipFree(d_hist);
-        if (e != hipSuccess)
-            return fail_hip(e, "calibration histogram");
-    }
-    // Rank all 256 exponents by count (descending), ties by exponent (ascending).
-    int order[256];
-    for (int e = 0; e < 256; ++e)
-        order[e] = e;
-    std::stable_sort(order, order + 256, [&](int a, int b) { return hist[a] > hist[b]; });
-    uint8_t cb[16];
-    uint64_t covered = 0;
-    for (int k = 0; k < 16; ++k) {
-        cb[k] = (uint8_t)order[k];
-        covered += hist[order[k]];
-    }
-    splitzip_codec *c = nullptr;
-    int rc = make_codec(cb, chunk_size, device, stream, &c);
+    std::vector<uint64_t> h(256 * (size_t)n_books);
+    int rc = run_histograms(n_books, d_cal, n_cal, stream, h.data());
     if (rc != SPLITZIP_OK)
         return rc;
-    if (out_coverage)
-        *out_coverage = n_cal ? (double)covered / (double)n_cal : 0.0;
-    if (out_hist)
-        std::memcpy(out_hist, hist, sizeof hist);
+    std::vector<uint8_t> cbs(16 * (size_t)n_books);
+    std::vector<double> cov(n_books);
+    for (uint32_t b = 0; b < n_books; ++b) {
+        const uint64_t covered = pick_codebook(&h[256 * (size_t)b], &cbs[16 * (size_t)b]);
+        cov[b] = n_cal[b] ? (double)covered / (double)n_cal[b] : 0.0;
+    }
+    splitzip_codec *c = nullptr;
+    rc = make_codec(cbs.data(), n_books, chunk_size, device, stream, &c);
+    if (rc != SPLITZIP_OK)
+        return rc;
+    if (coverage)
+        std::memcpy(coverage, cov.data(), n_books * sizeof(double));
+    if (hist)
+        std::memcpy(hist, h.data(), h.size() * sizeof(uint64_t));
     *out_codec = c;
     return SPLITZIP_OK;
+}
+
+int splitzip_calibrate(const uint16_t *d_cal, uint64_t n_cal, uint32_t chunk_size, void *stream,
+                       splitzip_codec **out_codec, double *out_coverage, uint64_t *out_hist)
+{
+    return splitzip_calibrate_books(1, &d_cal, &n_cal, chunk_size, stream, out_codec, out_coverage,
+                                    out_hist);
+}
+
+int splitzip_codec_from_codebooks(uint32_t n_books, const uint8_t *codebooks, uint32_t chunk_size,
+                                  splitzip_codec **out_codec)
+{
+    g_last_error.clear();
+    if (!codebooks || !out_codec)
+        return fail(SPLITZIP_E_INVALID, "codebooks or out_codec is NULL");
+    if (n_books == 0 || n_books > SPLITZIP_MAX_BOOKS)
+        return fail(SPLITZIP_E_INVALID, "n_books %u outside 1..%u", n_books, SPLITZIP_MAX_BOOKS);
+    if (!chunk_size_ok(chunk_size))
+        return fail(SPLITZIP_E_INVALID, "chunk_size %u is not a power of two in [16, 65536]", chunk_size);
+    for (uint32_t b = 0; b < n_books; ++b)
+        if (!codebook_distinct(codebooks + 16 * (size_t)b))
+            return fail(SPLITZIP_E_INVALID, "codebook %u: entries are not 16 distinct exponents", b);
+    int device = 0;
+    SZ_HIP(hipGetDevice(&device), "hipGetDevice");
+    return make_codec(codebooks, n_books, chunk_size, device, nullptr, out_codec);
 }
 
 int splitzip_codec_from_codebook(const uint8_t codebook[16], uint32_t chunk_size,
                                  splitzip_codec **out_codec)
 {
+    return splitzip_codec_from_codebooks(1, codebook, chunk_size, out_codec);
+}
+
+int splitzip_codec_books(const splitzip_codec *codec, uint32_t *n_books, uint8_t *codebooks)
+{
+    int rc = codec_check(codec);
+    if (rc != SPLITZIP_OK)
+        return rc;
+    if (n_books)
+        *n_books = codec->n_books;
+    if (codebooks)
+        std::memcpy(codebooks, codec->cbs.data(), codec->cbs.size());
+    return SPLITZIP_OK;
+}
+
+int splitzip_histogram(uint32_t n_seg, const uint16_t *const *d_x, const uint64_t *n, void *stream,
+                       uint64_t *hist)
+{
     g_last_error.clear();
-    if (!codebook || !out_codec)
-        return fail(SPLITZIP_E_INVALID, "codebook or out_codec is NULL");
-    if (!chunk_size_ok(chunk_size))
-        return fail(SPLITZIP_E_INVALID, "chunk_size %u is not a power of two in [16, 65536]", chunk_size);
-    if (!codebook_distinct(codebook))
-        return fail(SPLITZIP_E_INVALID, "codebook entries are not 16 distinct exponents");
-    int device = 0;
-    SZ_HIP(hipGetDevice(&device), "hipGetDevice");
-    return make_codec(codebook, chunk_size, device, nullptr, out_codec);
+    if (n_seg == 0 || !d_x || !n || !hist)
+        return fail(SPLITZIP_E_INVALID, "n_seg is 0 or an array is NULL");
+    return run_histograms(n_seg, d_x, n, static_cast<hipStream_t>(stream), hist);
+}
+
+int splitzip_exponent_stats(const uint64_t hist[256], double *entropy_bits, double *coverage,
+                            uint8_t codebook[16], uint32_t *distinct)
+{
+    g_last_error.clear();
+    if (!hist)
+        return fail(SPLITZIP_E_INVALID, "hist is NULL");
+    uint64_t m = 0;
+    uint32_t d = 0;
+    for (int e = 0; e < 256; ++e) {
+        m += hist[e];
+        d += hist[e] != 0;
+    }
+    double h = 0.0;
+    for (int e = 0; e < 256; ++e)
+        if (hist[e]) {
+            const double p = (double)hist[e] / (double)m;
+            h -= p * std::log2(p);
+        }
+    uint8_t cb[16];
+    const uint64_t covered = pick_codebook(hist, cb);
+    if (entropy_bits)
+        *entropy_bits = h;
+    if (coverage)
+        *coverage = m ? (double)covered / (double)m : 0.0;
+    if (codebook)
+        std::memcpy(codebook, cb, 16);
+    if (distinct)
+        *distinct = d;
+    return SPLITZIP_OK;
 }
 
 int splitzip_codec_info(const splitzip_codec *codec, uint8_t codebook[16], uint32_t *chunk_size,
@@ -540,7 +685,7 @@ int splitzip_codec_info(const splitzip_codec *codec, uint8_t codebook[16], uint3
     if (rc != SPLITZIP_OK)
         return rc;
     if (codebook)
-        std::memcpy(codebook, codec->cb, 16);
+        std::memcpy(codebook, codec->cbs.data(), 16);
     if (chunk_size)
         *chunk_size = codec->chunk_size;
     if (device)
@@ -585,7 +730,10 @@ int encode_launch(splitzip_codec *codec, uint32_t n_seg, const splitzip_segment 
     if (n_seg > 1 && (rc = stage_descriptors(w, desc, tiles, &a.segs, &a.tile_start)) != SPLITZIP_OK)
         return rc;
     uint8_t *res = d_result ? reinterpret_cast<uint8_t *>(d_result) : w->result;
-    a.lut = codec->d_lut;
+    // one book for the whole call: its LUT directly; several: the table, indexed per segment
+    const int64_t book = common_book(n_seg, segs);
+    a.lut = codec->d_lut + 256 * (book < 0 ? 0 : book);
+    a.multi_book = book < 0;
     a.tile_count = reinterpret_cast<uint32_t *>(w->scratch + lay.tile_count);
     a.tile_ovf = reinterpret_cast<uint64_t *>(w->scratch + lay.tile_ovf);
     a.tile_prefix = reinterpret_cast<uint64_t *>(w->scratch + lay.tile_prefix);
@@ -727,7 +875,10 @@ int splitzip_decode(splitzip_codec *codec, uint32_t n_seg, const splitzip_segmen
     }
     if (n_seg > 1 && (rc = stage_descriptors(w, desc, tiles, &a.segs, &a.tile_start)) != SPLITZIP_OK)
         return rc;
-    std::memcpy(a.cb, codec->cb, 16);
+    const int64_t book = common_book(n_seg, segs);
+    std::memcpy(a.cb, codec->cbs.data() + 16 * (book < 0 ? 0 : book), 16);
+    a.cbs = codec->d_cbs;
+    a.multi_book = book < 0;
     a.err = d_error;
     a.n_seg = n_seg;
     a.n_tiles = tiles[n_seg];
@@ -810,6 +961,7 @@ void splitzip_free(splitzip_codec *codec)
         DeviceGuard dg(codec->device);
         codec->ws.clear();
         (void)hipFree(codec->d_lut);
+        (void)hipFree(codec->d_cbs);
     }
     codec->magic = 0;
     delete codec;
@@ -841,8 +993,8 @@ static uint64_t le_get(const uint8_t *p, int bytes)
     return v;
 }
 
-int splitzip_write_header(const splitzip_codec *codec, uint64_t n, uint64_t n_escapes,
-                          uint8_t out[SPLITZIP_HEADER_BYTES])
+int splitzip_write_header(const splitzip_codec *codec, uint32_t book, uint64_t n,
+                          uint64_t n_escapes, uint8_t out[SPLITZIP_HEADER_BYTES])
 {
     g_last_error.clear();
     int rc = codec_check(codec);
@@ -850,6 +1002,8 @@ int splitzip_write_header(const splitzip_codec *codec, uint64_t n, uint64_t n_es
         return rc;
     if (!out)
         return fail(SPLITZIP_E_INVALID, "out is NULL");
+    if (book >= codec->n_books)
+        return fail(SPLITZIP_E_INVALID, "book %u, the codec has %u", book, codec->n_books);
     std::memset(out, 0, SPLITZIP_HEADER_BYTES);
     std::memcpy(out, "SZB1", 4);
     le_put(out + 4, 1, 2);
@@ -859,7 +1013,7 @@ int splitzip_write_header(const splitzip_codec *codec, uint64_t n, uint64_t n_es
     le_put(out + 16, n, 8);
     le_put(out + 24, ceil_div(n, codec->chunk_size), 8);
     le_put(out + 32, n_escapes, 8);
-    std::memcpy(out + 40, codec->cb, 16);
+    std::memcpy(out + 40, codec->cbs.data() + 16 * (size_t)book, 16);
     return SPLITZIP_OK;
 }
 
@@ -895,7 +1049,8 @@ int splitzip_read_header(const uint8_t *buf, uint64_t total_len, uint64_t *n, ui
     return SPLITZIP_OK;
 }
 
-int splitzip_check_header(const splitzip_codec *codec, const uint8_t *buf, uint64_t total_len)
+int splitzip_check_header(const splitzip_codec *codec, const uint8_t *buf, uint64_t total_len,
+                          uint32_t *book)
 {
     int rc = codec_check(codec);
     if (rc != SPLITZIP_OK)
@@ -905,9 +1060,15 @@ int splitzip_check_header(const splitzip_codec *codec, const uint8_t *buf, uint6
     rc = splitzip_read_header(buf, total_len, nullptr, &c, nullptr, cb);
     if (rc != SPLITZIP_OK)
         return rc;
-    if (c != codec->chunk_size || std::memcmp(cb, codec->cb, 16) != 0)
-        return fail(SPLITZIP_E_CODEBOOK, "stream codebook or chunk size differs from the codec's");
-    return SPLITZIP_OK;
+    if (c != codec->chunk_size)
+        return fail(SPLITZIP_E_CODEBOOK, "stream chunk size %u, the codec's is %u", c, codec->chunk_size);
+    for (uint32_t b = 0; b < codec->n_books; ++b)
+        if (std::memcmp(cb, codec->cbs.data() + 16 * (size_t)b, 16) == 0) {
+            if (book)
+                *book = b;
+            return SPLITZIP_OK;
+        }
+    return fail(SPLITZIP_E_CODEBOOK, "stream codebook is none of the codec's");
 }
 
 const char *splitzip_status_string(int status)

@@ -59,13 +59,16 @@ struct SegDesc {
     uint8_t *esc_exp;
     uint64_t n;
     uint64_t esc;           // encode: escape capacity; decode: E
+    uint32_t book;          // the segment's codebook (read only when multi_book is set)
+    uint32_t pad;
 };
 
 struct EncodeArgs {
     SegDesc seg0;                 // the only segment when n_seg == 1
     const SegDesc *segs;          // device table when n_seg > 1
     const uint32_t *tile_start;   // device [n_seg + 1] first tile of each segment
-    const uint8_t *lut;           // device [256] inverse LUT (code, or kEscapeEntry)
+    const uint8_t *lut;           // device inverse LUT (code, or kEscapeEntry): [256], or
+                                  // [256 * books] indexed by SegDesc::book when multi_book
     uint32_t *tile_count;         // [n_tiles] escapes per tile
     uint64_t *tile_ovf;           // [n_tiles] overflow offset of tiles past kSlotEscapes
     uint64_t *tile_prefix;        // [n_tiles] escape offset in the segment (overflow tiles)
@@ -82,7 +85,7 @@ struct EncodeArgs {
     uint32_t n_seg;
     uint32_t n_tiles;
     uint32_t log2_chunk;
-    uint32_t pad;
+    uint32_t multi_book;          // segments use different codebooks
 };
 
 struct DecodeArgs {
@@ -90,19 +93,35 @@ struct DecodeArgs {
     const SegDesc *segs;
     const uint32_t *tile_start;
     uint32_t *err;                // optional
+    const uint32_t *cbs;          // device [4 * books] codebooks, read when multi_book
     uint32_t cb[4];               // codebook bytes 0..15 as 4 little-endian words
     uint32_t n_seg;
     uint32_t n_tiles;
     uint32_t log2_chunk;
-    uint32_t pad;
+    uint32_t multi_book;
 };
 
-// Calibration histogram: per-workgroup partial counts, then one reduction.
-constexpr int kCalibBlocksMax = 1024;
+// Exponent histograms of one or more tensors: per-workgroup partial counts (each tensor
+// gets up to kHistBlocksMax workgroups), then one reduction per (tensor, exponent).
+constexpr int kHistBlocksMax = 1024;
 
-hipError_t launch_calibrate(const uint16_t *d_x, uint64_t n, uint32_t *d_partial,
-                            uint32_t n_blocks, uint64_t *d_hist, hipStream_t stream);
-uint32_t calibrate_blocks(uint64_t n);
+struct HistSeg {
+    const uint16_t *x;
+    uint64_t n;
+};
+
+struct HistArgs {
+    HistSeg seg0;                   // the only tensor when n_seg == 1
+    const HistSeg *segs;            // device [n_seg] when n_seg > 1
+    const uint32_t *block_start;    // device [n_seg + 1] first workgroup of each tensor
+    uint32_t *partial;              // [n_blocks * 256]
+    uint64_t *hist;                 // OUT [n_seg * 256]
+    uint32_t n_seg;
+    uint32_t n_blocks;
+};
+
+uint32_t hist_blocks(uint64_t n);
+hipError_t launch_histogram(const HistArgs &a, hipStream_t stream);
 // Encode stages, launched in order 0 (pack), 1 (sums), 2 (place), 3 (spill) on one stream.
 constexpr int kEncodeStages = 4;
 hipError_t launch_encode_stage(int stage, const EncodeArgs &a, hipStream_t stream);

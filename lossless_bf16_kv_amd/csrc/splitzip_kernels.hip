@@ -14,8 +14,9 @@
 //     bytes gathered with v_perm_b32, codes packed two per byte;
 //   - encode: escape ranks inside a tile by a wave prefix of packed per-group counts plus
 //     an LDS prefix over the 4 waves; the tile's escapes go compacted to a scratch slot, and
-//     two small launches turn the per-tile counts into global offsets (segmented sums) and
-//     move the escapes into place, so no workgroup ever waits on another;
+//     three small launches turn the per-tile counts into global offsets (segmented sums),
+//     move the escapes into place and move those of escape-heavy tiles, so no workgroup
+//     ever waits on another;
 //   - decode: codebook lookup with two v_perm_b32 byte selects per 4 codes (codebook in
 //     SGPRs), exponent bytes staged in LDS only for tiles that hold escapes, where the
 //     escapes overwrite them before the words are assembled.
@@ -141,25 +142,36 @@ __device__ uint32_t find_segment_block(const uint32_t *tile_start, uint32_t n_se
 }
 
 // ======================================================================================
-// a1  calibration histogram
+// a1  exponent histograms (calibration, and the per-tensor exponent statistics)
 // ======================================================================================
 
-__global__ __launch_bounds__(kThreads) void calib_hist_kernel(const uint16_t *__restrict__ x,
-                                                              uint64_t n,
-                                                              uint32_t *__restrict__ partial)
+// Workgroup b histograms its share of one tensor (grid-stride over that tensor's groups of
+// 8 words) into per-wave LDS sub-histograms and writes the 256 sums to partial[b].
+__global__ __launch_bounds__(kThreads) void hist_kernel(const HistArgs a)
 {
     // one sub-histogram per wave keeps LDS atomic contention on the few hot exponents down
     __shared__ uint32_t h[kWaves][256];
+    __shared__ uint32_t s_cnt[kWaves];
     const uint32_t tid = threadIdx.x;
+    const uint32_t lane = lane_id();
+    const uint32_t b = blockIdx.x;
     for (uint32_t i = tid; i < kWaves * 256; i += kThreads)
         (&h[0][0])[i] = 0;
+    HistSeg sg = a.seg0;
+    uint32_t first = 0, nb = a.n_blocks;
+    if (a.n_seg > 1) {
+        const uint32_t s = find_segment_block(a.block_start, a.n_seg, b, tid, lane, s_cnt);
+        first = a.block_start[s];
+        nb = a.block_start[s + 1] - first;
+        sg = a.segs[s];
+    }
     __syncthreads();
     uint32_t *mine = h[tid >> 6];
 
-    const uint64_t groups = n / kGroupWords;
-    const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-    for (uint64_t g = (uint64_t)blockIdx.x * kThreads + tid; g < groups; g += stride) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(x + g * kGroupWords);
+    const uint64_t groups = sg.n / kGroupWords;
+    const uint64_t stride = (uint64_t)nb * kThreads;
+    for (uint64_t g = (uint64_t)(b - first) * kThreads + tid; g < groups; g += stride) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(sg.x + g * kGroupWords);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -167,68 +179,71 @@ __global__ __launch_bounds__(kThreads) void calib_hist_kernel(const uint16_t *__
             atomicAdd(&mine[(w[k] >> 23) & 0xFFu], 1u);
         }
     }
-    // ragged tail (fewer than 8 words), handled by the first workgroup
-    if (blockIdx.x == 0 && tid < n - groups * kGroupWords)
-        atomicAdd(&mine[(x[groups * kGroupWords + tid] >> 7) & 0xFFu], 1u);
+    // ragged tail (fewer than 8 words), handled by the tensor's first workgroup
+    if (b == first && tid < sg.n - groups * kGroupWords)
+        atomicAdd(&mine[(sg.x[groups * kGroupWords + tid] >> 7) & 0xFFu], 1u);
     __syncthreads();
     for (uint32_t e = tid; e < 256; e += kThreads) {
-        uint32_t s = 0;
+        uint32_t sum = 0;
         for (int w = 0; w < kWaves; ++w)
-            s += h[w][e];
-        partial[(uint64_t)blockIdx.x * 256 + e] = s;
+            sum += h[w][e];
+        a.partial[(uint64_t)b * 256 + e] = sum;
     }
 }
 
-// One workgroup per exponent value: its threads add up that bin over the partial histograms.
-__global__ __launch_bounds__(kThreads) void calib_reduce_kernel(const uint32_t *__restrict__ partial,
-                                                                uint32_t blocks,
-                                                                uint64_t *__restrict__ hist)
+// One workgroup per (tensor, exponent value): its threads add up that bin over the tensor's
+// partial histograms.
+__global__ __launch_bounds__(kThreads) void hist_reduce_kernel(const HistArgs a)
 {
     __shared__ uint64_t s_wave[kWaves];
-    const uint32_t e = blockIdx.x;
+    const uint32_t s = blockIdx.x >> 8;
+    const uint32_t e = blockIdx.x & 255u;
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = lane_id();
-    uint64_t s = 0;
-    for (uint32_t b = tid; b < blocks; b += kThreads)
-        s += partial[(uint64_t)b * 256 + e];
-    s = wave_total_u64(s, lane);
+    const uint32_t first = a.n_seg > 1 ? a.block_start[s] : 0u;
+    const uint32_t end = a.n_seg > 1 ? a.block_start[s + 1] : a.n_blocks;
+    uint64_t sum = 0;
+    for (uint32_t b = first + tid; b < end; b += kThreads)
+        sum += a.partial[(uint64_t)b * 256 + e];
+    sum = wave_total_u64(sum, lane);
     if (lane == 0)
-        s_wave[tid >> 6] = s;
+        s_wave[tid >> 6] = sum;
     __syncthreads();
     if (tid == 0) {
         uint64_t t = 0;
         for (int w = 0; w < kWaves; ++w)
             t += s_wave[w];
-        hist[e] = t;
+        a.hist[(uint64_t)s * 256 + e] = t;
     }
 }
 
-uint32_t calibrate_blocks(uint64_t n)
+// Workgroups for one tensor of n words: one per 16 K words, at least 1, at most
+// kHistBlocksMax (then each grid-strides).
+uint32_t hist_blocks(uint64_t n)
 {
     const uint64_t per_block = (uint64_t)kThreads * kGroupWords * 8;
     uint64_t b = (n + per_block - 1) / per_block;
     if (b < 1)
         b = 1;
-    if (b > kCalibBlocksMax)
-        b = kCalibBlocksMax;
+    if (b > kHistBlocksMax)
+        b = kHistBlocksMax;
     return (uint32_t)b;
 }
 
-hipError_t launch_calibrate(const uint16_t *d_x, uint64_t n, uint32_t *d_partial,
-                            uint32_t n_blocks, uint64_t *d_hist, hipStream_t stream)
+hipError_t launch_histogram(const HistArgs &a, hipStream_t stream)
 {
-    calib_hist_kernel<<<n_blocks, kThreads, 0, stream>>>(d_x, n, d_partial);
+    hist_kernel<<<a.n_blocks, kThreads, 0, stream>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    calib_reduce_kernel<<<256, kThreads, 0, stream>>>(d_partial, n_blocks, d_hist);
+    hist_reduce_kernel<<<a.n_seg * 256u, kThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 
 // ======================================================================================
 // a2-a4, a7  encode
 //
-// Three launches, none of which waits on another workgroup:
+// Four launches, none of which waits on another workgroup:
 //   pack   (one workgroup per tile of kEncTileWords words): sign+mantissa bytes and codes,
 //          escape ranks inside the tile, escapes written compacted to the tile's scratch slot
 //          (or, past kSlotEscapes, to an overflow area reserved with one atomic), tile-local
@@ -306,11 +321,12 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
     const uint32_t wave = tid >> 6;
     const uint32_t t = blockIdx.x;
 
-    if (tid < 64)
-        reinterpret_cast<uint32_t *>(s_lut)[tid] = reinterpret_cast<const uint32_t *>(a.lut)[tid];
-
     const uint32_t s = a.n_seg > 1 ? find_segment_block(a.tile_start, a.n_seg, t, tid, lane, s_wave_total) : 0u;
     const SegDesc sd = segment_desc(a, s);
+    // the segment's inverse LUT (several codebooks in one call: one LUT per codebook)
+    const uint8_t *lut = a.multi_book ? a.lut + 256u * sd.book : a.lut;
+    if (tid < 64)
+        reinterpret_cast<uint32_t *>(s_lut)[tid] = reinterpret_cast<const uint32_t *>(lut)[tid];
     const uint64_t n = sd.n;
     const uint64_t base = (uint64_t)(t - segment_first_tile(a, s)) << kEncTileShift;
     const uint64_t cmask = (1ull << a.log2_chunk) - 1;
@@ -853,7 +869,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
     const uint32_t log2c = a.log2_chunk;
     const uint64_t C = 1ull << log2c;
     const uint64_t E = sd.esc;
-    const uint32_t cb[4] = {a.cb[0], a.cb[1], a.cb[2], a.cb[3]};
+    uint32_t cb[4] = {a.cb[0], a.cb[1], a.cb[2], a.cb[3]};
+    if (a.multi_book) {
+        // the segment's own codebook (uniform: the same four dwords for the whole tile)
+        const uint32_t *c = a.cbs + 4u * sd.book;
+        cb[0] = c[0];
+        cb[1] = c[1];
+        cb[2] = c[2];
+        cb[3] = c[3];
+    }
 
     // ---- loads ---------------------------------------------------------------------------
     uint2 smv[kDecGroups];

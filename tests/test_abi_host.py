@@ -32,8 +32,9 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_segment_struct_matches_header():
-    # ten 8-byte fields, no padding
-    assert ctypes.sizeof(sz.splitzip_segment) == 80
+    # ten 8-byte fields and two 4-byte ones, no padding
+    assert ctypes.sizeof(sz.splitzip_segment) == 88
+    assert sz.splitzip_segment.book.offset == 80
 
 
 @pytest.mark.parametrize("n,C,E", [(0, 16, 0), (7, 16, 3), (20, 16, 11), (1 << 32, 1024, 12345),
@@ -97,6 +98,62 @@ def test_argument_validation_before_any_device_call():
     assert L.splitzip_codec_from_codebook(cb, 1024, ctypes.byref(h)) == sz.E_INVALID
     L.splitzip_free(None)   # no-op
     assert sz.lib().splitzip_status_string(6) == b"escape capacity exceeded"
+
+
+def test_codebook_and_statistics_validation_before_any_device_call():
+    L = sz.lib()
+    h = ctypes.c_void_p()
+    P = ctypes.c_void_p * 2
+    N = ctypes.c_uint64 * 2
+    ok, bad = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1008)
+    for k in (0, sz.MAX_BOOKS + 1):
+        assert L.splitzip_calibrate_books(k, P(ok, ok), N(8, 8), 1024, None, ctypes.byref(h),
+                                          None, None) == sz.E_INVALID
+    assert L.splitzip_calibrate_books(2, P(ok, bad), N(8, 8), 1024, None, ctypes.byref(h),
+                                      None, None) == sz.E_INVALID
+    assert b"tensor 1" in L.splitzip_last_error()
+    assert L.splitzip_calibrate_books(2, P(ok, ok), N(8, 8), 48, None, ctypes.byref(h),
+                                      None, None) == sz.E_INVALID
+    hist = (ctypes.c_uint64 * 512)()
+    assert L.splitzip_histogram(0, P(ok, ok), N(8, 8), None, hist) == sz.E_INVALID
+    assert L.splitzip_histogram(2, P(bad, ok), N(8, 8), None, hist) == sz.E_INVALID
+    books = list(range(16)) + list(range(16, 32)) + [7] * 16
+    cbs = (ctypes.c_uint8 * 48)(*books)
+    assert L.splitzip_codec_from_codebooks(3, cbs, 1024, ctypes.byref(h)) == sz.E_INVALID
+    assert b"codebook 2" in L.splitzip_last_error()
+    assert L.splitzip_codec_from_codebooks(0, cbs, 1024, ctypes.byref(h)) == sz.E_INVALID
+    out = (ctypes.c_uint8 * 64)()
+    assert L.splitzip_write_header(None, 0, 10, 0, out) == sz.E_INVALID
+    assert L.splitzip_check_header(None, out, 64, None) == sz.E_INVALID
+    assert L.splitzip_exponent_stats(None, None, None, None, None) == sz.E_INVALID
+
+
+def _stats_agree(o, hist):
+    st = sz.exponent_stats(hist)
+    h = np.asarray(hist, np.uint64)
+    want_h = o.entropy(h)
+    assert abs(st["entropy_bits"] - want_h) <= 1e-12 * max(1.0, want_h)
+    assert st["codebook"] == bytes(o.codebook(h))
+    m = int(h.sum())
+    assert st["coverage"] == o.coverage(h, o.codebook(h), m)
+    assert st["distinct"] == int(np.count_nonzero(h))
+
+
+def test_exponent_stats_match_oracle():
+    """The library's host statistics of a histogram (entropy, codebook, coverage, distinct
+    values) against the oracle's on the same histograms."""
+    o = oracle.get()
+    _stats_agree(o, [0] * 256)
+    _stats_agree(o, o.histogram(np.arange(65536, dtype=np.uint16)).tolist())
+    g, cal, x = pins.worked_example()
+    _stats_agree(o, o.histogram(cal).tolist())
+    rng = np.random.default_rng(5)
+    for _ in range(30):
+        h = rng.integers(0, 1 << 40, 256, dtype=np.uint64)
+        h[rng.random(256) < rng.random()] = 0
+        _stats_agree(o, h.tolist())
+    st = sz.exponent_stats(o.histogram(np.arange(65536, dtype=np.uint16)).tolist())
+    assert st["entropy_bits"] == 8.0 and st["coverage"] == 1 / 16 and st["distinct"] == 256
 
 
 def test_no_cpu_fallback():

@@ -42,7 +42,7 @@ def codec_for(cal: np.ndarray, C: int) -> sz.Codec:
 
 
 def assert_same_stream(codec: sz.Codec, enc: sz.Encoded, x: np.ndarray):
-    cb = np.frombuffer(codec.codebook, np.uint8)
+    cb = np.frombuffer(enc.codebook, np.uint8)
     ref = O.encode(x, cb, codec.chunk_size)
     assert enc.n_escapes == ref["n_escapes"]
     assert enc.compressed_bytes == ref["compressed_bytes"]
@@ -256,7 +256,7 @@ def test_config4_escape_stress(C):
 def check_sampled_chunks(codec, enc, x, chunks):
     """Oracle-encode each sampled chunk on its own and compare with the GPU sections."""
     C = codec.chunk_size
-    cb = np.frombuffer(codec.codebook, np.uint8)
+    cb = np.frombuffer(enc.codebook, np.uint8)
     off = host(enc.chunk_off, np.uint64)
     for c in chunks:
         lo, hi = c * C, min((c + 1) * C, x.size)
@@ -272,7 +272,7 @@ def check_sampled_chunks(codec, enc, x, chunks):
 def check_properties(codec, enc, x, hist_x):
     """Size-independent checks: E from the oracle's exact histogram, offsets, sizes."""
     C = codec.chunk_size
-    cb = np.frombuffer(codec.codebook, np.uint8)
+    cb = np.frombuffer(enc.codebook, np.uint8)
     E = int(x.size - sum(int(hist_x[e]) for e in cb))
     assert enc.n_escapes == E
     off = enc.chunk_off

@@ -175,6 +175,14 @@ def config3(layers: int = 64, tokens: int = 32768, cal_tokens: int = 2048,
                     f"layer (seeds [32,l]); chunk {chunk_size}")
 
 
+def kv_parts(flat: np.ndarray, layers: int, tokens: int) -> list:
+    """Views of a [layer][K|V][token][channel] array as its 2 * layers tensors of
+    tokens * 1024 words (layer 0 K, layer 0 V, layer 1 K, ...)."""
+    per = tokens * CHANNELS
+    assert flat.size == 2 * layers * per
+    return [flat[i * per:(i + 1) * per] for i in range(2 * layers)]
+
+
 # ---- config 4: escape stress --------------------------------------------------------------
 
 def special_words(rng: np.random.Generator, count: int) -> np.ndarray:
