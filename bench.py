@@ -47,6 +47,11 @@ def measured_traffic(kernel: str, workload: str):
     return None
 
 
+def workloads_kv_parts(flat, layers, tokens):
+    import workloads
+    return workloads.kv_parts(flat, layers, tokens)
+
+
 def load_workload(args):
     import workloads
     if args.config == 3:
@@ -92,24 +97,32 @@ def roofline(name, bytes_, ms, workload):
             "avg_launch_ms": round(ms, 4)}
 
 
-def cpu_baseline(wl, codebook: bytes, sample_words: int):
-    """The plain single-threaded oracle timed on a bounded prefix of the same workload."""
+def cpu_baseline(segments, codebooks, chunk_size: int, sample_words: int):
+    """The plain single-threaded oracle timed on a bounded prefix of the same workload
+    (the first segments, each with its own codebook, up to sample_words words)."""
     import numpy as np
     import oracle
     o = oracle.get()
-    cb = np.frombuffer(codebook, np.uint8)
-    x = wl.segments[0][:sample_words]
-    t0 = time.perf_counter()
-    enc = o.encode(x, cb, wl.chunk_size)
-    t1 = time.perf_counter()
-    y = o.decode(enc)
-    t2 = time.perf_counter()
-    assert np.array_equal(y, x)
-    gb = 2 * x.size / 1e9
-    return {"value": round(gb / (t2 - t0), 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {x.size} BF16 words of the timed workload, encode + decode, "
+    t_enc = t_dec = 0.0
+    words = 0
+    for x, cb in zip(segments, codebooks):
+        x = x[:sample_words - words]
+        if x.size == 0:
+            break
+        t0 = time.perf_counter()
+        enc = o.encode(x, np.frombuffer(cb, np.uint8), chunk_size)
+        t1 = time.perf_counter()
+        y = o.decode(enc)
+        t2 = time.perf_counter()
+        assert np.array_equal(y, x)
+        t_enc += t1 - t0
+        t_dec += t2 - t1
+        words += x.size
+    gb = 2 * words / 1e9
+    return {"value": round(gb / (t_enc + t_dec), 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {words} BF16 words of the timed workload, encode + decode, "
                       f"single-threaded plain C",
-            "encode_GBps": round(gb / (t1 - t0), 4), "decode_GBps": round(gb / (t2 - t1), 4)}
+            "encode_GBps": round(gb / t_enc, 4), "decode_GBps": round(gb / t_dec, 4)}
 
 
 def main():
@@ -120,6 +133,9 @@ def main():
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--chunk-size", type=int, default=1024)
     ap.add_argument("--layers", type=int, default=64, help="long-prefill KV layers (64 = 8.6 GB)")
+    ap.add_argument("--books", choices=["one", "layer-kv"], default="one",
+                    help="one codebook for the whole input, or (long-prefill KV) one per layer "
+                         "and K/V, each tensor its own segment")
     ap.add_argument("--cpu-sample-words", type=int, default=1 << 30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
@@ -140,13 +156,27 @@ def main():
     dev = torch.device("cuda:0")
     C = wl.chunk_size
 
-    xs = [torch.from_numpy(s.view(np.int16)).to(dev) for s in wl.segments]
-    cal = torch.from_numpy(wl.calibration.view(np.int16)).to(dev)
+    segments, cal_parts, books = wl.segments, [wl.calibration], None
+    if args.books == "layer-kv":
+        if args.config != 3:
+            raise SystemExit("--books layer-kv applies to the long-prefill KV workload (--config 3)")
+        tokens = wl.segments[0].size // (2 * args.layers * 1024)
+        segments = workloads_kv_parts(wl.segments[0], args.layers, tokens)
+        cal_parts = workloads_kv_parts(wl.calibration, args.layers, wl.calibration.size // (2 * args.layers * 1024))
+        books = list(range(len(segments)))
+    xs = [torch.from_numpy(s.view(np.int16)).to(dev) for s in segments]
+    cals = [torch.from_numpy(c.view(np.int16)).to(dev) for c in cal_parts]
     codec = sz.Codec(dev, C)
-    coverage = codec.calibrate(cal)
-    del cal
+    if books is None:
+        coverage = codec.calibrate(cals[0])
+    else:
+        coverage = min(codec.calibrate_books(cals))
+    del cals
+    # exponent statistics of the input itself (one pass on the GPU)
+    hist_in = np.sum(np.array(sz.histograms(xs), dtype=np.uint64), axis=0).tolist()
+    stats_in = sz.exponent_stats(hist_in)
 
-    encs = codec.encode_batch(xs)              # sizes the escape arrays (retry if needed)
+    encs = codec.encode_batch(xs, books=books)  # sizes the escape arrays (retry if needed)
     ys = [torch.empty_like(x) for x in xs]
     result = torch.zeros(1 + len(xs), dtype=torch.int64, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -200,7 +230,7 @@ def main():
     alg = algorithmic_bytes(ns, Es, C)
     wall_s = t1 - t0
     value = 2 * n * args.steps / wall_s / 1e9
-    wname = wl.name + f"_c{C}"
+    wname = wl.name + f"_c{C}" + ("_books_layer_kv" if books is not None else "")
 
     # the spill launch moves only the escapes of escape-heavy tiles (a data-dependent amount)
     kernels = {k: roofline(k, alg[k], ms, wname) for k, (ms, cnt) in ktimes.items()
@@ -232,7 +262,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, codec.codebook, args.cpu_sample_words)
+        cpu = cpu_baseline(segments, [codec.books[e.book] for e in encs], C, args.cpu_sample_words)
 
     out = {
         "metric": "encode & decode GB/s (BF16 in) + % HBM roofline + compression ratio, 8.6 GB KV",
@@ -248,7 +278,7 @@ def main():
         "dtype": "u16",
         "data": "synthetic",
         "config": {"workload": wl.name, "n_words": n, "segments": len(ns), "chunk_size": C,
-                   "bytes_bf16": 2 * n, "description": wl.description},
+                   "codebooks": len(codec.books), "bytes_bf16": 2 * n, "description": wl.description},
         "encode_GBps": round(2 * n / (enc_avg * 1e-3) / 1e9, 2),
         "decode_GBps": round(2 * n / (dec_avg * 1e-3) / 1e9, 2),
         "encode_hbm_frac": ops["encode"]["frac"],
@@ -262,6 +292,8 @@ def main():
         "n_escapes": E,
         "coverage_calibration": coverage,
         "coverage_input": 1 - E / n if n else None,
+        "exponent_entropy_bits": round(stats_in["entropy_bits"], 5),
+        "entropy_bound_ratio": round(16 / (8 + stats_in["entropy_bits"]), 5),
         "roofline": kernels[dominant],
         "roofline_ops": ops,
         "roofline_kernels": kernels,
