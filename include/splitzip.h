@@ -175,6 +175,63 @@ int splitzip_encode_async(splitzip_codec *codec, uint32_t n_seg, const splitzip_
 int splitzip_decode(splitzip_codec *codec, uint32_t n_seg, const splitzip_segment *segs,
                     void *stream, uint32_t *d_error);
 
+/* ---- packed streams: one contiguous device buffer per tensor (README "Roadmap":
+ *      codebook and payload metadata that travel with the payload across a transfer
+ *      boundary) ---- */
+
+/*
+ * One tensor whose compressed form is the canonical stream itself, laid out in one device
+ * buffer exactly as the serialization above: the 64-byte header, sm, codes, chunk_off,
+ * esc_pos[E], esc_exp[E].  Encode writes all of it on the GPU (no host copy, no second
+ * pass); decode reads it there.  The header carries the codebook, so a packed stream is
+ * decoded with its own codebook by any codec of the same chunk size.
+ *
+ *   data          BF16 words, n of them (16-byte aligned).  encode reads, decode writes.
+ *   n             words; a multiple of 16 (then every section of the stream is aligned
+ *                 for vector access; KV tensors with a head dimension that is a multiple
+ *                 of 16 qualify).
+ *   buf           device, 16-byte aligned: the stream.
+ *   buf_bytes     encode: capacity of buf; splitzip_compressed_bytes(n, chunk_size, e)
+ *                 bytes hold up to e escapes (the capacity hint).  decode: the stream's
+ *                 length, which fixes E.
+ *   stream_bytes  blocking encode: OUT, the stream's length (also when it exceeds
+ *                 buf_bytes).  Otherwise ignored.
+ *   n_escapes     blocking encode: OUT, E.  Otherwise ignored.
+ *   book          encode: which codebook of the codec.  decode: ignored.
+ *   reserved      set to 0.
+ */
+typedef struct splitzip_packed {
+    uint16_t *data;
+    uint64_t n;
+    uint8_t *buf;
+    uint64_t buf_bytes;
+    uint64_t stream_bytes;
+    uint64_t n_escapes;
+    uint32_t book;
+    uint32_t reserved;
+} splitzip_packed;
+
+/*
+ * Encode n_seg tensors into packed streams in one launch sequence.  d_result == NULL:
+ * blocking, fills stream_bytes and n_escapes, and returns SPLITZIP_E_CAPACITY if a stream
+ * does not fit its buffer (its escapes are then not written; stream_bytes says how many
+ * bytes it needs).  d_result != NULL: non-blocking, as splitzip_encode_async (E of segment
+ * s in d_result[1 + s]; a stream with splitzip_compressed_bytes(n, chunk_size, E) >
+ * buf_bytes holds no escapes and must be re-encoded into a larger buffer).
+ */
+int splitzip_encode_packed(splitzip_codec *codec, uint32_t n_seg, splitzip_packed *segs,
+                           void *stream, uint64_t *d_result);
+
+/*
+ * Decode n_seg packed streams (buf, buf_bytes) into their data buffers, in one launch.
+ * Asynchronous.  The host checks that buf_bytes fits a stream of n words (else
+ * SPLITZIP_E_FORMAT); the kernel checks each header against n, the chunk size and the E
+ * the length implies, and for a stream whose header does not match writes nothing and ORs
+ * 16 into *d_error (optional).  Other metadata errors are flagged as by splitzip_decode.
+ */
+int splitzip_decode_packed(splitzip_codec *codec, uint32_t n_seg, const splitzip_packed *segs,
+                           void *stream, uint32_t *d_error);
+
 /* Release a codec, its tables and workspaces (NULL is a no-op).  Work that uses the
  * codec must have completed; freeing its device memory synchronizes the device. */
 void splitzip_free(splitzip_codec *codec);

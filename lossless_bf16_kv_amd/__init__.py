@@ -58,6 +58,20 @@ class splitzip_segment(ctypes.Structure):
     ]
 
 
+class splitzip_packed(ctypes.Structure):
+    """Mirror of ``splitzip_packed`` in include/splitzip.h."""
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("n", ctypes.c_uint64),
+        ("buf", ctypes.c_void_p),
+        ("buf_bytes", ctypes.c_uint64),
+        ("stream_bytes", ctypes.c_uint64),
+        ("n_escapes", ctypes.c_uint64),
+        ("book", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
+    ]
+
+
 _lib = None
 
 
@@ -84,6 +98,8 @@ def lib() -> ctypes.CDLL:
     L.splitzip_encode.argtypes = [vp, u32, P(splitzip_segment), vp]
     L.splitzip_encode_async.argtypes = [vp, u32, P(splitzip_segment), vp, vp]
     L.splitzip_decode.argtypes = [vp, u32, P(splitzip_segment), vp, vp]
+    L.splitzip_encode_packed.argtypes = [vp, u32, P(splitzip_packed), vp, vp]
+    L.splitzip_decode_packed.argtypes = [vp, u32, P(splitzip_packed), vp, vp]
     L.splitzip_profile.argtypes = [vp, i32]
     L.splitzip_profile_read.argtypes = [vp, vp, P(ctypes.c_double), P(u64), i32]
     L.splitzip_free.argtypes = [vp]
@@ -102,7 +118,8 @@ def lib() -> ctypes.CDLL:
     L.splitzip_last_error.restype = ctypes.c_char_p
     for f in ("splitzip_calibrate", "splitzip_codec_from_codebook", "splitzip_codec_info",
               "splitzip_calibrate_books", "splitzip_codec_from_codebooks", "splitzip_codec_books",
-              "splitzip_histogram", "splitzip_exponent_stats",
+              "splitzip_histogram", "splitzip_exponent_stats", "splitzip_encode_packed",
+              "splitzip_decode_packed",
               "splitzip_encode", "splitzip_encode_async", "splitzip_decode",
               "splitzip_write_header", "splitzip_profile", "splitzip_profile_read",
               "splitzip_read_header", "splitzip_check_header"):
@@ -222,6 +239,16 @@ def splitzip_decode(codec: int, segs, stream: int = 0, d_error: int = 0) -> None
     _check(lib().splitzip_decode(codec, len(segs), segs, stream or None, d_error or None))
 
 
+def splitzip_encode_packed(codec: int, segs, stream: int = 0, d_result: int = 0) -> int:
+    """Encode a ctypes array of splitzip_packed; blocking (OK or E_CAPACITY) unless d_result."""
+    return _check(lib().splitzip_encode_packed(codec, len(segs), segs, stream or None, d_result or None),
+                  allow=(E_CAPACITY,))
+
+
+def splitzip_decode_packed(codec: int, segs, stream: int = 0, d_error: int = 0) -> None:
+    _check(lib().splitzip_decode_packed(codec, len(segs), segs, stream or None, d_error or None))
+
+
 KERNELS = ("encode_pack", "encode_sums", "encode_place", "encode_spill", "decode")
 
 
@@ -317,6 +344,31 @@ class Encoded:
                  self.esc_pos.contiguous().view(torch.uint8), self.esc_exp]
         body = b"".join(p.cpu().numpy().tobytes() for p in parts)
         return head + body
+
+
+@dataclasses.dataclass
+class Packed:
+    """A tensor compressed into one contiguous device buffer holding the canonical stream
+    (64-byte header with the codebook, then the five sections)."""
+    n: int
+    shape: tuple
+    dtype: object
+    buf: object              # torch.uint8 device buffer (capacity)
+    stream_bytes: int = 0
+    n_escapes: int = 0
+    book: int = 0
+
+    @property
+    def stream(self):
+        """Device view of the stream (its exact length)."""
+        return self.buf[:self.stream_bytes]
+
+    def to_bytes(self) -> bytes:
+        return self.stream.cpu().numpy().tobytes()
+
+    @property
+    def ratio(self) -> float:
+        return 2 * self.n / self.stream_bytes
 
 
 def _ptr(t) -> int | None:
@@ -537,6 +589,77 @@ class Codec:
         if total:
             self._escape_rate = max(self._escape_rate, sum(e.n_escapes for e in encs) / total)
         return encs
+
+    # -- packed streams -------------------------------------------------------------
+    def packed_capacity(self, n: int, escapes: int | None = None) -> int:
+        """Buffer bytes for an n-word packed stream with up to `escapes` escapes (default:
+        a guess from the calibration coverage)."""
+        if escapes is None:
+            n_chunks = -(-n // self.chunk_size)
+            escapes = min(n, max(1024, math.ceil(n * max(self._escape_rate, 1e-4) * 1.25) + 64 * (n_chunks + 1)))
+        return splitzip_compressed_bytes(n, self.chunk_size, escapes)
+
+    def encode_packed(self, x, book: int = 0, capacity: int | None = None) -> Packed:
+        return self.encode_packed_batch([x], [book], None if capacity is None else [capacity])[0]
+
+    def encode_packed_batch(self, xs, books=None, capacities=None) -> list:
+        """Encode tensors (numel a multiple of 16) into packed streams, one launch sequence;
+        a buffer that turns out too small is reallocated and the batch re-encoded."""
+        import torch
+        self._need_handle()
+        books = list(books) if books is not None else [0] * len(xs)
+        words = [_words(x, self.device) for x in xs]
+        caps = list(capacities) if capacities is not None else [self.packed_capacity(w.numel()) for w in words]
+        out = [Packed(w.numel(), tuple(x.shape), x.dtype,
+                      torch.empty(c, dtype=torch.uint8, device=self.device), 0, 0, b)
+               for x, w, c, b in zip(xs, words, caps, books)]
+        for attempt in range(2):
+            segs = (splitzip_packed * len(out))()
+            for i, (w, p) in enumerate(zip(words, out)):
+                segs[i] = splitzip_packed(w.data_ptr() if w.numel() else None, p.n, p.buf.data_ptr(),
+                                          p.buf.numel(), 0, 0, p.book, 0)
+            with torch.cuda.device(self.device):
+                st = splitzip_encode_packed(self.handle, segs, self._stream())
+            for i, p in enumerate(out):
+                p.stream_bytes, p.n_escapes = int(segs[i].stream_bytes), int(segs[i].n_escapes)
+            if st == OK:
+                break
+            for p in out:
+                if p.stream_bytes > p.buf.numel():
+                    p.buf = torch.empty(p.stream_bytes, dtype=torch.uint8, device=self.device)
+        assert st == OK
+        total = sum(p.n for p in out)
+        if total:
+            self._escape_rate = max(self._escape_rate, sum(p.n_escapes for p in out) / total)
+        return out
+
+    def decode_packed(self, stream, n: int | None = None, shape=None, dtype=None):
+        return self.decode_packed_batch([stream], [n], [shape], [dtype])[0]
+
+    def decode_packed_batch(self, streams, ns=None, shapes=None, dtypes=None, d_error: int = 0) -> list:
+        """Decode packed streams (Packed objects, or device uint8 tensors holding a stream
+        with n given) in one launch; each stream is decoded with the codebook in its header."""
+        import torch
+        self._need_handle()
+        k = len(streams)
+        ns, shapes, dtypes = ns or [None] * k, shapes or [None] * k, dtypes or [None] * k
+        outs, segs = [], (splitzip_packed * k)()
+        for i, st in enumerate(streams):
+            buf = st.stream if isinstance(st, Packed) else st
+            n = st.n if isinstance(st, Packed) else ns[i]
+            shape = shapes[i] or (st.shape if isinstance(st, Packed) else (n,))
+            dtype = dtypes[i] or (st.dtype if isinstance(st, Packed) else torch.bfloat16)
+            if buf.dtype != torch.uint8 or buf.device != self.device or not buf.is_contiguous():
+                raise ValueError("a packed stream is a contiguous uint8 tensor on the codec's device")
+            y = torch.empty(shape, dtype=dtype, device=self.device)
+            w = _words(y, self.device)
+            if w.numel() != n:
+                raise ValueError("output shape does not hold n words")
+            outs.append(y)
+            segs[i] = splitzip_packed(w.data_ptr() if n else None, n, buf.data_ptr(), buf.numel(), 0, 0, 0, 0)
+        with torch.cuda.device(self.device):
+            splitzip_decode_packed(self.handle, segs, self._stream(), d_error)
+        return outs
 
     # -- a5-a7 ------------------------------------------------------------------------
     def decode_into(self, encs, outs, d_error: int = 0) -> None:

@@ -390,8 +390,9 @@ struct CallTimer {
 
 // Byte offsets of the encode scratch arrays for one launch.
 struct EncodeScratch {
-    uint64_t tile_count, tile_ovf, tile_prefix, ovf_tiles, slots, block_sum, group_sum, ovf, total;
-    EncodeScratch(uint64_t n_tiles, uint64_t ovf_cap)
+    uint64_t tile_count, tile_ovf, tile_prefix, ovf_tiles, slots, block_sum, group_sum, seg_total,
+        ovf, total;
+    EncodeScratch(uint64_t n_tiles, uint64_t ovf_cap, uint64_t n_seg)
     {
         auto up = [](uint64_t x) { return (x + 255) & ~uint64_t(255); };
         tile_count = 0;
@@ -401,7 +402,8 @@ struct EncodeScratch {
         slots = up(ovf_tiles + 4 * n_tiles);
         block_sum = up(slots + 4 * (uint64_t)sz::kSlotEscapes * n_tiles);
         group_sum = up(block_sum + 8 * ((n_tiles + sz::kSumTiles - 1) / sz::kSumTiles));
-        ovf = up(group_sum + 8 * ((n_tiles + sz::kPlaceTiles - 1) / sz::kPlaceTiles));
+        seg_total = up(group_sum + 8 * ((n_tiles + sz::kPlaceTiles - 1) / sz::kPlaceTiles));
+        ovf = up(seg_total + 8 * n_seg);
         total = up(ovf + 4 * ovf_cap);
     }
 };
@@ -520,7 +522,7 @@ int prepare_segments_tiled(const splitzip_codec *c, uint32_t n_seg, const splitz
             return fail(SPLITZIP_E_INVALID, "segment %u: book %u, the codec has %u", i, g.book,
                         c->n_books);
         desc[i] = sz::SegDesc{g.data, g.sm, g.codes, g.chunk_off, g.esc_pos, g.esc_exp, g.n, esc,
-                              g.book, 0u};
+                              g.book, 0u, nullptr};
         tiles[i] = (uint32_t)total;
         total += std::max<uint64_t>(1, ceil_div(g.n, tile_words));
         if (total > 0xFFFFFFF0ull)
@@ -544,6 +546,77 @@ int prepare_segments(const splitzip_codec *c, uint32_t n_seg, const splitzip_seg
 {
     const uint64_t tile_words = encode ? sz::kEncTileWords : sz::kDecTileWords;
     return prepare_segments_tiled(c, n_seg, segs, encode, tile_words, desc, tiles);
+}
+
+// Byte offsets inside a packed stream of n words (n a multiple of 16): sm, codes and
+// chunk_off at fixed places, then esc_pos[E] and esc_exp[E].
+struct PackedLayout {
+    uint64_t sm, codes, chunk_off, esc_pos, fixed;
+    PackedLayout(uint64_t n, uint32_t chunk_size)
+    {
+        sm = SPLITZIP_HEADER_BYTES;
+        codes = sm + n;
+        chunk_off = codes + n / 2;
+        esc_pos = chunk_off + 8 * (ceil_div(n, chunk_size) + 1);
+        fixed = esc_pos;
+    }
+};
+
+// Validation of packed segments; builds descriptors (SegDesc::header set) and tile starts.
+int prepare_packed(const splitzip_codec *c, uint32_t n_seg, const splitzip_packed *segs, bool encode,
+                   std::vector<sz::SegDesc> &desc, std::vector<uint32_t> &tiles)
+{
+    if (n_seg == 0)
+        return fail(SPLITZIP_E_INVALID, "n_seg is 0");
+    if (!segs)
+        return fail(SPLITZIP_E_INVALID, "segs is NULL");
+    const uint64_t tile_words = encode ? sz::kEncTileWords : sz::kDecTileWords;
+    desc.resize(n_seg);
+    tiles.resize((size_t)n_seg + 1);
+    uint64_t total = 0;
+    for (uint32_t i = 0; i < n_seg; ++i) {
+        const splitzip_packed &g = segs[i];
+        if (g.n >= sz::kMaxSegmentWords || g.n % 16)
+            return fail(SPLITZIP_E_INVALID, "segment %u: n = %llu is not a multiple of 16 below 2^38", i,
+                        (unsigned long long)g.n);
+        if (!g.buf || !aligned(g.buf, 16))
+            return fail(SPLITZIP_E_INVALID, "segment %u: stream buffer NULL or not 16-byte aligned", i);
+        if (g.n > 0 && (!g.data || !aligned(g.data, 16)))
+            return fail(SPLITZIP_E_INVALID, "segment %u: data NULL or not 16-byte aligned", i);
+        if (g.book >= c->n_books)
+            return fail(SPLITZIP_E_INVALID, "segment %u: book %u, the codec has %u", i, g.book,
+                        c->n_books);
+        const PackedLayout L(g.n, c->chunk_size);
+        if (g.buf_bytes < L.fixed)
+            return fail(encode ? SPLITZIP_E_INVALID : SPLITZIP_E_FORMAT,
+                        "segment %u: %llu bytes, the stream of %llu words needs at least %llu", i,
+                        (unsigned long long)g.buf_bytes, (unsigned long long)g.n,
+                        (unsigned long long)L.fixed);
+        uint64_t esc = (g.buf_bytes - L.fixed) / 3;     // encode: escape capacity
+        if (!encode) {
+            if ((g.buf_bytes - L.fixed) % 3 || esc > g.n)
+                return fail(SPLITZIP_E_FORMAT, "segment %u: stream length %llu does not fit %llu words", i,
+                            (unsigned long long)g.buf_bytes, (unsigned long long)g.n);
+        }
+        uint8_t *b = g.buf;
+        uint16_t *pos = reinterpret_cast<uint16_t *>(b + L.esc_pos);
+        desc[i] = sz::SegDesc{g.data, b + L.sm, b + L.codes, reinterpret_cast<uint64_t *>(b + L.chunk_off),
+                              pos, encode ? nullptr : b + L.esc_pos + 2 * esc, g.n, esc, g.book, 0u, b};
+        tiles[i] = (uint32_t)total;
+        total += std::max<uint64_t>(1, ceil_div(g.n, tile_words));
+        if (total > 0xFFFFFFF0ull)
+            return fail(SPLITZIP_E_INVALID, "too many tiles in one call");
+    }
+    tiles[n_seg] = (uint32_t)total;
+    return SPLITZIP_OK;
+}
+
+int64_t common_book_packed(uint32_t n_seg, const splitzip_packed *segs)
+{
+    for (uint32_t i = 1; i < n_seg; ++i)
+        if (segs[i].book != segs[0].book)
+            return -1;
+    return segs[0].book;
 }
 
 }  // namespace
@@ -697,29 +770,24 @@ int splitzip_codec_info(const splitzip_codec *codec, uint8_t codebook[16], uint3
 
 namespace {
 
-// Validation, workspace and launch shared by the blocking and non-blocking encode; the
-// caller holds the workspace lock.  d_result (optional): where the kernel writes its
-// error bits and per-segment escape counts instead of the workspace's result buffer.
-int encode_launch(splitzip_codec *codec, uint32_t n_seg, const splitzip_segment *segs,
-                  hipStream_t stream, uint64_t *d_result, Workspace **out_ws, uint32_t *out_tiles)
+// Workspace and launch shared by the blocking and non-blocking encodes (sections or packed
+// streams); the caller holds the workspace lock.  d_result (optional): where the kernel
+// writes its error bits and per-segment escape counts instead of the workspace's result
+// buffer.  book: the one codebook of every segment, or -1 when they differ.
+int encode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
+                  const std::vector<uint32_t> &tiles, int64_t book, bool packed, hipStream_t stream,
+                  uint64_t *d_result, Workspace **out_ws)
 {
-    int rc = codec_check(codec);
-    if (rc != SPLITZIP_OK)
-        return rc;
-    std::vector<sz::SegDesc> desc;
-    std::vector<uint32_t> tiles;
-    rc = prepare_segments(codec, n_seg, segs, true, desc, tiles);
-    if (rc != SPLITZIP_OK)
-        return rc;
+    const uint32_t n_seg = (uint32_t)desc.size();
     Workspace *w = nullptr;
-    rc = get_workspace(codec, stream, &w);
+    int rc = get_workspace(codec, stream, &w);
     if (rc != SPLITZIP_OK)
         return rc;
     const uint32_t n_tiles = tiles[n_seg];
     uint64_t ovf_cap = 1;
     for (uint32_t i = 0; i < n_seg; ++i)
-        ovf_cap += segs[i].esc_capacity;
-    const EncodeScratch lay(n_tiles, ovf_cap);
+        ovf_cap += desc[i].esc;
+    const EncodeScratch lay(n_tiles, ovf_cap, n_seg);
     if ((rc = ensure_scratch(w, lay.total)) != SPLITZIP_OK)
         return rc;
     if (!d_result && (rc = ensure_result(w, n_seg)) != SPLITZIP_OK)
@@ -731,9 +799,11 @@ int encode_launch(splitzip_codec *codec, uint32_t n_seg, const splitzip_segment 
         return rc;
     uint8_t *res = d_result ? reinterpret_cast<uint8_t *>(d_result) : w->result;
     // one book for the whole call: its LUT directly; several: the table, indexed per segment
-    const int64_t book = common_book(n_seg, segs);
     a.lut = codec->d_lut + 256 * (book < 0 ? 0 : book);
     a.multi_book = book < 0;
+    a.cbs = codec->d_cbs;
+    a.packed = packed;
+    a.seg_total = reinterpret_cast<uint64_t *>(w->scratch + lay.seg_total);
     a.tile_count = reinterpret_cast<uint32_t *>(w->scratch + lay.tile_count);
     a.tile_ovf = reinterpret_cast<uint64_t *>(w->scratch + lay.tile_ovf);
     a.tile_prefix = reinterpret_cast<uint64_t *>(w->scratch + lay.tile_prefix);
@@ -764,7 +834,33 @@ int encode_launch(splitzip_codec *codec, uint32_t n_seg, const splitzip_segment 
         return fail_hip(e, "encode launch");
     }
     *out_ws = w;
-    *out_tiles = n_tiles;
+    return SPLITZIP_OK;
+}
+
+// Blocking readback of an encode launched on the workspace's result buffer: error bits and
+// E per segment into E[], with the overflow-area bit tolerated only when some segment is
+// over capacity.
+int encode_readback(Workspace *w, hipStream_t stream, const std::vector<sz::SegDesc> &desc,
+                    std::vector<uint64_t> &E)
+{
+    const uint32_t n_seg = (uint32_t)desc.size();
+    hipError_t e = hipMemcpyAsync(w->h_result, w->result, 8 + 8 * (size_t)n_seg, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(stream);
+    if (e != hipSuccess)
+        return fail_hip(e, "encode readback");
+    uint32_t kerr = 0;
+    std::memcpy(&kerr, w->h_result, 4);
+    E.assign(n_seg, 0);
+    std::memcpy(E.data(), w->h_result + 8, 8 * (size_t)n_seg);
+    bool over_capacity = false;
+    for (uint32_t i = 0; i < n_seg; ++i)
+        over_capacity |= E[i] > desc[i].esc;
+    if (kerr) {
+        SZ_HIP(hipMemsetAsync(w->result, 0, 8, stream), "hipMemsetAsync(err)");
+        if ((kerr & ~sz::kErrOverflowArea) || !over_capacity)
+            return fail(SPLITZIP_E_DEVICE, "encode kernel reported error bits 0x%x", kerr);
+    }
     return SPLITZIP_OK;
 }
 
@@ -781,19 +877,21 @@ int splitzip_encode_async(splitzip_codec *codec, uint32_t n_seg, const splitzip_
     int rc = codec_check(codec);
     if (rc != SPLITZIP_OK)
         return rc;
+    std::vector<sz::SegDesc> desc;
+    std::vector<uint32_t> tiles;
+    if ((rc = prepare_segments(codec, n_seg, segs, true, desc, tiles)) != SPLITZIP_OK)
+        return rc;
     DeviceGuard dg(codec->device);
     if (dg.err != hipSuccess)
         return fail_hip(dg.err, "hipSetDevice");
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     Workspace *ws = nullptr;
-    rc = get_workspace(codec, stream, &ws);
-    if (rc != SPLITZIP_OK)
+    if ((rc = get_workspace(codec, stream, &ws)) != SPLITZIP_OK)
         return rc;
     // the lock covers only the launch: nothing is read back
     std::lock_guard<std::mutex> lock(ws->mu);
     Workspace *w = nullptr;
-    uint32_t n_tiles = 0;
-    return encode_launch(codec, n_seg, segs, stream, d_result, &w, &n_tiles);
+    return encode_launch(codec, desc, tiles, common_book(n_seg, segs), false, stream, d_result, &w);
 }
 
 int splitzip_encode(splitzip_codec *codec, uint32_t n_seg, splitzip_segment *segs, void *stream_)
@@ -802,38 +900,24 @@ int splitzip_encode(splitzip_codec *codec, uint32_t n_seg, splitzip_segment *seg
     int rc = codec_check(codec);
     if (rc != SPLITZIP_OK)
         return rc;
+    std::vector<sz::SegDesc> desc;
+    std::vector<uint32_t> tiles;
+    if ((rc = prepare_segments(codec, n_seg, segs, true, desc, tiles)) != SPLITZIP_OK)
+        return rc;
     DeviceGuard dg(codec->device);
     if (dg.err != hipSuccess)
         return fail_hip(dg.err, "hipSetDevice");
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     Workspace *ws = nullptr;
-    rc = get_workspace(codec, stream, &ws);
-    if (rc != SPLITZIP_OK)
+    if ((rc = get_workspace(codec, stream, &ws)) != SPLITZIP_OK)
         return rc;
     std::lock_guard<std::mutex> lock(ws->mu);
     Workspace *w = nullptr;
-    uint32_t n_tiles = 0;
-    rc = encode_launch(codec, n_seg, segs, stream, nullptr, &w, &n_tiles);
-    if (rc != SPLITZIP_OK)
+    if ((rc = encode_launch(codec, desc, tiles, common_book(n_seg, segs), false, stream, nullptr, &w)) != SPLITZIP_OK)
         return rc;
-    hipError_t e = hipMemcpyAsync(w->h_result, w->result, 8 + 8 * (size_t)n_seg, hipMemcpyDeviceToHost, stream);
-    if (e == hipSuccess)
-        e = hipStreamSynchronize(stream);
-    if (e != hipSuccess)
-        return fail_hip(e, "encode readback");
-    uint32_t kerr = 0;
-    std::memcpy(&kerr, w->h_result, 4);
-    const uint64_t *E = reinterpret_cast<const uint64_t *>(w->h_result + 8);
-    bool over_capacity = false;
-    for (uint32_t i = 0; i < n_seg; ++i)
-        over_capacity |= E[i] > segs[i].esc_capacity;
-    if (kerr) {
-        SZ_HIP(hipMemsetAsync(w->result, 0, 8, stream), "hipMemsetAsync(err)");
-        // an exhausted overflow area is expected only when some segment is over capacity
-        if ((kerr & ~sz::kErrOverflowArea) || !over_capacity)
-            return fail(SPLITZIP_E_DEVICE, "encode kernel reported error bits 0x%x", kerr);
-    }
-    rc = SPLITZIP_OK;
+    std::vector<uint64_t> E;
+    if ((rc = encode_readback(w, stream, desc, E)) != SPLITZIP_OK)
+        return rc;
     for (uint32_t i = 0; i < n_seg; ++i) {
         segs[i].n_escapes = E[i];
         segs[i].compressed_bytes = splitzip_compressed_bytes(segs[i].n, codec->chunk_size, E[i]);
@@ -844,38 +928,69 @@ int splitzip_encode(splitzip_codec *codec, uint32_t n_seg, splitzip_segment *seg
     return rc;
 }
 
-int splitzip_decode(splitzip_codec *codec, uint32_t n_seg, const splitzip_segment *segs,
-                    void *stream_, uint32_t *d_error)
+int splitzip_encode_packed(splitzip_codec *codec, uint32_t n_seg, splitzip_packed *segs,
+                           void *stream_, uint64_t *d_result)
 {
     g_last_error.clear();
+    if (d_result && !aligned(d_result, 8))
+        return fail(SPLITZIP_E_INVALID, "d_result not 8-byte aligned");
     int rc = codec_check(codec);
     if (rc != SPLITZIP_OK)
         return rc;
     std::vector<sz::SegDesc> desc;
     std::vector<uint32_t> tiles;
-    rc = prepare_segments(codec, n_seg, segs, false, desc, tiles);
-    if (rc != SPLITZIP_OK)
+    if ((rc = prepare_packed(codec, n_seg, segs, true, desc, tiles)) != SPLITZIP_OK)
         return rc;
+    DeviceGuard dg(codec->device);
+    if (dg.err != hipSuccess)
+        return fail_hip(dg.err, "hipSetDevice");
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    Workspace *ws = nullptr;
+    if ((rc = get_workspace(codec, stream, &ws)) != SPLITZIP_OK)
+        return rc;
+    std::lock_guard<std::mutex> lock(ws->mu);
+    Workspace *w = nullptr;
+    rc = encode_launch(codec, desc, tiles, common_book_packed(n_seg, segs), true, stream, d_result, &w);
+    if (rc != SPLITZIP_OK || d_result)
+        return rc;
+    std::vector<uint64_t> E;
+    if ((rc = encode_readback(w, stream, desc, E)) != SPLITZIP_OK)
+        return rc;
+    for (uint32_t i = 0; i < n_seg; ++i) {
+        segs[i].n_escapes = E[i];
+        segs[i].stream_bytes = splitzip_compressed_bytes(segs[i].n, codec->chunk_size, E[i]);
+        if (segs[i].stream_bytes > segs[i].buf_bytes && rc == SPLITZIP_OK)
+            rc = fail(SPLITZIP_E_CAPACITY, "segment %u needs %llu stream bytes, buffer holds %llu", i,
+                      (unsigned long long)segs[i].stream_bytes, (unsigned long long)segs[i].buf_bytes);
+    }
+    return rc;
+}
+
+}  // extern "C"
+
+namespace {
+
+int decode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
+                  const std::vector<uint32_t> &tiles, int64_t book, hipStream_t stream, uint32_t *d_error)
+{
+    const uint32_t n_seg = (uint32_t)desc.size();
     if (d_error && !aligned(d_error, 4))
         return fail(SPLITZIP_E_INVALID, "d_error not 4-byte aligned");
     DeviceGuard dg(codec->device);
     if (dg.err != hipSuccess)
         return fail_hip(dg.err, "hipSetDevice");
-    hipStream_t stream = static_cast<hipStream_t>(stream_);
-
     sz::DecodeArgs a{};
     a.seg0 = desc[0];
     Workspace *w = nullptr;
     std::unique_lock<std::mutex> lock;
+    int rc;
     if (n_seg > 1 || codec->profiling) {
-        rc = get_workspace(codec, stream, &w);
-        if (rc != SPLITZIP_OK)
+        if ((rc = get_workspace(codec, stream, &w)) != SPLITZIP_OK)
             return rc;
         lock = std::unique_lock<std::mutex>(w->mu);
     }
     if (n_seg > 1 && (rc = stage_descriptors(w, desc, tiles, &a.segs, &a.tile_start)) != SPLITZIP_OK)
         return rc;
-    const int64_t book = common_book(n_seg, segs);
     std::memcpy(a.cb, codec->cbs.data() + 16 * (book < 0 ? 0 : book), 16);
     a.cbs = codec->d_cbs;
     a.multi_book = book < 0;
@@ -893,6 +1008,40 @@ int splitzip_decode(splitzip_codec *codec, uint32_t n_seg, const splitzip_segmen
     if (e != hipSuccess)
         return fail_hip(e, "decode launch");
     return SPLITZIP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int splitzip_decode(splitzip_codec *codec, uint32_t n_seg, const splitzip_segment *segs,
+                    void *stream_, uint32_t *d_error)
+{
+    g_last_error.clear();
+    int rc = codec_check(codec);
+    if (rc != SPLITZIP_OK)
+        return rc;
+    std::vector<sz::SegDesc> desc;
+    std::vector<uint32_t> tiles;
+    if ((rc = prepare_segments(codec, n_seg, segs, false, desc, tiles)) != SPLITZIP_OK)
+        return rc;
+    return decode_launch(codec, desc, tiles, common_book(n_seg, segs), static_cast<hipStream_t>(stream_),
+                         d_error);
+}
+
+int splitzip_decode_packed(splitzip_codec *codec, uint32_t n_seg, const splitzip_packed *segs,
+                           void *stream_, uint32_t *d_error)
+{
+    g_last_error.clear();
+    int rc = codec_check(codec);
+    if (rc != SPLITZIP_OK)
+        return rc;
+    std::vector<sz::SegDesc> desc;
+    std::vector<uint32_t> tiles;
+    if ((rc = prepare_packed(codec, n_seg, segs, false, desc, tiles)) != SPLITZIP_OK)
+        return rc;
+    // each stream's codebook comes from its own header (read by the kernel)
+    return decode_launch(codec, desc, tiles, 0, static_cast<hipStream_t>(stream_), d_error);
 }
 
 int splitzip_profile(splitzip_codec *codec, int enable)

@@ -49,6 +49,7 @@ static_assert(kPlaceTiles % (kSumTiles / kThreads) == 0 && kPlaceTiles <= kThrea
 constexpr uint32_t kErrBadOffsets = 2u;      // decode: chunk offsets out of range
 constexpr uint32_t kErrBadPosition = 4u;     // decode: escape position outside its chunk
 constexpr uint32_t kErrOverflowArea = 8u;    // encode: overflow area too small
+constexpr uint32_t kErrBadHeader = 16u;      // decode: packed stream header does not match
 
 struct SegDesc {
     uint16_t *data;         // encode: input words; decode: output words
@@ -61,6 +62,11 @@ struct SegDesc {
     uint64_t esc;           // encode: escape capacity; decode: E
     uint32_t book;          // the segment's codebook (read only when multi_book is set)
     uint32_t pad;
+    // packed layout: the canonical stream's 64-byte header, followed by sm, codes and
+    // chunk_off (which the pointers above address) and then esc_pos[E], esc_exp[E]: the
+    // exponents start right after the E positions, so esc_exp above is unused and a kernel
+    // that writes or reads them needs E first.  NULL for separate section buffers.
+    uint8_t *header;
 };
 
 struct EncodeArgs {
@@ -81,11 +87,15 @@ struct EncodeArgs {
     uint64_t *block_sum;          // [ceil(n_tiles / kSumTiles)] segmented sums, bit 63 = head
     uint64_t *group_sum;          // [ceil(n_tiles / kPlaceTiles)] the same per placement group
     uint64_t *seg_escapes;        // [n_seg] OUT: E per segment
+    uint64_t *seg_total;          // [n_seg] packed layout: E per segment, from the sums launch
+    const uint32_t *cbs;          // device [4 * books] codebooks (packed layout: the header's)
     uint32_t *err;                // OUT: error bits
     uint32_t n_seg;
     uint32_t n_tiles;
     uint32_t log2_chunk;
     uint32_t multi_book;          // segments use different codebooks
+    uint32_t packed;              // segments are packed streams (SegDesc::header)
+    uint32_t pad;
 };
 
 struct DecodeArgs {

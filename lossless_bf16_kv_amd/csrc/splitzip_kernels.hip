@@ -327,6 +327,8 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
     const uint8_t *lut = a.multi_book ? a.lut + 256u * sd.book : a.lut;
     if (tid < 64)
         reinterpret_cast<uint32_t *>(s_lut)[tid] = reinterpret_cast<const uint32_t *>(lut)[tid];
+    if (a.packed && tid == 0 && t == segment_first_tile(a, s))
+        a.seg_total[s] = 0;      // the sums launch adds the segment's escapes into it
     const uint64_t n = sd.n;
     const uint64_t base = (uint64_t)(t - segment_first_tile(a, s)) << kEncTileShift;
     const uint64_t cmask = (1ull << a.log2_chunk) - 1;
@@ -551,6 +553,7 @@ __device__ __forceinline__ SegSum fold_tiles(const EncodeArgs &a, uint32_t u, ui
 __global__ __launch_bounds__(kThreads) void encode_sums_kernel(const EncodeArgs a)
 {
     __shared__ SegSum s_wave[kWaves];
+    __shared__ SegSum s_incl[kThreads];
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = lane_id();
     const uint32_t per = kSumTiles / kThreads;
@@ -579,6 +582,55 @@ __global__ __launch_bounds__(kThreads) void encode_sums_kernel(const EncodeArgs 
         a.ovf_ctr[1] = a.ovf_ctr[0];
         a.ovf_ctr[0] = 0;
     }
+    if (a.packed) {
+        // E of every segment, needed before placement (the exponents follow the E positions).
+        // Each thread adds up its tiles per segment, starting from the earlier threads' running
+        // sum of its first segment, and adds a segment's part of this block to its total where
+        // that part ends: at a segment end inside the thread's tiles, at the end of the
+        // thread's tiles if the segment ends there, or at the end of the block.
+        s_incl[tid] = all;
+        __syncthreads();
+        const uint32_t end = u0 + per < a.n_tiles ? u0 + per : a.n_tiles;
+        if (u0 < end) {
+            uint32_t sg = tile_segment(a, u0);
+            uint64_t acc = (tid > 0 && segment_first_tile(a, sg) != u0) ? s_incl[tid - 1].v : 0;
+            for (uint32_t u = u0; u < end; ++u) {
+                if (u == segment_end_tile(a, sg)) {
+                    if (acc)
+                        atomicAdd((unsigned long long *)&a.seg_total[sg], (unsigned long long)acc);
+                    acc = 0;
+                    ++sg;
+                }
+                acc += a.tile_count[u];
+            }
+            if (acc && (tid == kThreads - 1 || end == a.n_tiles || segment_end_tile(a, sg) == end))
+                atomicAdd((unsigned long long *)&a.seg_total[sg], (unsigned long long)acc);
+        }
+    }
+}
+
+// ---- packed layout --------------------------------------------------------------------------
+
+// Exponent array of a packed stream holding E escapes: right after the E positions.  NULL
+// when E exceeds the escape capacity (the exponents would run past the buffer): then no
+// escape is stored and the caller sees E > capacity.
+__device__ __forceinline__ uint8_t *packed_exps(const SegDesc &sd, uint64_t E)
+{
+    return E <= sd.esc ? reinterpret_cast<uint8_t *>(sd.esc_pos + E) : nullptr;
+}
+
+// The 64-byte canonical header: "SZB1", version 1, header bytes 64, chunk size, flags 0,
+// n, n_chunks, E, the segment's codebook, 8 zero bytes (all little-endian).
+__device__ void write_header(const SegDesc &sd, const EncodeArgs &a, uint64_t E)
+{
+    const uint64_t C = 1ull << a.log2_chunk;
+    const uint64_t n_chunks = (sd.n + C - 1) >> a.log2_chunk;
+    const uint32_t *cb = a.cbs + 4u * sd.book;
+    uint4 *h = reinterpret_cast<uint4 *>(sd.header);
+    h[0] = make_uint4(0x31425A53u, 1u | (64u << 16), (uint32_t)C, 0u);
+    h[1] = make_uint4((uint32_t)sd.n, (uint32_t)(sd.n >> 32), (uint32_t)n_chunks, (uint32_t)(n_chunks >> 32));
+    h[2] = make_uint4((uint32_t)E, (uint32_t)(E >> 32), cb[0], cb[1]);
+    h[3] = make_uint4(cb[2], cb[3], 0u, 0u);
 }
 
 // ---- place --------------------------------------------------------------------------------
@@ -606,6 +658,7 @@ __global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs
     __shared__ uint64_t s_base[kPlaceTiles];     // first word of each tile in its segment
     __shared__ uint64_t s_chunk0[kPlaceTiles];   // first chunk that starts inside each tile
     __shared__ uint32_t s_seg[kPlaceTiles];
+    __shared__ uint64_t s_E[kPlaceTiles];        // packed layout: E of each tile's segment
     __shared__ uint32_t s_first[kPlaceTiles + 1];   // escapes: start of each tile's range
     __shared__ uint32_t s_cfirst[kPlaceTiles + 1];  // chunk offsets: start of each tile's range
 
@@ -668,6 +721,8 @@ __global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs
             const uint64_t E = prefix + count;
             sd.chunk_off[(sd.n + cmask) >> a.log2_chunk] = E;
             a.seg_escapes[seg] = E;
+            if (a.packed)
+                write_header(sd, a, E);
         }
         if (base < sd.n) {
             // chunks that start inside this tile
@@ -685,6 +740,7 @@ __global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs
         s_base[tid] = base;
         s_chunk0[tid] = c_first;
         s_seg[tid] = seg;
+        s_E[tid] = a.packed && valid ? a.seg_total[seg] : 0;
     }
     // where each tile's escapes and chunk offsets fall in the workgroup's flattened ranges
     const uint32_t esc_incl = block_inclusive_sum_u32(spilled ? 0u : count, tid, lane, s_red32);
@@ -749,9 +805,10 @@ __global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs
             if (a.n_seg > 1)
                 sd = a.segs[s_seg[i]];
             const uint64_t d = s_prefix[i] + (j - s_first[i]);
-            if (d < sd.esc) {
+            uint8_t *exps = a.packed ? packed_exps(sd, s_E[i]) : sd.esc_exp;
+            if (d < sd.esc && exps) {
                 sd.esc_pos[d] = (uint16_t)((s_base[i] + (ent[k] & 0xFFFFu)) & cmask);
-                sd.esc_exp[d] = (uint8_t)(ent[k] >> 16);
+                exps[d] = (uint8_t)(ent[k] >> 16);
             }
         }
     }
@@ -773,6 +830,7 @@ __global__ __launch_bounds__(kThreads) void encode_spill_kernel(const EncodeArgs
         const uint32_t cnt = a.tile_count[t];
         const uint64_t off = a.tile_ovf[t];
         const uint64_t room = off < a.ovf_cap ? a.ovf_cap - off : 0;
+        uint8_t *exps = a.packed ? packed_exps(sd, a.seg_total[s]) : sd.esc_exp;
         // four loads in flight before the stores
         constexpr int kBatch = 4;
         const uint32_t lim = cnt < room ? cnt : (uint32_t)room;
@@ -786,9 +844,9 @@ __global__ __launch_bounds__(kThreads) void encode_spill_kernel(const EncodeArgs
             for (int k = 0; k < kBatch; ++k) {
                 const uint32_t r = r0 + k * kThreads;
                 const uint64_t d = pre + r;
-                if (r < lim && d < sd.esc) {
+                if (r < lim && d < sd.esc && exps) {
                     sd.esc_pos[d] = (uint16_t)((base + (e[k] & 0xFFFFu)) & cmask);
-                    sd.esc_exp[d] = (uint8_t)(e[k] >> 16);
+                    exps[d] = (uint8_t)(e[k] >> 16);
                 }
             }
         }
@@ -870,7 +928,26 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
     const uint64_t C = 1ull << log2c;
     const uint64_t E = sd.esc;
     uint32_t cb[4] = {a.cb[0], a.cb[1], a.cb[2], a.cb[3]};
-    if (a.multi_book) {
+    if (sd.header) {
+        // packed stream: it must describe exactly the segment the caller gave, and it carries
+        // its own codebook
+        const uint4 *h = reinterpret_cast<const uint4 *>(sd.header);
+        const uint4 h0 = h[0], h1 = h[1], h2 = h[2], h3 = h[3];
+        const uint64_t hn = h1.x | ((uint64_t)h1.y << 32), hc = h1.z | ((uint64_t)h1.w << 32);
+        const uint64_t he = h2.x | ((uint64_t)h2.y << 32);
+        const bool ok = h0.x == 0x31425A53u && h0.y == (1u | (64u << 16)) && h0.z == (uint32_t)C &&
+                        h0.w == 0u && hn == n && hc == ((n + C - 1) >> log2c) && he == E &&
+                        h3.z == 0u && h3.w == 0u;
+        if (!ok) {
+            if (tid == 0 && a.err)
+                atomicOr(a.err, kErrBadHeader);
+            return;
+        }
+        cb[0] = h2.z;
+        cb[1] = h2.w;
+        cb[2] = h3.x;
+        cb[3] = h3.y;
+    } else if (a.multi_book) {
         // the segment's own codebook (uniform: the same four dwords for the whole tile)
         const uint32_t *c = a.cbs + 4u * sd.book;
         cb[0] = c[0];
