@@ -136,6 +136,8 @@ def main():
     ap.add_argument("--books", choices=["one", "layer-kv"], default="one",
                     help="one codebook for the whole input, or (long-prefill KV) one per layer "
                          "and K/V, each tensor its own segment")
+    ap.add_argument("--packed", action="store_true",
+                    help="encode into / decode from one contiguous packed stream per segment")
     ap.add_argument("--cpu-sample-words", type=int, default=1 << 30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
@@ -176,11 +178,16 @@ def main():
     hist_in = np.sum(np.array(sz.histograms(xs), dtype=np.uint64), axis=0).tolist()
     stats_in = sz.exponent_stats(hist_in)
 
-    encs = codec.encode_batch(xs, books=books)  # sizes the escape arrays (retry if needed)
+    # sizes the escape arrays or stream buffers (retry if needed)
+    if args.packed:
+        encs = codec.encode_packed_batch(xs, books=books)
+    else:
+        encs = codec.encode_batch(xs, books=books)
     ys = [torch.empty_like(x) for x in xs]
     result = torch.zeros(1 + len(xs), dtype=torch.int64, device=dev)
     stream = torch.cuda.current_stream(dev)
-    batch = codec.prepare(xs, encs, ys)        # buffers fixed across steps
+    # buffers fixed across steps
+    batch = codec.prepare_packed(xs, encs, ys) if args.packed else codec.prepare(xs, encs, ys)
     batch.encode_async(result)
     torch.cuda.synchronize()
     assert batch.finish(result) == sz.OK
@@ -230,7 +237,8 @@ def main():
     alg = algorithmic_bytes(ns, Es, C)
     wall_s = t1 - t0
     value = 2 * n * args.steps / wall_s / 1e9
-    wname = wl.name + f"_c{C}" + ("_books_layer_kv" if books is not None else "")
+    wname = wl.name + f"_c{C}" + ("_books_layer_kv" if books is not None else "") + \
+        ("_packed" if args.packed else "")
 
     # the spill launch moves only the escapes of escape-heavy tiles (a data-dependent amount)
     kernels = {k: roofline(k, alg[k], ms, wname) for k, (ms, cnt) in ktimes.items()
@@ -278,7 +286,8 @@ def main():
         "dtype": "u16",
         "data": "synthetic",
         "config": {"workload": wl.name, "n_words": n, "segments": len(ns), "chunk_size": C,
-                   "codebooks": len(codec.books), "bytes_bf16": 2 * n, "description": wl.description},
+                   "codebooks": len(codec.books), "packed_streams": bool(args.packed),
+                   "bytes_bf16": 2 * n, "description": wl.description},
         "encode_GBps": round(2 * n / (enc_avg * 1e-3) / 1e9, 2),
         "decode_GBps": round(2 * n / (dec_avg * 1e-3) / 1e9, 2),
         "encode_hbm_frac": ops["encode"]["frac"],

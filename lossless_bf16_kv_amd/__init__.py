@@ -370,6 +370,24 @@ class Packed:
     def ratio(self) -> float:
         return 2 * self.n / self.stream_bytes
 
+    @property
+    def compressed_bytes(self) -> int:
+        return self.stream_bytes
+
+
+PACKED_OFFSET = 192
+
+
+def packed_buffer(nbytes: int, device):
+    """A device buffer for a packed stream, placed 64 bytes before a 256-byte boundary so
+    that the sections after the 64-byte header start on whole cache lines (the kernels
+    stream them in full lines; a stream at any other 16-byte-aligned place is correct but
+    slower)."""
+    import torch
+    raw = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (PACKED_OFFSET - raw.data_ptr()) % 256
+    return raw[off:off + nbytes]
+
 
 def _ptr(t) -> int | None:
     return t.data_ptr() if t is not None and t.numel() > 0 else None
@@ -610,8 +628,7 @@ class Codec:
         books = list(books) if books is not None else [0] * len(xs)
         words = [_words(x, self.device) for x in xs]
         caps = list(capacities) if capacities is not None else [self.packed_capacity(w.numel()) for w in words]
-        out = [Packed(w.numel(), tuple(x.shape), x.dtype,
-                      torch.empty(c, dtype=torch.uint8, device=self.device), 0, 0, b)
+        out = [Packed(w.numel(), tuple(x.shape), x.dtype, packed_buffer(c, self.device), 0, 0, b)
                for x, w, c, b in zip(xs, words, caps, books)]
         for attempt in range(2):
             segs = (splitzip_packed * len(out))()
@@ -626,12 +643,16 @@ class Codec:
                 break
             for p in out:
                 if p.stream_bytes > p.buf.numel():
-                    p.buf = torch.empty(p.stream_bytes, dtype=torch.uint8, device=self.device)
+                    p.buf = packed_buffer(p.stream_bytes, self.device)
         assert st == OK
         total = sum(p.n for p in out)
         if total:
             self._escape_rate = max(self._escape_rate, sum(p.n_escapes for p in out) / total)
         return out
+
+    def prepare_packed(self, xs, packed, outs=None) -> "PreparedPackedBatch":
+        """Fix the tensors and packed buffers of a batch for repeated encode/decode calls."""
+        return PreparedPackedBatch(self, xs, packed, outs)
 
     def decode_packed(self, stream, n: int | None = None, shape=None, dtype=None):
         return self.decode_packed_batch([stream], [n], [shape], [dtype])[0]
@@ -773,3 +794,56 @@ def histograms(xs, device=None) -> list:
 def exponent_stats(hist) -> dict:
     """Entropy in bits, top-16 codebook, coverage and distinct exponents of a histogram."""
     return splitzip_exponent_stats(hist)
+
+
+class PreparedPackedBatch:
+    """PreparedBatch for packed streams: descriptors built once, then repeated
+    non-blocking encodes into the same buffers and decodes from them."""
+
+    def __init__(self, codec: Codec, xs, packed, outs=None):
+        import torch
+        if len(xs) != len(packed) or (outs is not None and len(outs) != len(xs)):
+            raise ValueError("xs, packed and outs must have the same length")
+        self.codec, self.packed = codec, list(packed)
+        self._enc = (splitzip_packed * len(xs))()
+        for i, (x, p) in enumerate(zip(xs, self.packed)):
+            w = _words(x, codec.device)
+            if w.numel() != p.n:
+                raise ValueError("tensor size differs from the packed stream")
+            self._enc[i] = splitzip_packed(w.data_ptr() if p.n else None, p.n, p.buf.data_ptr(),
+                                           p.buf.numel(), 0, 0, p.book, 0)
+        self._dec = None
+        if outs is not None:
+            self._dec = (splitzip_packed * len(xs))()
+            for i, (y, p) in enumerate(zip(outs, self.packed)):
+                w = _words(y, codec.device)
+                if w.numel() != p.n:
+                    raise ValueError("output size differs from the packed stream")
+                self._dec[i] = splitzip_packed(w.data_ptr() if p.n else None, p.n, p.buf.data_ptr(),
+                                               p.stream_bytes, 0, 0, 0, 0)
+        self._torch = torch
+
+    def encode_async(self, result) -> None:
+        with self._torch.cuda.device(self.codec.device):
+            splitzip_encode_packed(self.codec.handle, self._enc, self.codec._stream(), result.data_ptr())
+
+    def finish(self, result) -> int:
+        """Read E per stream (synchronizes); E_CAPACITY if a stream outgrew its buffer."""
+        r = result.cpu().tolist()
+        st = OK
+        for i, p in enumerate(self.packed):
+            p.n_escapes = int(r[1 + i])
+            p.stream_bytes = splitzip_compressed_bytes(p.n, self.codec.chunk_size, p.n_escapes)
+            if p.stream_bytes > p.buf.numel():
+                st = E_CAPACITY
+            if self._dec is not None:
+                self._dec[i].buf_bytes = p.stream_bytes
+        if r[0] & ~8 or (r[0] and st != E_CAPACITY):
+            raise SplitZipError(E_DEVICE, f"encode kernel reported error bits {r[0]:#x}")
+        return st
+
+    def decode(self, d_error: int = 0) -> None:
+        if self._dec is None:
+            raise ValueError("no decode outputs were given")
+        with self._torch.cuda.device(self.codec.device):
+            splitzip_decode_packed(self.codec.handle, self._dec, self.codec._stream(), d_error)

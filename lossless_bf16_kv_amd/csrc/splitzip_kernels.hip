@@ -928,26 +928,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
     const uint64_t C = 1ull << log2c;
     const uint64_t E = sd.esc;
     uint32_t cb[4] = {a.cb[0], a.cb[1], a.cb[2], a.cb[3]};
-    if (sd.header) {
-        // packed stream: it must describe exactly the segment the caller gave, and it carries
-        // its own codebook
-        const uint4 *h = reinterpret_cast<const uint4 *>(sd.header);
-        const uint4 h0 = h[0], h1 = h[1], h2 = h[2], h3 = h[3];
-        const uint64_t hn = h1.x | ((uint64_t)h1.y << 32), hc = h1.z | ((uint64_t)h1.w << 32);
-        const uint64_t he = h2.x | ((uint64_t)h2.y << 32);
-        const bool ok = h0.x == 0x31425A53u && h0.y == (1u | (64u << 16)) && h0.z == (uint32_t)C &&
-                        h0.w == 0u && hn == n && hc == ((n + C - 1) >> log2c) && he == E &&
-                        h3.z == 0u && h3.w == 0u;
-        if (!ok) {
-            if (tid == 0 && a.err)
-                atomicOr(a.err, kErrBadHeader);
-            return;
-        }
-        cb[0] = h2.z;
-        cb[1] = h2.w;
-        cb[2] = h3.x;
-        cb[3] = h3.y;
-    } else if (a.multi_book) {
+    if (a.multi_book) {
         // the segment's own codebook (uniform: the same four dwords for the whole tile)
         const uint32_t *c = a.cbs + 4u * sd.book;
         cb[0] = c[0];
@@ -957,6 +938,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
     }
 
     // ---- loads ---------------------------------------------------------------------------
+    uint4 h0{}, h1{}, h2{}, h3{};
+    if (sd.header) {
+        const uint4 *h = reinterpret_cast<const uint4 *>(sd.header);
+        h0 = h[0];
+        h1 = h[1];
+        h2 = h[2];
+        h3 = h[3];
+    }
     uint2 smv[kDecGroups];
     uint32_t cw[kDecGroups];
 #pragma unroll
@@ -999,6 +988,26 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
         patch = false;
         if (tid == 0 && a.err)
             atomicOr(a.err, kErrBadOffsets);
+    }
+
+    if (sd.header) {
+        // packed stream: it must describe exactly the segment the caller gave, and it carries
+        // its own codebook.  Loaded with the data, checked here (the loads above all stay
+        // inside the buffer, whose length the host checked); nothing is written before it.
+        const uint64_t hn = h1.x | ((uint64_t)h1.y << 32), hc = h1.z | ((uint64_t)h1.w << 32);
+        const uint64_t he = h2.x | ((uint64_t)h2.y << 32);
+        const bool ok = h0.x == 0x31425A53u && h0.y == (1u | (64u << 16)) && h0.z == (uint32_t)C &&
+                        h0.w == 0u && hn == n && hc == ((n + C - 1) >> log2c) && he == E &&
+                        h3.z == 0u && h3.w == 0u;
+        if (!ok) {
+            if (tid == 0 && a.err)
+                atomicOr(a.err, kErrBadHeader);
+            return;
+        }
+        cb[0] = h2.z;
+        cb[1] = h2.w;
+        cb[2] = h3.x;
+        cb[3] = h3.y;
     }
 
     // ---- a5: dense path ------------------------------------------------------------------
