@@ -190,7 +190,9 @@ int splitzip_decode(splitzip_codec *codec, uint32_t n_seg, const splitzip_segmen
  *   n             words; a multiple of 16 (then every section of the stream is aligned
  *                 for vector access; KV tensors with a head dimension that is a multiple
  *                 of 16 qualify).
- *   buf           device, 16-byte aligned: the stream.
+ *   buf           device, 16-byte aligned: the stream.  Placed 64 bytes before a 256-byte
+ *                 boundary, every section after the header starts on whole cache lines
+ *                 (n a multiple of 256), which the kernels stream fastest.
  *   buf_bytes     encode: capacity of buf; splitzip_compressed_bytes(n, chunk_size, e)
  *                 bytes hold up to e escapes (the capacity hint).  decode: the stream's
  *                 length, which fixes E.
