@@ -79,6 +79,26 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.szo_stream_info.restype = ctypes.c_int
     lib.szo_decode_stream.argtypes = [_u8p, ctypes.c_uint64, _u8p, _u16p, ctypes.c_uint64]
     lib.szo_decode_stream.restype = ctypes.c_int
+    # FP8 E5M2
+    lib.szo8_histogram.argtypes = [_u8p, ctypes.c_uint64, _u64p]
+    lib.szo8_histogram.restype = None
+    lib.szo8_codebook.argtypes = [_u64p, _u8p]
+    lib.szo8_codebook.restype = None
+    lib.szo8_coverage.argtypes = [_u64p, _u8p, ctypes.c_uint64]
+    lib.szo8_coverage.restype = ctypes.c_double
+    lib.szo8_compressed_bytes.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint64]
+    lib.szo8_compressed_bytes.restype = ctypes.c_uint64
+    lib.szo8_encode.argtypes = [_u8p, ctypes.c_uint64, _u8p, ctypes.c_uint32, _u8p, _u8p, _u64p,
+                                _u16p, _u8p, ctypes.c_uint64, _u64p]
+    lib.szo8_encode.restype = ctypes.c_int
+    lib.szo8_decode.argtypes = [_u8p, _u8p, _u64p, _u16p, _u8p, ctypes.c_uint64, ctypes.c_uint64,
+                                _u8p, ctypes.c_uint32, _u8p]
+    lib.szo8_decode.restype = ctypes.c_int
+    lib.szo8_serialize.argtypes = [_u8p, _u8p, _u64p, _u16p, _u8p, ctypes.c_uint64,
+                                   ctypes.c_uint64, _u8p, ctypes.c_uint32, _u8p, ctypes.c_uint64]
+    lib.szo8_serialize.restype = ctypes.c_int
+    lib.szo8_decode_stream.argtypes = [_u8p, ctypes.c_uint64, _u8p, _u8p, ctypes.c_uint64]
+    lib.szo8_decode_stream.restype = ctypes.c_int
     return lib
 
 
@@ -207,6 +227,119 @@ class Oracle:
         if rc != OK:
             raise OracleError(rc, "decode stream")
         return y[:info_n]
+
+
+    # -- FP8 E5M2 elements (one byte each) -------------------------------------------
+    def histogram8(self, x: np.ndarray) -> np.ndarray:
+        x = _u8(x)
+        h = np.zeros(32, np.uint64)
+        self.lib.szo8_histogram(_ptr(x, _u8p), x.size, _ptr(h, _u64p))
+        return h
+
+    def codebook8(self, hist: np.ndarray) -> np.ndarray:
+        hist = np.ascontiguousarray(hist, np.uint64)
+        cb = np.zeros(16, np.uint8)
+        self.lib.szo8_codebook(_ptr(hist, _u64p), _ptr(cb, _u8p))
+        return cb
+
+    def coverage8(self, hist: np.ndarray, cb: np.ndarray, m: int) -> float:
+        hist = np.ascontiguousarray(hist, np.uint64)
+        cb = np.ascontiguousarray(cb, np.uint8)
+        return float(self.lib.szo8_coverage(_ptr(hist, _u64p), _ptr(cb, _u8p), m))
+
+    def calibrate8(self, cal: np.ndarray):
+        """(codebook, coverage, 32-bin histogram) of an E5M2 calibration tensor."""
+        h = self.histogram8(cal)
+        cb = self.codebook8(h)
+        return cb, self.coverage8(h, cb, _u8(cal).size), h
+
+    def compressed_bytes8(self, n: int, chunk_size: int, n_escapes: int) -> int:
+        return int(self.lib.szo8_compressed_bytes(n, chunk_size, n_escapes))
+
+    def encode8(self, x: np.ndarray, cb: np.ndarray, chunk_size: int) -> dict:
+        x = _u8(x)
+        cb = np.ascontiguousarray(cb, np.uint8)
+        n = x.size
+        n_chunks = -(-n // chunk_size) if chunk_size > 0 else 0
+        sm3 = np.zeros(-(-3 * n // 8), np.uint8)
+        codes = np.zeros((n + 1) // 2, np.uint8)
+        chunk_off = np.zeros(n_chunks + 1, np.uint64)
+        cap = n
+        esc_pos = np.zeros(max(cap, 1), np.uint16)
+        esc_exp = np.zeros(max(cap, 1), np.uint8)
+        E = ctypes.c_uint64(0)
+        rc = self.lib.szo8_encode(_ptr(x, _u8p), n, _ptr(cb, _u8p), chunk_size, _ptr(sm3, _u8p),
+                                  _ptr(codes, _u8p), _ptr(chunk_off, _u64p), _ptr(esc_pos, _u16p),
+                                  _ptr(esc_exp, _u8p), cap, ctypes.byref(E))
+        if rc != OK:
+            raise OracleError(rc, "encode (E5M2)")
+        E = E.value
+        return {
+            "n": n, "chunk_size": chunk_size, "codebook": cb.copy(), "n_escapes": E,
+            "sm3": sm3, "codes": codes, "chunk_off": chunk_off,
+            "esc_pos": esc_pos[:E].copy(), "esc_exp": esc_exp[:E].copy(),
+            "compressed_bytes": self.compressed_bytes8(n, chunk_size, E),
+        }
+
+    def decode8(self, enc: dict, cb: np.ndarray | None = None) -> np.ndarray:
+        cb = np.ascontiguousarray(enc["codebook"] if cb is None else cb, np.uint8)
+        n, E = int(enc["n"]), int(enc["n_escapes"])
+        sm3 = np.ascontiguousarray(enc["sm3"], np.uint8)
+        if sm3.size == 0:
+            sm3 = np.zeros(1, np.uint8)
+        codes = np.ascontiguousarray(enc["codes"], np.uint8)
+        if codes.size == 0:
+            codes = np.zeros(1, np.uint8)
+        chunk_off = np.ascontiguousarray(enc["chunk_off"], np.uint64)
+        esc_pos = np.ascontiguousarray(enc["esc_pos"], np.uint16)
+        esc_exp = np.ascontiguousarray(enc["esc_exp"], np.uint8)
+        if esc_pos.size == 0:
+            esc_pos = np.zeros(1, np.uint16)
+            esc_exp = np.zeros(1, np.uint8)
+        y = np.zeros(max(n, 1), np.uint8)
+        rc = self.lib.szo8_decode(_ptr(sm3, _u8p), _ptr(codes, _u8p), _ptr(chunk_off, _u64p),
+                                  _ptr(esc_pos, _u16p), _ptr(esc_exp, _u8p), n, E,
+                                  _ptr(cb, _u8p), int(enc["chunk_size"]), _ptr(y, _u8p))
+        if rc != OK:
+            raise OracleError(rc, "decode (E5M2)")
+        return y[:n]
+
+    def serialize8(self, enc: dict) -> bytes:
+        n, E, C = int(enc["n"]), int(enc["n_escapes"]), int(enc["chunk_size"])
+        total = self.compressed_bytes8(n, C, E)
+        out = np.zeros(total, np.uint8)
+        parts = [np.ascontiguousarray(enc[k], t) for k, t in (
+            ("sm3", np.uint8), ("codes", np.uint8), ("chunk_off", np.uint64),
+            ("esc_pos", np.uint16), ("esc_exp", np.uint8), ("codebook", np.uint8))]
+        parts = [p if p.size else np.zeros(1, p.dtype) for p in parts]
+        sm3, codes, chunk_off, esc_pos, esc_exp, cb = parts
+        rc = self.lib.szo8_serialize(_ptr(sm3, _u8p), _ptr(codes, _u8p), _ptr(chunk_off, _u64p),
+                                     _ptr(esc_pos, _u16p), _ptr(esc_exp, _u8p), n, E,
+                                     _ptr(cb, _u8p), C, _ptr(out, _u8p), total)
+        if rc != OK:
+            raise OracleError(rc, "serialize (E5M2)")
+        return out.tobytes()
+
+    def decode_stream8(self, buf: bytes, cb: np.ndarray) -> np.ndarray:
+        b = np.frombuffer(buf, np.uint8).copy()
+        info_n = int.from_bytes(bytes(b[16:24]), "little") if b.size >= 24 else 0
+        if b.size == 0:
+            b = np.zeros(1, np.uint8)
+        y = np.zeros(max(info_n, 1), np.uint8)
+        cb = np.ascontiguousarray(cb, np.uint8)
+        rc = self.lib.szo8_decode_stream(_ptr(b, _u8p), len(buf), _ptr(cb, _u8p), _ptr(y, _u8p), info_n)
+        if rc != OK:
+            raise OracleError(rc, "decode stream (E5M2)")
+        return y[:info_n]
+
+
+def _u8(x) -> np.ndarray:
+    a = np.asarray(x)
+    if a.dtype != np.uint8:
+        if a.dtype.itemsize != 1:
+            raise TypeError(f"expected bytes (E5M2 elements), got {a.dtype}")
+        a = a.view(np.uint8)
+    return np.ascontiguousarray(a).reshape(-1)
 
 
 def _u16(x) -> np.ndarray:

@@ -98,6 +98,27 @@ int szo_stream_info(const uint8_t *buf, uint64_t len, uint64_t *n, uint32_t *chu
 int szo_decode_stream(const uint8_t *buf, uint64_t len, const uint8_t cb[16], uint16_t *y,
                       uint64_t y_len);
 
+/* ---- FP8 E5M2 elements (sign bit 7, exponent bits 6..2, mantissa bits 1..0) ----------
+ * Same method and stream as above with: a 3-bit field (sign << 2) | mantissa per element
+ * packed into a little-endian bit stream sm3[ceil(3n/8)] (element i at bits 3i..3i+2); a
+ * codebook of 16 of the 32 exponent values; escape exponents 0..31; header flags = 1.
+ * total = 64 + ceil(3n/8) + ceil(n/2) + 8 (n_chunks + 1) + 3 E bytes. */
+void szo8_histogram(const uint8_t *x, uint64_t m, uint64_t hist[32]);
+void szo8_codebook(const uint64_t hist[32], uint8_t cb[16]);
+double szo8_coverage(const uint64_t hist[32], const uint8_t cb[16], uint64_t m);
+uint64_t szo8_compressed_bytes(uint64_t n, uint32_t chunk_size, uint64_t n_escapes);
+int szo8_encode(const uint8_t *x, uint64_t n, const uint8_t cb[16], uint32_t chunk_size,
+                uint8_t *sm3, uint8_t *codes, uint64_t *chunk_off, uint16_t *esc_pos,
+                uint8_t *esc_exp, uint64_t esc_capacity, uint64_t *n_escapes);
+int szo8_decode(const uint8_t *sm3, const uint8_t *codes, const uint64_t *chunk_off,
+                const uint16_t *esc_pos, const uint8_t *esc_exp, uint64_t n, uint64_t n_escapes,
+                const uint8_t cb[16], uint32_t chunk_size, uint8_t *y);
+int szo8_serialize(const uint8_t *sm3, const uint8_t *codes, const uint64_t *chunk_off,
+                   const uint16_t *esc_pos, const uint8_t *esc_exp, uint64_t n, uint64_t n_escapes,
+                   const uint8_t cb[16], uint32_t chunk_size, uint8_t *out, uint64_t out_len);
+int szo8_decode_stream(const uint8_t *buf, uint64_t len, const uint8_t cb[16], uint8_t *y,
+                       uint64_t y_len);
+
 #ifdef __cplusplus
 }
 #endif

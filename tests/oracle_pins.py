@@ -6,7 +6,9 @@ expected values come from: the hand-derived worked example under tests/golden
 (with its citations), closed forms of the exhaustive 65 536-word tensor, a
 brute-force re-derivation that reads BF16 fields through floating-point
 semantics (frexp, copysign) instead of bit masks, and invariants the pages fix
-(bitwise round trip; size = n + n/2 + escape bytes + chunk metadata).
+(bitwise round trip; size = n + n/2 + escape bytes + chunk metadata).  The FP8 E5M2
+variant has the same kinds of pin: a hand-derived example, the closed form of all 256
+bytes, fields read through torch's float8_e5m2 values, round trips and the 8/7 best case.
 """
 from __future__ import annotations
 
@@ -236,6 +238,145 @@ def check_entropy(o) -> None:
         assert abs(o.entropy(h) - want) <= 1e-12 * max(1.0, want)
 
 
+# ---- FP8 E5M2 ---------------------------------------------------------------------------------
+
+def check_worked_example8(o) -> None:
+    """The hand-derived E5M2 example (tests/golden/worked_example_e5m2_c16.txt)."""
+    g = load_golden("worked_example_e5m2_c16.txt")
+    C = int(g["chunk_size"])
+    cal = np.frombuffer(hex_bytes(g["calibration_u8"]), np.uint8)
+    cb, cov, _ = o.calibrate8(cal)
+    assert bytes(cb) == hex_bytes(g["codebook"])
+    num, den = (int(t) for t in g["calibration_coverage"].split("/"))
+    assert cov == num / den
+    x = np.frombuffer(hex_bytes(g["input_u8"]), np.uint8)
+    e = o.encode8(x, cb, C)
+    assert bytes(e["sm3"]) == hex_bytes(g["sm3"])
+    assert bytes(e["codes"]) == hex_bytes(g["codes"])
+    assert e["chunk_off"].tolist() == ints(g["chunk_off"])
+    assert e["esc_pos"].tolist() == ints(g["esc_pos"])
+    assert e["esc_exp"].tolist() == ints(g["esc_exp"])
+    assert e["n_escapes"] == int(g["n_escapes"])
+    assert e["compressed_bytes"] == int(g["compressed_bytes"])
+    s = o.serialize8(e)
+    assert len(s) == int(g["compressed_bytes"]) and s[:64] == hex_bytes(g["header"])
+    assert np.array_equal(o.decode8(e), x)
+    assert np.array_equal(o.decode_stream8(s, cb), x)
+    e7 = o.encode8(x[:7], cb, C)
+    assert bytes(e7["sm3"]) == hex_bytes(g["prefix7_sm3"])
+    assert bytes(e7["codes"]) == hex_bytes(g["prefix7_codes"])
+    assert e7["chunk_off"].tolist() == ints(g["prefix7_chunk_off"])
+    assert e7["compressed_bytes"] == int(g["prefix7_compressed_bytes"])
+    assert o.encode8(x[:0], cb, C)["compressed_bytes"] == int(g["empty_compressed_bytes"])
+
+
+def check_exhaustive8(o, C: int = 16) -> None:
+    """All 256 bytes once each: every exponent value occurs 8 times (2 signs x 4
+    mantissas), so the codebook is 0..15 and the escapes are the bytes whose exponent,
+    (b mod 128) // 4, is 16 or more.  Fields and codes from that arithmetic (division, not
+    bit masks)."""
+    x = np.arange(256, dtype=np.uint8)
+    cb, cov, h = o.calibrate8(x)
+    assert h.tolist() == [8] * 32
+    assert bytes(cb) == bytes(range(16)) and cov == 0.5
+    e = o.encode8(x, cb, C)
+    expo = [(b % 128) // 4 for b in range(256)]
+    field = [(b // 128) * 4 + b % 4 for b in range(256)]
+    bits = sum(f * 8 ** i for i, f in enumerate(field))            # 3 bits per element
+    assert bytes(e["sm3"]) == bits.to_bytes(96, "little")
+    want_codes = bytes((expo[2 * j] if expo[2 * j] < 16 else 0) + 16 * (expo[2 * j + 1] if expo[2 * j + 1] < 16 else 0)
+                       for j in range(128))
+    assert bytes(e["codes"]) == want_codes
+    assert e["n_escapes"] == 128
+    want_pos, want_exp, want_off = [], [], [0]
+    for c in range(-(-256 // C)):
+        for b in range(c * C, min(256, (c + 1) * C)):
+            if expo[b] >= 16:
+                want_pos.append(b - c * C)
+                want_exp.append(expo[b])
+        want_off.append(len(want_pos))
+    assert e["esc_pos"].tolist() == want_pos and e["esc_exp"].tolist() == want_exp
+    assert e["chunk_off"].tolist() == want_off
+    assert e["compressed_bytes"] == 64 + 96 + 128 + 8 * (len(want_off)) + 3 * 128
+    assert np.array_equal(o.decode8(e), x)
+
+
+def e5m2_fields_by_value(b: int):
+    """(sign, exponent, mantissa) of an E5M2 byte from the value torch's float8_e5m2 type
+    gives it: frexp for normals, multiples of 2^-16 for subnormals, 31 for Inf/NaN."""
+    import torch
+    v = float(torch.tensor([b], dtype=torch.uint8).view(torch.float8_e5m2).float()[0])
+    if math.isnan(v) or math.isinf(v):
+        return b >> 7, 31, b & 3                     # the non-finite codes, read as stored
+    sign = 1 if math.copysign(1.0, v) < 0 else 0
+    a = abs(v)
+    if a < 2.0 ** -14:
+        return sign, 0, int(round(a / 2.0 ** -16))
+    f, q = math.frexp(a)                             # a = f 2^q, f in [0.5, 1)
+    return sign, q + 14, int(round((2 * f - 1) * 4))
+
+
+def brute_force8(x: np.ndarray, C: int):
+    from collections import Counter
+    fields = [e5m2_fields_by_value(int(b)) for b in x]
+    cnt = Counter(e for _, e, _ in fields)
+    cb = sorted(range(32), key=lambda e: (-cnt.get(e, 0), e))[:16]
+    pos = {e: k for k, e in enumerate(cb)}
+    bits = 0
+    codes = [0] * ((len(x) + 1) // 2)
+    esc = []
+    off = []
+    for i, (s, e, m) in enumerate(fields):
+        if i % C == 0:
+            off.append(len(esc))
+        bits += (s * 4 + m) << (3 * i)
+        if e in pos:
+            codes[i // 2] += pos[e] << (4 * (i % 2))
+        else:
+            esc.append((i % C, e))
+    off.append(len(esc))
+    sm3 = bits.to_bytes(-(-3 * len(x) // 8), "little")
+    return bytes(cb), sm3, bytes(codes), off, esc
+
+
+def check_brute_force8(o, seeds=range(12)) -> None:
+    for seed in seeds:
+        rng = np.random.default_rng(1000 + seed)
+        n = int(rng.integers(16, 80))
+        C = [16, 32][seed % 2]
+        # mostly a narrow exponent band, some anywhere (specials included)
+        x = ((rng.integers(0, 2, n) << 7) | (rng.integers(12, 19, n) << 2) | rng.integers(0, 4, n)).astype(np.uint8)
+        wide = rng.random(n) < 0.25
+        x[wide] = rng.integers(0, 256, int(wide.sum())).astype(np.uint8)
+        cb, sm3, codes, off, esc = brute_force8(x, C)
+        ocb, _, _ = o.calibrate8(x)
+        assert bytes(ocb) == cb
+        e = o.encode8(x, ocb, C)
+        assert bytes(e["sm3"]) == sm3 and bytes(e["codes"]) == codes
+        assert e["chunk_off"].tolist() == off
+        assert list(zip(e["esc_pos"].tolist(), e["esc_exp"].tolist())) == esc
+        assert np.array_equal(o.decode8(e), x)
+
+
+def check_round_trips8(o) -> None:
+    rng = np.random.default_rng(77)
+    for n in (0, 1, 7, 8, 9, 31, 100, 1000):
+        for C in (16, 64, 65536):
+            x = rng.integers(0, 256, n).astype(np.uint8)
+            cb = o.calibrate8(rng.integers(0, 256, 500).astype(np.uint8))[0]
+            e = o.encode8(x, cb, C)
+            assert np.array_equal(o.decode8(e), x)
+            s = o.serialize8(e)
+            assert len(s) == 64 + -(-3 * n // 8) + (n + 1) // 2 + 8 * (-(-n // C) + 1) + 3 * e["n_escapes"]
+            assert np.array_equal(o.decode_stream8(s, cb), x)
+    # no escapes: 7 bits per element past the metadata, the pages' 8/7 best case
+    x = ((rng.integers(12, 28, 8000) << 2) | rng.integers(0, 4, 8000)).astype(np.uint8)
+    cb = o.calibrate8(x)[0]
+    e = o.encode8(x, cb, 1024)
+    assert e["n_escapes"] == 0
+    assert e["compressed_bytes"] - 64 - 8 * (8 + 1) == 8000 * 7 // 8
+
+
 def run_all(o) -> None:
     check_worked_example(o)
     check_exhaustive(o, 1024)
@@ -245,3 +386,8 @@ def run_all(o) -> None:
     check_round_trips(o)
     check_codebook_rules(o)
     check_entropy(o)
+    check_worked_example8(o)
+    check_exhaustive8(o, 16)
+    check_exhaustive8(o, 64)
+    check_brute_force8(o)
+    check_round_trips8(o)

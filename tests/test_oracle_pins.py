@@ -70,6 +70,39 @@ def test_normal_calibration_statistics():
     assert np.array_equal(O.decode(enc), wl.segments[0])
 
 
+def test_e5m2_worked_example():
+    pins.check_worked_example8(O)
+
+
+@pytest.mark.parametrize("C", [16, 64, 1024])
+def test_e5m2_all_bytes_closed_form(C):
+    pins.check_exhaustive8(O, C)
+
+
+def test_e5m2_brute_force_float_semantics():
+    pins.check_brute_force8(O, seeds=range(40))
+
+
+def test_e5m2_round_trips_and_best_case():
+    pins.check_round_trips8(O)
+
+
+def test_e5m2_rejects_bad_streams():
+    g, cal, x = None, None, None
+    x = np.arange(256, dtype=np.uint8)
+    cb = O.calibrate8(x)[0]
+    with pytest.raises(oracle.OracleError):
+        O.encode8(x, np.arange(20, 36, dtype=np.uint8), 16)      # exponents above 31
+    s = O.serialize8(O.encode8(x, cb, 16))
+    b = bytearray(s); b[12] = 0                                  # BF16 flags
+    with pytest.raises(oracle.OracleError):
+        O.decode_stream8(bytes(b), cb)
+    with pytest.raises(oracle.OracleError):
+        O.decode_stream(s, cb)                                   # not a BF16 stream
+    with pytest.raises(oracle.OracleError):
+        O.decode_stream8(s[:-1], cb)
+
+
 def test_entropy_closed_forms():
     pins.check_entropy(O)
 
@@ -169,19 +202,52 @@ MUTANTS = [
     ("entropy sign", "h -= p * log2(p);", "h += p * log2(p);"),
     ("entropy of unnormalized counts", "const double p = (double)hist[e] / (double)m;",
      "const double p = (double)hist[e];"),
+    ("E5M2 sign from bit 6", "static unsigned e5m2_sign(uint8_t b) { return (b >> 7) & 0x1u; }",
+     "static unsigned e5m2_sign(uint8_t b) { return (b >> 6) & 0x1u; }"),
+    ("E5M2 exponent shifted by 3", "return (b >> 2) & 0x1Fu;", "return (b >> 3) & 0x1Fu;"),
+    ("E5M2 mantissa 1 bit", "static unsigned e5m2_mantissa(uint8_t b) { return b & 0x3u; }",
+     "static unsigned e5m2_mantissa(uint8_t b) { return b & 0x1u; }"),
+    ("E5M2 field with the sign below", "field3_set(sm3, i, (e5m2_sign(b) << 2) | e5m2_mantissa(b));",
+     "field3_set(sm3, i, (e5m2_mantissa(b) << 1) | e5m2_sign(b));"),
+    ("E5M2 bit stream big-endian in a byte", "s[bit / 8] = (uint8_t)(s[bit / 8] | (1u << (bit % 8)));",
+     "s[bit / 8] = (uint8_t)(s[bit / 8] | (1u << (7 - bit % 8)));"),
+    ("E5M2 ranking misses exponent 31", "for (e = 0; e < 32; ++e) {\n            if (taken[e])",
+     "for (e = 0; e < 31; ++e) {\n            if (taken[e])"),
+    ("E5M2 ties ranked toward the larger exponent", "hist[best] < hist[e]", "hist[best] <= hist[e]"),
+    ("E5M2 header flags 0", "put_le(out + 12, 1, 4);         /* flags: E5M2 elements */",
+     "put_le(out + 12, 0, 4);         /* flags: E5M2 elements */"),
     ("codebook of 15", "for (k = 0; k < 16; ++k)\n        if (cb[k] == e)",
      "for (k = 0; k < 15; ++k)\n        if (cb[k] == e)"),
 ]
 
 
-@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_planted_mistake_is_caught(tmp_path, name, old, new):
+# the same statement in the E5M2 functions (second occurrence in the source)
+MUTANTS += [
+    ("E5M2 nibbles swapped in encode", "(code << (4 * (i % 2)))", "(code << (4 * (1 - i % 2)))", 1),
+    ("E5M2 escape position not chunk-local", "esc_pos[E] = (uint16_t)(i - start);",
+     "esc_pos[E] = (uint16_t)(i);", 1),
+    ("E5M2 escape nibble set to 15", "code = 0;\n                if", "code = 15;\n                if", 1),
+    ("E5M2 inclusive chunk offsets", "chunk_off[c] = E;\n        for", "for", 1),
+    ("E5M2 decode reads the wrong nibble", "unsigned code = (codes[i / 2] >> (4 * (i % 2))) & 0xFu;",
+     "unsigned code = (codes[i / 2] >> (4 * (1 - i % 2))) & 0xFu;", 1),
+]
+
+
+@pytest.mark.parametrize("mutant", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, mutant):
+    """Each mutant replaces the nth occurrence (default the first, which is in the BF16
+    functions; 1 = the E5M2 copy of the statement) of a statement of the oracle."""
+    name, old, new = mutant[:3]
+    nth = mutant[3] if len(mutant) > 3 else 0
     src = open(os.path.join(os.path.dirname(oracle.__file__), "splitzip_oracle.c")).read()
-    assert src.count(old) == 1, f"mutation site for '{name}' not unique"
+    assert src.count(old) > nth, f"mutation site for '{name}' missing"
+    at = -1
+    for _ in range(nth + 1):
+        at = src.index(old, at + 1)
     d = tmp_path / "mutant"
     d.mkdir()
     shutil.copy(os.path.join(os.path.dirname(oracle.__file__), "splitzip_oracle.h"), d)
-    (d / "splitzip_oracle.c").write_text(src.replace(old, new))
+    (d / "splitzip_oracle.c").write_text(src[:at] + new + src[at + len(old):])
     lib = str(d / "libmutant.so")
     oracle.build(out=lib, src=str(d / "splitzip_oracle.c"))
     mutant = oracle.Oracle(lib)
