@@ -20,6 +20,19 @@
  * canonical serialization is a 64-byte header followed by the five sections;
  * compressed_bytes = 64 + n + ceil(n/2) + 8 (n_chunks + 1) + 3 E.
  *
+ * FP8 E5M2 elements (README "FAQ" and arXiv abstract: the codec also runs on top of an
+ * FP8 E5M2 KV cache).  An E5M2 codec (splitzip_calibrate_e5m2 and the other *_e5m2
+ * constructors) codes bytes with sign bit 7, exponent bits 6..2 and mantissa bits 1..0.
+ * The same calls encode and decode them; a segment's `data` then points to n bytes and
+ * `sm` to the 3-bit field stream
+ *
+ *   sm[ceil(3n/8)] field (sign << 2) | mantissa of element i at bits 3i..3i+2 of a
+ *                  little-endian bit stream (byte j holds bits 8j..8j+7)
+ *
+ * while codes, chunk_off, esc_pos and esc_exp keep the layout above (exponents 0..31,
+ * codebook entries 0..31).  The header's flags field is 1 and
+ * compressed_bytes = 64 + ceil(3n/8) + ceil(n/2) + 8 (n_chunks + 1) + 3 E.
+ *
  * Conventions for every call
  *   - Pointers named d_* and every pointer inside splitzip_segment are DEVICE
  *     pointers on the codec's GPU; everything else is host memory.
@@ -30,7 +43,7 @@
  *     that was current when the codec was created; work is enqueued on it.
  *   - Every call returns a splitzip_status and never throws.  On error, a message
  *     is available from splitzip_last_error() (per host thread).
- *   - Alignment: BF16 data, sm and codes 16-byte aligned; chunk_off 8-byte;
+ *   - Alignment: data (BF16 or E5M2), sm and codes 16-byte aligned; chunk_off 8-byte;
  *     esc_pos 2-byte.  n per segment < 2^38.
  *   - A codec may be used from several host threads and streams; calls on one
  *     stream are ordered, calls on different streams use different workspaces.
@@ -44,11 +57,13 @@
 extern "C" {
 #endif
 
-#define SPLITZIP_ABI_VERSION 2
+#define SPLITZIP_ABI_VERSION 3
 #define SPLITZIP_HEADER_BYTES 64
 #define SPLITZIP_MIN_CHUNK 16
 #define SPLITZIP_MAX_CHUNK 65536
 #define SPLITZIP_MAX_BOOKS 4096   /* codebooks per codec */
+#define SPLITZIP_ELEM_BF16 0      /* element types; the stream header's flags field */
+#define SPLITZIP_ELEM_E5M2 1
 
 typedef enum splitzip_status {
     SPLITZIP_OK = 0,
@@ -67,8 +82,10 @@ typedef struct splitzip_codec splitzip_codec;
  * segments (a ragged batch, one kernel launch); each has its own chunking, which
  * restarts at the segment's first word, and its own output sections.
  *
- *   data             BF16 words, n of them.  encode reads, decode writes.
- *   sm, codes,       compressed sections (sizes above).  encode writes, decode reads.
+ *   data             BF16 words (E5M2 codec: bytes), n of them.  encode reads, decode
+ *                    writes.
+ *   sm, codes,       compressed sections (sizes above; sm is the 3-bit field stream for
+ *                    E5M2).  encode writes, decode reads.
  *   chunk_off
  *   esc_pos, esc_exp escape arrays with esc_capacity slots.
  *   esc_capacity     encode: slots available.  decode: ignored.
@@ -134,6 +151,24 @@ int splitzip_calibrate_books(uint32_t n_books, const uint16_t *const *d_cal, con
 int splitzip_codec_from_codebooks(uint32_t n_books, const uint8_t *codebooks, uint32_t chunk_size,
                                   splitzip_codec **out_codec);
 
+/*
+ * FP8 E5M2 codecs: as splitzip_calibrate, splitzip_calibrate_books and
+ * splitzip_codec_from_codebooks, for tensors of E5M2 bytes.  The codebook is the 16 of the
+ * 32 exponent values ranked first by (count descending, exponent ascending); hist
+ * (optional) receives 32 bins per book.  Known codebooks must hold 16 distinct values
+ * below 32.
+ */
+int splitzip_calibrate_e5m2(const uint8_t *d_cal, uint64_t n_cal, uint32_t chunk_size, void *stream,
+                            splitzip_codec **out_codec, double *out_coverage, uint64_t *out_hist);
+int splitzip_calibrate_books_e5m2(uint32_t n_books, const uint8_t *const *d_cal, const uint64_t *n_cal,
+                                  uint32_t chunk_size, void *stream, splitzip_codec **out_codec,
+                                  double *coverage, uint64_t *hist);
+int splitzip_codec_from_codebooks_e5m2(uint32_t n_books, const uint8_t *codebooks, uint32_t chunk_size,
+                                       splitzip_codec **out_codec);
+
+/* The element type a codec codes: SPLITZIP_ELEM_BF16 or SPLITZIP_ELEM_E5M2. */
+int splitzip_codec_element(const splitzip_codec *codec, uint32_t *elem);
+
 /* Number of codebooks of a codec and (if codebooks != NULL) all of them, host
  * uint8[n_books * 16]. */
 int splitzip_codec_books(const splitzip_codec *codec, uint32_t *n_books, uint8_t *codebooks);
@@ -186,16 +221,17 @@ int splitzip_decode(splitzip_codec *codec, uint32_t n_seg, const splitzip_segmen
  * pass); decode reads it there.  The header carries the codebook, so a packed stream is
  * decoded with its own codebook by any codec of the same chunk size.
  *
- *   data          BF16 words, n of them (16-byte aligned).  encode reads, decode writes.
- *   n             words; a multiple of 16 (then every section of the stream is aligned
- *                 for vector access; KV tensors with a head dimension that is a multiple
- *                 of 16 qualify).
+ *   data          BF16 words (E5M2 codec: bytes), n of them (16-byte aligned).  encode
+ *                 reads, decode writes.
+ *   n             elements; a multiple of 16 for BF16, of 128 for E5M2 (then every
+ *                 section of the stream is aligned for vector access; KV tensors with a
+ *                 head dimension that is a multiple of 128 qualify).
  *   buf           device, 16-byte aligned: the stream.  Placed 64 bytes before a 256-byte
  *                 boundary, every section after the header starts on whole cache lines
  *                 (n a multiple of 256), which the kernels stream fastest.
  *   buf_bytes     encode: capacity of buf; splitzip_compressed_bytes(n, chunk_size, e)
- *                 bytes hold up to e escapes (the capacity hint).  decode: the stream's
- *                 length, which fixes E.
+ *                 (E5M2: splitzip_e5m2_compressed_bytes) bytes hold up to e escapes (the
+ *                 capacity hint).  decode: the stream's length, which fixes E.
  *   stream_bytes  blocking encode: OUT, the stream's length (also when it exceeds
  *                 buf_bytes).  Otherwise ignored.
  *   n_escapes     blocking encode: OUT, E.  Otherwise ignored.
@@ -277,13 +313,19 @@ int splitzip_profile_read(splitzip_codec *codec, void *stream, double *avg_ms, u
 int splitzip_histogram(uint32_t n_seg, const uint16_t *const *d_x, const uint64_t *n, void *stream,
                        uint64_t *hist);
 
+/* The same for n_seg tensors of E5M2 bytes: hist[32 s + e] = number of bytes of tensor s
+ * whose exponent field (bits 6..2) is e. */
+int splitzip_histogram_e5m2(uint32_t n_seg, const uint8_t *const *d_x, const uint64_t *n, void *stream,
+                            uint64_t *hist);
+
 /*
  * Statistics of one exponent histogram (host only, no device work): the Shannon entropy
  * in bits, -sum p log2 p over the exponent values that occur with p = count / total
  * (ZipServ guide, "Information-Theoretic Limits and Exponent Entropy Bounds"); the top-16
  * codebook a calibration on this histogram picks (count descending, exponent ascending);
  * its coverage; and the number of distinct exponent values.  Any output may be NULL.  An
- * empty histogram gives entropy 0 and coverage 0.
+ * empty histogram gives entropy 0 and coverage 0.  For an E5M2 histogram pass its 32 bins
+ * followed by 224 zero bins: the ranking then stays inside the 32 exponent values.
  */
 int splitzip_exponent_stats(const uint64_t hist[256], double *entropy_bits, double *coverage,
                             uint8_t codebook[16], uint32_t *distinct);
@@ -296,25 +338,31 @@ uint64_t splitzip_chunk_count(uint64_t n, uint32_t chunk_size);
 /* 64 + n + ceil(n/2) + 8 (n_chunks + 1) + 3 n_escapes; 0 for an invalid chunk size. */
 uint64_t splitzip_compressed_bytes(uint64_t n, uint32_t chunk_size, uint64_t n_escapes);
 
+/* E5M2 streams: 64 + ceil(3n/8) + ceil(n/2) + 8 (n_chunks + 1) + 3 n_escapes. */
+uint64_t splitzip_e5m2_compressed_bytes(uint64_t n, uint32_t chunk_size, uint64_t n_escapes);
+
 /*
  * The canonical 64-byte stream header (little-endian): "SZB1", version u16 = 1,
- * header bytes u16 = 64, chunk_size u32, flags u32 = 0, n u64, n_chunks u64,
- * n_escapes u64, codebook[16] (that of `book`), 8 zero bytes.
+ * header bytes u16 = 64, chunk_size u32, flags u32 = the codec's element type (0 BF16,
+ * 1 E5M2), n u64, n_chunks u64, n_escapes u64, codebook[16] (that of `book`), 8 zero
+ * bytes.
  */
 int splitzip_write_header(const splitzip_codec *codec, uint32_t book, uint64_t n,
                           uint64_t n_escapes, uint8_t out[SPLITZIP_HEADER_BYTES]);
 
 /*
- * Parse a header; total_len is the full stream length (checked against the sizes).
- * Returns SPLITZIP_E_FORMAT for a malformed header.
+ * Parse a header; total_len is the full stream length (checked against the sizes of the
+ * element type the flags name).  *elem receives that type.  Returns SPLITZIP_E_FORMAT for a
+ * malformed header (including E5M2 codebook entries above 31).
  */
 int splitzip_read_header(const uint8_t *buf, uint64_t total_len, uint64_t *n,
-                         uint32_t *chunk_size, uint64_t *n_escapes, uint8_t codebook[16]);
+                         uint32_t *chunk_size, uint64_t *n_escapes, uint8_t codebook[16],
+                         uint32_t *elem);
 
 /*
  * Check that a received stream (header + total length) can be decoded by this codec:
- * SPLITZIP_E_FORMAT if the header is malformed, SPLITZIP_E_CODEBOOK if its chunk size
- * differs from the codec's or its codebook is none of the codec's (README "Codec API":
+ * SPLITZIP_E_FORMAT if the header is malformed, SPLITZIP_E_CODEBOOK if its chunk size or
+ * element type differs from the codec's or its codebook is none of the codec's (README "Codec API":
  * encoded objects are decoded with the same calibrated state).  On success *book
  * (optional) receives the first book whose codebook the header carries.
  */

@@ -17,6 +17,10 @@ Compression for Disaggregated LLM Serving" (README, "Codec API"):
   and ``calibrate_books`` for several codebooks (per layer, per K and V);
 * ``histograms`` / ``exponent_stats``: the exponent entropy and top-16 coverage
   analysis of BF16 tensors.
+
+``Codec(..., elem="e5m2")`` codes FP8 E5M2 tensors with the same calls (README "FAQ" and
+arXiv abstract: the codec also runs on top of an FP8 E5M2 KV cache): the 3-bit
+sign+mantissa fields form a bit stream, the 5-bit exponents take 4-bit codes and escapes.
 """
 from __future__ import annotations
 
@@ -32,6 +36,8 @@ OK, E_INVALID, E_NOMEM, E_DEVICE, E_CODEBOOK, E_FORMAT, E_CAPACITY = range(7)
 HEADER_BYTES = 64
 MIN_CHUNK, MAX_CHUNK = 16, 65536
 MAX_BOOKS = 4096
+ELEM_BF16, ELEM_E5M2 = 0, 1
+ELEMS = {"bf16": ELEM_BF16, "e5m2": ELEM_E5M2}
 
 
 class SplitZipError(RuntimeError):
@@ -95,6 +101,14 @@ def lib() -> ctypes.CDLL:
     L.splitzip_exponent_stats.argtypes = [P(u64), P(ctypes.c_double), P(ctypes.c_double),
                                           P(ctypes.c_uint8), P(u32)]
     L.splitzip_codec_info.argtypes = [vp, P(ctypes.c_uint8), P(u32), P(i32)]
+    L.splitzip_calibrate_e5m2.argtypes = [vp, u64, u32, vp, P(vp), P(ctypes.c_double), P(u64)]
+    L.splitzip_calibrate_books_e5m2.argtypes = [u32, P(vp), P(u64), u32, vp, P(vp),
+                                                P(ctypes.c_double), P(u64)]
+    L.splitzip_codec_from_codebooks_e5m2.argtypes = [u32, P(ctypes.c_uint8), u32, P(vp)]
+    L.splitzip_codec_element.argtypes = [vp, P(u32)]
+    L.splitzip_histogram_e5m2.argtypes = [u32, P(vp), P(u64), vp, P(u64)]
+    L.splitzip_e5m2_compressed_bytes.argtypes = [u64, u32, u64]
+    L.splitzip_e5m2_compressed_bytes.restype = u64
     L.splitzip_encode.argtypes = [vp, u32, P(splitzip_segment), vp]
     L.splitzip_encode_async.argtypes = [vp, u32, P(splitzip_segment), vp, vp]
     L.splitzip_decode.argtypes = [vp, u32, P(splitzip_segment), vp, vp]
@@ -110,7 +124,7 @@ def lib() -> ctypes.CDLL:
     L.splitzip_compressed_bytes.restype = u64
     L.splitzip_write_header.argtypes = [vp, u32, u64, u64, P(ctypes.c_uint8)]
     L.splitzip_read_header.argtypes = [P(ctypes.c_uint8), u64, P(u64), P(u32), P(u64),
-                                       P(ctypes.c_uint8)]
+                                       P(ctypes.c_uint8), P(u32)]
     L.splitzip_check_header.argtypes = [vp, P(ctypes.c_uint8), u64, P(u32)]
     L.splitzip_status_string.argtypes = [i32]
     L.splitzip_status_string.restype = ctypes.c_char_p
@@ -122,7 +136,9 @@ def lib() -> ctypes.CDLL:
               "splitzip_decode_packed",
               "splitzip_encode", "splitzip_encode_async", "splitzip_decode",
               "splitzip_write_header", "splitzip_profile", "splitzip_profile_read",
-              "splitzip_read_header", "splitzip_check_header"):
+              "splitzip_read_header", "splitzip_check_header", "splitzip_calibrate_e5m2",
+              "splitzip_calibrate_books_e5m2", "splitzip_codec_from_codebooks_e5m2",
+              "splitzip_codec_element", "splitzip_histogram_e5m2"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -195,6 +211,51 @@ def splitzip_codec_books(codec: int) -> list:
     return [raw[16 * b:16 * b + 16] for b in range(k.value)]
 
 
+def splitzip_calibrate_e5m2(d_cal: int, n_cal: int, chunk_size: int, stream: int = 0):
+    """E5M2 codec -> (codec handle, coverage, histogram list[32])."""
+    h = ctypes.c_void_p()
+    cov = ctypes.c_double()
+    hist = (ctypes.c_uint64 * 32)()
+    _check(lib().splitzip_calibrate_e5m2(d_cal or None, n_cal, chunk_size, stream or None,
+                                         ctypes.byref(h), ctypes.byref(cov), hist))
+    return h.value, cov.value, list(hist)
+
+
+def splitzip_calibrate_books_e5m2(d_cal, n_cal, chunk_size: int, stream: int = 0):
+    """E5M2 codec with one book per calibration tensor -> (handle, coverages, 32-bin hists)."""
+    k = len(d_cal)
+    h = ctypes.c_void_p()
+    cov = (ctypes.c_double * max(k, 1))()
+    hist = (ctypes.c_uint64 * (32 * max(k, 1)))()
+    _check(lib().splitzip_calibrate_books_e5m2(k, _ptr_array(d_cal), (ctypes.c_uint64 * max(k, 1))(*n_cal),
+                                               chunk_size, stream or None, ctypes.byref(h), cov, hist))
+    return h.value, list(cov)[:k], [list(hist[32 * b:32 * b + 32]) for b in range(k)]
+
+
+def splitzip_codec_from_codebooks_e5m2(codebooks: bytes, chunk_size: int) -> int:
+    if not codebooks or len(codebooks) % 16:
+        raise ValueError("codebooks must be a non-empty multiple of 16 bytes")
+    h = ctypes.c_void_p()
+    _check(lib().splitzip_codec_from_codebooks_e5m2(len(codebooks) // 16, _u8buf(bytes(codebooks)),
+                                                    chunk_size, ctypes.byref(h)))
+    return h.value
+
+
+def splitzip_codec_element(codec: int) -> int:
+    e = ctypes.c_uint32()
+    _check(lib().splitzip_codec_element(codec, ctypes.byref(e)))
+    return e.value
+
+
+def splitzip_histogram_e5m2(d_x, n, stream: int = 0) -> list:
+    """Exponent histograms of several E5M2 device tensors in one pass -> list of 32-lists."""
+    k = len(d_x)
+    hist = (ctypes.c_uint64 * (32 * max(k, 1)))()
+    _check(lib().splitzip_histogram_e5m2(k, _ptr_array(d_x), (ctypes.c_uint64 * max(k, 1))(*n),
+                                         stream or None, hist))
+    return [list(hist[32 * b:32 * b + 32]) for b in range(k)]
+
+
 def splitzip_histogram(d_x, n, stream: int = 0) -> list:
     """Exponent histograms of several device tensors in one pass -> list of 256-lists."""
     k = len(d_x)
@@ -206,9 +267,12 @@ def splitzip_histogram(d_x, n, stream: int = 0) -> list:
 
 def splitzip_exponent_stats(hist) -> dict:
     """Entropy (bits), top-16 codebook, its coverage and the distinct exponent count of
-    one 256-bin exponent histogram (host computation)."""
+    one exponent histogram (host computation): 256 bins (BF16) or 32 (E5M2, padded with
+    zero bins)."""
+    if len(hist) == 32:
+        hist = list(hist) + [0] * 224
     if len(hist) != 256:
-        raise ValueError("hist must have 256 bins")
+        raise ValueError("hist must have 256 (BF16) or 32 (E5M2) bins")
     h = (ctypes.c_uint64 * 256)(*[int(v) for v in hist])
     ent, cov = ctypes.c_double(), ctypes.c_double()
     cb = (ctypes.c_uint8 * 16)()
@@ -277,6 +341,17 @@ def splitzip_compressed_bytes(n: int, chunk_size: int, n_escapes: int) -> int:
     return int(lib().splitzip_compressed_bytes(n, chunk_size, n_escapes))
 
 
+def splitzip_e5m2_compressed_bytes(n: int, chunk_size: int, n_escapes: int) -> int:
+    return int(lib().splitzip_e5m2_compressed_bytes(n, chunk_size, n_escapes))
+
+
+def stream_bytes(elem: int, n: int, chunk_size: int, n_escapes: int) -> int:
+    """Canonical stream size of n elements of type elem (ELEM_BF16 or ELEM_E5M2)."""
+    if elem == ELEM_E5M2:
+        return splitzip_e5m2_compressed_bytes(n, chunk_size, n_escapes)
+    return splitzip_compressed_bytes(n, chunk_size, n_escapes)
+
+
 def splitzip_write_header(codec: int, book: int, n: int, n_escapes: int) -> bytes:
     out = (ctypes.c_uint8 * HEADER_BYTES)()
     _check(lib().splitzip_write_header(codec, book, n, n_escapes, out))
@@ -285,11 +360,12 @@ def splitzip_write_header(codec: int, book: int, n: int, n_escapes: int) -> byte
 
 def splitzip_read_header(buf: bytes) -> dict:
     n, e = ctypes.c_uint64(), ctypes.c_uint64()
-    c = ctypes.c_uint32()
+    c, el = ctypes.c_uint32(), ctypes.c_uint32()
     cb = (ctypes.c_uint8 * 16)()
     _check(lib().splitzip_read_header(_u8buf(buf[:HEADER_BYTES]), len(buf), ctypes.byref(n),
-                                      ctypes.byref(c), ctypes.byref(e), cb))
-    return {"n": n.value, "chunk_size": c.value, "n_escapes": e.value, "codebook": bytes(cb)}
+                                      ctypes.byref(c), ctypes.byref(e), cb, ctypes.byref(el)))
+    return {"n": n.value, "chunk_size": c.value, "n_escapes": e.value, "codebook": bytes(cb),
+            "elem": el.value}
 
 
 def splitzip_check_header(codec: int, buf: bytes) -> int:
@@ -317,6 +393,7 @@ class Encoded:
     n_escapes: int = 0
     compressed_bytes: int = 0
     book: int = 0         # which of the codec's codebooks
+    elem: int = ELEM_BF16  # element type (E5M2: sm is the 3-bit field stream)
 
     @property
     def esc_pos(self):
@@ -328,7 +405,7 @@ class Encoded:
 
     @property
     def ratio(self) -> float:
-        return 2 * self.n / self.compressed_bytes
+        return _elem_bytes(self.elem) * self.n / self.compressed_bytes
 
     def segment(self, data_ptr: int = 0) -> splitzip_segment:
         return splitzip_segment(data_ptr or None, self.n, _ptr(self.sm), _ptr(self.codes),
@@ -357,6 +434,7 @@ class Packed:
     stream_bytes: int = 0
     n_escapes: int = 0
     book: int = 0
+    elem: int = ELEM_BF16
 
     @property
     def stream(self):
@@ -368,7 +446,7 @@ class Packed:
 
     @property
     def ratio(self) -> float:
-        return 2 * self.n / self.stream_bytes
+        return _elem_bytes(self.elem) * self.n / self.stream_bytes
 
     @property
     def compressed_bytes(self) -> int:
@@ -393,6 +471,25 @@ def _ptr(t) -> int | None:
     return t.data_ptr() if t is not None and t.numel() > 0 else None
 
 
+def _elem_bytes(elem: int) -> int:
+    return 1 if elem == ELEM_E5M2 else 2
+
+
+def _elements(x, device, elem: int):
+    """Flat contiguous view of a device tensor as the codec's element words: int16 for BF16,
+    uint8 for E5M2 (float8_e5m2 or any 1-byte tensor)."""
+    import torch
+    if elem != ELEM_E5M2:
+        return _words(x, device)
+    if x.element_size() != 1:
+        raise TypeError(f"expected a 1-byte tensor (E5M2 bytes), got {x.dtype}")
+    if x.device != device:
+        raise ValueError(f"tensor is on {x.device}, codec is on {device}")
+    if not x.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return x.reshape(-1).view(torch.uint8)
+
+
 def _words(x, device):
     """Flat contiguous 16-bit view of a BF16 (or int16/uint16) device tensor."""
     import torch
@@ -406,10 +503,13 @@ def _words(x, device):
 
 
 class Codec:
-    """Stateful SplitZip codec bound to one GPU and one chunk size."""
+    """Stateful SplitZip codec bound to one GPU, one chunk size and one element type
+    (``elem="bf16"`` or ``"e5m2"``)."""
 
-    def __init__(self, device="cuda", chunk_size: int = 1024):
+    def __init__(self, device="cuda", chunk_size: int = 1024, elem: str = "bf16"):
         import torch
+        if elem not in ELEMS:
+            raise ValueError(f"elem must be one of {sorted(ELEMS)}")
         if not torch.cuda.is_available():
             raise SplitZipError(E_DEVICE, "no GPU: the SplitZip codec runs only on the GPU")
         d = torch.device(device)
@@ -420,6 +520,8 @@ class Codec:
         lib()
         self.device = d
         self.chunk_size = chunk_size
+        self.elem = ELEMS[elem]
+        self.elem_name = elem
         self.handle = 0
         self.coverage = None
         self.histogram = None
@@ -427,12 +529,9 @@ class Codec:
 
     # -- state -----------------------------------------------------------------------
     @classmethod
-    def from_codebook(cls, codebook: bytes, chunk_size: int = 1024, device="cuda") -> "Codec":
-        import torch
-        c = cls(device, chunk_size)
-        with torch.cuda.device(c.device):
-            c.handle = splitzip_codec_from_codebook(bytes(codebook), chunk_size)
-        return c
+    def from_codebook(cls, codebook: bytes, chunk_size: int = 1024, device="cuda",
+                      elem: str = "bf16") -> "Codec":
+        return cls.from_codebooks([codebook], chunk_size, device, elem)
 
     @property
     def codebook(self) -> bytes:
@@ -447,12 +546,24 @@ class Codec:
         return splitzip_codec_books(self.handle)
 
     @classmethod
-    def from_codebooks(cls, codebooks, chunk_size: int = 1024, device="cuda") -> "Codec":
+    def from_codebooks(cls, codebooks, chunk_size: int = 1024, device="cuda",
+                       elem: str = "bf16") -> "Codec":
         import torch
-        c = cls(device, chunk_size)
+        c = cls(device, chunk_size, elem)
+        books = b"".join(bytes(b) for b in codebooks)
         with torch.cuda.device(c.device):
-            c.handle = splitzip_codec_from_codebooks(b"".join(bytes(b) for b in codebooks), chunk_size)
+            if c.elem == ELEM_E5M2:
+                c.handle = splitzip_codec_from_codebooks_e5m2(books, chunk_size)
+            else:
+                c.handle = splitzip_codec_from_codebooks(books, chunk_size)
         return c
+
+    def _elements(self, x):
+        return _elements(x, self.device, self.elem)
+
+    def stream_bytes(self, n: int, n_escapes: int) -> int:
+        """Canonical stream size of n elements with n_escapes escapes."""
+        return stream_bytes(self.elem, n, self.chunk_size, n_escapes)
 
     def _need_handle(self):
         if not self.handle:
@@ -485,10 +596,11 @@ class Codec:
     def calibrate(self, x) -> float:
         """Fix the top-16 exponent codebook from a calibration tensor; returns its coverage."""
         import torch
-        w = _words(x, self.device)
+        w = self._elements(x)
+        cal = splitzip_calibrate_e5m2 if self.elem == ELEM_E5M2 else splitzip_calibrate
         with torch.cuda.device(self.device):
-            h, cov, hist = splitzip_calibrate(w.data_ptr() if w.numel() else 0, w.numel(),
-                                              self.chunk_size, self._stream())
+            h, cov, hist = cal(w.data_ptr() if w.numel() else 0, w.numel(), self.chunk_size,
+                               self._stream())
         splitzip_free(self.handle)
         self.handle, self.coverage, self.histogram = h, cov, hist
         self._escape_rate = 1.0 - cov if w.numel() else 0.0
@@ -498,11 +610,11 @@ class Codec:
         """One codebook per calibration tensor (e.g. per layer, per K and V), all histograms
         in one pass; returns the coverage of each.  Segments then pick a book on encode."""
         import torch
-        ws = [_words(x, self.device) for x in cals]
+        ws = [self._elements(x) for x in cals]
+        cal = splitzip_calibrate_books_e5m2 if self.elem == ELEM_E5M2 else splitzip_calibrate_books
         with torch.cuda.device(self.device):
-            h, cov, hist = splitzip_calibrate_books([w.data_ptr() if w.numel() else 0 for w in ws],
-                                                    [w.numel() for w in ws], self.chunk_size,
-                                                    self._stream())
+            h, cov, hist = cal([w.data_ptr() if w.numel() else 0 for w in ws], [w.numel() for w in ws],
+                               self.chunk_size, self._stream())
         splitzip_free(self.handle)
         self.handle, self.coverage, self.histogram = h, cov, hist
         rates = [1.0 - c for c, w in zip(cov, ws) if w.numel()]
@@ -512,18 +624,19 @@ class Codec:
     # -- a2-a4, a7 -----------------------------------------------------------------
     def empty_encoded(self, n: int, shape=None, dtype=None, escape_capacity: int | None = None,
                       book: int = 0):
-        """Allocate the device sections for an n-word tensor coded with codebook `book`."""
+        """Allocate the device sections for an n-element tensor coded with codebook `book`."""
         import torch
         n_chunks = -(-n // self.chunk_size)
         if escape_capacity is None:
             guess = math.ceil(n * max(self._escape_rate, 1e-4) * 1.25) + 64 * (n_chunks + 1)
             escape_capacity = min(n, max(1024, guess))
         kw = dict(device=self.device)
+        e5m2 = self.elem == ELEM_E5M2
         return Encoded(
             n=n, shape=tuple(shape) if shape is not None else (n,),
-            dtype=dtype if dtype is not None else torch.bfloat16,
-            chunk_size=self.chunk_size, codebook=self.books[book], book=book,
-            sm=torch.empty(n, dtype=torch.uint8, **kw),
+            dtype=dtype if dtype is not None else (torch.float8_e5m2 if e5m2 else torch.bfloat16),
+            chunk_size=self.chunk_size, codebook=self.books[book], book=book, elem=self.elem,
+            sm=torch.empty((3 * n + 7) // 8 if e5m2 else n, dtype=torch.uint8, **kw),
             codes=torch.empty((n + 1) // 2, dtype=torch.uint8, **kw),
             chunk_off=torch.empty(n_chunks + 1, dtype=torch.int64, **kw),
             esc_pos_buf=torch.empty(max(escape_capacity, 1), dtype=torch.int16, **kw),
@@ -534,7 +647,7 @@ class Codec:
         (then the Encoded whose n_escapes exceeds its capacity must be re-allocated)."""
         import torch
         self._need_handle()
-        words = [_words(x, self.device) for x in xs]
+        words = [self._elements(x) for x in xs]
         segs = (splitzip_segment * len(words))()
         for i, (w, e) in enumerate(zip(words, encs)):
             if w.numel() != e.n:
@@ -556,7 +669,7 @@ class Codec:
         self._need_handle()
         if result.dtype != torch.int64 or result.numel() < 1 + len(xs):
             raise ValueError("result must be an int64 device tensor of 1 + len(xs) words")
-        words = [_words(x, self.device) for x in xs]
+        words = [self._elements(x) for x in xs]
         segs = (splitzip_segment * len(words))()
         for i, (w, e) in enumerate(zip(words, encs)):
             if w.numel() != e.n:
@@ -571,7 +684,7 @@ class Codec:
         st = OK
         for i, e in enumerate(encs):
             e.n_escapes = int(r[1 + i])
-            e.compressed_bytes = splitzip_compressed_bytes(e.n, self.chunk_size, e.n_escapes)
+            e.compressed_bytes = self.stream_bytes(e.n, e.n_escapes)
             if e.n_escapes > e.esc_pos_buf.numel():
                 st = E_CAPACITY
         overflow_area = 8
@@ -610,25 +723,26 @@ class Codec:
 
     # -- packed streams -------------------------------------------------------------
     def packed_capacity(self, n: int, escapes: int | None = None) -> int:
-        """Buffer bytes for an n-word packed stream with up to `escapes` escapes (default:
+        """Buffer bytes for an n-element packed stream with up to `escapes` escapes (default:
         a guess from the calibration coverage)."""
         if escapes is None:
             n_chunks = -(-n // self.chunk_size)
             escapes = min(n, max(1024, math.ceil(n * max(self._escape_rate, 1e-4) * 1.25) + 64 * (n_chunks + 1)))
-        return splitzip_compressed_bytes(n, self.chunk_size, escapes)
+        return self.stream_bytes(n, escapes)
 
     def encode_packed(self, x, book: int = 0, capacity: int | None = None) -> Packed:
         return self.encode_packed_batch([x], [book], None if capacity is None else [capacity])[0]
 
     def encode_packed_batch(self, xs, books=None, capacities=None) -> list:
-        """Encode tensors (numel a multiple of 16) into packed streams, one launch sequence;
-        a buffer that turns out too small is reallocated and the batch re-encoded."""
+        """Encode tensors (numel a multiple of 16 for BF16, of 128 for E5M2) into packed
+        streams, one launch sequence; a buffer that turns out too small is reallocated and the
+        batch re-encoded."""
         import torch
         self._need_handle()
         books = list(books) if books is not None else [0] * len(xs)
-        words = [_words(x, self.device) for x in xs]
+        words = [self._elements(x) for x in xs]
         caps = list(capacities) if capacities is not None else [self.packed_capacity(w.numel()) for w in words]
-        out = [Packed(w.numel(), tuple(x.shape), x.dtype, packed_buffer(c, self.device), 0, 0, b)
+        out = [Packed(w.numel(), tuple(x.shape), x.dtype, packed_buffer(c, self.device), 0, 0, b, self.elem)
                for x, w, c, b in zip(xs, words, caps, books)]
         for attempt in range(2):
             segs = (splitzip_packed * len(out))()
@@ -669,13 +783,14 @@ class Codec:
             buf = st.stream if isinstance(st, Packed) else st
             n = st.n if isinstance(st, Packed) else ns[i]
             shape = shapes[i] or (st.shape if isinstance(st, Packed) else (n,))
-            dtype = dtypes[i] or (st.dtype if isinstance(st, Packed) else torch.bfloat16)
+            default = torch.float8_e5m2 if self.elem == ELEM_E5M2 else torch.bfloat16
+            dtype = dtypes[i] or (st.dtype if isinstance(st, Packed) else default)
             if buf.dtype != torch.uint8 or buf.device != self.device or not buf.is_contiguous():
                 raise ValueError("a packed stream is a contiguous uint8 tensor on the codec's device")
             y = torch.empty(shape, dtype=dtype, device=self.device)
-            w = _words(y, self.device)
+            w = self._elements(y)
             if w.numel() != n:
-                raise ValueError("output shape does not hold n words")
+                raise ValueError("output shape does not hold n elements")
             outs.append(y)
             segs[i] = splitzip_packed(w.data_ptr() if n else None, n, buf.data_ptr(), buf.numel(), 0, 0, 0, 0)
         with torch.cuda.device(self.device):
@@ -689,10 +804,11 @@ class Codec:
         segs = (splitzip_segment * len(encs))()
         books = self.books
         for i, (e, y) in enumerate(zip(encs, outs)):
-            w = _words(y, self.device)
+            w = self._elements(y)
             if w.numel() != e.n:
                 raise ValueError("output size differs from the encoded tensor")
-            if e.chunk_size != self.chunk_size or e.book >= len(books) or e.codebook != books[e.book]:
+            if (e.chunk_size != self.chunk_size or e.elem != self.elem or e.book >= len(books)
+                    or e.codebook != books[e.book]):
                 raise SplitZipError(E_CODEBOOK, "encoded with a different codec state")
             segs[i] = e.segment(w.data_ptr() if w.numel() else 0)
         with torch.cuda.device(self.device):
@@ -719,7 +835,8 @@ class Codec:
         enc = self.empty_encoded(n, shape, dtype, max(E, 1), book)
         b = np.frombuffer(buf, np.uint8)
         p = HEADER_BYTES
-        sizes = [n, (n + 1) // 2, 8 * (n_chunks + 1), 2 * E, E]
+        sm_bytes = (3 * n + 7) // 8 if self.elem == ELEM_E5M2 else n
+        sizes = [sm_bytes, (n + 1) // 2, 8 * (n_chunks + 1), 2 * E, E]
         dests = [enc.sm, enc.codes, enc.chunk_off.view(torch.uint8),
                  enc.esc_pos_buf[:E].view(torch.uint8), enc.esc_exp_buf[:E]]
         for size, dst in zip(sizes, dests):
@@ -743,7 +860,7 @@ class PreparedBatch:
         self.xs, self.encs, self.outs = list(xs), list(encs), (list(outs) if outs is not None else None)
         self._enc = (splitzip_segment * len(xs))()
         for i, (x, e) in enumerate(zip(self.xs, self.encs)):
-            w = _words(x, codec.device)
+            w = codec._elements(x)
             if w.numel() != e.n:
                 raise ValueError("tensor size differs from the preallocated sections")
             self._enc[i] = e.segment(w.data_ptr() if w.numel() else 0)
@@ -751,7 +868,7 @@ class PreparedBatch:
         if self.outs is not None:
             self._dec = (splitzip_segment * len(xs))()
             for i, (y, e) in enumerate(zip(self.outs, self.encs)):
-                w = _words(y, codec.device)
+                w = codec._elements(y)
                 if w.numel() != e.n:
                     raise ValueError("output size differs from the encoded tensor")
                 self._dec[i] = e.segment(w.data_ptr() if w.numel() else 0)
@@ -779,16 +896,19 @@ class PreparedBatch:
 
 # ---- exponent statistics ----------------------------------------------------------------
 
-def histograms(xs, device=None) -> list:
-    """Exponent histograms (256 bins each) of BF16 device tensors, one pass on the GPU."""
+def histograms(xs, device=None, elem: str = "bf16") -> list:
+    """Exponent histograms of device tensors, one pass on the GPU: 256 bins each for BF16,
+    32 for E5M2."""
     import torch
     if not torch.cuda.is_available():
         raise SplitZipError(E_DEVICE, "no GPU: histograms run only on the GPU")
     dev = torch.device(device) if device is not None else xs[0].device
-    ws = [_words(x, dev) for x in xs]
+    el = ELEMS[elem]
+    ws = [_elements(x, dev, el) for x in xs]
+    fn = splitzip_histogram_e5m2 if el == ELEM_E5M2 else splitzip_histogram
     with torch.cuda.device(dev):
-        return splitzip_histogram([w.data_ptr() if w.numel() else 0 for w in ws],
-                                  [w.numel() for w in ws], torch.cuda.current_stream(dev).cuda_stream)
+        return fn([w.data_ptr() if w.numel() else 0 for w in ws], [w.numel() for w in ws],
+                  torch.cuda.current_stream(dev).cuda_stream)
 
 
 def exponent_stats(hist) -> dict:
@@ -807,7 +927,7 @@ class PreparedPackedBatch:
         self.codec, self.packed = codec, list(packed)
         self._enc = (splitzip_packed * len(xs))()
         for i, (x, p) in enumerate(zip(xs, self.packed)):
-            w = _words(x, codec.device)
+            w = codec._elements(x)
             if w.numel() != p.n:
                 raise ValueError("tensor size differs from the packed stream")
             self._enc[i] = splitzip_packed(w.data_ptr() if p.n else None, p.n, p.buf.data_ptr(),
@@ -816,7 +936,7 @@ class PreparedPackedBatch:
         if outs is not None:
             self._dec = (splitzip_packed * len(xs))()
             for i, (y, p) in enumerate(zip(outs, self.packed)):
-                w = _words(y, codec.device)
+                w = codec._elements(y)
                 if w.numel() != p.n:
                     raise ValueError("output size differs from the packed stream")
                 self._dec[i] = splitzip_packed(w.data_ptr() if p.n else None, p.n, p.buf.data_ptr(),
@@ -833,7 +953,7 @@ class PreparedPackedBatch:
         st = OK
         for i, p in enumerate(self.packed):
             p.n_escapes = int(r[1 + i])
-            p.stream_bytes = splitzip_compressed_bytes(p.n, self.codec.chunk_size, p.n_escapes)
+            p.stream_bytes = self.codec.stream_bytes(p.n, p.n_escapes)
             if p.stream_bytes > p.buf.numel():
                 st = E_CAPACITY
             if self._dec is not None:

@@ -7,8 +7,10 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = [os.path.join(CSRC, "splitzip_kernels.hip"), os.path.join(CSRC, "splitzip_host.hip")]
-HEADERS = [os.path.join(CSRC, "splitzip_internal.h"), os.path.join(ROOT, "include", "splitzip.h")]
+SOURCES = [os.path.join(CSRC, "splitzip_kernels.hip"), os.path.join(CSRC, "splitzip_e5m2.hip"),
+           os.path.join(CSRC, "splitzip_host.hip")]
+HEADERS = [os.path.join(CSRC, "splitzip_internal.h"), os.path.join(CSRC, "splitzip_device.h"),
+           os.path.join(ROOT, "include", "splitzip.h")]
 LIB_PATH = os.path.join(HERE, "libsplitzip.so")
 ARCH = "gfx950"
 

@@ -159,6 +159,7 @@ struct Workspace {
 
 struct splitzip_codec {
     uint32_t magic = kCodecMagic;
+    uint32_t elem = sz::kElemBF16;   // element type of every tensor the codec codes
     int device = 0;
     bool profiling = false;
     uint32_t chunk_size = 0;
@@ -191,12 +192,13 @@ bool codebook_distinct(const uint8_t cb[16])
     return true;
 }
 
-int make_codec(const uint8_t *cbs, uint32_t n_books, uint32_t chunk_size, int device,
+int make_codec(const uint8_t *cbs, uint32_t n_books, uint32_t chunk_size, uint32_t elem, int device,
                hipStream_t stream, splitzip_codec **out)
 {
     std::unique_ptr<splitzip_codec> c(new (std::nothrow) splitzip_codec);
     if (!c)
         return fail(SPLITZIP_E_NOMEM, "host allocation of the codec failed");
+    c->elem = elem;
     c->device = device;
     c->chunk_size = chunk_size;
     c->log2_chunk = log2u(chunk_size);
@@ -240,8 +242,9 @@ uint64_t pick_codebook(const uint64_t hist[256], uint8_t cb[16])
     return covered;
 }
 
-// Exponent histograms of n_seg tensors into host hist[256 * n_seg]; blocks.
-int run_histograms(uint32_t n_seg, const uint16_t *const *d_x, const uint64_t *n,
+// Exponent histograms of n_seg tensors (BF16 words or E5M2 bytes) into host
+// hist[256 * n_seg]; blocks.
+int run_histograms(uint32_t n_seg, const void *const *d_x, const uint64_t *n, uint32_t elem,
                    hipStream_t stream, uint64_t *hist)
 {
     std::vector<sz::HistSeg> segs(n_seg);
@@ -250,7 +253,7 @@ int run_histograms(uint32_t n_seg, const uint16_t *const *d_x, const uint64_t *n
     for (uint32_t s = 0; s < n_seg; ++s) {
         if (n[s] > 0 && (!d_x[s] || !aligned(d_x[s], 16)))
             return fail(SPLITZIP_E_INVALID, "tensor %u: pointer NULL or not 16-byte aligned", s);
-        segs[s] = sz::HistSeg{n[s] ? d_x[s] : nullptr, n[s]};
+        segs[s] = sz::HistSeg{n[s] ? static_cast<const uint16_t *>(d_x[s]) : nullptr, n[s]};
         start[s] = (uint32_t)blocks;
         blocks += sz::hist_blocks(n[s]);
         if (blocks > 0x7FFFFFFFull)
@@ -273,6 +276,7 @@ int run_histograms(uint32_t n_seg, const uint16_t *const *d_x, const uint64_t *n
     a.hist = reinterpret_cast<uint64_t *>(d + off_hist);
     a.n_seg = n_seg;
     a.n_blocks = (uint32_t)blocks;
+    a.elem = elem;
     hipError_t e = hipSuccess;
     if (n_seg > 1) {
         e = hipMemcpyAsync(d + off_segs, segs.data(), n_seg * sizeof(sz::HistSeg), hipMemcpyHostToDevice, stream);
@@ -541,21 +545,37 @@ int64_t common_book(uint32_t n_seg, const splitzip_segment *segs)
     return segs[0].book;
 }
 
+// Elements per encode (pack) or decode tile of the codec's element type.
+uint64_t tile_elements(const splitzip_codec *c, bool encode)
+{
+    if (c->elem == sz::kElemE5M2)
+        return 1ull << (encode ? sz::kE8EncTileShift : sz::kE8DecTileShift);
+    return encode ? sz::kEncTileWords : sz::kDecTileWords;
+}
+
+// Canonical stream size of n elements with E escapes (0 for an invalid chunk size).
+uint64_t stream_bytes(uint32_t elem, uint64_t n, uint32_t chunk_size, uint64_t E)
+{
+    if (!chunk_size_ok(chunk_size))
+        return 0;
+    const uint64_t sm = elem == sz::kElemE5M2 ? ceil_div(3 * n, 8) : n;
+    return SPLITZIP_HEADER_BYTES + sm + ceil_div(n, 2) + 8 * (ceil_div(n, chunk_size) + 1) + 3 * E;
+}
+
 int prepare_segments(const splitzip_codec *c, uint32_t n_seg, const splitzip_segment *segs,
                      bool encode, std::vector<sz::SegDesc> &desc, std::vector<uint32_t> &tiles)
 {
-    const uint64_t tile_words = encode ? sz::kEncTileWords : sz::kDecTileWords;
-    return prepare_segments_tiled(c, n_seg, segs, encode, tile_words, desc, tiles);
+    return prepare_segments_tiled(c, n_seg, segs, encode, tile_elements(c, encode), desc, tiles);
 }
 
-// Byte offsets inside a packed stream of n words (n a multiple of 16): sm, codes and
-// chunk_off at fixed places, then esc_pos[E] and esc_exp[E].
+// Byte offsets inside a packed stream of n elements (n a multiple of 16 BF16 words, or of
+// 128 E5M2 bytes): sm, codes and chunk_off at fixed places, then esc_pos[E] and esc_exp[E].
 struct PackedLayout {
     uint64_t sm, codes, chunk_off, esc_pos, fixed;
-    PackedLayout(uint64_t n, uint32_t chunk_size)
+    PackedLayout(uint64_t n, uint32_t chunk_size, uint32_t elem)
     {
         sm = SPLITZIP_HEADER_BYTES;
-        codes = sm + n;
+        codes = sm + (elem == sz::kElemE5M2 ? 3 * n / 8 : n);
         chunk_off = codes + n / 2;
         esc_pos = chunk_off + 8 * (ceil_div(n, chunk_size) + 1);
         fixed = esc_pos;
@@ -570,15 +590,16 @@ int prepare_packed(const splitzip_codec *c, uint32_t n_seg, const splitzip_packe
         return fail(SPLITZIP_E_INVALID, "n_seg is 0");
     if (!segs)
         return fail(SPLITZIP_E_INVALID, "segs is NULL");
-    const uint64_t tile_words = encode ? sz::kEncTileWords : sz::kDecTileWords;
+    const uint64_t tile_words = tile_elements(c, encode);
+    const uint64_t multiple = c->elem == sz::kElemE5M2 ? 128 : 16;
     desc.resize(n_seg);
     tiles.resize((size_t)n_seg + 1);
     uint64_t total = 0;
     for (uint32_t i = 0; i < n_seg; ++i) {
         const splitzip_packed &g = segs[i];
-        if (g.n >= sz::kMaxSegmentWords || g.n % 16)
-            return fail(SPLITZIP_E_INVALID, "segment %u: n = %llu is not a multiple of 16 below 2^38", i,
-                        (unsigned long long)g.n);
+        if (g.n >= sz::kMaxSegmentWords || g.n % multiple)
+            return fail(SPLITZIP_E_INVALID, "segment %u: n = %llu is not a multiple of %llu below 2^38", i,
+                        (unsigned long long)g.n, (unsigned long long)multiple);
         if (!g.buf || !aligned(g.buf, 16))
             return fail(SPLITZIP_E_INVALID, "segment %u: stream buffer NULL or not 16-byte aligned", i);
         if (g.n > 0 && (!g.data || !aligned(g.data, 16)))
@@ -586,7 +607,7 @@ int prepare_packed(const splitzip_codec *c, uint32_t n_seg, const splitzip_packe
         if (g.book >= c->n_books)
             return fail(SPLITZIP_E_INVALID, "segment %u: book %u, the codec has %u", i, g.book,
                         c->n_books);
-        const PackedLayout L(g.n, c->chunk_size);
+        const PackedLayout L(g.n, c->chunk_size, c->elem);
         if (g.buf_bytes < L.fixed)
             return fail(encode ? SPLITZIP_E_INVALID : SPLITZIP_E_FORMAT,
                         "segment %u: %llu bytes, the stream of %llu words needs at least %llu", i,
@@ -627,9 +648,16 @@ int64_t common_book_packed(uint32_t n_seg, const splitzip_packed *segs)
 
 extern "C" {
 
-int splitzip_calibrate_books(uint32_t n_books, const uint16_t *const *d_cal, const uint64_t *n_cal,
-                             uint32_t chunk_size, void *stream_, splitzip_codec **out_codec,
-                             double *coverage, uint64_t *hist)
+}  // extern "C"
+
+namespace {
+
+// Calibration of n_books codebooks on tensors of one element type: all exponent histograms in
+// one pass, then each book = the 16 exponents ranked first by (count descending, exponent
+// ascending).  hist (optional) receives hist_bins bins per book (256 for BF16, 32 for E5M2).
+int calibrate_books(uint32_t elem, uint32_t n_books, const void *const *d_cal, const uint64_t *n_cal,
+                    uint32_t chunk_size, void *stream_, splitzip_codec **out_codec, double *coverage,
+                    uint64_t *hist, uint32_t hist_bins)
 {
     g_last_error.clear();
     if (!out_codec)
@@ -647,25 +675,63 @@ int splitzip_calibrate_books(uint32_t n_books, const uint16_t *const *d_cal, con
     int device = 0;
     SZ_HIP(hipGetDevice(&device), "hipGetDevice");
     std::vector<uint64_t> h(256 * (size_t)n_books);
-    int rc = run_histograms(n_books, d_cal, n_cal, stream, h.data());
+    int rc = run_histograms(n_books, d_cal, n_cal, elem, stream, h.data());
     if (rc != SPLITZIP_OK)
         return rc;
     std::vector<uint8_t> cbs(16 * (size_t)n_books);
     std::vector<double> cov(n_books);
     for (uint32_t b = 0; b < n_books; ++b) {
+        // an E5M2 histogram is 0 past bin 31, so its ranking stays inside the 32 exponents
         const uint64_t covered = pick_codebook(&h[256 * (size_t)b], &cbs[16 * (size_t)b]);
         cov[b] = n_cal[b] ? (double)covered / (double)n_cal[b] : 0.0;
     }
     splitzip_codec *c = nullptr;
-    rc = make_codec(cbs.data(), n_books, chunk_size, device, stream, &c);
+    rc = make_codec(cbs.data(), n_books, chunk_size, elem, device, stream, &c);
     if (rc != SPLITZIP_OK)
         return rc;
     if (coverage)
         std::memcpy(coverage, cov.data(), n_books * sizeof(double));
     if (hist)
-        std::memcpy(hist, h.data(), h.size() * sizeof(uint64_t));
+        for (uint32_t b = 0; b < n_books; ++b)
+            std::memcpy(hist + (size_t)hist_bins * b, &h[256 * (size_t)b], hist_bins * sizeof(uint64_t));
     *out_codec = c;
     return SPLITZIP_OK;
+}
+
+int codec_from_codebooks(uint32_t elem, uint32_t n_books, const uint8_t *codebooks, uint32_t chunk_size,
+                         splitzip_codec **out_codec)
+{
+    g_last_error.clear();
+    if (!codebooks || !out_codec)
+        return fail(SPLITZIP_E_INVALID, "codebooks or out_codec is NULL");
+    if (n_books == 0 || n_books > SPLITZIP_MAX_BOOKS)
+        return fail(SPLITZIP_E_INVALID, "n_books %u outside 1..%u", n_books, SPLITZIP_MAX_BOOKS);
+    if (!chunk_size_ok(chunk_size))
+        return fail(SPLITZIP_E_INVALID, "chunk_size %u is not a power of two in [16, 65536]", chunk_size);
+    for (uint32_t b = 0; b < n_books; ++b) {
+        if (!codebook_distinct(codebooks + 16 * (size_t)b))
+            return fail(SPLITZIP_E_INVALID, "codebook %u: entries are not 16 distinct exponents", b);
+        if (elem == sz::kElemE5M2)
+            for (int k = 0; k < 16; ++k)
+                if (codebooks[16 * (size_t)b + k] > 31)
+                    return fail(SPLITZIP_E_INVALID, "codebook %u: %u is not a 5-bit E5M2 exponent", b,
+                                codebooks[16 * (size_t)b + k]);
+    }
+    int device = 0;
+    SZ_HIP(hipGetDevice(&device), "hipGetDevice");
+    return make_codec(codebooks, n_books, chunk_size, elem, device, nullptr, out_codec);
+}
+
+}  // namespace
+
+extern "C" {
+
+int splitzip_calibrate_books(uint32_t n_books, const uint16_t *const *d_cal, const uint64_t *n_cal,
+                             uint32_t chunk_size, void *stream, splitzip_codec **out_codec,
+                             double *coverage, uint64_t *hist)
+{
+    return calibrate_books(sz::kElemBF16, n_books, reinterpret_cast<const void *const *>(d_cal), n_cal,
+                           chunk_size, stream, out_codec, coverage, hist, 256);
 }
 
 int splitzip_calibrate(const uint16_t *d_cal, uint64_t n_cal, uint32_t chunk_size, void *stream,
@@ -675,28 +741,48 @@ int splitzip_calibrate(const uint16_t *d_cal, uint64_t n_cal, uint32_t chunk_siz
                                     out_hist);
 }
 
+int splitzip_calibrate_books_e5m2(uint32_t n_books, const uint8_t *const *d_cal, const uint64_t *n_cal,
+                                  uint32_t chunk_size, void *stream, splitzip_codec **out_codec,
+                                  double *coverage, uint64_t *hist)
+{
+    return calibrate_books(sz::kElemE5M2, n_books, reinterpret_cast<const void *const *>(d_cal), n_cal,
+                           chunk_size, stream, out_codec, coverage, hist, 32);
+}
+
+int splitzip_calibrate_e5m2(const uint8_t *d_cal, uint64_t n_cal, uint32_t chunk_size, void *stream,
+                            splitzip_codec **out_codec, double *out_coverage, uint64_t *out_hist)
+{
+    return splitzip_calibrate_books_e5m2(1, &d_cal, &n_cal, chunk_size, stream, out_codec,
+                                         out_coverage, out_hist);
+}
+
 int splitzip_codec_from_codebooks(uint32_t n_books, const uint8_t *codebooks, uint32_t chunk_size,
                                   splitzip_codec **out_codec)
 {
-    g_last_error.clear();
-    if (!codebooks || !out_codec)
-        return fail(SPLITZIP_E_INVALID, "codebooks or out_codec is NULL");
-    if (n_books == 0 || n_books > SPLITZIP_MAX_BOOKS)
-        return fail(SPLITZIP_E_INVALID, "n_books %u outside 1..%u", n_books, SPLITZIP_MAX_BOOKS);
-    if (!chunk_size_ok(chunk_size))
-        return fail(SPLITZIP_E_INVALID, "chunk_size %u is not a power of two in [16, 65536]", chunk_size);
-    for (uint32_t b = 0; b < n_books; ++b)
-        if (!codebook_distinct(codebooks + 16 * (size_t)b))
-            return fail(SPLITZIP_E_INVALID, "codebook %u: entries are not 16 distinct exponents", b);
-    int device = 0;
-    SZ_HIP(hipGetDevice(&device), "hipGetDevice");
-    return make_codec(codebooks, n_books, chunk_size, device, nullptr, out_codec);
+    return codec_from_codebooks(sz::kElemBF16, n_books, codebooks, chunk_size, out_codec);
 }
 
 int splitzip_codec_from_codebook(const uint8_t codebook[16], uint32_t chunk_size,
                                  splitzip_codec **out_codec)
 {
     return splitzip_codec_from_codebooks(1, codebook, chunk_size, out_codec);
+}
+
+int splitzip_codec_from_codebooks_e5m2(uint32_t n_books, const uint8_t *codebooks, uint32_t chunk_size,
+                                       splitzip_codec **out_codec)
+{
+    return codec_from_codebooks(sz::kElemE5M2, n_books, codebooks, chunk_size, out_codec);
+}
+
+int splitzip_codec_element(const splitzip_codec *codec, uint32_t *elem)
+{
+    int rc = codec_check(codec);
+    if (rc != SPLITZIP_OK)
+        return rc;
+    if (!elem)
+        return fail(SPLITZIP_E_INVALID, "elem is NULL");
+    *elem = codec->elem;
+    return SPLITZIP_OK;
 }
 
 int splitzip_codec_books(const splitzip_codec *codec, uint32_t *n_books, uint8_t *codebooks)
@@ -717,7 +803,24 @@ int splitzip_histogram(uint32_t n_seg, const uint16_t *const *d_x, const uint64_
     g_last_error.clear();
     if (n_seg == 0 || !d_x || !n || !hist)
         return fail(SPLITZIP_E_INVALID, "n_seg is 0 or an array is NULL");
-    return run_histograms(n_seg, d_x, n, static_cast<hipStream_t>(stream), hist);
+    return run_histograms(n_seg, reinterpret_cast<const void *const *>(d_x), n, sz::kElemBF16,
+                          static_cast<hipStream_t>(stream), hist);
+}
+
+int splitzip_histogram_e5m2(uint32_t n_seg, const uint8_t *const *d_x, const uint64_t *n, void *stream,
+                            uint64_t *hist)
+{
+    g_last_error.clear();
+    if (n_seg == 0 || !d_x || !n || !hist)
+        return fail(SPLITZIP_E_INVALID, "n_seg is 0 or an array is NULL");
+    std::vector<uint64_t> h(256 * (size_t)n_seg);
+    const int rc = run_histograms(n_seg, reinterpret_cast<const void *const *>(d_x), n, sz::kElemE5M2,
+                                  static_cast<hipStream_t>(stream), h.data());
+    if (rc != SPLITZIP_OK)
+        return rc;
+    for (uint32_t s = 0; s < n_seg; ++s)
+        std::memcpy(hist + 32 * (size_t)s, &h[256 * (size_t)s], 32 * sizeof(uint64_t));
+    return SPLITZIP_OK;
 }
 
 int splitzip_exponent_stats(const uint64_t hist[256], double *entropy_bits, double *coverage,
@@ -819,6 +922,8 @@ int encode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
     a.n_seg = n_seg;
     a.n_tiles = n_tiles;
     a.log2_chunk = codec->log2_chunk;
+    a.elem = codec->elem;
+    a.tile_shift = codec->elem == sz::kElemE5M2 ? sz::kE8EncTileShift : sz::kEncTileShift;
     hipError_t e = hipSuccess;
     {
         CallTimer timer(codec, w, stream, SPLITZIP_KERNEL_PACK, sz::kEncodeStages);
@@ -920,7 +1025,7 @@ int splitzip_encode(splitzip_codec *codec, uint32_t n_seg, splitzip_segment *seg
         return rc;
     for (uint32_t i = 0; i < n_seg; ++i) {
         segs[i].n_escapes = E[i];
-        segs[i].compressed_bytes = splitzip_compressed_bytes(segs[i].n, codec->chunk_size, E[i]);
+        segs[i].compressed_bytes = stream_bytes(codec->elem, segs[i].n, codec->chunk_size, E[i]);
         if (E[i] > segs[i].esc_capacity && rc == SPLITZIP_OK)
             rc = fail(SPLITZIP_E_CAPACITY, "segment %u has %llu escapes, capacity %llu", i,
                       (unsigned long long)E[i], (unsigned long long)segs[i].esc_capacity);
@@ -958,7 +1063,7 @@ int splitzip_encode_packed(splitzip_codec *codec, uint32_t n_seg, splitzip_packe
         return rc;
     for (uint32_t i = 0; i < n_seg; ++i) {
         segs[i].n_escapes = E[i];
-        segs[i].stream_bytes = splitzip_compressed_bytes(segs[i].n, codec->chunk_size, E[i]);
+        segs[i].stream_bytes = stream_bytes(codec->elem, segs[i].n, codec->chunk_size, E[i]);
         if (segs[i].stream_bytes > segs[i].buf_bytes && rc == SPLITZIP_OK)
             rc = fail(SPLITZIP_E_CAPACITY, "segment %u needs %llu stream bytes, buffer holds %llu", i,
                       (unsigned long long)segs[i].stream_bytes, (unsigned long long)segs[i].buf_bytes);
@@ -998,6 +1103,7 @@ int decode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
     a.n_seg = n_seg;
     a.n_tiles = tiles[n_seg];
     a.log2_chunk = codec->log2_chunk;
+    a.elem = codec->elem;
     hipError_t e;
     {
         CallTimer timer(codec, w, stream, SPLITZIP_KERNEL_DECODE, 1);
@@ -1123,9 +1229,12 @@ uint64_t splitzip_chunk_count(uint64_t n, uint32_t chunk_size)
 
 uint64_t splitzip_compressed_bytes(uint64_t n, uint32_t chunk_size, uint64_t n_escapes)
 {
-    if (!chunk_size_ok(chunk_size))
-        return 0;
-    return SPLITZIP_HEADER_BYTES + n + ceil_div(n, 2) + 8 * (ceil_div(n, chunk_size) + 1) + 3 * n_escapes;
+    return stream_bytes(sz::kElemBF16, n, chunk_size, n_escapes);
+}
+
+uint64_t splitzip_e5m2_compressed_bytes(uint64_t n, uint32_t chunk_size, uint64_t n_escapes)
+{
+    return stream_bytes(sz::kElemE5M2, n, chunk_size, n_escapes);
 }
 
 static void le_put(uint8_t *p, uint64_t v, int bytes)
@@ -1158,7 +1267,7 @@ int splitzip_write_header(const splitzip_codec *codec, uint32_t book, uint64_t n
     le_put(out + 4, 1, 2);
     le_put(out + 6, SPLITZIP_HEADER_BYTES, 2);
     le_put(out + 8, codec->chunk_size, 4);
-    le_put(out + 12, 0, 4);
+    le_put(out + 12, codec->elem, 4);
     le_put(out + 16, n, 8);
     le_put(out + 24, ceil_div(n, codec->chunk_size), 8);
     le_put(out + 32, n_escapes, 8);
@@ -1167,7 +1276,7 @@ int splitzip_write_header(const splitzip_codec *codec, uint32_t book, uint64_t n
 }
 
 int splitzip_read_header(const uint8_t *buf, uint64_t total_len, uint64_t *n, uint32_t *chunk_size,
-                         uint64_t *n_escapes, uint8_t codebook[16])
+                         uint64_t *n_escapes, uint8_t codebook[16], uint32_t *elem)
 {
     g_last_error.clear();
     if (!buf)
@@ -1176,7 +1285,9 @@ int splitzip_read_header(const uint8_t *buf, uint64_t total_len, uint64_t *n, ui
         return fail(SPLITZIP_E_FORMAT, "stream shorter than its header");
     if (std::memcmp(buf, "SZB1", 4) != 0)
         return fail(SPLITZIP_E_FORMAT, "bad magic");
-    if (le_get(buf + 4, 2) != 1 || le_get(buf + 6, 2) != SPLITZIP_HEADER_BYTES || le_get(buf + 12, 4) != 0)
+    const uint64_t flags = le_get(buf + 12, 4);
+    if (le_get(buf + 4, 2) != 1 || le_get(buf + 6, 2) != SPLITZIP_HEADER_BYTES ||
+        (flags != sz::kElemBF16 && flags != sz::kElemE5M2))
         return fail(SPLITZIP_E_FORMAT, "unsupported version, header size or flags");
     for (int i = 56; i < 64; ++i)
         if (buf[i])
@@ -1185,8 +1296,12 @@ int splitzip_read_header(const uint8_t *buf, uint64_t total_len, uint64_t *n, ui
     const uint64_t nn = le_get(buf + 16, 8), nch = le_get(buf + 24, 8), e = le_get(buf + 32, 8);
     if (!chunk_size_ok(c) || nch != ceil_div(nn, c))
         return fail(SPLITZIP_E_FORMAT, "bad chunk size or chunk count");
-    if (e > nn || total_len != splitzip_compressed_bytes(nn, c, e))
+    if (e > nn || total_len != stream_bytes((uint32_t)flags, nn, c, e))
         return fail(SPLITZIP_E_FORMAT, "sizes do not match the stream length");
+    if (flags == sz::kElemE5M2)
+        for (int k = 0; k < 16; ++k)
+            if (buf[40 + k] > 31)
+                return fail(SPLITZIP_E_FORMAT, "E5M2 codebook entry %u is not a 5-bit exponent", buf[40 + k]);
     if (n)
         *n = nn;
     if (chunk_size)
@@ -1195,6 +1310,8 @@ int splitzip_read_header(const uint8_t *buf, uint64_t total_len, uint64_t *n, ui
         *n_escapes = e;
     if (codebook)
         std::memcpy(codebook, buf + 40, 16);
+    if (elem)
+        *elem = (uint32_t)flags;
     return SPLITZIP_OK;
 }
 
@@ -1204,11 +1321,13 @@ int splitzip_check_header(const splitzip_codec *codec, const uint8_t *buf, uint6
     int rc = codec_check(codec);
     if (rc != SPLITZIP_OK)
         return rc;
-    uint32_t c = 0;
+    uint32_t c = 0, elem = 0;
     uint8_t cb[16];
-    rc = splitzip_read_header(buf, total_len, nullptr, &c, nullptr, cb);
+    rc = splitzip_read_header(buf, total_len, nullptr, &c, nullptr, cb, &elem);
     if (rc != SPLITZIP_OK)
         return rc;
+    if (elem != codec->elem)
+        return fail(SPLITZIP_E_CODEBOOK, "stream element type %u, the codec's is %u", elem, codec->elem);
     if (c != codec->chunk_size)
         return fail(SPLITZIP_E_CODEBOOK, "stream chunk size %u, the codec's is %u", c, codec->chunk_size);
     for (uint32_t b = 0; b < codec->n_books; ++b)

@@ -25,6 +25,23 @@ static_assert(kThreads * kDecGroups * kGroupWords == kDecTileWords, "decode tile
 // Extra LDS reserved per decode workgroup to hold occupancy at 5 workgroups per CU.
 constexpr unsigned kDecodeLdsReserve = 16384;
 
+// ---- element types ----------------------------------------------------------------------
+// BF16 words (sign bit 15, exponent bits 14..7, mantissa bits 6..0) or FP8 E5M2 bytes (sign
+// bit 7, exponent bits 6..2, mantissa bits 1..0).  The value is the stream header's flags.
+constexpr uint32_t kElemBF16 = 0;
+constexpr uint32_t kElemE5M2 = 1;
+
+// E5M2 tiling: each lane owns groups of 32 consecutive bytes (two 16-byte loads), whose
+// 3-bit sign+mantissa fields fill 12 bytes and whose codes fill 16.  An encode tile is
+// 32768 elements (4 groups per lane), a decode tile 16384 (2 groups per lane).
+constexpr int kE8GroupElems = 32;
+constexpr int kE8EncGroups = 4;
+constexpr int kE8EncTileShift = 15;
+constexpr int kE8DecGroups = 2;
+constexpr int kE8DecTileShift = 14;
+static_assert(kThreads * kE8EncGroups * kE8GroupElems == (1 << kE8EncTileShift), "E5M2 encode tile");
+static_assert(kThreads * kE8DecGroups * kE8GroupElems == (1 << kE8DecTileShift), "E5M2 decode tile");
+
 // Inverse-LUT entry of an exponent outside the codebook: nibble 0 plus an escape bit.
 constexpr uint8_t kEscapeEntry = 0x10;
 
@@ -40,7 +57,7 @@ constexpr uint32_t kSpillBlocks = 1024;       // workgroups moving the overflow 
 constexpr int kOvfTileShift = 40;
 constexpr uint64_t kOvfOffsetMask = (1ull << kOvfTileShift) - 1;
 constexpr uint64_t kMaxSegmentWords = 1ull << 38;
-static_assert(kEncTileWords <= 65536, "in-tile positions must fit 16 bits");
+static_assert(kEncTileWords <= 65536 && (1 << kE8EncTileShift) <= 65536, "in-tile positions must fit 16 bits");
 static_assert(kSumTiles % kThreads == 0 && kSumTiles % kPlaceTiles == 0, "sum blocks");
 static_assert(kSumTiles / kPlaceTiles <= kThreads, "group sums of a block fit one pass");
 static_assert(kPlaceTiles % (kSumTiles / kThreads) == 0 && kPlaceTiles <= kThreads, "groups");
@@ -52,8 +69,8 @@ constexpr uint32_t kErrOverflowArea = 8u;    // encode: overflow area too small
 constexpr uint32_t kErrBadHeader = 16u;      // decode: packed stream header does not match
 
 struct SegDesc {
-    uint16_t *data;         // encode: input words; decode: output words
-    uint8_t *sm;            // [n]
+    uint16_t *data;         // encode: input words; decode: output words (E5M2: bytes)
+    uint8_t *sm;            // [n] (E5M2: the 3-bit field stream, [ceil(3n/8)])
     uint8_t *codes;         // [ceil(n/2)]
     uint64_t *chunk_off;    // [n_chunks + 1]
     uint16_t *esc_pos;      // encode: [esc] slots; decode: [esc] entries
@@ -95,6 +112,8 @@ struct EncodeArgs {
     uint32_t log2_chunk;
     uint32_t multi_book;          // segments use different codebooks
     uint32_t packed;              // segments are packed streams (SegDesc::header)
+    uint32_t elem;                // kElemBF16 or kElemE5M2
+    uint32_t tile_shift;          // log2 of the elements per pack tile
     uint32_t pad;
 };
 
@@ -109,6 +128,8 @@ struct DecodeArgs {
     uint32_t n_tiles;
     uint32_t log2_chunk;
     uint32_t multi_book;
+    uint32_t elem;                // kElemBF16 or kElemE5M2
+    uint32_t pad;
 };
 
 // Exponent histograms of one or more tensors: per-workgroup partial counts (each tensor
@@ -128,6 +149,8 @@ struct HistArgs {
     uint64_t *hist;                 // OUT [n_seg * 256]
     uint32_t n_seg;
     uint32_t n_blocks;
+    uint32_t elem;                  // kElemBF16 (words) or kElemE5M2 (bytes)
+    uint32_t pad;
 };
 
 uint32_t hist_blocks(uint64_t n);
@@ -136,5 +159,8 @@ hipError_t launch_histogram(const HistArgs &a, hipStream_t stream);
 constexpr int kEncodeStages = 4;
 hipError_t launch_encode_stage(int stage, const EncodeArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+// E5M2 pack and decode (the other encode stages are shared with BF16).
+hipError_t launch_encode_pack_e5m2(const EncodeArgs &a, hipStream_t stream);
+hipError_t launch_decode_e5m2(const DecodeArgs &a, hipStream_t stream);
 
 }  // namespace sz

@@ -20,138 +20,24 @@
 //   - decode: codebook lookup with two v_perm_b32 byte selects per 4 codes (codebook in
 //     SGPRs), exponent bytes staged in LDS only for tiles that hold escapes, where the
 //     escapes overwrite them before the words are assembled.
-#include "splitzip_internal.h"
+#include "splitzip_device.h"
 
 namespace sz {
-
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-// Streaming accesses of the pack kernel: every byte is touched once, so the loads and stores
-// carry the nontemporal hint and do not displace other data in the caches.
-__device__ __forceinline__ uint4 load_stream16(const uint16_t *p)
-{
-    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-    return make_uint4(t.x, t.y, t.z, t.w);
-}
-
-__device__ __forceinline__ void store_stream8(uint8_t *p, uint32_t lo, uint32_t hi)
-{
-    const u32x2 t = {lo, hi};
-    __builtin_nontemporal_store(t, reinterpret_cast<u32x2 *>(p));
-}
-
-__device__ __forceinline__ void store_stream4(uint8_t *p, uint32_t x)
-{
-    __builtin_nontemporal_store(x, reinterpret_cast<uint32_t *>(p));
-}
-
-// ---- small wave64 helpers -------------------------------------------------------------
-
-__device__ __forceinline__ uint32_t lane_id()
-{
-    return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-}
-
-__device__ __forceinline__ uint32_t shfl_u32(uint32_t v, uint32_t src_lane)
-{
-    return (uint32_t)__builtin_amdgcn_ds_bpermute((int)(src_lane << 2), (int)v);
-}
-
-// Inclusive prefix sum over the 64 lanes (all lanes must be active).  Used on words that
-// pack two 16-bit counters whose sums stay below 65536.
-__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v, uint32_t lane)
-{
-#pragma unroll
-    for (uint32_t d = 1; d < 64; d <<= 1) {
-        uint32_t t = shfl_u32(v, lane >= d ? lane - d : lane);
-        if (lane >= d)
-            v += t;
-    }
-    return v;
-}
-
-__device__ __forceinline__ uint64_t wave_total_u64(uint64_t v, uint32_t lane)
-{
-#pragma unroll
-    for (uint32_t d = 1; d < 64; d <<= 1) {
-        uint32_t lo = shfl_u32((uint32_t)v, lane ^ d);
-        uint32_t hi = shfl_u32((uint32_t)(v >> 32), lane ^ d);
-        v += ((uint64_t)hi << 32) | lo;
-    }
-    return v;
-}
-
-__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
-
-__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
-{
-    // v_perm_b32: selector byte s picks byte s of the 8-byte value {hi, lo} (s < 8).
-    return __builtin_amdgcn_perm(hi, lo, sel);
-}
-
-// Workgroups are started round robin over the 8 XCDs (workgroup b on XCD b mod 8).  Giving
-// each XCD a contiguous range of tiles instead of every 8th one streams measurably better
-// (about 3 % in a copy probe).  The mapping is a bijection on [0, n_tiles) whatever the
-// hardware does; extra workgroups of the rounded-up grid find t >= n_tiles and exit.
-constexpr uint32_t kXcds = 8;
-
-__device__ __forceinline__ uint32_t xcd_tile(uint32_t b, uint32_t n_tiles)
-{
-    const uint32_t per_xcd = (n_tiles + kXcds - 1) / kXcds;
-    return (b % kXcds) * per_xcd + b / kXcds;
-}
-
-static inline uint32_t xcd_grid(uint32_t n_tiles) { return (n_tiles + kXcds - 1) / kXcds * kXcds; }
-
-// Segment that owns global tile t: largest s with tile_start[s] <= t.
-__device__ __forceinline__ uint32_t find_segment(const uint32_t *tile_start, uint32_t n_seg,
-                                                 uint32_t t)
-{
-    uint32_t lo = 0, hi = n_seg;
-    while (hi - lo > 1) {
-        uint32_t mid = (lo + hi) >> 1;
-        if (tile_start[mid] <= t)
-            lo = mid;
-        else
-            hi = mid;
-    }
-    return lo;
-}
-
-// Segment of tile t, found by the whole workgroup with one round of independent loads (a
-// binary search would chain dependent ones): the number of s >= 1 with tile_start[s] <= t.
-// Call from uniform control flow; contains barriers.
-__device__ uint32_t find_segment_block(const uint32_t *tile_start, uint32_t n_seg, uint32_t t,
-                                       uint32_t tid, uint32_t lane, uint32_t *s_cnt)
-{
-    uint32_t c = 0;
-    for (uint32_t k = 1 + tid; k < n_seg; k += kThreads)
-        c += tile_start[k] <= t ? 1u : 0u;
-#pragma unroll
-    for (uint32_t d = 1; d < 64; d <<= 1)
-        c += shfl_u32(c, lane ^ d);
-    if (lane == 0)
-        s_cnt[tid >> 6] = c;
-    __syncthreads();
-    uint32_t seg = 0;
-    for (int w = 0; w < kWaves; ++w)
-        seg += s_cnt[w];
-    __syncthreads();
-    return __builtin_amdgcn_readfirstlane(seg);
-}
 
 // ======================================================================================
 // a1  exponent histograms (calibration, and the per-tensor exponent statistics)
 // ======================================================================================
 
-// Workgroup b histograms its share of one tensor (grid-stride over that tensor's groups of
-// 8 words) into per-wave LDS sub-histograms and writes the 256 sums to partial[b].
+// Workgroup b histograms its share of one tensor (grid-stride over that tensor's 16-byte
+// groups: 8 BF16 words or 16 E5M2 bytes) into per-wave LDS sub-histograms and writes the 256
+// sums to partial[b] (an E5M2 exponent is 5 bits: bins 32..255 stay 0).
+template <uint32_t kElem>
 __global__ __launch_bounds__(kThreads) void hist_kernel(const HistArgs a)
 {
     // one sub-histogram per wave keeps LDS atomic contention on the few hot exponents down
     __shared__ uint32_t h[kWaves][256];
     __shared__ uint32_t s_cnt[kWaves];
+    constexpr uint32_t kPerGroup = kElem == kElemE5M2 ? 16u : 8u;   // elements per 16 bytes
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = lane_id();
     const uint32_t b = blockIdx.x;
@@ -167,21 +53,31 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(const HistArgs a)
     }
     __syncthreads();
     uint32_t *mine = h[tid >> 6];
+    const uint8_t *bytes = reinterpret_cast<const uint8_t *>(sg.x);
 
-    const uint64_t groups = sg.n / kGroupWords;
+    const uint64_t groups = sg.n / kPerGroup;
     const uint64_t stride = (uint64_t)nb * kThreads;
     for (uint64_t g = (uint64_t)(b - first) * kThreads + tid; g < groups; g += stride) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(sg.x + g * kGroupWords);
+        const uint4 v = *reinterpret_cast<const uint4 *>(bytes + g * 16);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            atomicAdd(&mine[(w[k] >> 7) & 0xFFu], 1u);
-            atomicAdd(&mine[(w[k] >> 23) & 0xFFu], 1u);
+            if (kElem == kElemE5M2) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    atomicAdd(&mine[(w[k] >> (8 * i + 2)) & 0x1Fu], 1u);
+            } else {
+                atomicAdd(&mine[(w[k] >> 7) & 0xFFu], 1u);
+                atomicAdd(&mine[(w[k] >> 23) & 0xFFu], 1u);
+            }
         }
     }
-    // ragged tail (fewer than 8 words), handled by the tensor's first workgroup
-    if (b == first && tid < sg.n - groups * kGroupWords)
-        atomicAdd(&mine[(sg.x[groups * kGroupWords + tid] >> 7) & 0xFFu], 1u);
+    // ragged tail (fewer than one group), handled by the tensor's first workgroup
+    if (b == first && tid < sg.n - groups * kPerGroup) {
+        const uint64_t i = groups * kPerGroup + tid;
+        const uint32_t e = kElem == kElemE5M2 ? (bytes[i] >> 2) & 0x1Fu : (sg.x[i] >> 7) & 0xFFu;
+        atomicAdd(&mine[e], 1u);
+    }
     __syncthreads();
     for (uint32_t e = tid; e < 256; e += kThreads) {
         uint32_t sum = 0;
@@ -232,7 +128,10 @@ uint32_t hist_blocks(uint64_t n)
 
 hipError_t launch_histogram(const HistArgs &a, hipStream_t stream)
 {
-    hist_kernel<<<a.n_blocks, kThreads, 0, stream>>>(a);
+    if (a.elem == kElemE5M2)
+        hist_kernel<kElemE5M2><<<a.n_blocks, kThreads, 0, stream>>>(a);
+    else
+        hist_kernel<kElemBF16><<<a.n_blocks, kThreads, 0, stream>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
@@ -244,7 +143,8 @@ hipError_t launch_histogram(const HistArgs &a, hipStream_t stream)
 // a2-a4, a7  encode
 //
 // Four launches, none of which waits on another workgroup:
-//   pack   (one workgroup per tile of kEncTileWords words): sign+mantissa bytes and codes,
+//   pack   (one workgroup per tile: kEncTileWords BF16 words, or 2^kE8EncTileShift E5M2
+//          bytes in splitzip_e5m2.hip): sign+mantissa bits and codes,
 //          escape ranks inside the tile, escapes written compacted to the tile's scratch slot
 //          (or, past kSlotEscapes, to an overflow area reserved with one atomic), tile-local
 //          chunk offsets into chunk_off, the tile's escape count;
@@ -287,27 +187,6 @@ __device__ __forceinline__ uint32_t flags_keep(uint32_t nv)
     return nv >= 8 ? ~0u : (1u << (8 * (nv >> 1) + 4 + (nv & 1))) - 1u;
 }
 
-// Segment and first tile of global tile t (uniform when t is).
-__device__ __forceinline__ uint32_t tile_segment(const EncodeArgs &a, uint32_t t)
-{
-    return a.n_seg > 1 ? find_segment(a.tile_start, a.n_seg, t) : 0u;
-}
-
-__device__ __forceinline__ uint32_t segment_first_tile(const EncodeArgs &a, uint32_t s)
-{
-    return a.n_seg > 1 ? a.tile_start[s] : 0u;
-}
-
-__device__ __forceinline__ uint32_t segment_end_tile(const EncodeArgs &a, uint32_t s)
-{
-    return a.n_seg > 1 ? a.tile_start[s + 1] : a.n_tiles;
-}
-
-__device__ __forceinline__ SegDesc segment_desc(const EncodeArgs &a, uint32_t s)
-{
-    return a.n_seg > 1 ? a.segs[s] : a.seg0;
-}
-
 // ---- pack ---------------------------------------------------------------------------------
 
 __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs a)
@@ -330,6 +209,10 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
     if (a.packed && tid == 0 && t == segment_first_tile(a, s))
         a.seg_total[s] = 0;      // the sums launch adds the segment's escapes into it
     const uint64_t n = sd.n;
+    const SZ_GLOBAL uint16_t *xw = as_global(sd.data);
+    SZ_GLOBAL uint8_t *smb = as_global(sd.sm);
+    SZ_GLOBAL uint8_t *cdb = as_global(sd.codes);
+    SZ_GLOBAL uint64_t *chunk_off = as_global(sd.chunk_off);
     const uint64_t base = (uint64_t)(t - segment_first_tile(a, s)) << kEncTileShift;
     const uint64_t cmask = (1ull << a.log2_chunk) - 1;
 
@@ -346,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
             uint16_t wds[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k)
-                wds[k] = (g0[j] + k < n) ? sd.data[g0[j] + k] : (uint16_t)0;
+                wds[k] = (g0[j] + k < n) ? xw[g0[j] + k] : (uint16_t)0;
             v[j] = make_uint4(wds[0] | ((uint32_t)wds[1] << 16), wds[2] | ((uint32_t)wds[3] << 16),
                               wds[4] | ((uint32_t)wds[5] << 16), wds[6] | ((uint32_t)wds[7] << 16));
         }
@@ -368,70 +251,30 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
             codes &= codes_keep(nv);
             fl &= flags_keep(nv);
             for (uint32_t k = 0; k < nv; ++k)
-                sd.sm[g0[j] + k] = (uint8_t)((k < 4 ? sm_lo : sm_hi) >> (8 * (k & 3)));
+                smb[g0[j] + k] = (uint8_t)((k < 4 ? sm_lo : sm_hi) >> (8 * (k & 3)));
             for (uint32_t k = 0; k < (nv + 1) / 2; ++k)
-                sd.codes[(g0[j] >> 1) + k] = (uint8_t)(codes >> (8 * k));
+                cdb[(g0[j] >> 1) + k] = (uint8_t)(codes >> (8 * k));
         }
         flags[j] = fl;
         counts[j] = __popc(fl);
     }
 
     // ---- a3: escape ranks inside the tile ---------------------------------------------------
-    // Word order inside a wave is (group j, lane, word k).  Pack the per-group counts two per
-    // dword (16-bit fields), prefix-sum them over the lanes, then offset each group by the wave
-    // totals of the groups before it and by the totals of the earlier waves.
+    // Word order inside a wave is (group j, lane, word k).
     uint32_t rank[kEncGroups];
-    uint32_t wave_sum = 0;
-#pragma unroll
-    for (int j = 0; j < kEncGroups; j += 2) {
-        const uint32_t packed = counts[j] | (counts[j + 1] << 16);
-        const uint32_t incl = wave_inclusive_sum(packed, lane);
-        const uint32_t excl = incl - packed;
-        const uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
-        rank[j] = wave_sum + (excl & 0xFFFFu);
-        wave_sum += tot & 0xFFFFu;
-        rank[j + 1] = wave_sum + (excl >> 16);
-        wave_sum += tot >> 16;
-    }
-    if (lane == 0)
-        s_wave_total[wave] = wave_sum;
-    __syncthreads();
-    uint32_t wave_base = 0, tile_total = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        const uint32_t x = s_wave_total[w];
-        wave_base += (w < (int)wave) ? x : 0u;
-        tile_total += x;
-    }
+    uint32_t tile_total;
+    tile_escape_ranks<kEncGroups>(counts, lane, wave, s_wave_total, rank, tile_total);
 
     // where the tile's escapes go: its slot, or a range of the overflow area
-    uint32_t *dst = a.slots + (uint64_t)t * kSlotEscapes;
-    uint64_t room = kSlotEscapes;
-    if (tile_total > kSlotEscapes) {
-        if (tid == 0) {
-            // one atomic reserves the escapes' room and the tile's place in the overflow list
-            const uint64_t old = atomicAdd(a.ovf_ctr, (unsigned long long)tile_total + (1ull << kOvfTileShift));
-            const uint64_t off = old & kOvfOffsetMask;
-            s_ovf = off;
-            a.tile_ovf[t] = off;
-            a.ovf_tiles[old >> kOvfTileShift] = t;
-            if (off + tile_total > a.ovf_cap)
-                atomicOr(a.err, kErrOverflowArea);
-        }
-        __syncthreads();
-        const uint64_t off = s_ovf;
-        dst = a.ovf + off;
-        room = off < a.ovf_cap ? a.ovf_cap - off : 0;
-    }
-    if (tid == 0)
-        a.tile_count[t] = tile_total;
+    uint64_t room;
+    uint32_t *dst = tile_escape_dest(a, t, tile_total, tid, &s_ovf, room);
 
     // escapes: (position inside the tile, exponent); tile-local chunk offsets
 #pragma unroll
     for (int j = 0; j < kEncGroups; ++j) {
-        const uint32_t r0 = wave_base + rank[j];
+        const uint32_t r0 = rank[j];
         if (g0[j] < n && (g0[j] & cmask) == 0)
-            sd.chunk_off[g0[j] >> a.log2_chunk] = r0;
+            chunk_off[g0[j] >> a.log2_chunk] = r0;
         uint32_t z = flags[j];
         if (z) {
             // the group's 8 exponents, word k in byte k (a dword >> 7 holds the exponent of its
@@ -619,15 +462,16 @@ __device__ __forceinline__ uint8_t *packed_exps(const SegDesc &sd, uint64_t E)
     return E <= sd.esc ? reinterpret_cast<uint8_t *>(sd.esc_pos + E) : nullptr;
 }
 
-// The 64-byte canonical header: "SZB1", version 1, header bytes 64, chunk size, flags 0,
-// n, n_chunks, E, the segment's codebook, 8 zero bytes (all little-endian).
+// The 64-byte canonical header: "SZB1", version 1, header bytes 64, chunk size, flags (the
+// element type: 0 BF16, 1 E5M2), n, n_chunks, E, the segment's codebook, 8 zero bytes (all
+// little-endian).
 __device__ void write_header(const SegDesc &sd, const EncodeArgs &a, uint64_t E)
 {
     const uint64_t C = 1ull << a.log2_chunk;
     const uint64_t n_chunks = (sd.n + C - 1) >> a.log2_chunk;
     const uint32_t *cb = a.cbs + 4u * sd.book;
     uint4 *h = reinterpret_cast<uint4 *>(sd.header);
-    h[0] = make_uint4(0x31425A53u, 1u | (64u << 16), (uint32_t)C, 0u);
+    h[0] = make_uint4(0x31425A53u, 1u | (64u << 16), (uint32_t)C, a.elem);
     h[1] = make_uint4((uint32_t)sd.n, (uint32_t)(sd.n >> 32), (uint32_t)n_chunks, (uint32_t)(n_chunks >> 32));
     h[2] = make_uint4((uint32_t)E, (uint32_t)(E >> 32), cb[0], cb[1]);
     h[3] = make_uint4(cb[2], cb[3], 0u, 0u);
@@ -715,7 +559,7 @@ __global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs
     uint32_t n_chunks_here = 0;
     if (valid) {
         const SegDesc sd = segment_desc(a, seg);
-        base = (uint64_t)(u - segment_first_tile(a, seg)) << kEncTileShift;
+        base = (uint64_t)(u - segment_first_tile(a, seg)) << a.tile_shift;
         if (u + 1 == segment_end_tile(a, seg)) {
             // the segment's last tile knows the segment's escape count
             const uint64_t E = prefix + count;
@@ -726,7 +570,8 @@ __global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs
         }
         if (base < sd.n) {
             // chunks that start inside this tile
-            const uint64_t words = sd.n - base < (uint64_t)kEncTileWords ? sd.n - base : (uint64_t)kEncTileWords;
+            const uint64_t tile_words = 1ull << a.tile_shift;
+            const uint64_t words = sd.n - base < tile_words ? sd.n - base : tile_words;
             c_first = (base + cmask) >> a.log2_chunk;
             n_chunks_here = (uint32_t)(((base + words + cmask) >> a.log2_chunk) - c_first);
         }
@@ -772,13 +617,13 @@ __global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs
                 if (a.n_seg > 1)
                     sd = a.segs[s_seg[i]];
                 where[k] = sd.chunk_off + s_chunk0[i] + (e - s_cfirst[i]);
-                val[k] = *where[k] + s_prefix[i];
+                val[k] = *as_global(where[k]) + s_prefix[i];
             }
         }
 #pragma unroll
         for (int k = 0; k < kBatch; ++k)
             if (where[k])
-                *where[k] = val[k];
+                *as_global(where[k]) = val[k];
     }
 
     // move the slot escapes: consecutive threads take consecutive escapes (coalesced reads of
@@ -807,8 +652,8 @@ __global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs
             const uint64_t d = s_prefix[i] + (j - s_first[i]);
             uint8_t *exps = a.packed ? packed_exps(sd, s_E[i]) : sd.esc_exp;
             if (d < sd.esc && exps) {
-                sd.esc_pos[d] = (uint16_t)((s_base[i] + (ent[k] & 0xFFFFu)) & cmask);
-                exps[d] = (uint8_t)(ent[k] >> 16);
+                as_global(sd.esc_pos)[d] = (uint16_t)((s_base[i] + (ent[k] & 0xFFFFu)) & cmask);
+                as_global(exps)[d] = (uint8_t)(ent[k] >> 16);
             }
         }
     }
@@ -825,7 +670,7 @@ __global__ __launch_bounds__(kThreads) void encode_spill_kernel(const EncodeArgs
         const uint32_t t = a.ovf_tiles[i];
         const uint32_t s = tile_segment(a, t);
         const SegDesc sd = segment_desc(a, s);
-        const uint64_t base = (uint64_t)(t - segment_first_tile(a, s)) << kEncTileShift;
+        const uint64_t base = (uint64_t)(t - segment_first_tile(a, s)) << a.tile_shift;
         const uint64_t pre = a.tile_prefix[t];
         const uint32_t cnt = a.tile_count[t];
         const uint64_t off = a.tile_ovf[t];
@@ -845,8 +690,8 @@ __global__ __launch_bounds__(kThreads) void encode_spill_kernel(const EncodeArgs
                 const uint32_t r = r0 + k * kThreads;
                 const uint64_t d = pre + r;
                 if (r < lim && d < sd.esc && exps) {
-                    sd.esc_pos[d] = (uint16_t)((base + (e[k] & 0xFFFFu)) & cmask);
-                    exps[d] = (uint8_t)(e[k] >> 16);
+                    as_global(sd.esc_pos)[d] = (uint16_t)((base + (e[k] & 0xFFFFu)) & cmask);
+                    as_global(exps)[d] = (uint8_t)(e[k] >> 16);
                 }
             }
         }
@@ -857,6 +702,8 @@ hipError_t launch_encode_stage(int stage, const EncodeArgs &a, hipStream_t strea
 {
     switch (stage) {
     case 0:
+        if (a.elem == kElemE5M2)
+            return launch_encode_pack_e5m2(a, stream);
         encode_pack_kernel<<<a.n_tiles, kThreads, 0, stream>>>(a);
         break;
     case 1:
@@ -1100,6 +947,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream)
 {
+    if (a.elem == kElemE5M2)
+        return launch_decode_e5m2(a, stream);
     // The dynamic LDS reservation is unused: it caps decode at 5 workgroups per CU, which
     // streams about 3 % faster than the 8 that registers would allow (less contention for HBM).
     decode_kernel<<<xcd_grid(a.n_tiles), kThreads, kDecodeLdsReserve, stream>>>(a);

@@ -45,9 +45,16 @@ def test_sizes_match_oracle(n, C, E):
     assert sz.splitzip_chunk_count(n, C) == -(-n // C)
 
 
+@pytest.mark.parametrize("n,C,E", [(0, 16, 0), (7, 16, 3), (20, 16, 9), (1 << 32, 1024, 12345),
+                                   (256, 16, 128), (1000003, 4096, 77)])
+def test_e5m2_sizes_match_oracle(n, C, E):
+    assert sz.splitzip_e5m2_compressed_bytes(n, C, E) == oracle.get().compressed_bytes8(n, C, E)
+
+
 def test_bad_chunk_sizes_have_no_size():
     for C in (0, 8, 24, 131072):
         assert sz.splitzip_compressed_bytes(100, C, 0) == 0
+        assert sz.splitzip_e5m2_compressed_bytes(100, C, 0) == 0
         assert sz.splitzip_chunk_count(100, C) == 0
 
 
@@ -59,7 +66,24 @@ def test_read_header_of_oracle_streams():
         s = o.serialize(o.encode(x[:n], cb, 16))
         h = sz.splitzip_read_header(s)
         assert h == {"n": n, "chunk_size": 16, "n_escapes": o.stream_info(s)["n_escapes"],
-                     "codebook": bytes(cb)}
+                     "codebook": bytes(cb), "elem": sz.ELEM_BF16}
+
+
+def test_read_header_of_oracle_e5m2_streams():
+    o = oracle.get()
+    x = np.random.default_rng(3).integers(0, 256, 300).astype(np.uint8)
+    cb = o.calibrate8(x[:100])[0]
+    for n, C in ((0, 16), (7, 16), (300, 64)):
+        e = o.encode8(x[:n], cb, C)
+        s = o.serialize8(e)
+        assert sz.splitzip_read_header(s) == {"n": n, "chunk_size": C, "n_escapes": e["n_escapes"],
+                                              "codebook": bytes(cb), "elem": sz.ELEM_E5M2}
+    # an E5M2 header whose codebook holds a value above 31 is malformed
+    b = bytearray(o.serialize8(o.encode8(x, cb, 64)))
+    b[40] = 32
+    with pytest.raises(sz.SplitZipError) as ei:
+        sz.splitzip_read_header(bytes(b))
+    assert ei.value.status == sz.E_FORMAT
 
 
 def test_read_header_rejects_malformed():
@@ -67,7 +91,7 @@ def test_read_header_rejects_malformed():
     _, cal, x = pins.worked_example()
     cb, _, _ = o.calibrate(cal)
     s = o.serialize(o.encode(x, cb, 16))
-    for i, val in ((0, 0x54), (4, 2), (6, 65), (8, 24), (12, 1), (24, 9), (60, 1)):
+    for i, val in ((0, 0x54), (4, 2), (6, 65), (8, 24), (12, 1), (12, 2), (24, 9), (60, 1)):
         b = bytearray(s)
         b[i] = val
         with pytest.raises(sz.SplitZipError) as ei:
@@ -128,6 +152,27 @@ def test_codebook_and_statistics_validation_before_any_device_call():
     assert L.splitzip_exponent_stats(None, None, None, None, None) == sz.E_INVALID
 
 
+def test_e5m2_validation_before_any_device_call():
+    L = sz.lib()
+    h = ctypes.c_void_p()
+    cov = ctypes.c_double()
+    for C in (0, 8, 1000):
+        assert L.splitzip_calibrate_e5m2(None, 0, C, None, ctypes.byref(h), ctypes.byref(cov), None) == sz.E_INVALID
+    assert L.splitzip_calibrate_e5m2(ctypes.c_void_p(0x1004), 8, 1024, None, ctypes.byref(h),
+                                     ctypes.byref(cov), None) == sz.E_INVALID
+    P = ctypes.c_void_p * 1
+    N = ctypes.c_uint64 * 1
+    assert L.splitzip_calibrate_books_e5m2(0, P(0x1000), N(8), 1024, None, ctypes.byref(h),
+                                           None, None) == sz.E_INVALID
+    hist = (ctypes.c_uint64 * 32)()
+    assert L.splitzip_histogram_e5m2(1, P(0x1001), N(8), None, hist) == sz.E_INVALID
+    # codebook values must be 16 distinct 5-bit exponents
+    cb = (ctypes.c_uint8 * 16)(*range(16, 32))
+    cb[0] = 32
+    assert L.splitzip_codec_from_codebooks_e5m2(1, cb, 1024, ctypes.byref(h)) == sz.E_INVALID
+    assert b"5-bit" in L.splitzip_last_error()
+    assert L.splitzip_codec_element(None, None) == sz.E_INVALID
+
 def _stats_agree(o, hist):
     st = sz.exponent_stats(hist)
     h = np.asarray(hist, np.uint64)
@@ -154,6 +199,22 @@ def test_exponent_stats_match_oracle():
         _stats_agree(o, h.tolist())
     st = sz.exponent_stats(o.histogram(np.arange(65536, dtype=np.uint16)).tolist())
     assert st["entropy_bits"] == 8.0 and st["coverage"] == 1 / 16 and st["distinct"] == 256
+
+
+def test_e5m2_exponent_stats_match_oracle():
+    """A 32-bin E5M2 histogram (padded by the binding): the codebook the library ranks
+    equals the oracle's E5M2 codebook, coverage and distinct count too."""
+    o = oracle.get()
+    rng = np.random.default_rng(9)
+    for _ in range(30):
+        h = rng.integers(0, 1 << 30, 32, dtype=np.uint64)
+        h[rng.random(32) < rng.random()] = 0
+        st = sz.exponent_stats(h.tolist())
+        cb = o.codebook8(h)
+        assert st["codebook"] == bytes(cb)
+        assert st["coverage"] == o.coverage8(h, cb, int(h.sum()))
+        assert st["distinct"] == int(np.count_nonzero(h))
+        assert max(st["codebook"]) < 32
 
 
 def test_no_cpu_fallback():

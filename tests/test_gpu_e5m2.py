@@ -1,0 +1,293 @@
+"""GPU parity of the FP8 E5M2 codec (the same calls through the C ABI, E5M2 codec)
+against the CPU oracle's E5M2 functions.
+
+Streams must equal the oracle's byte for byte (3-bit field stream, codes, chunk offsets,
+escapes, canonical serialization), decode must return the input bit for bit, and
+calibration must give the oracle's 32-bin histogram, codebook and coverage.  Sizes span
+several pack tiles (32768 elements) and decode tiles (16384) with ragged tails, every
+chunk-size regime (chunks that start inside a 32-element lane group at C = 16, chunks
+larger than a decode tile), empty and tiny segments, several codebooks, packed streams,
+corrupt metadata, and the 4.3 GB E5M2 long-prefill KV at full size."""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import lossless_bf16_kv_amd as sz
+import oracle
+import oracle_pins as pins
+import workloads
+from conftest import hex_bytes, ints, load_golden
+
+pytestmark = pytest.mark.gpu
+
+O = oracle.get()
+DEV = torch.device("cuda:0")
+
+
+def dev8(b: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.array(b, np.uint8, copy=True)).to(DEV)
+
+
+def host(t: torch.Tensor, dtype) -> np.ndarray:
+    if t.dtype == torch.float8_e5m2:
+        t = t.view(torch.uint8)
+    return t.cpu().numpy().view(dtype)
+
+
+def codec_for(cal: np.ndarray, C: int) -> sz.Codec:
+    c = sz.Codec(DEV, C, elem="e5m2")
+    c.calibrate(dev8(cal))
+    return c
+
+
+def assert_same_stream(codec: sz.Codec, enc: sz.Encoded, x: np.ndarray):
+    cb = np.frombuffer(enc.codebook, np.uint8)
+    ref = O.encode8(x, cb, codec.chunk_size)
+    assert enc.n_escapes == ref["n_escapes"]
+    assert enc.compressed_bytes == ref["compressed_bytes"]
+    assert np.array_equal(host(enc.sm, np.uint8), ref["sm3"])
+    assert np.array_equal(host(enc.codes, np.uint8), ref["codes"])
+    assert np.array_equal(host(enc.chunk_off, np.uint64), ref["chunk_off"])
+    assert np.array_equal(host(enc.esc_pos, np.uint16), ref["esc_pos"])
+    assert np.array_equal(host(enc.esc_exp, np.uint8), ref["esc_exp"])
+    assert enc.to_bytes(codec) == O.serialize8(ref)
+    return ref
+
+
+def test_worked_example():
+    g = load_golden("worked_example_e5m2_c16.txt")
+    C = int(g["chunk_size"])
+    cal = np.frombuffer(hex_bytes(g["calibration_u8"]), np.uint8)
+    codec = sz.Codec(DEV, C, elem="e5m2")
+    cov = codec.calibrate(dev8(cal))
+    assert codec.codebook == hex_bytes(g["codebook"])
+    num, den = (int(t) for t in g["calibration_coverage"].split("/"))
+    assert cov == num / den
+    x = np.frombuffer(hex_bytes(g["input_u8"]), np.uint8)
+    enc = codec.encode(dev8(x))
+    assert bytes(host(enc.sm, np.uint8)) == hex_bytes(g["sm3"])
+    assert bytes(host(enc.codes, np.uint8)) == hex_bytes(g["codes"])
+    assert host(enc.chunk_off, np.uint64).tolist() == ints(g["chunk_off"])
+    assert host(enc.esc_pos, np.uint16).tolist() == ints(g["esc_pos"])
+    assert host(enc.esc_exp, np.uint8).tolist() == ints(g["esc_exp"])
+    assert enc.compressed_bytes == int(g["compressed_bytes"])
+    assert enc.to_bytes(codec)[:64] == hex_bytes(g["header"])
+    y = codec.decode(enc)
+    assert y.dtype == torch.uint8 and np.array_equal(host(y, np.uint8), x)   # the input's dtype
+    y8 = codec.decode(codec.encode(dev8(x).view(torch.float8_e5m2)))
+    assert y8.dtype == torch.float8_e5m2 and np.array_equal(host(y8, np.uint8), x)
+    e7 = codec.encode(dev8(x[:7]))
+    assert bytes(host(e7.sm, np.uint8)) == hex_bytes(g["prefix7_sm3"])
+    assert bytes(host(e7.codes, np.uint8)) == hex_bytes(g["prefix7_codes"])
+    assert e7.compressed_bytes == int(g["prefix7_compressed_bytes"])
+    assert np.array_equal(host(codec.decode(e7), np.uint8), x[:7])
+    e0 = codec.encode(dev8(x[:0]))
+    assert e0.compressed_bytes == int(g["empty_compressed_bytes"])
+
+
+@pytest.mark.parametrize("C", [16, 64, 1024, 65536])
+def test_every_byte_value(C):
+    """All 256 bytes, repeated 300 times: every exponent occurs equally often, so the
+    codebook is 0..15 and half the elements escape."""
+    x = np.tile(np.arange(256, dtype=np.uint8), 300)
+    codec = codec_for(x, C)
+    assert codec.codebook == bytes(range(16)) and codec.coverage == 0.5
+    enc = codec.encode(dev8(x))
+    ref = assert_same_stream(codec, enc, x)
+    assert ref["n_escapes"] == x.size // 2
+    assert np.array_equal(host(codec.decode(enc), np.uint8), x)
+
+
+@pytest.mark.parametrize("n", [1, 5, 16, 17, 4099, 1000003])
+def test_calibration_matches_oracle(n):
+    x = workloads.e5m2_mixed(n, seed=n, wide_fraction=0.3)
+    codec = codec_for(x, 1024)
+    cb, cov, h = O.calibrate8(x)
+    assert codec.histogram == h.tolist()
+    assert codec.codebook == bytes(cb)
+    assert codec.coverage == cov
+    assert sz.histograms([dev8(x)], elem="e5m2")[0] == h.tolist()
+
+
+FUZZ = [(n, C, gen) for n, C, gen in [
+    (1, 16, "random"), (9, 16, "mixed"), (31, 16, "random"), (33, 32, "mixed"),
+    (16383, 1024, "mixed"), (16384, 1024, "normal"), (16385, 16, "random"),
+    (32767, 64, "mixed"), (32768 + 5, 16, "mixed"), (3 * 32768 + 13, 32, "random"),
+    (100003, 1024, "random"), (100003, 4096, "mixed"), (196613, 16384, "mixed"),
+    (196613, 32768, "random"), (196613, 65536, "mixed"), ((1 << 20) + 77, 1024, "mixed"),
+    ((1 << 20) + 77, 16, "random"),
+]]
+
+
+@pytest.mark.parametrize("n,C,gen", FUZZ)
+def test_fuzz_stream_parity(n, C, gen):
+    make = {"random": workloads.e5m2_random, "mixed": workloads.e5m2_mixed,
+            "normal": workloads.e5m2_normal}[gen]
+    x = make(n, 19 * n + C)
+    codec = codec_for(workloads.e5m2_normal(50000, 3), C)
+    enc = codec.encode(dev8(x))
+    ref = assert_same_stream(codec, enc, x)
+    assert np.array_equal(host(codec.decode(enc), np.uint8), x)
+    y = codec.decode_bytes(O.serialize8(ref))
+    assert np.array_equal(host(y, np.uint8), x)
+
+
+def test_batch_with_empty_and_tiny_segments():
+    sizes = [0, 1, 7, 16384, 32769, 0, 100, 3 * 32768 + 5]
+    xs = [workloads.e5m2_mixed(n, 100 + i, wide_fraction=0.3) for i, n in enumerate(sizes)]
+    codec = codec_for(workloads.e5m2_normal(20000, 4), 16)
+    encs = codec.encode_batch([dev8(x) for x in xs])
+    for x, e in zip(xs, encs):
+        assert_same_stream(codec, e, x)
+    for x, y in zip(xs, codec.decode_batch(encs)):
+        assert np.array_equal(host(y, np.uint8), x)
+
+
+@pytest.mark.parametrize("C", [64, 1024, 65536])
+def test_several_codebooks(C):
+    """Three books calibrated on differently scaled draws; segments coded with their own
+    book and with another scale's book, one encode and one decode launch."""
+    cals = [workloads.e5m2_normal(40000, 60 + k, sigma=s) for k, s in enumerate((1.0, 300.0, 0.01))]
+    codec = sz.Codec(DEV, C, elem="e5m2")
+    covs = codec.calibrate_books([dev8(c) for c in cals])
+    for cal, book, cov in zip(cals, codec.books, covs):
+        cb, ocov, _ = O.calibrate8(cal)
+        assert book == bytes(cb) and cov == ocov
+    xs = [workloads.e5m2_normal(n, 70 + i, sigma=s) for i, (n, s) in
+          enumerate([(50000, 1.0), (70001, 300.0), (3, 0.01), (40000, 300.0), (0, 1.0)])]
+    books = [0, 1, 2, 0, 1]
+    encs = codec.encode_batch([dev8(x) for x in xs], books=books)
+    for x, e in zip(xs, encs):
+        assert_same_stream(codec, e, x)
+    for x, y in zip(xs, codec.decode_batch(encs)):
+        assert np.array_equal(host(y, np.uint8), x)
+
+
+def test_capacity_retry_gives_identical_stream():
+    x = workloads.e5m2_random(50000, 9)
+    codec = codec_for(workloads.e5m2_normal(20000, 5), 1024)
+    enc = codec.empty_encoded(x.size, escape_capacity=10)
+    assert codec.encode_into([dev8(x)], [enc]) == sz.E_CAPACITY
+    ref = O.encode8(x, np.frombuffer(codec.codebook, np.uint8), 1024)
+    assert enc.n_escapes == ref["n_escapes"]
+    assert_same_stream(codec, codec.encode(dev8(x)), x)
+
+
+def test_decode_flags_corrupt_metadata_without_faulting():
+    x = workloads.e5m2_mixed(4 * 16384, 12, wide_fraction=0.2)
+    codec = codec_for(workloads.e5m2_normal(20000, 7), 1024)
+    enc = codec.encode(dev8(x))
+    assert enc.n_escapes > 100
+    y = torch.empty_like(codec.decode(enc))
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    for field, idx, val in (("chunk_off", 3, enc.n_escapes + 1000), ("esc_pos_buf", 5, 4000),
+                            ("esc_exp_buf", 7, 40)):
+        bad = dataclasses.replace(enc, chunk_off=enc.chunk_off.clone(), esc_pos_buf=enc.esc_pos_buf.clone(),
+                                  esc_exp_buf=enc.esc_exp_buf.clone())
+        getattr(bad, field)[idx] = val
+        err.zero_()
+        codec.decode_into([bad], [y], d_error=err.data_ptr())
+        torch.cuda.synchronize()
+        assert int(err.item()) != 0, field
+    err.zero_()
+    codec.decode_into([enc], [y], d_error=err.data_ptr())
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0 and np.array_equal(host(y, np.uint8), x)
+
+
+def test_element_type_and_codebook_checks():
+    x = workloads.e5m2_normal(5000, 1)
+    a = codec_for(workloads.e5m2_normal(5000, 2), 1024)
+    enc = a.encode(dev8(x))
+    s = enc.to_bytes(a)
+    assert sz.splitzip_read_header(s)["elem"] == sz.ELEM_E5M2
+    # a BF16 codec with the same codebook bytes refuses the E5M2 stream
+    b = sz.Codec.from_codebook(a.codebook, 1024, DEV)
+    with pytest.raises(sz.SplitZipError) as ei:
+        b.decode_bytes(s)
+    assert ei.value.status == sz.E_CODEBOOK
+    # an E5M2 codec rebuilt from the header decodes it
+    c = sz.Codec.from_codebook(sz.splitzip_read_header(s)["codebook"], 1024, DEV, elem="e5m2")
+    assert np.array_equal(host(c.decode_bytes(s), np.uint8), x)
+    assert sz.splitzip_codec_element(c.handle) == sz.ELEM_E5M2
+
+
+# ---- packed streams ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,C", [(0, 1024), (128, 16), (32768 * 3 + 128 * 7, 1024), ((1 << 20) + 256, 65536)])
+def test_packed_stream_equals_oracle_serialization(n, C):
+    x = workloads.e5m2_mixed(n, 500 + n, wide_fraction=0.05)
+    codec = codec_for(workloads.e5m2_normal(30000, 13), C)
+    p = codec.encode_packed(dev8(x))
+    ref = O.encode8(x, np.frombuffer(codec.codebook, np.uint8), C)
+    assert p.n_escapes == ref["n_escapes"]
+    assert p.to_bytes() == O.serialize8(ref)
+    assert np.array_equal(host(codec.decode_packed(p), np.uint8), x)
+    # an oracle-written stream decodes through the packed path
+    buf = sz.packed_buffer(len(O.serialize8(ref)), DEV)
+    buf.copy_(torch.from_numpy(np.frombuffer(O.serialize8(ref), np.uint8).copy()))
+    y = codec.decode_packed(buf, n=n)
+    assert np.array_equal(host(y, np.uint8), x)
+
+
+def test_packed_header_checks():
+    n = 4096
+    x = workloads.e5m2_mixed(n, 3)
+    codec = codec_for(workloads.e5m2_normal(30000, 14), 1024)
+    p = codec.encode_packed(dev8(x))
+    good = p.to_bytes()
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    for off, val in ((12, 0), (40, 33), (16, 0x80), (0, 0x41)):
+        b = bytearray(good)
+        b[off] = val
+        buf = sz.packed_buffer(len(b), DEV)
+        buf.copy_(torch.from_numpy(np.frombuffer(bytes(b), np.uint8).copy()))
+        err.zero_()
+        out = codec.decode_packed_batch([buf], [n], d_error=err.data_ptr())[0]
+        torch.cuda.synchronize()
+        assert int(err.item()) & 16, off
+    with pytest.raises(sz.SplitZipError):
+        codec.encode_packed(dev8(x[:100]))         # not a multiple of 128
+
+
+# ---- full size: the long-prefill KV cast to E5M2 (2^32 bytes) ---------------------------------
+
+@pytest.fixture(scope="module")
+def kv8():
+    return workloads.config3_e5m2()
+
+
+def test_long_prefill_e5m2_full_size(kv8):
+    x = kv8.segments[0]
+    assert x.size == 1 << 32
+    C = kv8.chunk_size
+    xd = dev8(x)
+    codec = codec_for(kv8.calibration, C)
+    cb, cov, _ = O.calibrate8(kv8.calibration)
+    assert codec.codebook == bytes(cb) and codec.coverage == cov
+    enc = codec.encode(xd)
+    # E from the oracle's exact histogram of the whole input; offsets and size
+    h = O.histogram8(x)
+    E = int(x.size - sum(int(h[e]) for e in cb))
+    assert enc.n_escapes == E and enc.compressed_bytes == O.compressed_bytes8(x.size, C, E)
+    off = enc.chunk_off
+    assert int(off[0]) == 0 and int(off[-1]) == E and bool((off[1:] >= off[:-1]).all())
+    # sampled chunks, each oracle-encoded on its own (C = 1024: a chunk's fields are whole bytes)
+    rng = np.random.default_rng(8)
+    n_chunks = x.size // C
+    offs = host(enc.chunk_off, np.uint64)
+    for c in sorted(set(rng.integers(0, n_chunks, 40).tolist()) | {0, n_chunks - 1}):
+        lo, hi = c * C, (c + 1) * C
+        ref = O.encode8(x[lo:hi], cb, C)
+        a, b = int(offs[c]), int(offs[c + 1])
+        assert b - a == ref["n_escapes"], c
+        assert np.array_equal(host(enc.sm[3 * lo // 8:3 * hi // 8], np.uint8), ref["sm3"])
+        assert np.array_equal(host(enc.codes[lo // 2:hi // 2], np.uint8), ref["codes"])
+        assert np.array_equal(host(enc.esc_pos_buf[a:b], np.uint16), ref["esc_pos"])
+        assert np.array_equal(host(enc.esc_exp_buf[a:b], np.uint8), ref["esc_exp"])
+    y = codec.decode(enc)
+    assert torch.equal(y.view(torch.uint8), xd)

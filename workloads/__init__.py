@@ -16,6 +16,11 @@ Random numbers: numpy PCG64 via ``numpy.random.default_rng``; normals are
 ``standard_normal(dtype=float32)`` and scaling happens in float32.  Conversion
 to BF16 is round-to-nearest-even of the float32 bits.  Special values are
 written as raw bit patterns.
+
+FP8 E5M2 inputs (an FP8 E5M2 KV cache, which the pages' README "FAQ" names) are the
+same draws cast to E5M2: float32 to FP16 (numpy, round to nearest even), then FP16 to
+E5M2 by rounding the FP16 bits to their top byte (nearest even; both formats have a
+5-bit exponent with bias 15, so this is exact E5M2 rounding of the FP16 value).
 """
 from __future__ import annotations
 
@@ -47,6 +52,16 @@ def bf16_bits(f32: np.ndarray) -> np.ndarray:
 
 def bf16_to_f32(words: np.ndarray) -> np.ndarray:
     return (np.asarray(words, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def e5m2_bits(f32: np.ndarray) -> np.ndarray:
+    """Cast float32 values to FP8 E5M2 bytes: to FP16 (round to nearest even, overflow to
+    Inf), then the FP16 bits rounded to their top byte (nearest even).  Inputs must not be
+    NaN."""
+    with np.errstate(over="ignore"):
+        h = np.ascontiguousarray(f32, dtype=np.float32).astype(np.float16)
+    h = h.view(np.uint16).astype(np.uint32)
+    return ((h + np.uint32(0x7F) + ((h >> np.uint32(8)) & np.uint32(1))) >> np.uint32(8)).astype(np.uint8)
 
 
 @dataclasses.dataclass
@@ -242,6 +257,72 @@ def config5(requests: int = 256, threads: int | None = None) -> Workload:
                     f"[len,8,128] per request from the GQA layer generator (token seeds "
                     f"[50,r]) = {2 * requests} segments, one launch; calibrated on the GQA "
                     f"layer calibration draw; chunk 1024")
+
+
+# ---- FP8 E5M2: the long-prefill KV cast to E5M2 -------------------------------------------
+
+def config3_e5m2(layers: int = 64, tokens: int = 32768, cal_tokens: int = 2048,
+                 chunk_size: int = 1024, threads: int | None = None) -> Workload:
+    """The long-prefill KV of config3 (same parameters and token draws, hence the same BF16
+    values) cast to E5M2: an FP8 E5M2 KV cache, n = layers * 2 * tokens * 1024 bytes (2**32
+    = 4.3 GB with the defaults), one segment; calibration = the cast calibration draw."""
+    params = config3_params(layers)
+    per_layer = 2 * tokens * CHANNELS
+    m = 2 * cal_tokens * CHANNELS
+    data = np.empty(layers * per_layer, np.uint8)
+    cal = np.empty(layers * m, np.uint8)
+
+    def make(layer: int) -> None:
+        w = kv_layer(np.random.default_rng([31, layer]), params[layer], tokens)
+        data[layer * per_layer:(layer + 1) * per_layer] = e5m2_bits(bf16_to_f32(w))
+        c = kv_layer(np.random.default_rng([32, layer]), params[layer], cal_tokens)
+        cal[layer * m:(layer + 1) * m] = e5m2_bits(bf16_to_f32(c))
+
+    with _cf.ThreadPoolExecutor(min(_threads(threads), 8)) as ex:
+        list(ex.map(make, range(layers)))
+    return Workload(f"long_prefill_kv_e5m2_{layers}L_{tokens}tok_8x128", [data], cal, chunk_size,
+                    f"the {layers}-layer long-prefill K+V ({tokens} tokens per layer, 8 KV heads "
+                    f"x 128; params seed 30, token seeds [31,l]) cast to FP8 E5M2 ({data.size} "
+                    f"bytes = {data.size / 1e9:.2f} GB); calibration = the separate "
+                    f"{cal_tokens}-token draw per layer (seeds [32,l]) cast the same way; chunk "
+                    f"{chunk_size}")
+
+
+def e5m2_special_bytes(rng: np.random.Generator, count: int) -> np.ndarray:
+    """Uniformly one of {0, subnormal, Inf, NaN}, random sign; subnormal mantissas 1..3,
+    NaN mantissas 1..3 (raw bit patterns)."""
+    cls = rng.integers(0, 4, size=count)
+    sign = rng.integers(0, 2, size=count).astype(np.uint8) << np.uint8(7)
+    mant = rng.integers(1, 4, size=count).astype(np.uint8)
+    b = np.where(cls == 0, np.uint8(0),
+        np.where(cls == 1, mant,
+        np.where(cls == 2, np.uint8(0x7C), np.uint8(0x7C) | mant))).astype(np.uint8)
+    return (b | sign).astype(np.uint8)
+
+
+def e5m2_mixed(n: int, seed: int, wide_fraction: float = 0.02,
+               special_fraction: float = 0.01) -> np.ndarray:
+    """N(0,1) cast to E5M2, where a fraction gets a random power-of-two scale in 2^-20..2^20
+    and a fraction is replaced by special values (zeros, subnormals, Inf, NaN)."""
+    rng = np.random.default_rng(seed)
+    z = rng.standard_normal(n, dtype=np.float32)
+    wide = rng.random(n) < wide_fraction
+    z[wide] *= np.exp2(rng.integers(-20, 20, size=int(wide.sum()), endpoint=True)).astype(np.float32)
+    x = e5m2_bits(z)
+    k = int(round(special_fraction * n))
+    if k:
+        x[rng.choice(n, size=k, replace=False)] = e5m2_special_bytes(rng, k)
+    return x
+
+
+def e5m2_random(n: int, seed: int) -> np.ndarray:
+    """Uniformly random bytes (every E5M2 exponent equally likely)."""
+    return np.random.default_rng(seed).integers(0, 256, size=n, dtype=np.uint8)
+
+
+def e5m2_normal(n: int, seed: int, sigma: float = 1.0) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    return e5m2_bits(rng.standard_normal(n, dtype=np.float32) * np.float32(sigma))
 
 
 # ---- small fuzz inputs for parity tests -------------------------------------------------
