@@ -6,6 +6,8 @@ calibrated once on the workload's separate calibration draw before timing, as th
 pages prescribe (offline calibration).  Inputs are resident in HBM before timing.
 
 Prints one JSON line.  Throughput is GB/s of BF16 input (2 bytes per word, 10^9).
+``--elem e5m2`` measures the FP8 E5M2 codec on the same long-prefill KV cast to E5M2
+(GB/s of E5M2 input, 1 byte per element).
 """
 from __future__ import annotations
 
@@ -25,7 +27,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for name in ("splitzip_kernels.hip", "splitzip_internal.h"):
+    for name in ("splitzip_kernels.hip", "splitzip_e5m2.hip", "splitzip_device.h", "splitzip_internal.h"):
         with open(os.path.join(ROOT, "lossless_bf16_kv_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -54,6 +56,10 @@ def workloads_kv_parts(flat, layers, tokens):
 
 def load_workload(args):
     import workloads
+    if args.elem == "e5m2":
+        if args.config != 3:
+            raise SystemExit("--elem e5m2 measures the long-prefill KV cast to E5M2 (--config 3)")
+        return workloads.config3_e5m2(layers=args.layers, chunk_size=args.chunk_size)
     if args.config == 3:
         return workloads.config3(layers=args.layers, chunk_size=args.chunk_size)
     if args.config == 4:
@@ -64,9 +70,10 @@ def load_workload(args):
 
 
 ENC_TILE_WORDS = 16384     # encode tile (words per workgroup)
+ENC_TILE_E5M2 = 32768      # encode tile (E5M2 bytes per workgroup)
 
 
-def algorithmic_bytes(ns, Es, C):
+def algorithmic_bytes(ns, Es, C, e5m2: bool = False):
     """Bytes each kernel must move per launch (reads + writes), from the stream format.
 
     encode (its four launches together) reads 2n and writes the sections
@@ -79,11 +86,13 @@ def algorithmic_bytes(ns, Es, C):
     out = {"encode": 0, "decode": 0, "encode_pack": 0, "encode_sums": 0, "encode_place": 0}
     for n, E in zip(ns, Es):
         n_ch = -(-n // C)
-        tiles = max(1, -(-n // ENC_TILE_WORDS))
-        sections = n + (n + 1) // 2 + 8 * (n_ch + 1) + 3 * E
-        out["encode"] += 2 * n + sections
-        out["decode"] += sections + 2 * n
-        out["encode_pack"] += 2 * n + n + (n + 1) // 2 + 8 * n_ch + 4 * E + 4 * tiles
+        tiles = max(1, -(-n // (ENC_TILE_E5M2 if e5m2 else ENC_TILE_WORDS)))
+        x_bytes = n if e5m2 else 2 * n                    # input elements
+        sm_bytes = -(-3 * n // 8) if e5m2 else n          # sign+mantissa section
+        sections = sm_bytes + (n + 1) // 2 + 8 * (n_ch + 1) + 3 * E
+        out["encode"] += x_bytes + sections
+        out["decode"] += sections + x_bytes
+        out["encode_pack"] += x_bytes + sm_bytes + (n + 1) // 2 + 8 * n_ch + 4 * E + 4 * tiles
         out["encode_sums"] += 4 * tiles + 8 * (-(-tiles // 2048))
         out["encode_place"] += 4 * tiles + 4 * E + 3 * E + 16 * n_ch + 8
     return out
@@ -97,12 +106,13 @@ def roofline(name, bytes_, ms, workload):
             "avg_launch_ms": round(ms, 4)}
 
 
-def cpu_baseline(segments, codebooks, chunk_size: int, sample_words: int):
+def cpu_baseline(segments, codebooks, chunk_size: int, sample_words: int, e5m2: bool = False):
     """The plain single-threaded oracle timed on a bounded prefix of the same workload
-    (the first segments, each with its own codebook, up to sample_words words)."""
+    (the first segments, each with its own codebook, up to sample_words elements)."""
     import numpy as np
     import oracle
     o = oracle.get()
+    encode, decode = (o.encode8, o.decode8) if e5m2 else (o.encode, o.decode)
     t_enc = t_dec = 0.0
     words = 0
     for x, cb in zip(segments, codebooks):
@@ -110,17 +120,18 @@ def cpu_baseline(segments, codebooks, chunk_size: int, sample_words: int):
         if x.size == 0:
             break
         t0 = time.perf_counter()
-        enc = o.encode(x, np.frombuffer(cb, np.uint8), chunk_size)
+        enc = encode(x, np.frombuffer(cb, np.uint8), chunk_size)
         t1 = time.perf_counter()
-        y = o.decode(enc)
+        y = decode(enc)
         t2 = time.perf_counter()
         assert np.array_equal(y, x)
         t_enc += t1 - t0
         t_dec += t2 - t1
         words += x.size
-    gb = 2 * words / 1e9
+    gb = (1 if e5m2 else 2) * words / 1e9
+    kind = "E5M2 bytes" if e5m2 else "BF16 words"
     return {"value": round(gb / (t_enc + t_dec), 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {words} BF16 words of the timed workload, encode + decode, "
+            "sample": f"first {words} {kind} of the timed workload, encode + decode, "
                       f"single-threaded plain C",
             "encode_GBps": round(gb / t_enc, 4), "decode_GBps": round(gb / t_dec, 4)}
 
@@ -138,6 +149,8 @@ def main():
                          "and K/V, each tensor its own segment")
     ap.add_argument("--packed", action="store_true",
                     help="encode into / decode from one contiguous packed stream per segment")
+    ap.add_argument("--elem", choices=["bf16", "e5m2"], default="bf16",
+                    help="element type: BF16 words, or the long-prefill KV cast to FP8 E5M2")
     ap.add_argument("--cpu-sample-words", type=int, default=1 << 30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
@@ -166,17 +179,23 @@ def main():
         segments = workloads_kv_parts(wl.segments[0], args.layers, tokens)
         cal_parts = workloads_kv_parts(wl.calibration, args.layers, wl.calibration.size // (2 * args.layers * 1024))
         books = list(range(len(segments)))
-    xs = [torch.from_numpy(s.view(np.int16)).to(dev) for s in segments]
-    cals = [torch.from_numpy(c.view(np.int16)).to(dev) for c in cal_parts]
-    codec = sz.Codec(dev, C)
+    e5m2 = args.elem == "e5m2"
+    esize = 1 if e5m2 else 2                      # bytes per input element
+    view = (lambda a: a) if e5m2 else (lambda a: a.view(np.int16))
+    xs = [torch.from_numpy(view(s)).to(dev) for s in segments]
+    cals = [torch.from_numpy(view(c)).to(dev) for c in cal_parts]
+    codec = sz.Codec(dev, C, elem=args.elem)
     if books is None:
         coverage = codec.calibrate(cals[0])
     else:
         coverage = min(codec.calibrate_books(cals))
     del cals
     # exponent statistics of the input itself (one pass on the GPU)
-    hist_in = np.sum(np.array(sz.histograms(xs), dtype=np.uint64), axis=0).tolist()
+    hist_in = np.sum(np.array(sz.histograms(xs, elem=args.elem), dtype=np.uint64), axis=0).tolist()
     stats_in = sz.exponent_stats(hist_in)
+    # no coder that keeps the sign+mantissa bits exact beats (element bits) / (kept bits + H)
+    kept_bits = 3 if e5m2 else 8
+    entropy_bound = 8 * esize / (kept_bits + stats_in["entropy_bits"])
 
     # sizes the escape arrays or stream buffers (retry if needed)
     if args.packed:
@@ -234,9 +253,9 @@ def main():
     n = sum(ns)
     E = sum(Es)
     comp = sum(e.compressed_bytes for e in encs)
-    alg = algorithmic_bytes(ns, Es, C)
+    alg = algorithmic_bytes(ns, Es, C, e5m2)
     wall_s = t1 - t0
-    value = 2 * n * args.steps / wall_s / 1e9
+    value = esize * n * args.steps / wall_s / 1e9
     wname = wl.name + f"_c{C}" + ("_books_layer_kv" if books is not None else "") + \
         ("_packed" if args.packed else "")
 
@@ -270,10 +289,13 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(segments, [codec.books[e.book] for e in encs], C, args.cpu_sample_words)
+        cpu = cpu_baseline(segments, [codec.books[e.book] for e in encs], C, args.cpu_sample_words, e5m2)
 
+    metric = "encode & decode GB/s (BF16 in) + % HBM roofline + compression ratio, 8.6 GB KV"
+    if e5m2:
+        metric = "encode & decode GB/s (E5M2 in) + % HBM roofline + compression ratio, 4.3 GB E5M2 KV"
     out = {
-        "metric": "encode & decode GB/s (BF16 in) + % HBM roofline + compression ratio, 8.6 GB KV",
+        "metric": metric,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -283,26 +305,26 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u16",
+        "dtype": "u8" if e5m2 else "u16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "n_words": n, "segments": len(ns), "chunk_size": C,
-                   "codebooks": len(codec.books), "packed_streams": bool(args.packed),
-                   "bytes_bf16": 2 * n, "description": wl.description},
-        "encode_GBps": round(2 * n / (enc_avg * 1e-3) / 1e9, 2),
-        "decode_GBps": round(2 * n / (dec_avg * 1e-3) / 1e9, 2),
+        "config": {"workload": wl.name, "element": args.elem, "n_elements": n, "segments": len(ns),
+                   "chunk_size": C, "codebooks": len(codec.books), "packed_streams": bool(args.packed),
+                   "input_bytes": esize * n, "description": wl.description},
+        "encode_GBps": round(esize * n / (enc_avg * 1e-3) / 1e9, 2),
+        "decode_GBps": round(esize * n / (dec_avg * 1e-3) / 1e9, 2),
         "encode_hbm_frac": ops["encode"]["frac"],
         "decode_hbm_frac": ops["decode"]["frac"],
         "encode_ms": {"avg": round(enc_avg, 4), "min": round(enc_ms[0], 4),
                       "median": round(enc_ms[len(enc_ms) // 2], 4)},
         "decode_ms": {"avg": round(dec_avg, 4), "min": round(dec_ms[0], 4),
                       "median": round(dec_ms[len(dec_ms) // 2], 4)},
-        "compression_ratio": round(2 * n / comp, 5),
+        "compression_ratio": round(esize * n / comp, 5),
         "compressed_bytes": comp,
         "n_escapes": E,
         "coverage_calibration": coverage,
         "coverage_input": 1 - E / n if n else None,
         "exponent_entropy_bits": round(stats_in["entropy_bits"], 5),
-        "entropy_bound_ratio": round(16 / (8 + stats_in["entropy_bits"]), 5),
+        "entropy_bound_ratio": round(entropy_bound, 5),
         "roofline": kernels[dominant],
         "roofline_ops": ops,
         "roofline_kernels": kernels,

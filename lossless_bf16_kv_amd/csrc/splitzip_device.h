@@ -220,7 +220,7 @@ __device__ __forceinline__ void tile_escape_ranks(const uint32_t (&counts)[G], u
         rank[j] += wave_base;
 }
 
-// Where tile t's escapes go: its slot of kSlotEscapes entries, or, past that, a range of
+// Where tile t's escapes go: its slot of a.slot_escapes entries, or, past that, a range of
 // the overflow area reserved with one 64-bit atomic that also appends the tile to the
 // overflow list.  room: entries that may be written there.  Also stores the tile's escape
 // count.  Call from uniform control flow (contains a barrier when the tile overflows).
@@ -228,9 +228,9 @@ __device__ __forceinline__ uint32_t *tile_escape_dest(const EncodeArgs &a, uint3
                                                       uint32_t tile_total, uint32_t tid,
                                                       uint64_t *s_ovf, uint64_t &room)
 {
-    uint32_t *dst = a.slots + (uint64_t)t * kSlotEscapes;
-    room = kSlotEscapes;
-    if (tile_total > kSlotEscapes) {
+    uint32_t *dst = a.slots + (uint64_t)t * a.slot_escapes;
+    room = a.slot_escapes;
+    if (tile_total > a.slot_escapes) {
         if (tid == 0) {
             const uint64_t old = atomicAdd(a.ovf_ctr, (unsigned long long)tile_total + (1ull << kOvfTileShift));
             const uint64_t off = old & kOvfOffsetMask;

@@ -10,10 +10,13 @@
 // go to the same chunk-local escape stream as for BF16.  Codes, chunk offsets and escapes
 // have the BF16 layout, so the escape placement launches (sums, place, spill) are shared.
 //
-// Per lane, groups of 32 consecutive bytes (two 16-byte loads): their 32 fields fill 12
-// bytes (one 12-byte store) and their codes 16 bytes (one 16-byte store), so each store
-// instruction of a wave covers one contiguous range.  All work is integer byte manipulation:
-// no floating point touches a value and no MFMA is used.
+// Per lane, groups of 32 consecutive elements: their 32 fields fill 12 bytes (one 12-byte
+// store) and their codes 16 bytes (one 16-byte store), so each store instruction of a wave
+// covers one contiguous range.  The 32 input bytes of a lane (pack) and its 32 output bytes
+// (decode) would take two 16-byte accesses 32 bytes apart, which leave every cache line half
+// covered per instruction; they go through LDS instead, so that each global access
+// instruction of a wave covers 1 KiB contiguously.  All work is integer byte manipulation: no
+// floating point touches a value and no MFMA is used.
 #include "splitzip_device.h"
 
 namespace sz {
@@ -21,14 +24,6 @@ namespace sz {
 constexpr uint32_t kErrBadExponent = 32u;    // decode: escape exponent above 31
 
 // ---- pack -----------------------------------------------------------------------------------
-
-// The 3-bit fields of the 4 bytes of x packed into 12 bits (byte k's field at bits 3k..3k+2).
-__device__ __forceinline__ uint32_t pack_fields4(uint32_t x)
-{
-    const uint32_t f = ((x >> 5) & 0x04040404u) | (x & 0x03030303u);   // sign to bit 2
-    const uint32_t y = f | (f >> 5);               // byte k: field k, then field k + 1
-    return (y & 0x3Fu) | ((y >> 10) & 0xFC0u);    // fields 0,1 of byte 0 and 2,3 of byte 2
-}
 
 // Escape flag bits of the 8 elements of dword-group d (elements 8d..8d+7) inside a group's
 // flag word; within one mask, ascending bits are ascending elements.
@@ -45,44 +40,46 @@ __device__ __forceinline__ uint32_t e8_flag_element(uint32_t b)
     return 8u * d + 2u * (b >> 3) + (b & 1u);
 }
 
-// Split one group of 32 bytes (byte k of dword m is element 4m + k).
+// Split one group of 32 bytes (byte k of dword m is element 4m + k) with the byte LUT
+// (lut[b]: code in bits 0..3, escape flag in bit 4, field (sign << 2) | mantissa in 5..7).
 //   sm:    the 32 fields as 96 bits, element k at bits 3k..3k+2
 //   codes: nibble 2i + r of codes[d] = code of element 8d + 2i + r (0 for escapes)
 //   flags: escape flags, bit b for element e8_flag_element(b)
 __device__ __forceinline__ void split_group32(const uint32_t (&x)[8], const uint8_t *lut,
                                               uint32_t (&sm)[3], uint32_t (&codes)[4], uint32_t &flags)
 {
-    uint32_t z[8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m)
-        z[m] = pack_fields4(x[m]);
-    sm[0] = z[0] | (z[1] << 12) | (z[2] << 24);
-    sm[1] = (z[2] >> 8) | (z[3] << 4) | (z[4] << 16) | (z[5] << 28);
-    sm[2] = (z[5] >> 4) | (z[6] << 8) | (z[7] << 20);
-
-    uint32_t fl = 0;
+    uint32_t fl = 0, y[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
         const uint32_t lo = x[2 * d], hi = x[2 * d + 1];
-        const uint32_t c0 = lut[(lo >> 2) & 0x1Fu], c1 = lut[(lo >> 10) & 0x1Fu];
-        const uint32_t c2 = lut[(lo >> 18) & 0x1Fu], c3 = lut[(lo >> 26) & 0x1Fu];
-        const uint32_t c4 = lut[(hi >> 2) & 0x1Fu], c5 = lut[(hi >> 10) & 0x1Fu];
-        const uint32_t c6 = lut[(hi >> 18) & 0x1Fu], c7 = lut[(hi >> 26) & 0x1Fu];
-        const uint32_t even = c0 | (c2 << 8) | (c4 << 16) | (c6 << 24);
-        const uint32_t odd = c1 | (c3 << 8) | (c5 << 16) | (c7 << 24);
+        const uint32_t c0 = lut[lo & 0xFFu], c1 = lut[(lo >> 8) & 0xFFu];
+        const uint32_t c2 = lut[(lo >> 16) & 0xFFu], c3 = lut[lo >> 24];
+        const uint32_t c4 = lut[hi & 0xFFu], c5 = lut[(hi >> 8) & 0xFFu];
+        const uint32_t c6 = lut[(hi >> 16) & 0xFFu], c7 = lut[hi >> 24];
+        const uint32_t even = c0 | (c2 << 8) | (c4 << 16) | (c6 << 24);   // elements 8d + 2i
+        const uint32_t odd = c1 | (c3 << 8) | (c5 << 16) | (c7 << 24);    // elements 8d + 2i + 1
         codes[d] = (even & 0x0F0F0F0Fu) | ((odd & 0x0F0F0F0Fu) << 4);
         const uint32_t f = (even & 0x10101010u) | ((odd & 0x10101010u) << 1);   // bits 8i+4+r
         fl |= d == 0 ? f : d == 1 ? (f << 2) : d == 2 ? (f >> 4) : (f >> 2);
+        // byte i of g: the 6 field bits of elements 8d + 2i and 8d + 2i + 1; then 4 x 6 bits
+        // become 24 contiguous bits
+        const uint32_t g = ((even >> 5) & 0x07070707u) | ((odd >> 2) & 0x38383838u);
+        const uint32_t g2 = (g & 0x003F003Fu) | ((g >> 2) & 0x0FC00FC0u);
+        y[d] = (g2 & 0xFFFu) | ((g2 >> 4) & 0xFFF000u);
     }
+    sm[0] = y[0] | (y[1] << 24);
+    sm[1] = (y[1] >> 8) | (y[2] << 16);
+    sm[2] = (y[2] >> 16) | (y[3] << 8);
     flags = fl;
 }
 
 __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const EncodeArgs a)
 {
     constexpr int G = kE8EncGroups;
-    __shared__ uint8_t s_lut[32];
+    __shared__ uint8_t s_lut[256];
     __shared__ uint32_t s_wave_total[kWaves];
     __shared__ uint64_t s_ovf;
+    __shared__ uint4 s_in[kWaves][128];        // one 2048-byte group per wave, regrouped
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = lane_id();
@@ -92,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
     const uint32_t s = a.n_seg > 1 ? find_segment_block(a.tile_start, a.n_seg, t, tid, lane, s_wave_total) : 0u;
     const SegDesc sd = segment_desc(a, s);
     const uint8_t *lut = a.multi_book ? a.lut + 256u * sd.book : a.lut;
-    if (tid < 8)
+    if (tid < 64)
         reinterpret_cast<uint32_t *>(s_lut)[tid] = reinterpret_cast<const uint32_t *>(lut)[tid];
     if (a.packed && tid == 0 && t == segment_first_tile(a, s))
         a.seg_total[s] = 0;      // the sums launch adds the segment's escapes into it
@@ -107,17 +104,22 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
     const uint64_t code_bytes = (n + 1) >> 1;
 
     // element order inside the tile: wave w covers 64 * 32 * G consecutive elements, its group
-    // j covers 2048 of them, lane l the 32 at offset 32 l.
+    // j covers 2048 of them, lane l the 32 at offset 32 l.  A whole group is loaded 16 bytes
+    // per lane at offsets 16 l and 1024 + 16 l and regrouped through LDS; the segment's last,
+    // partial group is read byte by byte.
     uint64_t g0[G];
     uint32_t v[G][8];
+    uint4 ld[G][2];
+    bool whole[G];
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-        g0[j] = base + (uint64_t)(((wave * G + j) << 6) + lane) * kE8GroupElems;
-        if (g0[j] + kE8GroupElems <= n) {
-            const uint8_t *src = reinterpret_cast<const uint8_t *>(sd.data) + g0[j];
-            const uint4 lo = load_stream16(src), hi = load_stream16(src + 16);
-            v[j][0] = lo.x; v[j][1] = lo.y; v[j][2] = lo.z; v[j][3] = lo.w;
-            v[j][4] = hi.x; v[j][5] = hi.y; v[j][6] = hi.z; v[j][7] = hi.w;
+        const uint64_t gbase = base + ((uint64_t)(wave * G + j) << 11);
+        g0[j] = gbase + (uint64_t)lane * kE8GroupElems;
+        whole[j] = gbase + 2048 <= n;                  // uniform in the wave
+        if (whole[j]) {
+            const uint8_t *src = reinterpret_cast<const uint8_t *>(sd.data) + gbase;
+            ld[j][0] = load_stream16(src + 16 * lane);
+            ld[j][1] = load_stream16(src + 1024 + 16 * lane);
         } else {
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
@@ -130,6 +132,20 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
         }
     }
     __syncthreads();   // LUT in LDS
+    // Regroup, one group at a time through the wave's own buffer.  A wave's LDS accesses are
+    // performed in the order it issues them, so the wavefront-scope fences (which keep the
+    // compiler from reordering them) are all the ordering these exchanges need.
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+        if (whole[j]) {
+            s_in[wave][lane] = ld[j][0];
+            s_in[wave][64 + lane] = ld[j][1];
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            const uint4 lo = s_in[wave][2 * lane], hi = s_in[wave][2 * lane + 1];
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            v[j][0] = lo.x; v[j][1] = lo.y; v[j][2] = lo.z; v[j][3] = lo.w;
+            v[j][4] = hi.x; v[j][5] = hi.y; v[j][6] = hi.z; v[j][7] = hi.w;
+        }
 
     // ---- a2: dense split and pack ---------------------------------------------------------
     uint32_t flags[G], counts[G];
@@ -210,16 +226,11 @@ hipError_t launch_encode_pack_e5m2(const EncodeArgs &a, hipStream_t stream)
 
 // ---- decode ---------------------------------------------------------------------------------
 
-// Codebook lookup of 4 codes (one per byte, each 0..15): two byte-permutes over the low and
-// high halves of the 16-byte codebook, merged on bit 3 of each code.
-__device__ __forceinline__ uint32_t e8_codebook_lookup(uint32_t x, const uint32_t cb[4])
+// Entry k (0..15) of a codebook held as 4 little-endian dwords.
+__device__ __forceinline__ uint32_t codebook_byte(const uint32_t cb[4], uint32_t k)
 {
-    const uint32_t sel = x & 0x07070707u;
-    const uint32_t lo = __builtin_amdgcn_perm(cb[1], cb[0], sel);
-    const uint32_t hi = __builtin_amdgcn_perm(cb[3], cb[2], sel);
-    const uint32_t b3 = (x >> 3) & 0x01010101u;
-    const uint32_t m = (b3 << 8) - b3;   // 0xFF in every byte whose code has bit 3 set
-    return (hi & m) | (lo & ~m);
+    const bool upper = (k & 8u) != 0;
+    return __builtin_amdgcn_perm(upper ? cb[3] : cb[1], upper ? cb[2] : cb[0], k & 7u) & 0xFFu;
 }
 
 // 12 bits of 4 fields (field k at bits 3k..3k+2) spread to one field per byte.
@@ -241,6 +252,7 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
     constexpr uint32_t kTile = 1u << kE8DecTileShift;
     __shared__ uint32_t s_exp[kTile / 4];              // exponent bytes of the tile
     __shared__ uint64_t s_off[kTile / 16 + 1];         // chunk offsets of the tile
+    __shared__ uint16_t s_pair[256];                   // codes byte -> its two exponent bytes
     __shared__ uint32_t s_cnt[kWaves];
 
     const uint32_t tid = threadIdx.x;
@@ -316,6 +328,20 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
         }
     }
 
+    // The codebook as a table over codes bytes: entry c holds the exponents (moved to bits 6..2
+    // of an output byte) of the codes c & 15 (low byte) and c >> 4 (high byte).  A packed
+    // stream brings its own codebook (its header is checked below, before any store).
+    if (sd.header) {
+        cb[0] = h2.z;
+        cb[1] = h2.w;
+        cb[2] = h3.x;
+        cb[3] = h3.y;
+    }
+    for (uint32_t c = tid; c < 256; c += kThreads) {
+        const uint32_t e_lo = codebook_byte(cb, c & 15u) & 0x1Fu, e_hi = codebook_byte(cb, c >> 4) & 0x1Fu;
+        s_pair[c] = (uint16_t)((e_lo | (e_hi << 8)) << 2);
+    }
+
     // ---- escape range of the tile --------------------------------------------------------
     const bool sub_chunk = log2c > (uint32_t)kE8DecTileShift;   // the tile lies inside one chunk
     const uint64_t c0 = base >> log2c;
@@ -345,38 +371,27 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
                 atomicOr(a.err, kErrBadHeader);
             return;
         }
-        cb[0] = h2.z;
-        cb[1] = h2.w;
-        cb[2] = h3.x;
-        cb[3] = h3.y;
     }
-    // exponents move to bits 6..2 of the output byte (entries are below 32: no carry)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        cb[i] <<= 2;
 
-    // ---- a5: dense path ------------------------------------------------------------------
-    uint32_t ex_even[G][4], ex_odd[G][4];
+    // ---- a5: dense path: exponent bytes of 4 elements per dword, in element order ----------
+    uint32_t ex[G][8];
 #pragma unroll
     for (int j = 0; j < G; ++j)
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-            ex_even[j][d] = e8_codebook_lookup(cw[j][d] & 0x0F0F0F0Fu, cb);
-            ex_odd[j][d] = e8_codebook_lookup((cw[j][d] >> 4) & 0x0F0F0F0Fu, cb);
+            const uint32_t c = cw[j][d];
+            ex[j][2 * d] = s_pair[c & 0xFFu] | ((uint32_t)s_pair[(c >> 8) & 0xFFu] << 16);
+            ex[j][2 * d + 1] = s_pair[(c >> 16) & 0xFFu] | ((uint32_t)s_pair[c >> 24] << 16);
         }
 
-    // ---- a6: sparse escape correction (exponent bytes in LDS) ----------------------------
-    // Element p of the tile has its exponent byte at (p >> 3) * 8 + (p & 1) * 4 + ((p >> 1) & 3):
-    // per 8 elements, the even ones' dword, then the odd ones'.
+    // ---- a6: sparse escape correction (exponent bytes in LDS, element p at byte p) -------
     if (patch) {
 #pragma unroll
         for (int j = 0; j < G; ++j) {
             const uint32_t q = ((wave * G + j) << 6) + lane;
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                s_exp[2 * (4 * q + d)] = ex_even[j][d];
-                s_exp[2 * (4 * q + d) + 1] = ex_odd[j][d];
-            }
+            for (int m = 0; m < 8; ++m)
+                s_exp[8 * q + m] = ex[j][m];
         }
         __syncthreads();
         uint8_t *bytes = reinterpret_cast<uint8_t *>(s_exp);
@@ -402,8 +417,7 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
                         atomicOr(a.err, pos >= clen ? kErrBadPosition : kErrBadExponent);
                     continue;
                 }
-                const uint32_t p = (uint32_t)(cstart + pos - base);
-                bytes[(p >> 3) * 8 + (p & 1u) * 4 + ((p >> 1) & 3u)] = (uint8_t)(e << 2);
+                bytes[cstart + pos - base] = (uint8_t)(e << 2);
             }
         } else {
             const uint64_t lo = base - (c0 << log2c);
@@ -416,10 +430,8 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
                         atomicOr(a.err, pos >= clen ? kErrBadPosition : kErrBadExponent);
                     continue;
                 }
-                if (pos >= lo && pos < lo + valid) {
-                    const uint32_t p = (uint32_t)(pos - lo);
-                    bytes[(p >> 3) * 8 + (p & 1u) * 4 + ((p >> 1) & 3u)] = (uint8_t)(e << 2);
-                }
+                if (pos >= lo && pos < lo + valid)
+                    bytes[pos - lo] = (uint8_t)(e << 2);
             }
         }
         __syncthreads();
@@ -427,14 +439,16 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
         for (int j = 0; j < G; ++j) {
             const uint32_t q = ((wave * G + j) << 6) + lane;
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                ex_even[j][d] = s_exp[2 * (4 * q + d)];
-                ex_odd[j][d] = s_exp[2 * (4 * q + d) + 1];
-            }
+            for (int m = 0; m < 8; ++m)
+                ex[j][m] = s_exp[8 * q + m];
         }
     }
 
     // ---- assemble and store ------------------------------------------------------------------
+    // A whole 2048-element group of a wave is regrouped through the wave's own 2 KiB of s_exp
+    // (since the patch, only this wave reads it) and stored 16 bytes per lane at offsets 16 l
+    // and 1024 + 16 l; the segment's last, partial group is written byte by byte.  A wave's LDS
+    // accesses are performed in the order it issues them, so wavefront-scope fences suffice.
 #pragma unroll
     for (int j = 0; j < G; ++j) {
         const uint64_t g0 = base + (uint64_t)(((wave * G + j) << 6) + lane) * kE8GroupElems;
@@ -450,21 +464,23 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
             (s2 >> 8) & 0xFFFu,
             s2 >> 20,
         };
-        uint32_t o[8];
+        uint32_t out[8];
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            // elements 8d..8d+3 take even/odd bytes 0,1; elements 8d+4..8d+7 bytes 2,3
-            const uint32_t e_lo = __builtin_amdgcn_perm(ex_odd[j][d], ex_even[j][d], 0x05010400u);
-            const uint32_t e_hi = __builtin_amdgcn_perm(ex_odd[j][d], ex_even[j][d], 0x07030602u);
-            o[2 * d] = e8_assemble(e_lo, unpack_fields4(z[2 * d]));
-            o[2 * d + 1] = e8_assemble(e_hi, unpack_fields4(z[2 * d + 1]));
-        }
-        if (g0 + kE8GroupElems <= n) {
-            *as_global(reinterpret_cast<u32x4 *>(yb + g0)) = u32x4{o[0], o[1], o[2], o[3]};
-            *as_global(reinterpret_cast<u32x4 *>(yb + g0 + 16)) = u32x4{o[4], o[5], o[6], o[7]};
+        for (int m = 0; m < 8; ++m)
+            out[m] = e8_assemble(ex[j][m], unpack_fields4(z[m]));
+        const uint64_t gbase = base + ((uint64_t)(wave * G + j) << 11);
+        if (gbase + 2048 <= n) {                        // uniform in the wave
+            uint4 *grp = reinterpret_cast<uint4 *>(s_exp) + ((wave * G + j) << 7);
+            grp[2 * lane] = make_uint4(out[0], out[1], out[2], out[3]);
+            grp[2 * lane + 1] = make_uint4(out[4], out[5], out[6], out[7]);
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            const uint4 lo = grp[lane], hi = grp[64 + lane];
+            *as_global(reinterpret_cast<u32x4 *>(yb + gbase + 16 * lane)) = u32x4{lo.x, lo.y, lo.z, lo.w};
+            *as_global(reinterpret_cast<u32x4 *>(yb + gbase + 1024 + 16 * lane)) = u32x4{hi.x, hi.y, hi.z, hi.w};
         } else {
-            for (uint32_t k = 0; g0 + k < n; ++k)
-                yb[g0 + k] = (uint8_t)(o[k >> 2] >> (8 * (k & 3)));
+            // the lane's own 32 elements, those below n
+            for (uint32_t k = 0; k < kE8GroupElems && g0 + k < n; ++k)
+                yb[g0 + k] = (uint8_t)(out[k >> 2] >> (8 * (k & 3)));
         }
     }
 }

@@ -204,11 +204,21 @@ int make_codec(const uint8_t *cbs, uint32_t n_books, uint32_t chunk_size, uint32
     c->log2_chunk = log2u(chunk_size);
     c->n_books = n_books;
     c->cbs.assign(cbs, cbs + 16 * (size_t)n_books);
-    // inverse LUT of each book: exponent -> code, or the escape entry
+    // inverse LUT of each book.  BF16: exponent -> code, or the escape entry.  E5M2: element
+    // byte -> code or escape entry in bits 0..4, and the byte's 3-bit field (sign << 2) |
+    // mantissa in bits 5..7, so one lookup serves the codes, the flags and the field stream.
     std::vector<uint8_t> lut(256 * (size_t)n_books, sz::kEscapeEntry);
-    for (uint32_t b = 0; b < n_books; ++b)
+    for (uint32_t b = 0; b < n_books; ++b) {
+        uint8_t *l = &lut[256 * (size_t)b];
+        uint8_t inv[256];
+        std::memset(inv, sz::kEscapeEntry, sizeof inv);
         for (int k = 0; k < 16; ++k)
-            lut[256 * (size_t)b + cbs[16 * (size_t)b + k]] = (uint8_t)k;
+            inv[cbs[16 * (size_t)b + k]] = (uint8_t)k;
+        for (int v = 0; v < 256; ++v)
+            l[v] = elem == sz::kElemE5M2
+                       ? (uint8_t)(inv[(v >> 2) & 0x1F] | ((((v >> 7) << 2) | (v & 3)) << 5))
+                       : inv[v];
+    }
     SZ_HIP(hipMalloc(&c->d_lut, lut.size()), "hipMalloc(codec tables)");
     hipError_t e = hipMalloc(&c->d_cbs, c->cbs.size());
     if (e == hipSuccess)
@@ -396,7 +406,7 @@ struct CallTimer {
 struct EncodeScratch {
     uint64_t tile_count, tile_ovf, tile_prefix, ovf_tiles, slots, block_sum, group_sum, seg_total,
         ovf, total;
-    EncodeScratch(uint64_t n_tiles, uint64_t ovf_cap, uint64_t n_seg)
+    EncodeScratch(uint64_t n_tiles, uint64_t ovf_cap, uint64_t n_seg, uint64_t slot_escapes)
     {
         auto up = [](uint64_t x) { return (x + 255) & ~uint64_t(255); };
         tile_count = 0;
@@ -404,7 +414,7 @@ struct EncodeScratch {
         tile_prefix = up(tile_ovf + 8 * n_tiles);
         ovf_tiles = up(tile_prefix + 8 * n_tiles);
         slots = up(ovf_tiles + 4 * n_tiles);
-        block_sum = up(slots + 4 * (uint64_t)sz::kSlotEscapes * n_tiles);
+        block_sum = up(slots + 4 * slot_escapes * n_tiles);
         group_sum = up(block_sum + 8 * ((n_tiles + sz::kSumTiles - 1) / sz::kSumTiles));
         seg_total = up(group_sum + 8 * ((n_tiles + sz::kPlaceTiles - 1) / sz::kPlaceTiles));
         ovf = up(seg_total + 8 * n_seg);
@@ -890,7 +900,8 @@ int encode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
     uint64_t ovf_cap = 1;
     for (uint32_t i = 0; i < n_seg; ++i)
         ovf_cap += desc[i].esc;
-    const EncodeScratch lay(n_tiles, ovf_cap, n_seg);
+    const uint32_t slot_escapes = codec->elem == sz::kElemE5M2 ? sz::kE8SlotEscapes : sz::kSlotEscapes;
+    const EncodeScratch lay(n_tiles, ovf_cap, n_seg, slot_escapes);
     if ((rc = ensure_scratch(w, lay.total)) != SPLITZIP_OK)
         return rc;
     if (!d_result && (rc = ensure_result(w, n_seg)) != SPLITZIP_OK)
@@ -924,6 +935,7 @@ int encode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
     a.log2_chunk = codec->log2_chunk;
     a.elem = codec->elem;
     a.tile_shift = codec->elem == sz::kElemE5M2 ? sz::kE8EncTileShift : sz::kEncTileShift;
+    a.slot_escapes = slot_escapes;
     hipError_t e = hipSuccess;
     {
         CallTimer timer(codec, w, stream, SPLITZIP_KERNEL_PACK, sz::kEncodeStages);

@@ -46,10 +46,13 @@ static_assert(kThreads * kE8DecGroups * kE8GroupElems == (1 << kE8DecTileShift),
 constexpr uint8_t kEscapeEntry = 0x10;
 
 // ---- encode scratch --------------------------------------------------------------------
-// Each tile's escapes are first written compacted to a slot of kSlotEscapes entries (or, if
-// more, to an overflow area) as (position inside the tile | exponent << 16), then moved to
-// their final place once the tile's escape offset is known.
-constexpr uint32_t kSlotEscapes = 64;
+// Each tile's escapes are first written compacted to a slot (or, if more, to an overflow
+// area) as (position inside the tile | exponent << 16), then moved to their final place once
+// the tile's escape offset is known.  A slot holds 1/128 of the tile's elements: enough for
+// nearly every tile of KV-like inputs (about 0.3 % escapes, unevenly spread), so that few
+// tiles go to the overflow area and its spill launch.
+constexpr uint32_t kSlotEscapes = 128;                        // BF16 tiles
+constexpr uint32_t kE8SlotEscapes = 256;                      // E5M2 tiles (twice as long)
 constexpr uint32_t kSumTiles = 2048;          // tiles per segmented-sum block
 constexpr uint32_t kPlaceTiles = 64;          // tiles per placement workgroup
 constexpr uint32_t kSpillBlocks = 1024;       // workgroups moving the overflow tiles' escapes
@@ -58,6 +61,7 @@ constexpr int kOvfTileShift = 40;
 constexpr uint64_t kOvfOffsetMask = (1ull << kOvfTileShift) - 1;
 constexpr uint64_t kMaxSegmentWords = 1ull << 38;
 static_assert(kEncTileWords <= 65536 && (1 << kE8EncTileShift) <= 65536, "in-tile positions must fit 16 bits");
+static_assert(kSlotEscapes * 128 == kEncTileWords && kE8SlotEscapes * 128 == (1 << kE8EncTileShift), "slots");
 static_assert(kSumTiles % kThreads == 0 && kSumTiles % kPlaceTiles == 0, "sum blocks");
 static_assert(kSumTiles / kPlaceTiles <= kThreads, "group sums of a block fit one pass");
 static_assert(kPlaceTiles % (kSumTiles / kThreads) == 0 && kPlaceTiles <= kThreads, "groups");
@@ -91,12 +95,14 @@ struct EncodeArgs {
     const SegDesc *segs;          // device table when n_seg > 1
     const uint32_t *tile_start;   // device [n_seg + 1] first tile of each segment
     const uint8_t *lut;           // device inverse LUT (code, or kEscapeEntry): [256], or
-                                  // [256 * books] indexed by SegDesc::book when multi_book
+                                  // [256 * books] indexed by SegDesc::book when multi_book.
+                                  // BF16: by exponent.  E5M2: by element byte, with the
+                                  // byte's 3-bit field in bits 5..7
     uint32_t *tile_count;         // [n_tiles] escapes per tile
-    uint64_t *tile_ovf;           // [n_tiles] overflow offset of tiles past kSlotEscapes
+    uint64_t *tile_ovf;           // [n_tiles] overflow offset of tiles past slot_escapes
     uint64_t *tile_prefix;        // [n_tiles] escape offset in the segment (overflow tiles)
     uint32_t *ovf_tiles;          // [n_tiles] list of the overflow tiles
-    uint32_t *slots;              // [n_tiles * kSlotEscapes]
+    uint32_t *slots;              // [n_tiles * slot_escapes]
     uint32_t *ovf;                // [ovf_cap]
     unsigned long long *ovf_ctr;  // [2]: running overflow counter (0 between encodes), and
                                   // its final value saved by the sums launch
@@ -114,7 +120,7 @@ struct EncodeArgs {
     uint32_t packed;              // segments are packed streams (SegDesc::header)
     uint32_t elem;                // kElemBF16 or kElemE5M2
     uint32_t tile_shift;          // log2 of the elements per pack tile
-    uint32_t pad;
+    uint32_t slot_escapes;        // entries per tile slot
 };
 
 struct DecodeArgs {

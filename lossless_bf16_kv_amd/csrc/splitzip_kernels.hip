@@ -146,7 +146,7 @@ hipError_t launch_histogram(const HistArgs &a, hipStream_t stream)
 //   pack   (one workgroup per tile: kEncTileWords BF16 words, or 2^kE8EncTileShift E5M2
 //          bytes in splitzip_e5m2.hip): sign+mantissa bits and codes,
 //          escape ranks inside the tile, escapes written compacted to the tile's scratch slot
-//          (or, past kSlotEscapes, to an overflow area reserved with one atomic), tile-local
+//          (or, past its size, to an overflow area reserved with one atomic), tile-local
 //          chunk offsets into chunk_off, the tile's escape count;
 //   sums   (one workgroup per kSumTiles tiles): segmented sums of the tile counts;
 //   place  (one workgroup per kPlaceTiles tiles): each tile's escape offset from those sums,
@@ -577,7 +577,7 @@ __global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs
         }
     }
     // overflow tiles are moved by the spill launch; the others here, from their slots
-    const bool spilled = count > kSlotEscapes;
+    const bool spilled = count > a.slot_escapes;
     if (spilled)
         a.tile_prefix[u] = prefix;
     if (tid < kPlaceTiles) {
@@ -638,7 +638,7 @@ __global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs
             if (j < total) {
                 const uint32_t i = range_of(s_first, kPlaceTiles, j);
                 tile_of[k] = i;
-                ent[k] = a.slots[(uint64_t)(u_first + i) * kSlotEscapes + (j - s_first[i])];
+                ent[k] = a.slots[(uint64_t)(u_first + i) * a.slot_escapes + (j - s_first[i])];
             }
         }
 #pragma unroll
