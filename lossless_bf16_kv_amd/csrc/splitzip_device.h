@@ -105,6 +105,13 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
     return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
+// Entry k (0..15) of a codebook held as 4 little-endian dwords.
+__device__ __forceinline__ uint32_t codebook_byte(const uint32_t cb[4], uint32_t k)
+{
+    const bool upper = (k & 8u) != 0;
+    return __builtin_amdgcn_perm(upper ? cb[3] : cb[1], upper ? cb[2] : cb[0], k & 7u) & 0xFFu;
+}
+
 // Workgroups are started round robin over the 8 XCDs (workgroup b on XCD b mod 8).  Giving
 // each XCD a contiguous range of tiles instead of every 8th one streams measurably better
 // (about 3 % in a copy probe).  The mapping is a bijection on [0, n_tiles) whatever the

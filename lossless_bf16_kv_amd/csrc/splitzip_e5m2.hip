@@ -226,13 +226,6 @@ hipError_t launch_encode_pack_e5m2(const EncodeArgs &a, hipStream_t stream)
 
 // ---- decode ---------------------------------------------------------------------------------
 
-// Entry k (0..15) of a codebook held as 4 little-endian dwords.
-__device__ __forceinline__ uint32_t codebook_byte(const uint32_t cb[4], uint32_t k)
-{
-    const bool upper = (k & 8u) != 0;
-    return __builtin_amdgcn_perm(upper ? cb[3] : cb[1], upper ? cb[2] : cb[0], k & 7u) & 0xFFu;
-}
-
 // 12 bits of 4 fields (field k at bits 3k..3k+2) spread to one field per byte.
 __device__ __forceinline__ uint32_t unpack_fields4(uint32_t z)
 {
