@@ -291,3 +291,78 @@ def test_long_prefill_e5m2_full_size(kv8):
         assert np.array_equal(host(enc.esc_exp_buf[a:b], np.uint8), ref["esc_exp"])
     y = codec.decode(enc)
     assert torch.equal(y.view(torch.uint8), xd)
+
+
+# ---- the escape-stress input and the ragged batch, cast to E5M2 --------------------------------
+
+def test_escape_stress_e5m2():
+    """Config 4 (N(0,1) x 2^k per 4096-element block, 1 % specials) cast to E5M2: a large share
+    of escapes, every tile over its slot; the whole stream against the oracle."""
+    wl = workloads.cast_e5m2(workloads.config4())
+    x = wl.segments[0]
+    codec = codec_for(wl.calibration, 1024)
+    enc = codec.encode(dev8(x))
+    ref = assert_same_stream(codec, enc, x)
+    assert ref["n_escapes"] > 0.05 * x.size
+    assert np.array_equal(host(codec.decode(enc), np.uint8), x)
+
+
+def test_ragged_batch_e5m2():
+    """Config 5 (512 K/V segments of 256 requests, one launch) cast to E5M2: full streams of a
+    spread of segments against the oracle, E and offsets of every segment from the oracle's
+    histograms, and round trips."""
+    wl = workloads.cast_e5m2(workloads.config5())
+    assert len(wl.segments) == 512
+    codec = codec_for(wl.calibration, 1024)
+    cb = np.frombuffer(codec.codebook, np.uint8)
+    xds = [dev8(s) for s in wl.segments]
+    encs = codec.encode_batch(xds)
+    for i in range(0, 512, 37):
+        assert_same_stream(codec, encs[i], wl.segments[i])
+    for x, e in zip(wl.segments, encs):
+        h = O.histogram8(x)
+        E = int(x.size - sum(int(h[v]) for v in cb))
+        assert e.n_escapes == E and e.compressed_bytes == O.compressed_bytes8(x.size, 1024, E)
+        off = e.chunk_off
+        assert int(off[0]) == 0 and int(off[-1]) == E and bool((off[1:] >= off[:-1]).all())
+    for xd, y in zip(xds, codec.decode_batch(encs)):
+        assert torch.equal(y, xd)
+
+
+def test_async_and_prepared_e5m2():
+    """Non-blocking encode and prepared batches (sections and packed streams) on E5M2."""
+    xs_np = [workloads.e5m2_mixed(n, 400 + n, wide_fraction=0.05) for n in (3 * 32768 + 11, 70000, 0, 5)]
+    codec = codec_for(workloads.e5m2_normal(30000, 15), 1024)
+    xs = [dev8(x) for x in xs_np]
+    ref = codec.encode_batch(xs)
+    encs = [codec.empty_encoded(e.n, escape_capacity=max(e.n_escapes, 1)) for e in ref]
+    result = torch.zeros(1 + len(xs), dtype=torch.int64, device=DEV)
+    codec.encode_into_async(xs, encs, result)
+    torch.cuda.synchronize()
+    assert codec.finish_async(encs, result) == sz.OK
+    for x, e in zip(xs_np, encs):
+        assert_same_stream(codec, e, x)
+    ys = [torch.empty_like(x) for x in xs]
+    batch = codec.prepare(xs, encs, ys)
+    for _ in range(3):
+        batch.encode_async(result)
+        batch.decode()
+    torch.cuda.synchronize()
+    assert batch.finish(result) == sz.OK
+    for x, y in zip(xs_np, ys):
+        assert np.array_equal(host(y, np.uint8), x)
+    # packed streams (sizes a multiple of 128)
+    xs8 = [dev8(workloads.e5m2_mixed(n, 500 + n)) for n in (128 * 513, 32768 * 2)]
+    packed = codec.encode_packed_batch(xs8)
+    outs = [torch.empty_like(x) for x in xs8]
+    pb = codec.prepare_packed(xs8, packed, outs)
+    res = torch.zeros(1 + len(xs8), dtype=torch.int64, device=DEV)
+    for _ in range(2):
+        pb.encode_async(res)
+        pb.decode()
+    torch.cuda.synchronize()
+    assert pb.finish(res) == sz.OK
+    for x, y, p in zip(xs8, outs, packed):
+        assert torch.equal(x, y)
+        ref = O.encode8(x.cpu().numpy(), np.frombuffer(codec.codebook, np.uint8), 1024)
+        assert p.to_bytes() == O.serialize8(ref)

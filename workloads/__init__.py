@@ -288,6 +288,19 @@ def config3_e5m2(layers: int = 64, tokens: int = 32768, cal_tokens: int = 2048,
                     f"{chunk_size}")
 
 
+def cast_e5m2(wl: Workload, chunk_size: int | None = None) -> Workload:
+    """A workload's BF16 segments and calibration draw cast to E5M2 (segment by segment), e.g.
+    the escape-stress input or the ragged batch as an FP8 E5M2 KV cache."""
+    def cast(words: np.ndarray) -> np.ndarray:
+        out = np.empty(words.size, np.uint8)
+        step = 1 << 24
+        for i in range(0, words.size, step):
+            out[i:i + step] = e5m2_bits(bf16_to_f32(words[i:i + step]))
+        return out
+    return Workload(wl.name + "_e5m2", [cast(x) for x in wl.segments], cast(wl.calibration),
+                    chunk_size or wl.chunk_size, wl.description + "; cast to FP8 E5M2")
+
+
 def e5m2_special_bytes(rng: np.random.Generator, count: int) -> np.ndarray:
     """Uniformly one of {0, subnormal, Inf, NaN}, random sign; subnormal mantissas 1..3,
     NaN mantissas 1..3 (raw bit patterns)."""
