@@ -224,3 +224,49 @@ def test_no_cpu_fallback():
         pytest.skip("GPU present")
     with pytest.raises(sz.SplitZipError):
         sz.Codec("cuda", 1024)
+
+
+C_CONSUMER = r"""
+#include <splitzip.h>
+#include <stdio.h>
+#include <string.h>
+
+int main(void)
+{
+    /* host helpers only: sizes, a header round trip through the parser, status strings */
+    if (splitzip_compressed_bytes(20, 16, 11) != 151) return 1;
+    if (splitzip_e5m2_compressed_bytes(20, 16, 9) != 64 + 8 + 10 + 24 + 27) return 2;
+    if (splitzip_chunk_count(1u << 20, 1024) != 1024) return 3;
+    uint8_t h[SPLITZIP_HEADER_BYTES + 8 + 4 + 8 * 2] = {0};
+    memcpy(h, "SZB1", 4);
+    h[4] = 1; h[6] = SPLITZIP_HEADER_BYTES; h[8] = 16; h[12] = SPLITZIP_ELEM_BF16;
+    h[16] = 8; h[24] = 1;
+    for (int k = 0; k < 16; ++k) h[40 + k] = (uint8_t)(100 + k);
+    uint64_t n = 0, e = 1;
+    uint32_t c = 0, elem = 7;
+    uint8_t cb[16];
+    if (splitzip_read_header(h, sizeof h, &n, &c, &e, cb, &elem) != SPLITZIP_OK) return 4;
+    if (n != 8 || c != 16 || e != 0 || elem != SPLITZIP_ELEM_BF16 || cb[15] != 115) return 5;
+    if (splitzip_read_header(h, sizeof h - 1, 0, 0, 0, 0, 0) != SPLITZIP_E_FORMAT) return 6;
+    if (strcmp(splitzip_status_string(SPLITZIP_E_CAPACITY), "escape capacity exceeded") != 0) return 7;
+    splitzip_free(NULL);
+    printf("ok\n");
+    return 0;
+}
+"""
+
+
+def test_header_compiles_as_c_and_links(tmp_path):
+    """A plain C99 program includes include/splitzip.h, links against the library and uses its
+    host helpers (no device call)."""
+    import subprocess
+    src = tmp_path / "consumer.c"
+    src.write_text(C_CONSUMER)
+    exe = tmp_path / "consumer"
+    lib_dir = os.path.dirname(sz.LIB_PATH)
+    cmd = ["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"), str(src),
+           "-o", str(exe), "-L", lib_dir, "-lsplitzip", f"-Wl,-rpath,{lib_dir}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", (r.returncode, r.stdout, r.stderr)
