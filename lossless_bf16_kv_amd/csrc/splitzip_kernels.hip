@@ -336,48 +336,6 @@ __device__ SegSum block_seg_scan(SegSum x, uint32_t tid, uint32_t lane, SegSum *
     return seg_combine(carry, x);
 }
 
-__device__ uint32_t block_max_u32(uint32_t x, uint32_t tid, uint32_t lane, uint32_t *s_red)
-{
-#pragma unroll
-    for (uint32_t d = 1; d < 64; d <<= 1)
-        x = max(x, shfl_u32(x, lane ^ d));
-    if (lane == 0)
-        s_red[tid >> 6] = x;
-    __syncthreads();
-    uint32_t m = 0;
-    for (int w = 0; w < kWaves; ++w)
-        m = max(m, s_red[w]);
-    __syncthreads();
-    return m;
-}
-
-// Inclusive prefix sum over the 256 threads of the workgroup (thread order).
-__device__ uint32_t block_inclusive_sum_u32(uint32_t x, uint32_t tid, uint32_t lane, uint32_t *s_red)
-{
-    x = wave_inclusive_sum(x, lane);
-    if (lane == 63)
-        s_red[tid >> 6] = x;
-    __syncthreads();
-    uint32_t carry = 0;
-    for (uint32_t w = 0; w < (tid >> 6); ++w)
-        carry += s_red[w];
-    __syncthreads();
-    return carry + x;
-}
-
-__device__ uint64_t block_sum_u64(uint64_t x, uint32_t tid, uint32_t lane, uint64_t *s_red)
-{
-    x = wave_total_u64(x, lane);
-    if (lane == 0)
-        s_red[tid >> 6] = x;
-    __syncthreads();
-    uint64_t m = 0;
-    for (int w = 0; w < kWaves; ++w)
-        m += s_red[w];
-    __syncthreads();
-    return m;
-}
-
 __device__ __forceinline__ bool is_segment_head(const EncodeArgs &a, uint32_t u)
 {
     return segment_first_tile(a, tile_segment(a, u)) == u;
@@ -493,11 +451,33 @@ __device__ __forceinline__ uint32_t range_of(const uint32_t *first, uint32_t n, 
     return lo;
 }
 
+// Inclusive segmented scan over the 64 lanes of a wave (all lanes active).
+__device__ __forceinline__ SegSum wave_seg_scan(SegSum x, uint32_t lane)
+{
+#pragma unroll
+    for (uint32_t d = 1; d < 64; d <<= 1) {
+        const SegSum y = seg_shfl_up(x, d, lane);
+        if (lane >= d)
+            x = seg_combine(y, x);
+    }
+    return x;
+}
+
+__device__ __forceinline__ SegSum lane63(SegSum x)
+{
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)x.v, 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(x.v >> 32), 63);
+    return SegSum{(uint32_t)__builtin_amdgcn_readlane(x.head, 63), ((uint64_t)hi << 32) | lo};
+}
+
+__device__ __forceinline__ SegSum unpack_sum(uint64_t x)
+{
+    return SegSum{(uint32_t)(x >> 63), x & ~(1ull << 63)};
+}
+
 __global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs a)
 {
-    __shared__ SegSum s_wave[kWaves + 1];
-    __shared__ uint32_t s_red32[kWaves];
-    __shared__ uint64_t s_red64[kWaves];
+    static_assert(kPlaceTiles == 64, "a placement group is one wave: one lane per tile");
     __shared__ uint64_t s_prefix[kPlaceTiles];   // escape offset of each tile in its segment
     __shared__ uint64_t s_base[kPlaceTiles];     // first word of each tile in its segment
     __shared__ uint64_t s_chunk0[kPlaceTiles];   // first chunk that starts inside each tile
@@ -510,93 +490,73 @@ __global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs
     const uint32_t lane = lane_id();
     const uint32_t group = blockIdx.x;
     const uint32_t u_first = group * kPlaceTiles;
-    const uint32_t sum_block = u_first / kSumTiles;
     const uint64_t cmask = (1ull << a.log2_chunk) - 1;
 
-    // carry-in: segmented sum of every tile before u_first.  (1) The sum blocks before this
-    // one: from the last one holding a segment head (if any) to the end.  (2) The groups of
-    // this sum block before this one, folded in order.
-    uint32_t last_head = 0, any_head = 0;
-    for (uint32_t b = tid; b < sum_block; b += kThreads)
-        if (a.block_sum[b] >> 63) {
-            last_head = b;        // b grows with the loop, so this keeps the largest
-            any_head = 1;
-        }
-    last_head = block_max_u32(any_head ? last_head + 1 : 0u, tid, lane, s_red32);
-    any_head = last_head != 0;
-    const uint32_t from = any_head ? last_head - 1 : 0u;
-    uint64_t part = 0;
-    for (uint32_t b = from + tid; b < sum_block; b += kThreads)
-        part += a.block_sum[b] & ~(1ull << 63);
-    part = block_sum_u64(part, tid, lane, s_red64);
-    SegSum before{any_head, part};
-    {
-        const uint32_t g0 = sum_block * (kSumTiles / kPlaceTiles);
-        SegSum mine{0, 0};
-        if (g0 + tid < group) {
-            const uint64_t x = a.group_sum[g0 + tid];
-            mine = SegSum{(uint32_t)(x >> 63), x & ~(1ull << 63)};
-        }
-        const SegSum all = block_seg_scan(mine, tid, lane, s_wave);
-        if (tid == kThreads - 1)
-            s_wave[kWaves] = all;
-        __syncthreads();
-        before = seg_combine(before, s_wave[kWaves]);
-        __syncthreads();
-    }
+    // Wave 0 (one lane per tile) works out each tile's escape offset and the flattened ranges
+    // of the group's escapes and chunk offsets, with wave-level scans only: every load it needs
+    // is known up front, and no workgroup barrier stands between them.
+    if (tid < 64) {
+        const uint32_t u = u_first + lane;
+        const bool valid = u < a.n_tiles;
+        const uint32_t count = valid ? a.tile_count[u] : 0u;
+        const uint32_t seg = valid ? tile_segment(a, u) : 0u;
+        const uint32_t head = valid && segment_first_tile(a, seg) == u ? 1u : 0u;
 
-    // each of the first kPlaceTiles threads: one tile; exclusive segmented prefix = carry-in
-    // combined with the earlier tiles
-    const uint32_t u = u_first + tid;
-    const bool valid = tid < kPlaceTiles && u < a.n_tiles;
-    const uint32_t seg = valid ? tile_segment(a, u) : 0u;
-    const uint32_t head = valid && segment_first_tile(a, seg) == u ? 1u : 0u;
-    const uint32_t count = valid ? a.tile_count[u] : 0u;
-    const SegSum incl = block_seg_scan(SegSum{head, count}, tid, lane, s_wave);
-    const SegSum with_carry = seg_combine(before, incl);
-    const uint64_t prefix = head ? 0 : with_carry.v - count;
-    uint64_t base = 0, c_first = 0;
-    uint32_t n_chunks_here = 0;
-    if (valid) {
-        const SegDesc sd = segment_desc(a, seg);
-        base = (uint64_t)(u - segment_first_tile(a, seg)) << a.tile_shift;
-        if (u + 1 == segment_end_tile(a, seg)) {
-            // the segment's last tile knows the segment's escape count
-            const uint64_t E = prefix + count;
-            sd.chunk_off[(sd.n + cmask) >> a.log2_chunk] = E;
-            a.seg_escapes[seg] = E;
-            if (a.packed)
-                write_header(sd, a, E);
+        // carry-in: segmented sum of every tile before u_first, folded in order from the sums of
+        // the earlier sum blocks (64 at a time) and of this block's earlier groups
+        const uint32_t sum_block = u_first / kSumTiles;
+        const uint32_t g0 = sum_block * (kSumTiles / kPlaceTiles);
+        const SegSum grp = g0 + lane < group ? unpack_sum(a.group_sum[g0 + lane]) : SegSum{0, 0};
+        SegSum before{0, 0};
+        for (uint32_t r = 0; r < sum_block; r += 64) {
+            const uint32_t b = r + lane;
+            const SegSum blk = b < sum_block ? unpack_sum(a.block_sum[b]) : SegSum{0, 0};
+            before = seg_combine(before, lane63(wave_seg_scan(blk, lane)));
         }
-        if (base < sd.n) {
-            // chunks that start inside this tile
-            const uint64_t tile_words = 1ull << a.tile_shift;
-            const uint64_t words = sd.n - base < tile_words ? sd.n - base : tile_words;
-            c_first = (base + cmask) >> a.log2_chunk;
-            n_chunks_here = (uint32_t)(((base + words + cmask) >> a.log2_chunk) - c_first);
+        before = seg_combine(before, lane63(wave_seg_scan(grp, lane)));
+
+        // exclusive segmented prefix of each tile = carry-in combined with the earlier tiles
+        const SegSum incl = wave_seg_scan(SegSum{head, count}, lane);
+        const SegSum with_carry = seg_combine(before, incl);
+        const uint64_t prefix = head ? 0 : with_carry.v - count;
+        uint64_t base = 0, c_first = 0;
+        uint32_t n_chunks_here = 0;
+        if (valid) {
+            const SegDesc sd = segment_desc(a, seg);
+            base = (uint64_t)(u - segment_first_tile(a, seg)) << a.tile_shift;
+            if (u + 1 == segment_end_tile(a, seg)) {
+                // the segment's last tile knows the segment's escape count
+                const uint64_t E = prefix + count;
+                sd.chunk_off[(sd.n + cmask) >> a.log2_chunk] = E;
+                a.seg_escapes[seg] = E;
+                if (a.packed)
+                    write_header(sd, a, E);
+            }
+            if (base < sd.n) {
+                // chunks that start inside this tile
+                const uint64_t tile_words = 1ull << a.tile_shift;
+                const uint64_t words = sd.n - base < tile_words ? sd.n - base : tile_words;
+                c_first = (base + cmask) >> a.log2_chunk;
+                n_chunks_here = (uint32_t)(((base + words + cmask) >> a.log2_chunk) - c_first);
+            }
         }
-    }
-    // overflow tiles are moved by the spill launch; the others here, from their slots
-    const bool spilled = count > a.slot_escapes;
-    if (spilled)
-        a.tile_prefix[u] = prefix;
-    if (tid < kPlaceTiles) {
-        s_prefix[tid] = prefix;
-        s_base[tid] = base;
-        s_chunk0[tid] = c_first;
-        s_seg[tid] = seg;
-        s_E[tid] = a.packed && valid ? a.seg_total[seg] : 0;
-    }
-    // where each tile's escapes and chunk offsets fall in the workgroup's flattened ranges
-    const uint32_t esc_incl = block_inclusive_sum_u32(spilled ? 0u : count, tid, lane, s_red32);
-    const uint32_t chunk_incl = block_inclusive_sum_u32(n_chunks_here, tid, lane, s_red32);
-    if (tid < kPlaceTiles) {
-        s_first[tid + 1] = esc_incl;
-        s_cfirst[tid + 1] = chunk_incl;
-    }
-    if (tid == 0) {
-        s_first[0] = 0;
-        s_cfirst[0] = 0;
+        // overflow tiles are moved by the spill launch; the others here, from their slots
+        const bool spilled = count > a.slot_escapes;
+        if (spilled)
+            a.tile_prefix[u] = prefix;
+        s_prefix[lane] = prefix;
+        s_base[lane] = base;
+        s_chunk0[lane] = c_first;
+        s_seg[lane] = seg;
+        s_E[lane] = a.packed && valid ? a.seg_total[seg] : 0;
+        // where each tile's escapes and chunk offsets fall in the group's flattened ranges (at
+        // most 64 slots of escapes and 64 x 2048 chunk starts: both fit 32 bits)
+        s_first[lane + 1] = wave_inclusive_sum(spilled ? 0u : count, lane);
+        s_cfirst[lane + 1] = wave_inclusive_sum(n_chunks_here, lane);
+        if (lane == 0) {
+            s_first[0] = 0;
+            s_cfirst[0] = 0;
+        }
     }
     __syncthreads();
 
