@@ -366,3 +366,23 @@ def test_async_and_prepared_e5m2():
         assert torch.equal(x, y)
         ref = O.encode8(x.cpu().numpy(), np.frombuffer(codec.codebook, np.uint8), 1024)
         assert p.to_bytes() == O.serialize8(ref)
+
+
+def test_packed_several_codebooks_e5m2():
+    """E5M2 packed streams coded with three codebooks in one launch: each equals the oracle's
+    serialization with its own book, and all decode in one launch through a codec that holds
+    none of those books (each stream brings its codebook in its header)."""
+    cals = [workloads.e5m2_normal(40000, 80 + k, sigma=s) for k, s in enumerate((1.0, 300.0, 0.01))]
+    codec = sz.Codec(DEV, 1024, elem="e5m2")
+    codec.calibrate_books([dev8(c) for c in cals])
+    xs = [workloads.e5m2_normal(n, 90 + i, sigma=s) for i, (n, s) in
+          enumerate([(128 * 400, 1.0), (128 * 777, 300.0), (128, 0.01), (0, 1.0)])]
+    books = [0, 1, 2, 1]
+    packed = codec.encode_packed_batch([dev8(x) for x in xs], books=books)
+    for x, p, b in zip(xs, packed, books):
+        ref = O.encode8(x, np.frombuffer(codec.books[b], np.uint8), 1024)
+        assert p.to_bytes() == O.serialize8(ref)
+    other = sz.Codec.from_codebook(bytes(range(16, 32)), 1024, DEV, elem="e5m2")
+    ys = other.decode_packed_batch(packed)
+    for x, y in zip(xs, ys):
+        assert np.array_equal(host(y, np.uint8), x)
