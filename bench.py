@@ -152,6 +152,9 @@ def main():
                     help="encode into / decode from one contiguous packed stream per segment")
     ap.add_argument("--elem", choices=["bf16", "e5m2"], default="bf16",
                     help="element type: BF16 words, or the configuration's inputs cast to FP8 E5M2")
+    ap.add_argument("--scrub-mb", type=int, default=-1,
+                    help="MiB read between timed steps to flush the 256 MB Infinity Cache "
+                         "(default: 2048 when the input is under 1 GiB, else 0)")
     ap.add_argument("--cpu-sample-words", type=int, default=1 << 30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
@@ -225,7 +228,20 @@ def main():
         if ev is not None:
             ev[2].record(stream)
 
+    # Inputs that fit the 256 MB Infinity Cache would otherwise be timed hot: a read of a larger
+    # buffer between steps (outside the timed events) evicts them.  Then the step time comes
+    # from the events, since the wall clock also holds the scrubs.
+    input_bytes = sum(x.numel() * x.element_size() for x in xs)
+    scrub_mb = args.scrub_mb if args.scrub_mb >= 0 else (2048 if input_bytes < (1 << 30) else 0)
+    scrub = torch.ones(scrub_mb << 18, dtype=torch.int32, device=dev) if scrub_mb else None
+    sink = torch.zeros((), dtype=torch.int64, device=dev)
+
+    def flush():
+        if scrub is not None:
+            sink.add_(torch.sum(scrub, dtype=torch.int64))
+
     for _ in range(args.warmup):
+        flush()
         step()
     torch.cuda.synchronize()
     assert batch.finish(result) == sz.OK
@@ -234,6 +250,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
+        flush()
         step(events[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -256,7 +273,12 @@ def main():
     comp = sum(e.compressed_bytes for e in encs)
     alg = algorithmic_bytes(ns, Es, C, e5m2)
     wall_s = t1 - t0
-    value = esize * n * args.steps / wall_s / 1e9
+    if scrub is None:
+        value = esize * n * args.steps / wall_s / 1e9
+        step_ms = wall_s / args.steps * 1e3
+    else:
+        step_ms = enc_avg + dec_avg
+        value = esize * n / (step_ms * 1e-3) / 1e9
     wname = wl.name + f"_c{C}" + ("_books_layer_kv" if books is not None else "") + \
         ("_packed" if args.packed else "")
 
@@ -303,7 +325,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall_s / args.steps * 1e3, 4),
+        "ms_per_step": round(step_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -335,6 +357,9 @@ def main():
         "generate_s": round(t_gen, 1),
         "kernel_source": kernel_source_hash(),
         "round_trip_bitwise": True,
+        "cache_scrub_mb": scrub_mb,
+        "value_basis": "wall clock over the timed steps" if scrub is None else
+                       "encode + decode events (cache flushed between steps)",
     }
     print(json.dumps(out), flush=True)
 
