@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SPLITZIP_ABI_VERSION 3
+#define SPLITZIP_ABI_VERSION 4
 #define SPLITZIP_HEADER_BYTES 64
 #define SPLITZIP_MIN_CHUNK 16
 #define SPLITZIP_MAX_CHUNK 65536
@@ -181,8 +181,10 @@ int splitzip_codec_info(const splitzip_codec *codec, uint8_t codebook[16], uint3
  * Encode n_seg segments (host array `segs`) in one launch.  Blocks until each
  * segment's escape count is known, then fills n_escapes and compressed_bytes.
  * Returns SPLITZIP_E_CAPACITY if some segment has more escapes than esc_capacity:
- * its n_escapes then holds the count needed, its escape arrays hold only the first
- * esc_capacity escapes, and the caller re-encodes with larger escape arrays.
+ * its n_escapes then holds the count needed and the caller re-encodes with larger escape
+ * arrays.  Such a segment's sm, codes and chunk_off are complete; of its escape arrays,
+ * entries below esc_capacity are either the final escape or left unwritten (which ones
+ * depends on the order in which tiles reserve scratch space).
  * Segments with n = 0 are allowed (chunk_off[0] = 0 is written).
  */
 int splitzip_encode(splitzip_codec *codec, uint32_t n_seg, splitzip_segment *segs, void *stream);
@@ -274,6 +276,22 @@ int splitzip_decode_packed(splitzip_codec *codec, uint32_t n_seg, const splitzip
  * codec must have completed; freeing its device memory synchronizes the device. */
 void splitzip_free(splitzip_codec *codec);
 
+/* ---- launch sequence of an encode ---- */
+
+/* Default and largest value of splitzip_set_small_tiles. */
+#define SPLITZIP_SMALL_TILES 2048
+
+/*
+ * An encode call (any of the encode entry points) splits its segments into tiles of
+ * 16384 BF16 words or 32768 E5M2 bytes, at least one per segment.  A call of at most
+ * max_tiles tiles runs two kernel launches (pack, then finish: each tile's escape offset,
+ * escape placement, chunk offsets), a larger call four (pack, sums, place, spill); on
+ * inputs of a few MiB the launches, not the bytes, set the time.  Both sequences write
+ * identical bytes.  max_tiles <= SPLITZIP_SMALL_TILES (default), 0 = always four launches;
+ * larger values give SPLITZIP_E_INVALID.  Applies to calls that start after it returns.
+ */
+int splitzip_set_small_tiles(splitzip_codec *codec, uint32_t max_tiles);
+
 /* ---- per-kernel timing (for benchmarks and profilers) ---- */
 
 /* Kernels whose durations splitzip_profile_read reports, in this order. */
@@ -282,7 +300,8 @@ void splitzip_free(splitzip_codec *codec);
 #define SPLITZIP_KERNEL_PLACE 2   /* encode: escape placement, global chunk offsets      */
 #define SPLITZIP_KERNEL_SPILL 3   /* encode: placement of escape-heavy tiles' escapes    */
 #define SPLITZIP_KERNEL_DECODE 4  /* decode                                               */
-#define SPLITZIP_KERNELS 5
+#define SPLITZIP_KERNEL_FINISH 5  /* encode, small calls: offsets and placement per tile  */
+#define SPLITZIP_KERNELS 6
 
 /*
  * enable != 0: every later encode/decode call on this codec records HIP events around

@@ -34,6 +34,7 @@ LIB_PATH = os.path.join(_HERE, "libsplitzip.so")
 
 OK, E_INVALID, E_NOMEM, E_DEVICE, E_CODEBOOK, E_FORMAT, E_CAPACITY = range(7)
 HEADER_BYTES = 64
+SMALL_TILES = 2048      # encodes of at most this many tiles run pack + finish (two launches)
 MIN_CHUNK, MAX_CHUNK = 16, 65536
 MAX_BOOKS = 4096
 ELEM_BF16, ELEM_E5M2 = 0, 1
@@ -115,6 +116,7 @@ def lib() -> ctypes.CDLL:
     L.splitzip_encode_packed.argtypes = [vp, u32, P(splitzip_packed), vp, vp]
     L.splitzip_decode_packed.argtypes = [vp, u32, P(splitzip_packed), vp, vp]
     L.splitzip_profile.argtypes = [vp, i32]
+    L.splitzip_set_small_tiles.argtypes = [vp, u32]
     L.splitzip_profile_read.argtypes = [vp, vp, P(ctypes.c_double), P(u64), i32]
     L.splitzip_free.argtypes = [vp]
     L.splitzip_free.restype = None
@@ -136,6 +138,7 @@ def lib() -> ctypes.CDLL:
               "splitzip_decode_packed",
               "splitzip_encode", "splitzip_encode_async", "splitzip_decode",
               "splitzip_write_header", "splitzip_profile", "splitzip_profile_read",
+              "splitzip_set_small_tiles",
               "splitzip_read_header", "splitzip_check_header", "splitzip_calibrate_e5m2",
               "splitzip_calibrate_books_e5m2", "splitzip_codec_from_codebooks_e5m2",
               "splitzip_codec_element", "splitzip_histogram_e5m2"):
@@ -313,7 +316,11 @@ def splitzip_decode_packed(codec: int, segs, stream: int = 0, d_error: int = 0) 
     _check(lib().splitzip_decode_packed(codec, len(segs), segs, stream or None, d_error or None))
 
 
-KERNELS = ("encode_pack", "encode_sums", "encode_place", "encode_spill", "decode")
+KERNELS = ("encode_pack", "encode_sums", "encode_place", "encode_spill", "decode", "encode_finish")
+
+
+def splitzip_set_small_tiles(codec: int, max_tiles: int) -> None:
+    _check(lib().splitzip_set_small_tiles(codec, max_tiles))
 
 
 def splitzip_profile(codec: int, enable: bool) -> None:
@@ -572,6 +579,12 @@ class Codec:
     def _stream(self) -> int:
         import torch
         return torch.cuda.current_stream(self.device).cuda_stream
+
+    def set_small_tiles(self, max_tiles: int = SMALL_TILES) -> None:
+        """Encodes of at most max_tiles tiles run two launches instead of four (same bytes);
+        0: always four."""
+        self._need_handle()
+        splitzip_set_small_tiles(self.handle, max_tiles)
 
     def profile(self, enable: bool = True) -> None:
         """Time every kernel launch of later calls with HIP events (see kernel_times)."""

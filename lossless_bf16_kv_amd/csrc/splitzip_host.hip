@@ -16,6 +16,7 @@
 #include <splitzip.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -30,7 +31,7 @@
 namespace {
 
 constexpr uint32_t kCodecMagic = 0x53a2c0dcu;
-constexpr int kStagingSlots = 4;
+constexpr int kStagingSlots = 16;
 
 thread_local std::string g_last_error;
 
@@ -102,13 +103,14 @@ struct Staging {
     sz::SegDesc *d_segs = nullptr;
     uint32_t *d_tiles = nullptr;
     uint32_t cap = 0;
+    uint32_t n = 0;              // descriptors held (h_* and d_* have the same contents)
     hipEvent_t done = nullptr;   // recorded after the last copy out of h_*
     bool used = false;
 };
 
-// Events of one profiled call: kind of the first kernel, then n + 1 events around n kernels.
+// Events of one profiled call: the kind of each of its n kernels and n + 1 events around them.
 struct TimedCall {
-    int first_kind = 0;
+    int kind[SPLITZIP_KERNELS] = {};   // kernel kind of each launch
     int n = 0;
     hipEvent_t ev[SPLITZIP_KERNELS] = {};
 };
@@ -162,6 +164,7 @@ struct splitzip_codec {
     uint32_t elem = sz::kElemBF16;   // element type of every tensor the codec codes
     int device = 0;
     bool profiling = false;
+    std::atomic<uint32_t> small_tiles{sz::kSmallTiles};   // calls of at most this many tiles: pack + finish
     uint32_t chunk_size = 0;
     uint32_t log2_chunk = 0;
     uint32_t n_books = 0;
@@ -352,8 +355,8 @@ void resolve_timings(Workspace *w, bool wait)
         for (int i = 0; i < c.n; ++i) {
             float ms = 0.f;
             if (hipEventElapsedTime(&ms, c.ev[i], c.ev[i + 1]) == hipSuccess) {
-                w->sum_ms[c.first_kind + i] += ms;
-                w->timed[c.first_kind + i] += 1;
+                w->sum_ms[c.kind[i]] += ms;
+                w->timed[c.kind[i]] += 1;
             }
         }
         for (int i = 0; i <= c.n; ++i)
@@ -368,12 +371,13 @@ struct CallTimer {
     TimedCall call;
     int recorded = 0;
     hipStream_t stream = nullptr;
-    CallTimer(splitzip_codec *c, Workspace *ws, hipStream_t s, int first_kind, int n)
+    CallTimer(splitzip_codec *c, Workspace *ws, hipStream_t s, const int *kinds, int n)
     {
-        if (!c->profiling || !ws)
+        if (!c->profiling || !ws || n >= SPLITZIP_KERNELS)
             return;
         resolve_timings(ws, false);
-        call.first_kind = first_kind;
+        for (int i = 0; i < n; ++i)
+            call.kind[i] = kinds[i];
         call.n = n;
         for (int i = 0; i <= n; ++i)
             if (!(call.ev[i] = take_event(ws))) {
@@ -459,15 +463,26 @@ int ensure_result(Workspace *w, uint32_t n_seg)
     return SPLITZIP_OK;
 }
 
-// Copy the descriptor tables of a ragged batch to the device through a pinned slot.
+// Copy the descriptor tables of a ragged batch to the device through a pinned slot.  A
+// batch called again with the same buffers (the same tables) uses the device copy a slot
+// still holds: no copy is enqueued.  Slots are only rewritten by later calls on the same
+// stream, so a kernel that reads one has finished before the copy that replaces it runs.
 int stage_descriptors(Workspace *w, const std::vector<sz::SegDesc> &segs,
                       const std::vector<uint32_t> &tiles, const sz::SegDesc **d_segs,
                       const uint32_t **d_tiles)
 {
+    const uint32_t n = (uint32_t)segs.size();
+    for (const Staging &h : w->staging)
+        if (h.used && h.n == n && std::memcmp(h.h_segs, segs.data(), n * sizeof(sz::SegDesc)) == 0 &&
+            std::memcmp(h.h_tiles, tiles.data(), (n + 1) * sizeof(uint32_t)) == 0) {
+            *d_segs = h.d_segs;
+            *d_tiles = h.d_tiles;
+            return SPLITZIP_OK;
+        }
     Staging &s = w->staging[w->next_slot];
     w->next_slot = (w->next_slot + 1) % kStagingSlots;
-    const uint32_t n = (uint32_t)segs.size();
-    if (s.used)
+    s.used = false;          // until the copy below is enqueued
+    if (s.done && s.n)
         SZ_HIP(hipEventSynchronize(s.done), "hipEventSynchronize(staging)");
     if (s.cap < n) {
         (void)hipHostFree(s.h_segs);
@@ -495,6 +510,7 @@ int stage_descriptors(Workspace *w, const std::vector<sz::SegDesc> &segs,
     SZ_HIP(hipMemcpyAsync(s.d_tiles, s.h_tiles, (n + 1) * sizeof(uint32_t), hipMemcpyHostToDevice, w->stream),
            "hipMemcpyAsync(tiles)");
     SZ_HIP(hipEventRecord(s.done, w->stream), "hipEventRecord(staging)");
+    s.n = n;
     s.used = true;
     *d_segs = s.d_segs;
     *d_tiles = s.d_tiles;
@@ -938,10 +954,19 @@ int encode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
     a.slot_escapes = slot_escapes;
     hipError_t e = hipSuccess;
     {
-        CallTimer timer(codec, w, stream, SPLITZIP_KERNEL_PACK, sz::kEncodeStages);
+        // small calls: pack and finish; else pack, sums, place and spill
+        static const int kSmallStages[] = {sz::kStagePack, sz::kStageFinish};
+        static const int kSmallKinds[] = {SPLITZIP_KERNEL_PACK, SPLITZIP_KERNEL_FINISH};
+        static const int kStages[] = {sz::kStagePack, sz::kStageSums, sz::kStagePlace, sz::kStageSpill};
+        static const int kKinds[] = {SPLITZIP_KERNEL_PACK, SPLITZIP_KERNEL_SUMS, SPLITZIP_KERNEL_PLACE,
+                                     SPLITZIP_KERNEL_SPILL};
+        const bool small = n_tiles <= codec->small_tiles.load(std::memory_order_relaxed);
+        const int *stages = small ? kSmallStages : kStages;
+        const int n_stages = small ? 2 : 4;
+        CallTimer timer(codec, w, stream, small ? kSmallKinds : kKinds, n_stages);
         timer.mark();
-        for (int stage = 0; stage < sz::kEncodeStages && e == hipSuccess; ++stage) {
-            e = sz::launch_encode_stage(stage, a, stream);
+        for (int i = 0; i < n_stages && e == hipSuccess; ++i) {
+            e = sz::launch_encode_stage(stages[i], a, stream);
             timer.mark();
         }
     }
@@ -1118,7 +1143,8 @@ int decode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
     a.elem = codec->elem;
     hipError_t e;
     {
-        CallTimer timer(codec, w, stream, SPLITZIP_KERNEL_DECODE, 1);
+        static const int kDecodeKind[] = {SPLITZIP_KERNEL_DECODE};
+        CallTimer timer(codec, w, stream, kDecodeKind, 1);
         timer.mark();
         e = sz::launch_decode(a, stream);
         timer.mark();
@@ -1160,6 +1186,18 @@ int splitzip_decode_packed(splitzip_codec *codec, uint32_t n_seg, const splitzip
         return rc;
     // each stream's codebook comes from its own header (read by the kernel)
     return decode_launch(codec, desc, tiles, 0, static_cast<hipStream_t>(stream_), d_error);
+}
+
+int splitzip_set_small_tiles(splitzip_codec *codec, uint32_t max_tiles)
+{
+    g_last_error.clear();
+    int rc = codec_check(codec);
+    if (rc != SPLITZIP_OK)
+        return rc;
+    if (max_tiles > sz::kSmallTiles)
+        return fail(SPLITZIP_E_INVALID, "max_tiles %u exceeds %u", max_tiles, sz::kSmallTiles);
+    codec->small_tiles.store(max_tiles, std::memory_order_relaxed);
+    return SPLITZIP_OK;
 }
 
 int splitzip_profile(splitzip_codec *codec, int enable)

@@ -56,6 +56,10 @@ constexpr uint32_t kE8SlotEscapes = 256;                      // E5M2 tiles (twi
 constexpr uint32_t kSumTiles = 2048;          // tiles per segmented-sum block
 constexpr uint32_t kPlaceTiles = 64;          // tiles per placement workgroup
 constexpr uint32_t kSpillBlocks = 1024;       // workgroups moving the overflow tiles' escapes
+// Calls of at most this many tiles finish in one launch after pack (kStageFinish, one
+// workgroup per tile) instead of sums, place and spill: each workgroup adds up the escape
+// counts of its segment's earlier tiles itself (at most kSmallTiles - 1 loads).
+constexpr uint32_t kSmallTiles = 2048;
 // overflow counter: escapes reserved so far (low 40 bits) and overflow tiles listed (high 24)
 constexpr int kOvfTileShift = 40;
 constexpr uint64_t kOvfOffsetMask = (1ull << kOvfTileShift) - 1;
@@ -161,8 +165,9 @@ struct HistArgs {
 
 uint32_t hist_blocks(uint64_t n);
 hipError_t launch_histogram(const HistArgs &a, hipStream_t stream);
-// Encode stages, launched in order 0 (pack), 1 (sums), 2 (place), 3 (spill) on one stream.
-constexpr int kEncodeStages = 4;
+// Encode stages, launched in order on one stream: pack, sums, place, spill; or, for calls of
+// at most kSmallTiles tiles, pack and finish.
+enum EncodeStage { kStagePack = 0, kStageSums, kStagePlace, kStageSpill, kStageFinish };
 hipError_t launch_encode_stage(int stage, const EncodeArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 // E5M2 pack and decode (the other encode stages are shared with BF16).

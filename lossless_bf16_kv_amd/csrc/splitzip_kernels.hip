@@ -142,7 +142,7 @@ hipError_t launch_histogram(const HistArgs &a, hipStream_t stream)
 // ======================================================================================
 // a2-a4, a7  encode
 //
-// Four launches, none of which waits on another workgroup:
+// Four launches (two for small calls), none of which waits on another workgroup:
 //   pack   (one workgroup per tile: kEncTileWords BF16 words, or 2^kE8EncTileShift E5M2
 //          bytes in splitzip_e5m2.hip): sign+mantissa bits and codes,
 //          escape ranks inside the tile, escapes written compacted to the tile's scratch slot
@@ -154,6 +154,10 @@ hipError_t launch_histogram(const HistArgs &a, hipStream_t stream)
 //          per-segment totals;
 //   spill  (a fixed grid over the list of overflow tiles): their escapes moved into place,
 //          one tile per workgroup at a time, so escape-heavy inputs keep the whole GPU busy.
+// Calls of at most kSmallTiles tiles (up to 64 MiB of input) replace sums, place and spill
+// with one launch, finish (one workgroup per tile), which adds up the earlier tiles' escape
+// counts itself: on inputs of a few MiB every launch costs a few microseconds of the GPU's
+// time, more than the data takes to move.
 // ======================================================================================
 
 // Split one group of 8 words (4 dwords, word 2m in the low half of dword m).
@@ -478,11 +482,13 @@ __device__ __forceinline__ SegSum unpack_sum(uint64_t x)
 __global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs a)
 {
     static_assert(kPlaceTiles == 64, "a placement group is one wave: one lane per tile");
-    __shared__ uint64_t s_prefix[kPlaceTiles];   // escape offset of each tile in its segment
-    __shared__ uint64_t s_base[kPlaceTiles];     // first word of each tile in its segment
-    __shared__ uint64_t s_chunk0[kPlaceTiles];   // first chunk that starts inside each tile
-    __shared__ uint32_t s_seg[kPlaceTiles];
-    __shared__ uint64_t s_E[kPlaceTiles];        // packed layout: E of each tile's segment
+    // per tile, so that the loops below load no segment descriptor
+    __shared__ uint64_t s_prefix[kPlaceTiles];   // escape offset of the tile in its segment
+    __shared__ uint64_t s_base[kPlaceTiles];     // first word of the tile in its segment
+    __shared__ uint64_t s_room[kPlaceTiles];     // escape capacity left from s_prefix on
+    __shared__ uint64_t *s_cptr[kPlaceTiles];    // first chunk offset that starts in the tile
+    __shared__ uint16_t *s_pos[kPlaceTiles];     // the segment's escape positions
+    __shared__ uint8_t *s_exps[kPlaceTiles];     // its escape exponents (NULL: none written)
     __shared__ uint32_t s_first[kPlaceTiles + 1];   // escapes: start of each tile's range
     __shared__ uint32_t s_cfirst[kPlaceTiles + 1];  // chunk offsets: start of each tile's range
 
@@ -519,7 +525,10 @@ __global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs
         const SegSum incl = wave_seg_scan(SegSum{head, count}, lane);
         const SegSum with_carry = seg_combine(before, incl);
         const uint64_t prefix = head ? 0 : with_carry.v - count;
-        uint64_t base = 0, c_first = 0;
+        uint64_t base = 0, room = 0;
+        uint64_t *cptr = nullptr;
+        uint16_t *pos = nullptr;
+        uint8_t *exps = nullptr;
         uint32_t n_chunks_here = 0;
         if (valid) {
             const SegDesc sd = segment_desc(a, seg);
@@ -536,9 +545,13 @@ __global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs
                 // chunks that start inside this tile
                 const uint64_t tile_words = 1ull << a.tile_shift;
                 const uint64_t words = sd.n - base < tile_words ? sd.n - base : tile_words;
-                c_first = (base + cmask) >> a.log2_chunk;
+                const uint64_t c_first = (base + cmask) >> a.log2_chunk;
                 n_chunks_here = (uint32_t)(((base + words + cmask) >> a.log2_chunk) - c_first);
+                cptr = sd.chunk_off + c_first;
             }
+            pos = sd.esc_pos;
+            exps = a.packed ? packed_exps(sd, a.seg_total[seg]) : sd.esc_exp;
+            room = prefix < sd.esc ? sd.esc - prefix : 0;
         }
         // overflow tiles are moved by the spill launch; the others here, from their slots
         const bool spilled = count > a.slot_escapes;
@@ -546,9 +559,10 @@ __global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs
             a.tile_prefix[u] = prefix;
         s_prefix[lane] = prefix;
         s_base[lane] = base;
-        s_chunk0[lane] = c_first;
-        s_seg[lane] = seg;
-        s_E[lane] = a.packed && valid ? a.seg_total[seg] : 0;
+        s_room[lane] = room;
+        s_cptr[lane] = cptr;
+        s_pos[lane] = pos;
+        s_exps[lane] = exps;
         // where each tile's escapes and chunk offsets fall in the group's flattened ranges (at
         // most 64 slots of escapes and 64 x 2048 chunk starts: both fit 32 bits)
         s_first[lane + 1] = wave_inclusive_sum(spilled ? 0u : count, lane);
@@ -563,7 +577,6 @@ __global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs
     // tile-local chunk offsets become segment offsets: consecutive threads take consecutive
     // entries, four loads in flight before the stores
     constexpr int kBatch = 4;
-    SegDesc sd = a.seg0;
     const uint32_t total_c = s_cfirst[kPlaceTiles];
     for (uint32_t e0 = tid; e0 < total_c; e0 += kBatch * kThreads) {
         uint64_t *where[kBatch];
@@ -574,9 +587,7 @@ __global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs
             where[k] = nullptr;
             if (e < total_c) {
                 const uint32_t i = range_of(s_cfirst, kPlaceTiles, e);
-                if (a.n_seg > 1)
-                    sd = a.segs[s_seg[i]];
-                where[k] = sd.chunk_off + s_chunk0[i] + (e - s_cfirst[i]);
+                where[k] = s_cptr[i] + (e - s_cfirst[i]);
                 val[k] = *as_global(where[k]) + s_prefix[i];
             }
         }
@@ -606,13 +617,11 @@ __global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs
             const uint32_t i = tile_of[k];
             if (i == kPlaceTiles)
                 continue;
-            const uint32_t j = j0 + k * kThreads;
-            if (a.n_seg > 1)
-                sd = a.segs[s_seg[i]];
-            const uint64_t d = s_prefix[i] + (j - s_first[i]);
-            uint8_t *exps = a.packed ? packed_exps(sd, s_E[i]) : sd.esc_exp;
-            if (d < sd.esc && exps) {
-                as_global(sd.esc_pos)[d] = (uint16_t)((s_base[i] + (ent[k] & 0xFFFFu)) & cmask);
+            const uint32_t r = j0 + k * kThreads - s_first[i];
+            uint8_t *exps = s_exps[i];
+            if (r < s_room[i] && exps) {
+                const uint64_t d = s_prefix[i] + r;
+                as_global(s_pos[i])[d] = (uint16_t)((s_base[i] + (ent[k] & 0xFFFFu)) & cmask);
                 as_global(exps)[d] = (uint8_t)(ent[k] >> 16);
             }
         }
@@ -658,23 +667,144 @@ __global__ __launch_bounds__(kThreads) void encode_spill_kernel(const EncodeArgs
     }
 }
 
+// ---- finish (calls of at most kSmallTiles tiles) ------------------------------------------
+
+// Sum of v over the workgroup, in every thread.  Contains barriers.
+__device__ __forceinline__ uint64_t block_total_u64(uint64_t v, uint32_t tid, uint32_t lane,
+                                                    uint64_t *s_part)
+{
+    v = wave_total_u64(v, lane);
+    if (lane == 0)
+        s_part[tid >> 6] = v;
+    __syncthreads();
+    uint64_t total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+        total += s_part[w];
+    __syncthreads();
+    return total;
+}
+
+// One workgroup per tile does the work of the sums, place and spill launches for its own
+// tile: its escape offset is the sum of the escape counts of its segment's earlier tiles
+// (fewer than kSmallTiles, all loaded at once), then its chunk offsets become segment offsets
+// and its escapes move from the slot, or from the overflow area, to their final positions.
+// The segment's last tile also writes E (and the header of a packed stream).
+__global__ __launch_bounds__(kThreads) void encode_finish_kernel(const EncodeArgs a)
+{
+    __shared__ uint32_t s_cnt[kWaves];
+    __shared__ uint64_t s_part[kWaves];
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = lane_id();
+    const uint32_t t = blockIdx.x;
+    const uint64_t cmask = (1ull << a.log2_chunk) - 1;
+
+    const uint32_t s = a.n_seg > 1 ? find_segment_block(a.tile_start, a.n_seg, t, tid, lane, s_cnt) : 0u;
+    const SegDesc sd = segment_desc(a, s);
+    const uint32_t first = segment_first_tile(a, s);
+    const uint32_t end = segment_end_tile(a, s);
+    const uint32_t count = a.tile_count[t];
+
+    // the escapes before this tile in its segment; a packed stream needs the segment's E
+    // as well (its exponents follow the E positions)
+    const uint32_t stop = a.packed ? end : t;
+    uint64_t before = 0, all = 0;
+    for (uint32_t u = first + tid; u < stop; u += kThreads) {
+        const uint32_t c = a.tile_count[u];
+        before += u < t ? c : 0u;
+        all += c;
+    }
+    const uint64_t prefix = block_total_u64(before, tid, lane, s_part);
+    const uint64_t E = a.packed ? block_total_u64(all, tid, lane, s_part) : prefix + count;
+    if (t + 1 == end && tid == 0) {
+        sd.chunk_off[(sd.n + cmask) >> a.log2_chunk] = E;
+        a.seg_escapes[s] = E;
+        if (a.packed)
+            write_header(sd, a, E);
+    }
+    if (t == 0 && tid == 0)
+        a.ovf_ctr[0] = 0;    // the pack launch has finished with the overflow counter
+
+    // tile-local chunk offsets become segment offsets, four loads in flight before the stores
+    constexpr int kBatch = 4;
+    const uint64_t base = (uint64_t)(t - first) << a.tile_shift;
+    if (base < sd.n) {
+        const uint64_t tile_words = 1ull << a.tile_shift;
+        const uint64_t words = sd.n - base < tile_words ? sd.n - base : tile_words;
+        const uint64_t c0 = (base + cmask) >> a.log2_chunk;
+        const uint32_t nc = (uint32_t)(((base + words + cmask) >> a.log2_chunk) - c0);
+        SZ_GLOBAL uint64_t *co = as_global(sd.chunk_off + c0);
+        for (uint32_t i0 = tid; i0 < nc; i0 += kBatch * kThreads) {
+            uint64_t v[kBatch];
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k)
+                if (i0 + k * kThreads < nc)
+                    v[k] = co[i0 + k * kThreads];
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k)
+                if (i0 + k * kThreads < nc)
+                    co[i0 + k * kThreads] = v[k] + prefix;
+        }
+    }
+
+    // the tile's escapes: from its slot, or, past the slot, from its range of the overflow area
+    const uint32_t *src = a.slots + (uint64_t)t * a.slot_escapes;
+    uint64_t lim = count;
+    if (count > a.slot_escapes) {
+        const uint64_t off = a.tile_ovf[t];
+        const uint64_t room = off < a.ovf_cap ? a.ovf_cap - off : 0;
+        src = a.ovf + off;
+        lim = count < room ? count : room;
+    }
+    uint8_t *exps = a.packed ? packed_exps(sd, E) : sd.esc_exp;
+    const uint64_t dlim = prefix < sd.esc ? sd.esc - prefix : 0;   // escape capacity left
+    if (lim > dlim)
+        lim = dlim;
+    if (!exps)
+        lim = 0;
+    SZ_GLOBAL uint16_t *pos = as_global(lim ? sd.esc_pos + prefix : sd.esc_pos);
+    SZ_GLOBAL uint8_t *ex = as_global(lim ? exps + prefix : exps);
+    for (uint32_t r0 = tid; r0 < lim; r0 += kBatch * kThreads) {
+        uint32_t e[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k)
+            if (r0 + k * kThreads < lim)
+                e[k] = src[r0 + k * kThreads];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const uint32_t r = r0 + k * kThreads;
+            if (r < lim) {
+                pos[r] = (uint16_t)((base + (e[k] & 0xFFFFu)) & cmask);
+                ex[r] = (uint8_t)(e[k] >> 16);
+            }
+        }
+    }
+}
+
 hipError_t launch_encode_stage(int stage, const EncodeArgs &a, hipStream_t stream)
 {
     switch (stage) {
-    case 0:
+    case kStagePack:
         if (a.elem == kElemE5M2)
             return launch_encode_pack_e5m2(a, stream);
         encode_pack_kernel<<<a.n_tiles, kThreads, 0, stream>>>(a);
         break;
-    case 1:
+    case kStageSums:
         encode_sums_kernel<<<(a.n_tiles + kSumTiles - 1) / kSumTiles, kThreads, 0, stream>>>(a);
         break;
-    case 2:
+    case kStagePlace:
         encode_place_kernel<<<(a.n_tiles + kPlaceTiles - 1) / kPlaceTiles, kThreads, 0, stream>>>(a);
         break;
-    default:
+    case kStageSpill:
         encode_spill_kernel<<<a.n_tiles < kSpillBlocks ? a.n_tiles : kSpillBlocks, kThreads, 0, stream>>>(a);
         break;
+    case kStageFinish:
+        if (a.n_tiles > kSmallTiles)
+            return hipErrorInvalidValue;
+        encode_finish_kernel<<<a.n_tiles, kThreads, 0, stream>>>(a);
+        break;
+    default:
+        return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }

@@ -1,0 +1,171 @@
+"""GPU parity of both encode launch sequences: calls of at most SMALL_TILES tiles run pack
+and finish (one workgroup per tile adds up the earlier tiles' escape counts itself), larger
+calls run pack, sums, place and spill.  Each case is encoded both ways
+(``Codec.set_small_tiles``) and both must equal the oracle byte for byte: BF16 and E5M2
+streams spanning several tiles with ragged tails, tiles whose escapes overflow their
+slot, batches with empty and tiny segments and several codebooks, packed streams, too
+little escape room, and the 2048 / 2049-tile boundary of the default."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import lossless_bf16_kv_amd as sz
+import oracle
+import workloads
+from test_gpu_parity import DEV, assert_same_stream, codec_for, dev, host
+import test_gpu_e5m2 as t8
+
+pytestmark = pytest.mark.gpu
+
+O = oracle.get()
+MODES = {"four_launches": 0, "pack_finish": sz.SMALL_TILES}
+TILE = 16384          # BF16 words per pack tile
+TILE8 = 32768         # E5M2 bytes per pack tile
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("n,C,wide", [
+    (1, 16, 0.02), (TILE - 1, 1024, 0.02), (TILE + 1, 16, 0.3), (5 * TILE + 3, 64, 0.02),
+    (5 * TILE + 3, 1024, 0.3), (300_007, 4096, 0.05), (300_007, 65536, 0.3),
+])
+def test_bf16_streams(mode, n, C, wide):
+    # wide = 0.3 puts about 30 % of the words outside the codebook: every tile overflows its
+    # 128-entry slot and its escapes go through the overflow area
+    x = workloads.mixed_words(n, 31 * n + C, wide_fraction=wide)
+    codec = codec_for(workloads.normal_words(50_000, 3), C)
+    codec.set_small_tiles(MODES[mode])
+    enc = codec.encode(dev(x))
+    assert_same_stream(codec, enc, x)
+    assert np.array_equal(host(codec.decode(enc), np.uint16), x)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_bf16_batch_empty_tiny_and_books(mode):
+    cals = [workloads.normal_words(60_000, 70 + k, sigma=2.0 ** (6 * k - 6)) for k in range(3)]
+    codec = sz.Codec(DEV, 64)
+    codec.calibrate_books([dev(c) for c in cals])
+    codec.set_small_tiles(MODES[mode])
+    sizes = [0, 1, 7, TILE, TILE + 1, 0, 100, 3 * TILE + 5, 40_000]
+    xs = [workloads.mixed_words(n, 500 + i, wide_fraction=0.1 * (i % 4)) for i, n in enumerate(sizes)]
+    books = [i % 3 for i in range(len(xs))]
+    encs = codec.encode_batch([dev(x) for x in xs], books=books)
+    for x, e, b in zip(xs, encs, books):
+        assert e.book == b
+        assert_same_stream(codec, e, x)
+    for x, y in zip(xs, codec.decode_batch(encs)):
+        assert np.array_equal(host(y, np.uint16), x)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("escapes", ["in_slots", "overflowing"])
+def test_bf16_too_little_escape_room(mode, escapes):
+    """E_CAPACITY with the exact count; sm, codes and chunk offsets complete.  Escapes of
+    tiles that fit their slot are all written below the capacity; an overflowing tile's
+    escapes only when its range of the overflow area (sized from the capacity, reserved in
+    whatever order the tiles finish) lies inside it, so there every entry is either final
+    or untouched."""
+    n = 4 * TILE + 9
+    if escapes == "in_slots":       # N(0,1) against its own calibration: ~0.01 % escapes
+        x = workloads.normal_words(n, 77)
+    else:                           # ~30 % escapes: every tile overflows its slot
+        x = workloads.mixed_words(n, 77, wide_fraction=0.3)
+    codec = codec_for(workloads.normal_words(20_000, 5), 1024)
+    codec.set_small_tiles(MODES[mode])
+    ref = O.encode(x, np.frombuffer(codec.codebook, np.uint8), 1024)
+    assert ref["n_escapes"] >= 3
+    cap = ref["n_escapes"] // 3
+    enc = codec.empty_encoded(x.size, escape_capacity=cap)
+    enc.esc_pos_buf.fill_(-1)            # 0xFFFF: no position inside a 1024-word chunk
+    enc.esc_exp_buf.fill_(0)
+    assert codec.encode_into([dev(x)], [enc]) == sz.E_CAPACITY
+    assert enc.n_escapes == ref["n_escapes"]
+    assert np.array_equal(host(enc.sm, np.uint8), ref["sm"])
+    assert np.array_equal(host(enc.codes, np.uint8), ref["codes"])
+    assert np.array_equal(host(enc.chunk_off, np.uint64), ref["chunk_off"])
+    pos = host(enc.esc_pos_buf, np.uint16)[:cap]
+    exp = host(enc.esc_exp_buf, np.uint8)[:cap]
+    written = pos != 0xFFFF
+    if escapes == "in_slots":
+        assert written.all()
+    assert np.array_equal(pos[written], ref["esc_pos"][:cap][written])
+    assert np.array_equal(exp[written], ref["esc_exp"][:cap][written])
+    assert not exp[~written].any()
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_packed_streams(mode):
+    C = 1024
+    codec = codec_for(workloads.mixed_words(100_000, 41, wide_fraction=0.05), C)
+    codec.set_small_tiles(MODES[mode])
+    xs = [workloads.mixed_words(n, 900 + n % 97, wide_fraction=w)
+          for n, w in [(0, 0.0), (16, 0.1), (3 * TILE + 16, 0.3), (250_000, 0.05)]]
+    packed = codec.encode_packed_batch([dev(x) for x in xs])
+    for x, p in zip(xs, packed):
+        assert p.to_bytes() == O.serialize(O.encode(x, np.frombuffer(codec.codebook, np.uint8), C))
+    for x, y in zip(xs, codec.decode_packed_batch(packed)):
+        assert np.array_equal(host(y, np.uint16), x)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("n,C,wide", [
+    (1, 16, 0.02), (TILE8 + 5, 16, 0.3), (3 * TILE8 + 77, 1024, 0.02), (200_003, 4096, 0.3),
+])
+def test_e5m2_streams(mode, n, C, wide):
+    x = workloads.e5m2_mixed(n, 13 * n + C, wide_fraction=wide)
+    codec = t8.codec_for(workloads.e5m2_normal(50_000, 4), C)
+    codec.set_small_tiles(MODES[mode])
+    enc = codec.encode(t8.dev8(x))
+    t8.assert_same_stream(codec, enc, x)
+    assert np.array_equal(t8.host(codec.decode(enc), np.uint8), x)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_e5m2_packed_batch(mode):
+    C = 64
+    codec = t8.codec_for(workloads.e5m2_normal(50_000, 8), C)
+    codec.set_small_tiles(MODES[mode])
+    xs = [workloads.e5m2_mixed(n, 40 + n % 89, wide_fraction=0.2) for n in (0, 128, TILE8 * 2 + 256)]
+    packed = codec.encode_packed_batch([t8.dev8(x) for x in xs])
+    for x, p in zip(xs, packed):
+        assert p.to_bytes() == O.serialize8(O.encode8(x, np.frombuffer(codec.codebook, np.uint8), C))
+
+
+@pytest.mark.parametrize("tiles", [sz.SMALL_TILES, sz.SMALL_TILES + 1])
+def test_default_boundary(tiles):
+    """The last call size that runs pack + finish and the first that runs four launches."""
+    n = (tiles - 1) * TILE + 1
+    x = workloads.mixed_words(n, tiles, wide_fraction=0.01)
+    codec = codec_for(workloads.normal_words(50_000, 9), 1024)
+    codec.profile(True)
+    enc = codec.encode(dev(x))
+    times = codec.kernel_times()
+    codec.profile(False)
+    small = tiles <= sz.SMALL_TILES
+    packs = times["encode_pack"][1]        # one per encode attempt (a retry adds one)
+    assert packs >= 1
+    assert times["encode_finish"][1] == (packs if small else 0)
+    assert times["encode_sums"][1] == (0 if small else packs)
+    assert_same_stream(codec, enc, x)
+
+
+def test_launch_counts_and_limit():
+    x = dev(workloads.normal_words(5 * TILE, 9))
+    codec = codec_for(workloads.normal_words(30_000, 10), 1024)
+    codec.profile(True)
+    codec.encode(x)
+    codec.set_small_tiles(0)
+    codec.encode(x)
+    codec.set_small_tiles(5)
+    codec.encode(x)
+    codec.set_small_tiles(4)
+    codec.encode(x)
+    times = codec.kernel_times(reset=True)
+    codec.profile(False)
+    assert times["encode_pack"][1] == 4
+    assert times["encode_finish"][1] == 2
+    assert all(times[k][1] == 2 for k in ("encode_sums", "encode_place", "encode_spill"))
+    with pytest.raises(sz.SplitZipError) as e:
+        codec.set_small_tiles(sz.SMALL_TILES + 1)
+    assert e.value.status == sz.E_INVALID
