@@ -24,6 +24,7 @@
 #include <map>
 #include <memory>
 #include <mutex>
+#include <exception>
 #include <new>
 #include <string>
 #include <vector>
@@ -33,16 +34,14 @@ namespace {
 constexpr uint32_t kCodecMagic = 0x53a2c0dcu;
 constexpr int kStagingSlots = 16;
 
-thread_local std::string g_last_error;
+thread_local char g_last_error[512];   // no allocation: fail() cannot throw
 
 int fail(int status, const char *fmt, ...)
 {
-    char buf[512];
     va_list ap;
     va_start(ap, fmt);
-    vsnprintf(buf, sizeof buf, fmt, ap);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
     va_end(ap);
-    g_last_error = buf;
     return status;
 }
 
@@ -50,6 +49,22 @@ int fail_hip(hipError_t e, const char *what)
 {
     return fail(e == hipErrorOutOfMemory ? SPLITZIP_E_NOMEM : SPLITZIP_E_DEVICE, "%s: %s", what,
                 hipGetErrorString(e));
+}
+
+// Runs the body of an entry point: a C++ exception (host memory exhausted, a mutex error)
+// becomes a status instead of crossing the C ABI.
+template <class F>
+int guarded(F &&body) noexcept
+{
+    try {
+        return body();
+    } catch (const std::bad_alloc &) {
+        return fail(SPLITZIP_E_NOMEM, "host memory allocation failed");
+    } catch (const std::exception &ex) {
+        return fail(SPLITZIP_E_DEVICE, "internal error: %s", ex.what());
+    } catch (...) {
+        return fail(SPLITZIP_E_DEVICE, "internal error");
+    }
 }
 
 #define SZ_HIP(call, what)                     \
@@ -672,10 +687,6 @@ int64_t common_book_packed(uint32_t n_seg, const splitzip_packed *segs)
 // C ABI
 // ======================================================================================
 
-extern "C" {
-
-}  // extern "C"
-
 namespace {
 
 // Calibration of n_books codebooks on tensors of one element type: all exponent histograms in
@@ -685,7 +696,7 @@ int calibrate_books(uint32_t elem, uint32_t n_books, const void *const *d_cal, c
                     uint32_t chunk_size, void *stream_, splitzip_codec **out_codec, double *coverage,
                     uint64_t *hist, uint32_t hist_bins)
 {
-    g_last_error.clear();
+    g_last_error[0] = '\0';
     if (!out_codec)
         return fail(SPLITZIP_E_INVALID, "out_codec is NULL");
     if (n_books == 0 || n_books > SPLITZIP_MAX_BOOKS)
@@ -727,7 +738,7 @@ int calibrate_books(uint32_t elem, uint32_t n_books, const void *const *d_cal, c
 int codec_from_codebooks(uint32_t elem, uint32_t n_books, const uint8_t *codebooks, uint32_t chunk_size,
                          splitzip_codec **out_codec)
 {
-    g_last_error.clear();
+    g_last_error[0] = '\0';
     if (!codebooks || !out_codec)
         return fail(SPLITZIP_E_INVALID, "codebooks or out_codec is NULL");
     if (n_books == 0 || n_books > SPLITZIP_MAX_BOOKS)
@@ -756,143 +767,169 @@ int splitzip_calibrate_books(uint32_t n_books, const uint16_t *const *d_cal, con
                              uint32_t chunk_size, void *stream, splitzip_codec **out_codec,
                              double *coverage, uint64_t *hist)
 {
-    return calibrate_books(sz::kElemBF16, n_books, reinterpret_cast<const void *const *>(d_cal), n_cal,
-                           chunk_size, stream, out_codec, coverage, hist, 256);
+    return guarded([&]() -> int {
+        return calibrate_books(sz::kElemBF16, n_books, reinterpret_cast<const void *const *>(d_cal), n_cal,
+                               chunk_size, stream, out_codec, coverage, hist, 256);
+    });
 }
 
 int splitzip_calibrate(const uint16_t *d_cal, uint64_t n_cal, uint32_t chunk_size, void *stream,
                        splitzip_codec **out_codec, double *out_coverage, uint64_t *out_hist)
 {
-    return splitzip_calibrate_books(1, &d_cal, &n_cal, chunk_size, stream, out_codec, out_coverage,
-                                    out_hist);
+    return guarded([&]() -> int {
+        return splitzip_calibrate_books(1, &d_cal, &n_cal, chunk_size, stream, out_codec, out_coverage,
+                                        out_hist);
+    });
 }
 
 int splitzip_calibrate_books_e5m2(uint32_t n_books, const uint8_t *const *d_cal, const uint64_t *n_cal,
                                   uint32_t chunk_size, void *stream, splitzip_codec **out_codec,
                                   double *coverage, uint64_t *hist)
 {
-    return calibrate_books(sz::kElemE5M2, n_books, reinterpret_cast<const void *const *>(d_cal), n_cal,
-                           chunk_size, stream, out_codec, coverage, hist, 32);
+    return guarded([&]() -> int {
+        return calibrate_books(sz::kElemE5M2, n_books, reinterpret_cast<const void *const *>(d_cal), n_cal,
+                               chunk_size, stream, out_codec, coverage, hist, 32);
+    });
 }
 
 int splitzip_calibrate_e5m2(const uint8_t *d_cal, uint64_t n_cal, uint32_t chunk_size, void *stream,
                             splitzip_codec **out_codec, double *out_coverage, uint64_t *out_hist)
 {
-    return splitzip_calibrate_books_e5m2(1, &d_cal, &n_cal, chunk_size, stream, out_codec,
-                                         out_coverage, out_hist);
+    return guarded([&]() -> int {
+        return splitzip_calibrate_books_e5m2(1, &d_cal, &n_cal, chunk_size, stream, out_codec,
+                                             out_coverage, out_hist);
+    });
 }
 
 int splitzip_codec_from_codebooks(uint32_t n_books, const uint8_t *codebooks, uint32_t chunk_size,
                                   splitzip_codec **out_codec)
 {
-    return codec_from_codebooks(sz::kElemBF16, n_books, codebooks, chunk_size, out_codec);
+    return guarded([&]() -> int {
+        return codec_from_codebooks(sz::kElemBF16, n_books, codebooks, chunk_size, out_codec);
+    });
 }
 
 int splitzip_codec_from_codebook(const uint8_t codebook[16], uint32_t chunk_size,
                                  splitzip_codec **out_codec)
 {
-    return splitzip_codec_from_codebooks(1, codebook, chunk_size, out_codec);
+    return guarded([&]() -> int {
+        return splitzip_codec_from_codebooks(1, codebook, chunk_size, out_codec);
+    });
 }
 
 int splitzip_codec_from_codebooks_e5m2(uint32_t n_books, const uint8_t *codebooks, uint32_t chunk_size,
                                        splitzip_codec **out_codec)
 {
-    return codec_from_codebooks(sz::kElemE5M2, n_books, codebooks, chunk_size, out_codec);
+    return guarded([&]() -> int {
+        return codec_from_codebooks(sz::kElemE5M2, n_books, codebooks, chunk_size, out_codec);
+    });
 }
 
 int splitzip_codec_element(const splitzip_codec *codec, uint32_t *elem)
 {
-    int rc = codec_check(codec);
-    if (rc != SPLITZIP_OK)
-        return rc;
-    if (!elem)
-        return fail(SPLITZIP_E_INVALID, "elem is NULL");
-    *elem = codec->elem;
-    return SPLITZIP_OK;
+    return guarded([&]() -> int {
+        int rc = codec_check(codec);
+        if (rc != SPLITZIP_OK)
+            return rc;
+        if (!elem)
+            return fail(SPLITZIP_E_INVALID, "elem is NULL");
+        *elem = codec->elem;
+        return SPLITZIP_OK;
+    });
 }
 
 int splitzip_codec_books(const splitzip_codec *codec, uint32_t *n_books, uint8_t *codebooks)
 {
-    int rc = codec_check(codec);
-    if (rc != SPLITZIP_OK)
-        return rc;
-    if (n_books)
-        *n_books = codec->n_books;
-    if (codebooks)
-        std::memcpy(codebooks, codec->cbs.data(), codec->cbs.size());
-    return SPLITZIP_OK;
+    return guarded([&]() -> int {
+        int rc = codec_check(codec);
+        if (rc != SPLITZIP_OK)
+            return rc;
+        if (n_books)
+            *n_books = codec->n_books;
+        if (codebooks)
+            std::memcpy(codebooks, codec->cbs.data(), codec->cbs.size());
+        return SPLITZIP_OK;
+    });
 }
 
 int splitzip_histogram(uint32_t n_seg, const uint16_t *const *d_x, const uint64_t *n, void *stream,
                        uint64_t *hist)
 {
-    g_last_error.clear();
-    if (n_seg == 0 || !d_x || !n || !hist)
-        return fail(SPLITZIP_E_INVALID, "n_seg is 0 or an array is NULL");
-    return run_histograms(n_seg, reinterpret_cast<const void *const *>(d_x), n, sz::kElemBF16,
-                          static_cast<hipStream_t>(stream), hist);
+    return guarded([&]() -> int {
+        g_last_error[0] = '\0';
+        if (n_seg == 0 || !d_x || !n || !hist)
+            return fail(SPLITZIP_E_INVALID, "n_seg is 0 or an array is NULL");
+        return run_histograms(n_seg, reinterpret_cast<const void *const *>(d_x), n, sz::kElemBF16,
+                              static_cast<hipStream_t>(stream), hist);
+    });
 }
 
 int splitzip_histogram_e5m2(uint32_t n_seg, const uint8_t *const *d_x, const uint64_t *n, void *stream,
                             uint64_t *hist)
 {
-    g_last_error.clear();
-    if (n_seg == 0 || !d_x || !n || !hist)
-        return fail(SPLITZIP_E_INVALID, "n_seg is 0 or an array is NULL");
-    std::vector<uint64_t> h(256 * (size_t)n_seg);
-    const int rc = run_histograms(n_seg, reinterpret_cast<const void *const *>(d_x), n, sz::kElemE5M2,
-                                  static_cast<hipStream_t>(stream), h.data());
-    if (rc != SPLITZIP_OK)
-        return rc;
-    for (uint32_t s = 0; s < n_seg; ++s)
-        std::memcpy(hist + 32 * (size_t)s, &h[256 * (size_t)s], 32 * sizeof(uint64_t));
-    return SPLITZIP_OK;
+    return guarded([&]() -> int {
+        g_last_error[0] = '\0';
+        if (n_seg == 0 || !d_x || !n || !hist)
+            return fail(SPLITZIP_E_INVALID, "n_seg is 0 or an array is NULL");
+        std::vector<uint64_t> h(256 * (size_t)n_seg);
+        const int rc = run_histograms(n_seg, reinterpret_cast<const void *const *>(d_x), n, sz::kElemE5M2,
+                                      static_cast<hipStream_t>(stream), h.data());
+        if (rc != SPLITZIP_OK)
+            return rc;
+        for (uint32_t s = 0; s < n_seg; ++s)
+            std::memcpy(hist + 32 * (size_t)s, &h[256 * (size_t)s], 32 * sizeof(uint64_t));
+        return SPLITZIP_OK;
+    });
 }
 
 int splitzip_exponent_stats(const uint64_t hist[256], double *entropy_bits, double *coverage,
                             uint8_t codebook[16], uint32_t *distinct)
 {
-    g_last_error.clear();
-    if (!hist)
-        return fail(SPLITZIP_E_INVALID, "hist is NULL");
-    uint64_t m = 0;
-    uint32_t d = 0;
-    for (int e = 0; e < 256; ++e) {
-        m += hist[e];
-        d += hist[e] != 0;
-    }
-    double h = 0.0;
-    for (int e = 0; e < 256; ++e)
-        if (hist[e]) {
-            const double p = (double)hist[e] / (double)m;
-            h -= p * std::log2(p);
+    return guarded([&]() -> int {
+        g_last_error[0] = '\0';
+        if (!hist)
+            return fail(SPLITZIP_E_INVALID, "hist is NULL");
+        uint64_t m = 0;
+        uint32_t d = 0;
+        for (int e = 0; e < 256; ++e) {
+            m += hist[e];
+            d += hist[e] != 0;
         }
-    uint8_t cb[16];
-    const uint64_t covered = pick_codebook(hist, cb);
-    if (entropy_bits)
-        *entropy_bits = h;
-    if (coverage)
-        *coverage = m ? (double)covered / (double)m : 0.0;
-    if (codebook)
-        std::memcpy(codebook, cb, 16);
-    if (distinct)
-        *distinct = d;
-    return SPLITZIP_OK;
+        double h = 0.0;
+        for (int e = 0; e < 256; ++e)
+            if (hist[e]) {
+                const double p = (double)hist[e] / (double)m;
+                h -= p * std::log2(p);
+            }
+        uint8_t cb[16];
+        const uint64_t covered = pick_codebook(hist, cb);
+        if (entropy_bits)
+            *entropy_bits = h;
+        if (coverage)
+            *coverage = m ? (double)covered / (double)m : 0.0;
+        if (codebook)
+            std::memcpy(codebook, cb, 16);
+        if (distinct)
+            *distinct = d;
+        return SPLITZIP_OK;
+    });
 }
 
 int splitzip_codec_info(const splitzip_codec *codec, uint8_t codebook[16], uint32_t *chunk_size,
                         int *device)
 {
-    int rc = codec_check(codec);
-    if (rc != SPLITZIP_OK)
-        return rc;
-    if (codebook)
-        std::memcpy(codebook, codec->cbs.data(), 16);
-    if (chunk_size)
-        *chunk_size = codec->chunk_size;
-    if (device)
-        *device = codec->device;
-    return SPLITZIP_OK;
+    return guarded([&]() -> int {
+        int rc = codec_check(codec);
+        if (rc != SPLITZIP_OK)
+            return rc;
+        if (codebook)
+            std::memcpy(codebook, codec->cbs.data(), 16);
+        if (chunk_size)
+            *chunk_size = codec->chunk_size;
+        if (device)
+            *device = codec->device;
+        return SPLITZIP_OK;
+    });
 }
 
 }  // extern "C"
@@ -1013,99 +1050,105 @@ extern "C" {
 int splitzip_encode_async(splitzip_codec *codec, uint32_t n_seg, const splitzip_segment *segs,
                           void *stream_, uint64_t *d_result)
 {
-    g_last_error.clear();
-    if (!d_result || !aligned(d_result, 8))
-        return fail(SPLITZIP_E_INVALID, "d_result NULL or not 8-byte aligned");
-    int rc = codec_check(codec);
-    if (rc != SPLITZIP_OK)
-        return rc;
-    std::vector<sz::SegDesc> desc;
-    std::vector<uint32_t> tiles;
-    if ((rc = prepare_segments(codec, n_seg, segs, true, desc, tiles)) != SPLITZIP_OK)
-        return rc;
-    DeviceGuard dg(codec->device);
-    if (dg.err != hipSuccess)
-        return fail_hip(dg.err, "hipSetDevice");
-    hipStream_t stream = static_cast<hipStream_t>(stream_);
-    Workspace *ws = nullptr;
-    if ((rc = get_workspace(codec, stream, &ws)) != SPLITZIP_OK)
-        return rc;
-    // the lock covers only the launch: nothing is read back
-    std::lock_guard<std::mutex> lock(ws->mu);
-    Workspace *w = nullptr;
-    return encode_launch(codec, desc, tiles, common_book(n_seg, segs), false, stream, d_result, &w);
+    return guarded([&]() -> int {
+        g_last_error[0] = '\0';
+        if (!d_result || !aligned(d_result, 8))
+            return fail(SPLITZIP_E_INVALID, "d_result NULL or not 8-byte aligned");
+        int rc = codec_check(codec);
+        if (rc != SPLITZIP_OK)
+            return rc;
+        std::vector<sz::SegDesc> desc;
+        std::vector<uint32_t> tiles;
+        if ((rc = prepare_segments(codec, n_seg, segs, true, desc, tiles)) != SPLITZIP_OK)
+            return rc;
+        DeviceGuard dg(codec->device);
+        if (dg.err != hipSuccess)
+            return fail_hip(dg.err, "hipSetDevice");
+        hipStream_t stream = static_cast<hipStream_t>(stream_);
+        Workspace *ws = nullptr;
+        if ((rc = get_workspace(codec, stream, &ws)) != SPLITZIP_OK)
+            return rc;
+        // the lock covers only the launch: nothing is read back
+        std::lock_guard<std::mutex> lock(ws->mu);
+        Workspace *w = nullptr;
+        return encode_launch(codec, desc, tiles, common_book(n_seg, segs), false, stream, d_result, &w);
+    });
 }
 
 int splitzip_encode(splitzip_codec *codec, uint32_t n_seg, splitzip_segment *segs, void *stream_)
 {
-    g_last_error.clear();
-    int rc = codec_check(codec);
-    if (rc != SPLITZIP_OK)
+    return guarded([&]() -> int {
+        g_last_error[0] = '\0';
+        int rc = codec_check(codec);
+        if (rc != SPLITZIP_OK)
+            return rc;
+        std::vector<sz::SegDesc> desc;
+        std::vector<uint32_t> tiles;
+        if ((rc = prepare_segments(codec, n_seg, segs, true, desc, tiles)) != SPLITZIP_OK)
+            return rc;
+        DeviceGuard dg(codec->device);
+        if (dg.err != hipSuccess)
+            return fail_hip(dg.err, "hipSetDevice");
+        hipStream_t stream = static_cast<hipStream_t>(stream_);
+        Workspace *ws = nullptr;
+        if ((rc = get_workspace(codec, stream, &ws)) != SPLITZIP_OK)
+            return rc;
+        std::lock_guard<std::mutex> lock(ws->mu);
+        Workspace *w = nullptr;
+        if ((rc = encode_launch(codec, desc, tiles, common_book(n_seg, segs), false, stream, nullptr, &w)) != SPLITZIP_OK)
+            return rc;
+        std::vector<uint64_t> E;
+        if ((rc = encode_readback(w, stream, desc, E)) != SPLITZIP_OK)
+            return rc;
+        for (uint32_t i = 0; i < n_seg; ++i) {
+            segs[i].n_escapes = E[i];
+            segs[i].compressed_bytes = stream_bytes(codec->elem, segs[i].n, codec->chunk_size, E[i]);
+            if (E[i] > segs[i].esc_capacity && rc == SPLITZIP_OK)
+                rc = fail(SPLITZIP_E_CAPACITY, "segment %u has %llu escapes, capacity %llu", i,
+                          (unsigned long long)E[i], (unsigned long long)segs[i].esc_capacity);
+        }
         return rc;
-    std::vector<sz::SegDesc> desc;
-    std::vector<uint32_t> tiles;
-    if ((rc = prepare_segments(codec, n_seg, segs, true, desc, tiles)) != SPLITZIP_OK)
-        return rc;
-    DeviceGuard dg(codec->device);
-    if (dg.err != hipSuccess)
-        return fail_hip(dg.err, "hipSetDevice");
-    hipStream_t stream = static_cast<hipStream_t>(stream_);
-    Workspace *ws = nullptr;
-    if ((rc = get_workspace(codec, stream, &ws)) != SPLITZIP_OK)
-        return rc;
-    std::lock_guard<std::mutex> lock(ws->mu);
-    Workspace *w = nullptr;
-    if ((rc = encode_launch(codec, desc, tiles, common_book(n_seg, segs), false, stream, nullptr, &w)) != SPLITZIP_OK)
-        return rc;
-    std::vector<uint64_t> E;
-    if ((rc = encode_readback(w, stream, desc, E)) != SPLITZIP_OK)
-        return rc;
-    for (uint32_t i = 0; i < n_seg; ++i) {
-        segs[i].n_escapes = E[i];
-        segs[i].compressed_bytes = stream_bytes(codec->elem, segs[i].n, codec->chunk_size, E[i]);
-        if (E[i] > segs[i].esc_capacity && rc == SPLITZIP_OK)
-            rc = fail(SPLITZIP_E_CAPACITY, "segment %u has %llu escapes, capacity %llu", i,
-                      (unsigned long long)E[i], (unsigned long long)segs[i].esc_capacity);
-    }
-    return rc;
+    });
 }
 
 int splitzip_encode_packed(splitzip_codec *codec, uint32_t n_seg, splitzip_packed *segs,
                            void *stream_, uint64_t *d_result)
 {
-    g_last_error.clear();
-    if (d_result && !aligned(d_result, 8))
-        return fail(SPLITZIP_E_INVALID, "d_result not 8-byte aligned");
-    int rc = codec_check(codec);
-    if (rc != SPLITZIP_OK)
+    return guarded([&]() -> int {
+        g_last_error[0] = '\0';
+        if (d_result && !aligned(d_result, 8))
+            return fail(SPLITZIP_E_INVALID, "d_result not 8-byte aligned");
+        int rc = codec_check(codec);
+        if (rc != SPLITZIP_OK)
+            return rc;
+        std::vector<sz::SegDesc> desc;
+        std::vector<uint32_t> tiles;
+        if ((rc = prepare_packed(codec, n_seg, segs, true, desc, tiles)) != SPLITZIP_OK)
+            return rc;
+        DeviceGuard dg(codec->device);
+        if (dg.err != hipSuccess)
+            return fail_hip(dg.err, "hipSetDevice");
+        hipStream_t stream = static_cast<hipStream_t>(stream_);
+        Workspace *ws = nullptr;
+        if ((rc = get_workspace(codec, stream, &ws)) != SPLITZIP_OK)
+            return rc;
+        std::lock_guard<std::mutex> lock(ws->mu);
+        Workspace *w = nullptr;
+        rc = encode_launch(codec, desc, tiles, common_book_packed(n_seg, segs), true, stream, d_result, &w);
+        if (rc != SPLITZIP_OK || d_result)
+            return rc;
+        std::vector<uint64_t> E;
+        if ((rc = encode_readback(w, stream, desc, E)) != SPLITZIP_OK)
+            return rc;
+        for (uint32_t i = 0; i < n_seg; ++i) {
+            segs[i].n_escapes = E[i];
+            segs[i].stream_bytes = stream_bytes(codec->elem, segs[i].n, codec->chunk_size, E[i]);
+            if (segs[i].stream_bytes > segs[i].buf_bytes && rc == SPLITZIP_OK)
+                rc = fail(SPLITZIP_E_CAPACITY, "segment %u needs %llu stream bytes, buffer holds %llu", i,
+                          (unsigned long long)segs[i].stream_bytes, (unsigned long long)segs[i].buf_bytes);
+        }
         return rc;
-    std::vector<sz::SegDesc> desc;
-    std::vector<uint32_t> tiles;
-    if ((rc = prepare_packed(codec, n_seg, segs, true, desc, tiles)) != SPLITZIP_OK)
-        return rc;
-    DeviceGuard dg(codec->device);
-    if (dg.err != hipSuccess)
-        return fail_hip(dg.err, "hipSetDevice");
-    hipStream_t stream = static_cast<hipStream_t>(stream_);
-    Workspace *ws = nullptr;
-    if ((rc = get_workspace(codec, stream, &ws)) != SPLITZIP_OK)
-        return rc;
-    std::lock_guard<std::mutex> lock(ws->mu);
-    Workspace *w = nullptr;
-    rc = encode_launch(codec, desc, tiles, common_book_packed(n_seg, segs), true, stream, d_result, &w);
-    if (rc != SPLITZIP_OK || d_result)
-        return rc;
-    std::vector<uint64_t> E;
-    if ((rc = encode_readback(w, stream, desc, E)) != SPLITZIP_OK)
-        return rc;
-    for (uint32_t i = 0; i < n_seg; ++i) {
-        segs[i].n_escapes = E[i];
-        segs[i].stream_bytes = stream_bytes(codec->elem, segs[i].n, codec->chunk_size, E[i]);
-        if (segs[i].stream_bytes > segs[i].buf_bytes && rc == SPLITZIP_OK)
-            rc = fail(SPLITZIP_E_CAPACITY, "segment %u needs %llu stream bytes, buffer holds %llu", i,
-                      (unsigned long long)segs[i].stream_bytes, (unsigned long long)segs[i].buf_bytes);
-    }
-    return rc;
+    });
 }
 
 }  // extern "C"
@@ -1161,101 +1204,111 @@ extern "C" {
 int splitzip_decode(splitzip_codec *codec, uint32_t n_seg, const splitzip_segment *segs,
                     void *stream_, uint32_t *d_error)
 {
-    g_last_error.clear();
-    int rc = codec_check(codec);
-    if (rc != SPLITZIP_OK)
-        return rc;
-    std::vector<sz::SegDesc> desc;
-    std::vector<uint32_t> tiles;
-    if ((rc = prepare_segments(codec, n_seg, segs, false, desc, tiles)) != SPLITZIP_OK)
-        return rc;
-    return decode_launch(codec, desc, tiles, common_book(n_seg, segs), static_cast<hipStream_t>(stream_),
-                         d_error);
+    return guarded([&]() -> int {
+        g_last_error[0] = '\0';
+        int rc = codec_check(codec);
+        if (rc != SPLITZIP_OK)
+            return rc;
+        std::vector<sz::SegDesc> desc;
+        std::vector<uint32_t> tiles;
+        if ((rc = prepare_segments(codec, n_seg, segs, false, desc, tiles)) != SPLITZIP_OK)
+            return rc;
+        return decode_launch(codec, desc, tiles, common_book(n_seg, segs), static_cast<hipStream_t>(stream_),
+                             d_error);
+    });
 }
 
 int splitzip_decode_packed(splitzip_codec *codec, uint32_t n_seg, const splitzip_packed *segs,
                            void *stream_, uint32_t *d_error)
 {
-    g_last_error.clear();
-    int rc = codec_check(codec);
-    if (rc != SPLITZIP_OK)
-        return rc;
-    std::vector<sz::SegDesc> desc;
-    std::vector<uint32_t> tiles;
-    if ((rc = prepare_packed(codec, n_seg, segs, false, desc, tiles)) != SPLITZIP_OK)
-        return rc;
-    // each stream's codebook comes from its own header (read by the kernel)
-    return decode_launch(codec, desc, tiles, 0, static_cast<hipStream_t>(stream_), d_error);
+    return guarded([&]() -> int {
+        g_last_error[0] = '\0';
+        int rc = codec_check(codec);
+        if (rc != SPLITZIP_OK)
+            return rc;
+        std::vector<sz::SegDesc> desc;
+        std::vector<uint32_t> tiles;
+        if ((rc = prepare_packed(codec, n_seg, segs, false, desc, tiles)) != SPLITZIP_OK)
+            return rc;
+        // each stream's codebook comes from its own header (read by the kernel)
+        return decode_launch(codec, desc, tiles, 0, static_cast<hipStream_t>(stream_), d_error);
+    });
 }
 
 int splitzip_set_small_tiles(splitzip_codec *codec, uint32_t max_tiles)
 {
-    g_last_error.clear();
-    int rc = codec_check(codec);
-    if (rc != SPLITZIP_OK)
-        return rc;
-    if (max_tiles > sz::kSmallTiles)
-        return fail(SPLITZIP_E_INVALID, "max_tiles %u exceeds %u", max_tiles, sz::kSmallTiles);
-    codec->small_tiles.store(max_tiles, std::memory_order_relaxed);
-    return SPLITZIP_OK;
+    return guarded([&]() -> int {
+        g_last_error[0] = '\0';
+        int rc = codec_check(codec);
+        if (rc != SPLITZIP_OK)
+            return rc;
+        if (max_tiles > sz::kSmallTiles)
+            return fail(SPLITZIP_E_INVALID, "max_tiles %u exceeds %u", max_tiles, sz::kSmallTiles);
+        codec->small_tiles.store(max_tiles, std::memory_order_relaxed);
+        return SPLITZIP_OK;
+    });
 }
 
 int splitzip_profile(splitzip_codec *codec, int enable)
 {
-    g_last_error.clear();
-    int rc = codec_check(codec);
-    if (rc != SPLITZIP_OK)
-        return rc;
-    DeviceGuard dg(codec->device);
-    std::vector<Workspace *> all;
-    {
-        // workspace locks are taken without the codec lock held (calls hold them the other
-        // way round)
-        std::lock_guard<std::mutex> lock(codec->mu);
-        codec->profiling = enable != 0;
-        for (auto &kv : codec->ws)
-            all.push_back(kv.second.get());
-    }
-    if (!enable) {
-        for (Workspace *w : all) {
-            std::lock_guard<std::mutex> wl(w->mu);
-            resolve_timings(w, true);
-            std::fill(w->sum_ms, w->sum_ms + SPLITZIP_KERNELS, 0.0);
-            std::fill(w->timed, w->timed + SPLITZIP_KERNELS, 0);
+    return guarded([&]() -> int {
+        g_last_error[0] = '\0';
+        int rc = codec_check(codec);
+        if (rc != SPLITZIP_OK)
+            return rc;
+        DeviceGuard dg(codec->device);
+        std::vector<Workspace *> all;
+        {
+            // workspace locks are taken without the codec lock held (calls hold them the other
+            // way round)
+            std::lock_guard<std::mutex> lock(codec->mu);
+            codec->profiling = enable != 0;
+            for (auto &kv : codec->ws)
+                all.push_back(kv.second.get());
         }
-    }
-    return SPLITZIP_OK;
+        if (!enable) {
+            for (Workspace *w : all) {
+                std::lock_guard<std::mutex> wl(w->mu);
+                resolve_timings(w, true);
+                std::fill(w->sum_ms, w->sum_ms + SPLITZIP_KERNELS, 0.0);
+                std::fill(w->timed, w->timed + SPLITZIP_KERNELS, 0);
+            }
+        }
+        return SPLITZIP_OK;
+    });
 }
 
 int splitzip_profile_read(splitzip_codec *codec, void *stream_, double *avg_ms, uint64_t *counts,
                           int reset)
 {
-    g_last_error.clear();
-    int rc = codec_check(codec);
-    if (rc != SPLITZIP_OK)
-        return rc;
-    if (!avg_ms || !counts)
-        return fail(SPLITZIP_E_INVALID, "avg_ms or counts is NULL");
-    DeviceGuard dg(codec->device);
-    if (dg.err != hipSuccess)
-        return fail_hip(dg.err, "hipSetDevice");
-    hipStream_t stream = static_cast<hipStream_t>(stream_);
-    Workspace *w = nullptr;
-    rc = get_workspace(codec, stream, &w);
-    if (rc != SPLITZIP_OK)
-        return rc;
-    std::lock_guard<std::mutex> lock(w->mu);
-    SZ_HIP(hipStreamSynchronize(stream), "hipStreamSynchronize");
-    resolve_timings(w, true);
-    for (int k = 0; k < SPLITZIP_KERNELS; ++k) {
-        counts[k] = w->timed[k];
-        avg_ms[k] = w->timed[k] ? w->sum_ms[k] / (double)w->timed[k] : 0.0;
-        if (reset) {
-            w->sum_ms[k] = 0.0;
-            w->timed[k] = 0;
+    return guarded([&]() -> int {
+        g_last_error[0] = '\0';
+        int rc = codec_check(codec);
+        if (rc != SPLITZIP_OK)
+            return rc;
+        if (!avg_ms || !counts)
+            return fail(SPLITZIP_E_INVALID, "avg_ms or counts is NULL");
+        DeviceGuard dg(codec->device);
+        if (dg.err != hipSuccess)
+            return fail_hip(dg.err, "hipSetDevice");
+        hipStream_t stream = static_cast<hipStream_t>(stream_);
+        Workspace *w = nullptr;
+        rc = get_workspace(codec, stream, &w);
+        if (rc != SPLITZIP_OK)
+            return rc;
+        std::lock_guard<std::mutex> lock(w->mu);
+        SZ_HIP(hipStreamSynchronize(stream), "hipStreamSynchronize");
+        resolve_timings(w, true);
+        for (int k = 0; k < SPLITZIP_KERNELS; ++k) {
+            counts[k] = w->timed[k];
+            avg_ms[k] = w->timed[k] ? w->sum_ms[k] / (double)w->timed[k] : 0.0;
+            if (reset) {
+                w->sum_ms[k] = 0.0;
+                w->timed[k] = 0;
+            }
         }
-    }
-    return SPLITZIP_OK;
+        return SPLITZIP_OK;
+    });
 }
 
 void splitzip_free(splitzip_codec *codec)
@@ -1304,89 +1357,95 @@ static uint64_t le_get(const uint8_t *p, int bytes)
 int splitzip_write_header(const splitzip_codec *codec, uint32_t book, uint64_t n,
                           uint64_t n_escapes, uint8_t out[SPLITZIP_HEADER_BYTES])
 {
-    g_last_error.clear();
-    int rc = codec_check(codec);
-    if (rc != SPLITZIP_OK)
-        return rc;
-    if (!out)
-        return fail(SPLITZIP_E_INVALID, "out is NULL");
-    if (book >= codec->n_books)
-        return fail(SPLITZIP_E_INVALID, "book %u, the codec has %u", book, codec->n_books);
-    std::memset(out, 0, SPLITZIP_HEADER_BYTES);
-    std::memcpy(out, "SZB1", 4);
-    le_put(out + 4, 1, 2);
-    le_put(out + 6, SPLITZIP_HEADER_BYTES, 2);
-    le_put(out + 8, codec->chunk_size, 4);
-    le_put(out + 12, codec->elem, 4);
-    le_put(out + 16, n, 8);
-    le_put(out + 24, ceil_div(n, codec->chunk_size), 8);
-    le_put(out + 32, n_escapes, 8);
-    std::memcpy(out + 40, codec->cbs.data() + 16 * (size_t)book, 16);
-    return SPLITZIP_OK;
+    return guarded([&]() -> int {
+        g_last_error[0] = '\0';
+        int rc = codec_check(codec);
+        if (rc != SPLITZIP_OK)
+            return rc;
+        if (!out)
+            return fail(SPLITZIP_E_INVALID, "out is NULL");
+        if (book >= codec->n_books)
+            return fail(SPLITZIP_E_INVALID, "book %u, the codec has %u", book, codec->n_books);
+        std::memset(out, 0, SPLITZIP_HEADER_BYTES);
+        std::memcpy(out, "SZB1", 4);
+        le_put(out + 4, 1, 2);
+        le_put(out + 6, SPLITZIP_HEADER_BYTES, 2);
+        le_put(out + 8, codec->chunk_size, 4);
+        le_put(out + 12, codec->elem, 4);
+        le_put(out + 16, n, 8);
+        le_put(out + 24, ceil_div(n, codec->chunk_size), 8);
+        le_put(out + 32, n_escapes, 8);
+        std::memcpy(out + 40, codec->cbs.data() + 16 * (size_t)book, 16);
+        return SPLITZIP_OK;
+    });
 }
 
 int splitzip_read_header(const uint8_t *buf, uint64_t total_len, uint64_t *n, uint32_t *chunk_size,
                          uint64_t *n_escapes, uint8_t codebook[16], uint32_t *elem)
 {
-    g_last_error.clear();
-    if (!buf)
-        return fail(SPLITZIP_E_INVALID, "buf is NULL");
-    if (total_len < SPLITZIP_HEADER_BYTES)
-        return fail(SPLITZIP_E_FORMAT, "stream shorter than its header");
-    if (std::memcmp(buf, "SZB1", 4) != 0)
-        return fail(SPLITZIP_E_FORMAT, "bad magic");
-    const uint64_t flags = le_get(buf + 12, 4);
-    if (le_get(buf + 4, 2) != 1 || le_get(buf + 6, 2) != SPLITZIP_HEADER_BYTES ||
-        (flags != sz::kElemBF16 && flags != sz::kElemE5M2))
-        return fail(SPLITZIP_E_FORMAT, "unsupported version, header size or flags");
-    for (int i = 56; i < 64; ++i)
-        if (buf[i])
-            return fail(SPLITZIP_E_FORMAT, "reserved header bytes are not zero");
-    const uint32_t c = (uint32_t)le_get(buf + 8, 4);
-    const uint64_t nn = le_get(buf + 16, 8), nch = le_get(buf + 24, 8), e = le_get(buf + 32, 8);
-    if (!chunk_size_ok(c) || nch != ceil_div(nn, c))
-        return fail(SPLITZIP_E_FORMAT, "bad chunk size or chunk count");
-    if (e > nn || total_len != stream_bytes((uint32_t)flags, nn, c, e))
-        return fail(SPLITZIP_E_FORMAT, "sizes do not match the stream length");
-    if (flags == sz::kElemE5M2)
-        for (int k = 0; k < 16; ++k)
-            if (buf[40 + k] > 31)
-                return fail(SPLITZIP_E_FORMAT, "E5M2 codebook entry %u is not a 5-bit exponent", buf[40 + k]);
-    if (n)
-        *n = nn;
-    if (chunk_size)
-        *chunk_size = c;
-    if (n_escapes)
-        *n_escapes = e;
-    if (codebook)
-        std::memcpy(codebook, buf + 40, 16);
-    if (elem)
-        *elem = (uint32_t)flags;
-    return SPLITZIP_OK;
+    return guarded([&]() -> int {
+        g_last_error[0] = '\0';
+        if (!buf)
+            return fail(SPLITZIP_E_INVALID, "buf is NULL");
+        if (total_len < SPLITZIP_HEADER_BYTES)
+            return fail(SPLITZIP_E_FORMAT, "stream shorter than its header");
+        if (std::memcmp(buf, "SZB1", 4) != 0)
+            return fail(SPLITZIP_E_FORMAT, "bad magic");
+        const uint64_t flags = le_get(buf + 12, 4);
+        if (le_get(buf + 4, 2) != 1 || le_get(buf + 6, 2) != SPLITZIP_HEADER_BYTES ||
+            (flags != sz::kElemBF16 && flags != sz::kElemE5M2))
+            return fail(SPLITZIP_E_FORMAT, "unsupported version, header size or flags");
+        for (int i = 56; i < 64; ++i)
+            if (buf[i])
+                return fail(SPLITZIP_E_FORMAT, "reserved header bytes are not zero");
+        const uint32_t c = (uint32_t)le_get(buf + 8, 4);
+        const uint64_t nn = le_get(buf + 16, 8), nch = le_get(buf + 24, 8), e = le_get(buf + 32, 8);
+        if (!chunk_size_ok(c) || nch != ceil_div(nn, c))
+            return fail(SPLITZIP_E_FORMAT, "bad chunk size or chunk count");
+        if (e > nn || total_len != stream_bytes((uint32_t)flags, nn, c, e))
+            return fail(SPLITZIP_E_FORMAT, "sizes do not match the stream length");
+        if (flags == sz::kElemE5M2)
+            for (int k = 0; k < 16; ++k)
+                if (buf[40 + k] > 31)
+                    return fail(SPLITZIP_E_FORMAT, "E5M2 codebook entry %u is not a 5-bit exponent", buf[40 + k]);
+        if (n)
+            *n = nn;
+        if (chunk_size)
+            *chunk_size = c;
+        if (n_escapes)
+            *n_escapes = e;
+        if (codebook)
+            std::memcpy(codebook, buf + 40, 16);
+        if (elem)
+            *elem = (uint32_t)flags;
+        return SPLITZIP_OK;
+    });
 }
 
 int splitzip_check_header(const splitzip_codec *codec, const uint8_t *buf, uint64_t total_len,
                           uint32_t *book)
 {
-    int rc = codec_check(codec);
-    if (rc != SPLITZIP_OK)
-        return rc;
-    uint32_t c = 0, elem = 0;
-    uint8_t cb[16];
-    rc = splitzip_read_header(buf, total_len, nullptr, &c, nullptr, cb, &elem);
-    if (rc != SPLITZIP_OK)
-        return rc;
-    if (elem != codec->elem)
-        return fail(SPLITZIP_E_CODEBOOK, "stream element type %u, the codec's is %u", elem, codec->elem);
-    if (c != codec->chunk_size)
-        return fail(SPLITZIP_E_CODEBOOK, "stream chunk size %u, the codec's is %u", c, codec->chunk_size);
-    for (uint32_t b = 0; b < codec->n_books; ++b)
-        if (std::memcmp(cb, codec->cbs.data() + 16 * (size_t)b, 16) == 0) {
-            if (book)
-                *book = b;
-            return SPLITZIP_OK;
-        }
-    return fail(SPLITZIP_E_CODEBOOK, "stream codebook is none of the codec's");
+    return guarded([&]() -> int {
+        int rc = codec_check(codec);
+        if (rc != SPLITZIP_OK)
+            return rc;
+        uint32_t c = 0, elem = 0;
+        uint8_t cb[16];
+        rc = splitzip_read_header(buf, total_len, nullptr, &c, nullptr, cb, &elem);
+        if (rc != SPLITZIP_OK)
+            return rc;
+        if (elem != codec->elem)
+            return fail(SPLITZIP_E_CODEBOOK, "stream element type %u, the codec's is %u", elem, codec->elem);
+        if (c != codec->chunk_size)
+            return fail(SPLITZIP_E_CODEBOOK, "stream chunk size %u, the codec's is %u", c, codec->chunk_size);
+        for (uint32_t b = 0; b < codec->n_books; ++b)
+            if (std::memcmp(cb, codec->cbs.data() + 16 * (size_t)b, 16) == 0) {
+                if (book)
+                    *book = b;
+                return SPLITZIP_OK;
+            }
+        return fail(SPLITZIP_E_CODEBOOK, "stream codebook is none of the codec's");
+    });
 }
 
 const char *splitzip_status_string(int status)
@@ -1403,6 +1462,6 @@ const char *splitzip_status_string(int status)
     }
 }
 
-const char *splitzip_last_error(void) { return g_last_error.c_str(); }
+const char *splitzip_last_error(void) { return g_last_error; }
 
 }  // extern "C"
