@@ -178,7 +178,7 @@ struct splitzip_codec {
     uint32_t magic = kCodecMagic;
     uint32_t elem = sz::kElemBF16;   // element type of every tensor the codec codes
     int device = 0;
-    bool profiling = false;
+    std::atomic<bool> profiling{false};   // set by splitzip_profile, read by every call
     std::atomic<uint32_t> small_tiles{sz::kSmallTiles};   // calls of at most this many tiles: pack + finish
     uint32_t chunk_size = 0;
     uint32_t log2_chunk = 0;
