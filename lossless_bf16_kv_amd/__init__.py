@@ -533,6 +533,7 @@ class Codec:
         self.coverage = None
         self.histogram = None
         self._escape_rate = 0.0
+        self._small_tiles = SMALL_TILES
 
     # -- state -----------------------------------------------------------------------
     @classmethod
@@ -560,9 +561,9 @@ class Codec:
         books = b"".join(bytes(b) for b in codebooks)
         with torch.cuda.device(c.device):
             if c.elem == ELEM_E5M2:
-                c.handle = splitzip_codec_from_codebooks_e5m2(books, chunk_size)
+                c._set_handle(splitzip_codec_from_codebooks_e5m2(books, chunk_size))
             else:
-                c.handle = splitzip_codec_from_codebooks(books, chunk_size)
+                c._set_handle(splitzip_codec_from_codebooks(books, chunk_size))
         return c
 
     def _elements(self, x):
@@ -576,15 +577,25 @@ class Codec:
         if not self.handle:
             raise SplitZipError(E_INVALID, "codec is not calibrated")
 
+    def _set_handle(self, h: int) -> None:
+        """Replace the C codec (a new calibration) and carry the launch setting over."""
+        splitzip_free(self.handle)
+        self.handle = h
+        if self._small_tiles != SMALL_TILES:
+            splitzip_set_small_tiles(h, self._small_tiles)
+
     def _stream(self) -> int:
         import torch
         return torch.cuda.current_stream(self.device).cuda_stream
 
     def set_small_tiles(self, max_tiles: int = SMALL_TILES) -> None:
         """Encodes of at most max_tiles tiles run two launches instead of four (same bytes);
-        0: always four."""
-        self._need_handle()
-        splitzip_set_small_tiles(self.handle, max_tiles)
+        0: always four.  Kept across later calibrations of this codec."""
+        if not 0 <= max_tiles <= SMALL_TILES:
+            raise SplitZipError(E_INVALID, f"max_tiles must be in [0, {SMALL_TILES}]")
+        if self.handle:
+            splitzip_set_small_tiles(self.handle, max_tiles)
+        self._small_tiles = max_tiles
 
     def profile(self, enable: bool = True) -> None:
         """Time every kernel launch of later calls with HIP events (see kernel_times)."""
@@ -614,8 +625,8 @@ class Codec:
         with torch.cuda.device(self.device):
             h, cov, hist = cal(w.data_ptr() if w.numel() else 0, w.numel(), self.chunk_size,
                                self._stream())
-        splitzip_free(self.handle)
-        self.handle, self.coverage, self.histogram = h, cov, hist
+        self._set_handle(h)
+        self.coverage, self.histogram = cov, hist
         self._escape_rate = 1.0 - cov if w.numel() else 0.0
         return cov
 
@@ -628,8 +639,8 @@ class Codec:
         with torch.cuda.device(self.device):
             h, cov, hist = cal([w.data_ptr() if w.numel() else 0 for w in ws], [w.numel() for w in ws],
                                self.chunk_size, self._stream())
-        splitzip_free(self.handle)
-        self.handle, self.coverage, self.histogram = h, cov, hist
+        self._set_handle(h)
+        self.coverage, self.histogram = cov, hist
         rates = [1.0 - c for c, w in zip(cov, ws) if w.numel()]
         self._escape_rate = max(rates) if rates else 0.0
         return cov

@@ -169,3 +169,19 @@ def test_launch_counts_and_limit():
     with pytest.raises(sz.SplitZipError) as e:
         codec.set_small_tiles(sz.SMALL_TILES + 1)
     assert e.value.status == sz.E_INVALID
+
+
+def test_setting_kept_across_calibrations():
+    """set_small_tiles before the first calibration, and every calibration makes a new C
+    codec: the setting applies to each."""
+    x = dev(workloads.normal_words(3 * TILE, 9))
+    codec = sz.Codec(DEV, 1024)
+    codec.set_small_tiles(0)
+    codec.calibrate(dev(workloads.normal_words(30_000, 10)))
+    codec.calibrate(dev(workloads.normal_words(30_000, 11)))
+    codec.profile(True)
+    codec.encode(x)
+    times = codec.kernel_times()
+    codec.profile(False)
+    assert times["encode_sums"][1] == times["encode_pack"][1] >= 1
+    assert times["encode_finish"][1] == 0
