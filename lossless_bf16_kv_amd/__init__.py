@@ -877,7 +877,6 @@ class PreparedBatch:
     another): the segment descriptors are built once."""
 
     def __init__(self, codec: Codec, xs, encs, outs=None):
-        import torch
         if len(xs) != len(encs) or (outs is not None and len(outs) != len(xs)):
             raise ValueError("xs, encs and outs must have the same length")
         self.codec = codec
@@ -896,12 +895,12 @@ class PreparedBatch:
                 if w.numel() != e.n:
                     raise ValueError("output size differs from the encoded tensor")
                 self._dec[i] = e.segment(w.data_ptr() if w.numel() else 0)
-        self._torch = torch
 
     def encode_async(self, result) -> None:
-        """Enqueue the encode; see Codec.encode_into_async and Codec.finish_async."""
-        with self._torch.cuda.device(self.codec.device):
-            splitzip_encode_async(self.codec.handle, self._enc, self.codec._stream(), result.data_ptr())
+        """Enqueue the encode; see Codec.encode_into_async and Codec.finish_async.  (The
+        library makes the codec's device current itself; the stream is the device's current
+        one.)"""
+        splitzip_encode_async(self.codec.handle, self._enc, self.codec._stream(), result.data_ptr())
 
     def finish(self, result) -> int:
         st = self.codec.finish_async(self.encs, result)
@@ -914,8 +913,7 @@ class PreparedBatch:
         """Enqueue the decode of the batch into its outputs (n_escapes as of the last finish)."""
         if self._dec is None:
             raise ValueError("no decode outputs were given")
-        with self._torch.cuda.device(self.codec.device):
-            splitzip_decode(self.codec.handle, self._dec, self.codec._stream(), d_error)
+        splitzip_decode(self.codec.handle, self._dec, self.codec._stream(), d_error)
 
 
 # ---- exponent statistics ----------------------------------------------------------------
@@ -945,7 +943,6 @@ class PreparedPackedBatch:
     non-blocking encodes into the same buffers and decodes from them."""
 
     def __init__(self, codec: Codec, xs, packed, outs=None):
-        import torch
         if len(xs) != len(packed) or (outs is not None and len(outs) != len(xs)):
             raise ValueError("xs, packed and outs must have the same length")
         self.codec, self.packed = codec, list(packed)
@@ -965,11 +962,9 @@ class PreparedPackedBatch:
                     raise ValueError("output size differs from the packed stream")
                 self._dec[i] = splitzip_packed(w.data_ptr() if p.n else None, p.n, p.buf.data_ptr(),
                                                p.stream_bytes, 0, 0, 0, 0)
-        self._torch = torch
 
     def encode_async(self, result) -> None:
-        with self._torch.cuda.device(self.codec.device):
-            splitzip_encode_packed(self.codec.handle, self._enc, self.codec._stream(), result.data_ptr())
+        splitzip_encode_packed(self.codec.handle, self._enc, self.codec._stream(), result.data_ptr())
 
     def finish(self, result) -> int:
         """Read E per stream (synchronizes); E_CAPACITY if a stream outgrew its buffer."""
@@ -989,5 +984,4 @@ class PreparedPackedBatch:
     def decode(self, d_error: int = 0) -> None:
         if self._dec is None:
             raise ValueError("no decode outputs were given")
-        with self._torch.cuda.device(self.codec.device):
-            splitzip_decode_packed(self.codec.handle, self._dec, self.codec._stream(), d_error)
+        splitzip_decode_packed(self.codec.handle, self._dec, self.codec._stream(), d_error)
