@@ -164,8 +164,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
-                                   "(segments shard across GPUs with no exchange, see DESIGN.md)"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus must be 1 (segments "
+                                   "shard across GPUs with no exchange between them)"}))
         sys.exit(2)
 
     import numpy as np
