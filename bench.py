@@ -140,6 +140,66 @@ def cpu_baseline(segments, codebooks, chunk_size: int, sample_words: int, e5m2: 
             "encode_GBps": round(gb / t_enc, 4), "decode_GBps": round(gb / t_dec, 4)}
 
 
+def transfer_bench(args, codec, xs, books, wl, esize, coverage):
+    """Compressed against raw transfer of the tensors xs across the host link (one JSON line)."""
+    import torch
+    from lossless_bf16_kv_amd.transfer import TransferPlan
+    # the tensors as consecutive views of one pool on each side, as a KV pool holds them
+    sizes = [x.numel() for x in xs]
+    pool_in = torch.cat([x.view(-1) for x in xs])
+    pool_out = torch.empty_like(pool_in)
+    xs[:] = list(pool_in.split(sizes))
+    ys = list(pool_out.split(sizes))
+    # the sending buffers sized from the escape counts of a first encode
+    first = codec.encode_packed_batch(xs, books=books)
+    escapes = [p.n_escapes for p in first]
+    del first
+    plan = TransferPlan(codec, xs, ys, books, escapes=escapes)
+    n = sum(x.numel() for x in xs)
+    times = {True: [], False: []}
+    link = {}
+    for k in range(args.warmup + args.steps):
+        for compress in (True, False):        # interleaved
+            pool_out.zero_()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            link[compress] = plan.run(compress)
+            dt = time.perf_counter() - t0
+            assert all(torch.equal(x, y) for x, y in zip(xs, ys)), "transfer is not bitwise"
+            if k >= args.warmup:
+                times[compress].append(dt)
+    comp_s = sorted(times[True])[len(times[True]) // 2]
+    raw_s = sorted(times[False])[len(times[False]) // 2]
+    out = {
+        "metric": "KV transfer across the PCIe link (device to pinned host to device, pipelined per "
+                  "tensor): GB/s of " + ("E5M2" if esize == 1 else "BF16") + " moved, compressed",
+        "value": round(esize * n / comp_s / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(comp_s * 1e3, 3),
+        "higher_is_better": True,
+        "vs_baseline": None,
+        "dtype": "u8" if esize == 1 else "u16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "element": args.elem, "n_elements": n, "tensors": len(xs),
+                   "chunk_size": wl.chunk_size, "input_bytes": esize * n},
+        "raw_GBps": round(esize * n / raw_s / 1e9, 2),
+        "speedup": round(raw_s / comp_s, 4),
+        "ms": {"compressed_median": round(comp_s * 1e3, 3), "raw_median": round(raw_s * 1e3, 3),
+               "compressed_min": round(min(times[True]) * 1e3, 3), "raw_min": round(min(times[False]) * 1e3, 3)},
+        "link_bytes": {"compressed": link[True], "raw": link[False]},
+        "compression_ratio": round(link[False] / link[True], 5),
+        "n_escapes": sum(plan.n_escapes),
+        "coverage_calibration": coverage,
+        "timing": "wall clock of each whole transfer (all tensors), from the first encode to the "
+                  "last decode; median over the timed runs",
+        "round_trip_bitwise": True,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -158,6 +218,10 @@ def main():
     ap.add_argument("--scrub-mb", type=int, default=-1,
                     help="MiB read between timed steps to flush the 256 MB Infinity Cache "
                          "(default: 2048 when the input is under 1 GiB, else 0)")
+    ap.add_argument("--transfer", action="store_true",
+                    help="time the compressed, pipelined transfer of the input's tensors (the "
+                         "long-prefill KV: one per layer and K/V) across the PCIe link through "
+                         "pinned host memory against the raw transfer, instead of the codec")
     ap.add_argument("--cpu-sample-words", type=int, default=1 << 30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
@@ -179,6 +243,10 @@ def main():
     C = wl.chunk_size
 
     segments, cal_parts, books = wl.segments, [wl.calibration], None
+    if args.transfer and args.config == 3:
+        # one tensor per layer and K/V, as a serving stack would send them
+        tokens = wl.segments[0].size // (2 * args.layers * 1024)
+        segments = workloads_kv_parts(wl.segments[0], args.layers, tokens)
     if args.books == "layer-kv":
         if args.config != 3:
             raise SystemExit("--books layer-kv applies to the long-prefill KV workload (--config 3)")
@@ -197,6 +265,9 @@ def main():
     else:
         coverage = min(codec.calibrate_books(cals))
     del cals
+    if args.transfer:
+        transfer_bench(args, codec, xs, books, wl, esize, coverage)
+        return
     # exponent statistics of the input itself (one pass on the GPU)
     hist_in = np.sum(np.array(sz.histograms(xs, elem=args.elem), dtype=np.uint64), axis=0).tolist()
     stats_in = sz.exponent_stats(hist_in)
