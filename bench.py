@@ -171,8 +171,8 @@ def transfer_bench(args, codec, xs, books, wl, esize, coverage):
     comp_s = sorted(times[True])[len(times[True]) // 2]
     raw_s = sorted(times[False])[len(times[False]) // 2]
     out = {
-        "metric": "KV transfer across the PCIe link (device to pinned host to device, pipelined per "
-                  "tensor): GB/s of " + ("E5M2" if esize == 1 else "BF16") + " moved, compressed",
+        "metric": "KV transfer across the PCIe link (device to pinned host to device, spans of "
+                  "streams pipelined): GB/s of " + ("E5M2" if esize == 1 else "BF16") + " moved, compressed",
         "value": round(esize * n / comp_s / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
