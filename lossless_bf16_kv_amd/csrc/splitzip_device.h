@@ -126,13 +126,16 @@ __device__ __forceinline__ uint32_t xcd_tile(uint32_t b, uint32_t n_tiles)
 
 static inline uint32_t xcd_grid(uint32_t n_tiles) { return (n_tiles + kXcds - 1) / kXcds * kXcds; }
 
-// Segment that owns global tile t: largest s with tile_start[s] <= t.
-__device__ __forceinline__ uint32_t find_segment(const uint32_t *tile_start, uint32_t n_seg,
+// Segment that owns global tile t: the largest s with tile_start[s] <= t.
+// By one thread: a binary search over tile_start limited to the bracket
+// that seg_at gives (usually a single segment, so no load at all).
+__device__ __forceinline__ uint32_t find_segment(const uint32_t *tile_start, const uint32_t *seg_at,
                                                  uint32_t t)
 {
-    uint32_t lo = 0, hi = n_seg;
+    uint32_t lo = seg_at[t >> kSegAtShift];
+    uint32_t hi = seg_at[(t >> kSegAtShift) + 1] + 1;
     while (hi - lo > 1) {
-        uint32_t mid = (lo + hi) >> 1;
+        const uint32_t mid = (lo + hi) >> 1;
         if (tile_start[mid] <= t)
             lo = mid;
         else
@@ -141,14 +144,19 @@ __device__ __forceinline__ uint32_t find_segment(const uint32_t *tile_start, uin
     return lo;
 }
 
-// Segment of tile t, found by the whole workgroup with one round of independent loads (a
-// binary search would chain dependent ones): the number of s >= 1 with tile_start[s] <= t.
-// Call from uniform control flow; contains barriers.
-__device__ uint32_t find_segment_block(const uint32_t *tile_start, uint32_t n_seg, uint32_t t,
+// Segment of tile t, found by the whole workgroup: seg_at brackets it, and the segments
+// inside the bracket (usually none) are counted with one round of independent loads, the
+// number of s in the bracket with tile_start[s] <= t.  Call from uniform control flow with t
+// uniform; contains barriers when the bracket holds more than one segment.
+__device__ uint32_t find_segment_block(const uint32_t *tile_start, const uint32_t *seg_at, uint32_t t,
                                        uint32_t tid, uint32_t lane, uint32_t *s_cnt)
 {
+    const uint32_t s0 = seg_at[t >> kSegAtShift];
+    const uint32_t s1 = seg_at[(t >> kSegAtShift) + 1];
+    if (s0 == s1)
+        return s0;
     uint32_t c = 0;
-    for (uint32_t k = 1 + tid; k < n_seg; k += kThreads)
+    for (uint32_t k = s0 + 1 + tid; k <= s1; k += kThreads)
         c += tile_start[k] <= t ? 1u : 0u;
 #pragma unroll
     for (uint32_t d = 1; d < 64; d <<= 1)
@@ -156,17 +164,39 @@ __device__ uint32_t find_segment_block(const uint32_t *tile_start, uint32_t n_se
     if (lane == 0)
         s_cnt[tid >> 6] = c;
     __syncthreads();
-    uint32_t seg = 0;
+    uint32_t seg = s0;
     for (int w = 0; w < kWaves; ++w)
         seg += s_cnt[w];
     __syncthreads();
     return __builtin_amdgcn_readfirstlane(seg);
 }
 
-// Segment and first tile of global tile t (uniform when t is).
+// Index s of a sorted start array with starts[s] <= b < starts[s + 1], by the whole workgroup
+// with one round of loads over all n entries (the calibration histograms, where n is the
+// number of tensors).  Call from uniform control flow; contains barriers.
+__device__ uint32_t find_range_block(const uint32_t *starts, uint32_t n, uint32_t b, uint32_t tid,
+                                     uint32_t lane, uint32_t *s_cnt)
+{
+    uint32_t c = 0;
+    for (uint32_t k = 1 + tid; k < n; k += kThreads)
+        c += starts[k] <= b ? 1u : 0u;
+#pragma unroll
+    for (uint32_t d = 1; d < 64; d <<= 1)
+        c += shfl_u32(c, lane ^ d);
+    if (lane == 0)
+        s_cnt[tid >> 6] = c;
+    __syncthreads();
+    uint32_t r = 0;
+    for (int w = 0; w < kWaves; ++w)
+        r += s_cnt[w];
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(r);
+}
+
+// Segment of global tile t (uniform when t is).
 __device__ __forceinline__ uint32_t tile_segment(const EncodeArgs &a, uint32_t t)
 {
-    return a.n_seg > 1 ? find_segment(a.tile_start, a.n_seg, t) : 0u;
+    return a.n_seg > 1 ? find_segment(a.tile_start, a.seg_at, t) : 0u;
 }
 
 __device__ __forceinline__ uint32_t segment_first_tile(const EncodeArgs &a, uint32_t s)

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
     const uint32_t wave = tid >> 6;
     const uint32_t t = blockIdx.x;
 
-    const uint32_t s = a.n_seg > 1 ? find_segment_block(a.tile_start, a.n_seg, t, tid, lane, s_wave_total) : 0u;
+    const uint32_t s = a.n_seg > 1 ? find_segment_block(a.tile_start, a.seg_at, t, tid, lane, s_wave_total) : 0u;
     const SegDesc sd = segment_desc(a, s);
     const uint8_t *lut = a.multi_book ? a.lut + 256u * sd.book : a.lut;
     if (tid < 64)
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
     uint32_t first = 0;
     SegDesc sd = a.seg0;
     if (a.n_seg > 1) {
-        const uint32_t s = find_segment_block(a.tile_start, a.n_seg, t, tid, lane, s_cnt);
+        const uint32_t s = find_segment_block(a.tile_start, a.seg_at, t, tid, lane, s_cnt);
         first = a.tile_start[s];
         sd = a.segs[s];
     }

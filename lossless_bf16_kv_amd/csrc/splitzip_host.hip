@@ -114,11 +114,12 @@ struct DeviceGuard {
 // Descriptor tables of one ragged-batch launch, staged through pinned memory.
 struct Staging {
     sz::SegDesc *h_segs = nullptr;
-    uint32_t *h_tiles = nullptr;
+    uint32_t *h_tiles = nullptr;   // the n + 1 tile starts, then the coarse segment table
     sz::SegDesc *d_segs = nullptr;
     uint32_t *d_tiles = nullptr;
-    uint32_t cap = 0;
-    uint32_t n = 0;              // descriptors held (h_* and d_* have the same contents)
+    uint32_t cap = 0;              // descriptors
+    uint64_t tcap = 0;             // entries of h_tiles / d_tiles
+    uint32_t n = 0;                // descriptors held (h_* and d_* have the same contents)
     hipEvent_t done = nullptr;   // recorded after the last copy out of h_*
     bool used = false;
 };
@@ -478,22 +479,52 @@ int ensure_result(Workspace *w, uint32_t n_seg)
     return SPLITZIP_OK;
 }
 
-// Copy the descriptor tables of a ragged batch to the device through a pinned slot.  A
-// batch called again with the same buffers (the same tables) uses the device copy a slot
-// still holds: no copy is enqueued.  Slots are only rewritten by later calls on the same
-// stream, so a kernel that reads one has finished before the copy that replaces it runs.
+// Entries of the coarse segment table of a call with these tile starts: one per group of
+// 1 << kSegAtShift tiles, and the end of the last group's bracket (kernels read entries g and
+// g + 1 for the group g of a tile).
+uint64_t seg_at_entries(const std::vector<uint32_t> &tiles)
+{
+    const uint64_t n_tiles = tiles.back();
+    return ((n_tiles + (1u << sz::kSegAtShift) - 1) >> sz::kSegAtShift) + 1;
+}
+
+// The coarse segment table: entry g = the segment holding tile g << kSegAtShift, then the
+// last segment.
+void build_seg_at(const std::vector<uint32_t> &tiles, uint32_t *out)
+{
+    const uint32_t n_seg = (uint32_t)tiles.size() - 1;
+    const uint64_t n_tiles = tiles[n_seg];
+    uint32_t s = 0;
+    uint64_t g = 0;
+    for (; (g << sz::kSegAtShift) < n_tiles; ++g) {
+        const uint64_t t = g << sz::kSegAtShift;
+        while (s + 1 < n_seg && tiles[s + 1] <= t)
+            ++s;
+        out[g] = s;
+    }
+    out[g] = n_seg - 1;
+}
+
+// Copy the descriptor tables of a ragged batch to the device through a pinned slot: the
+// descriptors, the tile starts and the coarse segment table.  A batch called again with the
+// same buffers (the same tables) uses the device copy a slot still holds: no copy is
+// enqueued.  Slots are only rewritten by later calls on the same stream, so a kernel that
+// reads one has finished before the copy that replaces it runs.
 int stage_descriptors(Workspace *w, const std::vector<sz::SegDesc> &segs,
                       const std::vector<uint32_t> &tiles, const sz::SegDesc **d_segs,
-                      const uint32_t **d_tiles)
+                      const uint32_t **d_tiles, const uint32_t **d_seg_at)
 {
     const uint32_t n = (uint32_t)segs.size();
+    // the coarse table follows from the tile starts, so equal starts mean an equal table
     for (const Staging &h : w->staging)
         if (h.used && h.n == n && std::memcmp(h.h_segs, segs.data(), n * sizeof(sz::SegDesc)) == 0 &&
             std::memcmp(h.h_tiles, tiles.data(), (n + 1) * sizeof(uint32_t)) == 0) {
             *d_segs = h.d_segs;
             *d_tiles = h.d_tiles;
+            *d_seg_at = h.d_tiles + n + 1;
             return SPLITZIP_OK;
         }
+    const uint64_t t_entries = n + 1 + seg_at_entries(tiles);
     Staging &s = w->staging[w->next_slot];
     w->next_slot = (w->next_slot + 1) % kStagingSlots;
     s.used = false;          // until the copy below is enqueued
@@ -501,34 +532,41 @@ int stage_descriptors(Workspace *w, const std::vector<sz::SegDesc> &segs,
         SZ_HIP(hipEventSynchronize(s.done), "hipEventSynchronize(staging)");
     if (s.cap < n) {
         (void)hipHostFree(s.h_segs);
-        (void)hipHostFree(s.h_tiles);
         (void)hipFree(s.d_segs);
-        (void)hipFree(s.d_tiles);
         s.h_segs = nullptr;
-        s.h_tiles = nullptr;
         s.d_segs = nullptr;
-        s.d_tiles = nullptr;
         s.cap = 0;
         const uint32_t cap = std::max<uint32_t>(n, 64);
         SZ_HIP(hipHostMalloc(&s.h_segs, cap * sizeof(sz::SegDesc), hipHostMallocDefault), "hipHostMalloc(descriptors)");
-        SZ_HIP(hipHostMalloc(&s.h_tiles, (cap + 1) * sizeof(uint32_t), hipHostMallocDefault), "hipHostMalloc(tiles)");
         SZ_HIP(hipMalloc(&s.d_segs, cap * sizeof(sz::SegDesc)), "hipMalloc(descriptors)");
-        SZ_HIP(hipMalloc(&s.d_tiles, (cap + 1) * sizeof(uint32_t)), "hipMalloc(tiles)");
         s.cap = cap;
+    }
+    if (s.tcap < t_entries) {
+        (void)hipHostFree(s.h_tiles);
+        (void)hipFree(s.d_tiles);
+        s.h_tiles = nullptr;
+        s.d_tiles = nullptr;
+        s.tcap = 0;
+        const uint64_t cap = std::max<uint64_t>(t_entries, 1024);
+        SZ_HIP(hipHostMalloc(&s.h_tiles, cap * sizeof(uint32_t), hipHostMallocDefault), "hipHostMalloc(tiles)");
+        SZ_HIP(hipMalloc(&s.d_tiles, cap * sizeof(uint32_t)), "hipMalloc(tiles)");
+        s.tcap = cap;
     }
     if (!s.done)
         SZ_HIP(hipEventCreateWithFlags(&s.done, hipEventDisableTiming), "hipEventCreate");
     std::memcpy(s.h_segs, segs.data(), n * sizeof(sz::SegDesc));
     std::memcpy(s.h_tiles, tiles.data(), (n + 1) * sizeof(uint32_t));
+    build_seg_at(tiles, s.h_tiles + n + 1);
     SZ_HIP(hipMemcpyAsync(s.d_segs, s.h_segs, n * sizeof(sz::SegDesc), hipMemcpyHostToDevice, w->stream),
            "hipMemcpyAsync(descriptors)");
-    SZ_HIP(hipMemcpyAsync(s.d_tiles, s.h_tiles, (n + 1) * sizeof(uint32_t), hipMemcpyHostToDevice, w->stream),
+    SZ_HIP(hipMemcpyAsync(s.d_tiles, s.h_tiles, t_entries * sizeof(uint32_t), hipMemcpyHostToDevice, w->stream),
            "hipMemcpyAsync(tiles)");
     SZ_HIP(hipEventRecord(s.done, w->stream), "hipEventRecord(staging)");
     s.n = n;
     s.used = true;
     *d_segs = s.d_segs;
     *d_tiles = s.d_tiles;
+    *d_seg_at = s.d_tiles + n + 1;
     return SPLITZIP_OK;
 }
 
@@ -962,7 +1000,7 @@ int encode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
 
     sz::EncodeArgs a{};
     a.seg0 = desc[0];
-    if (n_seg > 1 && (rc = stage_descriptors(w, desc, tiles, &a.segs, &a.tile_start)) != SPLITZIP_OK)
+    if (n_seg > 1 && (rc = stage_descriptors(w, desc, tiles, &a.segs, &a.tile_start, &a.seg_at)) != SPLITZIP_OK)
         return rc;
     uint8_t *res = d_result ? reinterpret_cast<uint8_t *>(d_result) : w->result;
     // one book for the whole call: its LUT directly; several: the table, indexed per segment
@@ -1174,7 +1212,7 @@ int decode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
             return rc;
         lock = std::unique_lock<std::mutex>(w->mu);
     }
-    if (n_seg > 1 && (rc = stage_descriptors(w, desc, tiles, &a.segs, &a.tile_start)) != SPLITZIP_OK)
+    if (n_seg > 1 && (rc = stage_descriptors(w, desc, tiles, &a.segs, &a.tile_start, &a.seg_at)) != SPLITZIP_OK)
         return rc;
     std::memcpy(a.cb, codec->cbs.data() + 16 * (book < 0 ? 0 : book), 16);
     a.cbs = codec->d_cbs;

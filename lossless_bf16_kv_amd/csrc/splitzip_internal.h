@@ -94,10 +94,16 @@ struct SegDesc {
     uint8_t *header;
 };
 
+// Several segments: seg_at[g] is the segment holding tile g << kSegAtShift, and the table
+// ends with the last segment (ceil(n_tiles / 2^kSegAtShift) + 1 entries), so tile t's
+// segment lies between seg_at[t >> kSegAtShift] and the entry after it.
+constexpr int kSegAtShift = 6;
+
 struct EncodeArgs {
     SegDesc seg0;                 // the only segment when n_seg == 1
     const SegDesc *segs;          // device table when n_seg > 1
     const uint32_t *tile_start;   // device [n_seg + 1] first tile of each segment
+    const uint32_t *seg_at;       // device, n_seg > 1: segment of every (1 << kSegAtShift)-th tile
     const uint8_t *lut;           // device inverse LUT (code, or kEscapeEntry): [256], or
                                   // [256 * books] indexed by SegDesc::book when multi_book.
                                   // BF16: by exponent.  E5M2: by element byte, with the
@@ -131,6 +137,7 @@ struct DecodeArgs {
     SegDesc seg0;
     const SegDesc *segs;
     const uint32_t *tile_start;
+    const uint32_t *seg_at;       // as in EncodeArgs, for the decode tiles
     uint32_t *err;                // optional
     const uint32_t *cbs;          // device [4 * books] codebooks, read when multi_book
     uint32_t cb[4];               // codebook bytes 0..15 as 4 little-endian words

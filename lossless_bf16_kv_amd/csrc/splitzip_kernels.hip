@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(const HistArgs a)
     HistSeg sg = a.seg0;
     uint32_t first = 0, nb = a.n_blocks;
     if (a.n_seg > 1) {
-        const uint32_t s = find_segment_block(a.block_start, a.n_seg, b, tid, lane, s_cnt);
+        const uint32_t s = find_range_block(a.block_start, a.n_seg, b, tid, lane, s_cnt);
         first = a.block_start[s];
         nb = a.block_start[s + 1] - first;
         sg = a.segs[s];
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
     const uint32_t wave = tid >> 6;
     const uint32_t t = blockIdx.x;
 
-    const uint32_t s = a.n_seg > 1 ? find_segment_block(a.tile_start, a.n_seg, t, tid, lane, s_wave_total) : 0u;
+    const uint32_t s = a.n_seg > 1 ? find_segment_block(a.tile_start, a.seg_at, t, tid, lane, s_wave_total) : 0u;
     const SegDesc sd = segment_desc(a, s);
     // the segment's inverse LUT (several codebooks in one call: one LUT per codebook)
     const uint8_t *lut = a.multi_book ? a.lut + 256u * sd.book : a.lut;
@@ -699,7 +699,7 @@ __global__ __launch_bounds__(kThreads) void encode_finish_kernel(const EncodeArg
     const uint32_t t = blockIdx.x;
     const uint64_t cmask = (1ull << a.log2_chunk) - 1;
 
-    const uint32_t s = a.n_seg > 1 ? find_segment_block(a.tile_start, a.n_seg, t, tid, lane, s_cnt) : 0u;
+    const uint32_t s = a.n_seg > 1 ? find_segment_block(a.tile_start, a.seg_at, t, tid, lane, s_cnt) : 0u;
     const SegDesc sd = segment_desc(a, s);
     const uint32_t first = segment_first_tile(a, s);
     const uint32_t end = segment_end_tile(a, s);
@@ -852,7 +852,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
     uint32_t first = 0;
     SegDesc sd = a.seg0;
     if (a.n_seg > 1) {
-        const uint32_t s = find_segment_block(a.tile_start, a.n_seg, t, tid, lane, s_cnt);
+        const uint32_t s = find_segment_block(a.tile_start, a.seg_at, t, tid, lane, s_cnt);
         first = a.tile_start[s];
         sd = a.segs[s];
     }
