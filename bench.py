@@ -26,10 +26,15 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
 
 
 def kernel_source_hash() -> str:
+    """Identifies the kernel code the counters were taken on: the device sources with
+    comments, trailing spaces and blank lines removed (a comment edit changes no kernel)."""
     h = hashlib.sha256()
     for name in ("splitzip_kernels.hip", "splitzip_e5m2.hip", "splitzip_device.h", "splitzip_internal.h"):
-        with open(os.path.join(ROOT, "lossless_bf16_kv_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "lossless_bf16_kv_amd", "csrc", name)) as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

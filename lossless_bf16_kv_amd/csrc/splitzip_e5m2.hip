@@ -8,7 +8,8 @@
 // packed into a little-endian bit stream (element i at bits 3i..3i+2); the exponent becomes
 // a 4-bit code into a top-16 codebook over the 32 exponent values, and exponents outside it
 // go to the same chunk-local escape stream as for BF16.  Codes, chunk offsets and escapes
-// have the BF16 layout, so the escape placement launches (sums, place, spill) are shared.
+// have the BF16 layout, so the escape placement launches (sums, place and spill, or finish)
+// are shared.
 //
 // Per lane, groups of 32 consecutive elements: their 32 fields fill 12 bytes (one 12-byte
 // store) and their codes 16 bytes (one 16-byte store), so each store instruction of a wave

@@ -15,8 +15,8 @@
 //   - encode: escape ranks inside a tile by a wave prefix of packed per-group counts plus
 //     an LDS prefix over the 4 waves; the tile's escapes go compacted to a scratch slot, and
 //     three small launches turn the per-tile counts into global offsets (segmented sums),
-//     move the escapes into place and move those of escape-heavy tiles, so no workgroup
-//     ever waits on another;
+//     move the escapes into place and move those of escape-heavy tiles (one launch for
+//     calls of at most kSmallTiles tiles), so no workgroup ever waits on another;
 //   - decode: codebook lookup with two v_perm_b32 byte selects per 4 codes (codebook in
 //     SGPRs), exponent bytes staged in LDS only for tiles that hold escapes, where the
 //     escapes overwrite them before the words are assembled.
