@@ -185,3 +185,33 @@ def test_setting_kept_across_calibrations():
     codec.profile(False)
     assert times["encode_sums"][1] == times["encode_pack"][1] >= 1
     assert times["encode_finish"][1] == 0
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("elem", ["bf16", "e5m2"])
+def test_many_tiny_segments(mode, elem):
+    """300 segments of 0 to 3 pack tiles (many empty or of a few elements) in one call: a
+    group of 64 tiles then holds many segments, so the lookup counts inside its bracket;
+    every stream equals the oracle's and decodes in one launch."""
+    rng = np.random.default_rng(4)
+    tile = TILE8 if elem == "e5m2" else TILE
+    sizes = []
+    for i in range(300):
+        kind = rng.integers(0, 4)
+        sizes.append(0 if kind == 0 else int(rng.integers(1, 40)) if kind == 1 else
+                     int(rng.integers(1, 3 * tile)))
+    C = 256
+    if elem == "e5m2":
+        xs_np = [workloads.e5m2_mixed(n, 900 + i, wide_fraction=0.05) for i, n in enumerate(sizes)]
+        codec = t8.codec_for(workloads.e5m2_normal(50_000, 6), C)
+        to_dev, check, back = t8.dev8, t8.assert_same_stream, (lambda y: t8.host(y, np.uint8))
+    else:
+        xs_np = [workloads.mixed_words(n, 900 + i, wide_fraction=0.05) for i, n in enumerate(sizes)]
+        codec = codec_for(workloads.normal_words(50_000, 6), C)
+        to_dev, check, back = dev, assert_same_stream, (lambda y: host(y, np.uint16))
+    codec.set_small_tiles(MODES[mode])
+    encs = codec.encode_batch([to_dev(x) for x in xs_np])
+    for x, e in zip(xs_np, encs):
+        check(codec, e, x)
+    for x, y in zip(xs_np, codec.decode_batch(encs)):
+        assert np.array_equal(back(y), x)
