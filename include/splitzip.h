@@ -354,17 +354,18 @@ int splitzip_exponent_stats(const uint64_t hist[256], double *entropy_bits, doub
 /* ceil(n / chunk_size); 0 for an invalid chunk size. */
 uint64_t splitzip_chunk_count(uint64_t n, uint32_t chunk_size);
 
-/* 64 + n + ceil(n/2) + 8 (n_chunks + 1) + 3 n_escapes; 0 for an invalid chunk size. */
+/* 64 + n + ceil(n/2) + 8 (n_chunks + 1) + 3 n_escapes; 0 for an invalid chunk size or for
+ * n or n_escapes not below 2^38 (the largest segment). */
 uint64_t splitzip_compressed_bytes(uint64_t n, uint32_t chunk_size, uint64_t n_escapes);
 
-/* E5M2 streams: 64 + ceil(3n/8) + ceil(n/2) + 8 (n_chunks + 1) + 3 n_escapes. */
+/* E5M2 streams: 64 + ceil(3n/8) + ceil(n/2) + 8 (n_chunks + 1) + 3 n_escapes; 0 as above. */
 uint64_t splitzip_e5m2_compressed_bytes(uint64_t n, uint32_t chunk_size, uint64_t n_escapes);
 
 /*
  * The canonical 64-byte stream header (little-endian): "SZB1", version u16 = 1,
  * header bytes u16 = 64, chunk_size u32, flags u32 = the codec's element type (0 BF16,
  * 1 E5M2), n u64, n_chunks u64, n_escapes u64, codebook[16] (that of `book`), 8 zero
- * bytes.
+ * bytes.  SPLITZIP_E_INVALID for n not below 2^38 or n_escapes above n.
  */
 int splitzip_write_header(const splitzip_codec *codec, uint32_t book, uint64_t n,
                           uint64_t n_escapes, uint8_t out[SPLITZIP_HEADER_BYTES]);
@@ -372,7 +373,8 @@ int splitzip_write_header(const splitzip_codec *codec, uint32_t book, uint64_t n
 /*
  * Parse a header; total_len is the full stream length (checked against the sizes of the
  * element type the flags name).  *elem receives that type.  Returns SPLITZIP_E_FORMAT for a
- * malformed header (including E5M2 codebook entries above 31).
+ * malformed header (including n not below 2^38, E above n and E5M2 codebook entries above
+ * 31).
  */
 int splitzip_read_header(const uint8_t *buf, uint64_t total_len, uint64_t *n,
                          uint32_t *chunk_size, uint64_t *n_escapes, uint8_t codebook[16],

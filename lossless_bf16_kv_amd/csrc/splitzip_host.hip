@@ -635,7 +635,8 @@ uint64_t tile_elements(const splitzip_codec *c, bool encode)
 // Canonical stream size of n elements with E escapes (0 for an invalid chunk size).
 uint64_t stream_bytes(uint32_t elem, uint64_t n, uint32_t chunk_size, uint64_t E)
 {
-    if (!chunk_size_ok(chunk_size))
+    // n and E below 2^38 keep every term, and the sum, far from 64-bit overflow
+    if (!chunk_size_ok(chunk_size) || n >= sz::kMaxSegmentWords || E >= sz::kMaxSegmentWords)
         return 0;
     const uint64_t sm = elem == sz::kElemE5M2 ? ceil_div(3 * n, 8) : n;
     return SPLITZIP_HEADER_BYTES + sm + ceil_div(n, 2) + 8 * (ceil_div(n, chunk_size) + 1) + 3 * E;
@@ -1404,6 +1405,9 @@ int splitzip_write_header(const splitzip_codec *codec, uint32_t book, uint64_t n
             return fail(SPLITZIP_E_INVALID, "out is NULL");
         if (book >= codec->n_books)
             return fail(SPLITZIP_E_INVALID, "book %u, the codec has %u", book, codec->n_books);
+        if (n >= sz::kMaxSegmentWords || n_escapes > n)
+            return fail(SPLITZIP_E_INVALID, "n = %llu (below 2^38) with %llu escapes (at most n)",
+                        (unsigned long long)n, (unsigned long long)n_escapes);
         std::memset(out, 0, SPLITZIP_HEADER_BYTES);
         std::memcpy(out, "SZB1", 4);
         le_put(out + 4, 1, 2);
@@ -1438,6 +1442,9 @@ int splitzip_read_header(const uint8_t *buf, uint64_t total_len, uint64_t *n, ui
                 return fail(SPLITZIP_E_FORMAT, "reserved header bytes are not zero");
         const uint32_t c = (uint32_t)le_get(buf + 8, 4);
         const uint64_t nn = le_get(buf + 16, 8), nch = le_get(buf + 24, 8), e = le_get(buf + 32, 8);
+        // before any size arithmetic: a larger n could wrap the size sum to the buffer length
+        if (nn >= sz::kMaxSegmentWords)
+            return fail(SPLITZIP_E_FORMAT, "n = %llu is not below 2^38", (unsigned long long)nn);
         if (!chunk_size_ok(c) || nch != ceil_div(nn, c))
             return fail(SPLITZIP_E_FORMAT, "bad chunk size or chunk count");
         if (e > nn || total_len != stream_bytes((uint32_t)flags, nn, c, e))

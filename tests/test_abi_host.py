@@ -270,3 +270,66 @@ def test_header_compiles_as_c_and_links(tmp_path):
     assert r.returncode == 0, r.stderr
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0 and r.stdout.strip() == "ok", (r.returncode, r.stdout, r.stderr)
+
+
+# ---- header parsing of untrusted bytes ------------------------------------------------
+
+def exact_stream_bytes(elem: int, n: int, C: int, E: int) -> int:
+    """The canonical size in unbounded integers (no wrap-around)."""
+    sm = -(-3 * n // 8) if elem == 1 else n
+    return 64 + sm + -(-n // 2) + 8 * (-(-n // C) + 1) + 3 * E
+
+
+def header(n: int, C: int, E: int, flags: int = 0, cb: bytes = bytes(range(16))) -> bytes:
+    import struct
+    return (b"SZB1" + struct.pack("<HHII", 1, 64, C, flags) +
+            struct.pack("<QQQ", n % (1 << 64), (-(-n // C)) % (1 << 64), E % (1 << 64)) + cb + bytes(8))
+
+
+def test_read_header_rejects_sizes_that_wrap_around():
+    """n near 2^64 whose size sum wraps to a small buffer length must not parse."""
+    C = 65536
+    lo, hi = 0, 1 << 64
+    while hi - lo > 1:                        # smallest n whose true size reaches 2^64
+        mid = (lo + hi) // 2
+        lo, hi = (lo, mid) if exact_stream_bytes(0, mid, C, 0) >= 1 << 64 else (mid, hi)
+    n = hi + 700
+    wrapped = exact_stream_bytes(0, n, C, 0) % (1 << 64)
+    assert 64 < wrapped < 4096
+    buf = header(n, C, 0) + bytes(wrapped - 64)
+    with pytest.raises(sz.SplitZipError) as ei:
+        sz.splitzip_read_header(buf)
+    assert ei.value.status == sz.E_FORMAT
+    assert sz.splitzip_compressed_bytes(1 << 38, 1024, 0) == 0
+    assert sz.splitzip_compressed_bytes((1 << 38) - 16, 1024, 1 << 38) == 0
+    assert sz.splitzip_compressed_bytes((1 << 38) - 16, 1024, 5) == exact_stream_bytes(0, (1 << 38) - 16, 1024, 5)
+
+
+def test_read_header_fuzz():
+    """Random headers (valid ones with fields and lengths perturbed, huge n and E included):
+    every header the parser accepts is self-consistent in exact arithmetic."""
+    from hypothesis import given, settings, strategies as st
+
+    big = st.one_of(st.integers(0, 1 << 20), st.integers(0, (1 << 64) - 1),
+                    st.integers((1 << 38) - 4, (1 << 38) + 4))
+
+    @settings(max_examples=400, deadline=None, derandomize=True)
+    @given(n=big, e=big, c_log=st.integers(3, 17), flags=st.integers(0, 2),
+           extra=st.integers(-3, 3), flip=st.one_of(st.none(), st.integers(0, 63)))
+    def check(n, e, c_log, flags, extra, flip):
+        C = 1 << c_log
+        hdr = bytearray(header(n, C, e, flags, bytes(range(16))))
+        if flip is not None:
+            hdr[flip] ^= 0x01
+        length = max(0, min(exact_stream_bytes(flags, n % (1 << 64), C, e % (1 << 64)) + extra, 1 << 22))
+        buf = bytes(hdr) + bytes(max(0, length - 64))
+        try:
+            r = sz.splitzip_read_header(buf[:length] if length >= 64 else buf[:length])
+        except sz.SplitZipError as err:
+            assert err.status in (sz.E_FORMAT, sz.E_INVALID)
+            return
+        assert r["n"] < 1 << 38 and r["n_escapes"] <= r["n"]
+        assert r["elem"] in (0, 1) and 16 <= r["chunk_size"] <= 65536
+        assert exact_stream_bytes(r["elem"], r["n"], r["chunk_size"], r["n_escapes"]) == length
+
+    check()
