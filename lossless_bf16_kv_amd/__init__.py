@@ -872,6 +872,12 @@ class Codec:
         return self.decode(enc)
 
 
+# The class name of the codec the SplitZip README's *Codec API* shows, with the same
+# constructor (device, chunk_size), calibrate -> coverage, encode -> object with
+# compressed_bytes, and decode.
+ChunkLocalSplitZipGPU = Codec
+
+
 class PreparedBatch:
     """A batch whose device buffers stay fixed across calls (e.g. one serving step after
     another): the segment descriptors are built once."""

@@ -422,3 +422,21 @@ def test_descriptor_tables_reused_and_replaced():
             if k % 5 == 0:
                 for o_np, y in zip(other_np, codec.decode_batch(other)):
                     assert np.array_equal(host(y, np.uint16), o_np)
+
+
+def test_readme_codec_api_usage():
+    """The usage the SplitZip README's Codec API shows, under its class name: constructor
+    (device, chunk_size), calibrate -> coverage, encode -> object with compressed_bytes,
+    decode -> a tensor equal bit for bit, of the input's shape and dtype."""
+    torch.manual_seed(0)
+    x = torch.randn(1024, 4096, dtype=torch.bfloat16, device="cuda")
+    codec = sz.ChunkLocalSplitZipGPU(device="cuda", chunk_size=1024)
+    coverage = codec.calibrate(x)
+    encoded = codec.encode(x)
+    decoded = codec.decode(encoded)
+    assert torch.equal(x.view(torch.int16), decoded.view(torch.int16))
+    assert decoded.shape == x.shape and decoded.dtype == x.dtype
+    words = x.view(torch.int16).cpu().numpy().view(np.uint16).ravel()
+    cb, cov, _ = O.calibrate(words)
+    assert codec.codebook == bytes(cb) and coverage == cov
+    assert encoded.compressed_bytes == O.encode(words, np.frombuffer(bytes(cb), np.uint8), 1024)["compressed_bytes"]
