@@ -68,6 +68,10 @@ def load_workload(args):
         return workloads.cast_e5m2(load_workload(args_bf16), args.chunk_size)
     if args.config == 3:
         return workloads.config3(layers=args.layers, chunk_size=args.chunk_size)
+    if args.config == 1 and (args.rows or args.hidden_dim):
+        wl = workloads.config1(args.rows or 1024, args.hidden_dim or 4096)
+        wl.chunk_size = args.chunk_size
+        return wl
     if args.config == 4:
         return workloads.config4(chunk_size=args.chunk_size)
     wl = workloads.CONFIGS[args.config]()
@@ -208,10 +212,16 @@ def transfer_bench(args, codec, xs, books, wl, esize, coverage):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", "--iters", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--chunk-size", type=int, default=1024)
+    ap.add_argument("--rows", type=int, default=0,
+                    help="single N(0,1) tensor of [rows, hidden-dim] (selects --config 1)")
+    ap.add_argument("--hidden-dim", type=int, default=0, help="see --rows (default 4096)")
+    ap.add_argument("--calibrate-on-input", action="store_true",
+                    help="calibrate on the benchmark input itself instead of the workload's "
+                         "separate calibration draw")
     ap.add_argument("--layers", type=int, default=64, help="long-prefill KV layers (64 = 8.6 GB)")
     ap.add_argument("--books", choices=["one", "layer-kv"], default="one",
                     help="one codebook for the whole input, or (long-prefill KV) one per layer "
@@ -231,6 +241,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
     args = ap.parse_args()
+    if args.rows or args.hidden_dim:
+        args.config = 1
 
     if args.gpus != 1:
         print(json.dumps({"error": "the benchmark runs on one GPU; --gpus must be 1 (segments "
@@ -243,6 +255,9 @@ def main():
 
     t_gen = time.perf_counter()
     wl = load_workload(args)
+    if args.calibrate_on_input:
+        wl.calibration = np.concatenate(wl.segments) if len(wl.segments) > 1 else wl.segments[0]
+        wl.description += "; calibrated on the input itself"
     t_gen = time.perf_counter() - t_gen
     dev = torch.device("cuda:0")
     C = wl.chunk_size

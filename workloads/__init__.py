@@ -83,7 +83,7 @@ class Workload:
 def config1(rows: int = 1024, hidden: int = 4096) -> Workload:
     x = bf16_bits(np.random.default_rng(0).standard_normal((rows, hidden), dtype=np.float32))
     cal = bf16_bits(np.random.default_rng(1).standard_normal((rows, hidden), dtype=np.float32))
-    return Workload("single_tensor_1024x4096_normal", [x.reshape(-1)], cal.reshape(-1), 1024,
+    return Workload(f"single_tensor_{rows}x{hidden}_normal", [x.reshape(-1)], cal.reshape(-1), 1024,
                     f"one [{rows},{hidden}] BF16 N(0,1) tensor (seed 0), calibrated on a "
                     f"separate N(0,1) draw (seed 1), chunk 1024")
 
