@@ -440,3 +440,66 @@ def test_readme_codec_api_usage():
     cb, cov, _ = O.calibrate(words)
     assert codec.codebook == bytes(cb) and coverage == cov
     assert encoded.compressed_bytes == O.encode(words, np.frombuffer(bytes(cb), np.uint8), 1024)["compressed_bytes"]
+
+
+def test_concurrent_host_threads_share_one_codec():
+    """Four host threads, each with its own stream, encode and decode different batches
+    (one and several segments, blocking and non-blocking) through one codec at the same
+    time (ctypes releases the GIL during the library calls), while a fifth thread switches
+    per-kernel timing on and off: every stream equals the oracle's and every round trip is
+    bitwise."""
+    import threading
+    codec = codec_for(workloads.normal_words(30000, 21), 256)
+    cb = np.frombuffer(codec.codebook, np.uint8)
+    errors = []
+
+    def work(tid):
+        try:
+            stream = torch.cuda.Stream(device=DEV)
+            with torch.cuda.stream(stream):
+                for it in range(12):
+                    sizes = [int(n) for n in np.random.default_rng(100 * tid + it).integers(0, 70_000, 1 + (it % 3))]
+                    xs_np = [workloads.mixed_words(n, 1000 * tid + 10 * it + k, wide_fraction=0.05)
+                             for k, n in enumerate(sizes)]
+                    xs = [dev(x) for x in xs_np]
+                    if it % 2:
+                        encs = codec.encode_batch(xs)
+                    else:
+                        encs = [codec.empty_encoded(x.numel(), escape_capacity=max(x.numel(), 1)) for x in xs]
+                        result = torch.zeros(1 + len(xs), dtype=torch.int64, device=DEV)
+                        codec.encode_into_async(xs, encs, result)
+                        stream.synchronize()
+                        assert codec.finish_async(encs, result) == sz.OK
+                    ys = codec.decode_batch(encs)
+                    stream.synchronize()
+                    for x_np, e, y in zip(xs_np, encs, ys):
+                        ref = O.encode(x_np, cb, 256)
+                        assert e.n_escapes == ref["n_escapes"]
+                        assert np.array_equal(host(e.chunk_off, np.uint64), ref["chunk_off"])
+                        assert np.array_equal(host(e.esc_pos, np.uint16), ref["esc_pos"])
+                        assert np.array_equal(host(y, np.uint16), x_np)
+        except Exception as ex:          # reported by the main thread
+            errors.append((tid, repr(ex)))
+
+    done = threading.Event()
+
+    def toggle_profiling():
+        # a fifth thread switches per-kernel timing on and off and reads its totals meanwhile
+        try:
+            while not done.is_set():
+                codec.profile(True)
+                codec.kernel_times()
+                codec.profile(False)
+        except Exception as ex:
+            errors.append(("profiling", repr(ex)))
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(4)]
+    prof = threading.Thread(target=toggle_profiling)
+    prof.start()
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    done.set()
+    prof.join()
+    assert not errors, errors
