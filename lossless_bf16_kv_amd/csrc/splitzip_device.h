@@ -97,8 +97,6 @@ __device__ __forceinline__ uint64_t wave_total_u64(uint64_t v, uint32_t lane)
     return v;
 }
 
-__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
-
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 {
     // v_perm_b32: selector byte s picks byte s of the 8-byte value {hi, lo} (s < 8).
@@ -213,7 +211,6 @@ __device__ __forceinline__ SegDesc segment_desc(const EncodeArgs &a, uint32_t s)
 {
     return a.n_seg > 1 ? a.segs[s] : a.seg0;
 }
-
 
 // ---- pack kernels: escape ranks inside a tile and where the tile's escapes go -----------
 
