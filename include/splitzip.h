@@ -147,12 +147,14 @@ int splitzip_calibrate_books(uint32_t n_books, const uint16_t *const *d_cal, con
                              double *coverage, uint64_t *hist);
 
 /* A codec from n_books known codebooks (host uint8[n_books * 16], book b at 16 b), each
- * 16 distinct exponents, bound to the current HIP device. */
+ * 16 distinct exponents, bound to the current HIP device (README "Highlights": codebooks
+ * calibrated offline; "Roadmap": codebook metadata that travels with the payload). */
 int splitzip_codec_from_codebooks(uint32_t n_books, const uint8_t *codebooks, uint32_t chunk_size,
                                   splitzip_codec **out_codec);
 
 /*
- * FP8 E5M2 codecs: as splitzip_calibrate, splitzip_calibrate_books and
+ * FP8 E5M2 codecs (README "FAQ" and arXiv abstract: the method applied on top of an FP8
+ * E5M2 KV cache): as splitzip_calibrate, splitzip_calibrate_books and
  * splitzip_codec_from_codebooks, for tensors of E5M2 bytes.  The codebook is the 16 of the
  * 32 exponent values ranked first by (count descending, exponent ascending); hist
  * (optional) receives 32 bins per book.  Known codebooks must hold 16 distinct values
@@ -166,18 +168,23 @@ int splitzip_calibrate_books_e5m2(uint32_t n_books, const uint8_t *const *d_cal,
 int splitzip_codec_from_codebooks_e5m2(uint32_t n_books, const uint8_t *codebooks, uint32_t chunk_size,
                                        splitzip_codec **out_codec);
 
-/* The element type a codec codes: SPLITZIP_ELEM_BF16 or SPLITZIP_ELEM_E5M2. */
+/* The element type a codec codes: SPLITZIP_ELEM_BF16 or SPLITZIP_ELEM_E5M2 (README "FAQ":
+ * BF16 and FP8 E5M2 KV caches). */
 int splitzip_codec_element(const splitzip_codec *codec, uint32_t *elem);
 
 /* Number of codebooks of a codec and (if codebooks != NULL) all of them, host
- * uint8[n_books * 16]. */
+ * uint8[n_books * 16] (README "Codec API": the codec's calibrated state). */
 int splitzip_codec_books(const splitzip_codec *codec, uint32_t *n_books, uint8_t *codebooks);
 
-/* Read back a codec's codebook (book 0), chunk size and device (any output may be NULL). */
+/* Read back a codec's codebook (book 0), chunk size and device (any output may be NULL;
+ * README "Codec API": the codec's calibrated state). */
 int splitzip_codec_info(const splitzip_codec *codec, uint8_t codebook[16], uint32_t *chunk_size,
                         int *device);
 
 /*
+ * Encode (README "Abstract" and "Highlights", arXiv abstract: each word's sign and mantissa
+ * kept exactly, its exponent as a 4-bit code into the codebook, exponents outside it in a
+ * chunk-local escape stream; README "Codec API": encode, then compressed_bytes).
  * Encode n_seg segments (host array `segs`) in one launch.  Blocks until each
  * segment's escape count is known, then fills n_escapes and compressed_bytes.
  * Returns SPLITZIP_E_CAPACITY if some segment has more escapes than esc_capacity:
@@ -190,7 +197,9 @@ int splitzip_codec_info(const splitzip_codec *codec, uint8_t codebook[16], uint3
 int splitzip_encode(splitzip_codec *codec, uint32_t n_seg, splitzip_segment *segs, void *stream);
 
 /*
- * Non-blocking encode: the same launches as splitzip_encode without the wait.  The
+ * Non-blocking encode (the encode of README "Codec API", left on the stream so that a
+ * transfer can follow it without a host round trip): the same launches as
+ * splitzip_encode without the wait.  The
  * kernels write into d_result (device, caller-owned, 1 + n_seg uint64 words):
  * d_result[1 + s] = E of segment s, and error bits are OR-ed into d_result[0] (the
  * caller zeroes it; bit 3 alone means some segment exceeded its escape capacity).
@@ -203,7 +212,9 @@ int splitzip_encode_async(splitzip_codec *codec, uint32_t n_seg, const splitzip_
                           void *stream, uint64_t *d_result);
 
 /*
- * Decode n_seg segments (host array `segs`, n_escapes as written by encode) into
+ * Decode (README "Abstract": the dense path looks each code up in the codebook, the sparse
+ * escape correction restores the other exponents; "Codec API": decode returns the tensor
+ * bit for bit).  Decode n_seg segments (host array `segs`, n_escapes as written by encode) into
  * their `data` buffers, in one launch.  Asynchronous: only enqueues work on `stream`.
  * The kernel never reads or writes outside the given sections even when the escape
  * metadata is corrupt; it then ORs a nonzero flag into *d_error (optional device
@@ -252,6 +263,7 @@ typedef struct splitzip_packed {
 } splitzip_packed;
 
 /*
+ * The encode of README "Codec API" into the portable form of README "Roadmap".
  * Encode n_seg tensors into packed streams in one launch sequence.  d_result == NULL:
  * blocking, fills stream_bytes and n_escapes, and returns SPLITZIP_E_CAPACITY if a stream
  * does not fit its buffer (its escapes are then not written; stream_bytes says how many
@@ -263,6 +275,8 @@ int splitzip_encode_packed(splitzip_codec *codec, uint32_t n_seg, splitzip_packe
                            void *stream, uint64_t *d_result);
 
 /*
+ * The decode of README "Codec API" from the portable form of README "Roadmap", with the
+ * codebook the stream carries.
  * Decode n_seg packed streams (buf, buf_bytes) into their data buffers, in one launch.
  * Asynchronous.  The host checks that buf_bytes fits a stream of n words (else
  * SPLITZIP_E_FORMAT); the kernel checks each header against n, the chunk size and the E
@@ -272,8 +286,9 @@ int splitzip_encode_packed(splitzip_codec *codec, uint32_t n_seg, splitzip_packe
 int splitzip_decode_packed(splitzip_codec *codec, uint32_t n_seg, const splitzip_packed *segs,
                            void *stream, uint32_t *d_error);
 
-/* Release a codec, its tables and workspaces (NULL is a no-op).  Work that uses the
- * codec must have completed; freeing its device memory synchronizes the device. */
+/* Release a codec, its tables and workspaces (NULL is a no-op; the end of the stateful
+ * codec object of README "Codec API").  Work that uses the codec must have completed;
+ * freeing its device memory synchronizes the device. */
 void splitzip_free(splitzip_codec *codec);
 
 /* ---- launch sequence of an encode ---- */
@@ -282,6 +297,8 @@ void splitzip_free(splitzip_codec *codec);
 #define SPLITZIP_SMALL_TILES 2048
 
 /*
+ * How the encode of README "Codec API" is launched; no page fixes it, and the bytes
+ * written are the same either way.
  * An encode call (any of the encode entry points) splits its segments into tiles of
  * 16384 BF16 words or 32768 E5M2 bytes, at least one per segment.  A call of at most
  * max_tiles tiles runs two kernel launches (pack, then finish: each tile's escape offset,
@@ -292,7 +309,8 @@ void splitzip_free(splitzip_codec *codec);
  */
 int splitzip_set_small_tiles(splitzip_codec *codec, uint32_t max_tiles);
 
-/* ---- per-kernel timing (for benchmarks and profilers) ---- */
+/* ---- per-kernel timing (for benchmarks and profilers: the codec throughput measurement
+ *      of README "Quick Start") ---- */
 
 /* Kernels whose durations splitzip_profile_read reports, in this order. */
 #define SPLITZIP_KERNEL_PACK 0    /* encode: split, pack, in-tile escape compaction      */
@@ -304,6 +322,7 @@ int splitzip_set_small_tiles(splitzip_codec *codec, uint32_t max_tiles);
 #define SPLITZIP_KERNELS 6
 
 /*
+ * Timing of the codec's kernels, which README "Quick Start" measures as codec throughput.
  * enable != 0: every later encode/decode call on this codec records HIP events around
  * each of its kernel launches, on the call's stream.  enable == 0 stops recording and
  * discards accumulated timings.
@@ -311,6 +330,7 @@ int splitzip_set_small_tiles(splitzip_codec *codec, uint32_t max_tiles);
 int splitzip_profile(splitzip_codec *codec, int enable);
 
 /*
+ * (README "Quick Start": codec throughput.)
  * Wait for `stream`, then report for each kernel kind the mean duration in ms and the
  * number of launches timed on that stream since profiling was enabled or last reset
  * (reset != 0 clears the totals after reading).  avg_ms and counts: host arrays of
@@ -323,7 +343,9 @@ int splitzip_profile_read(splitzip_codec *codec, void *stream, double *avg_ms, u
  *      Scripts": BF16 KV exponent entropy and top-16 coverage analysis) ---- */
 
 /*
- * Exponent histograms of n_seg BF16 tensors in one pass (two launches):
+ * Exponent histograms (README "Reproducing Paper Artifact Scripts": the exponent analysis;
+ * "Highlights": the histogram calibration takes offline) of n_seg BF16 tensors in one pass
+ * (two launches):
  * hist[256 s + e] = number of words of tensor s whose exponent field (bits 14..7) is e.
  * d_x and n are host arrays of n_seg device pointers (16-byte aligned) and word counts
  * (n[s] = 0 allowed).  hist is host memory; the call blocks until it is filled.  Scratch
@@ -332,8 +354,8 @@ int splitzip_profile_read(splitzip_codec *codec, void *stream, double *avg_ms, u
 int splitzip_histogram(uint32_t n_seg, const uint16_t *const *d_x, const uint64_t *n, void *stream,
                        uint64_t *hist);
 
-/* The same for n_seg tensors of E5M2 bytes: hist[32 s + e] = number of bytes of tensor s
- * whose exponent field (bits 6..2) is e. */
+/* The same for n_seg tensors of E5M2 bytes (README "FAQ": FP8 E5M2 KV caches):
+ * hist[32 s + e] = number of bytes of tensor s whose exponent field (bits 6..2) is e. */
 int splitzip_histogram_e5m2(uint32_t n_seg, const uint8_t *const *d_x, const uint64_t *n, void *stream,
                             uint64_t *hist);
 
@@ -351,17 +373,22 @@ int splitzip_exponent_stats(const uint64_t hist[256], double *entropy_bits, doub
 
 /* ---- host helpers (no device work) ---- */
 
-/* ceil(n / chunk_size); 0 for an invalid chunk size. */
+/* ceil(n / chunk_size), the chunk count of README "Highlights" (chunk-local escape
+ * metadata); 0 for an invalid chunk size. */
 uint64_t splitzip_chunk_count(uint64_t n, uint32_t chunk_size);
 
-/* 64 + n + ceil(n/2) + 8 (n_chunks + 1) + 3 n_escapes; 0 for an invalid chunk size or for
- * n or n_escapes not below 2^38 (the largest segment). */
+/* The compressed_bytes of README "Codec API": 64 + n + ceil(n/2) + 8 (n_chunks + 1) +
+ * 3 n_escapes; 0 for an invalid chunk size or for n or n_escapes not below 2^38 (the
+ * largest segment). */
 uint64_t splitzip_compressed_bytes(uint64_t n, uint32_t chunk_size, uint64_t n_escapes);
 
-/* E5M2 streams: 64 + ceil(3n/8) + ceil(n/2) + 8 (n_chunks + 1) + 3 n_escapes; 0 as above. */
+/* E5M2 streams (README "FAQ"): 64 + ceil(3n/8) + ceil(n/2) + 8 (n_chunks + 1) +
+ * 3 n_escapes; 0 as above. */
 uint64_t splitzip_e5m2_compressed_bytes(uint64_t n, uint32_t chunk_size, uint64_t n_escapes);
 
 /*
+ * The header that carries the codebook and payload metadata with a stream (README
+ * "Roadmap": portable transfer boundaries); its layout is this library's reading.
  * The canonical 64-byte stream header (little-endian): "SZB1", version u16 = 1,
  * header bytes u16 = 64, chunk_size u32, flags u32 = the codec's element type (0 BF16,
  * 1 E5M2), n u64, n_chunks u64, n_escapes u64, codebook[16] (that of `book`), 8 zero
@@ -371,6 +398,7 @@ int splitzip_write_header(const splitzip_codec *codec, uint32_t book, uint64_t n
                           uint64_t n_escapes, uint8_t out[SPLITZIP_HEADER_BYTES]);
 
 /*
+ * (README "Roadmap": the receiving side of a portable transfer boundary.)
  * Parse a header; total_len is the full stream length (checked against the sizes of the
  * element type the flags name).  *elem receives that type.  Returns SPLITZIP_E_FORMAT for a
  * malformed header (including n not below 2^38, E above n and E5M2 codebook entries above
@@ -390,9 +418,11 @@ int splitzip_read_header(const uint8_t *buf, uint64_t total_len, uint64_t *n,
 int splitzip_check_header(const splitzip_codec *codec, const uint8_t *buf, uint64_t total_len,
                           uint32_t *book);
 
+/* Error reporting of this ABI (no page defines it): a fixed description of a status. */
 const char *splitzip_status_string(int status);
 
-/* Message describing the last failing call on this host thread ("" if none). */
+/* Error reporting of this ABI (no page defines it): the message of the last failing call
+ * on this host thread ("" if none), valid until that thread's next call. */
 const char *splitzip_last_error(void);
 
 #ifdef __cplusplus
