@@ -75,6 +75,7 @@ void szo_histogram(const uint16_t *x, uint64_t m, uint64_t hist[256])
         hist[bf16_exponent(x[i])] += 1;
 }
 
+/* The top-16 codebook [README Highlights]; ties by the smaller exponent (this project's reading). */
 void szo_codebook(const uint64_t hist[256], uint8_t cb[16])
 {
     /* Rank the 256 exponent values by count, most frequent first; equal counts are
@@ -96,6 +97,7 @@ void szo_codebook(const uint64_t hist[256], uint8_t cb[16])
     }
 }
 
+/* The coverage that calibrate returns [README Codec API]. */
 double szo_coverage(const uint64_t hist[256], const uint8_t cb[16], uint64_t m)
 {
     uint64_t covered = 0;
@@ -216,6 +218,7 @@ static int escape_metadata_ok(const uint64_t *chunk_off, const uint16_t *esc_pos
     return 1;
 }
 
+/* Decode [README Abstract]: codebook lookup of every code, then the sparse escape correction. */
 int szo_decode(const uint8_t *sm, const uint8_t *codes, const uint64_t *chunk_off,
                const uint16_t *esc_pos, const uint8_t *esc_exp, uint64_t n, uint64_t n_escapes,
                const uint8_t cb[16], uint32_t chunk_size, uint16_t *y)
@@ -262,6 +265,7 @@ static uint64_t get_le(const uint8_t *p, int bytes)
     return v;
 }
 
+/* The canonical stream: header with the codebook, then the sections [README Roadmap]. */
 int szo_serialize(const uint8_t *sm, const uint8_t *codes, const uint64_t *chunk_off,
                   const uint16_t *esc_pos, const uint8_t *esc_exp, uint64_t n, uint64_t n_escapes,
                   const uint8_t cb[16], uint32_t chunk_size, uint8_t *out, uint64_t out_len)
@@ -308,6 +312,7 @@ int szo_serialize(const uint8_t *sm, const uint8_t *codes, const uint64_t *chunk
     return p == out_len ? SZO_OK : SZO_BAD_ARGUMENT;
 }
 
+/* Header of a canonical stream [README Roadmap: payload metadata that travels with it]. */
 int szo_stream_info(const uint8_t *buf, uint64_t len, uint64_t *n, uint32_t *chunk_size,
                     uint64_t *n_escapes, uint8_t cb[16])
 {
@@ -341,6 +346,7 @@ int szo_stream_info(const uint8_t *buf, uint64_t len, uint64_t *n, uint32_t *chu
     return SZO_OK;
 }
 
+/* Decode a stream with the codec's own codebook [README Codec API: same calibrated state]. */
 int szo_decode_stream(const uint8_t *buf, uint64_t len, const uint8_t cb[16], uint16_t *y,
                       uint64_t y_len)
 {
@@ -435,6 +441,7 @@ static void field3_set(uint8_t *s, uint64_t i, unsigned v)
     }
 }
 
+/* E5M2 exponent histogram [README FAQ], as szo_histogram. */
 void szo8_histogram(const uint8_t *x, uint64_t m, uint64_t hist[32])
 {
     uint64_t i;
@@ -445,6 +452,7 @@ void szo8_histogram(const uint8_t *x, uint64_t m, uint64_t hist[32])
         hist[e5m2_exponent(x[i])] += 1;
 }
 
+/* E5M2 top-16 codebook over the 32 exponent values [README FAQ], as szo_codebook. */
 void szo8_codebook(const uint64_t hist[32], uint8_t cb[16])
 {
     /* as for BF16, over the 32 exponent values: most frequent first, equal counts by the
@@ -466,6 +474,7 @@ void szo8_codebook(const uint64_t hist[32], uint8_t cb[16])
     }
 }
 
+/* E5M2 coverage [README FAQ, Codec API], as szo_coverage. */
 double szo8_coverage(const uint64_t hist[32], const uint8_t cb[16], uint64_t m)
 {
     uint64_t covered = 0;
@@ -477,6 +486,7 @@ double szo8_coverage(const uint64_t hist[32], const uint8_t cb[16], uint64_t m)
     return (double)covered / (double)m;
 }
 
+/* E5M2 stream size [README FAQ]: the 3-bit field stream replaces the sign+mantissa bytes. */
 uint64_t szo8_compressed_bytes(uint64_t n, uint32_t chunk_size, uint64_t n_escapes)
 {
     if (!chunk_size_ok(chunk_size))
@@ -485,6 +495,7 @@ uint64_t szo8_compressed_bytes(uint64_t n, uint32_t chunk_size, uint64_t n_escap
            3u * n_escapes;
 }
 
+/* E5M2 encode [README FAQ; arXiv abstract], in the order of szo_encode. */
 int szo8_encode(const uint8_t *x, uint64_t n, const uint8_t cb[16], uint32_t chunk_size,
                 uint8_t *sm3, uint8_t *codes, uint64_t *chunk_off, uint16_t *esc_pos,
                 uint8_t *esc_exp, uint64_t esc_capacity, uint64_t *n_escapes)
@@ -531,6 +542,7 @@ int szo8_encode(const uint8_t *x, uint64_t n, const uint8_t cb[16], uint32_t chu
     return E <= esc_capacity ? SZO_OK : SZO_NO_ROOM;
 }
 
+/* E5M2 decode [README FAQ], in the order of szo_decode. */
 int szo8_decode(const uint8_t *sm3, const uint8_t *codes, const uint64_t *chunk_off,
                 const uint16_t *esc_pos, const uint8_t *esc_exp, uint64_t n, uint64_t n_escapes,
                 const uint8_t cb[16], uint32_t chunk_size, uint8_t *y)
@@ -560,6 +572,7 @@ int szo8_decode(const uint8_t *sm3, const uint8_t *codes, const uint64_t *chunk_
     return SZO_OK;
 }
 
+/* E5M2 canonical stream [README FAQ, Roadmap], flags = 1. */
 int szo8_serialize(const uint8_t *sm3, const uint8_t *codes, const uint64_t *chunk_off,
                    const uint16_t *esc_pos, const uint8_t *esc_exp, uint64_t n, uint64_t n_escapes,
                    const uint8_t cb[16], uint32_t chunk_size, uint8_t *out, uint64_t out_len)
@@ -605,6 +618,7 @@ int szo8_serialize(const uint8_t *sm3, const uint8_t *codes, const uint64_t *chu
     return p == out_len ? SZO_OK : SZO_BAD_ARGUMENT;
 }
 
+/* Decode an E5M2 stream with the codec's own codebook [README FAQ, Codec API]. */
 int szo8_decode_stream(const uint8_t *buf, uint64_t len, const uint8_t cb[16], uint8_t *y,
                        uint64_t y_len)
 {
