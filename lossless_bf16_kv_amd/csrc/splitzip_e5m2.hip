@@ -389,43 +389,74 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
         }
         __syncthreads();
         uint8_t *bytes = reinterpret_cast<uint8_t *>(s_exp);
+        // the tile's escapes are the contiguous range [j0, j1), kPatch per thread and round;
+        // every load of a round goes out before its LDS writes (global pointers: the loads
+        // cannot alias LDS, so nothing holds them back)
+        constexpr int kPatch = 4;
+        const SZ_GLOBAL uint16_t *gpos = as_global(static_cast<const uint16_t *>(sd.esc_pos));
+        const SZ_GLOBAL uint8_t *gexp = as_global(static_cast<const uint8_t *>(sd.esc_exp));
         if (!sub_chunk) {
             for (uint64_t ci = tid; ci < nc; ci += kThreads)
                 if (s_off[ci] > s_off[ci + 1] && a.err)
                     atomicOr(a.err, kErrBadOffsets);
-            for (uint64_t jj = j0 + tid; jj < j1; jj += kThreads) {
-                uint32_t lo = 0, hi = (uint32_t)nc;          // s_off[lo] <= jj < s_off[hi]
-                while (hi - lo > 1) {
-                    const uint32_t mid = (lo + hi) >> 1;
-                    if (s_off[mid] <= jj)
-                        lo = mid;
-                    else
-                        hi = mid;
+            for (uint64_t jb = j0 + tid; jb < j1; jb += kPatch * kThreads) {
+                uint32_t pos[kPatch], ev[kPatch];
+#pragma unroll
+                for (int k = 0; k < kPatch; ++k) {
+                    const uint64_t jj = jb + (uint64_t)k * kThreads;
+                    if (jj < j1) {
+                        pos[k] = gpos[jj];
+                        ev[k] = gexp[jj];
+                    }
                 }
-                const uint64_t cstart = (c0 + lo) << log2c;
-                const uint64_t clen = n - cstart < C ? n - cstart : C;
-                const uint32_t pos = sd.esc_pos[jj];
-                const uint32_t e = sd.esc_exp[jj];
-                if (pos >= clen || e > 31u) {
-                    if (a.err)
-                        atomicOr(a.err, pos >= clen ? kErrBadPosition : kErrBadExponent);
-                    continue;
+#pragma unroll
+                for (int k = 0; k < kPatch; ++k) {
+                    const uint64_t jj = jb + (uint64_t)k * kThreads;
+                    if (jj >= j1)
+                        continue;
+                    uint32_t lo = 0, hi = (uint32_t)nc;      // s_off[lo] <= jj < s_off[hi]
+                    while (hi - lo > 1) {
+                        const uint32_t mid = (lo + hi) >> 1;
+                        if (s_off[mid] <= jj)
+                            lo = mid;
+                        else
+                            hi = mid;
+                    }
+                    const uint64_t cstart = (c0 + lo) << log2c;
+                    const uint64_t clen = n - cstart < C ? n - cstart : C;
+                    if (pos[k] >= clen || ev[k] > 31u) {
+                        if (a.err)
+                            atomicOr(a.err, pos[k] >= clen ? kErrBadPosition : kErrBadExponent);
+                        continue;
+                    }
+                    bytes[cstart + pos[k] - base] = (uint8_t)(ev[k] << 2);
                 }
-                bytes[cstart + pos - base] = (uint8_t)(e << 2);
             }
         } else {
             const uint64_t lo = base - (c0 << log2c);
             const uint64_t clen = n - (c0 << log2c) < C ? n - (c0 << log2c) : C;
-            for (uint64_t jj = j0 + tid; jj < j1; jj += kThreads) {
-                const uint32_t pos = sd.esc_pos[jj];
-                const uint32_t e = sd.esc_exp[jj];
-                if (pos >= clen || e > 31u) {
-                    if (a.err)
-                        atomicOr(a.err, pos >= clen ? kErrBadPosition : kErrBadExponent);
-                    continue;
+            for (uint64_t jb = j0 + tid; jb < j1; jb += kPatch * kThreads) {
+                uint32_t pos[kPatch], ev[kPatch];
+#pragma unroll
+                for (int k = 0; k < kPatch; ++k) {
+                    const uint64_t jj = jb + (uint64_t)k * kThreads;
+                    if (jj < j1) {
+                        pos[k] = gpos[jj];
+                        ev[k] = gexp[jj];
+                    }
                 }
-                if (pos >= lo && pos < lo + valid)
-                    bytes[pos - lo] = (uint8_t)(e << 2);
+#pragma unroll
+                for (int k = 0; k < kPatch; ++k) {
+                    if (jb + (uint64_t)k * kThreads >= j1)
+                        continue;
+                    if (pos[k] >= clen || ev[k] > 31u) {
+                        if (a.err)
+                            atomicOr(a.err, pos[k] >= clen ? kErrBadPosition : kErrBadExponent);
+                        continue;
+                    }
+                    if (pos[k] >= lo && pos[k] < lo + valid)
+                        bytes[pos[k] - lo] = (uint8_t)(ev[k] << 2);
+                }
             }
         }
         __syncthreads();

@@ -645,15 +645,17 @@ __global__ __launch_bounds__(kThreads) void encode_spill_kernel(const EncodeArgs
         const uint64_t off = a.tile_ovf[t];
         const uint64_t room = off < a.ovf_cap ? a.ovf_cap - off : 0;
         uint8_t *exps = a.packed ? packed_exps(sd, a.seg_total[s]) : sd.esc_exp;
-        // four loads in flight before the stores
-        constexpr int kBatch = 4;
+        // an overflow tile holds thousands of escapes: sixteen loads in flight per thread
+        // before the stores (global pointers, so the stores do not hold the next loads back)
+        constexpr int kBatch = 16;
+        const SZ_GLOBAL uint32_t *src = as_global(static_cast<const uint32_t *>(a.ovf + off));
         const uint32_t lim = cnt < room ? cnt : (uint32_t)room;
         for (uint32_t r0 = tid; r0 < lim; r0 += kBatch * kThreads) {
             uint32_t e[kBatch];
 #pragma unroll
             for (int k = 0; k < kBatch; ++k)
                 if (r0 + k * kThreads < lim)
-                    e[k] = a.ovf[off + r0 + k * kThreads];
+                    e[k] = src[r0 + k * kThreads];
 #pragma unroll
             for (int k = 0; k < kBatch; ++k) {
                 const uint32_t r = r0 + k * kThreads;
@@ -764,14 +766,17 @@ __global__ __launch_bounds__(kThreads) void encode_finish_kernel(const EncodeArg
         lim = 0;
     SZ_GLOBAL uint16_t *pos = as_global(lim ? sd.esc_pos + prefix : sd.esc_pos);
     SZ_GLOBAL uint8_t *ex = as_global(lim ? exps + prefix : exps);
-    for (uint32_t r0 = tid; r0 < lim; r0 += kBatch * kThreads) {
-        uint32_t e[kBatch];
+    // an overflow tile holds thousands of escapes: sixteen loads in flight per thread
+    constexpr int kOvfBatch = 16;
+    const SZ_GLOBAL uint32_t *gsrc = as_global(src);
+    for (uint32_t r0 = tid; r0 < lim; r0 += kOvfBatch * kThreads) {
+        uint32_t e[kOvfBatch];
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k)
+        for (int k = 0; k < kOvfBatch; ++k)
             if (r0 + k * kThreads < lim)
-                e[k] = src[r0 + k * kThreads];
+                e[k] = gsrc[r0 + k * kThreads];
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
+        for (int k = 0; k < kOvfBatch; ++k) {
             const uint32_t r = r0 + k * kThreads;
             if (r < lim) {
                 pos[r] = (uint16_t)((base + (e[k] & 0xFFFFu)) & cmask);
@@ -965,45 +970,77 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
         }
         __syncthreads();
         uint8_t *bytes = reinterpret_cast<uint8_t *>(s_exp);
+        // the tile's escapes are the contiguous range [j0, j1), kPatch per thread and round;
+        // every load of a round goes out before its LDS writes (global pointers: the loads
+        // cannot alias LDS, so nothing holds them back)
+        constexpr int kPatch = 4;
+        const SZ_GLOBAL uint16_t *gpos = as_global(static_cast<const uint16_t *>(sd.esc_pos));
+        const SZ_GLOBAL uint8_t *gexp = as_global(static_cast<const uint8_t *>(sd.esc_exp));
         if (!sub_chunk) {
-            // the tile's escapes are the contiguous range [j0, j1): one per thread and round;
             // escape jj belongs to the last chunk ci whose offset s_off[ci] <= jj
             for (uint64_t ci = tid; ci < nc; ci += kThreads)
                 if (s_off[ci] > s_off[ci + 1] && a.err)
                     atomicOr(a.err, kErrBadOffsets);
-            for (uint64_t jj = j0 + tid; jj < j1; jj += kThreads) {
-                uint32_t lo = 0, hi = (uint32_t)nc;          // s_off[lo] <= jj < s_off[hi]
-                while (hi - lo > 1) {
-                    const uint32_t mid = (lo + hi) >> 1;
-                    if (s_off[mid] <= jj)
-                        lo = mid;
-                    else
-                        hi = mid;
+            for (uint64_t jb = j0 + tid; jb < j1; jb += kPatch * kThreads) {
+                uint32_t pos[kPatch], ev[kPatch];
+#pragma unroll
+                for (int k = 0; k < kPatch; ++k) {
+                    const uint64_t jj = jb + (uint64_t)k * kThreads;
+                    if (jj < j1) {
+                        pos[k] = gpos[jj];
+                        ev[k] = gexp[jj];
+                    }
                 }
-                const uint64_t cstart = (c0 + lo) << log2c;
-                const uint64_t clen = n - cstart < C ? n - cstart : C;
-                const uint32_t pos = sd.esc_pos[jj];
-                if (pos >= clen) {
-                    if (a.err)
-                        atomicOr(a.err, kErrBadPosition);
-                    continue;
+#pragma unroll
+                for (int k = 0; k < kPatch; ++k) {
+                    const uint64_t jj = jb + (uint64_t)k * kThreads;
+                    if (jj >= j1)
+                        continue;
+                    uint32_t lo = 0, hi = (uint32_t)nc;      // s_off[lo] <= jj < s_off[hi]
+                    while (hi - lo > 1) {
+                        const uint32_t mid = (lo + hi) >> 1;
+                        if (s_off[mid] <= jj)
+                            lo = mid;
+                        else
+                            hi = mid;
+                    }
+                    const uint64_t cstart = (c0 + lo) << log2c;
+                    const uint64_t clen = n - cstart < C ? n - cstart : C;
+                    if (pos[k] >= clen) {
+                        if (a.err)
+                            atomicOr(a.err, kErrBadPosition);
+                        continue;
+                    }
+                    const uint32_t p = (uint32_t)(cstart + pos[k] - base);
+                    bytes[(p >> 3) * 8 + (p & 1u) * 4 + ((p >> 1) & 3u)] = (uint8_t)ev[k];
                 }
-                const uint32_t p = (uint32_t)(cstart + pos - base);
-                bytes[(p >> 3) * 8 + (p & 1u) * 4 + ((p >> 1) & 3u)] = sd.esc_exp[jj];
             }
         } else {
             const uint64_t lo = base - (c0 << log2c);
             const uint64_t clen = n - (c0 << log2c) < C ? n - (c0 << log2c) : C;
-            for (uint64_t jj = j0 + tid; jj < j1; jj += kThreads) {
-                const uint32_t pos = sd.esc_pos[jj];
-                if (pos >= clen) {
-                    if (a.err)
-                        atomicOr(a.err, kErrBadPosition);
-                    continue;
+            for (uint64_t jb = j0 + tid; jb < j1; jb += kPatch * kThreads) {
+                uint32_t pos[kPatch], ev[kPatch];
+#pragma unroll
+                for (int k = 0; k < kPatch; ++k) {
+                    const uint64_t jj = jb + (uint64_t)k * kThreads;
+                    if (jj < j1) {
+                        pos[k] = gpos[jj];
+                        ev[k] = gexp[jj];
+                    }
                 }
-                if (pos >= lo && pos < lo + valid) {
-                    const uint32_t p = (uint32_t)(pos - lo);
-                    bytes[(p >> 3) * 8 + (p & 1u) * 4 + ((p >> 1) & 3u)] = sd.esc_exp[jj];
+#pragma unroll
+                for (int k = 0; k < kPatch; ++k) {
+                    if (jb + (uint64_t)k * kThreads >= j1)
+                        continue;
+                    if (pos[k] >= clen) {
+                        if (a.err)
+                            atomicOr(a.err, kErrBadPosition);
+                        continue;
+                    }
+                    if (pos[k] >= lo && pos[k] < lo + valid) {
+                        const uint32_t p = (uint32_t)(pos[k] - lo);
+                        bytes[(p >> 3) * 8 + (p & 1u) * 4 + ((p >> 1) & 3u)] = (uint8_t)ev[k];
+                    }
                 }
             }
         }
