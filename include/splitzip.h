@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SPLITZIP_ABI_VERSION 4
+#define SPLITZIP_ABI_VERSION 5
 #define SPLITZIP_HEADER_BYTES 64
 #define SPLITZIP_MIN_CHUNK 16
 #define SPLITZIP_MAX_CHUNK 65536
@@ -308,6 +308,21 @@ void splitzip_free(splitzip_codec *codec);
  * larger values give SPLITZIP_E_INVALID.  Applies to calls that start after it returns.
  */
 int splitzip_set_small_tiles(splitzip_codec *codec, uint32_t max_tiles);
+
+/* Default of splitzip_set_stage_tiles. */
+#define SPLITZIP_STAGE_TILES 1024
+
+/*
+ * Which build of the pack kernel an encode call runs; no page fixes it, and the bytes
+ * written are the same either way.  A call of more than min_tiles tiles (tiles as for
+ * splitzip_set_small_tiles) runs the build in which a wave gathers a group's escapes in LDS
+ * and stores them as one contiguous run when there are more than 64 of them: much faster on
+ * escape-heavy inputs.  Smaller calls run the build without it, whose smaller code costs
+ * less when the call is short and its instructions are not yet in the caches.  Any value
+ * is accepted: 0 = always the gathering build, UINT32_MAX = never.  Applies to calls that
+ * start after it returns.
+ */
+int splitzip_set_stage_tiles(splitzip_codec *codec, uint32_t min_tiles);
 
 /* ---- per-kernel timing (for benchmarks and profilers: the codec throughput measurement
  *      of README "Quick Start") ---- */

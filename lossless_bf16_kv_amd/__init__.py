@@ -35,6 +35,7 @@ LIB_PATH = os.path.join(_HERE, "libsplitzip.so")
 OK, E_INVALID, E_NOMEM, E_DEVICE, E_CODEBOOK, E_FORMAT, E_CAPACITY = range(7)
 HEADER_BYTES = 64
 SMALL_TILES = 2048      # encodes of at most this many tiles run pack + finish (two launches)
+STAGE_TILES = 1024      # encodes of more tiles run the pack build that gathers escapes in LDS
 MIN_CHUNK, MAX_CHUNK = 16, 65536
 MAX_BOOKS = 4096
 ELEM_BF16, ELEM_E5M2 = 0, 1
@@ -117,6 +118,7 @@ def lib() -> ctypes.CDLL:
     L.splitzip_decode_packed.argtypes = [vp, u32, P(splitzip_packed), vp, vp]
     L.splitzip_profile.argtypes = [vp, i32]
     L.splitzip_set_small_tiles.argtypes = [vp, u32]
+    L.splitzip_set_stage_tiles.argtypes = [vp, u32]
     L.splitzip_profile_read.argtypes = [vp, vp, P(ctypes.c_double), P(u64), i32]
     L.splitzip_free.argtypes = [vp]
     L.splitzip_free.restype = None
@@ -138,7 +140,7 @@ def lib() -> ctypes.CDLL:
               "splitzip_decode_packed",
               "splitzip_encode", "splitzip_encode_async", "splitzip_decode",
               "splitzip_write_header", "splitzip_profile", "splitzip_profile_read",
-              "splitzip_set_small_tiles",
+              "splitzip_set_small_tiles", "splitzip_set_stage_tiles",
               "splitzip_read_header", "splitzip_check_header", "splitzip_calibrate_e5m2",
               "splitzip_calibrate_books_e5m2", "splitzip_codec_from_codebooks_e5m2",
               "splitzip_codec_element", "splitzip_histogram_e5m2"):
@@ -321,6 +323,10 @@ KERNELS = ("encode_pack", "encode_sums", "encode_place", "encode_spill", "decode
 
 def splitzip_set_small_tiles(codec: int, max_tiles: int) -> None:
     _check(lib().splitzip_set_small_tiles(codec, max_tiles))
+
+
+def splitzip_set_stage_tiles(codec: int, min_tiles: int) -> None:
+    _check(lib().splitzip_set_stage_tiles(codec, min_tiles))
 
 
 def splitzip_profile(codec: int, enable: bool) -> None:
@@ -534,6 +540,7 @@ class Codec:
         self.histogram = None
         self._escape_rate = 0.0
         self._small_tiles = SMALL_TILES
+        self._stage_tiles = STAGE_TILES
 
     # -- state -----------------------------------------------------------------------
     @classmethod
@@ -583,6 +590,8 @@ class Codec:
         self.handle = h
         if self._small_tiles != SMALL_TILES:
             splitzip_set_small_tiles(h, self._small_tiles)
+        if self._stage_tiles != STAGE_TILES:
+            splitzip_set_stage_tiles(h, self._stage_tiles)
 
     def _stream(self) -> int:
         import torch
@@ -596,6 +605,16 @@ class Codec:
         if self.handle:
             splitzip_set_small_tiles(self.handle, max_tiles)
         self._small_tiles = max_tiles
+
+    def set_stage_tiles(self, min_tiles: int = STAGE_TILES) -> None:
+        """Encodes of more than min_tiles tiles run the pack build that gathers escape-heavy
+        groups in LDS (same bytes; faster on escape-heavy inputs, larger code); 0: always,
+        2**32 - 1: never.  Kept across later calibrations of this codec."""
+        if not 0 <= min_tiles < 1 << 32:
+            raise SplitZipError(E_INVALID, "min_tiles must fit 32 bits")
+        if self.handle:
+            splitzip_set_stage_tiles(self.handle, min_tiles)
+        self._stage_tiles = min_tiles
 
     def profile(self, enable: bool = True) -> None:
         """Time every kernel launch of later calls with HIP events (see kernel_times)."""

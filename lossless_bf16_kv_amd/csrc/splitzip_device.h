@@ -223,7 +223,8 @@ __device__ __forceinline__ SegDesc segment_desc(const EncodeArgs &a, uint32_t s)
 template <int G>
 __device__ __forceinline__ void tile_escape_ranks(const uint32_t (&counts)[G], uint32_t lane,
                                                   uint32_t wave, uint32_t *s_wave_total,
-                                                  uint32_t (&rank)[G], uint32_t &tile_total)
+                                                  uint32_t (&rank)[G], uint32_t &tile_total,
+                                                  uint32_t &wave_end)
 {
     static_assert(G % 2 == 0, "groups are ranked in pairs");
     uint32_t wave_sum = 0;
@@ -252,6 +253,7 @@ __device__ __forceinline__ void tile_escape_ranks(const uint32_t (&counts)[G], u
 #pragma unroll
     for (int j = 0; j < G; ++j)
         rank[j] += wave_base;
+    wave_end = wave_base + wave_sum;
 }
 
 // Where tile t's escapes go: its slot of a.slot_escapes entries, or, past that, a range of
@@ -275,7 +277,10 @@ __device__ __forceinline__ uint32_t *tile_escape_dest(const EncodeArgs &a, uint3
                 atomicOr(a.err, kErrOverflowArea);
         }
         __syncthreads();
-        const uint64_t off = *s_ovf;
+        // the same in every lane: keep it in scalar registers
+        const uint64_t v = *s_ovf;
+        const uint64_t off = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32)
+                           | __builtin_amdgcn_readfirstlane((uint32_t)v);
         dst = a.ovf + off;
         room = off < a.ovf_cap ? a.ovf_cap - off : 0;
     }

@@ -16,8 +16,9 @@
 // covers one contiguous range.  The 32 input bytes of a lane (pack) and its 32 output bytes
 // (decode) would take two 16-byte accesses 32 bytes apart, which leave every cache line half
 // covered per instruction; they go through LDS instead, so that each global access
-// instruction of a wave covers 1 KiB contiguously.  All work is integer byte manipulation: no
-// floating point touches a value and no MFMA is used.
+// instruction of a wave covers 1 KiB contiguously.  For the same reason a group with many
+// escapes is gathered in LDS before its escape entries are stored.  All work is integer byte
+// manipulation: no floating point touches a value and no MFMA is used.
 #include "splitzip_device.h"
 
 namespace sz {
@@ -74,6 +75,7 @@ __device__ __forceinline__ void split_group32(const uint32_t (&x)[8], const uint
     flags = fl;
 }
 
+template <bool kStage>
 __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const EncodeArgs a)
 {
     constexpr int G = kE8EncGroups;
@@ -81,10 +83,11 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
     __shared__ uint32_t s_wave_total[kWaves];
     __shared__ uint64_t s_ovf;
     __shared__ uint4 s_in[kWaves][128];        // one 2048-byte group per wave, regrouped
+    __shared__ uint16_t s_stage[kWaves][2048];  // one group's escapes per wave (11-bit place, exponent)
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = lane_id();
-    const uint32_t wave = tid >> 6;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t t = blockIdx.x;
 
     const uint32_t s = a.n_seg > 1 ? find_segment_block(a.tile_start, a.seg_at, t, tid, lane, s_wave_total) : 0u;
@@ -111,42 +114,47 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
     uint64_t g0[G];
     uint32_t v[G][8];
     uint4 ld[G][2];
-    bool whole[G];
 #pragma unroll
     for (int j = 0; j < G; ++j) {
         const uint64_t gbase = base + ((uint64_t)(wave * G + j) << 11);
         g0[j] = gbase + (uint64_t)lane * kE8GroupElems;
-        whole[j] = gbase + 2048 <= n;                  // uniform in the wave
-        if (whole[j]) {
-            const uint8_t *src = reinterpret_cast<const uint8_t *>(sd.data) + gbase;
+        const uint8_t *src = reinterpret_cast<const uint8_t *>(sd.data) + gbase;
+        if (gbase + 2048 <= n) {                       // uniform in the wave
             ld[j][0] = load_stream16(src + 16 * lane);
             ld[j][1] = load_stream16(src + 1024 + 16 * lane);
         } else {
+            // the segment's last group: the same 16-byte pieces byte by byte, 0 past the end
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                uint32_t w = 0;
-                for (uint32_t k = 0; k < 4; ++k)
-                    if (g0[j] + 4 * m + k < n)
-                        w |= (uint32_t)xb[g0[j] + 4 * m + k] << (8 * k);
-                v[j][m] = w;
+            for (int h = 0; h < 2; ++h) {
+                uint32_t w[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    w[m] = 0;
+                    for (uint32_t k = 0; k < 4; ++k) {
+                        const uint64_t at = gbase + 1024u * h + 16u * lane + 4u * m + k;
+                        if (at < n)
+                            w[m] |= (uint32_t)xb[at] << (8 * k);
+                    }
+                }
+                ld[j][h] = make_uint4(w[0], w[1], w[2], w[3]);
             }
         }
     }
     __syncthreads();   // LUT in LDS
-    // Regroup, one group at a time through the wave's own buffer.  A wave's LDS accesses are
+    // Regroup, one group at a time through the wave's own buffer: lane l loaded bytes 16 l and
+    // 1024 + 16 l of the group and takes bytes 32 l .. 32 l + 31.  A wave's LDS accesses are
     // performed in the order it issues them, so the wavefront-scope fences (which keep the
     // compiler from reordering them) are all the ordering these exchanges need.
 #pragma unroll
-    for (int j = 0; j < G; ++j)
-        if (whole[j]) {
-            s_in[wave][lane] = ld[j][0];
-            s_in[wave][64 + lane] = ld[j][1];
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-            const uint4 lo = s_in[wave][2 * lane], hi = s_in[wave][2 * lane + 1];
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-            v[j][0] = lo.x; v[j][1] = lo.y; v[j][2] = lo.z; v[j][3] = lo.w;
-            v[j][4] = hi.x; v[j][5] = hi.y; v[j][6] = hi.z; v[j][7] = hi.w;
-        }
+    for (int j = 0; j < G; ++j) {
+        s_in[wave][lane] = ld[j][0];
+        s_in[wave][64 + lane] = ld[j][1];
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        const uint4 lo = s_in[wave][2 * lane], hi = s_in[wave][2 * lane + 1];
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        v[j][0] = lo.x; v[j][1] = lo.y; v[j][2] = lo.z; v[j][3] = lo.w;
+        v[j][4] = hi.x; v[j][5] = hi.y; v[j][6] = hi.z; v[j][7] = hi.w;
+    }
 
     // ---- a2: dense split and pack ---------------------------------------------------------
     uint32_t flags[G], counts[G];
@@ -185,9 +193,11 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
     // ---- a3: escape ranks inside the tile ---------------------------------------------------
     uint32_t rank[G];
     uint32_t tile_total;
-    tile_escape_ranks<G>(counts, lane, wave, s_wave_total, rank, tile_total);
+    uint32_t wave_end;
+    tile_escape_ranks<G>(counts, lane, wave, s_wave_total, rank, tile_total, wave_end);
     uint64_t room;
     uint32_t *dst = tile_escape_dest(a, t, tile_total, tid, &s_ovf, room);
+    SZ_GLOBAL uint32_t *gdst = as_global(dst);
 
     // escapes: (position inside the tile, exponent); tile-local chunk offsets (a chunk of 16
     // elements also starts in the middle of a group)
@@ -198,30 +208,69 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
             chunk_off[g0[j] >> a.log2_chunk] = r0;
         if (a.log2_chunk == 4 && g0[j] + 16 < n)
             chunk_off[(g0[j] + 16) >> 4] = r0 + __popc(flags[j] & 0xF0F0F0F0u);
+        // a wave's escapes of one group have consecutive ranks; more than kStageMin of them
+        // are gathered in the wave's LDS buffer (place inside the group in 11 bits, exponent
+        // in 5) and stored 64 consecutive entries per instruction: stored by the lanes that
+        // hold them, a lane's 32 elements put its escapes up to 32 entries apart, and one
+        // store instruction touched as many cache lines as the wave has lanes
+        const uint32_t w0 = __builtin_amdgcn_readfirstlane(r0);
+        const uint32_t wcnt = (j + 1 < G ? __builtin_amdgcn_readfirstlane(rank[j + 1]) : wave_end) - w0;
+        const bool staged = kStage && __builtin_expect(wcnt > kStageMin, 0);   // uniform in the wave
         if (flags[j]) {
             const uint32_t p0 = (uint32_t)(g0[j] - base);
             uint32_t r = r0;
+            if (staged) {
+                // place inside the group: the lane's first element is 32 lane
+                const uint32_t q0 = lane * kE8GroupElems;
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                uint32_t z = flags[j] & e8_flag_mask(d);
-                const uint64_t bytes8 = ((uint64_t)v[j][2 * d + 1] << 32) | v[j][2 * d];
-                while (z) {
-                    const uint32_t b = (uint32_t)__builtin_ctz(z);
-                    const uint32_t k = 2u * (b >> 3) + (b & 1u);          // element 8d + k
-                    const uint32_t e = (uint32_t)(bytes8 >> (8 * k + 2)) & 0x1Fu;
-                    if (r < room)
-                        dst[r] = (p0 + 8u * d + k) | (e << 16);
-                    ++r;
-                    z &= z - 1;
+                for (int d = 0; d < 4; ++d) {
+                    uint32_t z = flags[j] & e8_flag_mask(d);
+                    const uint64_t bytes8 = ((uint64_t)v[j][2 * d + 1] << 32) | v[j][2 * d];
+                    while (z) {
+                        const uint32_t b = (uint32_t)__builtin_ctz(z);
+                        const uint32_t k = 2u * (b >> 3) + (b & 1u);          // element 8d + k
+                        const uint32_t e = (uint32_t)(bytes8 >> (8 * k + 2)) & 0x1Fu;
+                        s_stage[wave][r - w0] = (uint16_t)((q0 + 8u * d + k) | (e << 11));
+                        ++r;
+                        z &= z - 1;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    uint32_t z = flags[j] & e8_flag_mask(d);
+                    const uint64_t bytes8 = ((uint64_t)v[j][2 * d + 1] << 32) | v[j][2 * d];
+                    while (z) {
+                        const uint32_t b = (uint32_t)__builtin_ctz(z);
+                        const uint32_t k = 2u * (b >> 3) + (b & 1u);          // element 8d + k
+                        const uint32_t e = (uint32_t)(bytes8 >> (8 * k + 2)) & 0x1Fu;
+                        if (r < room)
+                            gdst[r] = (p0 + 8u * d + k) | (e << 16);
+                        ++r;
+                        z &= z - 1;
+                    }
                 }
             }
+        }
+        if (staged) {
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            const uint32_t gp = (uint32_t)(wave * G + j) << 11;   // the group's place in the tile
+            for (uint32_t i = lane; i < wcnt; i += 64)
+                if (w0 + i < room) {
+                    const uint32_t h = s_stage[wave][i];
+                    gdst[w0 + i] = (gp + (h & 0x7FFu)) | ((h >> 11) << 16);
+                }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         }
     }
 }
 
 hipError_t launch_encode_pack_e5m2(const EncodeArgs &a, hipStream_t stream)
 {
-    encode_pack_e5m2_kernel<<<a.n_tiles, kThreads, 0, stream>>>(a);
+    if (a.stage)
+        encode_pack_e5m2_kernel<true><<<a.n_tiles, kThreads, 0, stream>>>(a);
+    else
+        encode_pack_e5m2_kernel<false><<<a.n_tiles, kThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 

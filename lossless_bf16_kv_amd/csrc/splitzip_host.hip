@@ -181,6 +181,7 @@ struct splitzip_codec {
     int device = 0;
     std::atomic<bool> profiling{false};   // set by splitzip_profile, read by every call
     std::atomic<uint32_t> small_tiles{sz::kSmallTiles};   // calls of at most this many tiles: pack + finish
+    std::atomic<uint32_t> stage_tiles{sz::kStageTiles};   // calls of more tiles: the staging pack build
     uint32_t chunk_size = 0;
     uint32_t log2_chunk = 0;
     uint32_t n_books = 0;
@@ -1028,6 +1029,7 @@ int encode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
     a.elem = codec->elem;
     a.tile_shift = codec->elem == sz::kElemE5M2 ? sz::kE8EncTileShift : sz::kEncTileShift;
     a.slot_escapes = slot_escapes;
+    a.stage = n_tiles > codec->stage_tiles.load(std::memory_order_relaxed) ? 1u : 0u;
     hipError_t e = hipSuccess;
     {
         // small calls: pack and finish; else pack, sums, place and spill
@@ -1284,6 +1286,18 @@ int splitzip_set_small_tiles(splitzip_codec *codec, uint32_t max_tiles)
         if (max_tiles > sz::kSmallTiles)
             return fail(SPLITZIP_E_INVALID, "max_tiles %u exceeds %u", max_tiles, sz::kSmallTiles);
         codec->small_tiles.store(max_tiles, std::memory_order_relaxed);
+        return SPLITZIP_OK;
+    });
+}
+
+int splitzip_set_stage_tiles(splitzip_codec *codec, uint32_t min_tiles)
+{
+    return guarded([&]() -> int {
+        g_last_error[0] = '\0';
+        int rc = codec_check(codec);
+        if (rc != SPLITZIP_OK)
+            return rc;
+        codec->stage_tiles.store(min_tiles, std::memory_order_relaxed);
         return SPLITZIP_OK;
     });
 }

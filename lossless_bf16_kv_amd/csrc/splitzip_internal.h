@@ -55,7 +55,13 @@ constexpr uint32_t kSlotEscapes = 128;                        // BF16 tiles
 constexpr uint32_t kE8SlotEscapes = 256;                      // E5M2 tiles (twice as long)
 constexpr uint32_t kSumTiles = 2048;          // tiles per segmented-sum block
 constexpr uint32_t kPlaceTiles = 64;          // tiles per placement workgroup
-constexpr uint32_t kSpillBlocks = 1024;       // workgroups moving the overflow tiles' escapes
+constexpr uint32_t kSpillBlocks = 4096;       // workgroups moving the overflow tiles' escapes
+// a wave gathers one group's escapes in LDS before storing them when it has more than this
+constexpr uint32_t kStageMin = 64;
+// calls of more than this many tiles run the pack kernel build that gathers escape-heavy
+// groups in LDS; smaller calls, whose time is mostly the launch and its first instruction
+// fetches, run the smaller build without it
+constexpr uint32_t kStageTiles = 1024;
 // Calls of at most this many tiles finish in one launch after pack (kStageFinish, one
 // workgroup per tile) instead of sums, place and spill: each workgroup adds up the escape
 // counts of its segment's earlier tiles itself (at most kSmallTiles - 1 loads).
@@ -131,6 +137,7 @@ struct EncodeArgs {
     uint32_t elem;                // kElemBF16 or kElemE5M2
     uint32_t tile_shift;          // log2 of the elements per pack tile
     uint32_t slot_escapes;        // entries per tile slot
+    uint32_t stage;               // pack: gather escape-heavy groups in LDS (the larger build)
 };
 
 struct DecodeArgs {

@@ -13,7 +13,8 @@
 //   - encode: 256-byte inverse LUT in LDS (exponent -> code or escape bit), sign+mantissa
 //     bytes gathered with v_perm_b32, codes packed two per byte;
 //   - encode: escape ranks inside a tile by a wave prefix of packed per-group counts plus
-//     an LDS prefix over the 4 waves; the tile's escapes go compacted to a scratch slot, and
+//     an LDS prefix over the 4 waves; the tile's escapes go compacted to a scratch slot
+//     (escape-heavy groups gathered in LDS first, so a wave stores them contiguously), and
 //     three small launches turn the per-tile counts into global offsets (segmented sums),
 //     move the escapes into place and move those of escape-heavy tiles (one launch for
 //     calls of at most kSmallTiles tiles), so no workgroup ever waits on another;
@@ -193,15 +194,17 @@ __device__ __forceinline__ uint32_t flags_keep(uint32_t nv)
 
 // ---- pack ---------------------------------------------------------------------------------
 
+template <bool kStage>
 __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs a)
 {
     __shared__ uint8_t s_lut[256];
     __shared__ uint32_t s_wave_total[kWaves];
     __shared__ uint64_t s_ovf;
+    __shared__ uint32_t s_stage[kWaves][64 * kGroupWords];   // one group's escapes per wave
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = lane_id();
-    const uint32_t wave = tid >> 6;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t t = blockIdx.x;
 
     const uint32_t s = a.n_seg > 1 ? find_segment_block(a.tile_start, a.seg_at, t, tid, lane, s_wave_total) : 0u;
@@ -267,33 +270,62 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
     // Word order inside a wave is (group j, lane, word k).
     uint32_t rank[kEncGroups];
     uint32_t tile_total;
-    tile_escape_ranks<kEncGroups>(counts, lane, wave, s_wave_total, rank, tile_total);
+    uint32_t wave_end;
+    tile_escape_ranks<kEncGroups>(counts, lane, wave, s_wave_total, rank, tile_total, wave_end);
 
     // where the tile's escapes go: its slot, or a range of the overflow area
     uint64_t room;
     uint32_t *dst = tile_escape_dest(a, t, tile_total, tid, &s_ovf, room);
 
-    // escapes: (position inside the tile, exponent); tile-local chunk offsets
+    // escapes: (position inside the tile, exponent); tile-local chunk offsets.  A wave's
+    // escapes of one group have consecutive ranks.  When there are more than kStageMin of
+    // them they are gathered in the wave's LDS buffer first (each word in turn, at its rank)
+    // and stored 64 consecutive entries per instruction; a few are stored directly by the
+    // lanes that hold them.
+    SZ_GLOBAL uint32_t *gdst = as_global(dst);
+    uint32_t *stage = s_stage[wave];
 #pragma unroll
     for (int j = 0; j < kEncGroups; ++j) {
         const uint32_t r0 = rank[j];
         if (g0[j] < n && (g0[j] & cmask) == 0)
             chunk_off[g0[j] >> a.log2_chunk] = r0;
-        uint32_t z = flags[j];
+        const uint32_t z = flags[j];
+        const uint32_t w0 = __builtin_amdgcn_readfirstlane(r0);
+        const uint32_t wcnt = (j + 1 < kEncGroups ? __builtin_amdgcn_readfirstlane(rank[j + 1]) : wave_end) - w0;
+        const bool staged = kStage && __builtin_expect(wcnt > kStageMin, 0);   // uniform in the wave
         if (z) {
             // the group's 8 exponents, word k in byte k (a dword >> 7 holds the exponent of its
             // low word in byte 0 and of its high word in byte 2)
             const uint64_t ex8 = perm(v[j].y >> 7, v[j].x >> 7, 0x06040200u)
                                | ((uint64_t)perm(v[j].w >> 7, v[j].z >> 7, 0x06040200u) << 32);
             const uint32_t p0 = (uint32_t)(g0[j] - base);
-            uint32_t r = r0;
-            do {
-                const uint32_t k = flag_bit_to_word((uint32_t)__builtin_ctz(z));
-                if (r < room)
-                    dst[r] = (p0 + k) | ((uint32_t)(uint8_t)(ex8 >> (8 * k)) << 16);
-                ++r;
-                z &= z - 1;
-            } while (z);
+            if (staged) {
+                // each of the 8 words in turn: an escape goes to its rank in the wave's buffer
+                const uint32_t at = r0 - w0;
+#pragma unroll
+                for (int k = 0; k < kGroupWords; ++k) {
+                    const uint32_t bit = ((k >> 1) << 3) + 4 + (k & 1);    // flag bit of word k
+                    if ((z >> bit) & 1u)
+                        stage[at + __popc(z & ((1u << bit) - 1u))] =
+                            (p0 + k) | ((uint32_t)(uint8_t)(ex8 >> (8 * k)) << 16);
+                }
+            } else {
+                uint32_t zz = z, r = r0;
+                do {
+                    const uint32_t k = flag_bit_to_word((uint32_t)__builtin_ctz(zz));
+                    if (r < room)
+                        gdst[r] = (p0 + k) | ((uint32_t)(uint8_t)(ex8 >> (8 * k)) << 16);
+                    ++r;
+                    zz &= zz - 1;
+                } while (zz);
+            }
+        }
+        if (staged) {
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            for (uint32_t i = lane; i < wcnt; i += 64)
+                if (w0 + i < room)
+                    gdst[w0 + i] = stage[i];
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         }
     }
 }
@@ -630,8 +662,77 @@ __global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs
 
 // ---- spill --------------------------------------------------------------------------------
 
+// Moves lim scratch escapes src[0 .. lim) of the tile whose words start at `base` to their
+// final places pos[0 .. lim) and ex[0 .. lim), kMovePass at a time: loaded 16 per thread
+// (consecutive threads, consecutive entries), split into position and exponent in LDS at
+// indices shifted so that LDS quads line up with 8-byte (positions) and 4-byte (exponents)
+// boundaries of the destination, then stored a whole quad per store, the partial quads at the
+// two ends element by element.  Stored one element per lane, the 2- and 1-byte stores cost
+// four times as many store instructions.  Contains barriers: lim must be the same in every
+// thread of the workgroup.
+constexpr int kMoveBatch = 16;
+constexpr uint32_t kMovePass = kMoveBatch * kThreads;
+struct MoveLds {
+    __align__(16) uint16_t pos[kMovePass + 8];
+    __align__(16) uint8_t exp[kMovePass + 8];
+};
+
+__device__ void move_escapes(const uint32_t *src, uint64_t lim, uint16_t *pos, uint8_t *ex,
+                             uint64_t base, uint64_t cmask, uint32_t tid, MoveLds &L)
+{
+    const SZ_GLOBAL uint32_t *gsrc = as_global(src);
+    for (uint64_t p0 = 0; p0 < lim; p0 += kMovePass) {
+        const uint32_t m = lim - p0 < kMovePass ? (uint32_t)(lim - p0) : kMovePass;
+        SZ_GLOBAL uint16_t *gpos = as_global(pos + p0);
+        SZ_GLOBAL uint8_t *gexp = as_global(ex + p0);
+        const uint32_t shp = (uint32_t)(((uintptr_t)(pos + p0) >> 1) & 3u);
+        const uint32_t shx = (uint32_t)((uintptr_t)(ex + p0) & 3u);
+        uint32_t e[kMoveBatch];
+#pragma unroll
+        for (int k = 0; k < kMoveBatch; ++k)
+            if (tid + k * kThreads < m)
+                e[k] = gsrc[p0 + tid + k * kThreads];
+#pragma unroll
+        for (int k = 0; k < kMoveBatch; ++k) {
+            const uint32_t r = tid + k * kThreads;
+            if (r < m) {
+                L.pos[shp + r] = (uint16_t)((base + (e[k] & 0xFFFFu)) & cmask);
+                L.exp[shx + r] = (uint8_t)(e[k] >> 16);
+            }
+        }
+        __syncthreads();
+        // LDS quad q holds destination elements 4 q - sh .. 4 q - sh + 3 of this pass
+        const uint32_t nqp = (shp + m + 3) >> 2;
+        for (uint32_t q = tid; q < nqp; q += kThreads) {
+            const uint32_t lo = 4 * q, hi = 4 * q + 4;
+            if (lo >= shp && hi <= shp + m) {
+                *reinterpret_cast<SZ_GLOBAL uint64_t *>(gpos + lo - shp) =
+                    *reinterpret_cast<const uint64_t *>(L.pos + lo);
+            } else {
+                for (uint32_t x = lo; x < hi; ++x)
+                    if (x >= shp && x < shp + m)
+                        gpos[x - shp] = L.pos[x];
+            }
+        }
+        const uint32_t nqx = (shx + m + 3) >> 2;
+        for (uint32_t q = tid; q < nqx; q += kThreads) {
+            const uint32_t lo = 4 * q, hi = 4 * q + 4;
+            if (lo >= shx && hi <= shx + m) {
+                *reinterpret_cast<SZ_GLOBAL uint32_t *>(gexp + lo - shx) =
+                    *reinterpret_cast<const uint32_t *>(L.exp + lo);
+            } else {
+                for (uint32_t x = lo; x < hi; ++x)
+                    if (x >= shx && x < shx + m)
+                        gexp[x - shx] = L.exp[x];
+            }
+        }
+        __syncthreads();
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void encode_spill_kernel(const EncodeArgs a)
 {
+    __shared__ MoveLds s_move;
     const uint32_t tid = threadIdx.x;
     const uint64_t cmask = (1ull << a.log2_chunk) - 1;
     const uint32_t n_spilled = (uint32_t)(a.ovf_ctr[1] >> kOvfTileShift);
@@ -645,27 +746,13 @@ __global__ __launch_bounds__(kThreads) void encode_spill_kernel(const EncodeArgs
         const uint64_t off = a.tile_ovf[t];
         const uint64_t room = off < a.ovf_cap ? a.ovf_cap - off : 0;
         uint8_t *exps = a.packed ? packed_exps(sd, a.seg_total[s]) : sd.esc_exp;
-        // an overflow tile holds thousands of escapes: sixteen loads in flight per thread
-        // before the stores (global pointers, so the stores do not hold the next loads back)
-        constexpr int kBatch = 16;
-        const SZ_GLOBAL uint32_t *src = as_global(static_cast<const uint32_t *>(a.ovf + off));
-        const uint32_t lim = cnt < room ? cnt : (uint32_t)room;
-        for (uint32_t r0 = tid; r0 < lim; r0 += kBatch * kThreads) {
-            uint32_t e[kBatch];
-#pragma unroll
-            for (int k = 0; k < kBatch; ++k)
-                if (r0 + k * kThreads < lim)
-                    e[k] = src[r0 + k * kThreads];
-#pragma unroll
-            for (int k = 0; k < kBatch; ++k) {
-                const uint32_t r = r0 + k * kThreads;
-                const uint64_t d = pre + r;
-                if (r < lim && d < sd.esc && exps) {
-                    as_global(sd.esc_pos)[d] = (uint16_t)((base + (e[k] & 0xFFFFu)) & cmask);
-                    as_global(exps)[d] = (uint8_t)(e[k] >> 16);
-                }
-            }
-        }
+        if (!exps)
+            continue;                                  // uniform: no room for the exponents
+        // entries that lie inside the overflow area and land inside the escape sections
+        uint64_t lim = cnt < room ? cnt : room;
+        const uint64_t fit = sd.esc > pre ? sd.esc - pre : 0;
+        lim = lim < fit ? lim : fit;
+        move_escapes(a.ovf + off, lim, sd.esc_pos + pre, exps + pre, base, cmask, tid, s_move);
     }
 }
 
@@ -766,7 +853,9 @@ __global__ __launch_bounds__(kThreads) void encode_finish_kernel(const EncodeArg
         lim = 0;
     SZ_GLOBAL uint16_t *pos = as_global(lim ? sd.esc_pos + prefix : sd.esc_pos);
     SZ_GLOBAL uint8_t *ex = as_global(lim ? exps + prefix : exps);
-    // an overflow tile holds thousands of escapes: sixteen loads in flight per thread
+    // an overflow tile holds thousands of escapes: sixteen loads in flight per thread.  (The
+    // spill launch's LDS-staged stores gained nothing here: a small call's finish waits on its
+    // sum over the earlier tiles' counts, and the larger code cost a cold call 0.8 us.)
     constexpr int kOvfBatch = 16;
     const SZ_GLOBAL uint32_t *gsrc = as_global(src);
     for (uint32_t r0 = tid; r0 < lim; r0 += kOvfBatch * kThreads) {
@@ -792,7 +881,10 @@ hipError_t launch_encode_stage(int stage, const EncodeArgs &a, hipStream_t strea
     case kStagePack:
         if (a.elem == kElemE5M2)
             return launch_encode_pack_e5m2(a, stream);
-        encode_pack_kernel<<<a.n_tiles, kThreads, 0, stream>>>(a);
+        if (a.stage)
+            encode_pack_kernel<true><<<a.n_tiles, kThreads, 0, stream>>>(a);
+        else
+            encode_pack_kernel<false><<<a.n_tiles, kThreads, 0, stream>>>(a);
         break;
     case kStageSums:
         encode_sums_kernel<<<(a.n_tiles + kSumTiles - 1) / kSumTiles, kThreads, 0, stream>>>(a);

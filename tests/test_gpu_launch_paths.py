@@ -1,7 +1,9 @@
-"""GPU parity of both encode launch sequences: calls of at most SMALL_TILES tiles run pack
-and finish (one workgroup per tile adds up the earlier tiles' escape counts itself), larger
-calls run pack, sums, place and spill.  Each case is encoded both ways
-(``Codec.set_small_tiles``) and both must equal the oracle byte for byte: BF16 and E5M2
+"""GPU parity of both encode launch sequences and both pack builds: calls of at most
+SMALL_TILES tiles run pack and finish (one workgroup per tile adds up the earlier tiles'
+escape counts itself), larger calls run pack, sums, place and spill; calls of more than
+STAGE_TILES tiles run the pack build in which a wave gathers a group's escapes in LDS when
+it has more than 64.  Each case is encoded all four ways (``Codec.set_small_tiles``,
+``Codec.set_stage_tiles``) and each must equal the oracle byte for byte: BF16 and E5M2
 streams spanning several tiles with ragged tails, tiles whose escapes overflow their
 slot, batches with empty and tiny segments and several codebooks, packed streams, too
 little escape room, and the 2048 / 2049-tile boundary of the default."""
@@ -20,7 +22,16 @@ import test_gpu_e5m2 as t8
 pytestmark = pytest.mark.gpu
 
 O = oracle.get()
-MODES = {"four_launches": 0, "pack_finish": sz.SMALL_TILES}
+NEVER = (1 << 32) - 1
+# (set_small_tiles, set_stage_tiles)
+MODES = {"four_launches": (0, NEVER), "pack_finish": (sz.SMALL_TILES, NEVER),
+         "four_launches_gather": (0, 0), "pack_finish_gather": (sz.SMALL_TILES, 0)}
+
+
+def use_mode(codec, mode):
+    small, stage = MODES[mode]
+    codec.set_small_tiles(small)
+    codec.set_stage_tiles(stage)
 TILE = 16384          # BF16 words per pack tile
 TILE8 = 32768         # E5M2 bytes per pack tile
 
@@ -35,7 +46,7 @@ def test_bf16_streams(mode, n, C, wide):
     # 128-entry slot and its escapes go through the overflow area
     x = workloads.mixed_words(n, 31 * n + C, wide_fraction=wide)
     codec = codec_for(workloads.normal_words(50_000, 3), C)
-    codec.set_small_tiles(MODES[mode])
+    use_mode(codec, mode)
     enc = codec.encode(dev(x))
     assert_same_stream(codec, enc, x)
     assert np.array_equal(host(codec.decode(enc), np.uint16), x)
@@ -46,7 +57,7 @@ def test_bf16_batch_empty_tiny_and_books(mode):
     cals = [workloads.normal_words(60_000, 70 + k, sigma=2.0 ** (6 * k - 6)) for k in range(3)]
     codec = sz.Codec(DEV, 64)
     codec.calibrate_books([dev(c) for c in cals])
-    codec.set_small_tiles(MODES[mode])
+    use_mode(codec, mode)
     sizes = [0, 1, 7, TILE, TILE + 1, 0, 100, 3 * TILE + 5, 40_000]
     xs = [workloads.mixed_words(n, 500 + i, wide_fraction=0.1 * (i % 4)) for i, n in enumerate(sizes)]
     books = [i % 3 for i in range(len(xs))]
@@ -72,7 +83,7 @@ def test_bf16_too_little_escape_room(mode, escapes):
     else:                           # ~30 % escapes: every tile overflows its slot
         x = workloads.mixed_words(n, 77, wide_fraction=0.3)
     codec = codec_for(workloads.normal_words(20_000, 5), 1024)
-    codec.set_small_tiles(MODES[mode])
+    use_mode(codec, mode)
     ref = O.encode(x, np.frombuffer(codec.codebook, np.uint8), 1024)
     assert ref["n_escapes"] >= 3
     cap = ref["n_escapes"] // 3
@@ -98,7 +109,7 @@ def test_bf16_too_little_escape_room(mode, escapes):
 def test_packed_streams(mode):
     C = 1024
     codec = codec_for(workloads.mixed_words(100_000, 41, wide_fraction=0.05), C)
-    codec.set_small_tiles(MODES[mode])
+    use_mode(codec, mode)
     xs = [workloads.mixed_words(n, 900 + n % 97, wide_fraction=w)
           for n, w in [(0, 0.0), (16, 0.1), (3 * TILE + 16, 0.3), (250_000, 0.05)]]
     packed = codec.encode_packed_batch([dev(x) for x in xs])
@@ -115,7 +126,7 @@ def test_packed_streams(mode):
 def test_e5m2_streams(mode, n, C, wide):
     x = workloads.e5m2_mixed(n, 13 * n + C, wide_fraction=wide)
     codec = t8.codec_for(workloads.e5m2_normal(50_000, 4), C)
-    codec.set_small_tiles(MODES[mode])
+    use_mode(codec, mode)
     enc = codec.encode(t8.dev8(x))
     t8.assert_same_stream(codec, enc, x)
     assert np.array_equal(t8.host(codec.decode(enc), np.uint8), x)
@@ -125,7 +136,7 @@ def test_e5m2_streams(mode, n, C, wide):
 def test_e5m2_packed_batch(mode):
     C = 64
     codec = t8.codec_for(workloads.e5m2_normal(50_000, 8), C)
-    codec.set_small_tiles(MODES[mode])
+    use_mode(codec, mode)
     xs = [workloads.e5m2_mixed(n, 40 + n % 89, wide_fraction=0.2) for n in (0, 128, TILE8 * 2 + 256)]
     packed = codec.encode_packed_batch([t8.dev8(x) for x in xs])
     for x, p in zip(xs, packed):
@@ -209,7 +220,7 @@ def test_many_tiny_segments(mode, elem):
         xs_np = [workloads.mixed_words(n, 900 + i, wide_fraction=0.05) for i, n in enumerate(sizes)]
         codec = codec_for(workloads.normal_words(50_000, 6), C)
         to_dev, check, back = dev, assert_same_stream, (lambda y: host(y, np.uint16))
-    codec.set_small_tiles(MODES[mode])
+    use_mode(codec, mode)
     encs = codec.encode_batch([to_dev(x) for x in xs_np])
     for x, e in zip(xs_np, encs):
         check(codec, e, x)
