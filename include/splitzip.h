@@ -313,14 +313,17 @@ int splitzip_set_small_tiles(splitzip_codec *codec, uint32_t max_tiles);
 #define SPLITZIP_STAGE_TILES 1024
 
 /*
- * Which build of the pack kernel an encode call runs; no page fixes it, and the bytes
- * written are the same either way.  A call of more than min_tiles tiles (tiles as for
- * splitzip_set_small_tiles) runs the build in which a wave gathers a group's escapes in LDS
- * and stores them as one contiguous run when there are more than 64 of them: much faster on
- * escape-heavy inputs.  Smaller calls run the build without it, whose smaller code costs
- * less when the call is short and its instructions are not yet in the caches.  Any value
- * is accepted: 0 = always the gathering build, UINT32_MAX = never.  Applies to calls that
- * start after it returns.
+ * Which builds of the pack and decode kernels a call runs; no page fixes it, and the bytes
+ * written are the same either way.  An encode call of more than min_tiles tiles (tiles as
+ * for splitzip_set_small_tiles), and a decode call of more than 2 * min_tiles decode tiles
+ * (8192 BF16 words or 16384 E5M2 bytes, at least one per segment: the same elements), run
+ * the builds tuned for escape-heavy inputs: in pack a wave gathers a group's escapes in LDS
+ * and stores them as one contiguous run when there are more than 64 of them; in decode an
+ * escape finds its chunk among offsets held in scalar registers when a tile spans at most 8
+ * chunks (16 for E5M2) instead of by a binary search in LDS.  Smaller calls run the builds
+ * without them, whose smaller code costs less when the call is short and its instructions
+ * are not yet in the caches.  Any value is accepted: 0 = always the tuned builds,
+ * UINT32_MAX = never.  Applies to calls that start after it returns.
  */
 int splitzip_set_stage_tiles(splitzip_codec *codec, uint32_t min_tiles);
 

@@ -35,7 +35,7 @@ LIB_PATH = os.path.join(_HERE, "libsplitzip.so")
 OK, E_INVALID, E_NOMEM, E_DEVICE, E_CODEBOOK, E_FORMAT, E_CAPACITY = range(7)
 HEADER_BYTES = 64
 SMALL_TILES = 2048      # encodes of at most this many tiles run pack + finish (two launches)
-STAGE_TILES = 1024      # encodes of more tiles run the pack build that gathers escapes in LDS
+STAGE_TILES = 1024      # larger calls run the kernel builds tuned for escape-heavy inputs
 MIN_CHUNK, MAX_CHUNK = 16, 65536
 MAX_BOOKS = 4096
 ELEM_BF16, ELEM_E5M2 = 0, 1
@@ -607,9 +607,10 @@ class Codec:
         self._small_tiles = max_tiles
 
     def set_stage_tiles(self, min_tiles: int = STAGE_TILES) -> None:
-        """Encodes of more than min_tiles tiles run the pack build that gathers escape-heavy
-        groups in LDS (same bytes; faster on escape-heavy inputs, larger code); 0: always,
-        2**32 - 1: never.  Kept across later calibrations of this codec."""
+        """Encodes of more than min_tiles tiles, and decodes of more than 2 * min_tiles decode
+        tiles (the same elements), run the kernel builds tuned for escape-heavy inputs (same
+        bytes; larger code, which costs short calls more); 0: always, 2**32 - 1: never.
+        Kept across later calibrations of this codec."""
         if not 0 <= min_tiles < 1 << 32:
             raise SplitZipError(E_INVALID, "min_tiles must fit 32 bits")
         if self.handle:

@@ -289,6 +289,7 @@ __device__ __forceinline__ uint32_t e8_assemble(uint32_t ex4, uint32_t f)
     return ex4 | (f & 0x03030303u) | ((f << 5) & 0x80808080u);
 }
 
+template <bool kLarge>
 __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs a)
 {
     constexpr int G = kE8DecGroups;
@@ -441,13 +442,24 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
         // the tile's escapes are the contiguous range [j0, j1), kPatch per thread and round;
         // every load of a round goes out before its LDS writes (global pointers: the loads
         // cannot alias LDS, so nothing holds them back)
-        constexpr int kPatch = 4;
+        constexpr int kPatch = kLarge ? 8 : 4;
         const SZ_GLOBAL uint16_t *gpos = as_global(static_cast<const uint16_t *>(sd.esc_pos));
         const SZ_GLOBAL uint8_t *gexp = as_global(static_cast<const uint8_t *>(sd.esc_exp));
         if (!sub_chunk) {
             for (uint64_t ci = tid; ci < nc; ci += kThreads)
                 if (s_off[ci] > s_off[ci + 1] && a.err)
                     atomicOr(a.err, kErrBadOffsets);
+            // chunk of escape jj: the last c with s_off[c] <= jj.  In the large-call build a
+            // tile of at most kFew chunks (chunk size 1024 or more) keeps the tile-relative
+            // offsets in scalar registers, and each escape counts those at or below it; a
+            // binary search in LDS costs three or more dependent LDS reads per escape.
+            constexpr int kFew = 16;
+            const bool few = kLarge && nc <= (uint64_t)kFew;       // uniform
+            uint32_t rel[kFew];
+#pragma unroll
+            for (int c = 0; c < kFew; ++c)
+                rel[c] = (few && c >= 1 && (uint64_t)c < nc) ? __builtin_amdgcn_readfirstlane((uint32_t)(s_off[c] - j0))
+                                                      : 0xFFFFFFFFu;
             for (uint64_t jb = j0 + tid; jb < j1; jb += kPatch * kThreads) {
                 uint32_t pos[kPatch], ev[kPatch];
 #pragma unroll
@@ -463,13 +475,21 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
                     const uint64_t jj = jb + (uint64_t)k * kThreads;
                     if (jj >= j1)
                         continue;
-                    uint32_t lo = 0, hi = (uint32_t)nc;      // s_off[lo] <= jj < s_off[hi]
-                    while (hi - lo > 1) {
-                        const uint32_t mid = (lo + hi) >> 1;
-                        if (s_off[mid] <= jj)
-                            lo = mid;
-                        else
-                            hi = mid;
+                    uint32_t lo = 0;
+                    if (few) {
+                        const uint32_t r = (uint32_t)(jj - j0);
+#pragma unroll
+                        for (int c = 1; c < kFew; ++c)
+                            lo += r >= rel[c] ? 1u : 0u;
+                    } else {
+                        uint32_t hi = (uint32_t)nc;          // s_off[lo] <= jj < s_off[hi]
+                        while (hi - lo > 1) {
+                            const uint32_t mid = (lo + hi) >> 1;
+                            if (s_off[mid] <= jj)
+                                lo = mid;
+                            else
+                                hi = mid;
+                        }
                     }
                     const uint64_t cstart = (c0 + lo) << log2c;
                     const uint64_t clen = n - cstart < C ? n - cstart : C;
@@ -561,7 +581,10 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
 
 hipError_t launch_decode_e5m2(const DecodeArgs &a, hipStream_t stream)
 {
-    decode_e5m2_kernel<<<(a.n_tiles + kXcds - 1) / kXcds * kXcds, kThreads, 0, stream>>>(a);
+    if (a.large)
+        decode_e5m2_kernel<true><<<(a.n_tiles + kXcds - 1) / kXcds * kXcds, kThreads, 0, stream>>>(a);
+    else
+        decode_e5m2_kernel<false><<<(a.n_tiles + kXcds - 1) / kXcds * kXcds, kThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 

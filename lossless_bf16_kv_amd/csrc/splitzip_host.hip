@@ -181,7 +181,7 @@ struct splitzip_codec {
     int device = 0;
     std::atomic<bool> profiling{false};   // set by splitzip_profile, read by every call
     std::atomic<uint32_t> small_tiles{sz::kSmallTiles};   // calls of at most this many tiles: pack + finish
-    std::atomic<uint32_t> stage_tiles{sz::kStageTiles};   // calls of more tiles: the staging pack build
+    std::atomic<uint32_t> stage_tiles{sz::kStageTiles};   // larger calls: the builds for escape-heavy inputs
     uint32_t chunk_size = 0;
     uint32_t log2_chunk = 0;
     uint32_t n_books = 0;
@@ -1225,6 +1225,7 @@ int decode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
     a.n_tiles = tiles[n_seg];
     a.log2_chunk = codec->log2_chunk;
     a.elem = codec->elem;
+    a.large = (uint64_t)a.n_tiles > 2ull * codec->stage_tiles.load(std::memory_order_relaxed) ? 1u : 0u;
     hipError_t e;
     {
         static const int kDecodeKind[] = {SPLITZIP_KERNEL_DECODE};

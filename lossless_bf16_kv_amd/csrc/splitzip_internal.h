@@ -58,9 +58,11 @@ constexpr uint32_t kPlaceTiles = 64;          // tiles per placement workgroup
 constexpr uint32_t kSpillBlocks = 4096;       // workgroups moving the overflow tiles' escapes
 // a wave gathers one group's escapes in LDS before storing them when it has more than this
 constexpr uint32_t kStageMin = 64;
-// calls of more than this many tiles run the pack kernel build that gathers escape-heavy
-// groups in LDS; smaller calls, whose time is mostly the launch and its first instruction
-// fetches, run the smaller build without it
+// calls of more than this many pack tiles (decode: twice as many decode tiles, the same
+// elements) run the kernel builds tuned for escape-heavy inputs: pack gathers escape-heavy
+// groups in LDS, decode finds an escape's chunk among offsets held in scalar registers and
+// loads 8 escapes per thread and round.  Smaller calls, whose time is mostly the launch and
+// its first instruction fetches, run the smaller builds without them.
 constexpr uint32_t kStageTiles = 1024;
 // Calls of at most this many tiles finish in one launch after pack (kStageFinish, one
 // workgroup per tile) instead of sums, place and spill: each workgroup adds up the escape
@@ -153,7 +155,7 @@ struct DecodeArgs {
     uint32_t log2_chunk;
     uint32_t multi_book;
     uint32_t elem;                // kElemBF16 or kElemE5M2
-    uint32_t pad;
+    uint32_t large;               // the build for large calls (chunk lookup in scalar registers)
 };
 
 // Exponent histograms of one or more tensors: per-workgroup partial counts (each tensor

@@ -932,6 +932,7 @@ __device__ __forceinline__ uint32_t assemble(uint32_t s, uint32_t sm_sel, uint32
     return (p & 0x807F807Fu) | (q << 7);
 }
 
+template <bool kLarge>
 __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
 {
     __shared__ uint32_t s_exp[kDecTileWords / 4];              // exponent bytes of the tile
@@ -1065,7 +1066,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
         // the tile's escapes are the contiguous range [j0, j1), kPatch per thread and round;
         // every load of a round goes out before its LDS writes (global pointers: the loads
         // cannot alias LDS, so nothing holds them back)
-        constexpr int kPatch = 4;
+        constexpr int kPatch = kLarge ? 8 : 4;
         const SZ_GLOBAL uint16_t *gpos = as_global(static_cast<const uint16_t *>(sd.esc_pos));
         const SZ_GLOBAL uint8_t *gexp = as_global(static_cast<const uint8_t *>(sd.esc_exp));
         if (!sub_chunk) {
@@ -1073,6 +1074,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
             for (uint64_t ci = tid; ci < nc; ci += kThreads)
                 if (s_off[ci] > s_off[ci + 1] && a.err)
                     atomicOr(a.err, kErrBadOffsets);
+            // chunk of escape jj: the last c with s_off[c] <= jj.  In the large-call build a
+            // tile of at most kFew chunks (chunk size 1024 or more) keeps the tile-relative
+            // offsets in scalar registers, and each escape counts those at or below it; a
+            // binary search in LDS costs three or more dependent LDS reads per escape.
+            constexpr int kFew = 8;
+            const bool few = kLarge && nc <= (uint64_t)kFew;       // uniform
+            uint32_t rel[kFew];
+#pragma unroll
+            for (int c = 0; c < kFew; ++c)
+                rel[c] = (few && c >= 1 && (uint64_t)c < nc) ? __builtin_amdgcn_readfirstlane((uint32_t)(s_off[c] - j0))
+                                                      : 0xFFFFFFFFu;
             for (uint64_t jb = j0 + tid; jb < j1; jb += kPatch * kThreads) {
                 uint32_t pos[kPatch], ev[kPatch];
 #pragma unroll
@@ -1088,13 +1100,21 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
                     const uint64_t jj = jb + (uint64_t)k * kThreads;
                     if (jj >= j1)
                         continue;
-                    uint32_t lo = 0, hi = (uint32_t)nc;      // s_off[lo] <= jj < s_off[hi]
-                    while (hi - lo > 1) {
-                        const uint32_t mid = (lo + hi) >> 1;
-                        if (s_off[mid] <= jj)
-                            lo = mid;
-                        else
-                            hi = mid;
+                    uint32_t lo = 0;
+                    if (few) {
+                        const uint32_t r = (uint32_t)(jj - j0);
+#pragma unroll
+                        for (int c = 1; c < kFew; ++c)
+                            lo += r >= rel[c] ? 1u : 0u;
+                    } else {
+                        uint32_t hi = (uint32_t)nc;          // s_off[lo] <= jj < s_off[hi]
+                        while (hi - lo > 1) {
+                            const uint32_t mid = (lo + hi) >> 1;
+                            if (s_off[mid] <= jj)
+                                lo = mid;
+                            else
+                                hi = mid;
+                        }
                     }
                     const uint64_t cstart = (c0 + lo) << log2c;
                     const uint64_t clen = n - cstart < C ? n - cstart : C;
@@ -1170,7 +1190,10 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream)
         return launch_decode_e5m2(a, stream);
     // The dynamic LDS reservation is unused: it caps decode at 5 workgroups per CU, which
     // streams about 3 % faster than the 8 that registers would allow (less contention for HBM).
-    decode_kernel<<<xcd_grid(a.n_tiles), kThreads, kDecodeLdsReserve, stream>>>(a);
+    if (a.large)
+        decode_kernel<true><<<xcd_grid(a.n_tiles), kThreads, kDecodeLdsReserve, stream>>>(a);
+    else
+        decode_kernel<false><<<xcd_grid(a.n_tiles), kThreads, kDecodeLdsReserve, stream>>>(a);
     return hipGetLastError();
 }
 
