@@ -177,15 +177,19 @@ def test_capacity_retry_gives_identical_stream():
     assert_same_stream(codec, codec.encode(dev8(x)), x)
 
 
-def test_decode_flags_corrupt_metadata_without_faulting():
+@pytest.mark.parametrize("stage_tiles", [sz.STAGE_TILES, 0])
+def test_decode_flags_corrupt_metadata_without_faulting(stage_tiles):
+    """Both decode builds flag corrupt metadata without a fault (0: the large-call build)."""
     x = workloads.e5m2_mixed(4 * 16384, 12, wide_fraction=0.2)
     codec = codec_for(workloads.e5m2_normal(20000, 7), 1024)
+    codec.set_stage_tiles(stage_tiles)
     enc = codec.encode(dev8(x))
     assert enc.n_escapes > 100
     y = torch.empty_like(codec.decode(enc))
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    assert int(enc.chunk_off[9]) > int(enc.chunk_off[3])
     for field, idx, val in (("chunk_off", 3, enc.n_escapes + 1000), ("esc_pos_buf", 5, 4000),
-                            ("esc_exp_buf", 7, 40)):
+                            ("esc_exp_buf", 7, 40), ("chunk_off", 2, int(enc.chunk_off[9]))):
         bad = dataclasses.replace(enc, chunk_off=enc.chunk_off.clone(), esc_pos_buf=enc.esc_pos_buf.clone(),
                                   esc_exp_buf=enc.esc_exp_buf.clone())
         getattr(bad, field)[idx] = val

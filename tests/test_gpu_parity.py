@@ -173,9 +173,13 @@ def test_deterministic_and_stream_independent():
     assert a == b == c.to_bytes(codec) == d.to_bytes(codec)
 
 
-def test_decode_flags_corrupt_metadata_without_faulting():
+@pytest.mark.parametrize("stage_tiles", [sz.STAGE_TILES, 0])
+def test_decode_flags_corrupt_metadata_without_faulting(stage_tiles):
+    """Both decode builds (0: the large-call build, whose escapes find their chunk by
+    counting offsets held in scalar registers) flag corrupt metadata without a fault."""
     x = workloads.mixed_words(4 * 8192, 12, wide_fraction=0.2)
     codec = codec_for(workloads.normal_words(20000, 7), 1024)
+    codec.set_stage_tiles(stage_tiles)
     enc = codec.encode(dev(x))
     assert enc.n_escapes > 100
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
@@ -183,6 +187,14 @@ def test_decode_flags_corrupt_metadata_without_faulting():
     bad.chunk_off[3] = enc.n_escapes + 1000            # offset beyond E
     bad.esc_pos_buf[5] = 4000                          # position beyond its chunk
     y = torch.empty_like(codec.decode(enc))
+    codec.decode_into([bad], [y], d_error=err.data_ptr())
+    torch.cuda.synchronize()
+    assert int(err.item()) != 0
+    # offsets that decrease inside a tile but stay below E
+    bad = dataclass_copy(enc)
+    bad.chunk_off[2] = enc.chunk_off[6]
+    assert int(enc.chunk_off[6]) > int(enc.chunk_off[3])
+    err.zero_()
     codec.decode_into([bad], [y], d_error=err.data_ptr())
     torch.cuda.synchronize()
     assert int(err.item()) != 0
