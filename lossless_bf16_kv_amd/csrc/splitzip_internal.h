@@ -56,6 +56,7 @@ constexpr uint32_t kE8SlotEscapes = 256;                      // E5M2 tiles (twi
 constexpr uint32_t kSumTiles = 2048;          // tiles per segmented-sum block
 constexpr uint32_t kPlaceTiles = 64;          // tiles per placement workgroup
 constexpr uint32_t kSpillBlocks = 4096;       // workgroups moving the overflow tiles' escapes
+constexpr uint32_t kFinishPartShift = 2;     // large-call finish: 4 workgroups per tile
 // a wave gathers one group's escapes in LDS before storing them when it has more than this
 constexpr uint32_t kStageMin = 64;
 // calls of more than this many pack tiles (decode: twice as many decode tiles, the same

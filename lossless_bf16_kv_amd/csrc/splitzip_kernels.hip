@@ -736,6 +736,8 @@ __global__ __launch_bounds__(kThreads) void encode_spill_kernel(const EncodeArgs
     const uint32_t tid = threadIdx.x;
     const uint64_t cmask = (1ull << a.log2_chunk) - 1;
     const uint32_t n_spilled = (uint32_t)(a.ovf_ctr[1] >> kOvfTileShift);
+    // one workgroup per overflow tile (splitting a tile over 4 workgroups of this grid was
+    // slower: each workgroup then worked through four items one after the other)
     for (uint32_t i = blockIdx.x; i < n_spilled; i += gridDim.x) {
         const uint32_t t = a.ovf_tiles[i];
         const uint32_t s = tile_segment(a, t);
@@ -785,7 +787,13 @@ __global__ __launch_bounds__(kThreads) void encode_finish_kernel(const EncodeArg
     __shared__ uint64_t s_part[kWaves];
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = lane_id();
-    const uint32_t t = blockIdx.x;
+    // In the large-call build each tile has kFinishParts workgroups, which share its escape
+    // moves: a tile whose elements all escape needs several rounds of loads and stores, most
+    // tiles one, and the slowest tiles set the launch's time.  Part 0 also makes the chunk
+    // offsets global and writes the segment's totals.
+    const uint32_t pshift = a.stage ? kFinishPartShift : 0u;
+    const uint32_t t = blockIdx.x >> pshift;
+    const uint32_t part = blockIdx.x & ((1u << pshift) - 1u);
     const uint64_t cmask = (1ull << a.log2_chunk) - 1;
 
     const uint32_t s = a.n_seg > 1 ? find_segment_block(a.tile_start, a.seg_at, t, tid, lane, s_cnt) : 0u;
@@ -805,19 +813,19 @@ __global__ __launch_bounds__(kThreads) void encode_finish_kernel(const EncodeArg
     }
     const uint64_t prefix = block_total_u64(before, tid, lane, s_part);
     const uint64_t E = a.packed ? block_total_u64(all, tid, lane, s_part) : prefix + count;
-    if (t + 1 == end && tid == 0) {
+    if (part == 0 && t + 1 == end && tid == 0) {
         sd.chunk_off[(sd.n + cmask) >> a.log2_chunk] = E;
         a.seg_escapes[s] = E;
         if (a.packed)
             write_header(sd, a, E);
     }
-    if (t == 0 && tid == 0)
+    if (blockIdx.x == 0 && tid == 0)
         a.ovf_ctr[0] = 0;    // the pack launch has finished with the overflow counter
 
     // tile-local chunk offsets become segment offsets, four loads in flight before the stores
     constexpr int kBatch = 4;
     const uint64_t base = (uint64_t)(t - first) << a.tile_shift;
-    if (base < sd.n) {
+    if (part == 0 && base < sd.n) {
         const uint64_t tile_words = 1ull << a.tile_shift;
         const uint64_t words = sd.n - base < tile_words ? sd.n - base : tile_words;
         const uint64_t c0 = (base + cmask) >> a.log2_chunk;
@@ -858,16 +866,20 @@ __global__ __launch_bounds__(kThreads) void encode_finish_kernel(const EncodeArg
     // sum over the earlier tiles' counts, and the larger code cost a cold call 0.8 us.)
     constexpr int kOvfBatch = 16;
     const SZ_GLOBAL uint32_t *gsrc = as_global(src);
-    for (uint32_t r0 = tid; r0 < lim; r0 += kOvfBatch * kThreads) {
+    // this part's share of the tile's escapes
+    const uint32_t share = (uint32_t)((lim + (1u << pshift) - 1u) >> pshift);
+    const uint32_t r_begin = part * share;
+    const uint32_t r_end = (uint64_t)r_begin + share < lim ? r_begin + share : (uint32_t)lim;
+    for (uint32_t r0 = r_begin + tid; r0 < r_end; r0 += kOvfBatch * kThreads) {
         uint32_t e[kOvfBatch];
 #pragma unroll
         for (int k = 0; k < kOvfBatch; ++k)
-            if (r0 + k * kThreads < lim)
+            if (r0 + k * kThreads < r_end)
                 e[k] = gsrc[r0 + k * kThreads];
 #pragma unroll
         for (int k = 0; k < kOvfBatch; ++k) {
             const uint32_t r = r0 + k * kThreads;
-            if (r < lim) {
+            if (r < r_end) {
                 pos[r] = (uint16_t)((base + (e[k] & 0xFFFFu)) & cmask);
                 ex[r] = (uint8_t)(e[k] >> 16);
             }
@@ -898,7 +910,7 @@ hipError_t launch_encode_stage(int stage, const EncodeArgs &a, hipStream_t strea
     case kStageFinish:
         if (a.n_tiles > kSmallTiles)
             return hipErrorInvalidValue;
-        encode_finish_kernel<<<a.n_tiles, kThreads, 0, stream>>>(a);
+        encode_finish_kernel<<<a.n_tiles << (a.stage ? kFinishPartShift : 0u), kThreads, 0, stream>>>(a);
         break;
     default:
         return hipErrorInvalidValue;
