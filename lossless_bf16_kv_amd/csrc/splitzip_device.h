@@ -256,17 +256,25 @@ __device__ __forceinline__ void tile_escape_ranks(const uint32_t (&counts)[G], u
     wave_end = wave_base + wave_sum;
 }
 
-// Where tile t's escapes go: its slot of a.slot_escapes entries, or, past that, a range of
-// the overflow area reserved with one 64-bit atomic that also appends the tile to the
-// overflow list.  room: entries that may be written there.  Also stores the tile's escape
-// count.  Call from uniform control flow (contains a barrier when the tile overflows).
+// Where tile t's escapes go: its slot of a.slot_escapes entries, or, past that, the tile's
+// own region of the overflow area (calls with private_ovf) or a range of it reserved with one
+// 64-bit atomic that also appends the tile to the overflow list.  room: entries that may be
+// written there.  Also stores the tile's escape count.  Call from uniform control flow
+// (contains a barrier when the tile overflows).
 __device__ __forceinline__ uint32_t *tile_escape_dest(const EncodeArgs &a, uint32_t t,
                                                       uint32_t tile_total, uint32_t tid,
                                                       uint64_t *s_ovf, uint64_t &room)
 {
     uint32_t *dst = a.slots + (uint64_t)t * a.slot_escapes;
     room = a.slot_escapes;
-    if (tile_total > a.slot_escapes) {
+    if (tile_total > a.slot_escapes && a.private_ovf) {
+        // the tile's own region, as long as the tile: nothing to reserve
+        const uint64_t off = (uint64_t)t << a.tile_shift;
+        if (tid == 0)
+            a.tile_ovf[t] = off;
+        dst = a.ovf + off;
+        room = 1ull << a.tile_shift;
+    } else if (tile_total > a.slot_escapes) {
         if (tid == 0) {
             const uint64_t old = atomicAdd(a.ovf_ctr, (unsigned long long)tile_total + (1ull << kOvfTileShift));
             const uint64_t off = old & kOvfOffsetMask;

@@ -990,9 +990,15 @@ int encode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
     if (rc != SPLITZIP_OK)
         return rc;
     const uint32_t n_tiles = tiles[n_seg];
+    const uint32_t tile_shift = codec->elem == sz::kElemE5M2 ? sz::kE8EncTileShift : sz::kEncTileShift;
+    // every tile its own overflow region when those fit the limit; else one shared area as
+    // large as the escape capacity, reserved from with an atomic counter
+    const bool private_ovf = ((uint64_t)n_tiles << tile_shift) * 4 <= sz::kPrivateOvfBytes;
     uint64_t ovf_cap = 1;
     for (uint32_t i = 0; i < n_seg; ++i)
         ovf_cap += desc[i].esc;
+    if (private_ovf)
+        ovf_cap = (uint64_t)n_tiles << tile_shift;
     const uint32_t slot_escapes = codec->elem == sz::kElemE5M2 ? sz::kE8SlotEscapes : sz::kSlotEscapes;
     const EncodeScratch lay(n_tiles, ovf_cap, n_seg, slot_escapes);
     if ((rc = ensure_scratch(w, lay.total)) != SPLITZIP_OK)
@@ -1027,8 +1033,9 @@ int encode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
     a.n_tiles = n_tiles;
     a.log2_chunk = codec->log2_chunk;
     a.elem = codec->elem;
-    a.tile_shift = codec->elem == sz::kElemE5M2 ? sz::kE8EncTileShift : sz::kEncTileShift;
+    a.tile_shift = tile_shift;
     a.slot_escapes = slot_escapes;
+    a.private_ovf = private_ovf ? 1u : 0u;
     a.stage = n_tiles > codec->stage_tiles.load(std::memory_order_relaxed) ? 1u : 0u;
     hipError_t e = hipSuccess;
     {

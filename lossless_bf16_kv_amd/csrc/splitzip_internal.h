@@ -65,6 +65,10 @@ constexpr uint32_t kStageMin = 64;
 // loads 8 escapes per thread and round.  Smaller calls, whose time is mostly the launch and
 // its first instruction fetches, run the smaller builds without them.
 constexpr uint32_t kStageTiles = 1024;
+// calls whose tiles' worst-case overflow regions (one entry per element, 4 bytes each) fit
+// this many bytes give every tile its own region of the overflow area: no tile reserves space
+// with the overflow counter, which thousands of escape-heavy tiles contend for
+constexpr uint64_t kPrivateOvfBytes = 256ull << 20;
 // Calls of at most this many tiles finish in one launch after pack (kStageFinish, one
 // workgroup per tile) instead of sums, place and spill: each workgroup adds up the escape
 // counts of its segment's earlier tiles itself (at most kSmallTiles - 1 loads).
@@ -141,6 +145,7 @@ struct EncodeArgs {
     uint32_t tile_shift;          // log2 of the elements per pack tile
     uint32_t slot_escapes;        // entries per tile slot
     uint32_t stage;               // pack: gather escape-heavy groups in LDS (the larger build)
+    uint32_t private_ovf;         // each tile owns entries [t << tile_shift, +1 << tile_shift) of ovf
 };
 
 struct DecodeArgs {

@@ -735,11 +735,15 @@ __global__ __launch_bounds__(kThreads) void encode_spill_kernel(const EncodeArgs
     __shared__ MoveLds s_move;
     const uint32_t tid = threadIdx.x;
     const uint64_t cmask = (1ull << a.log2_chunk) - 1;
-    const uint32_t n_spilled = (uint32_t)(a.ovf_ctr[1] >> kOvfTileShift);
+    // the overflow tiles: listed by the pack launch, or, with private regions, every tile
+    // whose escapes outgrew its slot
+    const uint32_t n_items = a.private_ovf ? a.n_tiles : (uint32_t)(a.ovf_ctr[1] >> kOvfTileShift);
     // one workgroup per overflow tile (splitting a tile over 4 workgroups of this grid was
     // slower: each workgroup then worked through four items one after the other)
-    for (uint32_t i = blockIdx.x; i < n_spilled; i += gridDim.x) {
-        const uint32_t t = a.ovf_tiles[i];
+    for (uint32_t i = blockIdx.x; i < n_items; i += gridDim.x) {
+        if (a.private_ovf && a.tile_count[i] <= a.slot_escapes)
+            continue;                                  // uniform: the tile fit its slot
+        const uint32_t t = a.private_ovf ? i : a.ovf_tiles[i];
         const uint32_t s = tile_segment(a, t);
         const SegDesc sd = segment_desc(a, s);
         const uint64_t base = (uint64_t)(t - segment_first_tile(a, s)) << a.tile_shift;
