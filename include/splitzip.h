@@ -327,6 +327,21 @@ int splitzip_set_small_tiles(splitzip_codec *codec, uint32_t max_tiles);
  */
 int splitzip_set_stage_tiles(splitzip_codec *codec, uint32_t min_tiles);
 
+/* Default of splitzip_set_private_overflow: 256 MiB. */
+#define SPLITZIP_PRIVATE_OVERFLOW_BYTES (256ull << 20)
+
+/*
+ * Where an encode call's escape-heavy tiles put the escapes that do not fit their slot; no
+ * page fixes it, and the bytes written are the same either way.  When 4 bytes per element
+ * of all the call's tiles (tiles as for splitzip_set_small_tiles) come to at most max_bytes,
+ * every tile gets its own region of the library's scratch memory, so no tile waits on a
+ * shared counter; otherwise tiles reserve ranges of one area, as large as the call's escape
+ * capacity, with an atomic counter (thousands of escape-heavy tiles contend for it).  The
+ * scratch memory stays allocated with the codec's workspace.  0 = always the shared area.
+ * Applies to calls that start after it returns.
+ */
+int splitzip_set_private_overflow(splitzip_codec *codec, uint64_t max_bytes);
+
 /* ---- per-kernel timing (for benchmarks and profilers: the codec throughput measurement
  *      of README "Quick Start") ---- */
 

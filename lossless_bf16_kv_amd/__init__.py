@@ -36,6 +36,7 @@ OK, E_INVALID, E_NOMEM, E_DEVICE, E_CODEBOOK, E_FORMAT, E_CAPACITY = range(7)
 HEADER_BYTES = 64
 SMALL_TILES = 2048      # encodes of at most this many tiles run pack + finish (two launches)
 STAGE_TILES = 1024      # larger calls run the kernel builds tuned for escape-heavy inputs
+PRIVATE_OVERFLOW_BYTES = 256 << 20   # calls up to this much per-tile overflow scratch use it
 MIN_CHUNK, MAX_CHUNK = 16, 65536
 MAX_BOOKS = 4096
 ELEM_BF16, ELEM_E5M2 = 0, 1
@@ -119,6 +120,7 @@ def lib() -> ctypes.CDLL:
     L.splitzip_profile.argtypes = [vp, i32]
     L.splitzip_set_small_tiles.argtypes = [vp, u32]
     L.splitzip_set_stage_tiles.argtypes = [vp, u32]
+    L.splitzip_set_private_overflow.argtypes = [vp, ctypes.c_uint64]
     L.splitzip_profile_read.argtypes = [vp, vp, P(ctypes.c_double), P(u64), i32]
     L.splitzip_free.argtypes = [vp]
     L.splitzip_free.restype = None
@@ -140,7 +142,7 @@ def lib() -> ctypes.CDLL:
               "splitzip_decode_packed",
               "splitzip_encode", "splitzip_encode_async", "splitzip_decode",
               "splitzip_write_header", "splitzip_profile", "splitzip_profile_read",
-              "splitzip_set_small_tiles", "splitzip_set_stage_tiles",
+              "splitzip_set_small_tiles", "splitzip_set_stage_tiles", "splitzip_set_private_overflow",
               "splitzip_read_header", "splitzip_check_header", "splitzip_calibrate_e5m2",
               "splitzip_calibrate_books_e5m2", "splitzip_codec_from_codebooks_e5m2",
               "splitzip_codec_element", "splitzip_histogram_e5m2"):
@@ -327,6 +329,10 @@ def splitzip_set_small_tiles(codec: int, max_tiles: int) -> None:
 
 def splitzip_set_stage_tiles(codec: int, min_tiles: int) -> None:
     _check(lib().splitzip_set_stage_tiles(codec, min_tiles))
+
+
+def splitzip_set_private_overflow(codec: int, max_bytes: int) -> None:
+    _check(lib().splitzip_set_private_overflow(codec, max_bytes))
 
 
 def splitzip_profile(codec: int, enable: bool) -> None:
@@ -541,6 +547,7 @@ class Codec:
         self._escape_rate = 0.0
         self._small_tiles = SMALL_TILES
         self._stage_tiles = STAGE_TILES
+        self._private_overflow = PRIVATE_OVERFLOW_BYTES
 
     # -- state -----------------------------------------------------------------------
     @classmethod
@@ -592,6 +599,8 @@ class Codec:
             splitzip_set_small_tiles(h, self._small_tiles)
         if self._stage_tiles != STAGE_TILES:
             splitzip_set_stage_tiles(h, self._stage_tiles)
+        if self._private_overflow != PRIVATE_OVERFLOW_BYTES:
+            splitzip_set_private_overflow(h, self._private_overflow)
 
     def _stream(self) -> int:
         import torch
@@ -616,6 +625,16 @@ class Codec:
         if self.handle:
             splitzip_set_stage_tiles(self.handle, min_tiles)
         self._stage_tiles = min_tiles
+
+    def set_private_overflow(self, max_bytes: int = PRIVATE_OVERFLOW_BYTES) -> None:
+        """Encodes whose tiles' own overflow regions (4 bytes per element) fit max_bytes of
+        scratch use them instead of reserving from one shared counter (same bytes; faster
+        on escape-heavy inputs); 0: never.  Kept across later calibrations of this codec."""
+        if not 0 <= max_bytes < 1 << 64:
+            raise SplitZipError(E_INVALID, "max_bytes must fit 64 bits")
+        if self.handle:
+            splitzip_set_private_overflow(self.handle, max_bytes)
+        self._private_overflow = max_bytes
 
     def profile(self, enable: bool = True) -> None:
         """Time every kernel launch of later calls with HIP events (see kernel_times)."""

@@ -182,6 +182,7 @@ struct splitzip_codec {
     std::atomic<bool> profiling{false};   // set by splitzip_profile, read by every call
     std::atomic<uint32_t> small_tiles{sz::kSmallTiles};   // calls of at most this many tiles: pack + finish
     std::atomic<uint32_t> stage_tiles{sz::kStageTiles};   // larger calls: the builds for escape-heavy inputs
+    std::atomic<uint64_t> private_ovf_bytes{sz::kPrivateOvfBytes};   // per-tile overflow regions up to this
     uint32_t chunk_size = 0;
     uint32_t log2_chunk = 0;
     uint32_t n_books = 0;
@@ -993,7 +994,8 @@ int encode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
     const uint32_t tile_shift = codec->elem == sz::kElemE5M2 ? sz::kE8EncTileShift : sz::kEncTileShift;
     // every tile its own overflow region when those fit the limit; else one shared area as
     // large as the escape capacity, reserved from with an atomic counter
-    const bool private_ovf = ((uint64_t)n_tiles << tile_shift) * 4 <= sz::kPrivateOvfBytes;
+    const bool private_ovf = ((uint64_t)n_tiles << tile_shift) * 4 <=
+                             codec->private_ovf_bytes.load(std::memory_order_relaxed);
     uint64_t ovf_cap = 1;
     for (uint32_t i = 0; i < n_seg; ++i)
         ovf_cap += desc[i].esc;
@@ -1294,6 +1296,18 @@ int splitzip_set_small_tiles(splitzip_codec *codec, uint32_t max_tiles)
         if (max_tiles > sz::kSmallTiles)
             return fail(SPLITZIP_E_INVALID, "max_tiles %u exceeds %u", max_tiles, sz::kSmallTiles);
         codec->small_tiles.store(max_tiles, std::memory_order_relaxed);
+        return SPLITZIP_OK;
+    });
+}
+
+int splitzip_set_private_overflow(splitzip_codec *codec, uint64_t max_bytes)
+{
+    return guarded([&]() -> int {
+        g_last_error[0] = '\0';
+        int rc = codec_check(codec);
+        if (rc != SPLITZIP_OK)
+            return rc;
+        codec->private_ovf_bytes.store(max_bytes, std::memory_order_relaxed);
         return SPLITZIP_OK;
     });
 }

@@ -2,8 +2,10 @@
 SMALL_TILES tiles run pack and finish (one workgroup per tile adds up the earlier tiles'
 escape counts itself), larger calls run pack, sums, place and spill; calls of more than
 STAGE_TILES tiles run the pack build in which a wave gathers a group's escapes in LDS when
-it has more than 64.  Each case is encoded all four ways (``Codec.set_small_tiles``,
-``Codec.set_stage_tiles``) and each must equal the oracle byte for byte: BF16 and E5M2
+it has more than 64; escapes past a tile's slot go to the tile's own region or to a shared
+area reserved with a counter.  Each case is encoded four ways that cover every pair of these
+settings (``Codec.set_small_tiles``, ``Codec.set_stage_tiles``,
+``Codec.set_private_overflow``) and each must equal the oracle byte for byte: BF16 and E5M2
 streams spanning several tiles with ragged tails, tiles whose escapes overflow their
 slot, batches with empty and tiny segments and several codebooks, packed streams, too
 little escape room, and the 2048 / 2049-tile boundary of the default."""
@@ -23,15 +25,18 @@ pytestmark = pytest.mark.gpu
 
 O = oracle.get()
 NEVER = (1 << 32) - 1
-# (set_small_tiles, set_stage_tiles)
-MODES = {"four_launches": (0, NEVER), "pack_finish": (sz.SMALL_TILES, NEVER),
-         "four_launches_gather": (0, 0), "pack_finish_gather": (sz.SMALL_TILES, 0)}
+PRIV = sz.PRIVATE_OVERFLOW_BYTES
+# (set_small_tiles, set_stage_tiles, set_private_overflow): every pair of the three settings
+# appears with both of its values
+MODES = {"four_launches_shared": (0, NEVER, 0), "pack_finish_private": (sz.SMALL_TILES, NEVER, PRIV),
+         "four_launches_gather_private": (0, 0, PRIV), "pack_finish_gather_shared": (sz.SMALL_TILES, 0, 0)}
 
 
 def use_mode(codec, mode):
-    small, stage = MODES[mode]
+    small, stage, private = MODES[mode]
     codec.set_small_tiles(small)
     codec.set_stage_tiles(stage)
+    codec.set_private_overflow(private)
 TILE = 16384          # BF16 words per pack tile
 TILE8 = 32768         # E5M2 bytes per pack tile
 
