@@ -254,10 +254,16 @@ def test_config2_kv_layer_two_segments():
         assert np.array_equal(host(y, np.uint16), x)
 
 
+@pytest.mark.parametrize("private", [True, False])
 @pytest.mark.parametrize("C", [1024, 4096])
-def test_config4_escape_stress(C):
+def test_config4_escape_stress(C, private):
+    """The escape-stress input (4096 pack tiles, about 29 % escapes, every tile past its
+    slot): whole stream against the oracle, with the tiles' own overflow regions (the
+    default at this size) and with the shared area that they reserve from one counter."""
     wl = workloads.config4(chunk_size=C)
     codec = codec_for(wl.calibration, C)
+    if not private:
+        codec.set_private_overflow(0)
     x = wl.segments[0]
     enc = codec.encode(dev(x))
     ref = assert_same_stream(codec, enc, x)
