@@ -429,10 +429,11 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(segments, [codec.books[e.book] for e in encs], C, args.cpu_sample_words, e5m2)
 
-    metric = "encode & decode GB/s (BF16 in) + % HBM roofline + compression ratio, 8.6 GB KV"
+    metric = "encode & decode GB/s (BF16 in) + % HBM roofline + compression ratio" + \
+        (", 8.6 GB KV" if args.config == 3 and args.layers == 64 else "")
     if e5m2:
         metric = "encode & decode GB/s (E5M2 in) + % HBM roofline + compression ratio" + \
-            (", 4.3 GB E5M2 KV" if args.config == 3 else "")
+            (", 4.3 GB E5M2 KV" if args.config == 3 and args.layers == 64 else "")
     out = {
         "metric": metric,
         "value": round(value, 2),
