@@ -426,15 +426,15 @@ struct CallTimer {
 
 // Byte offsets of the encode scratch arrays for one launch.
 struct EncodeScratch {
-    uint64_t tile_count, tile_ovf, tile_prefix, ovf_tiles, slots, block_sum, group_sum, seg_total,
+    uint64_t tile_count, tile_ovf, spill_rec, ovf_tiles, slots, block_sum, group_sum, seg_total,
         ovf, total;
     EncodeScratch(uint64_t n_tiles, uint64_t ovf_cap, uint64_t n_seg, uint64_t slot_escapes)
     {
         auto up = [](uint64_t x) { return (x + 255) & ~uint64_t(255); };
         tile_count = 0;
         tile_ovf = up(tile_count + 4 * n_tiles);
-        tile_prefix = up(tile_ovf + 8 * n_tiles);
-        ovf_tiles = up(tile_prefix + 8 * n_tiles);
+        spill_rec = up(tile_ovf + 8 * n_tiles);
+        ovf_tiles = up(spill_rec + sizeof(sz::SpillRec) * n_tiles);
         slots = up(ovf_tiles + 4 * n_tiles);
         block_sum = up(slots + 4 * slot_escapes * n_tiles);
         group_sum = up(block_sum + 8 * ((n_tiles + sz::kSumTiles - 1) / sz::kSumTiles));
@@ -1021,7 +1021,7 @@ int encode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
     a.seg_total = reinterpret_cast<uint64_t *>(w->scratch + lay.seg_total);
     a.tile_count = reinterpret_cast<uint32_t *>(w->scratch + lay.tile_count);
     a.tile_ovf = reinterpret_cast<uint64_t *>(w->scratch + lay.tile_ovf);
-    a.tile_prefix = reinterpret_cast<uint64_t *>(w->scratch + lay.tile_prefix);
+    a.spill_rec = reinterpret_cast<sz::SpillRec *>(w->scratch + lay.spill_rec);
     a.ovf_tiles = reinterpret_cast<uint32_t *>(w->scratch + lay.ovf_tiles);
     a.slots = reinterpret_cast<uint32_t *>(w->scratch + lay.slots);
     a.block_sum = reinterpret_cast<uint64_t *>(w->scratch + lay.block_sum);

@@ -112,6 +112,17 @@ struct SegDesc {
 // segment lies between seg_at[t >> kSegAtShift] and the entry after it.
 constexpr int kSegAtShift = 6;
 
+// What the spill launch needs of one tile, written by place (which has it at hand) so that a
+// spill workgroup waits on one load before its data loads: the final places of the tile's
+// first escape, the tile's first word in its segment, and its range of the overflow area
+// (offset in the low 40 bits, entries to move in the high 24; 0 entries: nothing to move).
+struct __align__(16) SpillRec {
+    uint16_t *pos;
+    uint8_t *exp;
+    uint64_t base;
+    uint64_t src;
+};
+
 struct EncodeArgs {
     SegDesc seg0;                 // the only segment when n_seg == 1
     const SegDesc *segs;          // device table when n_seg > 1
@@ -123,7 +134,7 @@ struct EncodeArgs {
                                   // byte's 3-bit field in bits 5..7
     uint32_t *tile_count;         // [n_tiles] escapes per tile
     uint64_t *tile_ovf;           // [n_tiles] overflow offset of tiles past slot_escapes
-    uint64_t *tile_prefix;        // [n_tiles] escape offset in the segment (overflow tiles)
+    SpillRec *spill_rec;          // [n_tiles] written by place for the spill launch
     uint32_t *ovf_tiles;          // [n_tiles] list of the overflow tiles
     uint32_t *slots;              // [n_tiles * slot_escapes]
     uint32_t *ovf;                // [ovf_cap]

@@ -587,8 +587,24 @@ __global__ __launch_bounds__(kThreads) void encode_place_kernel(const EncodeArgs
         }
         // overflow tiles are moved by the spill launch; the others here, from their slots
         const bool spilled = count > a.slot_escapes;
-        if (spilled)
-            a.tile_prefix[u] = prefix;
+        if (valid && (spilled || a.private_ovf)) {
+            // the spill launch's record (with private regions every tile has one, so that spill
+            // reads it alone): escapes past the escape capacity, or with no exponent section,
+            // or outside the overflow area, are not moved
+            uint64_t lim = 0, off = 0;
+            if (spilled && exps) {
+                off = a.tile_ovf[u];
+                const uint64_t ovf_room = off < a.ovf_cap ? a.ovf_cap - off : 0;
+                lim = count < ovf_room ? count : ovf_room;
+                lim = lim < room ? lim : room;
+            }
+            SpillRec r;
+            r.pos = pos + prefix;
+            r.exp = exps ? exps + prefix : nullptr;
+            r.base = base;
+            r.src = off | (lim << kOvfTileShift);
+            a.spill_rec[u] = r;
+        }
         s_prefix[lane] = prefix;
         s_base[lane] = base;
         s_room[lane] = room;
@@ -735,30 +751,17 @@ __global__ __launch_bounds__(kThreads) void encode_spill_kernel(const EncodeArgs
     __shared__ MoveLds s_move;
     const uint32_t tid = threadIdx.x;
     const uint64_t cmask = (1ull << a.log2_chunk) - 1;
-    // the overflow tiles: listed by the pack launch, or, with private regions, every tile
-    // whose escapes outgrew its slot
+    // the overflow tiles: listed by the pack launch, or, with private regions, every tile (its
+    // record says how many entries it has to move: 0 when it fit its slot).  One workgroup per
+    // tile: splitting tiles, in this grid or in one sized to them, was slower.
     const uint32_t n_items = a.private_ovf ? a.n_tiles : (uint32_t)(a.ovf_ctr[1] >> kOvfTileShift);
-    // one workgroup per overflow tile (splitting a tile over 4 workgroups of this grid was
-    // slower: each workgroup then worked through four items one after the other)
     for (uint32_t i = blockIdx.x; i < n_items; i += gridDim.x) {
-        if (a.private_ovf && a.tile_count[i] <= a.slot_escapes)
-            continue;                                  // uniform: the tile fit its slot
         const uint32_t t = a.private_ovf ? i : a.ovf_tiles[i];
-        const uint32_t s = tile_segment(a, t);
-        const SegDesc sd = segment_desc(a, s);
-        const uint64_t base = (uint64_t)(t - segment_first_tile(a, s)) << a.tile_shift;
-        const uint64_t pre = a.tile_prefix[t];
-        const uint32_t cnt = a.tile_count[t];
-        const uint64_t off = a.tile_ovf[t];
-        const uint64_t room = off < a.ovf_cap ? a.ovf_cap - off : 0;
-        uint8_t *exps = a.packed ? packed_exps(sd, a.seg_total[s]) : sd.esc_exp;
-        if (!exps)
-            continue;                                  // uniform: no room for the exponents
-        // entries that lie inside the overflow area and land inside the escape sections
-        uint64_t lim = cnt < room ? cnt : room;
-        const uint64_t fit = sd.esc > pre ? sd.esc - pre : 0;
-        lim = lim < fit ? lim : fit;
-        move_escapes(a.ovf + off, lim, sd.esc_pos + pre, exps + pre, base, cmask, tid, s_move);
+        const SpillRec r = a.spill_rec[t];
+        const uint64_t lim = r.src >> kOvfTileShift;
+        if (lim == 0)
+            continue;                                  // uniform
+        move_escapes(a.ovf + (r.src & kOvfOffsetMask), lim, r.pos, r.exp, r.base, cmask, tid, s_move);
     }
 }
 
