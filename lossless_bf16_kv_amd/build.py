@@ -17,9 +17,13 @@ ARCH = "gfx950"
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Wall", "-Wextra", "-Wno-unused-parameter",
-    # never let the compiler form packed-FP32 instructions
+    # never let the compiler form packed-FP32 instructions.  The clang driver cannot scope an
+    # -Xclang pair to the device pass (-Xarch_device refuses options that take arguments), so
+    # the host pass sees the feature too and prints a notice that it does not know it; build()
+    # drops exactly that notice from the compiler output.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+_HOST_PASS_NOTICE = "'-packed-fp32-ops' is not a recognized feature for this target (ignoring feature)"
 
 
 def hipcc() -> str:
@@ -33,7 +37,13 @@ def build(out: str = LIB_PATH, extra_flags: tuple = (), verbose: bool = False) -
            "-I", CSRC, "-o", out + ".tmp", *SOURCES]
     if verbose:
         print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True, cwd=ROOT)
+    r = subprocess.run(cmd, cwd=ROOT, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    text = "".join(line for line in r.stdout.splitlines(keepends=True)
+                   if line.strip() != _HOST_PASS_NOTICE)
+    if text:
+        print(text, end="", flush=True)
+    if r.returncode != 0:
+        raise subprocess.CalledProcessError(r.returncode, cmd)
     os.replace(out + ".tmp", out)
     return out
 

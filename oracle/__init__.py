@@ -74,6 +74,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.szo_serialize.argtypes = [_u8p, _u8p, _u64p, _u16p, _u8p, ctypes.c_uint64,
                                   ctypes.c_uint64, _u8p, ctypes.c_uint32, _u8p, ctypes.c_uint64]
     lib.szo_serialize.restype = ctypes.c_int
+    lib.szo_header.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint64, _u8p,
+                               ctypes.c_uint32, _u8p]
+    lib.szo_header.restype = None
     lib.szo_stream_info.argtypes = [_u8p, ctypes.c_uint64, _u64p, ctypes.POINTER(ctypes.c_uint32),
                                     _u64p, _u8p]
     lib.szo_stream_info.restype = ctypes.c_int
@@ -202,6 +205,13 @@ class Oracle:
                                     _ptr(cb, _u8p), C, _ptr(out, _u8p), total)
         if rc != OK:
             raise OracleError(rc, "serialize")
+        return out.tobytes()
+
+    def header(self, n: int, chunk_size: int, n_escapes: int, cb: np.ndarray, flags: int = 0) -> bytes:
+        """The 64-byte canonical header (flags 0: BF16 words, 1: E5M2 bytes)."""
+        cb = np.ascontiguousarray(cb, np.uint8)
+        out = np.zeros(64, np.uint8)
+        self.lib.szo_header(n, chunk_size, n_escapes, _ptr(cb, _u8p), flags, _ptr(out, _u8p))
         return out.tobytes()
 
     def stream_info(self, buf: bytes) -> dict:

@@ -265,6 +265,31 @@ static uint64_t get_le(const uint8_t *p, int bytes)
     return v;
 }
 
+/* The 64-byte header of a canonical stream [README Roadmap: the codebook and payload
+ * metadata travel with the payload]: "SZB1", version 1, header bytes 64, chunk size, flags
+ * (0 BF16, 1 E5M2), n, n_chunks, E, the codebook, 8 reserved zero bytes; little-endian. */
+void szo_header(uint64_t n, uint32_t chunk_size, uint64_t n_escapes, const uint8_t cb[16],
+                uint32_t flags, uint8_t out[64])
+{
+    int i;
+
+    memset(out, 0, 64);
+    out[0] = 'S';
+    out[1] = 'Z';
+    out[2] = 'B';
+    out[3] = '1';
+    put_le(out + 4, 1, 2);          /* version */
+    put_le(out + 6, 64, 2);         /* header bytes */
+    put_le(out + 8, chunk_size, 4);
+    put_le(out + 12, flags, 4);
+    put_le(out + 16, n, 8);
+    put_le(out + 24, ceil_div(n, chunk_size), 8);
+    put_le(out + 32, n_escapes, 8);
+    for (i = 0; i < 16; ++i)
+        out[40 + i] = cb[i];
+    /* bytes 56..63 stay zero (reserved) */
+}
+
 /* The canonical stream: header with the codebook, then the sections [README Roadmap]. */
 int szo_serialize(const uint8_t *sm, const uint8_t *codes, const uint64_t *chunk_off,
                   const uint16_t *esc_pos, const uint8_t *esc_exp, uint64_t n, uint64_t n_escapes,
@@ -278,22 +303,7 @@ int szo_serialize(const uint8_t *sm, const uint8_t *codes, const uint64_t *chunk
         return SZO_BAD_ARGUMENT;
     n_chunks = ceil_div(n, chunk_size);
 
-    memset(out, 0, 64);
-    out[0] = 'S';
-    out[1] = 'Z';
-    out[2] = 'B';
-    out[3] = '1';
-    put_le(out + 4, 1, 2);          /* version */
-    put_le(out + 6, 64, 2);         /* header bytes */
-    put_le(out + 8, chunk_size, 4);
-    put_le(out + 12, 0, 4);         /* flags */
-    put_le(out + 16, n, 8);
-    put_le(out + 24, n_chunks, 8);
-    put_le(out + 32, n_escapes, 8);
-    for (i = 0; i < 16; ++i)
-        out[40 + i] = cb[i];
-    /* bytes 56..63 stay zero (reserved) */
-
+    szo_header(n, chunk_size, n_escapes, cb, 0, out);
     p = 64;
     for (i = 0; i < n; ++i)
         out[p++] = sm[i];
@@ -585,21 +595,7 @@ int szo8_serialize(const uint8_t *sm3, const uint8_t *codes, const uint64_t *chu
         return SZO_BAD_ARGUMENT;
     n_chunks = ceil_div(n, chunk_size);
 
-    memset(out, 0, 64);
-    out[0] = 'S';
-    out[1] = 'Z';
-    out[2] = 'B';
-    out[3] = '1';
-    put_le(out + 4, 1, 2);          /* version */
-    put_le(out + 6, 64, 2);         /* header bytes */
-    put_le(out + 8, chunk_size, 4);
-    put_le(out + 12, 1, 4);         /* flags: E5M2 elements */
-    put_le(out + 16, n, 8);
-    put_le(out + 24, n_chunks, 8);
-    put_le(out + 32, n_escapes, 8);
-    for (i = 0; i < 16; ++i)
-        out[40 + i] = cb[i];
-
+    szo_header(n, chunk_size, n_escapes, cb, 1, out);     /* flags 1: E5M2 elements */
     p = 64;
     for (i = 0; i < ceil_div(3u * n, 8u); ++i)
         out[p++] = sm3[i];

@@ -83,6 +83,9 @@ int szo_decode(const uint8_t *sm, const uint8_t *codes, const uint64_t *chunk_of
                const uint8_t cb[16], uint32_t chunk_size, uint16_t *y);
 
 /* Write the canonical stream into out[out_len]; out_len must equal szo_compressed_bytes. */
+/* The 64-byte header of a canonical stream (flags 0: BF16 words, 1: E5M2 bytes). */
+void szo_header(uint64_t n, uint32_t chunk_size, uint64_t n_escapes, const uint8_t cb[16],
+                uint32_t flags, uint8_t out[64]);
 int szo_serialize(const uint8_t *sm, const uint8_t *codes, const uint64_t *chunk_off,
                   const uint16_t *esc_pos, const uint8_t *esc_exp, uint64_t n, uint64_t n_escapes,
                   const uint8_t cb[16], uint32_t chunk_size, uint8_t *out, uint64_t out_len);

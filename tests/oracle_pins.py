@@ -46,6 +46,7 @@ def check_worked_example(o) -> None:
     s = o.serialize(enc)
     assert len(s) == int(g["compressed_bytes"])
     assert s[:64] == hex_bytes(g["header"]), "header"
+    assert o.header(x.size, C, enc["n_escapes"], cb, 0) == hex_bytes(g["header"]), "header writer"
     # body = sections in order, little-endian
     body = (hex_bytes(g["sm"]) + hex_bytes(g["codes"])
             + b"".join(v.to_bytes(8, "little") for v in ints(g["chunk_off"]))
@@ -260,6 +261,7 @@ def check_worked_example8(o) -> None:
     assert e["compressed_bytes"] == int(g["compressed_bytes"])
     s = o.serialize8(e)
     assert len(s) == int(g["compressed_bytes"]) and s[:64] == hex_bytes(g["header"])
+    assert o.header(x.size, C, e["n_escapes"], cb, 1) == hex_bytes(g["header"]), "header writer"
     assert np.array_equal(o.decode8(e), x)
     assert np.array_equal(o.decode_stream8(s, cb), x)
     e7 = o.encode8(x[:7], cb, C)

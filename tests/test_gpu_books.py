@@ -13,7 +13,8 @@ import torch
 import lossless_bf16_kv_amd as sz
 import oracle
 import workloads
-from test_gpu_parity import DEV, assert_same_stream, check_properties, check_sampled_chunks, dev, host
+import stream_check
+from test_gpu_parity import DEV, assert_same_stream, check_properties, dev, host
 
 pytestmark = pytest.mark.gpu
 
@@ -120,8 +121,9 @@ def kv8():
 def test_per_layer_kv_books_long_prefill(kv8):
     """8 layers of the long-prefill KV generator (2^29 words), one codebook per layer and
     K/V (16 books), all 16 tensors in one encode and one decode launch: codebooks from the
-    oracle's calibration of each part, E per tensor from the oracle's histogram, sampled
-    chunks against the oracle, bitwise round trip, and fewer escapes than one codebook."""
+    oracle's calibration of each part, E per tensor from the oracle's histogram, every
+    stream whole against the oracle with its own book, bitwise round trip, and fewer
+    escapes than one codebook."""
     wl = kv8
     parts = workloads.kv_parts(wl.segments[0], LAYERS, TOKENS)
     cals = workloads.kv_parts(wl.calibration, LAYERS, CAL_TOKENS)
@@ -132,12 +134,10 @@ def test_per_layer_kv_books_long_prefill(kv8):
         assert codec.books[b] == bytes(cb) and cov[b] == cv
     xds = [dev(p) for p in parts]
     encs = codec.encode_batch(xds, books=list(range(len(parts))))
-    rng = np.random.default_rng(7)
-    for i, (x, e) in enumerate(zip(parts, encs)):
+    for x, e in zip(parts, encs):
         check_properties(codec, e, x, O.histogram(x))
-        if i % 5 == 0:
-            n_chunks = x.size // 1024
-            check_sampled_chunks(codec, e, x, sorted(set(rng.integers(0, n_chunks, 6).tolist()) | {0, n_chunks - 1}))
+    stream_check.check_cases([stream_check.case_from_encoded(f"layer {i // 2} {'KV'[i % 2]}", e, x)
+                              for i, (x, e) in enumerate(zip(parts, encs))])
     for xd, y in zip(xds, codec.decode_batch(encs)):
         assert torch.equal(y, xd)
     one = sz.Codec(DEV, 1024)

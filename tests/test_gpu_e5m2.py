@@ -19,6 +19,7 @@ import torch
 import lossless_bf16_kv_amd as sz
 import oracle
 import oracle_pins as pins
+import stream_check
 import workloads
 from conftest import hex_bytes, ints, load_golden
 
@@ -280,19 +281,9 @@ def test_long_prefill_e5m2_full_size(kv8):
     assert enc.n_escapes == E and enc.compressed_bytes == O.compressed_bytes8(x.size, C, E)
     off = enc.chunk_off
     assert int(off[0]) == 0 and int(off[-1]) == E and bool((off[1:] >= off[:-1]).all())
-    # sampled chunks, each oracle-encoded on its own (C = 1024: a chunk's fields are whole bytes)
-    rng = np.random.default_rng(8)
-    n_chunks = x.size // C
-    offs = host(enc.chunk_off, np.uint64)
-    for c in sorted(set(rng.integers(0, n_chunks, 40).tolist()) | {0, n_chunks - 1}):
-        lo, hi = c * C, (c + 1) * C
-        ref = O.encode8(x[lo:hi], cb, C)
-        a, b = int(offs[c]), int(offs[c + 1])
-        assert b - a == ref["n_escapes"], c
-        assert np.array_equal(host(enc.sm[3 * lo // 8:3 * hi // 8], np.uint8), ref["sm3"])
-        assert np.array_equal(host(enc.codes[lo // 2:hi // 2], np.uint8), ref["codes"])
-        assert np.array_equal(host(enc.esc_pos_buf[a:b], np.uint16), ref["esc_pos"])
-        assert np.array_equal(host(enc.esc_exp_buf[a:b], np.uint8), ref["esc_exp"])
+    # every byte of every section against the oracle, window by window
+    stream_check.check_cases([stream_check.case_from_encoded("config3 e5m2", enc, x,
+                                                             stream_check.ELEM_E5M2)])
     y = codec.decode(enc)
     assert torch.equal(y.view(torch.uint8), xd)
 
@@ -312,17 +303,17 @@ def test_escape_stress_e5m2():
 
 
 def test_ragged_batch_e5m2():
-    """Config 5 (512 K/V segments of 256 requests, one launch) cast to E5M2: full streams of a
-    spread of segments against the oracle, E and offsets of every segment from the oracle's
-    histograms, and round trips."""
+    """Config 5 (512 K/V segments of 256 requests, one launch) cast to E5M2: every stream whole
+    against the oracle, E and offsets of every segment from the oracle's histograms, and
+    round trips."""
     wl = workloads.cast_e5m2(workloads.config5())
     assert len(wl.segments) == 512
     codec = codec_for(wl.calibration, 1024)
     cb = np.frombuffer(codec.codebook, np.uint8)
     xds = [dev8(s) for s in wl.segments]
     encs = codec.encode_batch(xds)
-    for i in range(0, 512, 37):
-        assert_same_stream(codec, encs[i], wl.segments[i])
+    stream_check.check_cases([stream_check.case_from_encoded(f"segment {i}", e, x, stream_check.ELEM_E5M2)
+                              for i, (x, e) in enumerate(zip(wl.segments, encs))])
     for x, e in zip(wl.segments, encs):
         h = O.histogram8(x)
         E = int(x.size - sum(int(h[v]) for v in cb))

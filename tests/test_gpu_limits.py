@@ -9,8 +9,9 @@ import torch
 
 import lossless_bf16_kv_amd as sz
 import oracle
+import stream_check
 import workloads
-from test_gpu_parity import DEV, assert_same_stream, dev
+from test_gpu_parity import DEV, dev
 
 pytestmark = pytest.mark.gpu
 
@@ -33,8 +34,8 @@ def test_max_books_and_4096_segments_in_one_call():
         ref = O.encode(x, np.frombuffer(books[i], np.uint8), C)
         assert e.book == i
         assert e.n_escapes == ref["n_escapes"] and e.compressed_bytes == ref["compressed_bytes"]
-        if i % 97 == 0:
-            assert_same_stream(codec, e, x)
+    stream_check.check_cases([stream_check.case_from_encoded(f"segment {i}", e, x)
+                              for i, (x, e) in enumerate(zip(xs_np, encs))])
     ys = codec.decode_batch(encs)
     got = torch.cat([y.view(torch.int16).reshape(-1) for y in ys]).cpu().numpy().view(np.uint16)
     assert np.array_equal(got, np.concatenate(xs_np))

@@ -11,6 +11,7 @@ import torch
 
 import lossless_bf16_kv_amd as sz
 import oracle
+import stream_check
 import workloads
 from test_gpu_parity import DEV, codec_for, dev, host
 
@@ -133,12 +134,18 @@ def test_packed_header_and_length_checks():
 
 
 def test_config5_ragged_batch_packed():
+    """512 packed streams in one launch: every stream whole against the oracle."""
     wl = workloads.config5()
     codec = codec_for(wl.calibration, wl.chunk_size)
+    cb = np.frombuffer(codec.codebook, np.uint8)
     xds = [dev(s) for s in wl.segments]
     packed = codec.encode_packed_batch(xds)
-    for i in range(0, 512, 41):
-        assert packed[i].to_bytes() == oracle_stream(wl.segments[i], codec.codebook, wl.chunk_size)
+    cases = []
+    for i, (x, p) in enumerate(zip(wl.segments, packed)):
+        case, head = stream_check.case_from_packed(f"segment {i}", p.stream, x, cb, wl.chunk_size)
+        assert head == O.header(x.size, wl.chunk_size, p.n_escapes, cb, 0)
+        cases.append(case)
+    stream_check.check_cases(cases)
     encs = codec.encode_batch(xds)
     assert [p.n_escapes for p in packed] == [e.n_escapes for e in encs]
     for xd, y in zip(xds, codec.decode_packed_batch(packed)):
@@ -146,8 +153,8 @@ def test_config5_ragged_batch_packed():
 
 
 def test_config3_packed_full_size():
-    """2^32 words into one 6.5 GB packed stream: header, sampled chunks of every section at
-    their packed offsets against the oracle, and the bitwise round trip."""
+    """2^32 words into one 6.5 GB packed stream: the header and every byte of every section
+    at its packed offset against the oracle, and the bitwise round trip."""
     wl = workloads.config3()
     x = wl.segments[0]
     C = 1024
@@ -158,24 +165,10 @@ def test_config3_packed_full_size():
     hist = O.histogram(x)
     assert E == n - sum(int(hist[e]) for e in codec.codebook)
     assert p.stream_bytes == O.compressed_bytes(n, C, E)
-    s = p.stream
-    head = s[:64].cpu().numpy().tobytes()
-    assert head[:4] == b"SZB1" and int.from_bytes(head[32:40], "little") == E and head[40:56] == codec.codebook
-    sm0, cd0 = 64, 64 + n
-    off0 = cd0 + n // 2
-    pos0 = off0 + 8 * (n // C + 1)
-    exp0 = pos0 + 2 * E
     cb = np.frombuffer(codec.codebook, np.uint8)
-    rng = np.random.default_rng(11)
-    for c in sorted(set(rng.integers(0, n // C, 40).tolist()) | {0, n // C - 1}):
-        lo, hi = c * C, (c + 1) * C
-        ref = O.encode(x[lo:hi], cb, C)
-        a = int(s[off0 + 8 * c:off0 + 8 * c + 8].cpu().numpy().view(np.uint64)[0])
-        b = int(s[off0 + 8 * (c + 1):off0 + 8 * (c + 2)].cpu().numpy().view(np.uint64)[0])
-        assert b - a == ref["n_escapes"]
-        assert np.array_equal(s[sm0 + lo:sm0 + hi].cpu().numpy(), ref["sm"])
-        assert np.array_equal(s[cd0 + lo // 2:cd0 + hi // 2].cpu().numpy(), ref["codes"])
-        assert np.array_equal(s[pos0 + 2 * a:pos0 + 2 * b].cpu().numpy().view(np.uint16), ref["esc_pos"])
-        assert np.array_equal(s[exp0 + a:exp0 + b].cpu().numpy(), ref["esc_exp"])
+    case, head = stream_check.case_from_packed("config3 packed", p.stream, x, cb, C)
+    assert head == O.header(n, C, E, cb, 0)
+    stream_check.check_cases([case])
+    del case
     y = codec.decode_packed(p)
     assert torch.equal(y.view(torch.int16), xd)

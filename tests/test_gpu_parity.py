@@ -2,9 +2,10 @@
 
 Encoded streams must equal the oracle's byte for byte, decode must return the input
 bit for bit, and calibration must give the oracle's histogram, codebook and coverage.
-Small and mid-size inputs are compared element by element; the full-size workloads
-(8.6 GB long-prefill KV, 512-segment ragged batch) are compared on sampled chunks
-plus properties that hold at any size."""
+Small and mid-size inputs are compared element by element in one piece; the full-size
+workloads (8.6 GB long-prefill KV, 512-segment ragged batch) are compared whole too, every
+byte of every section, against the oracle encoding the input window by window
+(tests/stream_check.py)."""
 from __future__ import annotations
 
 import ctypes
@@ -16,6 +17,7 @@ import torch
 import lossless_bf16_kv_amd as sz
 import oracle
 import oracle_pins as pins
+import stream_check
 import workloads
 from conftest import hex_bytes, ints
 
@@ -271,22 +273,6 @@ def test_config4_escape_stress(C, private):
     assert np.array_equal(host(codec.decode(enc), np.uint16), x)
 
 
-def check_sampled_chunks(codec, enc, x, chunks):
-    """Oracle-encode each sampled chunk on its own and compare with the GPU sections."""
-    C = codec.chunk_size
-    cb = np.frombuffer(enc.codebook, np.uint8)
-    off = host(enc.chunk_off, np.uint64)
-    for c in chunks:
-        lo, hi = c * C, min((c + 1) * C, x.size)
-        ref = O.encode(x[lo:hi], cb, C)
-        a, b = int(off[c]), int(off[c + 1])
-        assert b - a == ref["n_escapes"], f"chunk {c}"
-        assert np.array_equal(host(enc.sm[lo:hi], np.uint8), ref["sm"])
-        assert np.array_equal(host(enc.codes[lo // 2:(hi + 1) // 2], np.uint8), ref["codes"])
-        assert np.array_equal(host(enc.esc_pos_buf[a:b], np.uint16), ref["esc_pos"])
-        assert np.array_equal(host(enc.esc_exp_buf[a:b], np.uint8), ref["esc_exp"])
-
-
 def check_properties(codec, enc, x, hist_x):
     """Size-independent checks: E from the oracle's exact histogram, offsets, sizes."""
     C = codec.chunk_size
@@ -308,6 +294,8 @@ def config3_data():
 
 @pytest.mark.parametrize("C", [1024, 4096])
 def test_config3_long_prefill_full_size(config3_data, C):
+    """2^32 words in one segment, the launch sequence the bench times: every byte of every
+    section against the oracle, E from the oracle's histogram, the size, the round trip."""
     wl = config3_data
     x = wl.segments[0]
     assert x.size == 1 << 32
@@ -316,11 +304,8 @@ def test_config3_long_prefill_full_size(config3_data, C):
     cb, cov, _ = O.calibrate(wl.calibration)
     assert codec.codebook == bytes(cb) and codec.coverage == cov
     enc = codec.encode(xd)
-    rng = np.random.default_rng(C)
-    n_chunks = x.size // C
-    sample = sorted(set(rng.integers(0, n_chunks, 48).tolist()) | {0, 1, n_chunks - 1})
-    check_sampled_chunks(codec, enc, x, sample)
     check_properties(codec, enc, x, O.histogram(x))
+    stream_check.check_cases([stream_check.case_from_encoded(f"config3 C={C}", enc, x)])
     y = codec.decode(enc)
     assert torch.equal(y, xd)
     del y
@@ -333,15 +318,16 @@ def test_config3_full_size_histogram(config3_data):
 
 
 def test_config5_ragged_batch():
+    """512 segments in one encode launch and one decode launch: every stream whole."""
     wl = workloads.config5()
     codec = codec_for(wl.calibration, wl.chunk_size)
     assert len(wl.segments) == 512
     xds = [dev(s) for s in wl.segments]
     encs = codec.encode_batch(xds)                 # one launch, 512 segments
-    for i in range(0, 512, 37):                    # full streams of a spread of segments
-        assert_same_stream(codec, encs[i], wl.segments[i])
     for x, e in zip(wl.segments, encs):
         check_properties(codec, e, x, O.histogram(x))
+    stream_check.check_cases([stream_check.case_from_encoded(f"config5 segment {i}", e, x)
+                              for i, (x, e) in enumerate(zip(wl.segments, encs))])
     ys = codec.decode_batch(encs)                  # one launch
     for xd, y in zip(xds, ys):
         assert torch.equal(y, xd)

@@ -214,8 +214,9 @@ MUTANTS = [
     ("E5M2 ranking misses exponent 31", "for (e = 0; e < 32; ++e) {\n            if (taken[e])",
      "for (e = 0; e < 31; ++e) {\n            if (taken[e])"),
     ("E5M2 ties ranked toward the larger exponent", "hist[best] < hist[e]", "hist[best] <= hist[e]"),
-    ("E5M2 header flags 0", "put_le(out + 12, 1, 4);         /* flags: E5M2 elements */",
-     "put_le(out + 12, 0, 4);         /* flags: E5M2 elements */"),
+    ("E5M2 header flags 0", "szo_header(n, chunk_size, n_escapes, cb, 1, out);",
+     "szo_header(n, chunk_size, n_escapes, cb, 0, out);"),
+    ("header without n_chunks", "put_le(out + 24, ceil_div(n, chunk_size), 8);", "put_le(out + 24, n, 8);"),
     ("codebook of 15", "for (k = 0; k < 16; ++k)\n        if (cb[k] == e)",
      "for (k = 0; k < 15; ++k)\n        if (cb[k] == e)"),
 ]
