@@ -212,6 +212,35 @@ int splitzip_encode_async(splitzip_codec *codec, uint32_t n_seg, const splitzip_
                           void *stream, uint64_t *d_result);
 
 /*
+ * Allocation-free encode, for callers that cannot allocate device memory during the call:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same encode as splitzip_encode_async (same arguments, same d_result contract, the same
+ * kernels and the same bytes written), except that its scratch is one fixed device array of
+ * SPLITZIP_NOALLOC_SCRATCH_BYTES per GPU, held from the library's load until the process
+ * ends, instead of the codec's per-stream workspace.  The call allocates nothing (no
+ * hipMalloc, pinned staging or host heap) and only enqueues kernels on `stream`; segment
+ * descriptors travel to the GPU as kernel arguments.  Per-kernel timing does not cover it.
+ *
+ * Limits.  At most SPLITZIP_NOALLOC_MAX_SEGMENTS segments, and the call's scratch must fit
+ * the array:
+ *   256 + [n_seg > 1] (80 n_seg + 4 (n_seg + 2 + ceil(tiles / 64)))
+ *       + about 560 B per tile (BF16 tile = 16384 words; E5M2: 1072 B per 32768-byte tile)
+ *       + 4 (1 + sum of esc_capacity)
+ * (each part rounded up to 256 bytes); e.g. about 3 GB of BF16 input with an escape
+ * capacity of 0.5 % of its words.  A call over a limit returns SPLITZIP_E_INVALID before
+ * anything is enqueued, with the bytes it would need in the message.
+ *
+ * Every call on one GPU shares that GPU's array and leaves its contents behind; each call
+ * clears what must start at zero.  Calls whose GPU work overlaps on one GPU (different
+ * streams, or other host threads) race on the array and corrupt each other's output: order
+ * them on one stream or with events.
+ */
+#define SPLITZIP_NOALLOC_SCRATCH_BYTES (64ull << 20)
+#define SPLITZIP_NOALLOC_MAX_SEGMENTS 4096u
+int splitzip_encode_noalloc(splitzip_codec *codec, uint32_t n_seg, const splitzip_segment *segs,
+                            void *stream, uint64_t *d_result);
+
+/*
  * Decode (README "Abstract": the dense path looks each code up in the codebook, the sparse
  * escape correction restores the other exponents; "Codec API": decode returns the tensor
  * bit for bit).  Decode n_seg segments (host array `segs`, n_escapes as written by encode) into

@@ -114,6 +114,7 @@ def lib() -> ctypes.CDLL:
     L.splitzip_e5m2_compressed_bytes.restype = u64
     L.splitzip_encode.argtypes = [vp, u32, P(splitzip_segment), vp]
     L.splitzip_encode_async.argtypes = [vp, u32, P(splitzip_segment), vp, vp]
+    L.splitzip_encode_noalloc.argtypes = [vp, u32, P(splitzip_segment), vp, vp]
     L.splitzip_decode.argtypes = [vp, u32, P(splitzip_segment), vp, vp]
     L.splitzip_encode_packed.argtypes = [vp, u32, P(splitzip_packed), vp, vp]
     L.splitzip_decode_packed.argtypes = [vp, u32, P(splitzip_packed), vp, vp]
@@ -140,7 +141,7 @@ def lib() -> ctypes.CDLL:
               "splitzip_calibrate_books", "splitzip_codec_from_codebooks", "splitzip_codec_books",
               "splitzip_histogram", "splitzip_exponent_stats", "splitzip_encode_packed",
               "splitzip_decode_packed",
-              "splitzip_encode", "splitzip_encode_async", "splitzip_decode",
+              "splitzip_encode", "splitzip_encode_async", "splitzip_encode_noalloc", "splitzip_decode",
               "splitzip_write_header", "splitzip_profile", "splitzip_profile_read",
               "splitzip_set_small_tiles", "splitzip_set_stage_tiles", "splitzip_set_private_overflow",
               "splitzip_read_header", "splitzip_check_header", "splitzip_calibrate_e5m2",
@@ -304,6 +305,16 @@ def splitzip_encode(codec: int, segs, stream: int = 0) -> int:
 def splitzip_encode_async(codec: int, segs, stream: int, d_result: int) -> None:
     """Enqueue an encode; error bits and per-segment E land in d_result (device u64[1+n])."""
     _check(lib().splitzip_encode_async(codec, len(segs), segs, stream or None, d_result))
+
+
+def splitzip_encode_noalloc(codec: int, segs, stream: int, d_result: int) -> None:
+    """splitzip_encode_async with its scratch in the library's fixed device array: the call
+    allocates nothing (for callers that cannot allocate); the same d_result contract."""
+    _check(lib().splitzip_encode_noalloc(codec, len(segs), segs, stream or None, d_result))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20      # SPLITZIP_NOALLOC_SCRATCH_BYTES
+NOALLOC_MAX_SEGMENTS = 4096           # SPLITZIP_NOALLOC_MAX_SEGMENTS
 
 
 def splitzip_decode(codec: int, segs, stream: int = 0, d_error: int = 0) -> None:

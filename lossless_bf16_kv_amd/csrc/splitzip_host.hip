@@ -173,6 +173,21 @@ struct Workspace {
     }
 };
 
+// ---- scratch of the allocation-free encode -------------------------------------------------
+// One fixed array per device, shared by every splitzip_encode_noalloc call on that device.
+// In host code the name only stands for the array: a kernel gets the device copy's address,
+// which hipGetSymbolAddress returns with that device current (noalloc_base below).
+static __device__ __align__(256) uint8_t noalloc_scratch[SPLITZIP_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kNoAllocDevices = 64;
+
+struct NoAllocDevice {
+    std::mutex mu;             // serializes the host side of the calls on the device
+    uint8_t *base = nullptr;   // the device's copy of noalloc_scratch, once resolved
+};
+
+NoAllocDevice g_noalloc[kNoAllocDevices];
+
 }  // namespace
 
 struct splitzip_codec {
@@ -572,6 +587,38 @@ int stage_descriptors(Workspace *w, const std::vector<sz::SegDesc> &segs,
     return SPLITZIP_OK;
 }
 
+// Validation of segment i; its descriptor into out.
+int check_segment(const splitzip_codec *c, uint32_t i, const splitzip_segment &g, bool encode,
+                  sz::SegDesc &out)
+{
+    if (g.n >= sz::kMaxSegmentWords)
+        return fail(SPLITZIP_E_INVALID, "segment %u: n = %llu exceeds 2^38 - 1", i,
+                    (unsigned long long)g.n);
+    if (!g.chunk_off || !aligned(g.chunk_off, 8))
+        return fail(SPLITZIP_E_INVALID, "segment %u: chunk_off NULL or not 8-byte aligned", i);
+    if (g.n > 0) {
+        if (!g.data || !g.sm || !g.codes)
+            return fail(SPLITZIP_E_INVALID, "segment %u: NULL data/sm/codes", i);
+        if (!aligned(g.data, 16) || !aligned(g.sm, 16) || !aligned(g.codes, 16))
+            return fail(SPLITZIP_E_INVALID, "segment %u: data/sm/codes not 16-byte aligned", i);
+    }
+    const uint64_t esc = encode ? g.esc_capacity : g.n_escapes;
+    if (esc > 0 && (!g.esc_pos || !g.esc_exp || !aligned(g.esc_pos, 2)))
+        return fail(SPLITZIP_E_INVALID, "segment %u: escape arrays NULL or misaligned", i);
+    if (!encode && g.n_escapes > g.n)
+        return fail(SPLITZIP_E_FORMAT, "segment %u: %llu escapes for %llu words", i,
+                    (unsigned long long)g.n_escapes, (unsigned long long)g.n);
+    if (g.book >= c->n_books)
+        return fail(SPLITZIP_E_INVALID, "segment %u: book %u, the codec has %u", i, g.book,
+                    c->n_books);
+    out = sz::SegDesc{g.data, g.sm, g.codes, g.chunk_off, g.esc_pos, g.esc_exp, g.n, esc,
+                      g.book, 0u, nullptr};
+    return SPLITZIP_OK;
+}
+
+// Tiles of a segment of n elements (at least one, so that every segment has a first tile).
+uint64_t segment_tiles(uint64_t n, uint64_t tile_words) { return std::max<uint64_t>(1, ceil_div(n, tile_words)); }
+
 // Shared validation of segment arrays; builds descriptors and tile starts.
 int prepare_segments_tiled(const splitzip_codec *c, uint32_t n_seg, const splitzip_segment *segs,
                            bool encode, uint64_t tile_words, std::vector<sz::SegDesc> &desc,
@@ -585,31 +632,11 @@ int prepare_segments_tiled(const splitzip_codec *c, uint32_t n_seg, const splitz
     tiles.resize((size_t)n_seg + 1);
     uint64_t total = 0;
     for (uint32_t i = 0; i < n_seg; ++i) {
-        const splitzip_segment &g = segs[i];
-        if (g.n >= sz::kMaxSegmentWords)
-            return fail(SPLITZIP_E_INVALID, "segment %u: n = %llu exceeds 2^38 - 1", i,
-                        (unsigned long long)g.n);
-        if (!g.chunk_off || !aligned(g.chunk_off, 8))
-            return fail(SPLITZIP_E_INVALID, "segment %u: chunk_off NULL or not 8-byte aligned", i);
-        if (g.n > 0) {
-            if (!g.data || !g.sm || !g.codes)
-                return fail(SPLITZIP_E_INVALID, "segment %u: NULL data/sm/codes", i);
-            if (!aligned(g.data, 16) || !aligned(g.sm, 16) || !aligned(g.codes, 16))
-                return fail(SPLITZIP_E_INVALID, "segment %u: data/sm/codes not 16-byte aligned", i);
-        }
-        const uint64_t esc = encode ? g.esc_capacity : g.n_escapes;
-        if (esc > 0 && (!g.esc_pos || !g.esc_exp || !aligned(g.esc_pos, 2)))
-            return fail(SPLITZIP_E_INVALID, "segment %u: escape arrays NULL or misaligned", i);
-        if (!encode && g.n_escapes > g.n)
-            return fail(SPLITZIP_E_FORMAT, "segment %u: %llu escapes for %llu words", i,
-                        (unsigned long long)g.n_escapes, (unsigned long long)g.n);
-        if (g.book >= c->n_books)
-            return fail(SPLITZIP_E_INVALID, "segment %u: book %u, the codec has %u", i, g.book,
-                        c->n_books);
-        desc[i] = sz::SegDesc{g.data, g.sm, g.codes, g.chunk_off, g.esc_pos, g.esc_exp, g.n, esc,
-                              g.book, 0u, nullptr};
+        const int rc = check_segment(c, i, segs[i], encode, desc[i]);
+        if (rc != SPLITZIP_OK)
+            return rc;
         tiles[i] = (uint32_t)total;
-        total += std::max<uint64_t>(1, ceil_div(g.n, tile_words));
+        total += segment_tiles(segs[i].n, tile_words);
         if (total > 0xFFFFFFF0ull)
             return fail(SPLITZIP_E_INVALID, "too many tiles in one call");
     }
@@ -624,6 +651,12 @@ int64_t common_book(uint32_t n_seg, const splitzip_segment *segs)
         if (segs[i].book != segs[0].book)
             return -1;
     return segs[0].book;
+}
+
+// Entries of a pack tile's escape slot for the codec's element type.
+uint32_t slot_escapes(const splitzip_codec *c)
+{
+    return c->elem == sz::kElemE5M2 ? sz::kE8SlotEscapes : sz::kSlotEscapes;
 }
 
 // Elements per encode (pack) or decode tile of the codec's element type.
@@ -977,6 +1010,63 @@ int splitzip_codec_info(const splitzip_codec *codec, uint8_t codebook[16], uint3
 
 namespace {
 
+// The call's shape, its codebook tables and the encode scratch arrays at `base` (laid out as
+// `lay`) into a.  res: the error word, then E per segment.
+void set_encode_args(sz::EncodeArgs &a, const splitzip_codec *codec, uint32_t n_seg, uint32_t n_tiles,
+                     int64_t book, bool packed, uint8_t *base, const EncodeScratch &lay,
+                     unsigned long long *ovf_ctr, uint64_t ovf_cap, bool private_ovf, uint8_t *res)
+{
+    const uint32_t tile_shift = codec->elem == sz::kElemE5M2 ? sz::kE8EncTileShift : sz::kEncTileShift;
+    // one book for the whole call: its LUT directly; several: the table, indexed per segment
+    a.lut = codec->d_lut + 256 * (book < 0 ? 0 : book);
+    a.multi_book = book < 0;
+    a.cbs = codec->d_cbs;
+    a.packed = packed;
+    a.seg_total = reinterpret_cast<uint64_t *>(base + lay.seg_total);
+    a.tile_count = reinterpret_cast<uint32_t *>(base + lay.tile_count);
+    a.tile_ovf = reinterpret_cast<uint64_t *>(base + lay.tile_ovf);
+    a.spill_rec = reinterpret_cast<sz::SpillRec *>(base + lay.spill_rec);
+    a.ovf_tiles = reinterpret_cast<uint32_t *>(base + lay.ovf_tiles);
+    a.slots = reinterpret_cast<uint32_t *>(base + lay.slots);
+    a.block_sum = reinterpret_cast<uint64_t *>(base + lay.block_sum);
+    a.group_sum = reinterpret_cast<uint64_t *>(base + lay.group_sum);
+    a.ovf = reinterpret_cast<uint32_t *>(base + lay.ovf);
+    a.ovf_ctr = ovf_ctr;
+    a.ovf_cap = ovf_cap;
+    a.err = reinterpret_cast<uint32_t *>(res);
+    a.seg_escapes = reinterpret_cast<uint64_t *>(res + 8);
+    a.n_seg = n_seg;
+    a.n_tiles = n_tiles;
+    a.log2_chunk = codec->log2_chunk;
+    a.elem = codec->elem;
+    a.tile_shift = tile_shift;
+    a.slot_escapes = codec->elem == sz::kElemE5M2 ? sz::kE8SlotEscapes : sz::kSlotEscapes;
+    a.private_ovf = private_ovf ? 1u : 0u;
+    a.stage = n_tiles > codec->stage_tiles.load(std::memory_order_relaxed) ? 1u : 0u;
+}
+
+// The encode launches: pack and finish for calls of at most small_tiles tiles, else pack,
+// sums, place and spill.  w (optional) times them when the codec is profiling.
+hipError_t run_encode_stages(splitzip_codec *codec, Workspace *w, const sz::EncodeArgs &a, hipStream_t stream)
+{
+    static const int kSmallStages[] = {sz::kStagePack, sz::kStageFinish};
+    static const int kSmallKinds[] = {SPLITZIP_KERNEL_PACK, SPLITZIP_KERNEL_FINISH};
+    static const int kStages[] = {sz::kStagePack, sz::kStageSums, sz::kStagePlace, sz::kStageSpill};
+    static const int kKinds[] = {SPLITZIP_KERNEL_PACK, SPLITZIP_KERNEL_SUMS, SPLITZIP_KERNEL_PLACE,
+                                 SPLITZIP_KERNEL_SPILL};
+    const bool small = a.n_tiles <= codec->small_tiles.load(std::memory_order_relaxed);
+    const int *stages = small ? kSmallStages : kStages;
+    const int n_stages = small ? 2 : 4;
+    CallTimer timer(codec, w, stream, small ? kSmallKinds : kKinds, n_stages);
+    timer.mark();
+    hipError_t e = hipSuccess;
+    for (int i = 0; i < n_stages && e == hipSuccess; ++i) {
+        e = sz::launch_encode_stage(stages[i], a, stream);
+        timer.mark();
+    }
+    return e;
+}
+
 // Workspace and launch shared by the blocking and non-blocking encodes (sections or packed
 // streams); the caller holds the workspace lock.  d_result (optional): where the kernel
 // writes its error bits and per-segment escape counts instead of the workspace's result
@@ -1001,8 +1091,7 @@ int encode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
         ovf_cap += desc[i].esc;
     if (private_ovf)
         ovf_cap = (uint64_t)n_tiles << tile_shift;
-    const uint32_t slot_escapes = codec->elem == sz::kElemE5M2 ? sz::kE8SlotEscapes : sz::kSlotEscapes;
-    const EncodeScratch lay(n_tiles, ovf_cap, n_seg, slot_escapes);
+    const EncodeScratch lay(n_tiles, ovf_cap, n_seg, slot_escapes(codec));
     if ((rc = ensure_scratch(w, lay.total)) != SPLITZIP_OK)
         return rc;
     if (!d_result && (rc = ensure_result(w, n_seg)) != SPLITZIP_OK)
@@ -1013,50 +1102,9 @@ int encode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
     if (n_seg > 1 && (rc = stage_descriptors(w, desc, tiles, &a.segs, &a.tile_start, &a.seg_at)) != SPLITZIP_OK)
         return rc;
     uint8_t *res = d_result ? reinterpret_cast<uint8_t *>(d_result) : w->result;
-    // one book for the whole call: its LUT directly; several: the table, indexed per segment
-    a.lut = codec->d_lut + 256 * (book < 0 ? 0 : book);
-    a.multi_book = book < 0;
-    a.cbs = codec->d_cbs;
-    a.packed = packed;
-    a.seg_total = reinterpret_cast<uint64_t *>(w->scratch + lay.seg_total);
-    a.tile_count = reinterpret_cast<uint32_t *>(w->scratch + lay.tile_count);
-    a.tile_ovf = reinterpret_cast<uint64_t *>(w->scratch + lay.tile_ovf);
-    a.spill_rec = reinterpret_cast<sz::SpillRec *>(w->scratch + lay.spill_rec);
-    a.ovf_tiles = reinterpret_cast<uint32_t *>(w->scratch + lay.ovf_tiles);
-    a.slots = reinterpret_cast<uint32_t *>(w->scratch + lay.slots);
-    a.block_sum = reinterpret_cast<uint64_t *>(w->scratch + lay.block_sum);
-    a.group_sum = reinterpret_cast<uint64_t *>(w->scratch + lay.group_sum);
-    a.ovf = reinterpret_cast<uint32_t *>(w->scratch + lay.ovf);
-    a.ovf_ctr = w->ovf_ctr;
-    a.ovf_cap = ovf_cap;
-    a.err = reinterpret_cast<uint32_t *>(res);
-    a.seg_escapes = reinterpret_cast<uint64_t *>(res + 8);
-    a.n_seg = n_seg;
-    a.n_tiles = n_tiles;
-    a.log2_chunk = codec->log2_chunk;
-    a.elem = codec->elem;
-    a.tile_shift = tile_shift;
-    a.slot_escapes = slot_escapes;
-    a.private_ovf = private_ovf ? 1u : 0u;
-    a.stage = n_tiles > codec->stage_tiles.load(std::memory_order_relaxed) ? 1u : 0u;
-    hipError_t e = hipSuccess;
-    {
-        // small calls: pack and finish; else pack, sums, place and spill
-        static const int kSmallStages[] = {sz::kStagePack, sz::kStageFinish};
-        static const int kSmallKinds[] = {SPLITZIP_KERNEL_PACK, SPLITZIP_KERNEL_FINISH};
-        static const int kStages[] = {sz::kStagePack, sz::kStageSums, sz::kStagePlace, sz::kStageSpill};
-        static const int kKinds[] = {SPLITZIP_KERNEL_PACK, SPLITZIP_KERNEL_SUMS, SPLITZIP_KERNEL_PLACE,
-                                     SPLITZIP_KERNEL_SPILL};
-        const bool small = n_tiles <= codec->small_tiles.load(std::memory_order_relaxed);
-        const int *stages = small ? kSmallStages : kStages;
-        const int n_stages = small ? 2 : 4;
-        CallTimer timer(codec, w, stream, small ? kSmallKinds : kKinds, n_stages);
-        timer.mark();
-        for (int i = 0; i < n_stages && e == hipSuccess; ++i) {
-            e = sz::launch_encode_stage(stages[i], a, stream);
-            timer.mark();
-        }
-    }
+    set_encode_args(a, codec, n_seg, n_tiles, book, packed, w->scratch, lay, w->ovf_ctr, ovf_cap,
+                    private_ovf, res);
+    const hipError_t e = run_encode_stages(codec, w, a, stream);
     if (e != hipSuccess) {
         // a launch that did not run to its end may leave the overflow counter set
         (void)hipMemsetAsync(w->ovf_ctr, 0, 2 * sizeof(unsigned long long), stream);
@@ -1122,6 +1170,117 @@ int splitzip_encode_async(splitzip_codec *codec, uint32_t n_seg, const splitzip_
         std::lock_guard<std::mutex> lock(ws->mu);
         Workspace *w = nullptr;
         return encode_launch(codec, desc, tiles, common_book(n_seg, segs), false, stream, d_result, &w);
+    });
+}
+
+int splitzip_encode_noalloc(splitzip_codec *codec, uint32_t n_seg, const splitzip_segment *segs,
+                            void *stream_, uint64_t *d_result)
+{
+    return guarded([&]() -> int {
+        g_last_error[0] = '\0';
+        if (!d_result || !aligned(d_result, 8))
+            return fail(SPLITZIP_E_INVALID, "d_result NULL or not 8-byte aligned");
+        int rc = codec_check(codec);
+        if (rc != SPLITZIP_OK)
+            return rc;
+        if (n_seg == 0 || !segs)
+            return fail(SPLITZIP_E_INVALID, "n_seg is 0 or segs is NULL");
+        if (n_seg > SPLITZIP_NOALLOC_MAX_SEGMENTS)
+            return fail(SPLITZIP_E_INVALID, "%u segments; the allocation-free encode takes at most %u",
+                        n_seg, SPLITZIP_NOALLOC_MAX_SEGMENTS);
+        if (codec->device < 0 || codec->device >= kNoAllocDevices)
+            return fail(SPLITZIP_E_INVALID, "device %d out of range", codec->device);
+        // every segment checked, and the scratch the call needs, before anything is enqueued
+        const uint64_t tile_words = tile_elements(codec, true);
+        uint64_t n_tiles = 0, ovf_cap = 1;
+        int64_t book = segs[0].book;
+        sz::SegDesc d0{};
+        for (uint32_t i = 0; i < n_seg; ++i) {
+            sz::SegDesc d;
+            if ((rc = check_segment(codec, i, segs[i], true, d)) != SPLITZIP_OK)
+                return rc;
+            if (i == 0)
+                d0 = d;
+            n_tiles += segment_tiles(segs[i].n, tile_words);
+            if (n_tiles > 0xFFFFFFF0ull)
+                return fail(SPLITZIP_E_INVALID, "too many tiles in one call");
+            if (segs[i].esc_capacity > SPLITZIP_NOALLOC_SCRATCH_BYTES ||
+                (ovf_cap += segs[i].esc_capacity) > SPLITZIP_NOALLOC_SCRATCH_BYTES)
+                return fail(SPLITZIP_E_INVALID, "escape capacities exceed the allocation-free scratch");
+            if (segs[i].book != book)
+                book = -1;
+        }
+        const auto up = [](uint64_t x) { return (x + 255) & ~uint64_t(255); };
+        const uint64_t seg_table = n_seg > 1 ? 256 : 0;               // after the counter
+        const uint64_t tile_table = up(seg_table + (n_seg > 1 ? sizeof(sz::SegDesc) * n_seg : 0));
+        const uint64_t enc_base = up(
+            std::max<uint64_t>(256, tile_table + (n_seg > 1 ? 4 * (n_seg + 2 + ((n_tiles + 63) >> 6)) : 0)));
+        const EncodeScratch lay((uint32_t)n_tiles, ovf_cap, n_seg, slot_escapes(codec));
+        if (enc_base + lay.total > SPLITZIP_NOALLOC_SCRATCH_BYTES)
+            return fail(SPLITZIP_E_INVALID, "the call needs %llu bytes of scratch; the allocation-free encode has %llu",
+                        (unsigned long long)(enc_base + lay.total),
+                        (unsigned long long)SPLITZIP_NOALLOC_SCRATCH_BYTES);
+
+        DeviceGuard dg(codec->device);
+        if (dg.err != hipSuccess)
+            return fail_hip(dg.err, "hipSetDevice");
+        NoAllocDevice &nd = g_noalloc[codec->device];
+        std::lock_guard<std::mutex> lock(nd.mu);
+        if (!nd.base) {
+            // once per device, with the device current: its copy of the array
+            void *p = nullptr;
+            const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc_scratch));
+            if (e != hipSuccess || !p)
+                return fail_hip(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+            nd.base = static_cast<uint8_t *>(p);
+        }
+        uint8_t *base = nd.base;
+        hipStream_t stream = static_cast<hipStream_t>(stream_);
+        unsigned long long *ctr = reinterpret_cast<unsigned long long *>(base);
+        sz::SegDesc *d_segs = n_seg > 1 ? reinterpret_cast<sz::SegDesc *>(base + seg_table) : nullptr;
+        uint32_t *d_tiles = n_seg > 1 ? reinterpret_cast<uint32_t *>(base + tile_table) : nullptr;
+
+        // set-up launches: the overflow counter cleared, and for several segments their
+        // descriptors and tile starts (kernel arguments) written to the scratch, then the
+        // coarse segment table
+        hipError_t e = hipSuccess;
+        sz::SetupArgs sa{};
+        sa.d_segs = d_segs;
+        sa.d_tiles = d_tiles;
+        sa.ovf_ctr = ctr;
+        if (n_seg == 1) {
+            e = sz::launch_setup(sa, stream);
+        } else {
+            uint64_t t = 0;
+            for (uint32_t first = 0; first < n_seg && e == hipSuccess; first += sz::kSetupSegs) {
+                const uint32_t cnt = std::min<uint32_t>(sz::kSetupSegs, n_seg - first);
+                for (uint32_t k = 0; k < cnt; ++k) {
+                    (void)check_segment(codec, first + k, segs[first + k], true, sa.segs[k]);
+                    sa.tiles[k] = (uint32_t)t;
+                    t += segment_tiles(segs[first + k].n, tile_words);
+                }
+                sa.tiles[cnt] = (uint32_t)t;
+                sa.first = first;
+                sa.count = cnt;
+                sa.last = first + cnt == n_seg ? 1u : 0u;
+                e = sz::launch_setup(sa, stream);
+                sa.ovf_ctr = nullptr;      // cleared by the first launch
+            }
+            if (e == hipSuccess)
+                e = sz::launch_seg_at(d_tiles, n_seg, (uint32_t)n_tiles, d_tiles + n_seg + 1, stream);
+        }
+        sz::EncodeArgs a{};
+        a.seg0 = d0;
+        a.segs = d_segs;
+        a.tile_start = d_tiles;
+        a.seg_at = d_tiles ? d_tiles + n_seg + 1 : nullptr;
+        set_encode_args(a, codec, n_seg, (uint32_t)n_tiles, book, false, base + enc_base, lay, ctr, ovf_cap,
+                        false, reinterpret_cast<uint8_t *>(d_result));
+        if (e == hipSuccess)
+            e = run_encode_stages(codec, nullptr, a, stream);
+        if (e != hipSuccess)
+            return fail_hip(e, "allocation-free encode launch");
+        return SPLITZIP_OK;
     });
 }
 

@@ -196,6 +196,28 @@ struct HistArgs {
     uint32_t pad;
 };
 
+// Set-up of an encode whose scratch is a fixed device array (no allocation anywhere): the
+// segment descriptors and tile starts travel as kernel arguments, kSetupSegs per launch, and
+// are written to the scratch; the first launch also clears the overflow counter.
+constexpr uint32_t kSetupSegs = 24;
+
+struct SetupArgs {
+    SegDesc segs[kSetupSegs];
+    uint32_t tiles[kSetupSegs + 1];   // tile starts of segs[], then the next segment's start
+    SegDesc *d_segs;                  // device [n_seg] (NULL for a one-segment call)
+    uint32_t *d_tiles;                // device [n_seg + 1] tile starts
+    unsigned long long *ovf_ctr;      // [2] set to 0 when not NULL
+    uint32_t first;                   // index of segs[0] in the call
+    uint32_t count;                   // descriptors in this launch
+    uint32_t last;                    // this launch also writes the final tile start
+    uint32_t pad;
+};
+
+hipError_t launch_setup(const SetupArgs &a, hipStream_t stream);
+// The coarse segment table (see kSegAtShift) of n_seg segments with these device tile starts.
+hipError_t launch_seg_at(const uint32_t *tile_start, uint32_t n_seg, uint32_t n_tiles, uint32_t *seg_at,
+                         hipStream_t stream);
+
 uint32_t hist_blocks(uint64_t n);
 hipError_t launch_histogram(const HistArgs &a, hipStream_t stream);
 // Encode stages, launched in order on one stream: pack, sums, place, spill; or, for calls of

@@ -894,6 +894,61 @@ __global__ __launch_bounds__(kThreads) void encode_finish_kernel(const EncodeArg
     }
 }
 
+// ---- set-up of an encode with a fixed scratch array ------------------------------------------
+
+__global__ __launch_bounds__(64) void setup_kernel(const SetupArgs a)
+{
+    const uint32_t i = threadIdx.x;
+    if (i < a.count) {
+        a.d_segs[a.first + i] = a.segs[i];
+        a.d_tiles[a.first + i] = a.tiles[i];
+    }
+    if (a.last && i == a.count)
+        a.d_tiles[a.first + a.count] = a.tiles[a.count];
+    if (a.ovf_ctr && i < 2)
+        a.ovf_ctr[i] = 0;
+}
+
+// Entry g < n_groups: the segment holding tile g << kSegAtShift (the largest s with
+// tile_start[s] <= that tile); entry n_groups: the last segment.
+__global__ __launch_bounds__(kThreads) void seg_at_kernel(const uint32_t *tile_start, uint32_t n_seg,
+                                                          uint32_t n_groups, uint32_t *seg_at)
+{
+    const uint32_t g = blockIdx.x * kThreads + threadIdx.x;
+    if (g > n_groups)
+        return;
+    if (g == n_groups) {
+        seg_at[g] = n_seg - 1;
+        return;
+    }
+    const uint32_t t = g << kSegAtShift;
+    uint32_t lo = 0, hi = n_seg;
+    while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (tile_start[mid] <= t)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    seg_at[g] = lo;
+}
+
+hipError_t launch_setup(const SetupArgs &a, hipStream_t stream)
+{
+    if (a.count > kSetupSegs)
+        return hipErrorInvalidValue;
+    setup_kernel<<<1, 64, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_seg_at(const uint32_t *tile_start, uint32_t n_seg, uint32_t n_tiles, uint32_t *seg_at,
+                         hipStream_t stream)
+{
+    const uint32_t n_groups = (n_tiles + (1u << kSegAtShift) - 1) >> kSegAtShift;
+    seg_at_kernel<<<n_groups / kThreads + 1, kThreads, 0, stream>>>(tile_start, n_seg, n_groups, seg_at);
+    return hipGetLastError();
+}
+
 hipError_t launch_encode_stage(int stage, const EncodeArgs &a, hipStream_t stream)
 {
     switch (stage) {

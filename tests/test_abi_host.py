@@ -117,6 +117,10 @@ def test_argument_validation_before_any_device_call():
     segs = (sz.splitzip_segment * 1)()
     assert L.splitzip_encode(None, 1, segs, None) == sz.E_INVALID
     assert L.splitzip_decode(None, 1, segs, None, None) == sz.E_INVALID
+    res = ctypes.c_uint64(0)
+    assert L.splitzip_encode_noalloc(None, 1, segs, None, ctypes.byref(res)) == sz.E_INVALID
+    assert L.splitzip_encode_noalloc(None, 1, segs, None, None) == sz.E_INVALID
+    assert b"d_result" in L.splitzip_last_error()
     # duplicate codebook entries
     cb = (ctypes.c_uint8 * 16)(*([5] * 16))
     assert L.splitzip_codec_from_codebook(cb, 1024, ctypes.byref(h)) == sz.E_INVALID
