@@ -7,7 +7,13 @@ pages prescribe (offline calibration).  Inputs are resident in HBM before timing
 
 Prints one JSON line.  Throughput is GB/s of BF16 input (2 bytes per word, 10^9).
 ``--elem e5m2`` measures the FP8 E5M2 codec on the same inputs cast to E5M2 (GB/s of E5M2
-input, 1 byte per element).
+input, 1 byte per element).  The timing protocol follows the SplitZip README's throughput
+benchmark (Reproducing Paper Artifact Scripts): 10 warmup steps, 50 timed steps, reported
+also as the median of 5 repeats (the timed steps in 5 equal blocks).  The line also holds
+the achievable streaming ceiling of the same GPU (read, write and copy kernels shaped like
+the codec's), SHA-256 digests of the input and calibration words, and the host's CPU model
+and core count.  ``--input`` / ``--calibration-input`` run on saved tensors instead of the
+synthetic workloads; ``--stats`` prints per-tensor exponent statistics instead of timing.
 """
 from __future__ import annotations
 
@@ -149,6 +155,162 @@ def cpu_baseline(segments, codebooks, chunk_size: int, sample_words: int, e5m2: 
             "encode_GBps": round(gb / t_enc, 4), "decode_GBps": round(gb / t_dec, 4)}
 
 
+def sha256_words(arrays) -> str:
+    """SHA-256 of the arrays' bytes, in order (little-endian words as stored)."""
+    import numpy as np
+    h = hashlib.sha256()
+    step = 1 << 28
+    for a in arrays:
+        b = np.ascontiguousarray(a).reshape(-1).view(np.uint8)
+        for i in range(0, b.size, step):
+            h.update(memoryview(b[i:i + step]))
+    return h.hexdigest()
+
+
+def host_info() -> dict:
+    """CPU model and core counts of the host this runs on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cores": usable}
+
+
+def ceiling_leg(dev, reps: int = 10, mib: int = 4096) -> dict:
+    """Median GB/s (bytes read + written) of streaming kernels shaped like the codec's:
+    16-byte lane-contiguous nontemporal accesses, 32 KiB per 256-thread workgroup, tiles in
+    contiguous ranges per XCD; read and write over mib MiB, copy of mib/2 MiB."""
+    import ctypes
+    import torch
+    from lossless_bf16_kv_amd import build as szbuild
+    if not os.path.exists(szbuild.CEILING_PATH):
+        raise RuntimeError(f"{szbuild.CEILING_PATH} is not built; run __graft_entry__.build()")
+    L = ctypes.CDLL(szbuild.CEILING_PATH)
+    L.szc_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
+                             ctypes.c_void_p, ctypes.c_void_p]
+    L.szc_stream.restype = ctypes.c_int
+    nb = mib << 20
+    a = torch.ones(nb // 4, dtype=torch.int32, device=dev)
+    b = torch.empty_like(a)
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for kind, name in enumerate(("read", "write", "copy")):
+        nbytes = nb if kind != 2 else nb // 2
+        times = []
+        for r in range(reps + 2):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            rc = L.szc_stream(kind, a.data_ptr(), b.data_ptr(), nbytes, sink.data_ptr(), stream.cuda_stream)
+            ev[1].record(stream)
+            if rc != 0:
+                raise RuntimeError(f"ceiling kernel {name}: HIP error {rc}")
+            torch.cuda.synchronize()
+            if r >= 2:
+                times.append(ev[0].elapsed_time(ev[1]))
+        moved = nb                       # copy: nb / 2 read + nb / 2 written
+        out[name + "_GBps"] = round(moved / (sorted(times)[len(times) // 2] * 1e-3) / 1e9, 1)
+    del a, b
+    torch.cuda.empty_cache()
+    out["kernels"] = "stream_ceiling.hip: 16 B per lane, 32 KiB per workgroup, XCD-contiguous tiles, " \
+                     f"nontemporal; read/write {mib} MiB, copy {mib // 2} MiB; median of {reps}"
+    return out
+
+
+def ceiling_fraction(read_bytes: int, write_bytes: int, ms: float, ceil: dict) -> float:
+    """Time a kernel would take reading and then writing its bytes at the measured read and
+    write ceilings, over its measured time."""
+    model_s = read_bytes / (ceil["read_GBps"] * 1e9) + write_bytes / (ceil["write_GBps"] * 1e9)
+    return round(model_s / (ms * 1e-3), 4)
+
+
+def load_saved(path: str, elem: str) -> list:
+    """(name, flat numpy array) of every tensor in a saved file, loaded without executing
+    anything from it: .safetensors, .pt/.pth (torch.load with weights_only), .npy (no
+    pickles).  BF16 tensors give their uint16 words (raw int16/uint16 arrays are taken as
+    words); for --elem e5m2, float8_e5m2 tensors or raw uint8 bytes."""
+    import numpy as np
+    import torch
+    ext = os.path.splitext(path)[1].lower()
+    if ext == ".safetensors":
+        from safetensors.torch import load_file
+        items = list(load_file(path).items())
+    elif ext in (".pt", ".pth"):
+        obj = torch.load(path, map_location="cpu", weights_only=True)
+        if isinstance(obj, torch.Tensor):
+            items = [(os.path.basename(path), obj)]
+        elif isinstance(obj, dict):
+            items = list(obj.items())
+        elif isinstance(obj, (list, tuple)):
+            items = [(f"{i}", t) for i, t in enumerate(obj)]
+        else:
+            raise SystemExit(f"{path}: expected a tensor, a dict or a list of tensors")
+    elif ext == ".npy":
+        items = [(os.path.basename(path), torch.from_numpy(np.load(path, allow_pickle=False)))]
+    else:
+        raise SystemExit(f"{path}: unsupported file type (use .safetensors, .pt/.pth or .npy)")
+    out = []
+    for name, t in items:
+        if not isinstance(t, torch.Tensor):
+            raise SystemExit(f"{path}: entry {name} is not a tensor")
+        t = t.contiguous().reshape(-1)
+        if elem == "e5m2":
+            if t.dtype not in (torch.float8_e5m2, torch.uint8):
+                raise SystemExit(f"{path}: {name} is {t.dtype}; --elem e5m2 needs float8_e5m2 or uint8")
+            out.append((str(name), t.view(torch.uint8).numpy().copy()))
+        else:
+            if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+                raise SystemExit(f"{path}: {name} is {t.dtype}; the BF16 codec needs bfloat16 "
+                                 f"(or raw 16-bit words)")
+            out.append((str(name), t.view(torch.int16).numpy().view(np.uint16).copy()))
+    if not out:
+        raise SystemExit(f"{path}: no tensors")
+    return out
+
+
+def saved_workload(args):
+    """A workload from --input (every tensor a segment) and --calibration-input (all its
+    tensors pooled; default: the input itself)."""
+    import numpy as np
+    import workloads
+    parts = load_saved(args.input, args.elem)
+    if args.calibration_input:
+        cal = np.concatenate([a for _, a in load_saved(args.calibration_input, args.elem)])
+        cal_note = f"calibrated on {os.path.basename(args.calibration_input)}"
+    else:
+        cal = np.concatenate([a for _, a in parts])
+        cal_note = "calibrated on the input itself"
+    names = [nm for nm, _ in parts]
+    wl = workloads.Workload(name="saved_" + os.path.splitext(os.path.basename(args.input))[0],
+                            segments=[a for _, a in parts], calibration=cal, chunk_size=args.chunk_size,
+                            description=f"saved tensors from {os.path.basename(args.input)} "
+                                        f"({len(parts)} tensors); {cal_note}")
+    return wl, names
+
+
+def exponent_report(xs, names, elem: str) -> list:
+    """Per tensor: exponent entropy (bits), top-16 codebook and its coverage, distinct
+    exponents (histograms on the GPU, one pass over all tensors)."""
+    import lossless_bf16_kv_amd as sz
+    hists = sz.histograms(xs, elem=elem)
+    out = []
+    for name, x, h in zip(names, xs, hists):
+        st = sz.exponent_stats(list(h) + [0] * (256 - len(h)))
+        out.append({"tensor": name, "elements": int(x.numel()), "entropy_bits": round(st["entropy_bits"], 6),
+                    "coverage_top16": st["coverage"], "distinct_exponents": st["distinct"],
+                    "codebook": st["codebook"].hex()})
+    return out
+
+
 def transfer_bench(args, codec, xs, books, wl, esize, coverage):
     """Compressed against raw transfer of the tensors xs across the host link (one JSON line)."""
     import torch
@@ -209,11 +371,13 @@ def transfer_bench(args, codec, xs, books, wl, esize, coverage):
     print(json.dumps(out), flush=True)
 
 
-def main():
+def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", "--iters", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", "--iters", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="the timed steps in this many equal blocks; their median is reported too")
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--chunk-size", type=int, default=1024)
     ap.add_argument("--rows", type=int, default=0,
@@ -237,12 +401,23 @@ def main():
                     help="time the compressed, pipelined transfer of the input's tensors (the "
                          "long-prefill KV: one per layer and K/V) across the PCIe link through "
                          "pinned host memory against the raw transfer, instead of the codec")
+    ap.add_argument("--input", default="",
+                    help="saved tensors to encode (.safetensors, .pt/.pth loaded weights-only, "
+                         ".npy): every tensor one segment")
+    ap.add_argument("--calibration-input", default="",
+                    help="saved tensors to calibrate on (default: the input itself)")
+    ap.add_argument("--output", default="", help="also write the JSON line to this file")
+    ap.add_argument("--stats", action="store_true",
+                    help="print per-tensor exponent statistics (entropy, top-16 coverage, distinct "
+                         "exponents; the long-prefill KV per layer and K/V) instead of timing")
     ap.add_argument("--cpu-sample-words", type=int, default=1 << 30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-copy-ceiling", action="store_true")
-    args = ap.parse_args()
+    ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--no-digests", action="store_true", help="skip the SHA-256 of the inputs")
+    args = ap.parse_args(argv)
     if args.rows or args.hidden_dim:
         args.config = 1
+    args.repeats = max(1, min(args.repeats, args.steps))
 
     if args.gpus != 1:
         print(json.dumps({"error": "the benchmark runs on one GPU; --gpus must be 1 (segments "
@@ -254,7 +429,11 @@ def main():
     import lossless_bf16_kv_amd as sz
 
     t_gen = time.perf_counter()
-    wl = load_workload(args)
+    seg_names = None
+    if args.input:
+        wl, seg_names = saved_workload(args)
+    else:
+        wl = load_workload(args)
     if args.calibrate_on_input:
         wl.calibration = np.concatenate(wl.segments) if len(wl.segments) > 1 else wl.segments[0]
         wl.description += "; calibrated on the input itself"
@@ -263,6 +442,8 @@ def main():
     C = wl.chunk_size
 
     segments, cal_parts, books = wl.segments, [wl.calibration], None
+    if args.input and (args.books != "one" or args.transfer):
+        raise SystemExit("--books layer-kv and --transfer apply to the synthetic long-prefill KV only")
     if args.transfer and args.config == 3:
         # one tensor per layer and K/V, as a serving stack would send them
         tokens = wl.segments[0].size // (2 * args.layers * 1024)
@@ -277,6 +458,20 @@ def main():
     e5m2 = args.elem == "e5m2"
     esize = 1 if e5m2 else 2                      # bytes per input element
     view = (lambda a: a) if e5m2 else (lambda a: a.view(np.int16))
+    if args.stats:
+        xs = [torch.from_numpy(view(s)).to(dev) for s in segments]
+        names = seg_names or [f"segment {i}" for i in range(len(xs))]
+        if args.config == 3 and not args.input and len(xs) == 1:
+            # the long-prefill KV: one tensor per layer and K/V
+            tokens = wl.segments[0].size // (2 * args.layers * 1024)
+            xs = list(xs[0].split(tokens * 1024))
+            names = [f"layer {i // 2} {'KV'[i % 2]}" for i in range(len(xs))]
+        out = {"metric": "exponent statistics per tensor (entropy bits, top-16 coverage, distinct "
+                         "exponents)", "element": args.elem, "data": "synthetic" if not args.input else "saved",
+               "config": {"workload": wl.name, "tensors": len(xs), "description": wl.description},
+               "tensors": exponent_report(xs, names, args.elem)}
+        emit(out, args.output)
+        return
     xs = [torch.from_numpy(view(s)).to(dev) for s in segments]
     cals = [torch.from_numpy(view(c)).to(dev) for c in cal_parts]
     codec = sz.Codec(dev, C, elem=args.elem)
@@ -366,6 +561,16 @@ def main():
     for x, y in zip(xs, ys):
         assert torch.equal(x, y), "round trip is not bitwise"
 
+    # the timed steps in args.repeats equal blocks (step times from the events)
+    blocks = []
+    per = args.steps // args.repeats
+    for r in range(args.repeats):
+        evb = events[r * per:(r + 1) * per if r + 1 < args.repeats else args.steps]
+        if scrub is None:
+            ms = evb[0][0].elapsed_time(evb[-1][2])
+        else:
+            ms = sum(e[0].elapsed_time(e[2]) for e in evb)
+        blocks.append(round(esize * sum(x.numel() for x in xs) * len(evb) / (ms * 1e-3) / 1e9, 2))
     enc_ms = sorted(e[0].elapsed_time(e[1]) for e in events)
     dec_ms = sorted(e[1].elapsed_time(e[2]) for e in events)
     enc_avg = sum(enc_ms) / len(enc_ms)
@@ -410,30 +615,39 @@ def main():
     ops = {"encode": roofline("encode (all launches)", alg["encode"], enc_avg, wname),
            "decode": roofline("decode", alg["decode"], dec_avg, wname)}
 
-    copy_gbps = None
-    if not args.no_copy_ceiling:
-        a = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ce[0].record(stream)
-        for _ in range(5):
-            b.copy_(a)
-        ce[1].record(stream)
-        torch.cuda.synchronize()
-        copy_gbps = round(2 * a.numel() * 5 / (ce[0].elapsed_time(ce[1]) * 1e-3) / 1e9, 1)
-        del a, b
+    ceiling = None
+    if not args.no_ceiling:
+        ceiling = ceiling_leg(dev)
+        # the same bytes read and then written at the read and write ceilings, over the
+        # measured time: how close each op and kernel comes to what the GPU streams
+        comp_bytes = sum(e.compressed_bytes for e in encs)
+        x_bytes = esize * n
+        ceiling["frac_of_read_then_write"] = {
+            "encode": ceiling_fraction(x_bytes, comp_bytes, enc_avg, ceiling),
+            "decode": ceiling_fraction(comp_bytes, x_bytes, dec_avg, ceiling)}
+        if "encode_pack" in kernels:
+            pk = kernels["encode_pack"]
+            ceiling["frac_of_read_then_write"]["encode_pack"] = ceiling_fraction(
+                x_bytes, pk["algorithmic_bytes"] - x_bytes, pk["avg_launch_ms"], ceiling)
+        if "decode" in kernels:
+            ceiling["frac_of_read_then_write"]["decode_kernel"] = ceiling_fraction(
+                comp_bytes, x_bytes, kernels["decode"]["avg_launch_ms"], ceiling)
+
+    digests = None
+    if not args.no_digests:
+        digests = {"input_sha256": sha256_words(segments), "calibration_sha256": sha256_words(cal_parts),
+                   "basis": "SHA-256 of the input words (all segments in order) and of the "
+                            "calibration words, as stored (little-endian)"}
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(segments, [codec.books[e.book] for e in encs], C, args.cpu_sample_words, e5m2)
 
     metric = "encode & decode GB/s (BF16 in) + % HBM roofline + compression ratio" + \
-        (", 8.6 GB KV" if args.config == 3 and args.layers == 64 else "")
+        (", 8.6 GB KV" if args.config == 3 and args.layers == 64 and not args.input else "")
     if e5m2:
         metric = "encode & decode GB/s (E5M2 in) + % HBM roofline + compression ratio" + \
-            (", 4.3 GB E5M2 KV" if args.config == 3 and args.layers == 64 else "")
+            (", 4.3 GB E5M2 KV" if args.config == 3 and args.layers == 64 and not args.input else "")
     out = {
         "metric": metric,
         "value": round(value, 2),
@@ -471,8 +685,13 @@ def main():
         "kernel_times_basis": "a second pass of the same steps with HIP events around every "
                               "kernel launch on the launch stream",
         "profiled_pass_ms_per_step": round(prof_ms, 4),
-        "copy_ceiling_GBps": copy_gbps,
+        "repeats": {"n": args.repeats, "GBps": blocks, "median_GBps": sorted(blocks)[len(blocks) // 2],
+                    "basis": f"the {args.steps} timed steps in {args.repeats} blocks, each timed with "
+                             "events"},
+        "ceiling": ceiling,
         "cpu_baseline": cpu,
+        "host": host_info(),
+        "inputs": digests,
         "generate_s": round(t_gen, 1),
         "kernel_source": kernel_source_hash(),
         "round_trip_bitwise": True,
@@ -480,7 +699,15 @@ def main():
         "value_basis": "wall clock over the timed steps" if scrub is None else
                        "encode + decode events (cache flushed between steps)",
     }
-    print(json.dumps(out), flush=True)
+    emit(out, args.output)
+
+
+def emit(out: dict, path: str = "") -> None:
+    line = json.dumps(out)
+    print(line, flush=True)
+    if path:
+        with open(path, "w") as f:
+            f.write(line + "\n")
 
 
 if __name__ == "__main__":

@@ -30,8 +30,8 @@ __device__ __forceinline__ const SZ_GLOBAL T *as_global(const T *p)
     return (const SZ_GLOBAL T *)p;
 }
 
-// Streaming accesses of the pack kernels: every byte is touched once, so the loads and stores
-// carry the nontemporal hint and do not displace other data in the caches.
+// Streaming accesses of the pack and decode kernels: every byte is touched once, so the loads
+// and stores carry the nontemporal hint and do not displace other data in the caches.
 __device__ __forceinline__ uint4 load_stream16(const void *p)
 {
     const u32x4 t = __builtin_nontemporal_load(as_global(reinterpret_cast<const u32x4 *>(p)));

@@ -268,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
 hipError_t launch_encode_pack_e5m2(const EncodeArgs &a, hipStream_t stream)
 {
     if (a.stage)
-        encode_pack_e5m2_kernel<true><<<a.n_tiles, kThreads, 0, stream>>>(a);
+        encode_pack_e5m2_kernel<true><<<a.n_tiles, kThreads, kE8PackLdsReserve, stream>>>(a);
     else
         encode_pack_e5m2_kernel<false><<<a.n_tiles, kThreads, 0, stream>>>(a);
     return hipGetLastError();
@@ -348,8 +348,8 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
         const uint64_t g0 = base + (uint64_t)(((wave * G + j) << 6) + lane) * kE8GroupElems;
         const uint64_t q = g0 / kE8GroupElems;
         if (g0 + kE8GroupElems <= n) {
-            const u32x3 s3 = *(const SZ_GLOBAL u32x3 *)(sd.sm + 12 * q);
-            const u32x4 c4 = *as_global(reinterpret_cast<const u32x4 *>(sd.codes + 16 * q));
+            const u32x3 s3 = __builtin_nontemporal_load((const SZ_GLOBAL u32x3 *)(sd.sm + 12 * q));
+            const u32x4 c4 = __builtin_nontemporal_load(as_global(reinterpret_cast<const u32x4 *>(sd.codes + 16 * q)));
             smv[j][0] = s3.x; smv[j][1] = s3.y; smv[j][2] = s3.z;
             cw[j][0] = c4.x; cw[j][1] = c4.y; cw[j][2] = c4.z; cw[j][3] = c4.w;
         } else {
@@ -395,7 +395,10 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
     __syncthreads();
     const uint64_t j0 = s_off[0], j1 = s_off[nc];
     bool patch = j1 > j0;
-    if (j0 > j1 || j1 > E) {
+    // at most one escape per element: a tile's range may not exceed its elements (a tile
+    // inside one chunk: that chunk's), which also keeps tile-relative ranks below 2^32
+    const uint64_t c0_len = n - (c0 << log2c) < C ? n - (c0 << log2c) : C;
+    if (j0 > j1 || j1 > E || j1 - j0 > (sub_chunk ? c0_len : valid)) {
         patch = false;
         if (tid == 0 && a.err)
             atomicOr(a.err, kErrBadOffsets);
@@ -446,9 +449,11 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
         const SZ_GLOBAL uint16_t *gpos = as_global(static_cast<const uint16_t *>(sd.esc_pos));
         const SZ_GLOBAL uint8_t *gexp = as_global(static_cast<const uint8_t *>(sd.esc_exp));
         if (!sub_chunk) {
-            for (uint64_t ci = tid; ci < nc; ci += kThreads)
-                if (s_off[ci] > s_off[ci + 1] && a.err)
+            for (uint64_t ci = tid; ci < nc; ci += kThreads) {
+                const uint64_t cs = (c0 + ci) << log2c;
+                if ((s_off[ci] > s_off[ci + 1] || s_off[ci + 1] - s_off[ci] > (n - cs < C ? n - cs : C)) && a.err)
                     atomicOr(a.err, kErrBadOffsets);
+            }
             // chunk of escape jj: the last c with s_off[c] <= jj.  In the large-call build a
             // tile of at most kFew chunks (chunk size 1024 or more) keeps the tile-relative
             // offsets in scalar registers, and each escape counts those at or below it; a
@@ -481,6 +486,7 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
 #pragma unroll
                         for (int c = 1; c < kFew; ++c)
                             lo += r >= rel[c] ? 1u : 0u;
+                        lo = lo < (uint32_t)nc ? lo : (uint32_t)nc - 1u;
                     } else {
                         uint32_t hi = (uint32_t)nc;          // s_off[lo] <= jj < s_off[hi]
                         while (hi - lo > 1) {
@@ -569,8 +575,8 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
             grp[2 * lane + 1] = make_uint4(out[4], out[5], out[6], out[7]);
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             const uint4 lo = grp[lane], hi = grp[64 + lane];
-            *as_global(reinterpret_cast<u32x4 *>(yb + gbase + 16 * lane)) = u32x4{lo.x, lo.y, lo.z, lo.w};
-            *as_global(reinterpret_cast<u32x4 *>(yb + gbase + 1024 + 16 * lane)) = u32x4{hi.x, hi.y, hi.z, hi.w};
+            store_stream16(yb + gbase + 16 * lane, lo.x, lo.y, lo.z, lo.w);
+            store_stream16(yb + gbase + 1024 + 16 * lane, hi.x, hi.y, hi.z, hi.w);
         } else {
             // the lane's own 32 elements, those below n
             for (uint32_t k = 0; k < kE8GroupElems && g0 + k < n; ++k)

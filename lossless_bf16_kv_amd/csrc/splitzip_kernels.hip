@@ -956,7 +956,7 @@ hipError_t launch_encode_stage(int stage, const EncodeArgs &a, hipStream_t strea
         if (a.elem == kElemE5M2)
             return launch_encode_pack_e5m2(a, stream);
         if (a.stage)
-            encode_pack_kernel<true><<<a.n_tiles, kThreads, 0, stream>>>(a);
+            encode_pack_kernel<true><<<a.n_tiles, kThreads, kPackLdsReserve, stream>>>(a);
         else
             encode_pack_kernel<false><<<a.n_tiles, kThreads, 0, stream>>>(a);
         break;
@@ -1061,8 +1061,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
     for (int j = 0; j < kDecGroups; ++j) {
         const uint64_t g0 = base + (uint64_t)(((wave * kDecGroups + j) << 6) + lane) * kGroupWords;
         if (g0 + kGroupWords <= n) {
-            smv[j] = *reinterpret_cast<const uint2 *>(sd.sm + g0);
-            cw[j] = *reinterpret_cast<const uint32_t *>(sd.codes + (g0 >> 1));
+            const u32x2 s2 = __builtin_nontemporal_load(as_global(reinterpret_cast<const u32x2 *>(sd.sm + g0)));
+            smv[j] = make_uint2(s2.x, s2.y);
+            cw[j] = __builtin_nontemporal_load(as_global(reinterpret_cast<const uint32_t *>(sd.codes + (g0 >> 1))));
         } else {
             uint32_t b[8] = {0, 0, 0, 0, 0, 0, 0, 0};
             uint32_t c = 0;
@@ -1093,7 +1094,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
     __syncthreads();
     const uint64_t j0 = s_off[0], j1 = s_off[nc];
     bool patch = j1 > j0;
-    if (j0 > j1 || j1 > E) {
+    // at most one escape per element: a tile's range may not exceed its elements (a tile
+    // inside one chunk: that chunk's), which also keeps tile-relative ranks below 2^32
+    const uint64_t c0_len = n - (c0 << log2c) < C ? n - (c0 << log2c) : C;
+    if (j0 > j1 || j1 > E || j1 - j0 > (sub_chunk ? c0_len : valid)) {
         patch = false;
         if (tid == 0 && a.err)
             atomicOr(a.err, kErrBadOffsets);
@@ -1145,9 +1149,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
         const SZ_GLOBAL uint8_t *gexp = as_global(static_cast<const uint8_t *>(sd.esc_exp));
         if (!sub_chunk) {
             // escape jj belongs to the last chunk ci whose offset s_off[ci] <= jj
-            for (uint64_t ci = tid; ci < nc; ci += kThreads)
-                if (s_off[ci] > s_off[ci + 1] && a.err)
+            for (uint64_t ci = tid; ci < nc; ci += kThreads) {
+                const uint64_t cs = (c0 + ci) << log2c;
+                if ((s_off[ci] > s_off[ci + 1] || s_off[ci + 1] - s_off[ci] > (n - cs < C ? n - cs : C)) && a.err)
                     atomicOr(a.err, kErrBadOffsets);
+            }
             // chunk of escape jj: the last c with s_off[c] <= jj.  In the large-call build a
             // tile of at most kFew chunks (chunk size 1024 or more) keeps the tile-relative
             // offsets in scalar registers, and each escape counts those at or below it; a
@@ -1180,6 +1186,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
 #pragma unroll
                         for (int c = 1; c < kFew; ++c)
                             lo += r >= rel[c] ? 1u : 0u;
+                        lo = lo < (uint32_t)nc ? lo : (uint32_t)nc - 1u;
                     } else {
                         uint32_t hi = (uint32_t)nc;          // s_off[lo] <= jj < s_off[hi]
                         while (hi - lo > 1) {
@@ -1249,7 +1256,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
         o.z = assemble(smv[j].y, 0x01010000u, ex_even[j], ex_odd[j], 0x0C060C02u);
         o.w = assemble(smv[j].y, 0x03030202u, ex_even[j], ex_odd[j], 0x0C070C03u);
         if (g0 + kGroupWords <= n) {
-            *reinterpret_cast<uint4 *>(sd.data + g0) = o;
+            store_stream16(sd.data + g0, o.x, o.y, o.z, o.w);
         } else {
             const uint32_t w[4] = {o.x, o.y, o.z, o.w};
             for (uint32_t k = 0; g0 + k < n; ++k)

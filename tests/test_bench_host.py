@@ -66,3 +66,75 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert p.returncode == 2
     assert "one GPU" in json.loads(p.stdout.strip().splitlines()[-1])["error"]
+
+
+def test_input_digests_and_host_record():
+    import hashlib
+
+    import numpy as np
+    a = np.arange(1000, dtype=np.uint16)
+    b = np.arange(7, dtype=np.uint16)[::-1]
+    assert bench.sha256_words([a, b]) == hashlib.sha256(a.tobytes() + b.copy().tobytes()).hexdigest()
+    info = bench.host_info()
+    assert info["nproc"] == os.cpu_count() and 1 <= info["usable_cores"] <= info["nproc"]
+
+
+def test_ceiling_fraction():
+    # 6 GB read at 6000 GB/s (1 ms) then 4 GB written at 4000 GB/s (1 ms): 2 ms of model
+    # time against a 4 ms kernel
+    ceil = {"read_GBps": 6000.0, "write_GBps": 4000.0}
+    assert bench.ceiling_fraction(6_000_000_000, 4_000_000_000, 4.0, ceil) == 0.5
+
+
+def test_saved_inputs_load_without_executing_anything(tmp_path):
+    import numpy as np
+    import pytest
+    import torch
+    from safetensors.torch import save_file
+    k = torch.randn(4, 8, 16).to(torch.bfloat16)
+    v = torch.randn(4, 8, 16).to(torch.bfloat16)
+    words = lambda t: t.reshape(-1).view(torch.int16).numpy().view(np.uint16)
+    save_file({"k": k, "v": v}, str(tmp_path / "kv.safetensors"))
+    torch.save({"k": k, "v": v}, str(tmp_path / "kv.pt"))
+    np.save(str(tmp_path / "k.npy"), words(k))
+    for f in ("kv.safetensors", "kv.pt"):
+        got = dict(bench.load_saved(str(tmp_path / f), "bf16"))
+        assert set(got) == {"k", "v"}
+        assert np.array_equal(got["k"], words(k)) and np.array_equal(got["v"], words(v))
+    (name, arr), = bench.load_saved(str(tmp_path / "k.npy"), "bf16")
+    assert np.array_equal(arr, words(k))
+    # E5M2 tensors for the E5M2 codec; a float32 tensor is refused for either
+    e = torch.randn(100).to(torch.float8_e5m2)
+    torch.save(e, str(tmp_path / "e.pt"))
+    (_, b8), = bench.load_saved(str(tmp_path / "e.pt"), "e5m2")
+    assert np.array_equal(b8, e.view(torch.uint8).numpy())
+    torch.save(torch.randn(10), str(tmp_path / "f.pt"))
+    with pytest.raises(SystemExit):
+        bench.load_saved(str(tmp_path / "f.pt"), "bf16")
+    with pytest.raises(SystemExit):
+        bench.load_saved(str(tmp_path / "kv.pt"), "e5m2")
+    # a saved object outside the weights-only allowlist is refused by the loader
+    import datetime
+    torch.save({"k": datetime.date(2020, 1, 1)}, str(tmp_path / "obj.pt"))
+    with pytest.raises(Exception) as ei:
+        bench.load_saved(str(tmp_path / "obj.pt"), "bf16")
+    assert "weights" in str(ei.value).lower() or "unpickl" in str(ei.value).lower()
+
+
+def test_saved_workload_calibrates_on_the_given_tensors(tmp_path):
+    import argparse
+
+    import numpy as np
+    import torch
+    from safetensors.torch import save_file
+    save_file({"a": torch.randn(64).to(torch.bfloat16), "b": torch.randn(32).to(torch.bfloat16)},
+              str(tmp_path / "x.safetensors"))
+    save_file({"c": torch.randn(48).to(torch.bfloat16)}, str(tmp_path / "cal.safetensors"))
+    args = argparse.Namespace(input=str(tmp_path / "x.safetensors"), calibration_input="",
+                              elem="bf16", chunk_size=1024)
+    wl, names = bench.saved_workload(args)
+    assert names == ["a", "b"] and [s.size for s in wl.segments] == [64, 32]
+    assert wl.calibration.size == 96
+    args.calibration_input = str(tmp_path / "cal.safetensors")
+    wl, _ = bench.saved_workload(args)
+    assert wl.calibration.size == 48 and wl.chunk_size == 1024

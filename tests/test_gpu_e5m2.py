@@ -198,10 +198,28 @@ def test_decode_flags_corrupt_metadata_without_faulting(stage_tiles):
         codec.decode_into([bad], [y], d_error=err.data_ptr())
         torch.cuda.synchronize()
         assert int(err.item()) != 0, field
+    # every escape in the last chunk: more than that chunk's elements
+    bad = dataclasses.replace(enc, chunk_off=enc.chunk_off.clone())
+    bad.chunk_off[:-1] = 0
+    assert enc.n_escapes > 1024
+    err.zero_()
+    codec.decode_into([bad], [y], d_error=err.data_ptr())
+    torch.cuda.synchronize()
+    assert int(err.item()) & 2
     err.zero_()
     codec.decode_into([enc], [y], d_error=err.data_ptr())
     torch.cuda.synchronize()
     assert int(err.item()) == 0 and np.array_equal(host(y, np.uint8), x)
+    # more escapes than the last tile has elements
+    x2 = workloads.e5m2_mixed(4 * 16384, 13, wide_fraction=0.7)
+    enc2 = codec.encode(dev8(x2))
+    assert enc2.n_escapes > 16384
+    bad = dataclasses.replace(enc2, chunk_off=enc2.chunk_off.clone())
+    bad.chunk_off[:-1] = 0
+    err.zero_()
+    codec.decode_into([bad], [torch.empty_like(y)], d_error=err.data_ptr())
+    torch.cuda.synchronize()
+    assert int(err.item()) & 2
 
 
 def test_element_type_and_codebook_checks():

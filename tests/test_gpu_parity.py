@@ -200,11 +200,31 @@ def test_decode_flags_corrupt_metadata_without_faulting(stage_tiles):
     codec.decode_into([bad], [y], d_error=err.data_ptr())
     torch.cuda.synchronize()
     assert int(err.item()) != 0
+    # every escape in the last chunk (offsets 0 up to the final E): more escapes than that
+    # chunk has words
+    bad = dataclass_copy(enc)
+    bad.chunk_off[:-1] = 0
+    assert enc.n_escapes > 1024
+    err.zero_()
+    codec.decode_into([bad], [y], d_error=err.data_ptr())
+    torch.cuda.synchronize()
+    assert int(err.item()) & 2
     # an intact stream leaves the flag at zero
     err.zero_()
     codec.decode_into([enc], [y], d_error=err.data_ptr())
     torch.cuda.synchronize()
     assert int(err.item()) == 0 and np.array_equal(host(y, np.uint16), x)
+    # more escapes than the last tile has words: flagged, that tile left unpatched
+    x2 = workloads.mixed_words(4 * 8192, 13, wide_fraction=0.6)
+    enc2 = codec.encode(dev(x2))
+    assert enc2.n_escapes > 8192
+    bad = dataclass_copy(enc2)
+    bad.chunk_off[:-1] = 0
+    y2 = torch.empty_like(y)
+    err.zero_()
+    codec.decode_into([bad], [y2], d_error=err.data_ptr())
+    torch.cuda.synchronize()
+    assert int(err.item()) & 2
 
 
 def dataclass_copy(e: sz.Encoded) -> sz.Encoded:
