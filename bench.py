@@ -368,7 +368,8 @@ def transfer_bench(args, codec, xs, books, wl, esize, coverage):
                   "last decode; median over the timed runs",
         "round_trip_bitwise": True,
     }
-    print(json.dumps(out), flush=True)
+    plan.close()
+    emit(out, args.output)
 
 
 def main(argv=None):

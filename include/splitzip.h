@@ -47,6 +47,9 @@
  *     esc_pos 2-byte.  n per segment < 2^38.
  *   - A codec may be used from several host threads and streams; calls on one
  *     stream are ordered, calls on different streams use different workspaces.
+ *
+ * The calls that choose between kernel builds and launch sequences, and per-kernel timing,
+ * are in splitzip_tuning.h: no page fixes them and the bytes written do not depend on them.
  */
 #ifndef SPLITZIP_H
 #define SPLITZIP_H
@@ -320,86 +323,17 @@ int splitzip_decode_packed(splitzip_codec *codec, uint32_t n_seg, const splitzip
  * freeing its device memory synchronizes the device. */
 void splitzip_free(splitzip_codec *codec);
 
-/* ---- launch sequence of an encode ---- */
-
-/* Default and largest value of splitzip_set_small_tiles. */
-#define SPLITZIP_SMALL_TILES 2048
-
 /*
- * How the encode of README "Codec API" is launched; no page fixes it, and the bytes
- * written are the same either way.
- * An encode call (any of the encode entry points) splits its segments into tiles of
- * 16384 BF16 words or 32768 E5M2 bytes, at least one per segment.  A call of at most
- * max_tiles tiles runs two kernel launches (pack, then finish: each tile's escape offset,
- * escape placement, chunk offsets), a larger call four (pack, sums, place, spill); on
- * inputs of a few MiB the launches, not the bytes, set the time.  Both sequences write
- * identical bytes.  max_tiles <= SPLITZIP_SMALL_TILES (default), 0 = always four launches;
- * larger values give SPLITZIP_E_INVALID.  Applies to calls that start after it returns.
+ * Release the workspace a codec keeps for one stream (no page defines it; the stateful
+ * codec of README "Codec API" keeps scratch between calls).  A codec creates one workspace
+ * per stream it is used on and keeps it, with its encode scratch (about 1/30 of the largest
+ * input encoded on that stream, plus 4 bytes per entry of escape capacity or per element of
+ * the tiles' own overflow regions), until this call or splitzip_free: a long-lived codec
+ * used from short-lived streams calls this before destroying such a stream.  Waits for the
+ * stream, then frees; a stream with no workspace is a no-op (SPLITZIP_OK).  The codec stays
+ * usable on any stream; a later call on the same stream makes a new workspace.
  */
-int splitzip_set_small_tiles(splitzip_codec *codec, uint32_t max_tiles);
-
-/* Default of splitzip_set_stage_tiles. */
-#define SPLITZIP_STAGE_TILES 1024
-
-/*
- * Which builds of the pack and decode kernels a call runs; no page fixes it, and the bytes
- * written are the same either way.  An encode call of more than min_tiles tiles (tiles as
- * for splitzip_set_small_tiles), and a decode call of more than 2 * min_tiles decode tiles
- * (8192 BF16 words or 16384 E5M2 bytes, at least one per segment: the same elements), run
- * the builds tuned for escape-heavy inputs: in pack a wave gathers a group's escapes in LDS
- * and stores them as one contiguous run when there are more than 64 of them; in decode an
- * escape finds its chunk among offsets held in scalar registers when a tile spans at most 8
- * chunks (16 for E5M2) instead of by a binary search in LDS.  Smaller calls run the builds
- * without them, whose smaller code costs less when the call is short and its instructions
- * are not yet in the caches.  Any value is accepted: 0 = always the tuned builds,
- * UINT32_MAX = never.  Applies to calls that start after it returns.
- */
-int splitzip_set_stage_tiles(splitzip_codec *codec, uint32_t min_tiles);
-
-/* Default of splitzip_set_private_overflow: 256 MiB. */
-#define SPLITZIP_PRIVATE_OVERFLOW_BYTES (256ull << 20)
-
-/*
- * Where an encode call's escape-heavy tiles put the escapes that do not fit their slot; no
- * page fixes it, and the bytes written are the same either way.  When 4 bytes per element
- * of all the call's tiles (tiles as for splitzip_set_small_tiles) come to at most max_bytes,
- * every tile gets its own region of the library's scratch memory, so no tile waits on a
- * shared counter; otherwise tiles reserve ranges of one area, as large as the call's escape
- * capacity, with an atomic counter (thousands of escape-heavy tiles contend for it).  The
- * scratch memory stays allocated with the codec's workspace.  0 = always the shared area.
- * Applies to calls that start after it returns.
- */
-int splitzip_set_private_overflow(splitzip_codec *codec, uint64_t max_bytes);
-
-/* ---- per-kernel timing (for benchmarks and profilers: the codec throughput measurement
- *      of README "Quick Start") ---- */
-
-/* Kernels whose durations splitzip_profile_read reports, in this order. */
-#define SPLITZIP_KERNEL_PACK 0    /* encode: split, pack, in-tile escape compaction      */
-#define SPLITZIP_KERNEL_SUMS 1    /* encode: segmented sums of per-tile escape counts    */
-#define SPLITZIP_KERNEL_PLACE 2   /* encode: escape placement, global chunk offsets      */
-#define SPLITZIP_KERNEL_SPILL 3   /* encode: placement of escape-heavy tiles' escapes    */
-#define SPLITZIP_KERNEL_DECODE 4  /* decode                                               */
-#define SPLITZIP_KERNEL_FINISH 5  /* encode, small calls: offsets and placement per tile  */
-#define SPLITZIP_KERNELS 6
-
-/*
- * Timing of the codec's kernels, which README "Quick Start" measures as codec throughput.
- * enable != 0: every later encode/decode call on this codec records HIP events around
- * each of its kernel launches, on the call's stream.  enable == 0 stops recording and
- * discards accumulated timings.
- */
-int splitzip_profile(splitzip_codec *codec, int enable);
-
-/*
- * (README "Quick Start": codec throughput.)
- * Wait for `stream`, then report for each kernel kind the mean duration in ms and the
- * number of launches timed on that stream since profiling was enabled or last reset
- * (reset != 0 clears the totals after reading).  avg_ms and counts: host arrays of
- * SPLITZIP_KERNELS entries.
- */
-int splitzip_profile_read(splitzip_codec *codec, void *stream, double *avg_ms, uint64_t *counts,
-                          int reset);
+int splitzip_release_stream(splitzip_codec *codec, void *stream);
 
 /* ---- exponent statistics (README "Repository Contents" and "Reproducing Paper Artifact
  *      Scripts": BF16 KV exponent entropy and top-16 coverage analysis) ---- */

@@ -34,7 +34,7 @@ LIB_PATH = os.path.join(_HERE, "libsplitzip.so")
 
 OK, E_INVALID, E_NOMEM, E_DEVICE, E_CODEBOOK, E_FORMAT, E_CAPACITY = range(7)
 HEADER_BYTES = 64
-SMALL_TILES = 2048      # encodes of at most this many tiles run pack + finish (two launches)
+SMALL_TILES = 4096      # encodes of at most this many tiles run pack + finish (two launches)
 STAGE_TILES = 1024      # larger calls run the kernel builds tuned for escape-heavy inputs
 PRIVATE_OVERFLOW_BYTES = 256 << 20   # calls up to this much per-tile overflow scratch use it
 MIN_CHUNK, MAX_CHUNK = 16, 65536
@@ -125,6 +125,8 @@ def lib() -> ctypes.CDLL:
     L.splitzip_profile_read.argtypes = [vp, vp, P(ctypes.c_double), P(u64), i32]
     L.splitzip_free.argtypes = [vp]
     L.splitzip_free.restype = None
+    L.splitzip_release_stream.argtypes = [vp, vp]
+    L.splitzip_workspace_bytes.argtypes = [vp, vp, P(u64)]
     L.splitzip_chunk_count.argtypes = [u64, u32]
     L.splitzip_chunk_count.restype = u64
     L.splitzip_compressed_bytes.argtypes = [u64, u32, u64]
@@ -146,7 +148,8 @@ def lib() -> ctypes.CDLL:
               "splitzip_set_small_tiles", "splitzip_set_stage_tiles", "splitzip_set_private_overflow",
               "splitzip_read_header", "splitzip_check_header", "splitzip_calibrate_e5m2",
               "splitzip_calibrate_books_e5m2", "splitzip_codec_from_codebooks_e5m2",
-              "splitzip_codec_element", "splitzip_histogram_e5m2"):
+              "splitzip_codec_element", "splitzip_histogram_e5m2", "splitzip_release_stream",
+              "splitzip_workspace_bytes"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -356,6 +359,18 @@ def splitzip_profile_read(codec: int, stream: int = 0, reset: bool = False) -> d
     cnt = (ctypes.c_uint64 * len(KERNELS))()
     _check(lib().splitzip_profile_read(codec, stream or None, avg, cnt, 1 if reset else 0))
     return {k: (avg[i], int(cnt[i])) for i, k in enumerate(KERNELS)}
+
+
+def splitzip_release_stream(codec: int, stream: int = 0) -> None:
+    """Free the workspace the codec keeps for `stream` (waits for the stream first)."""
+    _check(lib().splitzip_release_stream(codec, stream or None))
+
+
+def splitzip_workspace_bytes(codec: int, stream: int = 0) -> int:
+    """Device bytes of the workspace the codec keeps for `stream` (0: none)."""
+    b = ctypes.c_uint64()
+    _check(lib().splitzip_workspace_bytes(codec, stream or None, ctypes.byref(b)))
+    return b.value
 
 
 def splitzip_free(codec: int) -> None:
@@ -658,6 +673,28 @@ class Codec:
         self._need_handle()
         with torch.cuda.device(self.device):
             return splitzip_profile_read(self.handle, self._stream(), reset)
+
+    def release_stream(self, stream=None) -> None:
+        """Free the workspace this codec keeps for a stream (a torch.cuda.Stream, a raw
+        hipStream_t, or None for the current stream); call before dropping a stream the codec
+        was used on."""
+        import torch
+        self._need_handle()
+        if stream is None:
+            raw = self._stream()
+        elif isinstance(stream, torch.cuda.Stream):
+            raw = stream.cuda_stream
+        else:
+            raw = int(stream)
+        splitzip_release_stream(self.handle, raw)
+
+    def workspace_bytes(self, stream=None) -> int:
+        """Device bytes of the workspace this codec keeps for a stream (0: none)."""
+        import torch
+        self._need_handle()
+        raw = self._stream() if stream is None else (stream.cuda_stream if isinstance(stream, torch.cuda.Stream)
+                                                     else int(stream))
+        return splitzip_workspace_bytes(self.handle, raw)
 
     def __del__(self):
         try:

@@ -268,7 +268,8 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
 hipError_t launch_encode_pack_e5m2(const EncodeArgs &a, hipStream_t stream)
 {
     if (a.stage)
-        encode_pack_e5m2_kernel<true><<<a.n_tiles, kThreads, kE8PackLdsReserve, stream>>>(a);
+        encode_pack_e5m2_kernel<true><<<a.n_tiles, kThreads, a.n_tiles >= kPackCapTiles ? kE8PackLdsReserve : 0u,
+                                        stream>>>(a);
     else
         encode_pack_e5m2_kernel<false><<<a.n_tiles, kThreads, 0, stream>>>(a);
     return hipGetLastError();
@@ -465,29 +466,35 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
             for (int c = 0; c < kFew; ++c)
                 rel[c] = (few && c >= 1 && (uint64_t)c < nc) ? __builtin_amdgcn_readfirstlane((uint32_t)(s_off[c] - j0))
                                                       : 0xFFFFFFFFu;
-            for (uint64_t jb = j0 + tid; jb < j1; jb += kPatch * kThreads) {
+            // 32-bit arithmetic relative to the tile: escape rank r in [0, cnt), chunk starts
+            // lo << log2c inside the tile (a chunk is at most a tile here), cnt <= valid
+            const uint32_t cnt = (uint32_t)(j1 - j0);
+            const SZ_GLOBAL uint16_t *tpos = gpos + j0;
+            const SZ_GLOBAL uint8_t *texp = gexp + j0;
+            const uint32_t tvalid = (uint32_t)valid;
+            for (uint32_t rb = tid; rb < cnt; rb += kPatch * kThreads) {
                 uint32_t pos[kPatch], ev[kPatch];
 #pragma unroll
                 for (int k = 0; k < kPatch; ++k) {
-                    const uint64_t jj = jb + (uint64_t)k * kThreads;
-                    if (jj < j1) {
-                        pos[k] = gpos[jj];
-                        ev[k] = gexp[jj];
+                    const uint32_t r = rb + (uint32_t)k * kThreads;
+                    if (r < cnt) {
+                        pos[k] = tpos[r];
+                        ev[k] = texp[r];
                     }
                 }
 #pragma unroll
                 for (int k = 0; k < kPatch; ++k) {
-                    const uint64_t jj = jb + (uint64_t)k * kThreads;
-                    if (jj >= j1)
+                    const uint32_t r = rb + (uint32_t)k * kThreads;
+                    if (r >= cnt)
                         continue;
                     uint32_t lo = 0;
                     if (few) {
-                        const uint32_t r = (uint32_t)(jj - j0);
 #pragma unroll
                         for (int c = 1; c < kFew; ++c)
                             lo += r >= rel[c] ? 1u : 0u;
                         lo = lo < (uint32_t)nc ? lo : (uint32_t)nc - 1u;
                     } else {
+                        const uint64_t jj = j0 + r;
                         uint32_t hi = (uint32_t)nc;          // s_off[lo] <= jj < s_off[hi]
                         while (hi - lo > 1) {
                             const uint32_t mid = (lo + hi) >> 1;
@@ -497,14 +504,14 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
                                 hi = mid;
                         }
                     }
-                    const uint64_t cstart = (c0 + lo) << log2c;
-                    const uint64_t clen = n - cstart < C ? n - cstart : C;
+                    const uint32_t cs = lo << log2c;
+                    const uint32_t clen = tvalid - cs < (uint32_t)C ? tvalid - cs : (uint32_t)C;
                     if (pos[k] >= clen || ev[k] > 31u) {
                         if (a.err)
                             atomicOr(a.err, pos[k] >= clen ? kErrBadPosition : kErrBadExponent);
                         continue;
                     }
-                    bytes[cstart + pos[k] - base] = (uint8_t)(ev[k] << 2);
+                    bytes[cs + pos[k]] = (uint8_t)(ev[k] << 2);
                 }
             }
         } else {

@@ -14,6 +14,7 @@
 #include "splitzip_internal.h"
 
 #include <splitzip.h>
+#include <splitzip_tuning.h>
 
 #include <algorithm>
 #include <atomic>
@@ -205,7 +206,9 @@ struct splitzip_codec {
     uint8_t *d_lut = nullptr;   // device [256 * n_books] inverse LUTs
     uint32_t *d_cbs = nullptr;  // device [4 * n_books] codebooks as little-endian dwords
     std::mutex mu;
-    std::map<hipStream_t, std::unique_ptr<Workspace>> ws;
+    // one workspace per stream; a call holds a reference for its duration, so that
+    // splitzip_release_stream can drop the map's reference while a call still uses it
+    std::map<hipStream_t, std::shared_ptr<Workspace>> ws;
 };
 
 namespace {
@@ -342,22 +345,32 @@ int run_histograms(uint32_t n_seg, const void *const *d_x, const uint64_t *n, ui
     return SPLITZIP_OK;
 }
 
-// Workspace of (codec, stream), created on first use.
-int get_workspace(splitzip_codec *c, hipStream_t stream, Workspace **out)
+// Workspace of (codec, stream), created on first use; the caller keeps *out for the call.
+int get_workspace(splitzip_codec *c, hipStream_t stream, std::shared_ptr<Workspace> *out)
 {
     std::lock_guard<std::mutex> lock(c->mu);
     auto it = c->ws.find(stream);
     if (it != c->ws.end()) {
-        *out = it->second.get();
+        *out = it->second;
         return SPLITZIP_OK;
     }
-    std::unique_ptr<Workspace> w(new (std::nothrow) Workspace);
+    std::shared_ptr<Workspace> w(new (std::nothrow) Workspace);
     if (!w)
         return fail(SPLITZIP_E_NOMEM, "host allocation of a workspace failed");
     w->stream = stream;
-    *out = w.get();
+    *out = w;
     c->ws.emplace(stream, std::move(w));
     return SPLITZIP_OK;
+}
+
+// Device bytes a workspace holds (its lock held).
+uint64_t workspace_device_bytes(const Workspace &w)
+{
+    uint64_t b = w.scratch_cap + (w.ovf_ctr ? 2 * sizeof(unsigned long long) : 0) +
+                 (w.result ? 8 + 8 * (uint64_t)w.result_cap : 0);
+    for (const Staging &s : w.staging)
+        b += (s.d_segs ? (uint64_t)s.cap * sizeof(sz::SegDesc) : 0) + (s.d_tiles ? s.tcap * sizeof(uint32_t) : 0);
+    return b;
 }
 
 // ---- profiling: events around each launch, resolved into per-kernel totals ----------
@@ -1076,10 +1089,11 @@ int encode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
                   uint64_t *d_result, Workspace **out_ws)
 {
     const uint32_t n_seg = (uint32_t)desc.size();
-    Workspace *w = nullptr;
-    int rc = get_workspace(codec, stream, &w);
+    std::shared_ptr<Workspace> hold;      // the caller holds its own reference too
+    int rc = get_workspace(codec, stream, &hold);
     if (rc != SPLITZIP_OK)
         return rc;
+    Workspace *w = hold.get();
     const uint32_t n_tiles = tiles[n_seg];
     const uint32_t tile_shift = codec->elem == sz::kElemE5M2 ? sz::kE8EncTileShift : sz::kEncTileShift;
     // every tile its own overflow region when those fit the limit; else one shared area as
@@ -1163,9 +1177,10 @@ int splitzip_encode_async(splitzip_codec *codec, uint32_t n_seg, const splitzip_
         if (dg.err != hipSuccess)
             return fail_hip(dg.err, "hipSetDevice");
         hipStream_t stream = static_cast<hipStream_t>(stream_);
-        Workspace *ws = nullptr;
-        if ((rc = get_workspace(codec, stream, &ws)) != SPLITZIP_OK)
+        std::shared_ptr<Workspace> hold;
+        if ((rc = get_workspace(codec, stream, &hold)) != SPLITZIP_OK)
             return rc;
+        Workspace *ws = hold.get();
         // the lock covers only the launch: nothing is read back
         std::lock_guard<std::mutex> lock(ws->mu);
         Workspace *w = nullptr;
@@ -1299,9 +1314,10 @@ int splitzip_encode(splitzip_codec *codec, uint32_t n_seg, splitzip_segment *seg
         if (dg.err != hipSuccess)
             return fail_hip(dg.err, "hipSetDevice");
         hipStream_t stream = static_cast<hipStream_t>(stream_);
-        Workspace *ws = nullptr;
-        if ((rc = get_workspace(codec, stream, &ws)) != SPLITZIP_OK)
+        std::shared_ptr<Workspace> hold;
+        if ((rc = get_workspace(codec, stream, &hold)) != SPLITZIP_OK)
             return rc;
+        Workspace *ws = hold.get();
         std::lock_guard<std::mutex> lock(ws->mu);
         Workspace *w = nullptr;
         if ((rc = encode_launch(codec, desc, tiles, common_book(n_seg, segs), false, stream, nullptr, &w)) != SPLITZIP_OK)
@@ -1338,9 +1354,10 @@ int splitzip_encode_packed(splitzip_codec *codec, uint32_t n_seg, splitzip_packe
         if (dg.err != hipSuccess)
             return fail_hip(dg.err, "hipSetDevice");
         hipStream_t stream = static_cast<hipStream_t>(stream_);
-        Workspace *ws = nullptr;
-        if ((rc = get_workspace(codec, stream, &ws)) != SPLITZIP_OK)
+        std::shared_ptr<Workspace> hold;
+        if ((rc = get_workspace(codec, stream, &hold)) != SPLITZIP_OK)
             return rc;
+        Workspace *ws = hold.get();
         std::lock_guard<std::mutex> lock(ws->mu);
         Workspace *w = nullptr;
         rc = encode_launch(codec, desc, tiles, common_book_packed(n_seg, segs), true, stream, d_result, &w);
@@ -1375,12 +1392,14 @@ int decode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
         return fail_hip(dg.err, "hipSetDevice");
     sz::DecodeArgs a{};
     a.seg0 = desc[0];
+    std::shared_ptr<Workspace> hold;
     Workspace *w = nullptr;
     std::unique_lock<std::mutex> lock;
     int rc;
     if (n_seg > 1 || codec->profiling) {
-        if ((rc = get_workspace(codec, stream, &w)) != SPLITZIP_OK)
+        if ((rc = get_workspace(codec, stream, &hold)) != SPLITZIP_OK)
             return rc;
+        w = hold.get();
         lock = std::unique_lock<std::mutex>(w->mu);
     }
     if (n_seg > 1 && (rc = stage_descriptors(w, desc, tiles, &a.segs, &a.tile_start, &a.seg_at)) != SPLITZIP_OK)
@@ -1491,19 +1510,19 @@ int splitzip_profile(splitzip_codec *codec, int enable)
         if (rc != SPLITZIP_OK)
             return rc;
         DeviceGuard dg(codec->device);
-        std::vector<Workspace *> all;
+        std::vector<std::shared_ptr<Workspace>> all;
         {
             // workspace locks are taken without the codec lock held (calls hold them the other
             // way round)
             std::lock_guard<std::mutex> lock(codec->mu);
             codec->profiling = enable != 0;
             for (auto &kv : codec->ws)
-                all.push_back(kv.second.get());
+                all.push_back(kv.second);
         }
         if (!enable) {
-            for (Workspace *w : all) {
+            for (const std::shared_ptr<Workspace> &w : all) {
                 std::lock_guard<std::mutex> wl(w->mu);
-                resolve_timings(w, true);
+                resolve_timings(w.get(), true);
                 std::fill(w->sum_ms, w->sum_ms + SPLITZIP_KERNELS, 0.0);
                 std::fill(w->timed, w->timed + SPLITZIP_KERNELS, 0);
             }
@@ -1526,10 +1545,11 @@ int splitzip_profile_read(splitzip_codec *codec, void *stream_, double *avg_ms, 
         if (dg.err != hipSuccess)
             return fail_hip(dg.err, "hipSetDevice");
         hipStream_t stream = static_cast<hipStream_t>(stream_);
-        Workspace *w = nullptr;
-        rc = get_workspace(codec, stream, &w);
+        std::shared_ptr<Workspace> hold;
+        rc = get_workspace(codec, stream, &hold);
         if (rc != SPLITZIP_OK)
             return rc;
+        Workspace *w = hold.get();
         std::lock_guard<std::mutex> lock(w->mu);
         SZ_HIP(hipStreamSynchronize(stream), "hipStreamSynchronize");
         resolve_timings(w, true);
@@ -1540,6 +1560,65 @@ int splitzip_profile_read(splitzip_codec *codec, void *stream_, double *avg_ms, 
                 w->sum_ms[k] = 0.0;
                 w->timed[k] = 0;
             }
+        }
+        return SPLITZIP_OK;
+    });
+}
+
+int splitzip_release_stream(splitzip_codec *codec, void *stream_)
+{
+    return guarded([&]() -> int {
+        g_last_error[0] = '\0';
+        int rc = codec_check(codec);
+        if (rc != SPLITZIP_OK)
+            return rc;
+        DeviceGuard dg(codec->device);
+        if (dg.err != hipSuccess)
+            return fail_hip(dg.err, "hipSetDevice");
+        hipStream_t stream = static_cast<hipStream_t>(stream_);
+        std::shared_ptr<Workspace> w;
+        {
+            std::lock_guard<std::mutex> lock(codec->mu);
+            auto it = codec->ws.find(stream);
+            if (it == codec->ws.end())
+                return SPLITZIP_OK;
+            w = std::move(it->second);
+            codec->ws.erase(it);
+        }
+        const hipError_t e = hipStreamSynchronize(stream);
+        {
+            // a call still inside the library on another thread holds the lock (and its own
+            // reference, so the workspace then goes when that call returns)
+            std::lock_guard<std::mutex> wl(w->mu);
+        }
+        w.reset();
+        if (e != hipSuccess)
+            return fail_hip(e, "hipStreamSynchronize");
+        return SPLITZIP_OK;
+    });
+}
+
+int splitzip_workspace_bytes(const splitzip_codec *codec, void *stream_, uint64_t *bytes)
+{
+    return guarded([&]() -> int {
+        g_last_error[0] = '\0';
+        int rc = codec_check(codec);
+        if (rc != SPLITZIP_OK)
+            return rc;
+        if (!bytes)
+            return fail(SPLITZIP_E_INVALID, "bytes is NULL");
+        splitzip_codec *c = const_cast<splitzip_codec *>(codec);   // only its locks change
+        std::shared_ptr<Workspace> w;
+        {
+            std::lock_guard<std::mutex> lock(c->mu);
+            auto it = c->ws.find(static_cast<hipStream_t>(stream_));
+            if (it != c->ws.end())
+                w = it->second;
+        }
+        *bytes = 0;
+        if (w) {
+            std::lock_guard<std::mutex> wl(w->mu);
+            *bytes = workspace_device_bytes(*w);
         }
         return SPLITZIP_OK;
     });

@@ -24,11 +24,13 @@ static_assert(kThreads * kEncGroups * kGroupWords == kEncTileWords, "encode tile
 static_assert(kThreads * kDecGroups * kGroupWords == kDecTileWords, "decode tile geometry");
 // Extra LDS reserved per decode workgroup to hold occupancy at 5 workgroups per CU.
 constexpr unsigned kDecodeLdsReserve = 16384;
-// The same for the large-call pack builds: 4 BF16 workgroups per CU (registers allow 5) and
-// 5 E5M2 workgroups (registers and LDS allow 6) stream 2 % and 2.5 % faster on inputs of GBs:
-// fewer concurrent tiles, each a long run of reads and writes.
+// The same for the pack kernels of calls of at least kPackCapTiles tiles: 4 BF16 workgroups
+// per CU (registers allow 5) and 5 E5M2 workgroups (registers and LDS allow 6) stream 2 % and
+// 2.5 % faster on inputs of GBs (fewer concurrent tiles, each a long run of reads and writes);
+// on a grid of a few thousand tiles the cap costs more in its last, partly filled round.
 constexpr unsigned kPackLdsReserve = 31744;
 constexpr unsigned kE8PackLdsReserve = 8192;
+constexpr uint32_t kPackCapTiles = 16384;
 
 // ---- element types ----------------------------------------------------------------------
 // BF16 words (sign bit 15, exponent bits 14..7, mantissa bits 6..0) or FP8 E5M2 bytes (sign
@@ -61,7 +63,8 @@ constexpr uint32_t kE8SlotEscapes = 256;                      // E5M2 tiles (twi
 constexpr uint32_t kSumTiles = 2048;          // tiles per segmented-sum block
 constexpr uint32_t kPlaceTiles = 64;          // tiles per placement workgroup
 constexpr uint32_t kSpillBlocks = 4096;       // workgroups moving the overflow tiles' escapes
-constexpr uint32_t kFinishPartShift = 2;     // large-call finish: 4 workgroups per tile
+constexpr uint32_t kFinishPartShift = 2;     // large-call finish: 4 workgroups per tile ...
+constexpr uint32_t kFinishPartTiles = 2048;  // ... in calls of at most this many tiles
 // a wave gathers one group's escapes in LDS before storing them when it has more than this
 constexpr uint32_t kStageMin = 64;
 // calls of more than this many pack tiles (decode: twice as many decode tiles, the same
@@ -76,8 +79,9 @@ constexpr uint32_t kStageTiles = 1024;
 constexpr uint64_t kPrivateOvfBytes = 256ull << 20;
 // Calls of at most this many tiles finish in one launch after pack (kStageFinish, one
 // workgroup per tile) instead of sums, place and spill: each workgroup adds up the escape
-// counts of its segment's earlier tiles itself (at most kSmallTiles - 1 loads).
-constexpr uint32_t kSmallTiles = 2048;
+// counts of its segment's earlier tiles itself (at most kSmallTiles - 1 loads, which the
+// workgroups of a call make T^2 / 2 of, from L2: a few microseconds at 4096 tiles).
+constexpr uint32_t kSmallTiles = 4096;
 // overflow counter: escapes reserved so far (low 40 bits) and overflow tiles listed (high 24)
 constexpr int kOvfTileShift = 40;
 constexpr uint64_t kOvfOffsetMask = (1ull << kOvfTileShift) - 1;

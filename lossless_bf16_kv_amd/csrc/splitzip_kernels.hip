@@ -767,6 +767,14 @@ __global__ __launch_bounds__(kThreads) void encode_spill_kernel(const EncodeArgs
 
 // ---- finish (calls of at most kSmallTiles tiles) ------------------------------------------
 
+// log2 of the finish workgroups per tile: several in the large-call build (they share an
+// escape-heavy tile's moves), one in calls of more than kFinishPartTiles tiles, whose every
+// workgroup also adds up the counts of the earlier tiles.
+__host__ __device__ inline uint32_t finish_part_shift(const EncodeArgs &a)
+{
+    return a.stage && a.n_tiles <= kFinishPartTiles ? kFinishPartShift : 0u;
+}
+
 // Sum of v over the workgroup, in every thread.  Contains barriers.
 __device__ __forceinline__ uint64_t block_total_u64(uint64_t v, uint32_t tid, uint32_t lane,
                                                     uint64_t *s_part)
@@ -798,7 +806,7 @@ __global__ __launch_bounds__(kThreads) void encode_finish_kernel(const EncodeArg
     // moves: a tile whose elements all escape needs several rounds of loads and stores, most
     // tiles one, and the slowest tiles set the launch's time.  Part 0 also makes the chunk
     // offsets global and writes the segment's totals.
-    const uint32_t pshift = a.stage ? kFinishPartShift : 0u;
+    const uint32_t pshift = finish_part_shift(a);
     const uint32_t t = blockIdx.x >> pshift;
     const uint32_t part = blockIdx.x & ((1u << pshift) - 1u);
     const uint64_t cmask = (1ull << a.log2_chunk) - 1;
@@ -956,7 +964,8 @@ hipError_t launch_encode_stage(int stage, const EncodeArgs &a, hipStream_t strea
         if (a.elem == kElemE5M2)
             return launch_encode_pack_e5m2(a, stream);
         if (a.stage)
-            encode_pack_kernel<true><<<a.n_tiles, kThreads, kPackLdsReserve, stream>>>(a);
+            encode_pack_kernel<true><<<a.n_tiles, kThreads, a.n_tiles >= kPackCapTiles ? kPackLdsReserve : 0u,
+                                       stream>>>(a);
         else
             encode_pack_kernel<false><<<a.n_tiles, kThreads, 0, stream>>>(a);
         break;
@@ -972,7 +981,7 @@ hipError_t launch_encode_stage(int stage, const EncodeArgs &a, hipStream_t strea
     case kStageFinish:
         if (a.n_tiles > kSmallTiles)
             return hipErrorInvalidValue;
-        encode_finish_kernel<<<a.n_tiles << (a.stage ? kFinishPartShift : 0u), kThreads, 0, stream>>>(a);
+        encode_finish_kernel<<<a.n_tiles << finish_part_shift(a), kThreads, 0, stream>>>(a);
         break;
     default:
         return hipErrorInvalidValue;
@@ -1165,29 +1174,35 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
             for (int c = 0; c < kFew; ++c)
                 rel[c] = (few && c >= 1 && (uint64_t)c < nc) ? __builtin_amdgcn_readfirstlane((uint32_t)(s_off[c] - j0))
                                                       : 0xFFFFFFFFu;
-            for (uint64_t jb = j0 + tid; jb < j1; jb += kPatch * kThreads) {
+            // 32-bit arithmetic relative to the tile: escape rank r in [0, cnt), chunk starts
+            // lo << log2c inside the tile (a chunk is at most a tile here), cnt <= valid
+            const uint32_t cnt = (uint32_t)(j1 - j0);
+            const SZ_GLOBAL uint16_t *tpos = gpos + j0;
+            const SZ_GLOBAL uint8_t *texp = gexp + j0;
+            const uint32_t tvalid = (uint32_t)valid;
+            for (uint32_t rb = tid; rb < cnt; rb += kPatch * kThreads) {
                 uint32_t pos[kPatch], ev[kPatch];
 #pragma unroll
                 for (int k = 0; k < kPatch; ++k) {
-                    const uint64_t jj = jb + (uint64_t)k * kThreads;
-                    if (jj < j1) {
-                        pos[k] = gpos[jj];
-                        ev[k] = gexp[jj];
+                    const uint32_t r = rb + (uint32_t)k * kThreads;
+                    if (r < cnt) {
+                        pos[k] = tpos[r];
+                        ev[k] = texp[r];
                     }
                 }
 #pragma unroll
                 for (int k = 0; k < kPatch; ++k) {
-                    const uint64_t jj = jb + (uint64_t)k * kThreads;
-                    if (jj >= j1)
+                    const uint32_t r = rb + (uint32_t)k * kThreads;
+                    if (r >= cnt)
                         continue;
                     uint32_t lo = 0;
                     if (few) {
-                        const uint32_t r = (uint32_t)(jj - j0);
 #pragma unroll
                         for (int c = 1; c < kFew; ++c)
                             lo += r >= rel[c] ? 1u : 0u;
                         lo = lo < (uint32_t)nc ? lo : (uint32_t)nc - 1u;
                     } else {
+                        const uint64_t jj = j0 + r;
                         uint32_t hi = (uint32_t)nc;          // s_off[lo] <= jj < s_off[hi]
                         while (hi - lo > 1) {
                             const uint32_t mid = (lo + hi) >> 1;
@@ -1197,14 +1212,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
                                 hi = mid;
                         }
                     }
-                    const uint64_t cstart = (c0 + lo) << log2c;
-                    const uint64_t clen = n - cstart < C ? n - cstart : C;
+                    const uint32_t cs = lo << log2c;
+                    const uint32_t clen = tvalid - cs < (uint32_t)C ? tvalid - cs : (uint32_t)C;
                     if (pos[k] >= clen) {
                         if (a.err)
                             atomicOr(a.err, kErrBadPosition);
                         continue;
                     }
-                    const uint32_t p = (uint32_t)(cstart + pos[k] - base);
+                    const uint32_t p = cs + pos[k];
                     bytes[(p >> 3) * 8 + (p & 1u) * 4 + ((p >> 1) & 3u)] = (uint8_t)ev[k];
                 }
             }

@@ -88,6 +88,13 @@ class TransferPlan:
         self.stream_bytes = [0] * k
         self.n_escapes = [0] * k
 
+    def close(self) -> None:
+        """Free the workspaces the codec keeps for this plan's streams (the plan is unusable
+        afterwards; the codec is not)."""
+        for st in getattr(self, "streams", []):
+            self.codec.release_stream(st)
+        self.streams = []
+
     def _allocate(self, caps) -> None:
         """Sending and receiving arenas for streams of capacities caps, and the pinned host
         arena (large enough for the raw bytes too)."""

@@ -17,15 +17,25 @@ import oracle_pins as pins
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
+HEADERS = ("splitzip.h", "splitzip_tuning.h")
+
+
 def declared_functions() -> list:
-    text = open(os.path.join(ROOT, "include", "splitzip.h")).read()
+    text = "".join(open(os.path.join(ROOT, "include", h)).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(splitzip_\w+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert {"splitzip_calibrate", "splitzip_encode", "splitzip_decode", "splitzip_free"} <= set(names)
+    assert {"splitzip_calibrate", "splitzip_encode", "splitzip_decode", "splitzip_free",
+            "splitzip_release_stream", "splitzip_encode_noalloc", "splitzip_set_small_tiles",
+            "splitzip_profile", "splitzip_workspace_bytes"} <= set(names)
+    # the tuning and timing calls live in their own header
+    main = open(os.path.join(ROOT, "include", "splitzip.h")).read()
+    for f in ("splitzip_set_small_tiles", "splitzip_set_stage_tiles", "splitzip_set_private_overflow",
+              "splitzip_profile", "splitzip_profile_read", "splitzip_workspace_bytes"):
+        assert f + "(" not in main, f
     L = sz.lib()
     for name in names:
         assert hasattr(L, name), name
@@ -232,6 +242,7 @@ def test_no_cpu_fallback():
 
 C_CONSUMER = r"""
 #include <splitzip.h>
+#include <splitzip_tuning.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -254,6 +265,11 @@ int main(void)
     if (splitzip_read_header(h, sizeof h - 1, 0, 0, 0, 0, 0) != SPLITZIP_E_FORMAT) return 6;
     if (strcmp(splitzip_status_string(SPLITZIP_E_CAPACITY), "escape capacity exceeded") != 0) return 7;
     splitzip_free(NULL);
+    /* calls without a codec fail cleanly, before any device work */
+    uint64_t ws = 1;
+    if (splitzip_release_stream(NULL, NULL) != SPLITZIP_E_INVALID) return 8;
+    if (splitzip_workspace_bytes(NULL, NULL, &ws) != SPLITZIP_E_INVALID) return 9;
+    if (splitzip_set_small_tiles(NULL, 0) != SPLITZIP_E_INVALID) return 10;
     printf("ok\n");
     return 0;
 }
@@ -261,8 +277,8 @@ int main(void)
 
 
 def test_header_compiles_as_c_and_links(tmp_path):
-    """A plain C99 program includes include/splitzip.h, links against the library and uses its
-    host helpers (no device call)."""
+    """A plain C99 program includes include/splitzip.h and splitzip_tuning.h, links against
+    the library and uses its host helpers (no device call)."""
     import subprocess
     src = tmp_path / "consumer.c"
     src.write_text(C_CONSUMER)

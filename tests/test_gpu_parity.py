@@ -527,3 +527,30 @@ def test_concurrent_host_threads_share_one_codec():
     done.set()
     prof.join()
     assert not errors, errors
+
+
+def test_release_stream_frees_its_workspace():
+    """A codec keeps one workspace per stream it encodes on; splitzip_release_stream frees
+    it (the C ABI reports 0 bytes afterwards) and a later call on that stream makes a new
+    one, with the same stream."""
+    codec = codec_for(workloads.normal_words(20000, 2), 1024)
+    s = torch.cuda.Stream(DEV)
+    assert sz.splitzip_workspace_bytes(codec.handle, s.cuda_stream) == 0
+    x_np = workloads.mixed_words(3_000_000, 5)
+    x = dev(x_np)
+    with torch.cuda.stream(s):
+        enc = codec.encode(x)
+    used = sz.splitzip_workspace_bytes(codec.handle, s.cuda_stream)
+    assert used >= (x_np.size // 16384) * 512            # at least the tiles' escape slots
+    sz.splitzip_release_stream(codec.handle, s.cuda_stream)
+    assert sz.splitzip_workspace_bytes(codec.handle, s.cuda_stream) == 0
+    sz.splitzip_release_stream(codec.handle, s.cuda_stream)          # nothing left: a no-op
+    with torch.cuda.stream(s):
+        again = codec.encode(x)
+        y = codec.decode(again)
+    s.synchronize()
+    assert sz.splitzip_workspace_bytes(codec.handle, s.cuda_stream) > 0
+    assert again.to_bytes(codec) == enc.to_bytes(codec)
+    assert np.array_equal(host(y, np.uint16), x_np)
+    codec.release_stream(s)
+    assert codec.workspace_bytes(s) == 0
