@@ -98,10 +98,11 @@ def algorithmic_bytes(ns, Es, C, e5m2: bool = False):
     count per tile; sums reads one count per tile; place reads the scratch escapes,
     counts and chunk offsets and writes escapes (3E) and chunk offsets.  The spill launch
     moves only the escapes of tiles with more than a slot's worth (a data-dependent
-    amount), so it has no fixed figure.  Calls of at most 2048 tiles run finish instead of
-    sums, place and spill: it moves what place and spill move."""
+    amount), so it has no fixed figure.  Calls of at most 4096 tiles run finish instead of
+    sums, place and spill: it moves what place and spill move.  The one-pass encode (one
+    launch) moves exactly the encode's bytes."""
     out = {"encode": 0, "decode": 0, "encode_pack": 0, "encode_sums": 0, "encode_place": 0,
-           "encode_finish": 0}
+           "encode_finish": 0, "encode_onepass": 0}
     for n, E in zip(ns, Es):
         n_ch = -(-n // C)
         tiles = max(1, -(-n // (ENC_TILE_E5M2 if e5m2 else ENC_TILE_WORDS)))
@@ -109,6 +110,7 @@ def algorithmic_bytes(ns, Es, C, e5m2: bool = False):
         sm_bytes = -(-3 * n // 8) if e5m2 else n          # sign+mantissa section
         sections = sm_bytes + (n + 1) // 2 + 8 * (n_ch + 1) + 3 * E
         out["encode"] += x_bytes + sections
+        out["encode_onepass"] += x_bytes + sections
         out["decode"] += sections + x_bytes
         out["encode_pack"] += x_bytes + sm_bytes + (n + 1) // 2 + 8 * n_ch + 4 * E + 4 * tiles
         out["encode_sums"] += 4 * tiles + 8 * (-(-tiles // 2048))
@@ -223,6 +225,44 @@ def ceiling_leg(dev, reps: int = 10, mib: int = 4096) -> dict:
     torch.cuda.empty_cache()
     out["kernels"] = "stream_ceiling.hip: 16 B per lane, 32 KiB per workgroup, XCD-contiguous tiles, " \
                      f"nontemporal; read/write {mib} MiB, copy {mib // 2} MiB; median of {reps}"
+    return out
+
+
+def floor_leg(dev, nbytes: int, flush, reps: int = 10) -> dict:
+    """What a call on this small input costs before any codec work: median microseconds,
+    with the caches flushed before each launch as in the timed steps, of a launch whose one
+    tile reads 16 bytes, and of the copy kernel of ceiling_leg over the call's own
+    input (reads and writes nbytes, about as many bytes as an encode or a decode moves)."""
+    import ctypes
+    import torch
+    from lossless_bf16_kv_amd import build as szbuild
+    L = ctypes.CDLL(szbuild.CEILING_PATH)
+    L.szc_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
+                             ctypes.c_void_p, ctypes.c_void_p]
+    L.szc_stream.restype = ctypes.c_int
+    nbytes = (nbytes + 15) // 16 * 16
+    a = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    b = torch.empty_like(a)
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for name, kind, size in (("one_tile_launch_us", 0, 16), ("copy_input_us", 2, nbytes)):
+        times = []
+        for r in range(reps + 2):
+            flush()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            rc = L.szc_stream(kind, a.data_ptr(), b.data_ptr(), size, sink.data_ptr(), stream.cuda_stream)
+            ev[1].record(stream)
+            if rc != 0:
+                raise RuntimeError(f"floor kernel {name}: HIP error {rc}")
+            torch.cuda.synchronize()
+            if r >= 2:
+                times.append(ev[0].elapsed_time(ev[1]) * 1e3)
+        out[name] = round(sorted(times)[len(times) // 2], 2)
+    out["copy_bytes"] = 2 * nbytes
+    out["copy_GBps"] = round(2 * nbytes / (out["copy_input_us"] * 1e-6) / 1e9, 1)
+    out["basis"] = f"median of {reps} launches, caches flushed before each, events on the launch stream"
     return out
 
 
@@ -611,7 +651,7 @@ def main(argv=None):
             ktimes["encode_place"][0] + ktimes["encode_spill"][0], wname)
         kernels["encode_place+spill"]["launches_timed"] = ktimes["encode_place"][1]
     # the kernel that moves the data: on small inputs a short launch can outlast it
-    dominant = max((k for k in ("encode_pack", "decode") if k in kernels),
+    dominant = max((k for k in ("encode_pack", "encode_onepass", "decode") if k in kernels),
                    key=lambda k: kernels[k]["avg_launch_ms"])
     ops = {"encode": roofline("encode (all launches)", alg["encode"], enc_avg, wname),
            "decode": roofline("decode", alg["decode"], dec_avg, wname)}
@@ -626,13 +666,18 @@ def main(argv=None):
         ceiling["frac_of_read_then_write"] = {
             "encode": ceiling_fraction(x_bytes, comp_bytes, enc_avg, ceiling),
             "decode": ceiling_fraction(comp_bytes, x_bytes, dec_avg, ceiling)}
-        if "encode_pack" in kernels:
-            pk = kernels["encode_pack"]
-            ceiling["frac_of_read_then_write"]["encode_pack"] = ceiling_fraction(
-                x_bytes, pk["algorithmic_bytes"] - x_bytes, pk["avg_launch_ms"], ceiling)
+        for k in ("encode_pack", "encode_onepass"):
+            if k in kernels:
+                pk = kernels[k]
+                ceiling["frac_of_read_then_write"][k] = ceiling_fraction(
+                    x_bytes, pk["algorithmic_bytes"] - x_bytes, pk["avg_launch_ms"], ceiling)
         if "decode" in kernels:
             ceiling["frac_of_read_then_write"]["decode_kernel"] = ceiling_fraction(
                 comp_bytes, x_bytes, kernels["decode"]["avg_launch_ms"], ceiling)
+
+    floor = None
+    if scrub is not None and not args.no_ceiling:
+        floor = floor_leg(dev, esize * n, flush)
 
     digests = None
     if not args.no_digests:
@@ -690,6 +735,7 @@ def main(argv=None):
                     "basis": f"the {args.steps} timed steps in {args.repeats} blocks, each timed with "
                              "events"},
         "ceiling": ceiling,
+        "small_call_floor": floor,
         "cpu_baseline": cpu,
         "host": host_info(),
         "inputs": digests,

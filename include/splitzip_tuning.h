@@ -32,6 +32,34 @@ extern "C" {
  */
 int splitzip_set_small_tiles(splitzip_codec *codec, uint32_t max_tiles);
 
+/* Default of splitzip_set_onepass_tiles. */
+#define SPLITZIP_ONEPASS_TILES 2048u
+
+/*
+ * Whether an encode runs as one launch; no page fixes it, and the bytes written are the same
+ * either way.  An encode call into separate section buffers (not a packed stream) of at most
+ * max_tiles tiles (tiles as for splitzip_set_small_tiles) runs one pack launch that also
+ * places every escape: each tile reads how many escapes its segment's earlier tiles hold from
+ * their status words (a decoupled look-back over tiles in launch order) and writes its
+ * escapes, chunk offsets and, as a segment's last tile, E straight to their final places.
+ * Other calls (larger ones, packed streams, and calls on a stream that is being captured
+ * into a graph, since each launch's tag is a kernel argument that a replay would repeat) run
+ * the launch sequences of splitzip_set_small_tiles.  Up to about 2048 tiles one launch is
+ * faster (no second launch); on larger calls, with many tiles in flight, each tile's wait
+ * for the earlier ones costs more than the other launches do.  The codec's workspace for the
+ * stream keeps 8 bytes per tile of state for it.  0 = never, UINT32_MAX = always; any value
+ * is accepted.  Applies to calls that start after it returns.
+ */
+int splitzip_set_onepass_tiles(splitzip_codec *codec, uint32_t max_tiles);
+
+/*
+ * Tests of the one-pass state: set the count of one-pass launches made with the codec's
+ * workspace for `stream`, whose low 23 bits tag the next launch's status words (at a tag of
+ * 0 the state is cleared before the launch).  SPLITZIP_E_INVALID when the codec has no
+ * workspace with one-pass state for the stream.
+ */
+int splitzip_set_onepass_launches(splitzip_codec *codec, void *stream, uint64_t launches);
+
 /* Default of splitzip_set_stage_tiles. */
 #define SPLITZIP_STAGE_TILES 1024
 
@@ -75,7 +103,8 @@ int splitzip_set_private_overflow(splitzip_codec *codec, uint64_t max_bytes);
 #define SPLITZIP_KERNEL_SPILL 3   /* encode: placement of escape-heavy tiles' escapes    */
 #define SPLITZIP_KERNEL_DECODE 4  /* decode                                               */
 #define SPLITZIP_KERNEL_FINISH 5  /* encode, small calls: offsets and placement per tile  */
-#define SPLITZIP_KERNELS 6
+#define SPLITZIP_KERNEL_ONEPASS 6 /* encode in one launch: pack and placement together    */
+#define SPLITZIP_KERNELS 7
 
 /*
  * Timing of the codec's kernels, which README "Quick Start" measures as codec throughput.

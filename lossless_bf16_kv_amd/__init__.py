@@ -34,7 +34,8 @@ LIB_PATH = os.path.join(_HERE, "libsplitzip.so")
 
 OK, E_INVALID, E_NOMEM, E_DEVICE, E_CODEBOOK, E_FORMAT, E_CAPACITY = range(7)
 HEADER_BYTES = 64
-SMALL_TILES = 4096      # encodes of at most this many tiles run pack + finish (two launches)
+ONEPASS_TILES = 2048    # section encodes of at most this many tiles run one launch
+SMALL_TILES = 4096      # other encodes of at most this many tiles run pack + finish (two launches)
 STAGE_TILES = 1024      # larger calls run the kernel builds tuned for escape-heavy inputs
 PRIVATE_OVERFLOW_BYTES = 256 << 20   # calls up to this much per-tile overflow scratch use it
 MIN_CHUNK, MAX_CHUNK = 16, 65536
@@ -120,6 +121,8 @@ def lib() -> ctypes.CDLL:
     L.splitzip_decode_packed.argtypes = [vp, u32, P(splitzip_packed), vp, vp]
     L.splitzip_profile.argtypes = [vp, i32]
     L.splitzip_set_small_tiles.argtypes = [vp, u32]
+    L.splitzip_set_onepass_tiles.argtypes = [vp, u32]
+    L.splitzip_set_onepass_launches.argtypes = [vp, vp, u64]
     L.splitzip_set_stage_tiles.argtypes = [vp, u32]
     L.splitzip_set_private_overflow.argtypes = [vp, ctypes.c_uint64]
     L.splitzip_profile_read.argtypes = [vp, vp, P(ctypes.c_double), P(u64), i32]
@@ -146,6 +149,7 @@ def lib() -> ctypes.CDLL:
               "splitzip_encode", "splitzip_encode_async", "splitzip_encode_noalloc", "splitzip_decode",
               "splitzip_write_header", "splitzip_profile", "splitzip_profile_read",
               "splitzip_set_small_tiles", "splitzip_set_stage_tiles", "splitzip_set_private_overflow",
+              "splitzip_set_onepass_tiles", "splitzip_set_onepass_launches",
               "splitzip_read_header", "splitzip_check_header", "splitzip_calibrate_e5m2",
               "splitzip_calibrate_books_e5m2", "splitzip_codec_from_codebooks_e5m2",
               "splitzip_codec_element", "splitzip_histogram_e5m2", "splitzip_release_stream",
@@ -334,7 +338,16 @@ def splitzip_decode_packed(codec: int, segs, stream: int = 0, d_error: int = 0) 
     _check(lib().splitzip_decode_packed(codec, len(segs), segs, stream or None, d_error or None))
 
 
-KERNELS = ("encode_pack", "encode_sums", "encode_place", "encode_spill", "decode", "encode_finish")
+KERNELS = ("encode_pack", "encode_sums", "encode_place", "encode_spill", "decode", "encode_finish",
+           "encode_onepass")
+
+
+def splitzip_set_onepass_tiles(codec: int, max_tiles: int) -> None:
+    _check(lib().splitzip_set_onepass_tiles(codec, max_tiles))
+
+
+def splitzip_set_onepass_launches(codec: int, stream: int, launches: int) -> None:
+    _check(lib().splitzip_set_onepass_launches(codec, stream or None, launches))
 
 
 def splitzip_set_small_tiles(codec: int, max_tiles: int) -> None:
@@ -572,6 +585,7 @@ class Codec:
         self.histogram = None
         self._escape_rate = 0.0
         self._small_tiles = SMALL_TILES
+        self._onepass_tiles = ONEPASS_TILES
         self._stage_tiles = STAGE_TILES
         self._private_overflow = PRIVATE_OVERFLOW_BYTES
 
@@ -623,6 +637,8 @@ class Codec:
         self.handle = h
         if self._small_tiles != SMALL_TILES:
             splitzip_set_small_tiles(h, self._small_tiles)
+        if self._onepass_tiles != ONEPASS_TILES:
+            splitzip_set_onepass_tiles(h, self._onepass_tiles)
         if self._stage_tiles != STAGE_TILES:
             splitzip_set_stage_tiles(h, self._stage_tiles)
         if self._private_overflow != PRIVATE_OVERFLOW_BYTES:
@@ -640,6 +656,16 @@ class Codec:
         if self.handle:
             splitzip_set_small_tiles(self.handle, max_tiles)
         self._small_tiles = max_tiles
+
+    def set_onepass_tiles(self, max_tiles: int = ONEPASS_TILES) -> None:
+        """Encodes into separate sections of at most max_tiles tiles run as one launch whose
+        tiles place their own escapes after a look-back over the earlier tiles (same bytes);
+        0: never.  Kept across later calibrations of this codec."""
+        if not 0 <= max_tiles < 1 << 32:
+            raise SplitZipError(E_INVALID, "max_tiles must fit 32 bits")
+        if self.handle:
+            splitzip_set_onepass_tiles(self.handle, max_tiles)
+        self._onepass_tiles = max_tiles
 
     def set_stage_tiles(self, min_tiles: int = STAGE_TILES) -> None:
         """Encodes of more than min_tiles tiles, and decodes of more than 2 * min_tiles decode

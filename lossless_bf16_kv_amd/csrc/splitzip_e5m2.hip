@@ -75,7 +75,8 @@ __device__ __forceinline__ void split_group32(const uint32_t (&x)[8], const uint
     flags = fl;
 }
 
-template <bool kStage>
+// kChain: the one-pass build (chained tiles), which writes the escapes to their final places.
+template <bool kStage, bool kChain>
 __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const EncodeArgs a)
 {
     constexpr int G = kE8EncGroups;
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
     const uint8_t *lut = a.multi_book ? a.lut + 256u * sd.book : a.lut;
     if (tid < 64)
         reinterpret_cast<uint32_t *>(s_lut)[tid] = reinterpret_cast<const uint32_t *>(lut)[tid];
-    if (a.packed && tid == 0 && t == segment_first_tile(a, s))
+    if (!kChain && a.packed && tid == 0 && t == segment_first_tile(a, s))
         a.seg_total[s] = 0;      // the sums launch adds the segment's escapes into it
     const uint64_t n = sd.n;
     const uint64_t base = (uint64_t)(t - segment_first_tile(a, s)) << kE8EncTileShift;
@@ -195,8 +196,24 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
     uint32_t tile_total;
     uint32_t wave_end;
     tile_escape_ranks<G>(counts, lane, wave, s_wave_total, rank, tile_total, wave_end);
-    uint64_t room;
-    uint32_t *dst = tile_escape_dest(a, t, tile_total, tid, &s_ovf, room);
+    // where the tile's escapes go: its slot or the overflow area; in the one-pass build their
+    // final places after the escapes of the segment's earlier tiles (at most `room` of them)
+    uint64_t room = 0, prefix = 0;
+    uint32_t *dst = nullptr;
+    SZ_GLOBAL uint16_t *fpos = nullptr;
+    SZ_GLOBAL uint8_t *fexp = nullptr;
+    if (kChain) {
+        prefix = chain_prefix(a, a.chain_tag, t, segment_first_tile(a, s), tile_total, tid, lane, &s_ovf);
+        room = sd.esc > prefix && sd.esc_exp ? sd.esc - prefix : 0;
+        fpos = as_global(sd.esc_pos + (room ? prefix : 0));
+        fexp = as_global(sd.esc_exp + (room ? prefix : 0));
+        if (tid == 0 && t + 1 == segment_end_tile(a, s)) {
+            chunk_off[(n + cmask) >> a.log2_chunk] = prefix + tile_total;
+            a.seg_escapes[s] = prefix + tile_total;
+        }
+    } else {
+        dst = tile_escape_dest(a, t, tile_total, tid, &s_ovf, room);
+    }
     SZ_GLOBAL uint32_t *gdst = as_global(dst);
 
     // escapes: (position inside the tile, exponent); tile-local chunk offsets (a chunk of 16
@@ -205,9 +222,9 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
     for (int j = 0; j < G; ++j) {
         const uint32_t r0 = rank[j];
         if (g0[j] < n && (g0[j] & cmask) == 0)
-            chunk_off[g0[j] >> a.log2_chunk] = r0;
+            chunk_off[g0[j] >> a.log2_chunk] = prefix + r0;
         if (a.log2_chunk == 4 && g0[j] + 16 < n)
-            chunk_off[(g0[j] + 16) >> 4] = r0 + __popc(flags[j] & 0xF0F0F0F0u);
+            chunk_off[(g0[j] + 16) >> 4] = prefix + r0 + __popc(flags[j] & 0xF0F0F0F0u);
         // a wave's escapes of one group have consecutive ranks; more than kStageMin of them
         // are gathered in the wave's LDS buffer (place inside the group in 11 bits, exponent
         // in 5) and stored 64 consecutive entries per instruction: stored by the lanes that
@@ -244,8 +261,14 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
                         const uint32_t b = (uint32_t)__builtin_ctz(z);
                         const uint32_t k = 2u * (b >> 3) + (b & 1u);          // element 8d + k
                         const uint32_t e = (uint32_t)(bytes8 >> (8 * k + 2)) & 0x1Fu;
-                        if (r < room)
-                            gdst[r] = (p0 + 8u * d + k) | (e << 16);
+                        if (r < room) {
+                            if (kChain) {
+                                fpos[r] = (uint16_t)((g0[j] + 8u * d + k) & cmask);
+                                fexp[r] = (uint8_t)e;
+                            } else {
+                                gdst[r] = (p0 + 8u * d + k) | (e << 16);
+                            }
+                        }
                         ++r;
                         z &= z - 1;
                     }
@@ -258,7 +281,12 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
             for (uint32_t i = lane; i < wcnt; i += 64)
                 if (w0 + i < room) {
                     const uint32_t h = s_stage[wave][i];
-                    gdst[w0 + i] = (gp + (h & 0x7FFu)) | ((h >> 11) << 16);
+                    if (kChain) {
+                        fpos[w0 + i] = (uint16_t)((base + gp + (h & 0x7FFu)) & cmask);
+                        fexp[w0 + i] = (uint8_t)(h >> 11);
+                    } else {
+                        gdst[w0 + i] = (gp + (h & 0x7FFu)) | ((h >> 11) << 16);
+                    }
                 }
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         }
@@ -267,11 +295,18 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
 
 hipError_t launch_encode_pack_e5m2(const EncodeArgs &a, hipStream_t stream)
 {
-    if (a.stage)
-        encode_pack_e5m2_kernel<true><<<a.n_tiles, kThreads, a.n_tiles >= kPackCapTiles ? kE8PackLdsReserve : 0u,
-                                        stream>>>(a);
-    else
-        encode_pack_e5m2_kernel<false><<<a.n_tiles, kThreads, 0, stream>>>(a);
+    const unsigned lds = a.n_tiles >= kPackCapTiles ? kE8PackLdsReserve : 0u;
+    if (a.chain_status) {
+        if (a.stage)
+            encode_pack_e5m2_kernel<true, true><<<a.n_tiles, kThreads, lds, stream>>>(a);
+        else
+            encode_pack_e5m2_kernel<false, true><<<a.n_tiles, kThreads, 0, stream>>>(a);
+    } else {
+        if (a.stage)
+            encode_pack_e5m2_kernel<true, false><<<a.n_tiles, kThreads, lds, stream>>>(a);
+        else
+            encode_pack_e5m2_kernel<false, false><<<a.n_tiles, kThreads, 0, stream>>>(a);
+    }
     return hipGetLastError();
 }
 

@@ -35,6 +35,7 @@ namespace {
 constexpr uint32_t kCodecMagic = 0x53a2c0dcu;
 constexpr int kStagingSlots = 16;
 
+
 thread_local char g_last_error[512];   // no allocation: fail() cannot throw
 
 int fail(int status, const char *fmt, ...)
@@ -140,6 +141,9 @@ struct Workspace {
     uint8_t *scratch = nullptr;       // encode scratch (see EncodeScratch)
     uint64_t scratch_cap = 0;         // bytes
     unsigned long long *ovf_ctr = nullptr;   // [2], see EncodeArgs
+    uint64_t *chain = nullptr;        // one-pass encode state: chain_cap status words
+    uint32_t chain_cap = 0;
+    uint64_t chain_launches = 0;      // one-pass launches on it (their tags)
     uint8_t *result = nullptr;        // [err u32, pad u32, seg_escapes u64 * result_cap]
     uint32_t result_cap = 0;
     // host
@@ -161,6 +165,7 @@ struct Workspace {
             (void)hipEventDestroy(e);
         (void)hipFree(scratch);
         (void)hipFree(ovf_ctr);
+        (void)hipFree(chain);
         (void)hipFree(result);
         (void)hipHostFree(h_result);
         for (Staging &s : staging) {
@@ -181,10 +186,17 @@ struct Workspace {
 static __device__ __align__(256) uint8_t noalloc_scratch[SPLITZIP_NOALLOC_SCRATCH_BYTES];
 
 constexpr int kNoAllocDevices = 64;
+// The last bytes of the array hold the one-pass state of the allocation-free encode: the
+// status words of up to kNoAllocChainTiles tiles (4 GiB of BF16).  Only one-pass calls touch
+// them, and the array starts zeroed (a cleared state).
+constexpr uint32_t kNoAllocChainTiles = 1u << 17;
+constexpr uint64_t kNoAllocChainBytes = 8ull * kNoAllocChainTiles;
+constexpr uint64_t kNoAllocScratchBytes = SPLITZIP_NOALLOC_SCRATCH_BYTES - kNoAllocChainBytes;
 
 struct NoAllocDevice {
     std::mutex mu;             // serializes the host side of the calls on the device
     uint8_t *base = nullptr;   // the device's copy of noalloc_scratch, once resolved
+    uint64_t chain_launches = 0;   // one-pass launches on its state
 };
 
 NoAllocDevice g_noalloc[kNoAllocDevices];
@@ -196,6 +208,7 @@ struct splitzip_codec {
     uint32_t elem = sz::kElemBF16;   // element type of every tensor the codec codes
     int device = 0;
     std::atomic<bool> profiling{false};   // set by splitzip_profile, read by every call
+    std::atomic<uint32_t> onepass_tiles{SPLITZIP_ONEPASS_TILES};   // calls of at most this many tiles: one pass
     std::atomic<uint32_t> small_tiles{sz::kSmallTiles};   // calls of at most this many tiles: pack + finish
     std::atomic<uint32_t> stage_tiles{sz::kStageTiles};   // larger calls: the builds for escape-heavy inputs
     std::atomic<uint64_t> private_ovf_bytes{sz::kPrivateOvfBytes};   // per-tile overflow regions up to this
@@ -367,6 +380,7 @@ int get_workspace(splitzip_codec *c, hipStream_t stream, std::shared_ptr<Workspa
 uint64_t workspace_device_bytes(const Workspace &w)
 {
     uint64_t b = w.scratch_cap + (w.ovf_ctr ? 2 * sizeof(unsigned long long) : 0) +
+                 8 * (uint64_t)w.chain_cap +
                  (w.result ? 8 + 8 * (uint64_t)w.result_cap : 0);
     for (const Staging &s : w.staging)
         b += (s.d_segs ? (uint64_t)s.cap * sizeof(sz::SegDesc) : 0) + (s.d_tiles ? s.tcap * sizeof(uint32_t) : 0);
@@ -488,6 +502,34 @@ int ensure_scratch(Workspace *w, uint64_t bytes)
     SZ_HIP(hipMalloc(&w->scratch, cap), "hipMalloc(encode scratch)");
     w->scratch_cap = cap;
     return SPLITZIP_OK;
+}
+
+// The one-pass state of a workspace, for calls of up to n_tiles tiles; a new one starts
+// cleared (no status word written).
+int ensure_chain(Workspace *w, uint32_t n_tiles)
+{
+    if (w->chain_cap >= n_tiles)
+        return SPLITZIP_OK;
+    const uint32_t cap = (uint32_t)std::min<uint64_t>(0xFFFFFFFFull,
+                                                      std::max<uint64_t>(n_tiles, w->chain_cap + w->chain_cap / 2));
+    SZ_HIP(hipStreamSynchronize(w->stream), "hipStreamSynchronize");
+    (void)hipFree(w->chain);
+    w->chain = nullptr;
+    w->chain_cap = 0;
+    SZ_HIP(hipMalloc(&w->chain, 8 * (uint64_t)cap), "hipMalloc(one-pass state)");
+    SZ_HIP(sz::launch_chain_clear(w->chain, cap, w->stream), "clear of the one-pass state");
+    w->chain_cap = cap;
+    return SPLITZIP_OK;
+}
+
+// The tag of the next one-pass launch on a state of cap status words, counted in *launches;
+// when the tag wraps to 0 the state is cleared first (on the stream, before that launch), so
+// that no status word is older than 2^23 launches.
+hipError_t chain_next_tag(uint64_t *launches, uint64_t *status, uint32_t cap, hipStream_t stream, uint32_t *tag)
+{
+    const uint64_t l = ++*launches;
+    *tag = (uint32_t)(l & sz::kChainTagMask);
+    return *tag == 0 ? sz::launch_chain_clear(status, cap, stream) : hipSuccess;
 }
 
 int ensure_result(Workspace *w, uint32_t n_seg)
@@ -1035,15 +1077,17 @@ void set_encode_args(sz::EncodeArgs &a, const splitzip_codec *codec, uint32_t n_
     a.multi_book = book < 0;
     a.cbs = codec->d_cbs;
     a.packed = packed;
-    a.seg_total = reinterpret_cast<uint64_t *>(base + lay.seg_total);
-    a.tile_count = reinterpret_cast<uint32_t *>(base + lay.tile_count);
-    a.tile_ovf = reinterpret_cast<uint64_t *>(base + lay.tile_ovf);
-    a.spill_rec = reinterpret_cast<sz::SpillRec *>(base + lay.spill_rec);
-    a.ovf_tiles = reinterpret_cast<uint32_t *>(base + lay.ovf_tiles);
-    a.slots = reinterpret_cast<uint32_t *>(base + lay.slots);
-    a.block_sum = reinterpret_cast<uint64_t *>(base + lay.block_sum);
-    a.group_sum = reinterpret_cast<uint64_t *>(base + lay.group_sum);
-    a.ovf = reinterpret_cast<uint32_t *>(base + lay.ovf);
+    if (base) {     // none for a one-pass encode
+        a.seg_total = reinterpret_cast<uint64_t *>(base + lay.seg_total);
+        a.tile_count = reinterpret_cast<uint32_t *>(base + lay.tile_count);
+        a.tile_ovf = reinterpret_cast<uint64_t *>(base + lay.tile_ovf);
+        a.spill_rec = reinterpret_cast<sz::SpillRec *>(base + lay.spill_rec);
+        a.ovf_tiles = reinterpret_cast<uint32_t *>(base + lay.ovf_tiles);
+        a.slots = reinterpret_cast<uint32_t *>(base + lay.slots);
+        a.block_sum = reinterpret_cast<uint64_t *>(base + lay.block_sum);
+        a.group_sum = reinterpret_cast<uint64_t *>(base + lay.group_sum);
+        a.ovf = reinterpret_cast<uint32_t *>(base + lay.ovf);
+    }
     a.ovf_ctr = ovf_ctr;
     a.ovf_cap = ovf_cap;
     a.err = reinterpret_cast<uint32_t *>(res);
@@ -1058,10 +1102,30 @@ void set_encode_args(sz::EncodeArgs &a, const splitzip_codec *codec, uint32_t n_
     a.stage = n_tiles > codec->stage_tiles.load(std::memory_order_relaxed) ? 1u : 0u;
 }
 
-// The encode launches: pack and finish for calls of at most small_tiles tiles, else pack,
-// sums, place and spill.  w (optional) times them when the codec is profiling.
+// Whether an encode of n_tiles tiles on `stream` runs in one pass (see
+// splitzip_set_onepass_tiles).  Not while the stream is being captured into a graph: a
+// launch's tag is a kernel argument, and every replay of a graph would repeat it.
+bool use_onepass(const splitzip_codec *codec, bool packed, uint64_t n_tiles, hipStream_t stream)
+{
+    if (packed || n_tiles > codec->onepass_tiles.load(std::memory_order_relaxed))
+        return false;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(stream, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone;
+}
+
+// The encode launches: the one-pass pack when a.chain_status is set; else pack and finish for
+// calls of at most small_tiles tiles, else pack, sums, place and spill.  w (optional) times
+// them when the codec is profiling.
 hipError_t run_encode_stages(splitzip_codec *codec, Workspace *w, const sz::EncodeArgs &a, hipStream_t stream)
 {
+    if (a.chain_status) {
+        static const int kOnePassKinds[] = {SPLITZIP_KERNEL_ONEPASS};
+        CallTimer timer(codec, w, stream, kOnePassKinds, 1);
+        timer.mark();
+        const hipError_t e = sz::launch_encode_stage(sz::kStageOnePass, a, stream);
+        timer.mark();
+        return e;
+    }
     static const int kSmallStages[] = {sz::kStagePack, sz::kStageFinish};
     static const int kSmallKinds[] = {SPLITZIP_KERNEL_PACK, SPLITZIP_KERNEL_FINISH};
     static const int kStages[] = {sz::kStagePack, sz::kStageSums, sz::kStagePlace, sz::kStageSpill};
@@ -1096,6 +1160,29 @@ int encode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
     Workspace *w = hold.get();
     const uint32_t n_tiles = tiles[n_seg];
     const uint32_t tile_shift = codec->elem == sz::kElemE5M2 ? sz::kE8EncTileShift : sz::kEncTileShift;
+    if (use_onepass(codec, packed, n_tiles, stream)) {
+        // no scratch: only the workspace's one-pass state
+        if ((rc = ensure_chain(w, n_tiles)) != SPLITZIP_OK)
+            return rc;
+        if (!d_result && (rc = ensure_result(w, n_seg)) != SPLITZIP_OK)
+            return rc;
+        sz::EncodeArgs a{};
+        a.seg0 = desc[0];
+        if (n_seg > 1 && (rc = stage_descriptors(w, desc, tiles, &a.segs, &a.tile_start, &a.seg_at)) != SPLITZIP_OK)
+            return rc;
+        uint8_t *res = d_result ? reinterpret_cast<uint8_t *>(d_result) : w->result;
+        set_encode_args(a, codec, n_seg, n_tiles, book, packed, nullptr, EncodeScratch(0, 0, 0, 0), nullptr, 0,
+                        false, res);
+        a.chain_status = w->chain;
+        a.chain_cap = w->chain_cap;
+        hipError_t e = chain_next_tag(&w->chain_launches, w->chain, w->chain_cap, stream, &a.chain_tag);
+        if (e == hipSuccess)
+            e = run_encode_stages(codec, w, a, stream);
+        if (e != hipSuccess)
+            return fail_hip(e, "encode launch");
+        *out_ws = w;
+        return SPLITZIP_OK;
+    }
     // every tile its own overflow region when those fit the limit; else one shared area as
     // large as the escape capacity, reserved from with an atomic counter
     const bool private_ovf = ((uint64_t)n_tiles << tile_shift) * 4 <=
@@ -1208,6 +1295,7 @@ int splitzip_encode_noalloc(splitzip_codec *codec, uint32_t n_seg, const splitzi
         // every segment checked, and the scratch the call needs, before anything is enqueued
         const uint64_t tile_words = tile_elements(codec, true);
         uint64_t n_tiles = 0, ovf_cap = 1;
+        bool cap_over = false;
         int64_t book = segs[0].book;
         sz::SegDesc d0{};
         for (uint32_t i = 0; i < n_seg; ++i) {
@@ -1219,22 +1307,27 @@ int splitzip_encode_noalloc(splitzip_codec *codec, uint32_t n_seg, const splitzi
             n_tiles += segment_tiles(segs[i].n, tile_words);
             if (n_tiles > 0xFFFFFFF0ull)
                 return fail(SPLITZIP_E_INVALID, "too many tiles in one call");
+            // (the overflow area of the launch sequences is as long as the capacities)
             if (segs[i].esc_capacity > SPLITZIP_NOALLOC_SCRATCH_BYTES ||
                 (ovf_cap += segs[i].esc_capacity) > SPLITZIP_NOALLOC_SCRATCH_BYTES)
-                return fail(SPLITZIP_E_INVALID, "escape capacities exceed the allocation-free scratch");
+                cap_over = true;
             if (segs[i].book != book)
                 book = -1;
         }
+        // a one-pass call needs no scratch besides its state at the end of the array
+        hipStream_t stream = static_cast<hipStream_t>(stream_);
+        const bool onepass = use_onepass(codec, false, n_tiles, stream) && n_tiles <= kNoAllocChainTiles;
+        if (cap_over && !onepass)
+            return fail(SPLITZIP_E_INVALID, "escape capacities exceed the allocation-free scratch");
         const auto up = [](uint64_t x) { return (x + 255) & ~uint64_t(255); };
         const uint64_t seg_table = n_seg > 1 ? 256 : 0;               // after the counter
         const uint64_t tile_table = up(seg_table + (n_seg > 1 ? sizeof(sz::SegDesc) * n_seg : 0));
         const uint64_t enc_base = up(
             std::max<uint64_t>(256, tile_table + (n_seg > 1 ? 4 * (n_seg + 2 + ((n_tiles + 63) >> 6)) : 0)));
         const EncodeScratch lay((uint32_t)n_tiles, ovf_cap, n_seg, slot_escapes(codec));
-        if (enc_base + lay.total > SPLITZIP_NOALLOC_SCRATCH_BYTES)
+        if (!onepass && enc_base + lay.total > kNoAllocScratchBytes)
             return fail(SPLITZIP_E_INVALID, "the call needs %llu bytes of scratch; the allocation-free encode has %llu",
-                        (unsigned long long)(enc_base + lay.total),
-                        (unsigned long long)SPLITZIP_NOALLOC_SCRATCH_BYTES);
+                        (unsigned long long)(enc_base + lay.total), (unsigned long long)kNoAllocScratchBytes);
 
         DeviceGuard dg(codec->device);
         if (dg.err != hipSuccess)
@@ -1250,7 +1343,6 @@ int splitzip_encode_noalloc(splitzip_codec *codec, uint32_t n_seg, const splitzi
             nd.base = static_cast<uint8_t *>(p);
         }
         uint8_t *base = nd.base;
-        hipStream_t stream = static_cast<hipStream_t>(stream_);
         unsigned long long *ctr = reinterpret_cast<unsigned long long *>(base);
         sz::SegDesc *d_segs = n_seg > 1 ? reinterpret_cast<sz::SegDesc *>(base + seg_table) : nullptr;
         uint32_t *d_tiles = n_seg > 1 ? reinterpret_cast<uint32_t *>(base + tile_table) : nullptr;
@@ -1289,8 +1381,17 @@ int splitzip_encode_noalloc(splitzip_codec *codec, uint32_t n_seg, const splitzi
         a.segs = d_segs;
         a.tile_start = d_tiles;
         a.seg_at = d_tiles ? d_tiles + n_seg + 1 : nullptr;
-        set_encode_args(a, codec, n_seg, (uint32_t)n_tiles, book, false, base + enc_base, lay, ctr, ovf_cap,
-                        false, reinterpret_cast<uint8_t *>(d_result));
+        if (onepass) {
+            set_encode_args(a, codec, n_seg, (uint32_t)n_tiles, book, false, nullptr, EncodeScratch(0, 0, 0, 0),
+                            nullptr, 0, false, reinterpret_cast<uint8_t *>(d_result));
+            a.chain_status = reinterpret_cast<uint64_t *>(base + kNoAllocScratchBytes);
+            a.chain_cap = kNoAllocChainTiles;
+            if (e == hipSuccess)
+                e = chain_next_tag(&nd.chain_launches, a.chain_status, a.chain_cap, stream, &a.chain_tag);
+        } else {
+            set_encode_args(a, codec, n_seg, (uint32_t)n_tiles, book, false, base + enc_base, lay, ctr, ovf_cap,
+                            false, reinterpret_cast<uint8_t *>(d_result));
+        }
         if (e == hipSuccess)
             e = run_encode_stages(codec, nullptr, a, stream);
         if (e != hipSuccess)
@@ -1474,6 +1575,42 @@ int splitzip_set_small_tiles(splitzip_codec *codec, uint32_t max_tiles)
         if (max_tiles > sz::kSmallTiles)
             return fail(SPLITZIP_E_INVALID, "max_tiles %u exceeds %u", max_tiles, sz::kSmallTiles);
         codec->small_tiles.store(max_tiles, std::memory_order_relaxed);
+        return SPLITZIP_OK;
+    });
+}
+
+int splitzip_set_onepass_launches(splitzip_codec *codec, void *stream, uint64_t launches)
+{
+    return guarded([&]() -> int {
+        g_last_error[0] = '\0';
+        int rc = codec_check(codec);
+        if (rc != SPLITZIP_OK)
+            return rc;
+        std::shared_ptr<Workspace> w;
+        {
+            std::lock_guard<std::mutex> lock(codec->mu);
+            auto it = codec->ws.find(static_cast<hipStream_t>(stream));
+            if (it != codec->ws.end())
+                w = it->second;
+        }
+        if (!w)
+            return fail(SPLITZIP_E_INVALID, "the codec has no workspace for this stream");
+        std::lock_guard<std::mutex> lock(w->mu);
+        if (!w->chain)
+            return fail(SPLITZIP_E_INVALID, "the workspace has no one-pass state");
+        w->chain_launches = launches;
+        return SPLITZIP_OK;
+    });
+}
+
+int splitzip_set_onepass_tiles(splitzip_codec *codec, uint32_t max_tiles)
+{
+    return guarded([&]() -> int {
+        g_last_error[0] = '\0';
+        int rc = codec_check(codec);
+        if (rc != SPLITZIP_OK)
+            return rc;
+        codec->onepass_tiles.store(max_tiles, std::memory_order_relaxed);
         return SPLITZIP_OK;
     });
 }

@@ -82,6 +82,33 @@ constexpr uint64_t kPrivateOvfBytes = 256ull << 20;
 // counts of its segment's earlier tiles itself (at most kSmallTiles - 1 loads, which the
 // workgroups of a call make T^2 / 2 of, from L2: a few microseconds at 4096 tiles).
 constexpr uint32_t kSmallTiles = 4096;
+// ---- one-pass encode (chained tiles) ----------------------------------------------------
+// In a one-pass encode the pack launch places every escape itself: tile t learns the escapes
+// of its segment's earlier tiles from their status words (a decoupled look-back over tiles in
+// launch order) and writes its escapes, chunk offsets and, as a segment's last tile, E to
+// their final places, with no scratch and no later launch.  Tile t's status word:
+//   bits 0..38  escape count: the tile's own (kChainAggregate) or the segment's escapes up to
+//               and including the tile (kChainPrefix)
+//   bits 39..40 kind: 0 = not written in this launch, kChainAggregate, kChainPrefix
+//   bits 41..63 tag: the launch's number modulo 2^23 (a kernel argument, counted by the host
+//               per state); a word with another tag is left from an earlier launch and reads
+//               as not written.  When the count wraps the host clears the state first, so no
+//               word can outlive 2^23 launches.
+// (A device-side launch counter, advanced by each launch's last workgroup, was measured:
+// the one atomic per workgroup on one address costs about 76 ns each, serialized, 20 ms
+// for 262144 tiles.)
+constexpr uint64_t kChainCountMask = (1ull << 39) - 1;
+constexpr uint32_t kChainKindShift = 39;
+constexpr uint32_t kChainTagShift = 41;
+constexpr uint64_t kChainTagMask = (1ull << 23) - 1;
+constexpr uint64_t kChainAggregate = 1;
+constexpr uint64_t kChainPrefix = 2;
+// a look-back poll that finds a predecessor not yet written sleeps and polls again, at most
+// this many times per tile (far longer than any tile takes) before it gives up, flags
+// kErrChainStall and goes on as if the rest had no escapes: a launch always ends
+constexpr uint32_t kChainSpinMax = 1u << 22;
+static_assert(kChainCountMask >= (1ull << 38), "a segment's escape count fits the status word");
+
 // overflow counter: escapes reserved so far (low 40 bits) and overflow tiles listed (high 24)
 constexpr int kOvfTileShift = 40;
 constexpr uint64_t kOvfOffsetMask = (1ull << kOvfTileShift) - 1;
@@ -97,6 +124,7 @@ constexpr uint32_t kErrBadOffsets = 2u;      // decode: chunk offsets out of ran
 constexpr uint32_t kErrBadPosition = 4u;     // decode: escape position outside its chunk
 constexpr uint32_t kErrOverflowArea = 8u;    // encode: overflow area too small
 constexpr uint32_t kErrBadHeader = 16u;      // decode: packed stream header does not match
+constexpr uint32_t kErrChainStall = 32u;     // one-pass encode: a look-back gave up waiting
 
 struct SegDesc {
     uint16_t *data;         // encode: input words; decode: output words (E5M2: bytes)
@@ -166,6 +194,11 @@ struct EncodeArgs {
     uint32_t slot_escapes;        // entries per tile slot
     uint32_t stage;               // pack: gather escape-heavy groups in LDS (the larger build)
     uint32_t private_ovf;         // each tile owns entries [t << tile_shift, +1 << tile_shift) of ovf
+    // one-pass encode: status words of chain_cap tiles (chain_cap >= n_tiles), and the
+    // launch's tag (see kChainTagShift)
+    uint64_t *chain_status;
+    uint32_t chain_cap;
+    uint32_t chain_tag;
 };
 
 struct DecodeArgs {
@@ -223,6 +256,8 @@ struct SetupArgs {
 };
 
 hipError_t launch_setup(const SetupArgs &a, hipStream_t stream);
+// Clears cap one-pass status words, with a kernel.
+hipError_t launch_chain_clear(uint64_t *status, uint32_t cap, hipStream_t stream);
 // The coarse segment table (see kSegAtShift) of n_seg segments with these device tile starts.
 hipError_t launch_seg_at(const uint32_t *tile_start, uint32_t n_seg, uint32_t n_tiles, uint32_t *seg_at,
                          hipStream_t stream);
@@ -231,7 +266,8 @@ uint32_t hist_blocks(uint64_t n);
 hipError_t launch_histogram(const HistArgs &a, hipStream_t stream);
 // Encode stages, launched in order on one stream: pack, sums, place, spill; or, for calls of
 // at most kSmallTiles tiles, pack and finish.
-enum EncodeStage { kStagePack = 0, kStageSums, kStagePlace, kStageSpill, kStageFinish };
+// kStageOnePass: the one-pass pack, alone (not for packed streams).
+enum EncodeStage { kStagePack = 0, kStageSums, kStagePlace, kStageSpill, kStageFinish, kStageOnePass };
 hipError_t launch_encode_stage(int stage, const EncodeArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 // E5M2 pack and decode (the other encode stages are shared with BF16).

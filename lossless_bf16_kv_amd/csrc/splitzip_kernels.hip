@@ -194,7 +194,8 @@ __device__ __forceinline__ uint32_t flags_keep(uint32_t nv)
 
 // ---- pack ---------------------------------------------------------------------------------
 
-template <bool kStage>
+// kChain: the one-pass build (chained tiles), which writes the escapes to their final places.
+template <bool kStage, bool kChain>
 __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs a)
 {
     __shared__ uint8_t s_lut[256];
@@ -213,8 +214,9 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
     const uint8_t *lut = a.multi_book ? a.lut + 256u * sd.book : a.lut;
     if (tid < 64)
         reinterpret_cast<uint32_t *>(s_lut)[tid] = reinterpret_cast<const uint32_t *>(lut)[tid];
-    if (a.packed && tid == 0 && t == segment_first_tile(a, s))
+    if (!kChain && a.packed && tid == 0 && t == segment_first_tile(a, s))
         a.seg_total[s] = 0;      // the sums launch adds the segment's escapes into it
+    const uint64_t tag = a.chain_tag;
     const uint64_t n = sd.n;
     const SZ_GLOBAL uint16_t *xw = as_global(sd.data);
     SZ_GLOBAL uint8_t *smb = as_global(sd.sm);
@@ -273,9 +275,25 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
     uint32_t wave_end;
     tile_escape_ranks<kEncGroups>(counts, lane, wave, s_wave_total, rank, tile_total, wave_end);
 
-    // where the tile's escapes go: its slot, or a range of the overflow area
-    uint64_t room;
-    uint32_t *dst = tile_escape_dest(a, t, tile_total, tid, &s_ovf, room);
+    // where the tile's escapes go: its slot, or a range of the overflow area; in the one-pass
+    // build their final places, after the escapes of the segment's earlier tiles (at most
+    // `room` of them, the escape capacity left).  A segment's last tile also writes E.
+    uint64_t room = 0, prefix = 0;
+    uint32_t *dst = nullptr;
+    SZ_GLOBAL uint16_t *fpos = nullptr;
+    SZ_GLOBAL uint8_t *fexp = nullptr;
+    if (kChain) {
+        prefix = chain_prefix(a, tag, t, segment_first_tile(a, s), tile_total, tid, lane, &s_ovf);
+        room = sd.esc > prefix && sd.esc_exp ? sd.esc - prefix : 0;
+        fpos = as_global(sd.esc_pos + (room ? prefix : 0));
+        fexp = as_global(sd.esc_exp + (room ? prefix : 0));
+        if (tid == 0 && t + 1 == segment_end_tile(a, s)) {
+            chunk_off[(n + cmask) >> a.log2_chunk] = prefix + tile_total;
+            a.seg_escapes[s] = prefix + tile_total;
+        }
+    } else {
+        dst = tile_escape_dest(a, t, tile_total, tid, &s_ovf, room);
+    }
 
     // escapes: (position inside the tile, exponent); tile-local chunk offsets.  A wave's
     // escapes of one group have consecutive ranks.  When there are more than kStageMin of
@@ -288,7 +306,7 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
     for (int j = 0; j < kEncGroups; ++j) {
         const uint32_t r0 = rank[j];
         if (g0[j] < n && (g0[j] & cmask) == 0)
-            chunk_off[g0[j] >> a.log2_chunk] = r0;
+            chunk_off[g0[j] >> a.log2_chunk] = prefix + r0;
         const uint32_t z = flags[j];
         const uint32_t w0 = __builtin_amdgcn_readfirstlane(r0);
         const uint32_t wcnt = (j + 1 < kEncGroups ? __builtin_amdgcn_readfirstlane(rank[j + 1]) : wave_end) - w0;
@@ -313,8 +331,14 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
                 uint32_t zz = z, r = r0;
                 do {
                     const uint32_t k = flag_bit_to_word((uint32_t)__builtin_ctz(zz));
-                    if (r < room)
-                        gdst[r] = (p0 + k) | ((uint32_t)(uint8_t)(ex8 >> (8 * k)) << 16);
+                    if (r < room) {
+                        if (kChain) {
+                            fpos[r] = (uint16_t)((g0[j] + k) & cmask);
+                            fexp[r] = (uint8_t)(ex8 >> (8 * k));
+                        } else {
+                            gdst[r] = (p0 + k) | ((uint32_t)(uint8_t)(ex8 >> (8 * k)) << 16);
+                        }
+                    }
                     ++r;
                     zz &= zz - 1;
                 } while (zz);
@@ -322,9 +346,17 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
         }
         if (staged) {
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-            for (uint32_t i = lane; i < wcnt; i += 64)
-                if (w0 + i < room)
-                    gdst[w0 + i] = stage[i];
+            for (uint32_t i = lane; i < wcnt; i += 64) {
+                if (w0 + i < room) {
+                    const uint32_t e = stage[i];
+                    if (kChain) {
+                        fpos[w0 + i] = (uint16_t)((base + (e & 0xFFFFu)) & cmask);
+                        fexp[w0 + i] = (uint8_t)(e >> 16);
+                    } else {
+                        gdst[w0 + i] = e;
+                    }
+                }
+            }
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         }
     }
@@ -941,6 +973,20 @@ __global__ __launch_bounds__(kThreads) void seg_at_kernel(const uint32_t *tile_s
     seg_at[g] = lo;
 }
 
+// Every status word of a one-pass state unwritten.
+__global__ __launch_bounds__(kThreads) void chain_clear_kernel(uint64_t *status, uint32_t cap)
+{
+    const uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i < cap)
+        status[i] = 0;
+}
+
+hipError_t launch_chain_clear(uint64_t *status, uint32_t cap, hipStream_t stream)
+{
+    chain_clear_kernel<<<cap / kThreads + 1, kThreads, 0, stream>>>(status, cap);
+    return hipGetLastError();
+}
+
 hipError_t launch_setup(const SetupArgs &a, hipStream_t stream)
 {
     if (a.count > kSetupSegs)
@@ -961,13 +1007,28 @@ hipError_t launch_encode_stage(int stage, const EncodeArgs &a, hipStream_t strea
 {
     switch (stage) {
     case kStagePack:
+        if (a.chain_status)
+            return hipErrorInvalidValue;
         if (a.elem == kElemE5M2)
             return launch_encode_pack_e5m2(a, stream);
         if (a.stage)
-            encode_pack_kernel<true><<<a.n_tiles, kThreads, a.n_tiles >= kPackCapTiles ? kPackLdsReserve : 0u,
-                                       stream>>>(a);
+            encode_pack_kernel<true, false><<<a.n_tiles, kThreads,
+                                              a.n_tiles >= kPackCapTiles ? kPackLdsReserve : 0u, stream>>>(a);
         else
-            encode_pack_kernel<false><<<a.n_tiles, kThreads, 0, stream>>>(a);
+            encode_pack_kernel<false, false><<<a.n_tiles, kThreads, 0, stream>>>(a);
+        break;
+    case kStageOnePass:
+        // tiles in launch order: workgroup t codes tile t, so every tile it waits for was
+        // started before it
+        if (a.packed || !a.chain_status || a.chain_cap < a.n_tiles || a.chain_tag > kChainTagMask)
+            return hipErrorInvalidValue;
+        if (a.elem == kElemE5M2)
+            return launch_encode_pack_e5m2(a, stream);
+        if (a.stage)
+            encode_pack_kernel<true, true><<<a.n_tiles, kThreads,
+                                             a.n_tiles >= kPackCapTiles ? kPackLdsReserve : 0u, stream>>>(a);
+        else
+            encode_pack_kernel<false, true><<<a.n_tiles, kThreads, 0, stream>>>(a);
         break;
     case kStageSums:
         encode_sums_kernel<<<(a.n_tiles + kSumTiles - 1) / kSumTiles, kThreads, 0, stream>>>(a);

@@ -270,6 +270,8 @@ int main(void)
     if (splitzip_release_stream(NULL, NULL) != SPLITZIP_E_INVALID) return 8;
     if (splitzip_workspace_bytes(NULL, NULL, &ws) != SPLITZIP_E_INVALID) return 9;
     if (splitzip_set_small_tiles(NULL, 0) != SPLITZIP_E_INVALID) return 10;
+    if (splitzip_set_onepass_tiles(NULL, SPLITZIP_ONEPASS_TILES) != SPLITZIP_E_INVALID) return 11;
+    if (splitzip_set_onepass_launches(NULL, NULL, 0) != SPLITZIP_E_INVALID) return 12;
     printf("ok\n");
     return 0;
 }
@@ -353,3 +355,22 @@ def test_read_header_fuzz():
         assert exact_stream_bytes(r["elem"], r["n"], r["chunk_size"], r["n_escapes"]) == length
 
     check()
+
+
+def test_python_constants_match_the_headers():
+    import re
+    text = open(os.path.join(ROOT, "include", "splitzip.h")).read() + \
+        open(os.path.join(ROOT, "include", "splitzip_tuning.h")).read()
+
+    def define(name):
+        m = re.search(r"#define\s+" + name + r"\s+\(?([0-9a-fx]+)(?:ull|u)?(?:\s*<<\s*(\d+))?\)?", text)
+        assert m, name
+        v = int(m.group(1), 0)
+        return v << int(m.group(2)) if m.group(2) else v
+    assert sz.SMALL_TILES == define("SPLITZIP_SMALL_TILES")
+    assert sz.STAGE_TILES == define("SPLITZIP_STAGE_TILES")
+    assert sz.ONEPASS_TILES == define("SPLITZIP_ONEPASS_TILES")
+    assert sz.PRIVATE_OVERFLOW_BYTES == define("SPLITZIP_PRIVATE_OVERFLOW_BYTES")
+    assert sz.NOALLOC_SCRATCH_BYTES == define("SPLITZIP_NOALLOC_SCRATCH_BYTES")
+    assert sz.NOALLOC_MAX_SEGMENTS == define("SPLITZIP_NOALLOC_MAX_SEGMENTS")
+    assert len(sz.KERNELS) == define("SPLITZIP_KERNELS")

@@ -26,6 +26,8 @@ def test_algorithmic_bytes_bf16():
     # place (and finish): counts, scratch escapes read and written as 3 B, offsets read and
     # written, E
     assert alg["encode_place"] == alg["encode_finish"] == 16 + 400 + 300 + 784 + 8
+    # the one-pass launch: exactly the encode's bytes
+    assert alg["encode_onepass"] == alg["encode"]
 
 
 def test_algorithmic_bytes_e5m2_and_batches():

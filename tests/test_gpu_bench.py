@@ -88,3 +88,11 @@ def test_ceiling_kernels():
                         torch.cuda.current_stream(DEV).cuda_stream) == 0
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_small_call_floor():
+    flushes = []
+    f = bench.floor_leg(DEV, 3 << 20, lambda: flushes.append(1), reps=3)
+    assert len(flushes) == 2 * 5
+    assert 0 < f["one_tile_launch_us"] < f["copy_input_us"] < 10_000
+    assert f["copy_bytes"] == 2 * (3 << 20)

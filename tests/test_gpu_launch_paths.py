@@ -1,14 +1,17 @@
-"""GPU parity of both encode launch sequences and both pack builds: calls of at most
-SMALL_TILES tiles run pack and finish (one workgroup per tile adds up the earlier tiles'
-escape counts itself), larger calls run pack, sums, place and spill; calls of more than
-STAGE_TILES tiles run the pack build in which a wave gathers a group's escapes in LDS when
-it has more than 64; escapes past a tile's slot go to the tile's own region or to a shared
-area reserved with a counter.  Each case is encoded four ways that cover every pair of these
-settings (``Codec.set_small_tiles``, ``Codec.set_stage_tiles``,
-``Codec.set_private_overflow``) and each must equal the oracle byte for byte: BF16 and E5M2
-streams spanning several tiles with ragged tails, tiles whose escapes overflow their
-slot, batches with empty and tiny segments and several codebooks, packed streams, too
-little escape room, and the 2048 / 2049-tile boundary of the default."""
+"""GPU parity of every encode launch sequence and both pack builds: calls into separate
+sections run one launch (each tile places its own escapes after a look-back over the
+earlier tiles' status words) up to ONEPASS_TILES tiles; other calls of at most SMALL_TILES
+tiles run pack and finish (one workgroup per tile adds up the earlier tiles' escape counts
+itself), larger calls run pack, sums, place and spill; calls of more than STAGE_TILES tiles
+run the pack build in which a wave gathers a group's escapes in LDS when it has more than
+64; escapes past a tile's slot go to the tile's own region or to a shared area reserved with
+a counter.  Each case is encoded six ways, which cover every pair of the launch settings
+(``Codec.set_small_tiles``, ``Codec.set_stage_tiles``, ``Codec.set_private_overflow``) with
+the one-pass launch off, and the one-pass launch with both pack builds; each must equal the
+oracle byte for byte: BF16 and E5M2 streams spanning several tiles with ragged tails, tiles
+whose escapes overflow their slot, batches with empty and tiny segments and several
+codebooks, packed streams, too little escape room, and the 4096 / 4097-tile boundary of the
+default."""
 from __future__ import annotations
 
 import numpy as np
@@ -26,17 +29,21 @@ pytestmark = pytest.mark.gpu
 O = oracle.get()
 NEVER = (1 << 32) - 1
 PRIV = sz.PRIVATE_OVERFLOW_BYTES
-# (set_small_tiles, set_stage_tiles, set_private_overflow): every pair of the three settings
-# appears with both of its values
-MODES = {"four_launches_shared": (0, NEVER, 0), "pack_finish_private": (sz.SMALL_TILES, NEVER, PRIV),
-         "four_launches_gather_private": (0, 0, PRIV), "pack_finish_gather_shared": (sz.SMALL_TILES, 0, 0)}
+# (set_small_tiles, set_stage_tiles, set_private_overflow, set_onepass_tiles): with the
+# one-pass launch off, every pair of the first three settings appears with both of its
+# values; the one-pass launch runs with both pack builds (packed streams, which it does not
+# take, then run pack + finish or the four launches)
+MODES = {"four_launches_shared": (0, NEVER, 0, 0), "pack_finish_private": (sz.SMALL_TILES, NEVER, PRIV, 0),
+         "four_launches_gather_private": (0, 0, PRIV, 0), "pack_finish_gather_shared": (sz.SMALL_TILES, 0, 0, 0),
+         "onepass": (0, NEVER, PRIV, NEVER), "onepass_gather": (sz.SMALL_TILES, 0, 0, NEVER)}
 
 
 def use_mode(codec, mode):
-    small, stage, private = MODES[mode]
+    small, stage, private, onepass = MODES[mode]
     codec.set_small_tiles(small)
     codec.set_stage_tiles(stage)
     codec.set_private_overflow(private)
+    codec.set_onepass_tiles(onepass)
 TILE = 16384          # BF16 words per pack tile
 TILE8 = 32768         # E5M2 bytes per pack tile
 
@@ -154,6 +161,7 @@ def test_default_boundary(tiles):
     n = (tiles - 1) * TILE + 1
     x = workloads.mixed_words(n, tiles, wide_fraction=0.01)
     codec = codec_for(workloads.normal_words(50_000, 9), 1024)
+    codec.set_onepass_tiles(0)
     codec.profile(True)
     enc = codec.encode(dev(x))
     times = codec.kernel_times()
@@ -169,6 +177,7 @@ def test_default_boundary(tiles):
 def test_launch_counts_and_limit():
     x = dev(workloads.normal_words(5 * TILE, 9))
     codec = codec_for(workloads.normal_words(30_000, 10), 1024)
+    codec.set_onepass_tiles(0)
     codec.profile(True)
     codec.encode(x)
     codec.set_small_tiles(0)
@@ -188,11 +197,12 @@ def test_launch_counts_and_limit():
 
 
 def test_setting_kept_across_calibrations():
-    """set_small_tiles before the first calibration, and every calibration makes a new C
-    codec: the setting applies to each."""
+    """set_small_tiles and set_onepass_tiles before the first calibration, and every
+    calibration makes a new C codec: the settings apply to each."""
     x = dev(workloads.normal_words(3 * TILE, 9))
     codec = sz.Codec(DEV, 1024)
     codec.set_small_tiles(0)
+    codec.set_onepass_tiles(0)
     codec.calibrate(dev(workloads.normal_words(30_000, 10)))
     codec.calibrate(dev(workloads.normal_words(30_000, 11)))
     codec.profile(True)
@@ -231,3 +241,83 @@ def test_many_tiny_segments(mode, elem):
         check(codec, e, x)
     for x, y in zip(xs_np, codec.decode_batch(encs)):
         assert np.array_equal(back(y), x)
+
+
+def test_onepass_launch_counts_and_limit():
+    """A call into sections of at most ONEPASS_TILES tiles is one launch (BF16 and E5M2); a
+    packed stream and a call over the limit run the launch sequences."""
+    x = dev(workloads.normal_words(5 * TILE, 9))
+    codec = codec_for(workloads.normal_words(30_000, 10), 1024)
+    codec.profile(True)
+    enc = codec.encode(x)
+    codec.set_onepass_tiles(5)
+    codec.encode(x)
+    codec.set_onepass_tiles(4)
+    codec.encode(x)
+    codec.set_onepass_tiles()
+    codec.encode_packed(x)
+    times = codec.kernel_times(reset=True)
+    codec.profile(False)
+    assert times["encode_onepass"][1] == 2
+    assert times["encode_pack"][1] == times["encode_finish"][1] == 2
+    assert times["encode_sums"][1] == 0
+    assert_same_stream(codec, enc, host(x, np.uint16))
+    c8 = t8.codec_for(workloads.e5m2_normal(50_000, 6), 1024)
+    c8.profile(True)
+    x8 = workloads.e5m2_normal(3 * TILE8, 7)
+    e8 = c8.encode(t8.dev8(x8))
+    c8.encode_packed(t8.dev8(x8))
+    t = c8.kernel_times()
+    assert t["encode_onepass"][1] == 1 and t["encode_pack"][1] == 1
+    t8.assert_same_stream(c8, e8, x8)
+
+
+@pytest.mark.parametrize("wide", [0.0, 0.02, 1.0])
+def test_onepass_many_tiles_and_repeats(wide):
+    """1100 tiles (more than one round of the GPU's workgroups, so look-backs find earlier
+    tiles still running) with few escapes, 2 % and (uniformly random words) about 94 %; the
+    same call three times in a row on one workspace, so every call reads status words that
+    the previous call left with the previous launch number."""
+    n = 1100 * TILE - 5
+    x = workloads.mixed_words(n, 77, wide_fraction=wide) if wide < 1.0 else workloads.random_words(n, 77)
+    codec = codec_for(workloads.normal_words(50_000, 9), 4096)
+    codec.set_stage_tiles(0)
+    xd = dev(x)
+    encs = [codec.encode(xd) for _ in range(3)]
+    for e in encs[1:]:
+        assert e.n_escapes == encs[0].n_escapes
+        for name in ("sm", "codes", "chunk_off", "esc_pos", "esc_exp"):
+            assert torch.equal(getattr(e, name), getattr(encs[0], name)), name
+    assert_same_stream(codec, encs[2], x)
+
+
+def test_onepass_e5m2_many_tiles():
+    """E5M2 in one pass over 700 tiles, with both pack builds, at 20 % escapes and C = 16
+    (chunks start inside a lane's group)."""
+    n = 700 * TILE8 - 3
+    x = workloads.e5m2_mixed(n, 55, wide_fraction=0.2)
+    for stage in (0, NEVER):
+        c8 = t8.codec_for(workloads.e5m2_normal(50_000, 6), 16)
+        c8.set_stage_tiles(stage)
+        c8.profile(True)
+        e8 = c8.encode(t8.dev8(x))
+        assert c8.kernel_times()["encode_onepass"][1] >= 1
+        t8.assert_same_stream(c8, e8, x)
+
+
+def test_onepass_tag_wrap():
+    """The launch tag is the low 23 bits of a count kept per workspace: at the wrap to 0 the
+    state is cleared before the launch, and the launches before, at and after the wrap (their
+    status words all written with other tags) each give the oracle's stream."""
+    x = workloads.mixed_words(300 * TILE + 7, 5, wide_fraction=0.05)
+    codec = codec_for(workloads.normal_words(50_000, 9), 1024)
+    xd = dev(x)
+    first = codec.encode(xd)
+    stream = torch.cuda.current_stream(DEV).cuda_stream
+    sz.splitzip_set_onepass_launches(codec.handle, stream, (1 << 23) - 2)
+    for _ in range(3):
+        e = codec.encode(xd)
+        assert e.to_bytes(codec) == first.to_bytes(codec)
+    assert_same_stream(codec, e, x)
+    with pytest.raises(sz.SplitZipError):
+        sz.splitzip_set_onepass_launches(codec.handle, torch.cuda.Stream(DEV).cuda_stream, 0)

@@ -385,13 +385,19 @@ def test_kernel_timing():
         codec.decode(codec.encode(x))
     times = codec.kernel_times(reset=True)
     assert set(times) == {"encode_pack", "encode_sums", "encode_place", "encode_spill", "decode",
-                          "encode_finish"}
-    # a call of 5 tiles runs pack + finish; the other encode kernels are not launched
+                          "encode_finish", "encode_onepass"}
+    # a BF16 call of 5 tiles runs the one-pass launch; the other encode kernels are not launched
     for k, (ms, count) in times.items():
-        if k in ("encode_pack", "encode_finish", "decode"):
+        if k in ("encode_onepass", "decode"):
             assert count == 3 and ms > 0, k
         else:
             assert count == 0, k
+    # without it, pack + finish
+    codec.set_onepass_tiles(0)
+    codec.encode(x)
+    times = codec.kernel_times(reset=True)
+    assert times["encode_pack"][1] == times["encode_finish"][1] == 1 and times["encode_onepass"][1] == 0
+    codec.set_onepass_tiles()
     assert all(c == 0 for _, c in codec.kernel_times().values())
     codec.profile(False)
     codec.decode(codec.encode(x))
@@ -541,7 +547,13 @@ def test_release_stream_frees_its_workspace():
     with torch.cuda.stream(s):
         enc = codec.encode(x)
     used = sz.splitzip_workspace_bytes(codec.handle, s.cuda_stream)
-    assert used >= (x_np.size // 16384) * 512            # at least the tiles' escape slots
+    assert used >= (x_np.size // 16384) * 8              # at least the tiles' one-pass status words
+    codec.set_onepass_tiles(0)
+    with torch.cuda.stream(s):
+        assert codec.encode(x).to_bytes(codec) == enc.to_bytes(codec)
+    used = sz.splitzip_workspace_bytes(codec.handle, s.cuda_stream)
+    assert used >= (x_np.size // 16384) * 512            # and the launch sequences' escape slots
+    codec.set_onepass_tiles()
     sz.splitzip_release_stream(codec.handle, s.cuda_stream)
     assert sz.splitzip_workspace_bytes(codec.handle, s.cuda_stream) == 0
     sz.splitzip_release_stream(codec.handle, s.cuda_stream)          # nothing left: a no-op

@@ -85,12 +85,15 @@ def bf16_codec(C=1024):
     return codec
 
 
-@pytest.mark.parametrize("small_tiles", [None, 0])
+@pytest.mark.parametrize("small_tiles", [None, 0, -1])
 def test_noalloc_matches_async_bf16(small_tiles):
-    """A ragged three-segment call, then a smaller one-segment call; pack + finish, and
-    (small_tiles 0) the four launches with their overflow counter."""
+    """A ragged three-segment call, then a smaller one-segment call; one pass (default),
+    pack + finish (None), and (small_tiles 0) the four launches with their overflow
+    counter."""
     codec = bf16_codec()
-    if small_tiles is not None:
+    if small_tiles != -1:
+        codec.set_onepass_tiles(0)
+    if small_tiles not in (None, -1):
         codec.set_small_tiles(small_tiles)
     xa = [workloads.mixed_words(5_000_003, 11), workloads.mixed_words(0, 12),
           workloads.mixed_words(1_234_567, 13)]
@@ -98,11 +101,15 @@ def test_noalloc_matches_async_bf16(small_tiles):
     run_pair(codec, (xa, xb), ([x.size // 8 + 64 for x in xa], [x.size // 8 + 64 for x in xb]))
 
 
-def test_noalloc_escape_heavy_and_many_segments():
+@pytest.mark.parametrize("onepass", [False, True])
+def test_noalloc_escape_heavy_and_many_segments(onepass):
     """About 30 % escapes (every tile past its slot, escapes reserved from the overflow
-    counter) over 61 segments (three set-up launches of descriptors), then 2 segments."""
+    counter; or, in one pass, placed by each tile) over 61 segments (three set-up launches
+    of descriptors), then 2 segments."""
     codec = bf16_codec(256)
     codec.set_small_tiles(0)
+    if not onepass:
+        codec.set_onepass_tiles(0)
     rng = np.random.default_rng(21)
     xa = [workloads.mixed_words(int(n), 100 + i, wide_fraction=0.3)
           for i, n in enumerate(rng.integers(0, 90_000, 61))]
@@ -121,7 +128,11 @@ def test_noalloc_e5m2():
 
 
 def test_noalloc_refuses_calls_over_its_scratch():
+    """The launch sequences' overflow area is as long as the escape capacity: a capacity
+    past the array is refused before any work.  The one-pass launch needs no overflow area
+    and takes the same call."""
     codec = bf16_codec()
+    codec.set_onepass_tiles(0)
     x = dev(workloads.normal_words(1 << 16, seed=5))
     # an escape capacity whose overflow area (4 bytes an entry) exceeds the fixed array;
     # the escape arrays are really that long, so nothing could be written out of bounds
@@ -144,3 +155,14 @@ def test_noalloc_refuses_calls_over_its_scratch():
     torch.cuda.synchronize()
     ok.n_escapes = int(res[1].item())
     stream_check.check_cases([stream_check.case_from_encoded("x", ok, x.cpu().numpy().view(np.uint16))])
+    # one pass: the same oversized capacity is fine
+    codec.set_onepass_tiles()
+    big = codec.empty_encoded(x.numel(), escape_capacity=cap)
+    segs[0] = big.segment(x.data_ptr())
+    res.zero_()
+    sz.splitzip_encode_noalloc(codec.handle, segs, torch.cuda.current_stream(DEV).cuda_stream, res.data_ptr())
+    torch.cuda.synchronize()
+    assert res[0].item() == 0
+    big.n_escapes = int(res[1].item())
+    assert big.n_escapes == ok.n_escapes
+    stream_check.check_cases([stream_check.case_from_encoded("x", big, x.cpu().numpy().view(np.uint16))])
