@@ -849,14 +849,61 @@ __global__ __launch_bounds__(kThreads) void encode_finish_kernel(const EncodeArg
     const uint32_t end = segment_end_tile(a, s);
     const uint32_t count = a.tile_count[t];
 
+    // The tile's escapes: from its slot, or, past the slot, from its range of the overflow
+    // area; this part's share of them.  An overflow tile holds thousands: sixteen loads in
+    // flight per thread, the first sixteen issued together with the loads of the earlier
+    // tiles' counts below (their stores need the sum of those).  (The spill launch's
+    // LDS-staged stores gained nothing here, and the larger code cost a cold call 0.8 us.)
+    constexpr int kOvfBatch = 16;
+    const uint32_t *src = a.slots + (uint64_t)t * a.slot_escapes;
+    uint64_t have = count;
+    if (count > a.slot_escapes) {
+        const uint64_t off = a.tile_ovf[t];
+        const uint64_t room = off < a.ovf_cap ? a.ovf_cap - off : 0;
+        src = a.ovf + off;
+        have = count < room ? count : room;
+    }
+    // (every load below is issued unconditionally, at an index clamped into its array, so
+    // that the compiler does not wait for each one before the next)
+    const SZ_GLOBAL uint32_t *gsrc = as_global(have ? src : a.slots);
+    const uint32_t share = (uint32_t)((have + (1u << pshift) - 1u) >> pshift);
+    const uint32_t r_begin = part * share;
+    const uint32_t r_end = (uint64_t)r_begin + share < have ? r_begin + share : (uint32_t)have;
+    const uint32_t r_last = r_end ? r_end - 1 : 0;
+
     // the escapes before this tile in its segment; a packed stream needs the segment's E
-    // as well (its exponents follow the E positions)
+    // as well (its exponents follow the E positions).  One round of 16-byte loads covers the
+    // counts of every tile of a finish call (at most kSmallTiles); a block of 4 counts past
+    // the array's end stays inside the scratch (each array is padded to 256 bytes).  They go
+    // out just before the escape loads, so that the sum waits only for them.
+    static_assert(kSmallTiles == 16 * kThreads, "one round of four 16-byte count loads per thread");
     const uint32_t stop = a.packed ? end : t;
+    const uint32_t blk0 = first >> 2, blk1 = (stop + 3) >> 2;
+    const SZ_GLOBAL u32x4 *cnt4 = as_global(reinterpret_cast<const u32x4 *>(a.tile_count));
+    u32x4 q[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t b = blk0 + tid + k * kThreads;
+        q[k] = cnt4[b < blk1 ? b : blk0];
+    }
+    uint32_t e[kOvfBatch];
+#pragma unroll
+    for (int k = 0; k < kOvfBatch; ++k) {
+        const uint32_t r = r_begin + tid + k * kThreads;
+        e[k] = gsrc[r < r_end ? r : r_last];
+    }
     uint64_t before = 0, all = 0;
-    for (uint32_t u = first + tid; u < stop; u += kThreads) {
-        const uint32_t c = a.tile_count[u];
-        before += u < t ? c : 0u;
-        all += c;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t b = blk0 + tid + k * kThreads;
+        const uint32_t c[4] = {q[k].x, q[k].y, q[k].z, q[k].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t u = 4 * b + i;
+            const bool in = b < blk1 && u >= first;
+            before += in && u < t ? c[i] : 0u;
+            all += in && u < stop ? c[i] : 0u;
+        }
     }
     const uint64_t prefix = block_total_u64(before, tid, lane, s_part);
     const uint64_t E = a.packed ? block_total_u64(all, tid, lane, s_part) : prefix + count;
@@ -891,42 +938,25 @@ __global__ __launch_bounds__(kThreads) void encode_finish_kernel(const EncodeArg
         }
     }
 
-    // the tile's escapes: from its slot, or, past the slot, from its range of the overflow area
-    const uint32_t *src = a.slots + (uint64_t)t * a.slot_escapes;
-    uint64_t lim = count;
-    if (count > a.slot_escapes) {
-        const uint64_t off = a.tile_ovf[t];
-        const uint64_t room = off < a.ovf_cap ? a.ovf_cap - off : 0;
-        src = a.ovf + off;
-        lim = count < room ? count : room;
-    }
+    // the escapes' final places: at most the escape capacity left is written
     uint8_t *exps = a.packed ? packed_exps(sd, E) : sd.esc_exp;
-    const uint64_t dlim = prefix < sd.esc ? sd.esc - prefix : 0;   // escape capacity left
-    if (lim > dlim)
-        lim = dlim;
-    if (!exps)
-        lim = 0;
+    const uint64_t dlim = prefix < sd.esc ? sd.esc - prefix : 0;
+    const uint64_t lim = exps ? (have < dlim ? have : dlim) : 0;
+    const uint32_t w_end = r_end < lim ? r_end : (uint32_t)lim;   // stores: ranks below this
     SZ_GLOBAL uint16_t *pos = as_global(lim ? sd.esc_pos + prefix : sd.esc_pos);
     SZ_GLOBAL uint8_t *ex = as_global(lim ? exps + prefix : exps);
-    // an overflow tile holds thousands of escapes: sixteen loads in flight per thread.  (The
-    // spill launch's LDS-staged stores gained nothing here: a small call's finish waits on its
-    // sum over the earlier tiles' counts, and the larger code cost a cold call 0.8 us.)
-    constexpr int kOvfBatch = 16;
-    const SZ_GLOBAL uint32_t *gsrc = as_global(src);
-    // this part's share of the tile's escapes
-    const uint32_t share = (uint32_t)((lim + (1u << pshift) - 1u) >> pshift);
-    const uint32_t r_begin = part * share;
-    const uint32_t r_end = (uint64_t)r_begin + share < lim ? r_begin + share : (uint32_t)lim;
-    for (uint32_t r0 = r_begin + tid; r0 < r_end; r0 += kOvfBatch * kThreads) {
-        uint32_t e[kOvfBatch];
+    for (uint32_t r0 = r_begin + tid; r0 < w_end; r0 += kOvfBatch * kThreads) {
+        if (r0 != r_begin + tid) {
 #pragma unroll
-        for (int k = 0; k < kOvfBatch; ++k)
-            if (r0 + k * kThreads < r_end)
-                e[k] = gsrc[r0 + k * kThreads];
+            for (int k = 0; k < kOvfBatch; ++k) {
+                const uint32_t r = r0 + k * kThreads;
+                e[k] = gsrc[r < r_end ? r : r_last];
+            }
+        }
 #pragma unroll
         for (int k = 0; k < kOvfBatch; ++k) {
             const uint32_t r = r0 + k * kThreads;
-            if (r < r_end) {
+            if (r < w_end) {
                 pos[r] = (uint16_t)((base + (e[k] & 0xFFFFu)) & cmask);
                 ex[r] = (uint8_t)(e[k] >> 16);
             }

@@ -92,7 +92,8 @@ def test_ceiling_kernels():
 
 def test_small_call_floor():
     flushes = []
-    f = bench.floor_leg(DEV, 3 << 20, lambda: flushes.append(1), reps=3)
+    f = bench.floor_leg(DEV, 64 << 20, lambda: flushes.append(1), reps=3)
     assert len(flushes) == 2 * 5
+    # a 16-byte launch against a copy of 64 MiB (reads and writes 128 MiB in all)
     assert 0 < f["one_tile_launch_us"] < f["copy_input_us"] < 10_000
-    assert f["copy_bytes"] == 2 * (3 << 20)
+    assert f["copy_bytes"] == 2 * (64 << 20)

@@ -321,3 +321,27 @@ def test_onepass_tag_wrap():
     assert_same_stream(codec, e, x)
     with pytest.raises(sz.SplitZipError):
         sz.splitzip_set_onepass_launches(codec.handle, torch.cuda.Stream(DEV).cuda_stream, 0)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("C", [16, 1024])
+def test_exact_escape_counts_per_tile(mode, C):
+    """Tiles with exactly 0, 127, 128, 129 (around the 128-entry slot), 1023, 1024, 1025, all
+    16384, 5000 and 1 escapes, then a partial tile with 2000, at random places: the stream
+    equals the oracle's in every launch sequence and build."""
+    rng = np.random.default_rng(8)
+    counts = [0, 127, 128, 129, 1023, 1024, 1025, TILE, 5000, 1]
+    n = len(counts) * TILE + 5000
+    # exponent 127 everywhere (inside any codebook of N(0,1) data), random sign and mantissa
+    x = (0x3F80 | rng.integers(0, 128, n) | (rng.integers(0, 2, n) << 15)).astype(np.uint16)
+    for t, k in enumerate(counts + [2000]):
+        size = min(TILE, n - t * TILE)
+        at = t * TILE + rng.choice(size, size=k, replace=False)
+        x[at] = (x[at] & 0x807F) | 0x7F00          # exponent 254: an escape
+    codec = codec_for(workloads.normal_words(50_000, 9), C)
+    assert 254 not in np.frombuffer(codec.codebook, np.uint8) and 127 in np.frombuffer(codec.codebook, np.uint8)
+    use_mode(codec, mode)
+    enc = codec.encode(dev(x))
+    assert enc.n_escapes == sum(counts) + 2000
+    assert_same_stream(codec, enc, x)
+    assert np.array_equal(host(codec.decode(enc), np.uint16), x)
