@@ -69,6 +69,16 @@ __device__ __forceinline__ uint32_t lane_id()
     return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
 }
 
+// A 64-bit value that is the same in every lane, as scalar registers.  (The builtin returns
+// int: each half goes through uint32_t, or the low half would be sign-extended into the high
+// one when the two are combined.)
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
 __device__ __forceinline__ uint32_t shfl_u32(uint32_t v, uint32_t src_lane)
 {
     return (uint32_t)__builtin_amdgcn_ds_bpermute((int)(src_lane << 2), (int)v);
@@ -288,8 +298,7 @@ __device__ __forceinline__ uint32_t *tile_escape_dest(const EncodeArgs &a, uint3
         __syncthreads();
         // the same in every lane: keep it in scalar registers
         const uint64_t v = *s_ovf;
-        const uint64_t off = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32)
-                           | __builtin_amdgcn_readfirstlane((uint32_t)v);
+        const uint64_t off = uniform_u64(v);
         dst = a.ovf + off;
         room = off < a.ovf_cap ? a.ovf_cap - off : 0;
     }
@@ -374,8 +383,7 @@ __device__ __forceinline__ uint64_t chain_prefix(const EncodeArgs &a, uint64_t t
     }
     __syncthreads();
     const uint64_t v = *s_prefix;
-    return ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
-           __builtin_amdgcn_readfirstlane((uint32_t)v);
+    return uniform_u64(v);
 }
 
 }  // namespace sz

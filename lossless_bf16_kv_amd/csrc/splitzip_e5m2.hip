@@ -478,29 +478,41 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
         }
         __syncthreads();
         uint8_t *bytes = reinterpret_cast<uint8_t *>(s_exp);
+        uint32_t bad = 0;               // error bits this thread found
         // the tile's escapes are the contiguous range [j0, j1), kPatch per thread and round;
-        // every load of a round goes out before its LDS writes (global pointers: the loads
-        // cannot alias LDS, so nothing holds them back)
+        // every load of a round goes out before its LDS writes, at an index clamped into the
+        // range (global pointers: the loads cannot alias LDS, so nothing holds them back)
         constexpr int kPatch = kLarge ? 8 : 4;
         const SZ_GLOBAL uint16_t *gpos = as_global(static_cast<const uint16_t *>(sd.esc_pos));
         const SZ_GLOBAL uint8_t *gexp = as_global(static_cast<const uint8_t *>(sd.esc_exp));
         if (!sub_chunk) {
             for (uint64_t ci = tid; ci < nc; ci += kThreads) {
                 const uint64_t cs = (c0 + ci) << log2c;
-                if ((s_off[ci] > s_off[ci + 1] || s_off[ci + 1] - s_off[ci] > (n - cs < C ? n - cs : C)) && a.err)
-                    atomicOr(a.err, kErrBadOffsets);
+                if (s_off[ci] > s_off[ci + 1] || s_off[ci + 1] - s_off[ci] > (n - cs < C ? n - cs : C))
+                    bad |= kErrBadOffsets;
             }
             // chunk of escape jj: the last c with s_off[c] <= jj.  In the large-call build a
-            // tile of at most kFew chunks (chunk size 1024 or more) keeps the tile-relative
-            // offsets in scalar registers, and each escape counts those at or below it; a
-            // binary search in LDS costs three or more dependent LDS reads per escape.
+            // tile of at most kFew chunks (chunk size 1024 or more) counts the tile-relative
+            // chunk starts at or below each escape's rank: the starts of chunks 1..kFew, two
+            // per dword (absent ones 0x7FFF), are subtracted from the rank with packed 16-bit
+            // subtractions (ranks and starts are below 2^14, so a half's sign bit says rank <
+            // start), and the sign bits are counted.  Otherwise a binary search in LDS
+            // (three or more dependent LDS reads per escape).
             constexpr int kFew = 16;
             const bool few = kLarge && nc <= (uint64_t)kFew;       // uniform
-            uint32_t rel[kFew];
+            static_assert(kTile < (1 << 15), "tile ranks fit a signed 16-bit half");
+            uint32_t starts[kFew / 2];
 #pragma unroll
-            for (int c = 0; c < kFew; ++c)
-                rel[c] = (few && c >= 1 && (uint64_t)c < nc) ? __builtin_amdgcn_readfirstlane((uint32_t)(s_off[c] - j0))
-                                                      : 0xFFFFFFFFu;
+            for (int m = 0; m < kFew / 2; ++m) {
+                uint32_t h[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int c = 2 * m + 1 + i;
+                    h[i] = (few && (uint64_t)c < nc) ? (uint32_t)(s_off[c] - j0) : 0x7FFFu;
+                    h[i] = h[i] < 0x7FFFu ? h[i] : 0x7FFFu;
+                }
+                starts[m] = __builtin_amdgcn_readfirstlane(h[0] | (h[1] << 16));
+            }
             // 32-bit arithmetic relative to the tile: escape rank r in [0, cnt), chunk starts
             // lo << log2c inside the tile (a chunk is at most a tile here), cnt <= valid
             const uint32_t cnt = (uint32_t)(j1 - j0);
@@ -512,10 +524,9 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
 #pragma unroll
                 for (int k = 0; k < kPatch; ++k) {
                     const uint32_t r = rb + (uint32_t)k * kThreads;
-                    if (r < cnt) {
-                        pos[k] = tpos[r];
-                        ev[k] = texp[r];
-                    }
+                    const uint32_t rc = r < cnt ? r : cnt - 1;
+                    pos[k] = tpos[rc];
+                    ev[k] = texp[rc];
                 }
 #pragma unroll
                 for (int k = 0; k < kPatch; ++k) {
@@ -524,9 +535,16 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
                         continue;
                     uint32_t lo = 0;
                     if (few) {
+                        typedef short s16x2 __attribute__((ext_vector_type(2)));
+                        const s16x2 rr = {(short)r, (short)r};
+                        uint32_t below = 0;             // chunk starts above r
 #pragma unroll
-                        for (int c = 1; c < kFew; ++c)
-                            lo += r >= rel[c] ? 1u : 0u;
+                        for (int m = 0; m < kFew / 2; ++m) {
+                            const s16x2 st = __builtin_bit_cast(s16x2, starts[m]);
+                            const uint32_t d = __builtin_bit_cast(uint32_t, (s16x2)(rr - st));
+                            below += (uint32_t)__popc(d & 0x80008000u);
+                        }
+                        lo = kFew - below;              // halves hold chunks 1 .. kFew
                         lo = lo < (uint32_t)nc ? lo : (uint32_t)nc - 1u;
                     } else {
                         const uint64_t jj = j0 + r;
@@ -541,12 +559,10 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
                     }
                     const uint32_t cs = lo << log2c;
                     const uint32_t clen = tvalid - cs < (uint32_t)C ? tvalid - cs : (uint32_t)C;
-                    if (pos[k] >= clen || ev[k] > 31u) {
-                        if (a.err)
-                            atomicOr(a.err, pos[k] >= clen ? kErrBadPosition : kErrBadExponent);
-                        continue;
-                    }
-                    bytes[cs + pos[k]] = (uint8_t)(ev[k] << 2);
+                    if (pos[k] < clen && ev[k] <= 31u)
+                        bytes[cs + pos[k]] = (uint8_t)(ev[k] << 2);
+                    else
+                        bad |= pos[k] >= clen ? kErrBadPosition : kErrBadExponent;
                 }
             }
         } else {
@@ -557,25 +573,23 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
 #pragma unroll
                 for (int k = 0; k < kPatch; ++k) {
                     const uint64_t jj = jb + (uint64_t)k * kThreads;
-                    if (jj < j1) {
-                        pos[k] = gpos[jj];
-                        ev[k] = gexp[jj];
-                    }
+                    const uint64_t jc = jj < j1 ? jj : j1 - 1;
+                    pos[k] = gpos[jc];
+                    ev[k] = gexp[jc];
                 }
 #pragma unroll
                 for (int k = 0; k < kPatch; ++k) {
                     if (jb + (uint64_t)k * kThreads >= j1)
                         continue;
-                    if (pos[k] >= clen || ev[k] > 31u) {
-                        if (a.err)
-                            atomicOr(a.err, pos[k] >= clen ? kErrBadPosition : kErrBadExponent);
-                        continue;
-                    }
-                    if (pos[k] >= lo && pos[k] < lo + valid)
+                    if (pos[k] >= clen || ev[k] > 31u)
+                        bad |= pos[k] >= clen ? kErrBadPosition : kErrBadExponent;
+                    else if (pos[k] >= lo && pos[k] < lo + valid)
                         bytes[pos[k] - lo] = (uint8_t)(ev[k] << 2);
                 }
             }
         }
+        if (bad && a.err)
+            atomicOr(a.err, bad);
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < G; ++j) {

@@ -22,8 +22,12 @@ constexpr int kDecTileShift = 13;
 constexpr int kDecTileWords = 1 << kDecTileShift;
 static_assert(kThreads * kEncGroups * kGroupWords == kEncTileWords, "encode tile geometry");
 static_assert(kThreads * kDecGroups * kGroupWords == kDecTileWords, "decode tile geometry");
-// Extra LDS reserved per decode workgroup to hold occupancy at 5 workgroups per CU.
+// Extra LDS reserved per decode workgroup of calls of at least kDecodeCapTiles tiles, to hold
+// occupancy at 5 workgroups per CU: on inputs of GBs that streams faster than the 6 that
+// registers allow (less contention for HBM); smaller calls run uncapped (an escape-heavy
+// 64 M-word input decodes 3 % faster at 6 than at 5).
 constexpr unsigned kDecodeLdsReserve = 16384;
+constexpr uint32_t kDecodeCapTiles = 65536;
 // The same for the pack kernels of calls of at least kPackCapTiles tiles: 4 BF16 workgroups
 // per CU (registers allow 5) and 5 E5M2 workgroups (registers and LDS allow 6) stream 2 % and
 // 2.5 % faster on inputs of GBs (fewer concurrent tiles, each a long run of reads and writes);

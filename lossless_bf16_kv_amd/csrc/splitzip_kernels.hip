@@ -1181,14 +1181,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
 
     // ---- escape range of the tile --------------------------------------------------------
     const bool sub_chunk = log2c > (uint32_t)kDecTileShift;     // the tile lies inside one chunk
-    uint64_t c0, nc;
-    if (!sub_chunk) {
-        c0 = base >> log2c;
-        nc = (valid + C - 1) >> log2c;                       // chunks of this tile
-    } else {
-        c0 = base >> log2c;
-        nc = 1;
-    }
+    const uint64_t c0 = base >> log2c;
+    const uint64_t nc = sub_chunk ? 1 : (valid + C - 1) >> log2c;   // chunks of this tile
     for (uint32_t i = tid; i <= nc; i += kThreads)
         s_off[i] = sd.chunk_off[c0 + i];
     __syncthreads();
@@ -1232,18 +1226,23 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
     }
 
     // ---- a6: sparse escape correction (exponent bytes in LDS) ----------------------------
+    // A tile with escapes keeps its exponent bytes in LDS in word order (byte p: word p): each
+    // group's two dwords in code order (even words, odd words) become two dwords in word
+    // order by two byte permutes, so that an escape's byte is at its word's index.
+    uint32_t asel[4] = {0x0C040C00u, 0x0C050C01u, 0x0C060C02u, 0x0C070C03u};   // code order
     if (patch) {
 #pragma unroll
         for (int j = 0; j < kDecGroups; ++j) {
             const uint32_t q = ((wave * kDecGroups + j) << 6) + lane;
-            s_exp[2 * q] = ex_even[j];
-            s_exp[2 * q + 1] = ex_odd[j];
+            s_exp[2 * q] = perm(ex_odd[j], ex_even[j], 0x05010400u);
+            s_exp[2 * q + 1] = perm(ex_odd[j], ex_even[j], 0x07030602u);
         }
         __syncthreads();
         uint8_t *bytes = reinterpret_cast<uint8_t *>(s_exp);
+        uint32_t bad = 0;               // error bits this thread found
         // the tile's escapes are the contiguous range [j0, j1), kPatch per thread and round;
-        // every load of a round goes out before its LDS writes (global pointers: the loads
-        // cannot alias LDS, so nothing holds them back)
+        // every load of a round goes out before its LDS writes, at an index clamped into the
+        // range (global pointers: the loads cannot alias LDS, so nothing holds them back)
         constexpr int kPatch = kLarge ? 8 : 4;
         const SZ_GLOBAL uint16_t *gpos = as_global(static_cast<const uint16_t *>(sd.esc_pos));
         const SZ_GLOBAL uint8_t *gexp = as_global(static_cast<const uint8_t *>(sd.esc_exp));
@@ -1251,20 +1250,31 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
             // escape jj belongs to the last chunk ci whose offset s_off[ci] <= jj
             for (uint64_t ci = tid; ci < nc; ci += kThreads) {
                 const uint64_t cs = (c0 + ci) << log2c;
-                if ((s_off[ci] > s_off[ci + 1] || s_off[ci + 1] - s_off[ci] > (n - cs < C ? n - cs : C)) && a.err)
-                    atomicOr(a.err, kErrBadOffsets);
+                if (s_off[ci] > s_off[ci + 1] || s_off[ci + 1] - s_off[ci] > (n - cs < C ? n - cs : C))
+                    bad |= kErrBadOffsets;
             }
             // chunk of escape jj: the last c with s_off[c] <= jj.  In the large-call build a
-            // tile of at most kFew chunks (chunk size 1024 or more) keeps the tile-relative
-            // offsets in scalar registers, and each escape counts those at or below it; a
-            // binary search in LDS costs three or more dependent LDS reads per escape.
+            // tile of at most kFew chunks (chunk size 1024 or more) counts the tile-relative
+            // chunk starts at or below each escape's rank: the starts of chunks 1..kFew, two
+            // per dword (absent ones 0x7FFF), are subtracted from the rank with packed 16-bit
+            // subtractions (ranks and starts are below 2^13, so a half's sign bit says rank <
+            // start), and the sign bits are counted.  Otherwise a binary search in LDS
+            // (three or more dependent LDS reads per escape).
             constexpr int kFew = 8;
             const bool few = kLarge && nc <= (uint64_t)kFew;       // uniform
-            uint32_t rel[kFew];
+            static_assert(kDecTileWords < (1 << 15), "tile ranks fit a signed 16-bit half");
+            uint32_t starts[kFew / 2];
 #pragma unroll
-            for (int c = 0; c < kFew; ++c)
-                rel[c] = (few && c >= 1 && (uint64_t)c < nc) ? __builtin_amdgcn_readfirstlane((uint32_t)(s_off[c] - j0))
-                                                      : 0xFFFFFFFFu;
+            for (int m = 0; m < kFew / 2; ++m) {
+                uint32_t h[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int c = 2 * m + 1 + i;
+                    h[i] = (few && (uint64_t)c < nc) ? (uint32_t)(s_off[c] - j0) : 0x7FFFu;
+                    h[i] = h[i] < 0x7FFFu ? h[i] : 0x7FFFu;
+                }
+                starts[m] = __builtin_amdgcn_readfirstlane(h[0] | (h[1] << 16));
+            }
             // 32-bit arithmetic relative to the tile: escape rank r in [0, cnt), chunk starts
             // lo << log2c inside the tile (a chunk is at most a tile here), cnt <= valid
             const uint32_t cnt = (uint32_t)(j1 - j0);
@@ -1276,10 +1286,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
 #pragma unroll
                 for (int k = 0; k < kPatch; ++k) {
                     const uint32_t r = rb + (uint32_t)k * kThreads;
-                    if (r < cnt) {
-                        pos[k] = tpos[r];
-                        ev[k] = texp[r];
-                    }
+                    const uint32_t rc = r < cnt ? r : cnt - 1;
+                    pos[k] = tpos[rc];
+                    ev[k] = texp[rc];
                 }
 #pragma unroll
                 for (int k = 0; k < kPatch; ++k) {
@@ -1288,9 +1297,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
                         continue;
                     uint32_t lo = 0;
                     if (few) {
+                        typedef short s16x2 __attribute__((ext_vector_type(2)));
+                        const s16x2 rr = {(short)r, (short)r};
+                        uint32_t below = 0;             // chunk starts above r
 #pragma unroll
-                        for (int c = 1; c < kFew; ++c)
-                            lo += r >= rel[c] ? 1u : 0u;
+                        for (int m = 0; m < kFew / 2; ++m) {
+                            const s16x2 st = __builtin_bit_cast(s16x2, starts[m]);
+                            const uint32_t d = __builtin_bit_cast(uint32_t, (s16x2)(rr - st));
+                            below += (uint32_t)__popc(d & 0x80008000u);
+                        }
+                        lo = kFew - below;              // halves hold chunks 1 .. kFew
                         lo = lo < (uint32_t)nc ? lo : (uint32_t)nc - 1u;
                     } else {
                         const uint64_t jj = j0 + r;
@@ -1305,13 +1321,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
                     }
                     const uint32_t cs = lo << log2c;
                     const uint32_t clen = tvalid - cs < (uint32_t)C ? tvalid - cs : (uint32_t)C;
-                    if (pos[k] >= clen) {
-                        if (a.err)
-                            atomicOr(a.err, kErrBadPosition);
-                        continue;
-                    }
-                    const uint32_t p = cs + pos[k];
-                    bytes[(p >> 3) * 8 + (p & 1u) * 4 + ((p >> 1) & 3u)] = (uint8_t)ev[k];
+                    if (pos[k] < clen)
+                        bytes[cs + pos[k]] = (uint8_t)ev[k];
+                    else
+                        bad |= kErrBadPosition;
                 }
             }
         } else {
@@ -1322,34 +1335,34 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
 #pragma unroll
                 for (int k = 0; k < kPatch; ++k) {
                     const uint64_t jj = jb + (uint64_t)k * kThreads;
-                    if (jj < j1) {
-                        pos[k] = gpos[jj];
-                        ev[k] = gexp[jj];
-                    }
+                    const uint64_t jc = jj < j1 ? jj : j1 - 1;
+                    pos[k] = gpos[jc];
+                    ev[k] = gexp[jc];
                 }
 #pragma unroll
                 for (int k = 0; k < kPatch; ++k) {
                     if (jb + (uint64_t)k * kThreads >= j1)
                         continue;
-                    if (pos[k] >= clen) {
-                        if (a.err)
-                            atomicOr(a.err, kErrBadPosition);
-                        continue;
-                    }
-                    if (pos[k] >= lo && pos[k] < lo + valid) {
-                        const uint32_t p = (uint32_t)(pos[k] - lo);
-                        bytes[(p >> 3) * 8 + (p & 1u) * 4 + ((p >> 1) & 3u)] = (uint8_t)ev[k];
-                    }
+                    if (pos[k] >= clen)
+                        bad |= kErrBadPosition;
+                    else if (pos[k] >= lo && pos[k] < lo + valid)
+                        bytes[pos[k] - lo] = (uint8_t)ev[k];
                 }
             }
         }
+        if (bad && a.err)
+            atomicOr(a.err, bad);
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < kDecGroups; ++j) {
             const uint32_t q = ((wave * kDecGroups + j) << 6) + lane;
-            ex_even[j] = s_exp[2 * q];
-            ex_odd[j] = s_exp[2 * q + 1];
+            ex_even[j] = s_exp[2 * q];              // words 8 q .. 8 q + 3
+            ex_odd[j] = s_exp[2 * q + 1];           // words 8 q + 4 .. 8 q + 7
         }
+        asel[0] = 0x0C010C00u;
+        asel[1] = 0x0C030C02u;
+        asel[2] = 0x0C050C04u;
+        asel[3] = 0x0C070C06u;
     }
 
     // ---- assemble and store ------------------------------------------------------------------
@@ -1357,10 +1370,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
     for (int j = 0; j < kDecGroups; ++j) {
         const uint64_t g0 = base + (uint64_t)(((wave * kDecGroups + j) << 6) + lane) * kGroupWords;
         uint4 o;
-        o.x = assemble(smv[j].x, 0x01010000u, ex_even[j], ex_odd[j], 0x0C040C00u);
-        o.y = assemble(smv[j].x, 0x03030202u, ex_even[j], ex_odd[j], 0x0C050C01u);
-        o.z = assemble(smv[j].y, 0x01010000u, ex_even[j], ex_odd[j], 0x0C060C02u);
-        o.w = assemble(smv[j].y, 0x03030202u, ex_even[j], ex_odd[j], 0x0C070C03u);
+        o.x = assemble(smv[j].x, 0x01010000u, ex_even[j], ex_odd[j], asel[0]);
+        o.y = assemble(smv[j].x, 0x03030202u, ex_even[j], ex_odd[j], asel[1]);
+        o.z = assemble(smv[j].y, 0x01010000u, ex_even[j], ex_odd[j], asel[2]);
+        o.w = assemble(smv[j].y, 0x03030202u, ex_even[j], ex_odd[j], asel[3]);
         if (g0 + kGroupWords <= n) {
             store_stream16(sd.data + g0, o.x, o.y, o.z, o.w);
         } else {
@@ -1375,12 +1388,13 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream)
 {
     if (a.elem == kElemE5M2)
         return launch_decode_e5m2(a, stream);
-    // The dynamic LDS reservation is unused: it caps decode at 5 workgroups per CU, which
-    // streams about 3 % faster than the 8 that registers would allow (less contention for HBM).
+    // The dynamic LDS reservation is unused: on large calls it caps decode at 5 workgroups per
+    // CU (see kDecodeLdsReserve).
+    const unsigned lds = a.n_tiles >= kDecodeCapTiles ? kDecodeLdsReserve : 0u;
     if (a.large)
-        decode_kernel<true><<<xcd_grid(a.n_tiles), kThreads, kDecodeLdsReserve, stream>>>(a);
+        decode_kernel<true><<<xcd_grid(a.n_tiles), kThreads, lds, stream>>>(a);
     else
-        decode_kernel<false><<<xcd_grid(a.n_tiles), kThreads, kDecodeLdsReserve, stream>>>(a);
+        decode_kernel<false><<<xcd_grid(a.n_tiles), kThreads, lds, stream>>>(a);
     return hipGetLastError();
 }
 
