@@ -208,14 +208,22 @@ __device__ __forceinline__ uint32_t tile_segment(const EncodeArgs &a, uint32_t t
     return a.n_seg > 1 ? find_segment(a.tile_start, a.seg_at, t) : 0u;
 }
 
+// A word of a table no kernel writes while it runs, read through the scalar data cache (a
+// load from the constant address space): the wait for it is not a wait for this wave's
+// vector memory operations.
+__device__ __forceinline__ uint32_t load_const_u32(const uint32_t *p, uint32_t i)
+{
+    return ((const __attribute__((address_space(4))) uint32_t *)p)[i];
+}
+
 __device__ __forceinline__ uint32_t segment_first_tile(const EncodeArgs &a, uint32_t s)
 {
-    return a.n_seg > 1 ? a.tile_start[s] : 0u;
+    return a.n_seg > 1 ? load_const_u32(a.tile_start, s) : 0u;
 }
 
 __device__ __forceinline__ uint32_t segment_end_tile(const EncodeArgs &a, uint32_t s)
 {
-    return a.n_seg > 1 ? a.tile_start[s + 1] : a.n_tiles;
+    return a.n_seg > 1 ? load_const_u32(a.tile_start, s + 1) : a.n_tiles;
 }
 
 __device__ __forceinline__ SegDesc segment_desc(const EncodeArgs &a, uint32_t s)
@@ -307,6 +315,45 @@ __device__ __forceinline__ uint32_t *tile_escape_dest(const EncodeArgs &a, uint3
     return dst;
 }
 
+// ---- one-pass encode: copies from the LDS stash to the final arrays -----------------------
+
+// Four dwords of LDS starting at byte offset o (any alignment): five aligned dword loads,
+// realigned by byte funnel shifts.
+__device__ __forceinline__ u32x4 lds_load16_unaligned(const uint8_t *lds, uint32_t o)
+{
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(lds + (o & ~3u));
+    const uint32_t m = o & 3u;
+    const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3], w4 = w[4];
+    const u32x4 r = {__builtin_amdgcn_alignbyte(w1, w0, m), __builtin_amdgcn_alignbyte(w2, w1, m),
+                     __builtin_amdgcn_alignbyte(w3, w2, m), __builtin_amdgcn_alignbyte(w4, w3, m)};
+    return r;
+}
+
+// dst[0, ne) = src[0, ne) for elements of kBytes (1 or 2) bytes, src in LDS, by one wave: the
+// destination is cut at its 16-byte boundaries; each lane stores whole 16-byte pieces, and
+// the elements before the first boundary and after the last are stored one per lane.  dst
+// must be kBytes-aligned; the LDS from 16 bytes before src to 19 bytes past its end is read
+// (and those bytes not stored).
+template <int kBytes, typename T>
+__device__ __forceinline__ void stash_copy(SZ_GLOBAL T *dst, const T *src, uint32_t ne, uint32_t lane)
+{
+    constexpr uint32_t kPer = 16 / kBytes;
+    const uint32_t lead = (uint32_t)(reinterpret_cast<uintptr_t>(dst) & 15u) / kBytes;
+    const uint32_t head = lead ? (kPer - lead < ne ? kPer - lead : ne) : 0u;   // before the first boundary
+    const uint32_t full = (ne - head) / kPer;
+    const uint32_t tail_at = head + full * kPer;
+    const uint8_t *sb = reinterpret_cast<const uint8_t *>(src) - 16;
+#pragma unroll 2
+    for (uint32_t j = lane; j < full; j += 64) {
+        const uint32_t i0 = head + j * kPer;
+        *reinterpret_cast<SZ_GLOBAL u32x4 *>(dst + i0) = lds_load16_unaligned(sb, 16 + i0 * kBytes);
+    }
+    if (lane < head)
+        dst[lane] = src[lane];
+    if (lane < ne - tail_at)
+        dst[tail_at + lane] = src[tail_at + lane];
+}
+
 // ---- one-pass encode: the look-back over the status words of earlier tiles -------------
 
 __device__ __forceinline__ uint64_t chain_word(uint64_t tag, uint64_t kind, uint64_t count)
@@ -316,19 +363,93 @@ __device__ __forceinline__ uint64_t chain_word(uint64_t tag, uint64_t kind, uint
 
 __device__ __forceinline__ void chain_publish(const EncodeArgs &a, uint32_t t, uint64_t word)
 {
-    __hip_atomic_store(a.chain_status + t, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.chain_status + (uint64_t)t * kChainStride, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Escapes of the segment's tiles before tile t (first: the segment's first tile), by a
-// decoupled look-back.  Tile t first publishes its own count (as the segment's running total
-// if it is the first tile); wave 0 then reads the status words of the 64 tiles below the
-// highest one not yet counted, one per lane: tiles up to and including the nearest one that
-// holds a running total must all be written (else the wave sleeps and reads them again), and
-// their counts give the result; when none of the 64 holds a running total their 64 counts
-// are added and the next 64 tiles are read.  Tiles before `first` read as a running total of
-// 0, so the walk ends at the segment's start.  Then tile t publishes its own running total.
-// Every thread gets the result.  Call from uniform control flow; contains a barrier.
-// (Reading 256 tiles per round, 4 per lane, was slower: 13 % on 4096 tiles, 3 % on 512.)
+// The status words of the 64 * kRows tiles below `top` (row h, lane l: the tile 64 h + l below
+// it), as loaded; a tile before `first` loads the word of `first` instead (chain_lookback reads
+// it as a running total of 0).  Loads are issued for every lane and row, so that the wave
+// waits for them once.
+template <int kRows>
+__device__ __forceinline__ void chain_load(const EncodeArgs &a, uint32_t top, uint32_t first, uint32_t lane,
+                                           uint64_t (&w)[kRows])
+{
+#pragma unroll
+    for (int h = 0; h < kRows; ++h) {
+        const uint32_t d = 64u * h + lane;
+        w[h] = __hip_atomic_load(a.chain_status + (uint64_t)(d <= top - first ? top - d : first) * kChainStride,
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Escapes of the segment's tiles before tile t (t > first, the segment's first tile), by a
+// decoupled look-back run by one whole wave; tile t's own count must already be published,
+// and w must hold chain_load(a, t - 1, first, lane, w) (issued early, so that its latency
+// overlaps other work).  Tiles up to and including the nearest one below t that holds a
+// running total must all be written (else the wave sleeps and loads the window again), and
+// their counts give the result; when none of the window's tiles holds a running total their
+// counts are added and the next window is loaded.  Tiles before `first` read as a running
+// total of 0, so the walk ends at the segment's start.  Every lane gets the result.
+// (Reading 128 or 256 tiles per round was slower, on 4096 tiles by 8 and 13 %.)
+template <int kRows>
+__device__ __forceinline__ uint64_t chain_lookback(const EncodeArgs &a, uint64_t tag, uint32_t t, uint32_t first,
+                                                   uint32_t lane, uint64_t (&w)[kRows])
+{
+    uint64_t before = 0;
+    uint32_t top = t - 1;            // highest tile not yet counted
+    uint32_t polls = 0;
+    for (;;) {
+        // the first row holding a running total (kRows if none)
+        int hs = kRows;
+        bool ok = true;
+        uint64_t part = 0;
+#pragma unroll
+        for (int h = 0; h < kRows; ++h) {
+            const bool inside = 64u * h + lane <= top - first;             // tile top - d >= first
+            const uint64_t x = inside ? w[h] : chain_word(tag, kChainPrefix, 0);
+            const uint64_t kind = (x >> kChainKindShift) & 3u;
+            const bool written = (x >> kChainTagShift) == tag && kind != 0;
+            const uint64_t totals = __ballot(written && kind == kChainPrefix);
+            const uint64_t ready = __ballot(written);
+            if (hs == kRows) {
+                // rows before hs must be written whole, row hs up to its first running total
+                const uint32_t st = totals ? (uint32_t)__builtin_ctzll(totals) : 63u;
+                const uint64_t need = st == 63u ? ~0ull : (2ull << st) - 1u;
+                ok = ok && (ready & need) == need;
+                part += lane <= st ? (x & kChainCountMask) : 0ull;
+                if (totals)
+                    hs = h;
+            }
+        }
+        if (ok) {
+            before += wave_total_u64(part, lane);
+            if (hs < kRows)
+                break;
+            // 64 kRows written tiles without a running total are all inside the segment, and
+            // the segment's first tile holds one: at least one tile is left below them.
+            // Checked anyway, so that no status word read can move the walk below `first`.
+            if (top - first < 64u * kRows) {
+                if (lane == 0)
+                    atomicOr(a.err, kErrChainStall);
+                break;
+            }
+            top -= 64u * kRows;
+        } else {
+            if (++polls > kChainSpinMax) {
+                if (lane == 0)
+                    atomicOr(a.err, kErrChainStall);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        chain_load<kRows>(a, top, first, lane, w);
+    }
+    return uniform_u64(before);
+}
+
+// Tile t's escape offset in its segment: it publishes its own count (as the segment's running
+// total if it is the first tile), wave 0 runs the look-back, and tile t publishes its running
+// total.  Every thread gets the result.  Call from uniform control flow; contains a barrier.
 __device__ __forceinline__ uint64_t chain_prefix(const EncodeArgs &a, uint64_t tag, uint32_t t, uint32_t first,
                                                  uint32_t tile_total, uint32_t tid, uint32_t lane,
                                                  uint64_t *s_prefix)
@@ -338,43 +459,9 @@ __device__ __forceinline__ uint64_t chain_prefix(const EncodeArgs &a, uint64_t t
         if (t > first) {
             if (lane == 0)
                 chain_publish(a, t, chain_word(tag, kChainAggregate, tile_total));
-            uint32_t top = t - 1;            // highest tile not yet counted
-            uint32_t polls = 0;
-            for (;;) {
-                const bool inside = lane <= top - first;          // tile top - lane >= first
-                const uint64_t w = inside ? __hip_atomic_load(a.chain_status + (top - lane), __ATOMIC_RELAXED,
-                                                              __HIP_MEMORY_SCOPE_AGENT)
-                                          : chain_word(tag, kChainPrefix, 0);
-                const uint64_t kind = (w >> kChainKindShift) & 3u;
-                const bool written = (w >> kChainTagShift) == tag && kind != 0;
-                const uint64_t totals = __ballot(written && kind == kChainPrefix);
-                const uint64_t ready = __ballot(written);
-                // lanes 0 .. stop must be written (all 64 when none holds a running total)
-                const uint32_t stop = totals ? (uint32_t)__builtin_ctzll(totals) : 63u;
-                const uint64_t need = stop == 63u ? ~0ull : (2ull << stop) - 1u;
-                if ((ready & need) == need) {
-                    before += wave_total_u64(lane <= stop ? (w & kChainCountMask) : 0ull, lane);
-                    if (totals)
-                        break;
-                    // 64 written tiles without a running total are all inside the segment,
-                    // and the segment's first tile holds one: at least one tile is left below
-                    // them.  Checked anyway, so that no status word read can move the walk
-                    // below `first`.
-                    if (top - first < 64) {
-                        if (lane == 0)
-                            atomicOr(a.err, kErrChainStall);
-                        break;
-                    }
-                    top -= 64;
-                    continue;
-                }
-                if (++polls > kChainSpinMax) {
-                    if (lane == 0)
-                        atomicOr(a.err, kErrChainStall);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(2);
-            }
+            uint64_t w[kChainRows];
+            chain_load<kChainRows>(a, t - 1, first, lane, w);
+            before = chain_lookback<kChainRows>(a, tag, t, first, lane, w);
         }
         if (lane == 0) {
             chain_publish(a, t, chain_word(tag, kChainPrefix, before + tile_total));

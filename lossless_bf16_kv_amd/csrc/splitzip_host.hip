@@ -187,10 +187,10 @@ static __device__ __align__(256) uint8_t noalloc_scratch[SPLITZIP_NOALLOC_SCRATC
 
 constexpr int kNoAllocDevices = 64;
 // The last bytes of the array hold the one-pass state of the allocation-free encode: the
-// status words of up to kNoAllocChainTiles tiles (4 GiB of BF16).  Only one-pass calls touch
+// status words of up to kNoAllocChainTiles tiles (4 GiB of BF16), 4 MiB.  Only one-pass calls touch
 // them, and the array starts zeroed (a cleared state).
 constexpr uint32_t kNoAllocChainTiles = 1u << 17;
-constexpr uint64_t kNoAllocChainBytes = 8ull * kNoAllocChainTiles;
+constexpr uint64_t kNoAllocChainBytes = 8ull * sz::kChainStride * kNoAllocChainTiles;
 constexpr uint64_t kNoAllocScratchBytes = SPLITZIP_NOALLOC_SCRATCH_BYTES - kNoAllocChainBytes;
 
 struct NoAllocDevice {
@@ -380,7 +380,7 @@ int get_workspace(splitzip_codec *c, hipStream_t stream, std::shared_ptr<Workspa
 uint64_t workspace_device_bytes(const Workspace &w)
 {
     uint64_t b = w.scratch_cap + (w.ovf_ctr ? 2 * sizeof(unsigned long long) : 0) +
-                 8 * (uint64_t)w.chain_cap +
+                 8ull * sz::kChainStride * w.chain_cap +
                  (w.result ? 8 + 8 * (uint64_t)w.result_cap : 0);
     for (const Staging &s : w.staging)
         b += (s.d_segs ? (uint64_t)s.cap * sizeof(sz::SegDesc) : 0) + (s.d_tiles ? s.tcap * sizeof(uint32_t) : 0);
@@ -516,7 +516,7 @@ int ensure_chain(Workspace *w, uint32_t n_tiles)
     (void)hipFree(w->chain);
     w->chain = nullptr;
     w->chain_cap = 0;
-    SZ_HIP(hipMalloc(&w->chain, 8 * (uint64_t)cap), "hipMalloc(one-pass state)");
+    SZ_HIP(hipMalloc(&w->chain, 8ull * sz::kChainStride * cap), "hipMalloc(one-pass state)");
     SZ_HIP(sz::launch_chain_clear(w->chain, cap, w->stream), "clear of the one-pass state");
     w->chain_cap = cap;
     return SPLITZIP_OK;

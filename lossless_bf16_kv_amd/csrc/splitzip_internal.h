@@ -111,6 +111,22 @@ constexpr uint64_t kChainPrefix = 2;
 // this many times per tile (far longer than any tile takes) before it gives up, flags
 // kErrChainStall and goes on as if the rest had no escapes: a launch always ends
 constexpr uint32_t kChainSpinMax = 1u << 22;
+// rows of 64 status words the look-back reads per round
+constexpr int kChainRows = 1;
+// u64 words per tile in the one-pass state: each tile's status word sits alone in its 32 bytes.
+// Packed 16 to a 128-byte line, the words that hundreds of waiting waves poll and that their
+// tiles write queued on a few lines (4096 tiles at 30 % escapes: 86 against 80 us).
+constexpr uint32_t kChainStride = 4;
+// One-pass encode, early release: a tile with at most kStashEscapes escapes keeps them (u16
+// position, u8 exponent) and its chunk starts' escape ranks (u16, at most one per 16 words)
+// in LDS; waves 1..3 then end and free their registers while wave 0 waits for the tile's
+// escape offset and writes them.  Tiles with more escapes wait with all four waves.
+constexpr uint32_t kStashEscapes = 8192;
+constexpr uint32_t kStashChunks = kEncTileWords / 16;
+// byte offset of the positions in the stash: the copy out reads 16 bytes before each array
+constexpr uint32_t kStashPosAt = 16;
+constexpr uint32_t kE8StashEscapes = 8192;
+constexpr uint32_t kE8StashChunks = (1u << kE8EncTileShift) / 16;
 static_assert(kChainCountMask >= (1ull << 38), "a segment's escape count fits the status word");
 
 // overflow counter: escapes reserved so far (low 40 bits) and overflow tiles listed (high 24)

@@ -201,7 +201,13 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
     __shared__ uint8_t s_lut[256];
     __shared__ uint32_t s_wave_total[kWaves];
     __shared__ uint64_t s_ovf;
-    __shared__ uint32_t s_stage[kWaves][64 * kGroupWords];   // one group's escapes per wave
+    // one group's escapes per wave; in the one-pass build also the early-release stash
+    constexpr uint32_t kStageWords = kWaves * 64 * kGroupWords;
+    constexpr uint32_t kStashExpAt = kStashPosAt + 2 * kStashEscapes + 16;
+    constexpr uint32_t kStashWords = (kStashExpAt + kStashEscapes + 2 * kStashChunks + 3) / 4;
+    __shared__ uint32_t s_stage[kChain && kStashWords > kStageWords ? kStashWords : kStageWords];
+    // one-pass build: for each 8-bit escape mask, the indices of its set bits, 4 bits each
+    __shared__ uint32_t s_bitpos[kChain ? 256 : 1];
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = lane_id();
@@ -216,6 +222,16 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
         reinterpret_cast<uint32_t *>(s_lut)[tid] = reinterpret_cast<const uint32_t *>(lut)[tid];
     if (!kChain && a.packed && tid == 0 && t == segment_first_tile(a, s))
         a.seg_total[s] = 0;      // the sums launch adds the segment's escapes into it
+    if (kChain) {
+        uint32_t e = 0, c = 0;
+#pragma unroll
+        for (uint32_t b = 0; b < 8; ++b)
+            if ((tid >> b) & 1u) {
+                e |= b << (4 * c);
+                ++c;
+            }
+        s_bitpos[tid & 255u] = e;
+    }
     const uint64_t tag = a.chain_tag;
     const uint64_t n = sd.n;
     const SZ_GLOBAL uint16_t *xw = as_global(sd.data);
@@ -275,6 +291,80 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
     uint32_t wave_end;
     tile_escape_ranks<kEncGroups>(counts, lane, wave, s_wave_total, rank, tile_total, wave_end);
 
+    if (kChain && tile_total <= kStashEscapes) {
+        // one pass, early release: the escapes (final u16 position, exponent byte, at their
+        // ranks) and the chunk starts' ranks wait in LDS; waves 1..3 end, and wave 0 waits for
+        // the tile's escape offset and writes them to their final places.
+        uint8_t *lds = reinterpret_cast<uint8_t *>(s_stage);
+        uint16_t *s_pos = reinterpret_cast<uint16_t *>(lds + kStashPosAt);
+        uint8_t *s_exp = lds + kStashExpAt;
+        uint16_t *s_start = reinterpret_cast<uint16_t *>(s_exp + kStashEscapes);
+        const uint32_t first = segment_first_tile(a, s);
+        const bool last = t + 1 == segment_end_tile(a, s);        // loaded before the waits below
+        if (tid == 0)
+            chain_publish(a, t, chain_word(tag, t > first ? kChainAggregate : kChainPrefix, tile_total));
+        // wave 0 issues the look-back's first loads now; they return while the escapes go to LDS
+        uint64_t w[kChainRows];
+        if (wave == 0 && t > first)
+            chain_load<kChainRows>(a, t - 1, first, lane, w);
+        const uint32_t cm = (uint32_t)cmask;
+#pragma unroll
+        for (int j = 0; j < kEncGroups; ++j) {
+            const uint32_t r0 = rank[j];
+            const uint32_t p0 = (uint32_t)(g0[j] - base);
+            if (g0[j] < n && (g0[j] & cmask) == 0)
+                s_start[p0 >> a.log2_chunk] = (uint16_t)r0;
+            const uint32_t z = flags[j];
+            if (z) {
+                // the lane's escapes go to ranks r0, r0 + 1, ...: the i-th in step i, its word
+                // index from the table of set bits
+                const uint32_t elo = perm(v[j].y >> 7, v[j].x >> 7, 0x06040200u);   // exponents, words 0..3
+                const uint32_t ehi = perm(v[j].w >> 7, v[j].z >> 7, 0x06040200u);   // words 4..7
+                const uint32_t f = (((z >> 4) & 0x03030303u) * 0x01041040u) >> 24;   // bit k: word k escapes
+                const uint32_t cnt = __popc(f);
+                const uint32_t ks = s_bitpos[f];
+                const uint32_t q0 = (uint32_t)g0[j];
+#pragma unroll
+                for (int i = 0; i < kGroupWords; ++i) {
+                    const bool act = (uint32_t)i < cnt;
+                    if (!__ballot(act))
+                        break;
+                    if (act) {
+                        const uint32_t k = (ks >> (4 * i)) & 15u;
+                        s_pos[r0 + i] = (uint16_t)((q0 + k) & cm);
+                        s_exp[r0 + i] = (uint8_t)perm(ehi, elo, k);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        if (wave != 0)
+            return;
+        const uint64_t before = t > first ? chain_lookback<kChainRows>(a, tag, t, first, lane, w) : 0ull;
+        if (lane == 0) {
+            if (t > first)
+                chain_publish(a, t, chain_word(tag, kChainPrefix, before + tile_total));
+            if (last) {
+                chunk_off[(n + cmask) >> a.log2_chunk] = before + tile_total;
+                a.seg_escapes[s] = before + tile_total;
+            }
+        }
+        const uint64_t tile_end = base + kEncTileWords < n ? base + kEncTileWords : n;
+        const uint32_t starts = a.log2_chunk <= (uint32_t)kEncTileShift
+                              ? (uint32_t)((tile_end - base + cmask) >> a.log2_chunk)
+                              : ((base & cmask) == 0 ? 1u : 0u);
+        SZ_GLOBAL uint64_t *co = chunk_off + (base >> a.log2_chunk);
+        for (uint32_t i = lane; i < starts; i += 64)
+            co[i] = before + s_start[i];
+        const uint64_t left = sd.esc > before && sd.esc_exp ? sd.esc - before : 0;
+        const uint32_t ne = left < tile_total ? (uint32_t)left : tile_total;
+        if (ne) {
+            stash_copy<2>(as_global(sd.esc_pos + before), s_pos, ne, lane);
+            stash_copy<1>(as_global(sd.esc_exp + before), s_exp, ne, lane);
+        }
+        return;
+    }
+
     // where the tile's escapes go: its slot, or a range of the overflow area; in the one-pass
     // build their final places, after the escapes of the segment's earlier tiles (at most
     // `room` of them, the escape capacity left).  A segment's last tile also writes E.
@@ -301,7 +391,7 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
     // and stored 64 consecutive entries per instruction; a few are stored directly by the
     // lanes that hold them.
     SZ_GLOBAL uint32_t *gdst = as_global(dst);
-    uint32_t *stage = s_stage[wave];
+    uint32_t *stage = s_stage + wave * 64 * kGroupWords;
 #pragma unroll
     for (int j = 0; j < kEncGroups; ++j) {
         const uint32_t r0 = rank[j];
@@ -1004,16 +1094,17 @@ __global__ __launch_bounds__(kThreads) void seg_at_kernel(const uint32_t *tile_s
 }
 
 // Every status word of a one-pass state unwritten.
-__global__ __launch_bounds__(kThreads) void chain_clear_kernel(uint64_t *status, uint32_t cap)
+__global__ __launch_bounds__(kThreads) void chain_clear_kernel(uint64_t *status, uint64_t words)
 {
     const uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (i < cap)
+    if (i < words)
         status[i] = 0;
 }
 
 hipError_t launch_chain_clear(uint64_t *status, uint32_t cap, hipStream_t stream)
 {
-    chain_clear_kernel<<<cap / kThreads + 1, kThreads, 0, stream>>>(status, cap);
+    const uint64_t words = (uint64_t)cap * kChainStride;
+    chain_clear_kernel<<<(unsigned)(words / kThreads + 1), kThreads, 0, stream>>>(status, words);
     return hipGetLastError();
 }
 
@@ -1054,9 +1145,9 @@ hipError_t launch_encode_stage(int stage, const EncodeArgs &a, hipStream_t strea
             return hipErrorInvalidValue;
         if (a.elem == kElemE5M2)
             return launch_encode_pack_e5m2(a, stream);
+        // (the early-release stash already holds occupancy at 4 workgroups per CU)
         if (a.stage)
-            encode_pack_kernel<true, true><<<a.n_tiles, kThreads,
-                                             a.n_tiles >= kPackCapTiles ? kPackLdsReserve : 0u, stream>>>(a);
+            encode_pack_kernel<true, true><<<a.n_tiles, kThreads, 0, stream>>>(a);
         else
             encode_pack_kernel<false, true><<<a.n_tiles, kThreads, 0, stream>>>(a);
         break;
