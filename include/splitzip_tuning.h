@@ -44,11 +44,16 @@ int splitzip_set_small_tiles(splitzip_codec *codec, uint32_t max_tiles);
  * escapes, chunk offsets and, as a segment's last tile, E straight to their final places.
  * Other calls (larger ones, packed streams, and calls on a stream that is being captured
  * into a graph, since each launch's tag is a kernel argument that a replay would repeat) run
- * the launch sequences of splitzip_set_small_tiles.  Up to about 2048 tiles one launch is
- * faster (no second launch); on larger calls, with many tiles in flight, each tile's wait
- * for the earlier ones costs more than the other launches do.  The codec's workspace for the
- * stream keeps 8 bytes per tile of state for it.  0 = never, UINT32_MAX = always; any value
- * is accepted.  Applies to calls that start after it returns.
+ * the launch sequences of splitzip_set_small_tiles, with one exception: when the previous
+ * encode on the same stream had more escapes in its first tile than a tile's slot in the
+ * launch sequences holds (128 BF16, 256 E5M2), a larger call runs in one launch too, since
+ * the launch sequences would move each escape through scratch.  On inputs with few escapes
+ * one launch is faster up to about 2048 tiles (no second launch); on larger calls, with many
+ * tiles in flight, each tile's wait for the earlier ones costs more than the other launches
+ * do.  The codec's workspace for the stream keeps 32 bytes per tile of state for it, and a
+ * word of host memory mapped for the GPU that each encode's first tile writes its escape
+ * count to.  0 = never (also for escape-heavy inputs), UINT32_MAX = always; any value is
+ * accepted.  Applies to calls that start after it returns.
  */
 int splitzip_set_onepass_tiles(splitzip_codec *codec, uint32_t max_tiles);
 

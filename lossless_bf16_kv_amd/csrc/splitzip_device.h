@@ -447,30 +447,4 @@ __device__ __forceinline__ uint64_t chain_lookback(const EncodeArgs &a, uint64_t
     return uniform_u64(before);
 }
 
-// Tile t's escape offset in its segment: it publishes its own count (as the segment's running
-// total if it is the first tile), wave 0 runs the look-back, and tile t publishes its running
-// total.  Every thread gets the result.  Call from uniform control flow; contains a barrier.
-__device__ __forceinline__ uint64_t chain_prefix(const EncodeArgs &a, uint64_t tag, uint32_t t, uint32_t first,
-                                                 uint32_t tile_total, uint32_t tid, uint32_t lane,
-                                                 uint64_t *s_prefix)
-{
-    if (tid < 64) {
-        uint64_t before = 0;
-        if (t > first) {
-            if (lane == 0)
-                chain_publish(a, t, chain_word(tag, kChainAggregate, tile_total));
-            uint64_t w[kChainRows];
-            chain_load<kChainRows>(a, t - 1, first, lane, w);
-            before = chain_lookback<kChainRows>(a, tag, t, first, lane, w);
-        }
-        if (lane == 0) {
-            chain_publish(a, t, chain_word(tag, kChainPrefix, before + tile_total));
-            *s_prefix = before;
-        }
-    }
-    __syncthreads();
-    const uint64_t v = *s_prefix;
-    return uniform_u64(v);
-}
-
 }  // namespace sz

@@ -83,8 +83,20 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
     __shared__ uint8_t s_lut[256];
     __shared__ uint32_t s_wave_total[kWaves];
     __shared__ uint64_t s_ovf;
-    __shared__ uint4 s_in[kWaves][128];        // one 2048-byte group per wave, regrouped
-    __shared__ uint16_t s_stage[kWaves][2048];  // one group's escapes per wave (11-bit place, exponent)
+    // per wave: one 2048-byte group, regrouped (s_in), and one group's escapes (s_stage: 11-bit
+    // place, exponent); in the one-pass build the same LDS also holds the early-release stash
+    // (its use begins after the last regroup and excludes the staged stores)
+    constexpr uint32_t kInWords = kWaves * 128 * 4, kStageWords = kWaves * 2048 / 2;
+    constexpr uint32_t kStashExpAt = kStashPosAt + 2 * kE8StashEscapes + 16;
+    constexpr uint32_t kStashWords = (kStashExpAt + kE8StashEscapes + 2 * kE8StashChunks + 3) / 4;
+    constexpr uint32_t kRawWords = kChain && kStashWords > kInWords + kStageWords ? kStashWords : kInWords + kStageWords;
+    __shared__ uint32_t s_raw[kRawWords];
+    __shared__ uint32_t s_bitpos[kChain ? 256 : 1];   // one-pass build: set-bit indices of each byte
+    __shared__ uint32_t s_ready;        // one-pass build: 2 when wave 0 has put the tile's offset in
+                                        // s_before and copied the stash out
+    __shared__ uint64_t s_before;
+    uint4(*s_in)[128] = reinterpret_cast<uint4(*)[128]>(s_raw);
+    uint16_t(*s_stage)[2048] = reinterpret_cast<uint16_t(*)[2048]>(s_raw + kInWords);
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = lane_id();
@@ -98,6 +110,16 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
         reinterpret_cast<uint32_t *>(s_lut)[tid] = reinterpret_cast<const uint32_t *>(lut)[tid];
     if (!kChain && a.packed && tid == 0 && t == segment_first_tile(a, s))
         a.seg_total[s] = 0;      // the sums launch adds the segment's escapes into it
+    if (kChain) {
+        uint32_t e = 0, c = 0;
+#pragma unroll
+        for (uint32_t b = 0; b < 8; ++b)
+            if ((tid >> b) & 1u) {
+                e |= b << (4 * c);
+                ++c;
+            }
+        s_bitpos[tid & 255u] = e;
+    }
     const uint64_t n = sd.n;
     const uint64_t base = (uint64_t)(t - segment_first_tile(a, s)) << kE8EncTileShift;
     const uint64_t cmask = (1ull << a.log2_chunk) - 1;
@@ -196,24 +218,160 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
     uint32_t tile_total;
     uint32_t wave_end;
     tile_escape_ranks<G>(counts, lane, wave, s_wave_total, rank, tile_total, wave_end);
-    // where the tile's escapes go: its slot or the overflow area; in the one-pass build their
-    // final places after the escapes of the segment's earlier tiles (at most `room` of them)
-    uint64_t room = 0, prefix = 0;
-    uint32_t *dst = nullptr;
-    SZ_GLOBAL uint16_t *fpos = nullptr;
-    SZ_GLOBAL uint8_t *fexp = nullptr;
+    if (a.first_tile_escapes && t == 0 && tid == 0)
+        __hip_atomic_store(a.first_tile_escapes, tile_total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+
     if (kChain) {
-        prefix = chain_prefix(a, a.chain_tag, t, segment_first_tile(a, s), tile_total, tid, lane, &s_ovf);
-        room = sd.esc > prefix && sd.esc_exp ? sd.esc - prefix : 0;
-        fpos = as_global(sd.esc_pos + (room ? prefix : 0));
-        fexp = as_global(sd.esc_exp + (room ? prefix : 0));
-        if (tid == 0 && t + 1 == segment_end_tile(a, s)) {
-            chunk_off[(n + cmask) >> a.log2_chunk] = prefix + tile_total;
-            a.seg_escapes[s] = prefix + tile_total;
+        // one pass, early release, as in the BF16 pack: the escapes of rank below
+        // kE8StashEscapes and the chunk starts' ranks wait in LDS; waves whose escapes all fit
+        // end, wave 0 waits for the tile's escape offset, a wave with escapes past the stash
+        // gets it from wave 0 and writes those itself
+        uint8_t *lds = reinterpret_cast<uint8_t *>(s_raw);
+        uint16_t *s_pos = reinterpret_cast<uint16_t *>(lds + kStashPosAt);
+        uint8_t *s_exp = lds + kStashExpAt;
+        uint16_t *s_start = reinterpret_cast<uint16_t *>(s_exp + kE8StashEscapes);
+        const uint64_t tag = a.chain_tag;
+        const uint32_t first = segment_first_tile(a, s);
+        const bool last = t + 1 == segment_end_tile(a, s);
+        if (tid == 0) {
+            chain_publish(a, t, chain_word(tag, t > first ? kChainAggregate : kChainPrefix, tile_total));
+            s_ready = 0;
         }
-    } else {
-        dst = tile_escape_dest(a, t, tile_total, tid, &s_ovf, room);
+        uint64_t w[kChainRows];
+        if (wave == 0 && t > first)
+            chain_load<kChainRows>(a, t - 1, first, lane, w);
+        const uint32_t cm = (uint32_t)cmask;
+        // the lane's escapes of rank lo .. hi - 1 to LDS at rank - lo (as in the BF16 pack, per
+        // 8 elements of a lane's 32)
+        auto stash = [&](uint32_t lo, uint32_t hi) {
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                uint32_t r = rank[j];
+                const uint32_t fl = flags[j];
+                if (fl && r < hi && r + 32u > lo) {
+                    const uint32_t q0 = (uint32_t)g0[j];
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        // escape flags of elements 8d .. 8d + 7, bit k for element 8d + k
+                        const uint32_t sh = 2u * (((uint32_t)d + 2u) & 3u);
+                        const uint32_t f = (((fl >> sh) & 0x03030303u) * 0x01041040u) >> 24;
+                        const uint32_t cnt = __popc(f);
+                        const uint32_t ks = s_bitpos[f];
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            if (!__ballot((uint32_t)i < cnt))
+                                break;
+                            const uint32_t ri = r + i;
+                            if ((uint32_t)i < cnt && ri >= lo && ri < hi) {
+                                const uint32_t k = (ks >> (4 * i)) & 15u;
+                                s_pos[ri - lo] = (uint16_t)((q0 + 8u * d + k) & cm);
+                                s_exp[ri - lo] = (uint8_t)((perm(v[j][2 * d + 1], v[j][2 * d], k) >> 2) & 0x1Fu);
+                            }
+                        }
+                        r += cnt;
+                    }
+                }
+            }
+        };
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const uint32_t p0 = (uint32_t)(g0[j] - base);
+            if (g0[j] < n && (g0[j] & cmask) == 0)
+                s_start[p0 >> a.log2_chunk] = (uint16_t)rank[j];
+            if (a.log2_chunk == 4 && g0[j] + 16 < n)
+                s_start[(p0 + 16) >> 4] = (uint16_t)(rank[j] + __popc(flags[j] & 0xF0F0F0F0u));
+        }
+        stash(0, kE8StashEscapes);
+        __syncthreads();
+        const bool past = wave_end > kE8StashEscapes;               // uniform in the wave
+        if (wave != 0 && !past)
+            return;
+        if (wave == 0) {
+            const uint64_t before = t > first ? chain_lookback<kChainRows>(a, tag, t, first, lane, w) : 0ull;
+            if (lane == 0) {
+                if (t > first)
+                    chain_publish(a, t, chain_word(tag, kChainPrefix, before + tile_total));
+                if (last) {
+                    chunk_off[(n + cmask) >> a.log2_chunk] = before + tile_total;
+                    a.seg_escapes[s] = before + tile_total;
+                }
+                if (tile_total > kE8StashEscapes)
+                    s_before = before;
+            }
+            const uint64_t tile_end = base + (1u << kE8EncTileShift) < n ? base + (1u << kE8EncTileShift) : n;
+            const uint32_t starts = a.log2_chunk <= (uint32_t)kE8EncTileShift
+                                  ? (uint32_t)((tile_end - base + cmask) >> a.log2_chunk)
+                                  : ((base & cmask) == 0 ? 1u : 0u);
+            SZ_GLOBAL uint64_t *co = chunk_off + (base >> a.log2_chunk);
+            for (uint32_t i = lane; i < starts; i += 64)
+                co[i] = before + s_start[i];
+            const uint64_t left = sd.esc > before && sd.esc_exp ? sd.esc - before : 0;
+            uint32_t ne = left < tile_total ? (uint32_t)left : tile_total;
+            ne = ne < kE8StashEscapes ? ne : kE8StashEscapes;
+            if (ne) {
+                stash_copy<2>(as_global(sd.esc_pos + before), s_pos, ne, lane);
+                stash_copy<1>(as_global(sd.esc_exp + before), s_exp, ne, lane);
+            }
+            if (tile_total > kE8StashEscapes && lane == 0)    // the stash is free again
+                __hip_atomic_store(&s_ready, 2u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            return;
+        }
+        // a wave with escapes past the stash: once wave 0 has copied the stash out (a bounded
+        // wait), its escapes of rank kE8StashEscapes .. 2 kE8StashEscapes - 1 go through the
+        // stash at rank - kE8StashEscapes and out, and any of higher rank straight from its
+        // registers
+        uint32_t polls = 0;
+        while (__hip_atomic_load(&s_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 2u) {
+            if (++polls > kChainSpinMax) {
+                if (lane == 0)
+                    atomicOr(a.err, kErrChainStall);
+                return;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        const uint64_t sb = s_before;
+        const uint64_t before = uniform_u64(sb);
+        const uint64_t left = sd.esc > before && sd.esc_exp ? sd.esc - before : 0;
+        const uint32_t wave_first = (uint32_t)__builtin_amdgcn_readfirstlane(rank[0]);   // lane 0's group 0
+        const uint32_t lo = wave_first > kE8StashEscapes ? wave_first : kE8StashEscapes;
+        uint32_t hi = (uint64_t)wave_end < left ? wave_end : (uint32_t)left;
+        hi = hi < 2 * kE8StashEscapes ? hi : 2 * kE8StashEscapes;
+        if (hi > lo) {
+            stash(kE8StashEscapes, 2 * kE8StashEscapes);
+            stash_copy<2>(as_global(sd.esc_pos + before + lo), s_pos + (lo - kE8StashEscapes), hi - lo, lane);
+            stash_copy<1>(as_global(sd.esc_exp + before + lo), s_exp + (lo - kE8StashEscapes), hi - lo, lane);
+        }
+        if (wave_end <= 2 * kE8StashEscapes || left <= 2 * kE8StashEscapes)
+            return;
+        SZ_GLOBAL uint16_t *ep = as_global(sd.esc_pos + before);
+        SZ_GLOBAL uint8_t *ee = as_global(sd.esc_exp + before);
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            if (flags[j] && rank[j] + (uint32_t)__popc(flags[j]) > 2 * kE8StashEscapes) {
+                uint32_t r = rank[j];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    uint32_t z = flags[j] & e8_flag_mask(d);
+                    const uint64_t bytes8 = ((uint64_t)v[j][2 * d + 1] << 32) | v[j][2 * d];
+                    while (z) {
+                        const uint32_t b = (uint32_t)__builtin_ctz(z);
+                        const uint32_t k = 2u * (b >> 3) + (b & 1u);          // element 8d + k
+                        if (r >= 2 * kE8StashEscapes && r < left) {
+                            ep[r] = (uint16_t)((g0[j] + 8u * d + k) & cmask);
+                            ee[r] = (uint8_t)((uint32_t)(bytes8 >> (8 * k + 2)) & 0x1Fu);
+                        }
+                        ++r;
+                        z &= z - 1;
+                    }
+                }
+            }
+        }
+        return;
     }
+
+    // where the tile's escapes go: its slot or the overflow area
+    uint64_t room = 0;
+    uint32_t *dst = tile_escape_dest(a, t, tile_total, tid, &s_ovf, room);
     SZ_GLOBAL uint32_t *gdst = as_global(dst);
 
     // escapes: (position inside the tile, exponent); tile-local chunk offsets (a chunk of 16
@@ -222,9 +380,9 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
     for (int j = 0; j < G; ++j) {
         const uint32_t r0 = rank[j];
         if (g0[j] < n && (g0[j] & cmask) == 0)
-            chunk_off[g0[j] >> a.log2_chunk] = prefix + r0;
+            chunk_off[g0[j] >> a.log2_chunk] = r0;
         if (a.log2_chunk == 4 && g0[j] + 16 < n)
-            chunk_off[(g0[j] + 16) >> 4] = prefix + r0 + __popc(flags[j] & 0xF0F0F0F0u);
+            chunk_off[(g0[j] + 16) >> 4] = r0 + __popc(flags[j] & 0xF0F0F0F0u);
         // a wave's escapes of one group have consecutive ranks; more than kStageMin of them
         // are gathered in the wave's LDS buffer (place inside the group in 11 bits, exponent
         // in 5) and stored 64 consecutive entries per instruction: stored by the lanes that
@@ -261,14 +419,8 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
                         const uint32_t b = (uint32_t)__builtin_ctz(z);
                         const uint32_t k = 2u * (b >> 3) + (b & 1u);          // element 8d + k
                         const uint32_t e = (uint32_t)(bytes8 >> (8 * k + 2)) & 0x1Fu;
-                        if (r < room) {
-                            if (kChain) {
-                                fpos[r] = (uint16_t)((g0[j] + 8u * d + k) & cmask);
-                                fexp[r] = (uint8_t)e;
-                            } else {
-                                gdst[r] = (p0 + 8u * d + k) | (e << 16);
-                            }
-                        }
+                        if (r < room)
+                            gdst[r] = (p0 + 8u * d + k) | (e << 16);
                         ++r;
                         z &= z - 1;
                     }
@@ -281,12 +433,7 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
             for (uint32_t i = lane; i < wcnt; i += 64)
                 if (w0 + i < room) {
                     const uint32_t h = s_stage[wave][i];
-                    if (kChain) {
-                        fpos[w0 + i] = (uint16_t)((base + gp + (h & 0x7FFu)) & cmask);
-                        fexp[w0 + i] = (uint8_t)(h >> 11);
-                    } else {
-                        gdst[w0 + i] = (gp + (h & 0x7FFu)) | ((h >> 11) << 16);
-                    }
+                    gdst[w0 + i] = (gp + (h & 0x7FFu)) | ((h >> 11) << 16);
                 }
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         }
@@ -298,7 +445,7 @@ hipError_t launch_encode_pack_e5m2(const EncodeArgs &a, hipStream_t stream)
     const unsigned lds = a.n_tiles >= kPackCapTiles ? kE8PackLdsReserve : 0u;
     if (a.chain_status) {
         if (a.stage)
-            encode_pack_e5m2_kernel<true, true><<<a.n_tiles, kThreads, lds, stream>>>(a);
+            encode_pack_e5m2_kernel<true, true><<<a.n_tiles, kThreads, 0, stream>>>(a);
         else
             encode_pack_e5m2_kernel<false, true><<<a.n_tiles, kThreads, 0, stream>>>(a);
     } else {

@@ -148,6 +148,8 @@ struct Workspace {
     uint32_t result_cap = 0;
     // host
     uint8_t *h_result = nullptr;      // pinned mirror of `result`
+    uint32_t *hint = nullptr;         // host memory mapped for the device: the escapes of the
+    uint32_t *d_hint = nullptr;       // last encode's first tile (d_hint: its device address)
     Staging staging[kStagingSlots];
     int next_slot = 0;
     // profiling
@@ -168,6 +170,7 @@ struct Workspace {
         (void)hipFree(chain);
         (void)hipFree(result);
         (void)hipHostFree(h_result);
+        (void)hipHostFree(hint);
         for (Staging &s : staging) {
             (void)hipHostFree(s.h_segs);
             (void)hipHostFree(s.h_tiles);
@@ -519,6 +522,24 @@ int ensure_chain(Workspace *w, uint32_t n_tiles)
     SZ_HIP(hipMalloc(&w->chain, 8ull * sz::kChainStride * cap), "hipMalloc(one-pass state)");
     SZ_HIP(sz::launch_chain_clear(w->chain, cap, w->stream), "clear of the one-pass state");
     w->chain_cap = cap;
+    return SPLITZIP_OK;
+}
+
+// The workspace's hint word (see Workspace::hint), 0 when new.
+int ensure_hint(Workspace *w)
+{
+    if (w->hint)
+        return SPLITZIP_OK;
+    void *h = nullptr, *d = nullptr;
+    SZ_HIP(hipHostMalloc(&h, 64, hipHostMallocMapped | hipHostMallocCoherent), "hipHostMalloc(hint)");
+    std::memset(h, 0, 64);
+    const hipError_t e = hipHostGetDevicePointer(&d, h, 0);
+    if (e != hipSuccess) {
+        (void)hipHostFree(h);
+        return fail_hip(e, "hipHostGetDevicePointer(hint)");
+    }
+    w->hint = static_cast<uint32_t *>(h);
+    w->d_hint = static_cast<uint32_t *>(d);
     return SPLITZIP_OK;
 }
 
@@ -1105,9 +1126,10 @@ void set_encode_args(sz::EncodeArgs &a, const splitzip_codec *codec, uint32_t n_
 // Whether an encode of n_tiles tiles on `stream` runs in one pass (see
 // splitzip_set_onepass_tiles).  Not while the stream is being captured into a graph: a
 // launch's tag is a kernel argument, and every replay of a graph would repeat it.
-bool use_onepass(const splitzip_codec *codec, bool packed, uint64_t n_tiles, hipStream_t stream)
+bool use_onepass(const splitzip_codec *codec, bool packed, uint64_t n_tiles, hipStream_t stream, bool heavy)
 {
-    if (packed || n_tiles > codec->onepass_tiles.load(std::memory_order_relaxed))
+    const uint32_t limit = codec->onepass_tiles.load(std::memory_order_relaxed);
+    if (packed || limit == 0 || (n_tiles > limit && !heavy))
         return false;
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     return hipStreamIsCapturing(stream, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone;
@@ -1160,7 +1182,12 @@ int encode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
     Workspace *w = hold.get();
     const uint32_t n_tiles = tiles[n_seg];
     const uint32_t tile_shift = codec->elem == sz::kElemE5M2 ? sz::kE8EncTileShift : sz::kEncTileShift;
-    if (use_onepass(codec, packed, n_tiles, stream)) {
+    if ((rc = ensure_hint(w)) != SPLITZIP_OK)
+        return rc;
+    // an input whose first tile outgrew its slot last time is taken to be escape-heavy again:
+    // the launch sequences would move its escapes through scratch
+    const bool heavy = *reinterpret_cast<volatile uint32_t *>(w->hint) > slot_escapes(codec);
+    if (use_onepass(codec, packed, n_tiles, stream, heavy)) {
         // no scratch: only the workspace's one-pass state
         if ((rc = ensure_chain(w, n_tiles)) != SPLITZIP_OK)
             return rc;
@@ -1175,6 +1202,7 @@ int encode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
                         false, res);
         a.chain_status = w->chain;
         a.chain_cap = w->chain_cap;
+        a.first_tile_escapes = w->d_hint;
         hipError_t e = chain_next_tag(&w->chain_launches, w->chain, w->chain_cap, stream, &a.chain_tag);
         if (e == hipSuccess)
             e = run_encode_stages(codec, w, a, stream);
@@ -1205,6 +1233,7 @@ int encode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
     uint8_t *res = d_result ? reinterpret_cast<uint8_t *>(d_result) : w->result;
     set_encode_args(a, codec, n_seg, n_tiles, book, packed, w->scratch, lay, w->ovf_ctr, ovf_cap,
                     private_ovf, res);
+    a.first_tile_escapes = w->d_hint;
     const hipError_t e = run_encode_stages(codec, w, a, stream);
     if (e != hipSuccess) {
         // a launch that did not run to its end may leave the overflow counter set
@@ -1316,7 +1345,7 @@ int splitzip_encode_noalloc(splitzip_codec *codec, uint32_t n_seg, const splitzi
         }
         // a one-pass call needs no scratch besides its state at the end of the array
         hipStream_t stream = static_cast<hipStream_t>(stream_);
-        const bool onepass = use_onepass(codec, false, n_tiles, stream) && n_tiles <= kNoAllocChainTiles;
+        const bool onepass = use_onepass(codec, false, n_tiles, stream, false) && n_tiles <= kNoAllocChainTiles;
         if (cap_over && !onepass)
             return fail(SPLITZIP_E_INVALID, "escape capacities exceed the allocation-free scratch");
         const auto up = [](uint64_t x) { return (x + 255) & ~uint64_t(255); };

@@ -125,7 +125,7 @@ constexpr uint32_t kStashEscapes = 8192;
 constexpr uint32_t kStashChunks = kEncTileWords / 16;
 // byte offset of the positions in the stash: the copy out reads 16 bytes before each array
 constexpr uint32_t kStashPosAt = 16;
-constexpr uint32_t kE8StashEscapes = 8192;
+constexpr uint32_t kE8StashEscapes = 8192;            // a quarter of an E5M2 tile's 32768 bytes
 constexpr uint32_t kE8StashChunks = (1u << kE8EncTileShift) / 16;
 static_assert(kChainCountMask >= (1ull << 38), "a segment's escape count fits the status word");
 
@@ -219,6 +219,9 @@ struct EncodeArgs {
     uint64_t *chain_status;
     uint32_t chain_cap;
     uint32_t chain_tag;
+    // optional, host memory mapped for the device: the call's first tile stores its escape
+    // count there (the host picks the next call's launch sequence with it)
+    uint32_t *first_tile_escapes;
 };
 
 struct DecodeArgs {

@@ -208,6 +208,9 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
     __shared__ uint32_t s_stage[kChain && kStashWords > kStageWords ? kStashWords : kStageWords];
     // one-pass build: for each 8-bit escape mask, the indices of its set bits, 4 bits each
     __shared__ uint32_t s_bitpos[kChain ? 256 : 1];
+    __shared__ uint32_t s_ready;        // one-pass build: 2 when wave 0 has put the tile's offset in
+                                        // s_before and copied the stash out
+    __shared__ uint64_t s_before;
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = lane_id();
@@ -290,100 +293,131 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
     uint32_t tile_total;
     uint32_t wave_end;
     tile_escape_ranks<kEncGroups>(counts, lane, wave, s_wave_total, rank, tile_total, wave_end);
+    if (a.first_tile_escapes && t == 0 && tid == 0)
+        __hip_atomic_store(a.first_tile_escapes, tile_total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 
-    if (kChain && tile_total <= kStashEscapes) {
-        // one pass, early release: the escapes (final u16 position, exponent byte, at their
-        // ranks) and the chunk starts' ranks wait in LDS; waves 1..3 end, and wave 0 waits for
-        // the tile's escape offset and writes them to their final places.
+    if (kChain) {
+        // one pass, early release: the escapes of rank below kStashEscapes (every escape of a
+        // tile with at most that many) wait in LDS with their final u16 position and exponent
+        // byte, and the chunk starts' ranks with them.  Waves whose escapes all fit end;
+        // wave 0 (whose escapes always fit) waits for the tile's escape offset and writes
+        // them to their final places; a wave with escapes past the stash gets the offset
+        // from wave 0 through LDS and writes those itself.
         uint8_t *lds = reinterpret_cast<uint8_t *>(s_stage);
         uint16_t *s_pos = reinterpret_cast<uint16_t *>(lds + kStashPosAt);
         uint8_t *s_exp = lds + kStashExpAt;
         uint16_t *s_start = reinterpret_cast<uint16_t *>(s_exp + kStashEscapes);
         const uint32_t first = segment_first_tile(a, s);
         const bool last = t + 1 == segment_end_tile(a, s);        // loaded before the waits below
-        if (tid == 0)
+        if (tid == 0) {
             chain_publish(a, t, chain_word(tag, t > first ? kChainAggregate : kChainPrefix, tile_total));
+            s_ready = 0;
+        }
         // wave 0 issues the look-back's first loads now; they return while the escapes go to LDS
         uint64_t w[kChainRows];
         if (wave == 0 && t > first)
             chain_load<kChainRows>(a, t - 1, first, lane, w);
         const uint32_t cm = (uint32_t)cmask;
+        // the lane's escapes of rank lo .. hi - 1 to LDS at rank - lo: a lane's escapes of
+        // group j have ranks rank[j], rank[j] + 1, ...; the i-th goes in step i, its word index
+        // from the table of set bits
+        auto stash = [&](uint32_t lo, uint32_t hi) {
 #pragma unroll
-        for (int j = 0; j < kEncGroups; ++j) {
-            const uint32_t r0 = rank[j];
-            const uint32_t p0 = (uint32_t)(g0[j] - base);
-            if (g0[j] < n && (g0[j] & cmask) == 0)
-                s_start[p0 >> a.log2_chunk] = (uint16_t)r0;
-            const uint32_t z = flags[j];
-            if (z) {
-                // the lane's escapes go to ranks r0, r0 + 1, ...: the i-th in step i, its word
-                // index from the table of set bits
-                const uint32_t elo = perm(v[j].y >> 7, v[j].x >> 7, 0x06040200u);   // exponents, words 0..3
-                const uint32_t ehi = perm(v[j].w >> 7, v[j].z >> 7, 0x06040200u);   // words 4..7
-                const uint32_t f = (((z >> 4) & 0x03030303u) * 0x01041040u) >> 24;   // bit k: word k escapes
-                const uint32_t cnt = __popc(f);
-                const uint32_t ks = s_bitpos[f];
-                const uint32_t q0 = (uint32_t)g0[j];
+            for (int j = 0; j < kEncGroups; ++j) {
+                const uint32_t r0 = rank[j];
+                const uint32_t z = flags[j];
+                if (z && r0 < hi && r0 + 8u > lo) {
+                    const uint32_t elo = perm(v[j].y >> 7, v[j].x >> 7, 0x06040200u);   // exponents, words 0..3
+                    const uint32_t ehi = perm(v[j].w >> 7, v[j].z >> 7, 0x06040200u);   // words 4..7
+                    const uint32_t f = (((z >> 4) & 0x03030303u) * 0x01041040u) >> 24;   // bit k: word k escapes
+                    const uint32_t cnt = __popc(f);
+                    const uint32_t ks = s_bitpos[f];
+                    const uint32_t q0 = (uint32_t)g0[j];
 #pragma unroll
-                for (int i = 0; i < kGroupWords; ++i) {
-                    const bool act = (uint32_t)i < cnt;
-                    if (!__ballot(act))
-                        break;
-                    if (act) {
-                        const uint32_t k = (ks >> (4 * i)) & 15u;
-                        s_pos[r0 + i] = (uint16_t)((q0 + k) & cm);
-                        s_exp[r0 + i] = (uint8_t)perm(ehi, elo, k);
+                    for (int i = 0; i < kGroupWords; ++i) {
+                        if (!__ballot((uint32_t)i < cnt))
+                            break;
+                        const uint32_t r = r0 + i;
+                        if ((uint32_t)i < cnt && r >= lo && r < hi) {
+                            const uint32_t k = (ks >> (4 * i)) & 15u;
+                            s_pos[r - lo] = (uint16_t)((q0 + k) & cm);
+                            s_exp[r - lo] = (uint8_t)perm(ehi, elo, k);
+                        }
                     }
                 }
             }
+        };
+#pragma unroll
+        for (int j = 0; j < kEncGroups; ++j) {
+            const uint32_t p0 = (uint32_t)(g0[j] - base);
+            if (g0[j] < n && (g0[j] & cmask) == 0)
+                s_start[p0 >> a.log2_chunk] = (uint16_t)rank[j];
         }
+        stash(0, kStashEscapes);
         __syncthreads();
-        if (wave != 0)
+        const bool past = wave_end > kStashEscapes;                 // uniform in the wave
+        if (wave != 0 && !past)
             return;
-        const uint64_t before = t > first ? chain_lookback<kChainRows>(a, tag, t, first, lane, w) : 0ull;
-        if (lane == 0) {
-            if (t > first)
-                chain_publish(a, t, chain_word(tag, kChainPrefix, before + tile_total));
-            if (last) {
-                chunk_off[(n + cmask) >> a.log2_chunk] = before + tile_total;
-                a.seg_escapes[s] = before + tile_total;
+        if (wave == 0) {
+            const uint64_t before = t > first ? chain_lookback<kChainRows>(a, tag, t, first, lane, w) : 0ull;
+            if (lane == 0) {
+                if (t > first)
+                    chain_publish(a, t, chain_word(tag, kChainPrefix, before + tile_total));
+                if (last) {
+                    chunk_off[(n + cmask) >> a.log2_chunk] = before + tile_total;
+                    a.seg_escapes[s] = before + tile_total;
+                }
+                if (tile_total > kStashEscapes)
+                    s_before = before;
             }
+            const uint64_t tile_end = base + kEncTileWords < n ? base + kEncTileWords : n;
+            const uint32_t starts = a.log2_chunk <= (uint32_t)kEncTileShift
+                                  ? (uint32_t)((tile_end - base + cmask) >> a.log2_chunk)
+                                  : ((base & cmask) == 0 ? 1u : 0u);
+            SZ_GLOBAL uint64_t *co = chunk_off + (base >> a.log2_chunk);
+            for (uint32_t i = lane; i < starts; i += 64)
+                co[i] = before + s_start[i];
+            const uint64_t left = sd.esc > before && sd.esc_exp ? sd.esc - before : 0;
+            uint32_t ne = left < tile_total ? (uint32_t)left : tile_total;
+            ne = ne < kStashEscapes ? ne : kStashEscapes;
+            if (ne) {
+                stash_copy<2>(as_global(sd.esc_pos + before), s_pos, ne, lane);
+                stash_copy<1>(as_global(sd.esc_exp + before), s_exp, ne, lane);
+            }
+            if (tile_total > kStashEscapes && lane == 0)      // the stash is free again
+                __hip_atomic_store(&s_ready, 2u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            return;
         }
-        const uint64_t tile_end = base + kEncTileWords < n ? base + kEncTileWords : n;
-        const uint32_t starts = a.log2_chunk <= (uint32_t)kEncTileShift
-                              ? (uint32_t)((tile_end - base + cmask) >> a.log2_chunk)
-                              : ((base & cmask) == 0 ? 1u : 0u);
-        SZ_GLOBAL uint64_t *co = chunk_off + (base >> a.log2_chunk);
-        for (uint32_t i = lane; i < starts; i += 64)
-            co[i] = before + s_start[i];
+        // a wave with escapes past the stash (a tile has at most twice as many): once wave 0
+        // has copied the stash out (a bounded wait), the wave puts its own escapes of rank
+        // kStashEscapes and up into it, at rank - kStashEscapes, and copies that range out
+        uint32_t polls = 0;
+        while (__hip_atomic_load(&s_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 2u) {
+            if (++polls > kChainSpinMax) {
+                if (lane == 0)
+                    atomicOr(a.err, kErrChainStall);
+                return;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        static_assert(2 * kStashEscapes >= kEncTileWords, "two rounds of the stash hold a tile");
+        const uint64_t sb = s_before;
+        const uint64_t before = uniform_u64(sb);
         const uint64_t left = sd.esc > before && sd.esc_exp ? sd.esc - before : 0;
-        const uint32_t ne = left < tile_total ? (uint32_t)left : tile_total;
-        if (ne) {
-            stash_copy<2>(as_global(sd.esc_pos + before), s_pos, ne, lane);
-            stash_copy<1>(as_global(sd.esc_exp + before), s_exp, ne, lane);
-        }
+        const uint32_t wave_first = (uint32_t)__builtin_amdgcn_readfirstlane(rank[0]);   // lane 0's group 0
+        const uint32_t lo = wave_first > kStashEscapes ? wave_first : kStashEscapes;
+        const uint32_t hi = (uint64_t)wave_end < left ? wave_end : (uint32_t)left;
+        if (hi <= lo)
+            return;
+        stash(kStashEscapes, 2 * kStashEscapes);
+        stash_copy<2>(as_global(sd.esc_pos + before + lo), s_pos + (lo - kStashEscapes), hi - lo, lane);
+        stash_copy<1>(as_global(sd.esc_exp + before + lo), s_exp + (lo - kStashEscapes), hi - lo, lane);
         return;
     }
 
-    // where the tile's escapes go: its slot, or a range of the overflow area; in the one-pass
-    // build their final places, after the escapes of the segment's earlier tiles (at most
-    // `room` of them, the escape capacity left).  A segment's last tile also writes E.
-    uint64_t room = 0, prefix = 0;
-    uint32_t *dst = nullptr;
-    SZ_GLOBAL uint16_t *fpos = nullptr;
-    SZ_GLOBAL uint8_t *fexp = nullptr;
-    if (kChain) {
-        prefix = chain_prefix(a, tag, t, segment_first_tile(a, s), tile_total, tid, lane, &s_ovf);
-        room = sd.esc > prefix && sd.esc_exp ? sd.esc - prefix : 0;
-        fpos = as_global(sd.esc_pos + (room ? prefix : 0));
-        fexp = as_global(sd.esc_exp + (room ? prefix : 0));
-        if (tid == 0 && t + 1 == segment_end_tile(a, s)) {
-            chunk_off[(n + cmask) >> a.log2_chunk] = prefix + tile_total;
-            a.seg_escapes[s] = prefix + tile_total;
-        }
-    } else {
-        dst = tile_escape_dest(a, t, tile_total, tid, &s_ovf, room);
-    }
+    // where the tile's escapes go: its slot, or a range of the overflow area
+    uint64_t room = 0;
+    uint32_t *dst = tile_escape_dest(a, t, tile_total, tid, &s_ovf, room);
 
     // escapes: (position inside the tile, exponent); tile-local chunk offsets.  A wave's
     // escapes of one group have consecutive ranks.  When there are more than kStageMin of
@@ -396,7 +430,7 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
     for (int j = 0; j < kEncGroups; ++j) {
         const uint32_t r0 = rank[j];
         if (g0[j] < n && (g0[j] & cmask) == 0)
-            chunk_off[g0[j] >> a.log2_chunk] = prefix + r0;
+            chunk_off[g0[j] >> a.log2_chunk] = r0;
         const uint32_t z = flags[j];
         const uint32_t w0 = __builtin_amdgcn_readfirstlane(r0);
         const uint32_t wcnt = (j + 1 < kEncGroups ? __builtin_amdgcn_readfirstlane(rank[j + 1]) : wave_end) - w0;
@@ -421,14 +455,8 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
                 uint32_t zz = z, r = r0;
                 do {
                     const uint32_t k = flag_bit_to_word((uint32_t)__builtin_ctz(zz));
-                    if (r < room) {
-                        if (kChain) {
-                            fpos[r] = (uint16_t)((g0[j] + k) & cmask);
-                            fexp[r] = (uint8_t)(ex8 >> (8 * k));
-                        } else {
-                            gdst[r] = (p0 + k) | ((uint32_t)(uint8_t)(ex8 >> (8 * k)) << 16);
-                        }
-                    }
+                    if (r < room)
+                        gdst[r] = (p0 + k) | ((uint32_t)(uint8_t)(ex8 >> (8 * k)) << 16);
                     ++r;
                     zz &= zz - 1;
                 } while (zz);
@@ -437,15 +465,8 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
         if (staged) {
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             for (uint32_t i = lane; i < wcnt; i += 64) {
-                if (w0 + i < room) {
-                    const uint32_t e = stage[i];
-                    if (kChain) {
-                        fpos[w0 + i] = (uint16_t)((base + (e & 0xFFFFu)) & cmask);
-                        fexp[w0 + i] = (uint8_t)(e >> 16);
-                    } else {
-                        gdst[w0 + i] = e;
-                    }
-                }
+                if (w0 + i < room)
+                    gdst[w0 + i] = stage[i];
             }
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         }

@@ -272,6 +272,53 @@ def test_onepass_launch_counts_and_limit():
     t8.assert_same_stream(c8, e8, x8)
 
 
+def test_onepass_for_escape_heavy_input_past_the_limit():
+    """A call over the one-pass limit runs the launch sequences; after an encode on the same
+    stream whose first tile had more escapes than a slot holds, it runs in one launch (same
+    bytes); with the one-pass launch off it never does; a call with few escapes in its first
+    tile turns the rule off again.  E5M2 likewise."""
+    n = 6 * TILE - 7
+    x_np = workloads.mixed_words(n, 31, wide_fraction=0.3)
+    x = dev(x_np)
+    codec = codec_for(workloads.normal_words(30_000, 10), 1024)
+    codec.set_onepass_tiles(4)                      # the call has 6 tiles
+    codec.profile(True)
+    first = codec.encode(x, escape_capacity=n)      # a new workspace: no hint yet
+    second = codec.encode(x, escape_capacity=n)
+    t = codec.kernel_times(reset=True)
+    assert t["encode_onepass"][1] == 1 and t["encode_pack"][1] == 1
+    for name in ("sm", "codes", "chunk_off", "esc_pos", "esc_exp"):
+        assert torch.equal(getattr(first, name), getattr(second, name)), name
+    assert_same_stream(codec, second, x_np)
+    codec.set_onepass_tiles(0)
+    codec.encode(x, escape_capacity=n)
+    t = codec.kernel_times(reset=True)
+    assert t["encode_onepass"][1] == 0 and t["encode_pack"][1] == 1
+    codec.set_onepass_tiles(4)
+    y_np = workloads.normal_words(n, 32)
+    y = dev(y_np)
+    codec.encode(y, escape_capacity=n)              # after the heavy call: one launch
+    last = codec.encode(y, escape_capacity=n)       # after a light one: the launch sequences
+    t = codec.kernel_times(reset=True)
+    codec.profile(False)
+    assert t["encode_onepass"][1] == 1 and t["encode_pack"][1] == 1
+    assert_same_stream(codec, last, y_np)
+
+    n8 = 6 * TILE8 - 5
+    x8 = workloads.e5m2_mixed(n8, 57, wide_fraction=0.3)
+    c8 = t8.codec_for(workloads.e5m2_normal(50_000, 6), 1024)
+    c8.set_onepass_tiles(4)
+    c8.profile(True)
+    e1 = c8.encode(t8.dev8(x8), escape_capacity=n8)
+    e2 = c8.encode(t8.dev8(x8), escape_capacity=n8)
+    t = c8.kernel_times(reset=True)
+    c8.profile(False)
+    assert t["encode_onepass"][1] == 1 and t["encode_pack"][1] == 1
+    for name in ("sm", "codes", "chunk_off", "esc_pos", "esc_exp"):
+        assert torch.equal(getattr(e1, name), getattr(e2, name)), name
+    t8.assert_same_stream(c8, e2, x8)
+
+
 @pytest.mark.parametrize("wide", [0.0, 0.02, 1.0])
 def test_onepass_many_tiles_and_repeats(wide):
     """1100 tiles (more than one round of the GPU's workgroups, so look-backs find earlier
