@@ -150,6 +150,7 @@ struct Workspace {
     uint8_t *h_result = nullptr;      // pinned mirror of `result`
     uint32_t *hint = nullptr;         // host memory mapped for the device: the escapes of the
     uint32_t *d_hint = nullptr;       // last encode's first tile (d_hint: its device address)
+    bool hint_failed = false;         // no mapped host memory for it: calls go on without
     Staging staging[kStagingSlots];
     int next_slot = 0;
     // profiling
@@ -525,22 +526,27 @@ int ensure_chain(Workspace *w, uint32_t n_tiles)
     return SPLITZIP_OK;
 }
 
-// The workspace's hint word (see Workspace::hint), 0 when new.
-int ensure_hint(Workspace *w)
+// The workspace's hint word (see Workspace::hint), 0 when new.  Only a hint: when the mapped
+// host memory cannot be had, calls go on without it (the size rule alone picks the launches).
+void ensure_hint(Workspace *w)
 {
-    if (w->hint)
-        return SPLITZIP_OK;
+    if (w->hint || w->hint_failed)
+        return;
     void *h = nullptr, *d = nullptr;
-    SZ_HIP(hipHostMalloc(&h, 64, hipHostMallocMapped | hipHostMallocCoherent), "hipHostMalloc(hint)");
+    if (hipHostMalloc(&h, 64, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess) {
+        (void)hipGetLastError();
+        w->hint_failed = true;
+        return;
+    }
     std::memset(h, 0, 64);
-    const hipError_t e = hipHostGetDevicePointer(&d, h, 0);
-    if (e != hipSuccess) {
+    if (hipHostGetDevicePointer(&d, h, 0) != hipSuccess) {
+        (void)hipGetLastError();
         (void)hipHostFree(h);
-        return fail_hip(e, "hipHostGetDevicePointer(hint)");
+        w->hint_failed = true;
+        return;
     }
     w->hint = static_cast<uint32_t *>(h);
     w->d_hint = static_cast<uint32_t *>(d);
-    return SPLITZIP_OK;
 }
 
 // The tag of the next one-pass launch on a state of cap status words, counted in *launches;
@@ -1182,11 +1188,10 @@ int encode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
     Workspace *w = hold.get();
     const uint32_t n_tiles = tiles[n_seg];
     const uint32_t tile_shift = codec->elem == sz::kElemE5M2 ? sz::kE8EncTileShift : sz::kEncTileShift;
-    if ((rc = ensure_hint(w)) != SPLITZIP_OK)
-        return rc;
+    ensure_hint(w);
     // an input whose first tile outgrew its slot last time is taken to be escape-heavy again:
     // the launch sequences would move its escapes through scratch
-    const bool heavy = *reinterpret_cast<volatile uint32_t *>(w->hint) > slot_escapes(codec);
+    const bool heavy = w->hint && *reinterpret_cast<volatile uint32_t *>(w->hint) > slot_escapes(codec);
     if (use_onepass(codec, packed, n_tiles, stream, heavy)) {
         // no scratch: only the workspace's one-pass state
         if ((rc = ensure_chain(w, n_tiles)) != SPLITZIP_OK)
