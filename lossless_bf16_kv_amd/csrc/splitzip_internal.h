@@ -117,10 +117,11 @@ constexpr int kChainRows = 1;
 // Packed 16 to a 128-byte line, the words that hundreds of waiting waves poll and that their
 // tiles write queued on a few lines (4096 tiles at 30 % escapes: 86 against 80 us).
 constexpr uint32_t kChainStride = 4;
-// One-pass encode, early release: a tile with at most kStashEscapes escapes keeps them (u16
+// One-pass encode, early release: a tile keeps its escapes of rank below kStashEscapes (u16
 // position, u8 exponent) and its chunk starts' escape ranks (u16, at most one per 16 words)
-// in LDS; waves 1..3 then end and free their registers while wave 0 waits for the tile's
-// escape offset and writes them.  Tiles with more escapes wait with all four waves.
+// in LDS; waves whose escapes all fit end and free their registers while wave 0 waits for
+// the tile's escape offset and writes them; a wave with escapes past the stash waits too and
+// sends those through the stash in a second round.
 constexpr uint32_t kStashEscapes = 8192;
 constexpr uint32_t kStashChunks = kEncTileWords / 16;
 // byte offset of the positions in the stash: the copy out reads 16 bytes before each array

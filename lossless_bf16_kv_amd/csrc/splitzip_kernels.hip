@@ -159,6 +159,11 @@ hipError_t launch_histogram(const HistArgs &a, hipStream_t stream)
 // with one launch, finish (one workgroup per tile), which adds up the earlier tiles' escape
 // counts itself: on inputs of a few MiB every launch costs a few microseconds of the GPU's
 // time, more than the data takes to move.
+// The one-pass build of pack (kChain) does it all in one launch: each tile publishes its
+// escape count in a status word, finds the escapes of the earlier tiles by a decoupled
+// look-back over theirs, and writes its escapes, chunk offsets and (as a segment's last tile)
+// E to their final places, staging the escapes in LDS so that most of its waves can end
+// before the look-back does.
 // ======================================================================================
 
 // Split one group of 8 words (4 dwords, word 2m in the low half of dword m).
