@@ -638,78 +638,119 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
                 if (s_off[ci] > s_off[ci + 1] || s_off[ci + 1] - s_off[ci] > (n - cs < C ? n - cs : C))
                     bad |= kErrBadOffsets;
             }
-            // chunk of escape jj: the last c with s_off[c] <= jj.  In the large-call build a
-            // tile of at most kFew chunks (chunk size 1024 or more) counts the tile-relative
-            // chunk starts at or below each escape's rank: the starts of chunks 1..kFew, two
-            // per dword (absent ones 0x7FFF), are subtracted from the rank with packed 16-bit
-            // subtractions (ranks and starts are below 2^14, so a half's sign bit says rank <
-            // start), and the sign bits are counted.  Otherwise a binary search in LDS
-            // (three or more dependent LDS reads per escape).
-            constexpr int kFew = 16;
-            const bool few = kLarge && nc <= (uint64_t)kFew;       // uniform
-            static_assert(kTile < (1 << 15), "tile ranks fit a signed 16-bit half");
-            uint32_t starts[kFew / 2];
-#pragma unroll
-            for (int m = 0; m < kFew / 2; ++m) {
-                uint32_t h[2];
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int c = 2 * m + 1 + i;
-                    h[i] = (few && (uint64_t)c < nc) ? (uint32_t)(s_off[c] - j0) : 0x7FFFu;
-                    h[i] = h[i] < 0x7FFFu ? h[i] : 0x7FFFu;
-                }
-                starts[m] = __builtin_amdgcn_readfirstlane(h[0] | (h[1] << 16));
-            }
-            // 32-bit arithmetic relative to the tile: escape rank r in [0, cnt), chunk starts
-            // lo << log2c inside the tile (a chunk is at most a tile here), cnt <= valid
-            const uint32_t cnt = (uint32_t)(j1 - j0);
-            const SZ_GLOBAL uint16_t *tpos = gpos + j0;
-            const SZ_GLOBAL uint8_t *texp = gexp + j0;
-            const uint32_t tvalid = (uint32_t)valid;
-            for (uint32_t rb = tid; rb < cnt; rb += kPatch * kThreads) {
-                uint32_t pos[kPatch], ev[kPatch];
-#pragma unroll
-                for (int k = 0; k < kPatch; ++k) {
-                    const uint32_t r = rb + (uint32_t)k * kThreads;
-                    const uint32_t rc = r < cnt ? r : cnt - 1;
-                    pos[k] = tpos[rc];
-                    ev[k] = texp[rc];
-                }
-#pragma unroll
-                for (int k = 0; k < kPatch; ++k) {
-                    const uint32_t r = rb + (uint32_t)k * kThreads;
-                    if (r >= cnt)
+            if (j1 - j0 > (uint64_t)kThreads) {
+                // more escapes than threads: each chunk's escapes [s_off[c], s_off[c + 1]) are
+                // patched by `per` threads (as in the BF16 decode), so an escape's chunk is known
+                // without a search; a chunk whose offsets are out of order, too long or outside
+                // the tile's range (flagged above) is skipped
+                const uint32_t lgc = nc > 1 ? 32u - (uint32_t)__builtin_clz((uint32_t)nc - 1u) : 0u;   // ceil log2(nc)
+                const uint32_t pshift = lgc >= 8u ? 0u : 8u - lgc;
+                const uint32_t per = 1u << pshift;
+                const uint32_t sub = tid & (per - 1u);
+                const uint32_t tvalid = (uint32_t)valid;
+                for (uint32_t c = tid >> pshift; c < (uint32_t)nc; c += kThreads >> pshift) {
+                    const uint64_t e0 = s_off[c], e1 = s_off[c + 1];
+                    const uint32_t cs = c << log2c;
+                    const uint32_t clen = tvalid - cs < (uint32_t)C ? tvalid - cs : (uint32_t)C;
+                    if (e0 > e1 || e1 - e0 > clen || e0 < j0 || e1 > j1)
                         continue;
-                    uint32_t lo = 0;
-                    if (few) {
-                        typedef short s16x2 __attribute__((ext_vector_type(2)));
-                        const s16x2 rr = {(short)r, (short)r};
-                        uint32_t below = 0;             // chunk starts above r
+                    const uint32_t m = (uint32_t)(e1 - e0);
+                    const SZ_GLOBAL uint16_t *cpos = gpos + e0;
+                    const SZ_GLOBAL uint8_t *cexp = gexp + e0;
+                    for (uint32_t rb = sub; rb < m; rb += kPatch * per) {
+                        uint32_t pos[kPatch], ev[kPatch];
 #pragma unroll
-                        for (int m = 0; m < kFew / 2; ++m) {
-                            const s16x2 st = __builtin_bit_cast(s16x2, starts[m]);
-                            const uint32_t d = __builtin_bit_cast(uint32_t, (s16x2)(rr - st));
-                            below += (uint32_t)__popc(d & 0x80008000u);
+                        for (int k = 0; k < kPatch; ++k) {
+                            const uint32_t r = rb + (uint32_t)k * per;
+                            const uint32_t rc = r < m ? r : m - 1u;
+                            pos[k] = cpos[rc];
+                            ev[k] = cexp[rc];
                         }
-                        lo = kFew - below;              // halves hold chunks 1 .. kFew
-                        lo = lo < (uint32_t)nc ? lo : (uint32_t)nc - 1u;
-                    } else {
-                        const uint64_t jj = j0 + r;
-                        uint32_t hi = (uint32_t)nc;          // s_off[lo] <= jj < s_off[hi]
-                        while (hi - lo > 1) {
-                            const uint32_t mid = (lo + hi) >> 1;
-                            if (s_off[mid] <= jj)
-                                lo = mid;
+#pragma unroll
+                        for (int k = 0; k < kPatch; ++k) {
+                            if (rb + (uint32_t)k * per >= m)
+                                continue;
+                            if (pos[k] < clen && ev[k] <= 31u)
+                                bytes[cs + pos[k]] = (uint8_t)(ev[k] << 2);
                             else
-                                hi = mid;
+                                bad |= pos[k] >= clen ? kErrBadPosition : kErrBadExponent;
                         }
                     }
-                    const uint32_t cs = lo << log2c;
-                    const uint32_t clen = tvalid - cs < (uint32_t)C ? tvalid - cs : (uint32_t)C;
-                    if (pos[k] < clen && ev[k] <= 31u)
-                        bytes[cs + pos[k]] = (uint8_t)(ev[k] << 2);
-                    else
-                        bad |= pos[k] >= clen ? kErrBadPosition : kErrBadExponent;
+                }
+            } else {
+                // chunk of escape jj: the last c with s_off[c] <= jj.  In the large-call build a
+                // tile of at most kFew chunks (chunk size 1024 or more) counts the tile-relative
+                // chunk starts at or below each escape's rank: the starts of chunks 1..kFew, two
+                // per dword (absent ones 0x7FFF), are subtracted from the rank with packed 16-bit
+                // subtractions (ranks and starts are below 2^14, so a half's sign bit says rank <
+                // start), and the sign bits are counted.  Otherwise a binary search in LDS
+                // (three or more dependent LDS reads per escape).
+                constexpr int kFew = 16;
+                const bool few = kLarge && nc <= (uint64_t)kFew;       // uniform
+                static_assert(kTile < (1 << 15), "tile ranks fit a signed 16-bit half");
+                uint32_t starts[kFew / 2];
+#pragma unroll
+                for (int m = 0; m < kFew / 2; ++m) {
+                    uint32_t h[2];
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        const int c = 2 * m + 1 + i;
+                        h[i] = (few && (uint64_t)c < nc) ? (uint32_t)(s_off[c] - j0) : 0x7FFFu;
+                        h[i] = h[i] < 0x7FFFu ? h[i] : 0x7FFFu;
+                    }
+                    starts[m] = __builtin_amdgcn_readfirstlane(h[0] | (h[1] << 16));
+                }
+                // 32-bit arithmetic relative to the tile: escape rank r in [0, cnt), chunk starts
+                // lo << log2c inside the tile (a chunk is at most a tile here), cnt <= valid
+                const uint32_t cnt = (uint32_t)(j1 - j0);
+                const SZ_GLOBAL uint16_t *tpos = gpos + j0;
+                const SZ_GLOBAL uint8_t *texp = gexp + j0;
+                const uint32_t tvalid = (uint32_t)valid;
+                for (uint32_t rb = tid; rb < cnt; rb += kPatch * kThreads) {
+                    uint32_t pos[kPatch], ev[kPatch];
+#pragma unroll
+                    for (int k = 0; k < kPatch; ++k) {
+                        const uint32_t r = rb + (uint32_t)k * kThreads;
+                        const uint32_t rc = r < cnt ? r : cnt - 1;
+                        pos[k] = tpos[rc];
+                        ev[k] = texp[rc];
+                    }
+#pragma unroll
+                    for (int k = 0; k < kPatch; ++k) {
+                        const uint32_t r = rb + (uint32_t)k * kThreads;
+                        if (r >= cnt)
+                            continue;
+                        uint32_t lo = 0;
+                        if (few) {
+                            typedef short s16x2 __attribute__((ext_vector_type(2)));
+                            const s16x2 rr = {(short)r, (short)r};
+                            uint32_t below = 0;             // chunk starts above r
+#pragma unroll
+                            for (int m = 0; m < kFew / 2; ++m) {
+                                const s16x2 st = __builtin_bit_cast(s16x2, starts[m]);
+                                const uint32_t d = __builtin_bit_cast(uint32_t, (s16x2)(rr - st));
+                                below += (uint32_t)__popc(d & 0x80008000u);
+                            }
+                            lo = kFew - below;              // halves hold chunks 1 .. kFew
+                            lo = lo < (uint32_t)nc ? lo : (uint32_t)nc - 1u;
+                        } else {
+                            const uint64_t jj = j0 + r;
+                            uint32_t hi = (uint32_t)nc;          // s_off[lo] <= jj < s_off[hi]
+                            while (hi - lo > 1) {
+                                const uint32_t mid = (lo + hi) >> 1;
+                                if (s_off[mid] <= jj)
+                                    lo = mid;
+                                else
+                                    hi = mid;
+                            }
+                        }
+                        const uint32_t cs = lo << log2c;
+                        const uint32_t clen = tvalid - cs < (uint32_t)C ? tvalid - cs : (uint32_t)C;
+                        if (pos[k] < clen && ev[k] <= 31u)
+                            bytes[cs + pos[k]] = (uint8_t)(ev[k] << 2);
+                        else
+                            bad |= pos[k] >= clen ? kErrBadPosition : kErrBadExponent;
+                    }
                 }
             }
         } else {
