@@ -75,11 +75,13 @@ __device__ __forceinline__ void split_group32(const uint32_t (&x)[8], const uint
     flags = fl;
 }
 
-// kChain: the one-pass build (chained tiles), which writes the escapes to their final places.
+// kChain: the one-pass build (chained tiles of 2^kE8ChainTileShift elements), which writes the
+// escapes to their final places.
 template <bool kStage, bool kChain>
 __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const EncodeArgs a)
 {
-    constexpr int G = kE8EncGroups;
+    constexpr int G = kChain ? kE8ChainGroups : kE8EncGroups;
+    constexpr int kShift = kChain ? kE8ChainTileShift : kE8EncTileShift;
     __shared__ uint8_t s_lut[256];
     __shared__ uint32_t s_wave_total[kWaves];
     __shared__ uint64_t s_ovf;
@@ -89,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
     constexpr uint32_t kInWords = kWaves * 128 * 4, kStageWords = kWaves * 2048 / 2;
     constexpr uint32_t kStashExpAt = kStashPosAt + 2 * kE8StashEscapes + 16;
     constexpr uint32_t kStashWords = (kStashExpAt + kE8StashEscapes + 2 * kE8StashChunks + 3) / 4;
-    constexpr uint32_t kRawWords = kChain && kStashWords > kInWords + kStageWords ? kStashWords : kInWords + kStageWords;
+    constexpr uint32_t kRawWords = kChain ? (kStashWords > kInWords ? kStashWords : kInWords) : kInWords + kStageWords;
     __shared__ uint32_t s_raw[kRawWords];
     __shared__ uint32_t s_bitpos[kChain ? 256 : 1];   // one-pass build: set-bit indices of each byte
     __shared__ uint32_t s_ready;        // one-pass build: 2 when wave 0 has put the tile's offset in
@@ -121,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
         s_bitpos[tid & 255u] = e;
     }
     const uint64_t n = sd.n;
-    const uint64_t base = (uint64_t)(t - segment_first_tile(a, s)) << kE8EncTileShift;
+    const uint64_t base = (uint64_t)(t - segment_first_tile(a, s)) << kShift;
     const uint64_t cmask = (1ull << a.log2_chunk) - 1;
     const SZ_GLOBAL uint8_t *xb = as_global(reinterpret_cast<const uint8_t *>(sd.data));
     SZ_GLOBAL uint8_t *smb = as_global(sd.sm);
@@ -218,8 +220,9 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
     uint32_t tile_total;
     uint32_t wave_end;
     tile_escape_ranks<G>(counts, lane, wave, s_wave_total, rank, tile_total, wave_end);
-    if (a.first_tile_escapes && t == 0 && tid == 0)
-        __hip_atomic_store(a.first_tile_escapes, tile_total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (a.first_tile_escapes && t == 0 && tid == 0)   // scaled to a tile of the launch sequences
+        __hip_atomic_store(a.first_tile_escapes, tile_total << (kE8EncTileShift - kShift), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_SYSTEM);
 
     if (kChain) {
         // one pass, early release, as in the BF16 pack: the escapes of rank below
@@ -298,8 +301,8 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
                 if (tile_total > kE8StashEscapes)
                     s_before = before;
             }
-            const uint64_t tile_end = base + (1u << kE8EncTileShift) < n ? base + (1u << kE8EncTileShift) : n;
-            const uint32_t starts = a.log2_chunk <= (uint32_t)kE8EncTileShift
+            const uint64_t tile_end = base + (1u << kShift) < n ? base + (1u << kShift) : n;
+            const uint32_t starts = a.log2_chunk <= (uint32_t)kShift
                                   ? (uint32_t)((tile_end - base + cmask) >> a.log2_chunk)
                                   : ((base & cmask) == 0 ? 1u : 0u);
             SZ_GLOBAL uint64_t *co = chunk_off + (base >> a.log2_chunk);
@@ -317,9 +320,8 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
             return;
         }
         // a wave with escapes past the stash: once wave 0 has copied the stash out (a bounded
-        // wait), its escapes of rank kE8StashEscapes .. 2 kE8StashEscapes - 1 go through the
-        // stash at rank - kE8StashEscapes and out, and any of higher rank straight from its
-        // registers
+        // wait), its escapes of rank kE8StashEscapes and above (at most a tile's elements, two
+        // rounds of the stash) go through the stash at rank - kE8StashEscapes and out
         uint32_t polls = 0;
         while (__hip_atomic_load(&s_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 2u) {
             if (++polls > kChainSpinMax) {
@@ -340,31 +342,6 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
             stash(kE8StashEscapes, 2 * kE8StashEscapes);
             stash_copy<2>(as_global(sd.esc_pos + before + lo), s_pos + (lo - kE8StashEscapes), hi - lo, lane);
             stash_copy<1>(as_global(sd.esc_exp + before + lo), s_exp + (lo - kE8StashEscapes), hi - lo, lane);
-        }
-        if (wave_end <= 2 * kE8StashEscapes || left <= 2 * kE8StashEscapes)
-            return;
-        SZ_GLOBAL uint16_t *ep = as_global(sd.esc_pos + before);
-        SZ_GLOBAL uint8_t *ee = as_global(sd.esc_exp + before);
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-            if (flags[j] && rank[j] + (uint32_t)__popc(flags[j]) > 2 * kE8StashEscapes) {
-                uint32_t r = rank[j];
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    uint32_t z = flags[j] & e8_flag_mask(d);
-                    const uint64_t bytes8 = ((uint64_t)v[j][2 * d + 1] << 32) | v[j][2 * d];
-                    while (z) {
-                        const uint32_t b = (uint32_t)__builtin_ctz(z);
-                        const uint32_t k = 2u * (b >> 3) + (b & 1u);          // element 8d + k
-                        if (r >= 2 * kE8StashEscapes && r < left) {
-                            ep[r] = (uint16_t)((g0[j] + 8u * d + k) & cmask);
-                            ee[r] = (uint8_t)((uint32_t)(bytes8 >> (8 * k + 2)) & 0x1Fu);
-                        }
-                        ++r;
-                        z &= z - 1;
-                    }
-                }
-            }
         }
         return;
     }

@@ -749,6 +749,15 @@ uint64_t tile_elements(const splitzip_codec *c, bool encode)
     return encode ? sz::kEncTileWords : sz::kDecTileWords;
 }
 
+// log2 of the elements per pack tile: the one-pass encode of E5M2 bytes takes tiles half as
+// long as the launch sequences'.
+uint32_t pack_tile_shift(const splitzip_codec *c, bool onepass)
+{
+    if (c->elem == sz::kElemE5M2)
+        return onepass ? sz::kE8ChainTileShift : sz::kE8EncTileShift;
+    return sz::kEncTileShift;
+}
+
 // Canonical stream size of n elements with E escapes (0 for an invalid chunk size).
 uint64_t stream_bytes(uint32_t elem, uint64_t n, uint32_t chunk_size, uint64_t E)
 {
@@ -1093,18 +1102,19 @@ int splitzip_codec_info(const splitzip_codec *codec, uint8_t codebook[16], uint3
 namespace {
 
 // The call's shape, its codebook tables and the encode scratch arrays at `base` (laid out as
-// `lay`) into a.  res: the error word, then E per segment.
+// `lay`; NULL for a one-pass encode, which has no scratch and its own tile length) into a.
+// res: the error word, then E per segment.
 void set_encode_args(sz::EncodeArgs &a, const splitzip_codec *codec, uint32_t n_seg, uint32_t n_tiles,
                      int64_t book, bool packed, uint8_t *base, const EncodeScratch &lay,
                      unsigned long long *ovf_ctr, uint64_t ovf_cap, bool private_ovf, uint8_t *res)
 {
-    const uint32_t tile_shift = codec->elem == sz::kElemE5M2 ? sz::kE8EncTileShift : sz::kEncTileShift;
+    const uint32_t tile_shift = pack_tile_shift(codec, base == nullptr);
     // one book for the whole call: its LUT directly; several: the table, indexed per segment
     a.lut = codec->d_lut + 256 * (book < 0 ? 0 : book);
     a.multi_book = book < 0;
     a.cbs = codec->d_cbs;
     a.packed = packed;
-    if (base) {     // none for a one-pass encode
+    if (base) {     // none for a one-pass encode (base NULL)
         a.seg_total = reinterpret_cast<uint64_t *>(base + lay.seg_total);
         a.tile_count = reinterpret_cast<uint32_t *>(base + lay.tile_count);
         a.tile_ovf = reinterpret_cast<uint64_t *>(base + lay.tile_ovf);
@@ -1129,8 +1139,30 @@ void set_encode_args(sz::EncodeArgs &a, const splitzip_codec *codec, uint32_t n_
     a.stage = n_tiles > codec->stage_tiles.load(std::memory_order_relaxed) ? 1u : 0u;
 }
 
-// Whether an encode of n_tiles tiles on `stream` runs in one pass (see
-// splitzip_set_onepass_tiles).  Not while the stream is being captured into a graph: a
+// Tile starts of a one-pass encode of the segments `desc` into `out` (the launch sequences'
+// `tiles` when the tile lengths agree); false when the call has too many such tiles.
+bool onepass_tiles(const splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
+                   const std::vector<uint32_t> &tiles, std::vector<uint32_t> &out)
+{
+    const uint32_t shift = pack_tile_shift(codec, true);
+    if (shift == pack_tile_shift(codec, false)) {
+        out = tiles;
+        return true;
+    }
+    out.resize(desc.size() + 1);
+    uint64_t total = 0;
+    for (size_t i = 0; i < desc.size(); ++i) {
+        out[i] = (uint32_t)total;
+        total += segment_tiles(desc[i].n, 1ull << shift);
+        if (total > 0xFFFFFFF0ull)
+            return false;
+    }
+    out[desc.size()] = (uint32_t)total;
+    return true;
+}
+
+// Whether an encode of n_tiles tiles (of the launch sequences) on `stream` runs in one pass
+// (see splitzip_set_onepass_tiles).  Not while the stream is being captured into a graph: a
 // launch's tag is a kernel argument, and every replay of a graph would repeat it.
 bool use_onepass(const splitzip_codec *codec, bool packed, uint64_t n_tiles, hipStream_t stream, bool heavy)
 {
@@ -1187,23 +1219,29 @@ int encode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
         return rc;
     Workspace *w = hold.get();
     const uint32_t n_tiles = tiles[n_seg];
-    const uint32_t tile_shift = codec->elem == sz::kElemE5M2 ? sz::kE8EncTileShift : sz::kEncTileShift;
+    const uint32_t tile_shift = pack_tile_shift(codec, false);
     ensure_hint(w);
     // an input whose first tile outgrew its slot last time is taken to be escape-heavy again:
     // the launch sequences would move its escapes through scratch
     const bool heavy = w->hint && *reinterpret_cast<volatile uint32_t *>(w->hint) > slot_escapes(codec);
-    if (use_onepass(codec, packed, n_tiles, stream, heavy)) {
+    // the one-pass tiles (shorter for E5M2)
+    std::vector<uint32_t> chain_tiles;
+    const bool onepass = use_onepass(codec, packed, n_tiles, stream, heavy) &&
+                         onepass_tiles(codec, desc, tiles, chain_tiles);
+    if (onepass) {
         // no scratch: only the workspace's one-pass state
-        if ((rc = ensure_chain(w, n_tiles)) != SPLITZIP_OK)
+        const uint32_t n_chain = chain_tiles[n_seg];
+        if ((rc = ensure_chain(w, n_chain)) != SPLITZIP_OK)
             return rc;
         if (!d_result && (rc = ensure_result(w, n_seg)) != SPLITZIP_OK)
             return rc;
         sz::EncodeArgs a{};
         a.seg0 = desc[0];
-        if (n_seg > 1 && (rc = stage_descriptors(w, desc, tiles, &a.segs, &a.tile_start, &a.seg_at)) != SPLITZIP_OK)
+        if (n_seg > 1 &&
+            (rc = stage_descriptors(w, desc, chain_tiles, &a.segs, &a.tile_start, &a.seg_at)) != SPLITZIP_OK)
             return rc;
         uint8_t *res = d_result ? reinterpret_cast<uint8_t *>(d_result) : w->result;
-        set_encode_args(a, codec, n_seg, n_tiles, book, packed, nullptr, EncodeScratch(0, 0, 0, 0), nullptr, 0,
+        set_encode_args(a, codec, n_seg, n_chain, book, packed, nullptr, EncodeScratch(0, 0, 0, 0), nullptr, 0,
                         false, res);
         a.chain_status = w->chain;
         a.chain_cap = w->chain_cap;
@@ -1327,8 +1365,10 @@ int splitzip_encode_noalloc(splitzip_codec *codec, uint32_t n_seg, const splitzi
         if (codec->device < 0 || codec->device >= kNoAllocDevices)
             return fail(SPLITZIP_E_INVALID, "device %d out of range", codec->device);
         // every segment checked, and the scratch the call needs, before anything is enqueued
-        const uint64_t tile_words = tile_elements(codec, true);
-        uint64_t n_tiles = 0, ovf_cap = 1;
+        // tiles of the launch sequences, and of a one-pass encode (shorter for E5M2)
+        const uint64_t seq_words = tile_elements(codec, true);
+        const uint64_t chain_words = 1ull << pack_tile_shift(codec, true);
+        uint64_t n_tiles = 0, n_chain = 0, ovf_cap = 1;
         bool cap_over = false;
         int64_t book = segs[0].book;
         sz::SegDesc d0{};
@@ -1338,7 +1378,8 @@ int splitzip_encode_noalloc(splitzip_codec *codec, uint32_t n_seg, const splitzi
                 return rc;
             if (i == 0)
                 d0 = d;
-            n_tiles += segment_tiles(segs[i].n, tile_words);
+            n_tiles += segment_tiles(segs[i].n, seq_words);
+            n_chain += segment_tiles(segs[i].n, chain_words);
             if (n_tiles > 0xFFFFFFF0ull)
                 return fail(SPLITZIP_E_INVALID, "too many tiles in one call");
             // (the overflow area of the launch sequences is as long as the capacities)
@@ -1350,7 +1391,10 @@ int splitzip_encode_noalloc(splitzip_codec *codec, uint32_t n_seg, const splitzi
         }
         // a one-pass call needs no scratch besides its state at the end of the array
         hipStream_t stream = static_cast<hipStream_t>(stream_);
-        const bool onepass = use_onepass(codec, false, n_tiles, stream, false) && n_tiles <= kNoAllocChainTiles;
+        const bool onepass = use_onepass(codec, false, n_tiles, stream, false) && n_chain <= kNoAllocChainTiles;
+        const uint64_t tile_words = onepass ? chain_words : seq_words;
+        if (onepass)
+            n_tiles = n_chain;
         if (cap_over && !onepass)
             return fail(SPLITZIP_E_INVALID, "escape capacities exceed the allocation-free scratch");
         const auto up = [](uint64_t x) { return (x + 255) & ~uint64_t(255); };

@@ -43,14 +43,20 @@ constexpr uint32_t kElemBF16 = 0;
 constexpr uint32_t kElemE5M2 = 1;
 
 // E5M2 tiling: each lane owns groups of 32 consecutive bytes (two 16-byte loads), whose
-// 3-bit sign+mantissa fields fill 12 bytes and whose codes fill 16.  An encode tile is
-// 32768 elements (4 groups per lane), a decode tile 16384 (2 groups per lane).
+// 3-bit sign+mantissa fields fill 12 bytes and whose codes fill 16.  A pack tile of the
+// launch sequences is 32768 elements (4 groups per lane); a one-pass pack tile and a decode
+// tile are 16384 (2 groups per lane): the one-pass pack waits on its predecessor, and twice
+// as many tiles of half the escapes each balance that chain better (the launch sequences,
+// with no chain, lose by the extra tiles).
 constexpr int kE8GroupElems = 32;
 constexpr int kE8EncGroups = 4;
 constexpr int kE8EncTileShift = 15;
+constexpr int kE8ChainGroups = 2;
+constexpr int kE8ChainTileShift = 14;
 constexpr int kE8DecGroups = 2;
 constexpr int kE8DecTileShift = 14;
 static_assert(kThreads * kE8EncGroups * kE8GroupElems == (1 << kE8EncTileShift), "E5M2 encode tile");
+static_assert(kThreads * kE8ChainGroups * kE8GroupElems == (1 << kE8ChainTileShift), "E5M2 one-pass tile");
 static_assert(kThreads * kE8DecGroups * kE8GroupElems == (1 << kE8DecTileShift), "E5M2 decode tile");
 
 // Inverse-LUT entry of an exponent outside the codebook: nibble 0 plus an escape bit.
@@ -126,8 +132,9 @@ constexpr uint32_t kStashEscapes = 8192;
 constexpr uint32_t kStashChunks = kEncTileWords / 16;
 // byte offset of the positions in the stash: the copy out reads 16 bytes before each array
 constexpr uint32_t kStashPosAt = 16;
-constexpr uint32_t kE8StashEscapes = 8192;            // a quarter of an E5M2 tile's 32768 bytes
-constexpr uint32_t kE8StashChunks = (1u << kE8EncTileShift) / 16;
+constexpr uint32_t kE8StashEscapes = 8192;            // half a one-pass E5M2 tile
+constexpr uint32_t kE8StashChunks = (1u << kE8ChainTileShift) / 16;
+static_assert(2 * kE8StashEscapes >= (1u << kE8ChainTileShift), "two rounds of the stash hold a tile");
 static_assert(kChainCountMask >= (1ull << 38), "a segment's escape count fits the status word");
 
 // overflow counter: escapes reserved so far (low 40 bits) and overflow tiles listed (high 24)

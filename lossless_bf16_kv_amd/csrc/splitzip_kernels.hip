@@ -163,7 +163,7 @@ hipError_t launch_histogram(const HistArgs &a, hipStream_t stream)
 // escape count in a status word, finds the escapes of the earlier tiles by a decoupled
 // look-back over theirs, and writes its escapes, chunk offsets and (as a segment's last tile)
 // E to their final places, staging the escapes in LDS so that most of its waves can end
-// before the look-back does.
+// before the look-back does.  Its E5M2 tiles are half as long (2^kE8ChainTileShift bytes).
 // ======================================================================================
 
 // Split one group of 8 words (4 dwords, word 2m in the low half of dword m).

@@ -45,7 +45,7 @@ def use_mode(codec, mode):
     codec.set_private_overflow(private)
     codec.set_onepass_tiles(onepass)
 TILE = 16384          # BF16 words per pack tile
-TILE8 = 32768         # E5M2 bytes per pack tile
+TILE8 = 32768         # E5M2 bytes per pack tile of the launch sequences (one pass: 16384)
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -392,3 +392,31 @@ def test_exact_escape_counts_per_tile(mode, C):
     assert enc.n_escapes == sum(counts) + 2000
     assert_same_stream(codec, enc, x)
     assert np.array_equal(host(codec.decode(enc), np.uint16), x)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("C", [16, 1024])
+def test_exact_escape_counts_per_tile_e5m2(mode, C):
+    """E5M2 blocks of 16384 bytes (a one-pass tile; two make a tile of the launch sequences)
+    with exactly 0, 127, 128, 128, 128, 129 escapes (pairs of 127, 256 and 257 around the
+    256-entry slot), 8191, 8192, 8193 (around the one-pass stash), all 16384 twice, 16383,
+    5000 and 1, then a partial block with 2000, at random places: the stream equals the
+    oracle's in every launch sequence and build."""
+    rng = np.random.default_rng(18)
+    B = 16384
+    counts = [0, 127, 128, 128, 128, 129, 8191, 8192, 8193, B, B, B - 1, 5000, 1]
+    n = len(counts) * B + 5000
+    # exponent 15 everywhere (inside any codebook of N(0,1) data), random sign and mantissa
+    x = ((15 << 2) | rng.integers(0, 4, n) | (rng.integers(0, 2, n) << 7)).astype(np.uint8)
+    for t, k in enumerate(counts + [2000]):
+        size = min(B, n - t * B)
+        at = t * B + rng.choice(size, size=k, replace=False)
+        x[at] = (x[at] & 0x83) | (30 << 2)          # exponent 30: an escape
+    codec = t8.codec_for(workloads.e5m2_normal(50_000, 6), C)
+    book = np.frombuffer(codec.codebook, np.uint8)
+    assert 30 not in book and 15 in book
+    use_mode(codec, mode)
+    enc = codec.encode(t8.dev8(x))
+    assert enc.n_escapes == sum(counts) + 2000
+    t8.assert_same_stream(codec, enc, x)
+    assert np.array_equal(t8.host(codec.decode(enc), np.uint8), x)
