@@ -114,6 +114,27 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
     return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
+// A compile-time flag passed to generic lambdas.
+template <bool B>
+struct BoolTag {
+    static constexpr bool value = B;
+};
+
+// Set-bit table of the one-pass packs: entry m (an 8-bit mask) holds the indices of m's set
+// bits, lowest first, one per byte (0 past the last).
+__device__ __forceinline__ uint2 set_bit_indices(uint32_t m)
+{
+    uint64_t e = 0;
+    uint32_t c = 0;
+#pragma unroll
+    for (uint32_t b = 0; b < 8; ++b)
+        if ((m >> b) & 1u) {
+            e |= (uint64_t)b << (8 * c);
+            ++c;
+        }
+    return make_uint2((uint32_t)e, (uint32_t)(e >> 32));
+}
+
 // Entry k (0..15) of a codebook held as 4 little-endian dwords.
 __device__ __forceinline__ uint32_t codebook_byte(const uint32_t cb[4], uint32_t k)
 {

@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
     constexpr uint32_t kStashWords = (kStashExpAt + kE8StashEscapes + 2 * kE8StashChunks + 3) / 4;
     constexpr uint32_t kRawWords = kChain ? (kStashWords > kInWords ? kStashWords : kInWords) : kInWords + kStageWords;
     __shared__ uint32_t s_raw[kRawWords];
-    __shared__ uint32_t s_bitpos[kChain ? 256 : 1];   // one-pass build: set-bit indices of each byte
+    __shared__ uint2 s_bitpos[kChain ? 256 : 1];      // one-pass build: set_bit_indices of each byte
     __shared__ uint32_t s_ready;        // one-pass build: 2 when wave 0 has put the tile's offset in
                                         // s_before and copied the stash out
     __shared__ uint64_t s_before;
@@ -112,16 +112,8 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
         reinterpret_cast<uint32_t *>(s_lut)[tid] = reinterpret_cast<const uint32_t *>(lut)[tid];
     if (!kChain && a.packed && tid == 0 && t == segment_first_tile(a, s))
         a.seg_total[s] = 0;      // the sums launch adds the segment's escapes into it
-    if (kChain) {
-        uint32_t e = 0, c = 0;
-#pragma unroll
-        for (uint32_t b = 0; b < 8; ++b)
-            if ((tid >> b) & 1u) {
-                e |= b << (4 * c);
-                ++c;
-            }
-        s_bitpos[tid & 255u] = e;
-    }
+    if (kChain)
+        s_bitpos[tid & 255u] = set_bit_indices(tid & 255u);
     const uint64_t n = sd.n;
     const uint64_t base = (uint64_t)(t - segment_first_tile(a, s)) << kShift;
     const uint64_t cmask = (1ull << a.log2_chunk) - 1;
@@ -244,31 +236,41 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
         if (wave == 0 && t > first)
             chain_load<kChainRows>(a, t - 1, first, lane, w);
         const uint32_t cm = (uint32_t)cmask;
-        // the lane's escapes of rank lo .. hi - 1 to LDS at rank - lo (as in the BF16 pack, per
-        // 8 elements of a lane's 32)
-        auto stash = [&](uint32_t lo, uint32_t hi) {
+        // the lane's escapes of rank lo .. hi - 1 to LDS at rank - lo, as in the BF16 pack, per
+        // 8 elements of a lane's 32 (positions two per byte permute, exponents four); without
+        // a range check (kRanged false) every escape of the lane must lie in lo .. hi - 1
+        auto stash = [&](auto ranged, uint32_t lo, uint32_t hi) {
+            constexpr bool kRanged = decltype(ranged)::value;
 #pragma unroll
             for (int j = 0; j < G; ++j) {
                 uint32_t r = rank[j];
                 const uint32_t fl = flags[j];
-                if (fl && r < hi && r + 32u > lo) {
-                    const uint32_t q0 = (uint32_t)g0[j];
+                if (fl && (!kRanged || (r < hi && r + 32u > lo))) {
+                    // the group's first element (recomputed: g0 is not kept)
+                    const uint32_t q0 = (uint32_t)base + ((wave * G + j) << 11) + lane * kE8GroupElems;
 #pragma unroll
                     for (int d = 0; d < 4; ++d) {
                         // escape flags of elements 8d .. 8d + 7, bit k for element 8d + k
                         const uint32_t sh = 2u * (((uint32_t)d + 2u) & 3u);
                         const uint32_t f = (((fl >> sh) & 0x03030303u) * 0x01041040u) >> 24;
                         const uint32_t cnt = __popc(f);
-                        const uint32_t ks = s_bitpos[f];
+                        const uint2 ks = s_bitpos[f];
+                        // elements 8d .. 8d + 7 start 8-aligned inside their chunk
+                        const uint32_t pq = ((q0 + 8u * d) & cm) * 0x10001u;
+                        uint32_t pp = 0, ee = 0;
 #pragma unroll
                         for (int i = 0; i < 8; ++i) {
                             if (!__ballot((uint32_t)i < cnt))
                                 break;
+                            const uint32_t kx = i < 4 ? ks.x : ks.y;
+                            if ((i & 1) == 0)
+                                pp = pq + perm(0u, kx, (i & 2) ? 0x0C030C02u : 0x0C010C00u);
+                            if ((i & 3) == 0)
+                                ee = (perm(v[j][2 * d + 1], v[j][2 * d], kx) >> 2) & 0x1F1F1F1Fu;
                             const uint32_t ri = r + i;
-                            if ((uint32_t)i < cnt && ri >= lo && ri < hi) {
-                                const uint32_t k = (ks >> (4 * i)) & 15u;
-                                s_pos[ri - lo] = (uint16_t)((q0 + 8u * d + k) & cm);
-                                s_exp[ri - lo] = (uint8_t)((perm(v[j][2 * d + 1], v[j][2 * d], k) >> 2) & 0x1Fu);
+                            if ((uint32_t)i < cnt && (!kRanged || (ri >= lo && ri < hi))) {
+                                s_pos[ri - lo] = (uint16_t)(pp >> (16 * (i & 1)));
+                                s_exp[ri - lo] = (uint8_t)(ee >> (8 * (i & 3)));
                             }
                         }
                         r += cnt;
@@ -284,9 +286,12 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
             if (a.log2_chunk == 4 && g0[j] + 16 < n)
                 s_start[(p0 + 16) >> 4] = (uint16_t)(rank[j] + __popc(flags[j] & 0xF0F0F0F0u));
         }
-        stash(0, kE8StashEscapes);
-        __syncthreads();
         const bool past = wave_end > kE8StashEscapes;               // uniform in the wave
+        if (past)
+            stash(BoolTag<true>{}, 0, kE8StashEscapes);
+        else
+            stash(BoolTag<false>{}, 0, kE8StashEscapes);
+        __syncthreads();
         if (wave != 0 && !past)
             return;
         if (wave == 0) {
@@ -339,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
         uint32_t hi = (uint64_t)wave_end < left ? wave_end : (uint32_t)left;
         hi = hi < 2 * kE8StashEscapes ? hi : 2 * kE8StashEscapes;
         if (hi > lo) {
-            stash(kE8StashEscapes, 2 * kE8StashEscapes);
+            stash(BoolTag<true>{}, kE8StashEscapes, 2 * kE8StashEscapes);
             stash_copy<2>(as_global(sd.esc_pos + before + lo), s_pos + (lo - kE8StashEscapes), hi - lo, lane);
             stash_copy<1>(as_global(sd.esc_exp + before + lo), s_exp + (lo - kE8StashEscapes), hi - lo, lane);
         }

@@ -211,8 +211,8 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
     constexpr uint32_t kStashExpAt = kStashPosAt + 2 * kStashEscapes + 16;
     constexpr uint32_t kStashWords = (kStashExpAt + kStashEscapes + 2 * kStashChunks + 3) / 4;
     __shared__ uint32_t s_stage[kChain && kStashWords > kStageWords ? kStashWords : kStageWords];
-    // one-pass build: for each 8-bit escape mask, the indices of its set bits, 4 bits each
-    __shared__ uint32_t s_bitpos[kChain ? 256 : 1];
+    // one-pass build: for each 8-bit escape mask, the indices of its set bits (set_bit_indices)
+    __shared__ uint2 s_bitpos[kChain ? 256 : 1];
     __shared__ uint32_t s_ready;        // one-pass build: 2 when wave 0 has put the tile's offset in
                                         // s_before and copied the stash out
     __shared__ uint64_t s_before;
@@ -230,16 +230,8 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
         reinterpret_cast<uint32_t *>(s_lut)[tid] = reinterpret_cast<const uint32_t *>(lut)[tid];
     if (!kChain && a.packed && tid == 0 && t == segment_first_tile(a, s))
         a.seg_total[s] = 0;      // the sums launch adds the segment's escapes into it
-    if (kChain) {
-        uint32_t e = 0, c = 0;
-#pragma unroll
-        for (uint32_t b = 0; b < 8; ++b)
-            if ((tid >> b) & 1u) {
-                e |= b << (4 * c);
-                ++c;
-            }
-        s_bitpos[tid & 255u] = e;
-    }
+    if (kChain)
+        s_bitpos[tid & 255u] = set_bit_indices(tid & 255u);
     const uint64_t tag = a.chain_tag;
     const uint64_t n = sd.n;
     const SZ_GLOBAL uint16_t *xw = as_global(sd.data);
@@ -324,29 +316,41 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
             chain_load<kChainRows>(a, t - 1, first, lane, w);
         const uint32_t cm = (uint32_t)cmask;
         // the lane's escapes of rank lo .. hi - 1 to LDS at rank - lo: a lane's escapes of
-        // group j have ranks rank[j], rank[j] + 1, ...; the i-th goes in step i, its word index
-        // from the table of set bits
-        auto stash = [&](uint32_t lo, uint32_t hi) {
+        // group j have ranks rank[j], rank[j] + 1, ...; the i-th goes in step i.  The word
+        // indices of a group's escapes come from the table of set bits, one per byte: one byte
+        // permute turns two of them into two u16 positions (a group starts 8-aligned inside its
+        // chunk, so position = the group's place in the chunk + index), and one more four of
+        // them into their exponent bytes.  Without a range check (kRanged false) every escape
+        // of the lane must lie in lo .. hi - 1.
+        auto stash = [&](auto ranged, uint32_t lo, uint32_t hi) {
+            constexpr bool kRanged = decltype(ranged)::value;
 #pragma unroll
             for (int j = 0; j < kEncGroups; ++j) {
                 const uint32_t r0 = rank[j];
                 const uint32_t z = flags[j];
-                if (z && r0 < hi && r0 + 8u > lo) {
+                if (z && (!kRanged || (r0 < hi && r0 + 8u > lo))) {
                     const uint32_t elo = perm(v[j].y >> 7, v[j].x >> 7, 0x06040200u);   // exponents, words 0..3
                     const uint32_t ehi = perm(v[j].w >> 7, v[j].z >> 7, 0x06040200u);   // words 4..7
                     const uint32_t f = (((z >> 4) & 0x03030303u) * 0x01041040u) >> 24;   // bit k: word k escapes
                     const uint32_t cnt = __popc(f);
-                    const uint32_t ks = s_bitpos[f];
-                    const uint32_t q0 = (uint32_t)g0[j];
+                    const uint2 ks = s_bitpos[f];
+                    // the group's place in its chunk, in both halves (recomputed: g0 is not kept)
+                    const uint32_t pq = (((uint32_t)base + ((wave * kEncGroups + j) << 9) + lane * kGroupWords) & cm) *
+                                        0x10001u;
+                    uint32_t pp = 0, ee = 0;
 #pragma unroll
                     for (int i = 0; i < kGroupWords; ++i) {
                         if (!__ballot((uint32_t)i < cnt))
                             break;
+                        const uint32_t kx = i < 4 ? ks.x : ks.y;
+                        if ((i & 1) == 0)    // positions of escapes i, i + 1
+                            pp = pq + perm(0u, kx, (i & 2) ? 0x0C030C02u : 0x0C010C00u);
+                        if ((i & 3) == 0)    // exponents of escapes i .. i + 3
+                            ee = perm(ehi, elo, kx);
                         const uint32_t r = r0 + i;
-                        if ((uint32_t)i < cnt && r >= lo && r < hi) {
-                            const uint32_t k = (ks >> (4 * i)) & 15u;
-                            s_pos[r - lo] = (uint16_t)((q0 + k) & cm);
-                            s_exp[r - lo] = (uint8_t)perm(ehi, elo, k);
+                        if ((uint32_t)i < cnt && (!kRanged || (r >= lo && r < hi))) {
+                            s_pos[r - lo] = (uint16_t)(pp >> (16 * (i & 1)));
+                            s_exp[r - lo] = (uint8_t)(ee >> (8 * (i & 3)));
                         }
                     }
                 }
@@ -358,9 +362,12 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
             if (g0[j] < n && (g0[j] & cmask) == 0)
                 s_start[p0 >> a.log2_chunk] = (uint16_t)rank[j];
         }
-        stash(0, kStashEscapes);
-        __syncthreads();
         const bool past = wave_end > kStashEscapes;                 // uniform in the wave
+        if (past)
+            stash(BoolTag<true>{}, 0, kStashEscapes);
+        else
+            stash(BoolTag<false>{}, 0, kStashEscapes);
+        __syncthreads();
         if (wave != 0 && !past)
             return;
         if (wave == 0) {
@@ -414,7 +421,7 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
         const uint32_t hi = (uint64_t)wave_end < left ? wave_end : (uint32_t)left;
         if (hi <= lo)
             return;
-        stash(kStashEscapes, 2 * kStashEscapes);
+        stash(BoolTag<true>{}, kStashEscapes, 2 * kStashEscapes);
         stash_copy<2>(as_global(sd.esc_pos + before + lo), s_pos + (lo - kStashEscapes), hi - lo, lane);
         stash_copy<1>(as_global(sd.esc_exp + before + lo), s_exp + (lo - kStashEscapes), hi - lo, lane);
         return;
