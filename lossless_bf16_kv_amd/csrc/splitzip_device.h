@@ -375,6 +375,61 @@ __device__ __forceinline__ void stash_copy(SZ_GLOBAL T *dst, const T *src, uint3
         dst[tail_at + lane] = src[tail_at + lane];
 }
 
+// One-pass encode, early release: a tile's escapes past its stash (rank kStash and up, in a tile
+// of kTileElems elements), written by the waves that hold them once wave 0 has copied the stash
+// out (*s_out set, the tile's escape offset in *s_before).  When a tile holds at most twice the
+// stash, each such wave puts them in the stash at rank - kStash (the waves' ranges do not
+// overlap) and copies its range out; in longer tiles each owns a quarter of the stash and sends
+// them through it a quarter at a time.  A wave's escapes have ranks wave_first .. wave_end - 1;
+// stash(tag, lo, hi, at) puts the calling wave's escapes of rank lo .. hi - 1 in the stash at
+// rank - lo + at.  The wait is bounded (kChainSpinMax polls, then an error bit), so every wave
+// ends.
+template <uint32_t kStash, uint32_t kTileElems, typename Stash>
+__device__ __forceinline__ void stash_rest(const EncodeArgs &a, const SegDesc &sd, const uint32_t *s_out,
+                                           const uint64_t *s_before, uint32_t wave, uint32_t wave_first,
+                                           uint32_t wave_end, uint32_t lane, uint16_t *s_pos, uint8_t *s_exp,
+                                           Stash &&stash)
+{
+    static_assert(kStash % kWaves == 0 && kTileElems % kStash == 0, "stash parts");
+    uint32_t polls = 0;
+    while (__hip_atomic_load(s_out, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0u) {
+        if (++polls > kChainSpinMax) {
+            if (lane == 0)
+                atomicOr(a.err, kErrChainStall);
+            return;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+    const uint64_t sb = *s_before;
+    const uint64_t before = uniform_u64(sb);
+    const uint64_t left = sd.esc > before && sd.esc_exp ? sd.esc - before : 0;
+    const uint32_t end = (uint64_t)wave_end < left ? wave_end : (uint32_t)left;
+    const uint32_t lo0 = wave_first > kStash ? wave_first : kStash;
+    if (kTileElems <= 2 * kStash) {
+        if (lo0 >= end)
+            return;
+        stash(BoolTag<true>{}, kStash, 2 * kStash, 0u);
+        stash_copy<2>(as_global(sd.esc_pos + before + lo0), s_pos + (lo0 - kStash), end - lo0, lane);
+        stash_copy<1>(as_global(sd.esc_exp + before + lo0), s_exp + (lo0 - kStash), end - lo0, lane);
+        return;
+    }
+    // (a loop with a trip count known at compile time: in a loop of unknown count the stash's
+    // unrolled steps took more than twice the registers)
+    constexpr uint32_t kPart = kStash / kWaves;
+    constexpr uint32_t kParts = kTileElems / kStash;      // a wave holds at most kTileElems / kWaves
+    const uint32_t at = wave * kPart;
+#pragma unroll
+    for (uint32_t q = 0; q < kParts; ++q) {
+        const uint32_t lo = lo0 + q * kPart;
+        if (lo >= end)
+            break;
+        stash(BoolTag<true>{}, lo, lo + kPart, at);
+        const uint32_t ne = end - lo < kPart ? end - lo : kPart;
+        stash_copy<2>(as_global(sd.esc_pos + before + lo), s_pos + at, ne, lane);
+        stash_copy<1>(as_global(sd.esc_exp + before + lo), s_exp + at, ne, lane);
+    }
+}
+
 // ---- one-pass encode: the look-back over the status words of earlier tiles -------------
 
 __device__ __forceinline__ uint64_t chain_word(uint64_t tag, uint64_t kind, uint64_t count)

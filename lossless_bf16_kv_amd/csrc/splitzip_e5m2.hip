@@ -75,13 +75,17 @@ __device__ __forceinline__ void split_group32(const uint32_t (&x)[8], const uint
     flags = fl;
 }
 
-// kChain: the one-pass build (chained tiles of 2^kE8ChainTileShift elements), which writes the
-// escapes to their final places.
-template <bool kStage, bool kChain>
+// kChain: the one-pass build (chained tiles), which writes the escapes to their final places.
+// G: groups per lane (4: tiles of 2^kE8EncTileShift elements; the one-pass build also runs
+// 2: tiles of 2^kE8ChainTileShift).
+template <bool kStage, bool kChain, int G>
 __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const EncodeArgs a)
 {
-    constexpr int G = kChain ? kE8ChainGroups : kE8EncGroups;
-    constexpr int kShift = kChain ? kE8ChainTileShift : kE8EncTileShift;
+    static_assert(G == kE8EncGroups || (kChain && G == kE8ChainGroups), "E5M2 pack tile");
+    constexpr int kShift = G == kE8EncGroups ? kE8EncTileShift : kE8ChainTileShift;
+    constexpr uint32_t kStashChunks = (1u << kShift) / 16;
+    static_assert(kE8StashEscapes >= (1u << kShift) / kWaves && kE8StashEscapes % kWaves == 0,
+                  "wave 0's escapes fit the stash");
     __shared__ uint8_t s_lut[256];
     __shared__ uint32_t s_wave_total[kWaves];
     __shared__ uint64_t s_ovf;
@@ -90,12 +94,13 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
     // (its use begins after the last regroup and excludes the staged stores)
     constexpr uint32_t kInWords = kWaves * 128 * 4, kStageWords = kWaves * 2048 / 2;
     constexpr uint32_t kStashExpAt = kStashPosAt + 2 * kE8StashEscapes + 16;
-    constexpr uint32_t kStashWords = (kStashExpAt + kE8StashEscapes + 2 * kE8StashChunks + 3) / 4;
+    constexpr uint32_t kStashWords = (kStashExpAt + kE8StashEscapes + 2 * kStashChunks + 3) / 4;
     constexpr uint32_t kRawWords = kChain ? (kStashWords > kInWords ? kStashWords : kInWords) : kInWords + kStageWords;
     __shared__ uint32_t s_raw[kRawWords];
     __shared__ uint2 s_bitpos[kChain ? 256 : 1];      // one-pass build: set_bit_indices of each byte
-    __shared__ uint32_t s_ready;        // one-pass build: 2 when wave 0 has put the tile's offset in
-                                        // s_before and copied the stash out
+    // one-pass build: set when wave 0 has copied the stash out and put the tile's escape offset
+    // in s_before (stash_rest)
+    __shared__ uint32_t s_out;
     __shared__ uint64_t s_before;
     uint4(*s_in)[128] = reinterpret_cast<uint4(*)[128]>(s_raw);
     uint16_t(*s_stage)[2048] = reinterpret_cast<uint16_t(*)[2048]>(s_raw + kInWords);
@@ -112,8 +117,11 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
         reinterpret_cast<uint32_t *>(s_lut)[tid] = reinterpret_cast<const uint32_t *>(lut)[tid];
     if (!kChain && a.packed && tid == 0 && t == segment_first_tile(a, s))
         a.seg_total[s] = 0;      // the sums launch adds the segment's escapes into it
-    if (kChain)
+    if (kChain) {
         s_bitpos[tid & 255u] = set_bit_indices(tid & 255u);
+        if (tid == 0)
+            s_out = 0;
+    }
     const uint64_t n = sd.n;
     const uint64_t base = (uint64_t)(t - segment_first_tile(a, s)) << kShift;
     const uint64_t cmask = (1ull << a.log2_chunk) - 1;
@@ -228,10 +236,8 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
         const uint64_t tag = a.chain_tag;
         const uint32_t first = segment_first_tile(a, s);
         const bool last = t + 1 == segment_end_tile(a, s);
-        if (tid == 0) {
+        if (tid == 0)
             chain_publish(a, t, chain_word(tag, t > first ? kChainAggregate : kChainPrefix, tile_total));
-            s_ready = 0;
-        }
         uint64_t w[kChainRows];
         if (wave == 0 && t > first)
             chain_load<kChainRows>(a, t - 1, first, lane, w);
@@ -239,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
         // the lane's escapes of rank lo .. hi - 1 to LDS at rank - lo, as in the BF16 pack, per
         // 8 elements of a lane's 32 (positions two per byte permute, exponents four); without
         // a range check (kRanged false) every escape of the lane must lie in lo .. hi - 1
-        auto stash = [&](auto ranged, uint32_t lo, uint32_t hi) {
+        auto stash = [&](auto ranged, uint32_t lo, uint32_t hi, uint32_t at) {
             constexpr bool kRanged = decltype(ranged)::value;
 #pragma unroll
             for (int j = 0; j < G; ++j) {
@@ -269,8 +275,8 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
                                 ee = (perm(v[j][2 * d + 1], v[j][2 * d], kx) >> 2) & 0x1F1F1F1Fu;
                             const uint32_t ri = r + i;
                             if ((uint32_t)i < cnt && (!kRanged || (ri >= lo && ri < hi))) {
-                                s_pos[ri - lo] = (uint16_t)(pp >> (16 * (i & 1)));
-                                s_exp[ri - lo] = (uint8_t)(ee >> (8 * (i & 3)));
+                                s_pos[ri - lo + at] = (uint16_t)(pp >> (16 * (i & 1)));
+                                s_exp[ri - lo + at] = (uint8_t)(ee >> (8 * (i & 3)));
                             }
                         }
                         r += cnt;
@@ -286,11 +292,11 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
             if (a.log2_chunk == 4 && g0[j] + 16 < n)
                 s_start[(p0 + 16) >> 4] = (uint16_t)(rank[j] + __popc(flags[j] & 0xF0F0F0F0u));
         }
-        const bool past = wave_end > kE8StashEscapes;               // uniform in the wave
+        const bool past = wave_end > kE8StashEscapes;                 // uniform in the wave
         if (past)
-            stash(BoolTag<true>{}, 0, kE8StashEscapes);
+            stash(BoolTag<true>{}, 0, kE8StashEscapes, 0);
         else
-            stash(BoolTag<false>{}, 0, kE8StashEscapes);
+            stash(BoolTag<false>{}, 0, kE8StashEscapes, 0);
         __syncthreads();
         if (wave != 0 && !past)
             return;
@@ -320,34 +326,15 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
                 stash_copy<2>(as_global(sd.esc_pos + before), s_pos, ne, lane);
                 stash_copy<1>(as_global(sd.esc_exp + before), s_exp, ne, lane);
             }
-            if (tile_total > kE8StashEscapes && lane == 0)    // the stash is free again
-                __hip_atomic_store(&s_ready, 2u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (tile_total > kE8StashEscapes && lane == 0)    // the stash is out
+                __hip_atomic_store(&s_out, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
             return;
         }
-        // a wave with escapes past the stash: once wave 0 has copied the stash out (a bounded
-        // wait), its escapes of rank kE8StashEscapes and above (at most a tile's elements, two
-        // rounds of the stash) go through the stash at rank - kE8StashEscapes and out
-        uint32_t polls = 0;
-        while (__hip_atomic_load(&s_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 2u) {
-            if (++polls > kChainSpinMax) {
-                if (lane == 0)
-                    atomicOr(a.err, kErrChainStall);
-                return;
-            }
-            __builtin_amdgcn_s_sleep(2);
-        }
-        const uint64_t sb = s_before;
-        const uint64_t before = uniform_u64(sb);
-        const uint64_t left = sd.esc > before && sd.esc_exp ? sd.esc - before : 0;
+        // a wave with escapes past the stash: once wave 0 has copied it out, they go through it
+        // again (stash_rest)
         const uint32_t wave_first = (uint32_t)__builtin_amdgcn_readfirstlane(rank[0]);   // lane 0's group 0
-        const uint32_t lo = wave_first > kE8StashEscapes ? wave_first : kE8StashEscapes;
-        uint32_t hi = (uint64_t)wave_end < left ? wave_end : (uint32_t)left;
-        hi = hi < 2 * kE8StashEscapes ? hi : 2 * kE8StashEscapes;
-        if (hi > lo) {
-            stash(BoolTag<true>{}, kE8StashEscapes, 2 * kE8StashEscapes);
-            stash_copy<2>(as_global(sd.esc_pos + before + lo), s_pos + (lo - kE8StashEscapes), hi - lo, lane);
-            stash_copy<1>(as_global(sd.esc_exp + before + lo), s_exp + (lo - kE8StashEscapes), hi - lo, lane);
-        }
+        stash_rest<kE8StashEscapes, (1u << kShift)>(a, sd, &s_out, &s_before, wave, wave_first, wave_end, lane,
+                                                    s_pos, s_exp, stash);
         return;
     }
 
@@ -425,16 +412,22 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
 hipError_t launch_encode_pack_e5m2(const EncodeArgs &a, hipStream_t stream)
 {
     const unsigned lds = a.n_tiles >= kPackCapTiles ? kE8PackLdsReserve : 0u;
-    if (a.chain_status) {
+    constexpr int G = kE8EncGroups, G1 = kE8ChainGroups;
+    if (a.chain_status && a.tile_shift == (uint32_t)kE8ChainTileShift) {
         if (a.stage)
-            encode_pack_e5m2_kernel<true, true><<<a.n_tiles, kThreads, 0, stream>>>(a);
+            encode_pack_e5m2_kernel<true, true, G1><<<a.n_tiles, kThreads, 0, stream>>>(a);
         else
-            encode_pack_e5m2_kernel<false, true><<<a.n_tiles, kThreads, 0, stream>>>(a);
+            encode_pack_e5m2_kernel<false, true, G1><<<a.n_tiles, kThreads, 0, stream>>>(a);
+    } else if (a.chain_status) {
+        if (a.stage)
+            encode_pack_e5m2_kernel<true, true, G><<<a.n_tiles, kThreads, 0, stream>>>(a);
+        else
+            encode_pack_e5m2_kernel<false, true, G><<<a.n_tiles, kThreads, 0, stream>>>(a);
     } else {
         if (a.stage)
-            encode_pack_e5m2_kernel<true, false><<<a.n_tiles, kThreads, lds, stream>>>(a);
+            encode_pack_e5m2_kernel<true, false, G><<<a.n_tiles, kThreads, lds, stream>>>(a);
         else
-            encode_pack_e5m2_kernel<false, false><<<a.n_tiles, kThreads, 0, stream>>>(a);
+            encode_pack_e5m2_kernel<false, false, G><<<a.n_tiles, kThreads, 0, stream>>>(a);
     }
     return hipGetLastError();
 }

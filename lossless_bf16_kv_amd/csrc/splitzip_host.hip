@@ -749,12 +749,13 @@ uint64_t tile_elements(const splitzip_codec *c, bool encode)
     return encode ? sz::kEncTileWords : sz::kDecTileWords;
 }
 
-// log2 of the elements per pack tile: the one-pass encode of E5M2 bytes takes tiles half as
-// long as the launch sequences'.
-uint32_t pack_tile_shift(const splitzip_codec *c, bool onepass)
+// log2 of the elements per pack tile of a call of n_tiles tiles of tile_elements(c, true): a
+// one-pass encode of E5M2 bytes over at most kE8ShortChainTiles of them takes tiles half as
+// long.
+uint32_t pack_tile_shift(const splitzip_codec *c, bool onepass, uint64_t n_tiles)
 {
     if (c->elem == sz::kElemE5M2)
-        return onepass ? sz::kE8ChainTileShift : sz::kE8EncTileShift;
+        return onepass && n_tiles <= sz::kE8ShortChainTiles ? sz::kE8ChainTileShift : sz::kE8EncTileShift;
     return sz::kEncTileShift;
 }
 
@@ -1101,14 +1102,13 @@ int splitzip_codec_info(const splitzip_codec *codec, uint8_t codebook[16], uint3
 
 namespace {
 
-// The call's shape, its codebook tables and the encode scratch arrays at `base` (laid out as
-// `lay`; NULL for a one-pass encode, which has no scratch and its own tile length) into a.
+// The call's shape (n_tiles pack tiles of 2^tile_shift elements), its codebook tables and the
+// encode scratch arrays at `base` (laid out as `lay`; NULL for a one-pass encode) into a.
 // res: the error word, then E per segment.
 void set_encode_args(sz::EncodeArgs &a, const splitzip_codec *codec, uint32_t n_seg, uint32_t n_tiles,
-                     int64_t book, bool packed, uint8_t *base, const EncodeScratch &lay,
+                     uint32_t tile_shift, int64_t book, bool packed, uint8_t *base, const EncodeScratch &lay,
                      unsigned long long *ovf_ctr, uint64_t ovf_cap, bool private_ovf, uint8_t *res)
 {
-    const uint32_t tile_shift = pack_tile_shift(codec, base == nullptr);
     // one book for the whole call: its LUT directly; several: the table, indexed per segment
     a.lut = codec->d_lut + 256 * (book < 0 ? 0 : book);
     a.multi_book = book < 0;
@@ -1144,8 +1144,8 @@ void set_encode_args(sz::EncodeArgs &a, const splitzip_codec *codec, uint32_t n_
 bool onepass_tiles(const splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
                    const std::vector<uint32_t> &tiles, std::vector<uint32_t> &out)
 {
-    const uint32_t shift = pack_tile_shift(codec, true);
-    if (shift == pack_tile_shift(codec, false)) {
+    const uint32_t shift = pack_tile_shift(codec, true, tiles[desc.size()]);
+    if (shift == pack_tile_shift(codec, false, tiles[desc.size()])) {
         out = tiles;
         return true;
     }
@@ -1219,7 +1219,7 @@ int encode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
         return rc;
     Workspace *w = hold.get();
     const uint32_t n_tiles = tiles[n_seg];
-    const uint32_t tile_shift = pack_tile_shift(codec, false);
+    const uint32_t tile_shift = pack_tile_shift(codec, false, n_tiles);
     ensure_hint(w);
     // an input whose first tile outgrew its slot last time is taken to be escape-heavy again:
     // the launch sequences would move its escapes through scratch
@@ -1241,8 +1241,8 @@ int encode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
             (rc = stage_descriptors(w, desc, chain_tiles, &a.segs, &a.tile_start, &a.seg_at)) != SPLITZIP_OK)
             return rc;
         uint8_t *res = d_result ? reinterpret_cast<uint8_t *>(d_result) : w->result;
-        set_encode_args(a, codec, n_seg, n_chain, book, packed, nullptr, EncodeScratch(0, 0, 0, 0), nullptr, 0,
-                        false, res);
+        set_encode_args(a, codec, n_seg, n_chain, pack_tile_shift(codec, true, n_tiles), book, packed, nullptr,
+                        EncodeScratch(0, 0, 0, 0), nullptr, 0, false, res);
         a.chain_status = w->chain;
         a.chain_cap = w->chain_cap;
         a.first_tile_escapes = w->d_hint;
@@ -1274,7 +1274,7 @@ int encode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
     if (n_seg > 1 && (rc = stage_descriptors(w, desc, tiles, &a.segs, &a.tile_start, &a.seg_at)) != SPLITZIP_OK)
         return rc;
     uint8_t *res = d_result ? reinterpret_cast<uint8_t *>(d_result) : w->result;
-    set_encode_args(a, codec, n_seg, n_tiles, book, packed, w->scratch, lay, w->ovf_ctr, ovf_cap,
+    set_encode_args(a, codec, n_seg, n_tiles, tile_shift, book, packed, w->scratch, lay, w->ovf_ctr, ovf_cap,
                     private_ovf, res);
     a.first_tile_escapes = w->d_hint;
     const hipError_t e = run_encode_stages(codec, w, a, stream);
@@ -1365,10 +1365,8 @@ int splitzip_encode_noalloc(splitzip_codec *codec, uint32_t n_seg, const splitzi
         if (codec->device < 0 || codec->device >= kNoAllocDevices)
             return fail(SPLITZIP_E_INVALID, "device %d out of range", codec->device);
         // every segment checked, and the scratch the call needs, before anything is enqueued
-        // tiles of the launch sequences, and of a one-pass encode (shorter for E5M2)
         const uint64_t seq_words = tile_elements(codec, true);
-        const uint64_t chain_words = 1ull << pack_tile_shift(codec, true);
-        uint64_t n_tiles = 0, n_chain = 0, ovf_cap = 1;
+        uint64_t n_tiles = 0, ovf_cap = 1;
         bool cap_over = false;
         int64_t book = segs[0].book;
         sz::SegDesc d0{};
@@ -1379,7 +1377,6 @@ int splitzip_encode_noalloc(splitzip_codec *codec, uint32_t n_seg, const splitzi
             if (i == 0)
                 d0 = d;
             n_tiles += segment_tiles(segs[i].n, seq_words);
-            n_chain += segment_tiles(segs[i].n, chain_words);
             if (n_tiles > 0xFFFFFFF0ull)
                 return fail(SPLITZIP_E_INVALID, "too many tiles in one call");
             // (the overflow area of the launch sequences is as long as the capacities)
@@ -1391,8 +1388,14 @@ int splitzip_encode_noalloc(splitzip_codec *codec, uint32_t n_seg, const splitzi
         }
         // a one-pass call needs no scratch besides its state at the end of the array
         hipStream_t stream = static_cast<hipStream_t>(stream_);
+        // a one-pass encode's tiles (shorter for small E5M2 calls)
+        const uint32_t chain_shift = pack_tile_shift(codec, true, n_tiles);
+        uint64_t n_chain = 0;
+        for (uint32_t i = 0; i < n_seg; ++i)
+            n_chain += segment_tiles(segs[i].n, 1ull << chain_shift);
         const bool onepass = use_onepass(codec, false, n_tiles, stream, false) && n_chain <= kNoAllocChainTiles;
-        const uint64_t tile_words = onepass ? chain_words : seq_words;
+        const uint64_t tile_words = onepass ? 1ull << chain_shift : seq_words;
+        const uint32_t tile_shift = onepass ? chain_shift : pack_tile_shift(codec, false, n_tiles);
         if (onepass)
             n_tiles = n_chain;
         if (cap_over && !onepass)
@@ -1460,15 +1463,15 @@ int splitzip_encode_noalloc(splitzip_codec *codec, uint32_t n_seg, const splitzi
         a.tile_start = d_tiles;
         a.seg_at = d_tiles ? d_tiles + n_seg + 1 : nullptr;
         if (onepass) {
-            set_encode_args(a, codec, n_seg, (uint32_t)n_tiles, book, false, nullptr, EncodeScratch(0, 0, 0, 0),
-                            nullptr, 0, false, reinterpret_cast<uint8_t *>(d_result));
+            set_encode_args(a, codec, n_seg, (uint32_t)n_tiles, tile_shift, book, false, nullptr,
+                            EncodeScratch(0, 0, 0, 0), nullptr, 0, false, reinterpret_cast<uint8_t *>(d_result));
             a.chain_status = reinterpret_cast<uint64_t *>(base + kNoAllocScratchBytes);
             a.chain_cap = kNoAllocChainTiles;
             if (e == hipSuccess)
                 e = chain_next_tag(&nd.chain_launches, a.chain_status, a.chain_cap, stream, &a.chain_tag);
         } else {
-            set_encode_args(a, codec, n_seg, (uint32_t)n_tiles, book, false, base + enc_base, lay, ctr, ovf_cap,
-                            false, reinterpret_cast<uint8_t *>(d_result));
+            set_encode_args(a, codec, n_seg, (uint32_t)n_tiles, tile_shift, book, false, base + enc_base, lay, ctr,
+                            ovf_cap, false, reinterpret_cast<uint8_t *>(d_result));
         }
         if (e == hipSuccess)
             e = run_encode_stages(codec, nullptr, a, stream);

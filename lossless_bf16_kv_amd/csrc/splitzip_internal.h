@@ -43,16 +43,17 @@ constexpr uint32_t kElemBF16 = 0;
 constexpr uint32_t kElemE5M2 = 1;
 
 // E5M2 tiling: each lane owns groups of 32 consecutive bytes (two 16-byte loads), whose
-// 3-bit sign+mantissa fields fill 12 bytes and whose codes fill 16.  A pack tile of the
-// launch sequences is 32768 elements (4 groups per lane); a one-pass pack tile and a decode
-// tile are 16384 (2 groups per lane): the one-pass pack waits on its predecessor, and twice
-// as many tiles of half the escapes each balance that chain better (the launch sequences,
-// with no chain, lose by the extra tiles).
+// 3-bit sign+mantissa fields fill 12 bytes and whose codes fill 16.  A pack tile is 32768
+// elements (4 groups per lane), a decode tile 16384 (2 groups per lane).  A one-pass encode
+// of at most kE8ShortChainTiles such pack tiles runs tiles of 16384 instead: on a grid far
+// from filling the GPU, twice as many tiles of half the work each end sooner; on larger ones
+// the longer chain of look-backs costs more.
 constexpr int kE8GroupElems = 32;
 constexpr int kE8EncGroups = 4;
 constexpr int kE8EncTileShift = 15;
 constexpr int kE8ChainGroups = 2;
 constexpr int kE8ChainTileShift = 14;
+constexpr uint32_t kE8ShortChainTiles = 512;
 constexpr int kE8DecGroups = 2;
 constexpr int kE8DecTileShift = 14;
 static_assert(kThreads * kE8EncGroups * kE8GroupElems == (1 << kE8EncTileShift), "E5M2 encode tile");
@@ -127,14 +128,12 @@ constexpr uint32_t kChainStride = 4;
 // position, u8 exponent) and its chunk starts' escape ranks (u16, at most one per 16 words)
 // in LDS; waves whose escapes all fit end and free their registers while wave 0 waits for
 // the tile's escape offset and writes them; a wave with escapes past the stash waits too and
-// sends those through the stash in a second round.
+// then sends those through a quarter of the stash, a quarter at a time.
 constexpr uint32_t kStashEscapes = 8192;
 constexpr uint32_t kStashChunks = kEncTileWords / 16;
 // byte offset of the positions in the stash: the copy out reads 16 bytes before each array
 constexpr uint32_t kStashPosAt = 16;
-constexpr uint32_t kE8StashEscapes = 8192;            // half a one-pass E5M2 tile
-constexpr uint32_t kE8StashChunks = (1u << kE8ChainTileShift) / 16;
-static_assert(2 * kE8StashEscapes >= (1u << kE8ChainTileShift), "two rounds of the stash hold a tile");
+constexpr uint32_t kE8StashEscapes = 8192;            // a quarter of an E5M2 pack tile
 static_assert(kChainCountMask >= (1ull << 38), "a segment's escape count fits the status word");
 
 // overflow counter: escapes reserved so far (low 40 bits) and overflow tiles listed (high 24)

@@ -213,8 +213,9 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
     __shared__ uint32_t s_stage[kChain && kStashWords > kStageWords ? kStashWords : kStageWords];
     // one-pass build: for each 8-bit escape mask, the indices of its set bits (set_bit_indices)
     __shared__ uint2 s_bitpos[kChain ? 256 : 1];
-    __shared__ uint32_t s_ready;        // one-pass build: 2 when wave 0 has put the tile's offset in
-                                        // s_before and copied the stash out
+    // one-pass build: set when wave 0 has copied the stash out and put the tile's escape offset
+    // in s_before (stash_rest)
+    __shared__ uint32_t s_out;
     __shared__ uint64_t s_before;
 
     const uint32_t tid = threadIdx.x;
@@ -230,8 +231,11 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
         reinterpret_cast<uint32_t *>(s_lut)[tid] = reinterpret_cast<const uint32_t *>(lut)[tid];
     if (!kChain && a.packed && tid == 0 && t == segment_first_tile(a, s))
         a.seg_total[s] = 0;      // the sums launch adds the segment's escapes into it
-    if (kChain)
+    if (kChain) {
         s_bitpos[tid & 255u] = set_bit_indices(tid & 255u);
+        if (tid == 0)
+            s_out = 0;
+    }
     const uint64_t tag = a.chain_tag;
     const uint64_t n = sd.n;
     const SZ_GLOBAL uint16_t *xw = as_global(sd.data);
@@ -306,10 +310,8 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
         uint16_t *s_start = reinterpret_cast<uint16_t *>(s_exp + kStashEscapes);
         const uint32_t first = segment_first_tile(a, s);
         const bool last = t + 1 == segment_end_tile(a, s);        // loaded before the waits below
-        if (tid == 0) {
+        if (tid == 0)
             chain_publish(a, t, chain_word(tag, t > first ? kChainAggregate : kChainPrefix, tile_total));
-            s_ready = 0;
-        }
         // wave 0 issues the look-back's first loads now; they return while the escapes go to LDS
         uint64_t w[kChainRows];
         if (wave == 0 && t > first)
@@ -322,7 +324,7 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
         // chunk, so position = the group's place in the chunk + index), and one more four of
         // them into their exponent bytes.  Without a range check (kRanged false) every escape
         // of the lane must lie in lo .. hi - 1.
-        auto stash = [&](auto ranged, uint32_t lo, uint32_t hi) {
+        auto stash = [&](auto ranged, uint32_t lo, uint32_t hi, uint32_t at) {
             constexpr bool kRanged = decltype(ranged)::value;
 #pragma unroll
             for (int j = 0; j < kEncGroups; ++j) {
@@ -349,8 +351,8 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
                             ee = perm(ehi, elo, kx);
                         const uint32_t r = r0 + i;
                         if ((uint32_t)i < cnt && (!kRanged || (r >= lo && r < hi))) {
-                            s_pos[r - lo] = (uint16_t)(pp >> (16 * (i & 1)));
-                            s_exp[r - lo] = (uint8_t)(ee >> (8 * (i & 3)));
+                            s_pos[r - lo + at] = (uint16_t)(pp >> (16 * (i & 1)));
+                            s_exp[r - lo + at] = (uint8_t)(ee >> (8 * (i & 3)));
                         }
                     }
                 }
@@ -364,9 +366,9 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
         }
         const bool past = wave_end > kStashEscapes;                 // uniform in the wave
         if (past)
-            stash(BoolTag<true>{}, 0, kStashEscapes);
+            stash(BoolTag<true>{}, 0, kStashEscapes, 0);
         else
-            stash(BoolTag<false>{}, 0, kStashEscapes);
+            stash(BoolTag<false>{}, 0, kStashEscapes, 0);
         __syncthreads();
         if (wave != 0 && !past)
             return;
@@ -396,34 +398,15 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
                 stash_copy<2>(as_global(sd.esc_pos + before), s_pos, ne, lane);
                 stash_copy<1>(as_global(sd.esc_exp + before), s_exp, ne, lane);
             }
-            if (tile_total > kStashEscapes && lane == 0)      // the stash is free again
-                __hip_atomic_store(&s_ready, 2u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (tile_total > kStashEscapes && lane == 0)      // the stash is out
+                __hip_atomic_store(&s_out, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
             return;
         }
-        // a wave with escapes past the stash (a tile has at most twice as many): once wave 0
-        // has copied the stash out (a bounded wait), the wave puts its own escapes of rank
-        // kStashEscapes and up into it, at rank - kStashEscapes, and copies that range out
-        uint32_t polls = 0;
-        while (__hip_atomic_load(&s_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 2u) {
-            if (++polls > kChainSpinMax) {
-                if (lane == 0)
-                    atomicOr(a.err, kErrChainStall);
-                return;
-            }
-            __builtin_amdgcn_s_sleep(2);
-        }
-        static_assert(2 * kStashEscapes >= kEncTileWords, "two rounds of the stash hold a tile");
-        const uint64_t sb = s_before;
-        const uint64_t before = uniform_u64(sb);
-        const uint64_t left = sd.esc > before && sd.esc_exp ? sd.esc - before : 0;
+        // a wave with escapes past the stash: once wave 0 has copied it out, they go through it
+        // again (stash_rest)
         const uint32_t wave_first = (uint32_t)__builtin_amdgcn_readfirstlane(rank[0]);   // lane 0's group 0
-        const uint32_t lo = wave_first > kStashEscapes ? wave_first : kStashEscapes;
-        const uint32_t hi = (uint64_t)wave_end < left ? wave_end : (uint32_t)left;
-        if (hi <= lo)
-            return;
-        stash(BoolTag<true>{}, kStashEscapes, 2 * kStashEscapes);
-        stash_copy<2>(as_global(sd.esc_pos + before + lo), s_pos + (lo - kStashEscapes), hi - lo, lane);
-        stash_copy<1>(as_global(sd.esc_exp + before + lo), s_exp + (lo - kStashEscapes), hi - lo, lane);
+        stash_rest<kStashEscapes, kEncTileWords>(a, sd, &s_out, &s_before, wave, wave_first, wave_end, lane,
+                                                 s_pos, s_exp, stash);
         return;
     }
 

@@ -420,3 +420,33 @@ def test_exact_escape_counts_per_tile_e5m2(mode, C):
     assert enc.n_escapes == sum(counts) + 2000
     t8.assert_same_stream(codec, enc, x)
     assert np.array_equal(t8.host(codec.decode(enc), np.uint8), x)
+
+
+@pytest.mark.parametrize("onepass", [True, False])
+def test_exact_escape_counts_long_e5m2_call(onepass):
+    """An E5M2 call of 520 pack tiles of 32768 bytes (past the short-tile limit of the one-pass
+    encode, so its one-pass tiles are that long too), whose first 16 tiles hold exactly 0, 8191,
+    8192, 8193, 16383, 16384, 16385, 24575, 24576, 24577, 32767, all 32768, 1, 5000, 20000 and
+    12345 escapes (around each round of the 8192-entry stash) and the rest 0 to 300: the stream
+    equals the oracle's, in one pass and in the launch sequences."""
+    rng = np.random.default_rng(28)
+    counts = [0, 8191, 8192, 8193, 16383, 16384, 16385, 24575, 24576, 24577, TILE8 - 1, TILE8, 1, 5000, 20000, 12345]
+    n_tiles = 520
+    counts += [int(c) for c in rng.integers(0, 301, n_tiles - len(counts))]
+    n = n_tiles * TILE8 - 77
+    x = ((15 << 2) | rng.integers(0, 4, n) | (rng.integers(0, 2, n) << 7)).astype(np.uint8)
+    for t, k in enumerate(counts):
+        size = min(TILE8, n - t * TILE8)
+        k = min(k, size)
+        at = t * TILE8 + rng.choice(size, size=k, replace=False)
+        x[at] = (x[at] & 0x83) | (30 << 2)          # exponent 30: an escape
+    codec = t8.codec_for(workloads.e5m2_normal(50_000, 6), 1024)
+    codec.set_onepass_tiles(NEVER if onepass else 0)
+    codec.profile(True)
+    enc = codec.encode(t8.dev8(x), escape_capacity=n)
+    times = codec.kernel_times(reset=True)
+    codec.profile(False)
+    assert (times["encode_onepass"][1] == 1) == onepass
+    assert enc.n_escapes == sum(min(k, min(TILE8, n - t * TILE8)) for t, k in enumerate(counts))
+    t8.assert_same_stream(codec, enc, x)
+    assert np.array_equal(t8.host(codec.decode(enc), np.uint8), x)
