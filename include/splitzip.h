@@ -226,8 +226,8 @@ int splitzip_encode_async(splitzip_codec *codec, uint32_t n_seg, const splitzip_
  *
  * Limits.  At most SPLITZIP_NOALLOC_MAX_SEGMENTS segments.  The last 4 MiB of the array
  * hold the state of the one-pass encode (splitzip_tuning.h): a call that runs in one pass
- * (at most 131072 tiles, and the codec's one-pass limit) needs no other scratch.  Any other
- * call's scratch must fit the rest of the array, 60 MiB:
+ * (at most 131072 one-pass tiles, and the codec's one-pass limit) needs no other scratch.
+ * Any other call's scratch must fit the rest of the array, 60 MiB:
  *   256 + [n_seg > 1] (80 n_seg + 4 (n_seg + 2 + ceil(tiles / 64)))
  *       + about 560 B per tile (BF16 tile = 16384 words; E5M2: 1072 B per 32768-byte tile)
  *       + 4 (1 + sum of esc_capacity)

@@ -41,7 +41,9 @@ int splitzip_set_small_tiles(splitzip_codec *codec, uint32_t max_tiles);
  * max_tiles tiles (tiles as for splitzip_set_small_tiles) runs one pack launch that also
  * places every escape: each tile reads how many escapes its segment's earlier tiles hold from
  * their status words (a decoupled look-back over tiles in launch order) and writes its
- * escapes, chunk offsets and, as a segment's last tile, E straight to their final places.
+ * escapes, chunk offsets and, as a segment's last tile, E straight to their final places
+ * (an E5M2 call of at most 512 tiles runs it on tiles of half the length, 16384 bytes: on a
+ * grid that far from fills the GPU, more tiles of less work each end sooner).
  * Other calls (larger ones, packed streams, and calls on a stream that is being captured
  * into a graph, since each launch's tag is a kernel argument that a replay would repeat) run
  * the launch sequences of splitzip_set_small_tiles, with one exception: when the previous
@@ -50,10 +52,10 @@ int splitzip_set_small_tiles(splitzip_codec *codec, uint32_t max_tiles);
  * the launch sequences would move each escape through scratch.  On inputs with few escapes
  * one launch is faster up to about 2048 tiles (no second launch); on larger calls, with many
  * tiles in flight, each tile's wait for the earlier ones costs more than the other launches
- * do.  The codec's workspace for the stream keeps 32 bytes per tile of state for it, and a
- * word of host memory mapped for the GPU that each encode's first tile writes its escape
- * count to.  0 = never (also for escape-heavy inputs), UINT32_MAX = always; any value is
- * accepted.  Applies to calls that start after it returns.
+ * do.  The codec's workspace for the stream keeps 32 bytes per one-pass tile of state for it,
+ * and a word of host memory mapped for the GPU that each encode's first tile writes its
+ * escape count to.  0 = never (also for escape-heavy inputs), UINT32_MAX = always; any value
+ * is accepted.  Applies to calls that start after it returns.
  */
 int splitzip_set_onepass_tiles(splitzip_codec *codec, uint32_t max_tiles);
 
