@@ -118,12 +118,15 @@ def test_noalloc_escape_heavy_and_many_segments(onepass):
     assert sum(e.n_escapes for e in na) > 0.2 * sum(x.size for x in xa)
 
 
-def test_noalloc_e5m2():
+@pytest.mark.parametrize("first", [3_000_017, 18_000_011])
+def test_noalloc_e5m2(first):
+    """E5M2 in one pass; the larger first call (550 pack tiles) runs the one-pass encode on
+    tiles of 32768 bytes, the second on tiles of 16384, over the same one-pass state."""
     codec = sz.Codec(DEV, 1024, elem="e5m2")
     codec.calibrate(dev(workloads.e5m2_normal(1 << 18, seed=4)))
-    xa = [workloads.e5m2_mixed(3_000_017, 31), workloads.e5m2_mixed(40_000, 32)]
-    xb = [workloads.e5m2_mixed(99_999, 33)]
-    run_pair(codec, (xa, xb), ([x.size // 4 + 64 for x in xa], [x.size // 4 + 64 for x in xb]),
+    xa = [workloads.e5m2_mixed(first, 31, wide_fraction=0.2), workloads.e5m2_mixed(40_000, 32)]
+    xb = [workloads.e5m2_mixed(2_099_999, 33, wide_fraction=0.2)]
+    run_pair(codec, (xa, xb), ([x.size // 2 + 64 for x in xa], [x.size // 2 + 64 for x in xb]),
              stream_check.ELEM_E5M2)
 
 
