@@ -447,11 +447,13 @@ __device__ __forceinline__ uint32_t e8_assemble(uint32_t ex4, uint32_t f)
     return ex4 | (f & 0x03030303u) | ((f << 5) & 0x80808080u);
 }
 
-template <bool kLarge>
+// G: groups per lane (kE8DecGroups, or kE8DecShortGroups in the short tiles).
+template <bool kLarge, int G>
 __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs a)
 {
-    constexpr int G = kE8DecGroups;
-    constexpr uint32_t kTile = 1u << kE8DecTileShift;
+    static_assert(G == kE8DecGroups || G == kE8DecShortGroups, "E5M2 decode tile");
+    constexpr int kShift = G == kE8DecGroups ? kE8DecTileShift : kE8DecShortTileShift;
+    constexpr uint32_t kTile = 1u << kShift;
     __shared__ uint32_t s_exp[kTile / 4];              // exponent bytes of the tile
     __shared__ uint64_t s_off[kTile / 16 + 1];         // chunk offsets of the tile
     __shared__ uint16_t s_pair[256];                   // codes byte -> its two exponent bytes
@@ -472,7 +474,7 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
         sd = a.segs[s];
     }
     const uint64_t n = sd.n;
-    const uint64_t base = (uint64_t)(t - first) << kE8DecTileShift;
+    const uint64_t base = (uint64_t)(t - first) << kShift;
     if (base >= n)
         return;                                              // empty segment
     const uint64_t valid = n - base < (uint64_t)kTile ? n - base : (uint64_t)kTile;
@@ -545,7 +547,7 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
     }
 
     // ---- escape range of the tile --------------------------------------------------------
-    const bool sub_chunk = log2c > (uint32_t)kE8DecTileShift;   // the tile lies inside one chunk
+    const bool sub_chunk = log2c > (uint32_t)kShift;   // the tile lies inside one chunk
     const uint64_t c0 = base >> log2c;
     const uint64_t nc = sub_chunk ? 1 : (valid + C - 1) >> log2c;
     for (uint32_t i = tid; i <= nc; i += kThreads)
@@ -806,10 +808,19 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
 
 hipError_t launch_decode_e5m2(const DecodeArgs &a, hipStream_t stream)
 {
-    if (a.large)
-        decode_e5m2_kernel<true><<<(a.n_tiles + kXcds - 1) / kXcds * kXcds, kThreads, 0, stream>>>(a);
-    else
-        decode_e5m2_kernel<false><<<(a.n_tiles + kXcds - 1) / kXcds * kXcds, kThreads, 0, stream>>>(a);
+    const unsigned grid = (a.n_tiles + kXcds - 1) / kXcds * kXcds;
+    constexpr int G = kE8DecGroups, G1 = kE8DecShortGroups;
+    if (a.tile_shift == (uint32_t)kE8DecShortTileShift) {
+        if (a.large)
+            decode_e5m2_kernel<true, G1><<<grid, kThreads, 0, stream>>>(a);
+        else
+            decode_e5m2_kernel<false, G1><<<grid, kThreads, 0, stream>>>(a);
+    } else {
+        if (a.large)
+            decode_e5m2_kernel<true, G><<<grid, kThreads, 0, stream>>>(a);
+        else
+            decode_e5m2_kernel<false, G><<<grid, kThreads, 0, stream>>>(a);
+    }
     return hipGetLastError();
 }
 

@@ -1139,16 +1139,10 @@ void set_encode_args(sz::EncodeArgs &a, const splitzip_codec *codec, uint32_t n_
     a.stage = n_tiles > codec->stage_tiles.load(std::memory_order_relaxed) ? 1u : 0u;
 }
 
-// Tile starts of a one-pass encode of the segments `desc` into `out` (the launch sequences'
-// `tiles` when the tile lengths agree); false when the call has too many such tiles.
-bool onepass_tiles(const splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
-                   const std::vector<uint32_t> &tiles, std::vector<uint32_t> &out)
+// Tile starts of the segments `desc` in tiles of 2^shift elements into `out`; false when the
+// call has too many such tiles.
+bool tile_starts(const std::vector<sz::SegDesc> &desc, uint32_t shift, std::vector<uint32_t> &out)
 {
-    const uint32_t shift = pack_tile_shift(codec, true, tiles[desc.size()]);
-    if (shift == pack_tile_shift(codec, false, tiles[desc.size()])) {
-        out = tiles;
-        return true;
-    }
     out.resize(desc.size() + 1);
     uint64_t total = 0;
     for (size_t i = 0; i < desc.size(); ++i) {
@@ -1159,6 +1153,19 @@ bool onepass_tiles(const splitzip_codec *codec, const std::vector<sz::SegDesc> &
     }
     out[desc.size()] = (uint32_t)total;
     return true;
+}
+
+// Tile starts of a one-pass encode of the segments `desc` into `out` (the launch sequences'
+// `tiles` when the tile lengths agree); false when the call has too many such tiles.
+bool onepass_tiles(const splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
+                   const std::vector<uint32_t> &tiles, std::vector<uint32_t> &out)
+{
+    const uint32_t shift = pack_tile_shift(codec, true, tiles[desc.size()]);
+    if (shift == pack_tile_shift(codec, false, tiles[desc.size()])) {
+        out = tiles;
+        return true;
+    }
+    return tile_starts(desc, shift, out);
 }
 
 // Whether an encode of n_tiles tiles (of the launch sequences) on `stream` runs in one pass
@@ -1563,12 +1570,31 @@ int splitzip_encode_packed(splitzip_codec *codec, uint32_t n_seg, splitzip_packe
 
 namespace {
 
+// Decode of the segments `desc` (tile starts `tiles`, in tiles of tile_elements(codec, false)
+// elements).  An E5M2 call with more than one escape per kE8ShortDecodeDensity elements, or of
+// at most kE8ShortDecodeTiles tiles, runs tiles of half that length.
 int decode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
-                  const std::vector<uint32_t> &tiles, int64_t book, hipStream_t stream, uint32_t *d_error)
+                  const std::vector<uint32_t> &tiles_in, int64_t book, hipStream_t stream, uint32_t *d_error)
 {
     const uint32_t n_seg = (uint32_t)desc.size();
     if (d_error && !aligned(d_error, 4))
         return fail(SPLITZIP_E_INVALID, "d_error not 4-byte aligned");
+    uint32_t tile_shift = codec->elem == sz::kElemE5M2 ? sz::kE8DecTileShift : sz::kDecTileShift;
+    std::vector<uint32_t> short_tiles;
+    const std::vector<uint32_t> *tp = &tiles_in;
+    if (codec->elem == sz::kElemE5M2) {
+        uint64_t n = 0, E = 0;
+        for (const sz::SegDesc &d : desc) {
+            n += d.n;
+            E += d.esc;
+        }
+        if ((E > n / sz::kE8ShortDecodeDensity || tiles_in[n_seg] <= sz::kE8ShortDecodeTiles) &&
+            tile_starts(desc, sz::kE8DecShortTileShift, short_tiles)) {
+            tile_shift = sz::kE8DecShortTileShift;
+            tp = &short_tiles;
+        }
+    }
+    const std::vector<uint32_t> &tiles = *tp;
     DeviceGuard dg(codec->device);
     if (dg.err != hipSuccess)
         return fail_hip(dg.err, "hipSetDevice");
@@ -1595,6 +1621,7 @@ int decode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
     a.log2_chunk = codec->log2_chunk;
     a.elem = codec->elem;
     a.large = (uint64_t)a.n_tiles > 2ull * codec->stage_tiles.load(std::memory_order_relaxed) ? 1u : 0u;
+    a.tile_shift = tile_shift;
     hipError_t e;
     {
         static const int kDecodeKind[] = {SPLITZIP_KERNEL_DECODE};

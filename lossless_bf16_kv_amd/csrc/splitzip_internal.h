@@ -56,9 +56,18 @@ constexpr int kE8ChainTileShift = 14;
 constexpr uint32_t kE8ShortChainTiles = 512;
 constexpr int kE8DecGroups = 2;
 constexpr int kE8DecTileShift = 14;
+// A decode call with more than one escape per kE8ShortDecodeDensity elements, or of at most
+// kE8ShortDecodeTiles tiles, runs tiles of 8192 (1 group per lane): the escape patch, not the
+// stream, sets the time of escape-heavy tiles, and half-length tiles halve the escapes each
+// workgroup patches; on inputs with few escapes the longer tiles stream better.
+constexpr int kE8DecShortGroups = 1;
+constexpr int kE8DecShortTileShift = 13;
+constexpr uint32_t kE8ShortDecodeDensity = 32;
+constexpr uint32_t kE8ShortDecodeTiles = 512;
 static_assert(kThreads * kE8EncGroups * kE8GroupElems == (1 << kE8EncTileShift), "E5M2 encode tile");
 static_assert(kThreads * kE8ChainGroups * kE8GroupElems == (1 << kE8ChainTileShift), "E5M2 one-pass tile");
 static_assert(kThreads * kE8DecGroups * kE8GroupElems == (1 << kE8DecTileShift), "E5M2 decode tile");
+static_assert(kThreads * kE8DecShortGroups * kE8GroupElems == (1 << kE8DecShortTileShift), "E5M2 short decode tile");
 
 // Inverse-LUT entry of an exponent outside the codebook: nibble 0 plus an escape bit.
 constexpr uint8_t kEscapeEntry = 0x10;
@@ -245,6 +254,7 @@ struct DecodeArgs {
     uint32_t multi_book;
     uint32_t elem;                // kElemBF16 or kElemE5M2
     uint32_t large;               // the build for large calls (chunk lookup in scalar registers)
+    uint32_t tile_shift;          // log2 of the elements per decode tile
 };
 
 // Exponent histograms of one or more tensors: per-workgroup partial counts (each tensor
