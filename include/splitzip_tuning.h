@@ -74,7 +74,9 @@ int splitzip_set_onepass_launches(splitzip_codec *codec, void *stream, uint64_t 
  * Which builds of the pack and decode kernels a call runs; no page fixes it, and the bytes
  * written are the same either way.  An encode call of more than min_tiles tiles (tiles as
  * for splitzip_set_small_tiles), and a decode call of more than 2 * min_tiles decode tiles
- * (8192 BF16 words or 16384 E5M2 bytes, at least one per segment: the same elements), run
+ * (8192 BF16 words or 16384 E5M2 bytes, at least one per segment: the same elements; an
+ * E5M2 call with more than one escape per 32 bytes, or of at most 512 such tiles, decodes on
+ * tiles of 8192 bytes, which count here), run
  * the builds tuned for escape-heavy inputs: in pack a wave gathers a group's escapes in LDS
  * and stores them as one contiguous run when there are more than 64 of them; in decode an
  * escape finds its chunk among offsets held in scalar registers when a tile spans at most 8
