@@ -247,9 +247,28 @@ __device__ __forceinline__ uint32_t segment_end_tile(const EncodeArgs &a, uint32
     return a.n_seg > 1 ? load_const_u32(a.tile_start, s + 1) : a.n_tiles;
 }
 
+// Descriptor s of a segment table the host wrote before the launch (s uniform): a read
+// through the constant address space, so scalar loads, not vector loads that the wave's
+// later loads would queue behind.
+__device__ __forceinline__ SegDesc load_const_segdesc(const SegDesc *segs, uint32_t s)
+{
+    static_assert(sizeof(SegDesc) % 4 == 0, "whole dwords");
+    constexpr uint32_t kWords = sizeof(SegDesc) / 4;
+    const uint32_t *p = reinterpret_cast<const uint32_t *>(segs + s);
+    uint32_t w[kWords];
+#pragma unroll
+    for (uint32_t k = 0; k < kWords; ++k)
+        w[k] = load_const_u32(p, k);
+    SegDesc d;
+    __builtin_memcpy(&d, w, sizeof(d));
+    return d;
+}
+
 __device__ __forceinline__ SegDesc segment_desc(const EncodeArgs &a, uint32_t s)
 {
-    return a.n_seg > 1 ? a.segs[s] : a.seg0;
+    if (a.n_seg > 1)
+        return load_const_segdesc(a.segs, s);
+    return a.seg0;
 }
 
 // ---- pack kernels: escape ranks inside a tile and where the tile's escapes go -----------

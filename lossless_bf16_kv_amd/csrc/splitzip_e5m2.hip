@@ -112,9 +112,9 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
 
     const uint32_t s = a.n_seg > 1 ? find_segment_block(a.tile_start, a.seg_at, t, tid, lane, s_wave_total) : 0u;
     const SegDesc sd = segment_desc(a, s);
+    // the inverse LUT: loaded now, put in LDS once the tile's loads are issued
     const uint8_t *lut = a.multi_book ? a.lut + 256u * sd.book : a.lut;
-    if (tid < 64)
-        reinterpret_cast<uint32_t *>(s_lut)[tid] = reinterpret_cast<const uint32_t *>(lut)[tid];
+    const uint32_t lut_word = tid < 64 ? reinterpret_cast<const uint32_t *>(lut)[tid & 63u] : 0u;
     if (!kChain && a.packed && tid == 0 && t == segment_first_tile(a, s))
         a.seg_total[s] = 0;      // the sums launch adds the segment's escapes into it
     if (kChain) {
@@ -165,6 +165,8 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
             }
         }
     }
+    if (tid < 64)
+        reinterpret_cast<uint32_t *>(s_lut)[tid] = lut_word;
     __syncthreads();   // LUT in LDS
     // Regroup, one group at a time through the wave's own buffer: lane l loaded bytes 16 l and
     // 1024 + 16 l of the group and takes bytes 32 l .. 32 l + 31.  A wave's LDS accesses are
@@ -470,8 +472,8 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
     SegDesc sd = a.seg0;
     if (a.n_seg > 1) {
         const uint32_t s = find_segment_block(a.tile_start, a.seg_at, t, tid, lane, s_cnt);
-        first = a.tile_start[s];
-        sd = a.segs[s];
+        first = load_const_u32(a.tile_start, s);
+        sd = load_const_segdesc(a.segs, s);
     }
     const uint64_t n = sd.n;
     const uint64_t base = (uint64_t)(t - first) << kShift;

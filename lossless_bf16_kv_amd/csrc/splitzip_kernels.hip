@@ -225,10 +225,10 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
 
     const uint32_t s = a.n_seg > 1 ? find_segment_block(a.tile_start, a.seg_at, t, tid, lane, s_wave_total) : 0u;
     const SegDesc sd = segment_desc(a, s);
-    // the segment's inverse LUT (several codebooks in one call: one LUT per codebook)
+    // the segment's inverse LUT (several codebooks in one call: one LUT per codebook), loaded
+    // now and put in LDS after the tile's loads are issued, so that none of them waits for it
     const uint8_t *lut = a.multi_book ? a.lut + 256u * sd.book : a.lut;
-    if (tid < 64)
-        reinterpret_cast<uint32_t *>(s_lut)[tid] = reinterpret_cast<const uint32_t *>(lut)[tid];
+    const uint32_t lut_word = tid < 64 ? reinterpret_cast<const uint32_t *>(lut)[tid & 63u] : 0u;
     if (!kChain && a.packed && tid == 0 && t == segment_first_tile(a, s))
         a.seg_total[s] = 0;      // the sums launch adds the segment's escapes into it
     if (kChain) {
@@ -263,6 +263,8 @@ __global__ __launch_bounds__(kThreads) void encode_pack_kernel(const EncodeArgs 
                               wds[4] | ((uint32_t)wds[5] << 16), wds[6] | ((uint32_t)wds[7] << 16));
         }
     }
+    if (tid < 64)
+        reinterpret_cast<uint32_t *>(s_lut)[tid] = lut_word;
     __syncthreads();   // LUT in LDS
 
     // ---- a2: dense split and pack ---------------------------------------------------------
@@ -1232,8 +1234,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
     SegDesc sd = a.seg0;
     if (a.n_seg > 1) {
         const uint32_t s = find_segment_block(a.tile_start, a.seg_at, t, tid, lane, s_cnt);
-        first = a.tile_start[s];
-        sd = a.segs[s];
+        first = load_const_u32(a.tile_start, s);
+        sd = load_const_segdesc(a.segs, s);
     }
     const uint64_t n = sd.n;
     const uint64_t base = (uint64_t)(t - first) << kDecTileShift;
