@@ -496,13 +496,18 @@ __global__ __launch_bounds__(kThreads) void decode_e5m2_kernel(const DecodeArgs 
     }
 
     // ---- loads ---------------------------------------------------------------------------
+    // a packed stream's header, through scalar loads as in the BF16 decode
     uint4 h0{}, h1{}, h2{}, h3{};
     if (sd.header) {
-        const uint4 *h = reinterpret_cast<const uint4 *>(sd.header);
-        h0 = h[0];
-        h1 = h[1];
-        h2 = h[2];
-        h3 = h[3];
+        const uint32_t *h = reinterpret_cast<const uint32_t *>(sd.header);
+        uint32_t w[16];
+#pragma unroll
+        for (uint32_t k = 0; k < 16; ++k)
+            w[k] = load_const_u32(h, k);
+        h0 = make_uint4(w[0], w[1], w[2], w[3]);
+        h1 = make_uint4(w[4], w[5], w[6], w[7]);
+        h2 = make_uint4(w[8], w[9], w[10], w[11]);
+        h3 = make_uint4(w[12], w[13], w[14], w[15]);
     }
     uint32_t smv[G][3], cw[G][4];
 #pragma unroll
