@@ -1247,12 +1247,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a)
     const uint64_t E = sd.esc;
     uint32_t cb[4] = {a.cb[0], a.cb[1], a.cb[2], a.cb[3]};
     if (a.multi_book) {
-        // the segment's own codebook (uniform: the same four dwords for the whole tile)
+        // the segment's own codebook (uniform and read-only: scalar loads)
         const uint32_t *c = a.cbs + 4u * sd.book;
-        cb[0] = c[0];
-        cb[1] = c[1];
-        cb[2] = c[2];
-        cb[3] = c[3];
+        cb[0] = load_const_u32(c, 0);
+        cb[1] = load_const_u32(c, 1);
+        cb[2] = load_const_u32(c, 2);
+        cb[3] = load_const_u32(c, 3);
     }
 
     // ---- loads ---------------------------------------------------------------------------
