@@ -137,7 +137,8 @@ constexpr uint32_t kChainStride = 4;
 // position, u8 exponent) and its chunk starts' escape ranks (u16, at most one per 16 words)
 // in LDS; waves whose escapes all fit end and free their registers while wave 0 waits for
 // the tile's escape offset and writes them; a wave with escapes past the stash waits too and
-// then sends those through a quarter of the stash, a quarter at a time.
+// then sends those through the stash again (stash_rest: a second round in tiles of at most
+// twice the stash, a quarter of it per wave in longer ones).
 constexpr uint32_t kStashEscapes = 8192;
 constexpr uint32_t kStashChunks = kEncTileWords / 16;
 // byte offset of the positions in the stash: the copy out reads 16 bytes before each array
