@@ -222,9 +222,18 @@ __global__ __launch_bounds__(kThreads) void encode_pack_e5m2_kernel(const Encode
     uint32_t tile_total;
     uint32_t wave_end;
     tile_escape_ranks<G>(counts, lane, wave, s_wave_total, rank, tile_total, wave_end);
-    if (a.first_tile_escapes && t == 0 && tid == 0)   // scaled to a tile of the launch sequences
-        __hip_atomic_store(a.first_tile_escapes, tile_total << (kE8EncTileShift - kShift), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_SYSTEM);
+    if (a.first_tile_escapes && t == 0 && tid == 0) {
+        // the count scaled to a tile of the launch sequences, and whether it falls unevenly
+        uint32_t lo = s_wave_total[0], hi = s_wave_total[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) {
+            lo = s_wave_total[w] < lo ? s_wave_total[w] : lo;
+            hi = s_wave_total[w] > hi ? s_wave_total[w] : hi;
+        }
+        const uint32_t uneven = hi > 2 * lo + 64 ? kHintUneven : 0u;
+        __hip_atomic_store(a.first_tile_escapes, (tile_total << (kE8EncTileShift - kShift)) | uneven,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
 
     if (kChain) {
         // one pass, early release, as in the BF16 pack: the escapes of rank below

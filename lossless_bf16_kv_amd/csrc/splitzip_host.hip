@@ -750,12 +750,14 @@ uint64_t tile_elements(const splitzip_codec *c, bool encode)
 }
 
 // log2 of the elements per pack tile of a call of n_tiles tiles of tile_elements(c, true): a
-// one-pass encode of E5M2 bytes over at most kE8ShortChainTiles of them takes tiles half as
-// long.
-uint32_t pack_tile_shift(const splitzip_codec *c, bool onepass, uint64_t n_tiles)
+// one-pass encode of E5M2 bytes takes tiles half as long over at most kE8ShortChainTiles of
+// them, or over any number when the input's escapes cluster (`clustered`: the previous
+// encode's first tile was escape-heavy with its escapes falling unevenly over its waves).
+uint32_t pack_tile_shift(const splitzip_codec *c, bool onepass, uint64_t n_tiles, bool clustered = false)
 {
     if (c->elem == sz::kElemE5M2)
-        return onepass && n_tiles <= sz::kE8ShortChainTiles ? sz::kE8ChainTileShift : sz::kE8EncTileShift;
+        return onepass && (n_tiles <= sz::kE8ShortChainTiles || clustered) ? sz::kE8ChainTileShift
+                                                                          : sz::kE8EncTileShift;
     return sz::kEncTileShift;
 }
 
@@ -1156,11 +1158,12 @@ bool tile_starts(const std::vector<sz::SegDesc> &desc, uint32_t shift, std::vect
 }
 
 // Tile starts of a one-pass encode of the segments `desc` into `out` (the launch sequences'
-// `tiles` when the tile lengths agree); false when the call has too many such tiles.
+// `tiles` when the tile lengths agree; `clustered` as for pack_tile_shift); false when the
+// call has too many such tiles.
 bool onepass_tiles(const splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
-                   const std::vector<uint32_t> &tiles, std::vector<uint32_t> &out)
+                   const std::vector<uint32_t> &tiles, bool clustered, std::vector<uint32_t> &out)
 {
-    const uint32_t shift = pack_tile_shift(codec, true, tiles[desc.size()]);
+    const uint32_t shift = pack_tile_shift(codec, true, tiles[desc.size()], clustered);
     if (shift == pack_tile_shift(codec, false, tiles[desc.size()])) {
         out = tiles;
         return true;
@@ -1230,11 +1233,13 @@ int encode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
     ensure_hint(w);
     // an input whose first tile outgrew its slot last time is taken to be escape-heavy again:
     // the launch sequences would move its escapes through scratch
-    const bool heavy = w->hint && *reinterpret_cast<volatile uint32_t *>(w->hint) > slot_escapes(codec);
-    // the one-pass tiles (shorter for E5M2)
+    const uint32_t hint = w->hint ? *reinterpret_cast<volatile uint32_t *>(w->hint) : 0u;
+    const bool heavy = (hint & ~sz::kHintUneven) > slot_escapes(codec);
+    const bool clustered = heavy && (hint & sz::kHintUneven) != 0;
+    // the one-pass tiles (shorter for some E5M2 calls)
     std::vector<uint32_t> chain_tiles;
     const bool onepass = use_onepass(codec, packed, n_tiles, stream, heavy) &&
-                         onepass_tiles(codec, desc, tiles, chain_tiles);
+                         onepass_tiles(codec, desc, tiles, clustered, chain_tiles);
     if (onepass) {
         // no scratch: only the workspace's one-pass state
         const uint32_t n_chain = chain_tiles[n_seg];
@@ -1248,8 +1253,8 @@ int encode_launch(splitzip_codec *codec, const std::vector<sz::SegDesc> &desc,
             (rc = stage_descriptors(w, desc, chain_tiles, &a.segs, &a.tile_start, &a.seg_at)) != SPLITZIP_OK)
             return rc;
         uint8_t *res = d_result ? reinterpret_cast<uint8_t *>(d_result) : w->result;
-        set_encode_args(a, codec, n_seg, n_chain, pack_tile_shift(codec, true, n_tiles), book, packed, nullptr,
-                        EncodeScratch(0, 0, 0, 0), nullptr, 0, false, res);
+        set_encode_args(a, codec, n_seg, n_chain, pack_tile_shift(codec, true, n_tiles, clustered), book, packed,
+                        nullptr, EncodeScratch(0, 0, 0, 0), nullptr, 0, false, res);
         a.chain_status = w->chain;
         a.chain_cap = w->chain_cap;
         a.first_tile_escapes = w->d_hint;

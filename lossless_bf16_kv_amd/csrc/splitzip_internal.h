@@ -54,6 +54,10 @@ constexpr int kE8EncTileShift = 15;
 constexpr int kE8ChainGroups = 2;
 constexpr int kE8ChainTileShift = 14;
 constexpr uint32_t kE8ShortChainTiles = 512;
+// Bit of the first-tile escape count (EncodeArgs::first_tile_escapes) set when that tile's
+// escapes fall unevenly over its waves (the most over twice the fewest, plus 64): an input
+// whose escapes cluster, for which the short one-pass tiles also pay at larger sizes.
+constexpr uint32_t kHintUneven = 0x80000000u;
 constexpr int kE8DecGroups = 2;
 constexpr int kE8DecTileShift = 14;
 // A decode call with more than one escape per kE8ShortDecodeDensity elements, or of at most
@@ -237,7 +241,8 @@ struct EncodeArgs {
     uint32_t chain_cap;
     uint32_t chain_tag;
     // optional, host memory mapped for the device: the call's first tile stores its escape
-    // count there (the host picks the next call's launch sequence with it)
+    // count there (E5M2: scaled to a tile of the launch sequences, with kHintUneven); the host
+    // picks the next call's launch sequence and one-pass tile length with it
     uint32_t *first_tile_escapes;
 };
 

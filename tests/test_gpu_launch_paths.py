@@ -319,6 +319,34 @@ def test_onepass_for_escape_heavy_input_past_the_limit():
     t8.assert_same_stream(c8, e2, x8)
 
 
+
+def test_e5m2_clustered_escapes_switch_the_onepass_tile():
+    """An E5M2 call of 600 pack tiles whose escapes cluster (blocks of 4096 bytes scaled by
+    2^k, k from -8 to 8, as in the escape-stress input): the first call runs one pass on tiles
+    of 32768 bytes, and its first tile marks the input escape-heavy and uneven, so the later
+    ones run on tiles of 16384; every call's stream equals the oracle's.  A uniform draw of
+    the same size stays on the long tiles (the same bytes either way)."""
+    n = 600 * TILE8 - 1000
+    rng = np.random.default_rng(61)
+    z = rng.standard_normal(n).astype(np.float32)
+    z *= np.repeat(np.exp2(rng.integers(-8, 9, -(-n // 4096))).astype(np.float32), 4096)[:n]
+    x = workloads.e5m2_bits(z)
+    c8 = t8.codec_for(workloads.e5m2_normal(50_000, 6), 1024)
+    c8.profile(True)
+    encs = [c8.encode(t8.dev8(x), escape_capacity=n) for _ in range(3)]
+    t = c8.kernel_times(reset=True)
+    c8.profile(False)
+    assert t["encode_onepass"][1] == 3
+    for e in encs[1:]:
+        for name in ("sm", "codes", "chunk_off", "esc_pos", "esc_exp"):
+            assert torch.equal(getattr(e, name), getattr(encs[0], name)), name
+    t8.assert_same_stream(c8, encs[2], x)
+    u = workloads.e5m2_mixed(n, 62, wide_fraction=0.3)
+    eu = [c8.encode(t8.dev8(u), escape_capacity=n) for _ in range(2)]
+    for name in ("sm", "codes", "chunk_off", "esc_pos", "esc_exp"):
+        assert torch.equal(getattr(eu[1], name), getattr(eu[0], name)), name
+    t8.assert_same_stream(c8, eu[1], u)
+
 @pytest.mark.parametrize("wide", [0.0, 0.02, 1.0])
 def test_onepass_many_tiles_and_repeats(wide):
     """1100 tiles (more than one round of the GPU's workgroups, so look-backs find earlier
