@@ -43,7 +43,8 @@ int splitzip_set_small_tiles(splitzip_codec *codec, uint32_t max_tiles);
  * their status words (a decoupled look-back over tiles in launch order) and writes its
  * escapes, chunk offsets and, as a segment's last tile, E straight to their final places
  * (an E5M2 call of at most 512 tiles runs it on tiles of half the length, 16384 bytes: on a
- * grid that far from fills the GPU, more tiles of less work each end sooner).
+ * grid that far from fills the GPU, more tiles of less work each end sooner; so does any
+ * escape-heavy E5M2 call after one whose first tile had its escapes unevenly spread).
  * Other calls (larger ones, packed streams, and calls on a stream that is being captured
  * into a graph, since each launch's tag is a kernel argument that a replay would repeat) run
  * the launch sequences of splitzip_set_small_tiles, with one exception: when the previous
